@@ -1,0 +1,197 @@
+"""KIVI reference oracle: TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It wraps the plain C oracle (kivi_oracle.c) with ctypes
+and numpy; it shares no code with the GPU library and the product path never
+calls it.  All tensors are numpy arrays; 16-bit floats travel as uint16 bit
+patterns (dtype 0 = fp16, 1 = bf16).
+
+`Oracle(path)` wraps any build of kivi_oracle.c (the mutation tests load
+deliberately broken copies); the module-level functions use the default
+build at oracle/libkivi_oracle.so.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build
+
+FP16 = 0
+BF16 = 1
+
+
+def n_groups(n, g):
+    return (n + g - 1) // g if g > 0 else 0
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    def __init__(self, path=LIB):
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        I = ctypes.c_int
+        F = ctypes.c_float
+        L.kivi_ref_half_to_float.argtypes = [ctypes.c_uint16]
+        L.kivi_ref_half_to_float.restype = F
+        L.kivi_ref_float_to_half.argtypes = [F]
+        L.kivi_ref_float_to_half.restype = ctypes.c_uint16
+        L.kivi_ref_bf16_to_float.argtypes = [ctypes.c_uint16]
+        L.kivi_ref_bf16_to_float.restype = F
+        L.kivi_ref_float_to_bf16.argtypes = [F]
+        L.kivi_ref_float_to_bf16.restype = ctypes.c_uint16
+        L.kivi_ref_widen_array.argtypes = [P, I64, I, P]
+        L.kivi_ref_narrow_array.argtypes = [P, I64, I, P]
+        L.kivi_ref_group_params.argtypes = [P, I64, I, P, P]
+        L.kivi_ref_code.argtypes = [F, F, F, I]
+        L.kivi_ref_recon.argtypes = [I, F, F]
+        L.kivi_ref_recon.restype = F
+        for name in ("kivi_ref_quant_keys_unpacked",
+                     "kivi_ref_quant_values_unpacked",
+                     "kivi_ref_quant_keys", "kivi_ref_quant_values"):
+            getattr(L, name).argtypes = [P, I, I64, I64, I64, I, I64, P, P, P]
+        L.kivi_ref_pack.argtypes = [P, I64, I64, I, P]
+        L.kivi_ref_unpack.argtypes = [P, I64, I64, I, P]
+        for name in ("kivi_ref_dequant_keys", "kivi_ref_dequant_values"):
+            getattr(L, name).argtypes = [P, P, P, I64, I64, I64, I, I64, I, P]
+        self.L = L
+        self.path = path
+
+    @staticmethod
+    def _check(st, what):
+        if st != 0:
+            raise ValueError(f"oracle {what}: bad arguments")
+
+    # conversions ------------------------------------------------------------
+    def widen(self, bits16, dtype):
+        a = np.ascontiguousarray(bits16, dtype=np.uint16)
+        out = np.zeros(a.shape, np.float32)
+        self._check(self.L.kivi_ref_widen_array(_ptr(a), a.size, dtype,
+                                                _ptr(out)), "widen")
+        return out
+
+    def narrow(self, f32, dtype):
+        a = np.ascontiguousarray(f32, dtype=np.float32)
+        out = np.zeros(a.shape, np.uint16)
+        self._check(self.L.kivi_ref_narrow_array(_ptr(a), a.size, dtype,
+                                                 _ptr(out)), "narrow")
+        return out
+
+    # one group / one element -----------------------------------------------
+    def group_params(self, vals, bits):
+        v = np.ascontiguousarray(vals, dtype=np.float32)
+        sc = np.zeros(1, np.float32)
+        z = np.zeros(1, np.float32)
+        self._check(self.L.kivi_ref_group_params(_ptr(v), v.size, bits,
+                                                 _ptr(sc), _ptr(z)),
+                    "group_params")
+        return sc[0], z[0]
+
+    def code(self, f, scale, zero, bits):
+        return self.L.kivi_ref_code(float(f), float(scale), float(zero), bits)
+
+    def recon(self, c, scale, zero):
+        return np.float32(self.L.kivi_ref_recon(int(c), float(scale),
+                                                float(zero)))
+
+    # tensors ----------------------------------------------------------------
+    def _quant(self, name, x, dtype, bits, group, packed, key_params):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        BH, S, D = x.shape
+        if key_params:
+            pshape = (BH, n_groups(S, group), D)
+        else:
+            pshape = (BH, S, n_groups(D, group))
+        sc = np.zeros(pshape, np.float32)
+        z = np.zeros(pshape, np.float32)
+        if packed:
+            if (D * bits) % 8:
+                raise ValueError("D*bits must be a multiple of 8")
+            codes = np.zeros((BH, S, D * bits // 8), np.uint8)
+        else:
+            codes = np.zeros((BH, S, D), np.uint8)
+        self._check(getattr(self.L, name)(_ptr(x), dtype, BH, S, D, bits,
+                                          group, _ptr(codes), _ptr(sc),
+                                          _ptr(z)), name)
+        return codes, sc, z
+
+    def quant_keys(self, x, dtype, bits, group):
+        """-> (packed [BH,S,D*bits/8] u8, scale [BH,NG,D], zero [BH,NG,D])"""
+        return self._quant("kivi_ref_quant_keys", x, dtype, bits, group,
+                           True, True)
+
+    def quant_values(self, x, dtype, bits, group):
+        """-> (packed [BH,S,D*bits/8] u8, scale [BH,S,NGD], zero [BH,S,NGD])"""
+        return self._quant("kivi_ref_quant_values", x, dtype, bits, group,
+                           True, False)
+
+    def quant_keys_unpacked(self, x, dtype, bits, group):
+        return self._quant("kivi_ref_quant_keys_unpacked", x, dtype, bits,
+                           group, False, True)
+
+    def quant_values_unpacked(self, x, dtype, bits, group):
+        return self._quant("kivi_ref_quant_values_unpacked", x, dtype, bits,
+                           group, False, False)
+
+    def pack(self, codes, bits):
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        D = codes.shape[-1]
+        rows = codes.size // D if D else 0
+        out = np.zeros(codes.shape[:-1] + (D * bits // 8,), np.uint8)
+        self._check(self.L.kivi_ref_pack(_ptr(codes), rows, D, bits,
+                                         _ptr(out)), "pack")
+        return out
+
+    def unpack(self, packed, D, bits):
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        rb = D * bits // 8
+        rows = packed.size // rb if rb else 0
+        out = np.zeros(packed.shape[:-1] + (D,), np.uint8)
+        self._check(self.L.kivi_ref_unpack(_ptr(packed), rows, D, bits,
+                                           _ptr(out)), "unpack")
+        return out
+
+    def _dequant(self, name, packed, scale, zero, shape, bits, group,
+                 out_dtype):
+        BH, S, D = shape
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        zero = np.ascontiguousarray(zero, dtype=np.float32)
+        out = np.zeros((BH, S, D), np.uint16)
+        self._check(getattr(self.L, name)(_ptr(packed), _ptr(scale),
+                                          _ptr(zero), BH, S, D, bits, group,
+                                          out_dtype, _ptr(out)), name)
+        return out
+
+    def dequant_keys(self, packed, scale, zero, shape, bits, group,
+                     out_dtype):
+        return self._dequant("kivi_ref_dequant_keys", packed, scale, zero,
+                             shape, bits, group, out_dtype)
+
+    def dequant_values(self, packed, scale, zero, shape, bits, group,
+                       out_dtype):
+        return self._dequant("kivi_ref_dequant_values", packed, scale, zero,
+                             shape, bits, group, out_dtype)
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def __getattr__(name):
+    # module-level access to the default oracle's methods
+    if name.startswith("_"):
+        raise AttributeError(name)
+    return getattr(default(), name)

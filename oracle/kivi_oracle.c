@@ -1,0 +1,371 @@
+/*
+ * KIVI reference oracle (TEST INFRASTRUCTURE ONLY; see kivi_oracle.h).
+ *
+ * Plain loops in the order the VeloxQuant-MLX pages state the method.  No
+ * blocking, no fusion, no vectorisation: every quantity is computed by the
+ * obvious loop so a reader can check it against the pages by eye.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off (no -ffast-math, no -march).
+ * On x86-64 every float operation below is one SSE binary32 operation,
+ * rounded to nearest even.
+ */
+#include "kivi_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+static uint32_t f32_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return u;
+}
+
+static float bits_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 16-bit formats.  IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10      */
+/* fraction bits.  bfloat16: the top half of a binary32.                    */
+/* ------------------------------------------------------------------------ */
+
+float kivi_ref_half_to_float(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    float v;
+    if (e == 0) {
+        v = ldexpf((float)m, -24); /* subnormal: m * 2^-24, exact */
+    } else if (e == 31) {
+        v = (m == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexpf((float)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+uint16_t kivi_ref_float_to_half(float f) {
+    uint32_t u = f32_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u); /* NaN */
+    /* 65520 is the midpoint between 65504 (odd fraction) and 2^16: ties go
+       to the even side, which overflows to infinity. */
+    if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);
+    if (a >= 0x38800000u) { /* result is a normal binary16 (>= 2^-14) */
+        uint32_t e16 = (a >> 23) - 127u + 15u;
+        uint32_t mant = a & 0x7fffffu;
+        uint32_t h = (e16 << 10) | (mant >> 13);
+        uint32_t rem = mant & 0x1fffu; /* the 13 dropped bits */
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;
+        return (uint16_t)(sign | h);
+    }
+    /* Subnormal or zero result: round a / 2^-24 to an integer, ties even. */
+    if (a <= 0x33000000u) return sign; /* <= 2^-25: rounds to 0 */
+    {
+        uint32_t E = a >> 23; /* biased exponent, 102..112 here */
+        uint32_t M = (a & 0x7fffffu) | 0x800000u;
+        uint32_t shift = 126u - E; /* value / 2^-24 = M * 2^-shift */
+        uint32_t q = M >> shift;
+        uint32_t rem = M & ((1u << shift) - 1u);
+        uint32_t half = 1u << (shift - 1u);
+        if (rem > half || (rem == half && (q & 1u))) q += 1u;
+        return (uint16_t)(sign | q);
+    }
+}
+
+float kivi_ref_bf16_to_float(uint16_t h) { return bits_f32((uint32_t)h << 16); }
+
+uint16_t kivi_ref_float_to_bf16(float f) {
+    uint32_t u = f32_bits(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u); /* NaN */
+    /* round to nearest even on the low 16 bits */
+    uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(r >> 16);
+}
+
+static float widen(uint16_t h, int dtype) {
+    return dtype == 0 ? kivi_ref_half_to_float(h) : kivi_ref_bf16_to_float(h);
+}
+
+static uint16_t narrow(float f, int dtype) {
+    return dtype == 0 ? kivi_ref_float_to_half(f) : kivi_ref_float_to_bf16(f);
+}
+
+int kivi_ref_widen_array(const uint16_t* in, int64_t n, int dtype, float* out) {
+    if (n < 0 || (dtype != 0 && dtype != 1)) return 1;
+    for (int64_t i = 0; i < n; ++i) out[i] = widen(in[i], dtype);
+    return 0;
+}
+
+int kivi_ref_narrow_array(const float* in, int64_t n, int dtype, uint16_t* out) {
+    if (n < 0 || (dtype != 0 && dtype != 1)) return 1;
+    for (int64_t i = 0; i < n; ++i) out[i] = narrow(in[i], dtype);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The quantizer on one group.                                              */
+/* ------------------------------------------------------------------------ */
+
+static int bits_ok(int bits) {
+    return bits == 1 || bits == 2 || bits == 4 || bits == 8;
+}
+
+/*
+ * KIVI blog post on the fused Metal kernels, section "What we're actually
+ * optimizing": zero = min(group); scale = (max(group) - min(group)) /
+ * (2^bits - 1).  Min and max are a sequential scan in fp32 as the pages'
+ * kernels keep them (sections "Kernel A" and "Kernel B").  A min or max that
+ * compares equal to zero is stored as +0 (reading: the pages are silent on
+ * signed zero; this makes the result independent of scan order).
+ */
+int kivi_ref_group_params(const float* vals, int64_t n, int bits, float* scale,
+                          float* zero) {
+    if (n <= 0 || !bits_ok(bits)) return 1;
+    float mn = vals[0];
+    float mx = vals[0];
+    for (int64_t i = 1; i < n; ++i) {
+        if (vals[i] < mn) mn = vals[i];
+        if (vals[i] > mx) mx = vals[i];
+    }
+    if (mn == 0.0f) mn = 0.0f;
+    if (mx == 0.0f) mx = 0.0f;
+    float range = mx - mn;
+    float levels = (float)((1 << bits) - 1);
+    *zero = mn;
+    *scale = range / levels;
+    return 0;
+}
+
+/*
+ * Same section and the 0.8.0 release post, section "What KIVI is":
+ * q = round((x - zero) / scale), an unsigned code in [0, 2^bits - 1].  The
+ * op order is the MLX chain the post lists: subtract, divide, round, clip.
+ * Rounding is half-to-even (section "Three ways to be off by one bit",
+ * item 2).  Reading for the silent case scale == 0 (a constant group): code 0.
+ * The clip is max-then-min with IEEE maxNum/minNum, so a NaN quotient (only
+ * possible when a group's range overflows binary32) gives code 0.
+ */
+int kivi_ref_code(float f, float scale, float zero, int bits) {
+    float maxc = (float)((1 << bits) - 1);
+    if (scale == 0.0f) return 0;
+    float a = f - zero;
+    float t = a / scale;
+    float r = rintf(t);
+    r = fmaxf(r, 0.0f);
+    r = fminf(r, maxc);
+    return (int)r;
+}
+
+/*
+ * Section "What we're actually optimizing": recon = q * scale + zero, and
+ * section "Three ways to be off by one bit", item 1: the product is rounded
+ * before the add (two roundings, never a fused multiply-add).
+ */
+float kivi_ref_recon(int code, float scale, float zero) {
+    float p = (float)code * scale;
+    float r = p + zero;
+    return r;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole tensors.  Layout: section "The layout problem that shapes          */
+/* everything": [BH, S, D] row-major.                                       */
+/* ------------------------------------------------------------------------ */
+
+static int shape_ok(int64_t BH, int64_t S, int64_t D, int bits, int64_t group) {
+    if (BH < 0 || S < 0 || D < 0) return 0;
+    if (!bits_ok(bits)) return 0;
+    if (group < 1) return 0;
+    if ((D * bits) % 8 != 0) return 0;
+    return 1;
+}
+
+/*
+ * Keys, per channel (section "Kernel A — per-channel keys"): for every
+ * (bh, token group g, channel d) the group is tokens
+ * s in [g*G, min(g*G + G, S)) of channel d.  Params are stored [BH, NG, D].
+ * A ragged last group is taken over its real tokens only; the pages pad it
+ * with copies of its last element (section "Three ways to be off by one bit",
+ * item 3), which cannot change a min or a max.
+ */
+int kivi_ref_quant_keys_unpacked(const uint16_t* x, int dtype, int64_t BH,
+                                 int64_t S, int64_t D, int bits, int64_t group,
+                                 uint8_t* codes, float* scale, float* zero) {
+    if (!shape_ok(BH, S, D, bits, group) || (dtype != 0 && dtype != 1)) return 1;
+    int64_t NG = (S + group - 1) / group;
+    float* vals = (float*)malloc((size_t)(group > 0 ? group : 1) * sizeof(float));
+    if (!vals) return 1;
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        for (int64_t g = 0; g < NG; ++g) {
+            int64_t s0 = g * group;
+            int64_t s1 = s0 + group < S ? s0 + group : S;
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t s = s0; s < s1; ++s)
+                    vals[s - s0] = widen(x[(bh * S + s) * D + d], dtype);
+                float sc, z;
+                kivi_ref_group_params(vals, s1 - s0, bits, &sc, &z);
+                scale[(bh * NG + g) * D + d] = sc;
+                zero[(bh * NG + g) * D + d] = z;
+                for (int64_t s = s0; s < s1; ++s)
+                    codes[(bh * S + s) * D + d] =
+                        (uint8_t)kivi_ref_code(vals[s - s0], sc, z, bits);
+            }
+        }
+    }
+    free(vals);
+    return 0;
+}
+
+/*
+ * Values, per token (section "Kernel B — per-token values"): for every
+ * (bh, token s, channel group j) the group is channels
+ * d in [j*G, min(j*G + G, D)) of token s.  Params are stored [BH, S, NGD].
+ */
+int kivi_ref_quant_values_unpacked(const uint16_t* x, int dtype, int64_t BH,
+                                   int64_t S, int64_t D, int bits,
+                                   int64_t group, uint8_t* codes, float* scale,
+                                   float* zero) {
+    if (!shape_ok(BH, S, D, bits, group) || (dtype != 0 && dtype != 1)) return 1;
+    int64_t NGD = (D + group - 1) / group;
+    float* vals = (float*)malloc((size_t)(group > 0 ? group : 1) * sizeof(float));
+    if (!vals) return 1;
+    for (int64_t bh = 0; bh < BH; ++bh) {
+        for (int64_t s = 0; s < S; ++s) {
+            for (int64_t j = 0; j < NGD; ++j) {
+                int64_t d0 = j * group;
+                int64_t d1 = d0 + group < D ? d0 + group : D;
+                for (int64_t d = d0; d < d1; ++d)
+                    vals[d - d0] = widen(x[(bh * S + s) * D + d], dtype);
+                float sc, z;
+                kivi_ref_group_params(vals, d1 - d0, bits, &sc, &z);
+                scale[(bh * S + s) * NGD + j] = sc;
+                zero[(bh * S + s) * NGD + j] = z;
+                for (int64_t d = d0; d < d1; ++d)
+                    codes[(bh * S + s) * D + d] =
+                        (uint8_t)kivi_ref_code(vals[d - d0], sc, z, bits);
+            }
+        }
+    }
+    free(vals);
+    return 0;
+}
+
+/*
+ * Packing (TurboQuant Metal kernels post, section "Kernel 1: Bit-Packing";
+ * TurboQuant port overview, section "The Bit-Packing Problem"): 8/bits codes
+ * per byte, code i of a byte in bits [i*bits, (i+1)*bits).  Applied along D
+ * for every row (bh, s); a row holds D*bits/8 bytes.
+ */
+int kivi_ref_pack(const uint8_t* codes, int64_t rows, int64_t D, int bits,
+                  uint8_t* packed) {
+    if (!bits_ok(bits) || rows < 0 || D < 0 || (D * bits) % 8 != 0) return 1;
+    int64_t per = 8 / bits;
+    int64_t row_bytes = D * bits / 8;
+    uint32_t mask = (1u << bits) - 1u;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < row_bytes; ++b) {
+            uint32_t byte = 0;
+            for (int64_t i = 0; i < per; ++i) {
+                uint32_t c = codes[r * D + b * per + i] & mask;
+                byte |= c << (i * bits);
+            }
+            packed[r * row_bytes + b] = (uint8_t)byte;
+        }
+    }
+    return 0;
+}
+
+int kivi_ref_unpack(const uint8_t* packed, int64_t rows, int64_t D, int bits,
+                    uint8_t* codes) {
+    if (!bits_ok(bits) || rows < 0 || D < 0 || (D * bits) % 8 != 0) return 1;
+    int64_t per = 8 / bits;
+    int64_t row_bytes = D * bits / 8;
+    uint32_t mask = (1u << bits) - 1u;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t d = 0; d < D; ++d) {
+            uint32_t byte = packed[r * row_bytes + d / per];
+            codes[r * D + d] = (uint8_t)((byte >> ((d % per) * bits)) & mask);
+        }
+    return 0;
+}
+
+int kivi_ref_quant_keys(const uint16_t* x, int dtype, int64_t BH, int64_t S,
+                        int64_t D, int bits, int64_t group, uint8_t* packed,
+                        float* scale, float* zero) {
+    if (!shape_ok(BH, S, D, bits, group)) return 1;
+    size_t n = (size_t)(BH * S * D);
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    if (!codes) return 1;
+    int st = kivi_ref_quant_keys_unpacked(x, dtype, BH, S, D, bits, group,
+                                          codes, scale, zero);
+    if (st == 0) st = kivi_ref_pack(codes, BH * S, D, bits, packed);
+    free(codes);
+    return st;
+}
+
+int kivi_ref_quant_values(const uint16_t* x, int dtype, int64_t BH, int64_t S,
+                          int64_t D, int bits, int64_t group, uint8_t* packed,
+                          float* scale, float* zero) {
+    if (!shape_ok(BH, S, D, bits, group)) return 1;
+    size_t n = (size_t)(BH * S * D);
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    if (!codes) return 1;
+    int st = kivi_ref_quant_values_unpacked(x, dtype, BH, S, D, bits, group,
+                                            codes, scale, zero);
+    if (st == 0) st = kivi_ref_pack(codes, BH * S, D, bits, packed);
+    free(codes);
+    return st;
+}
+
+/* Dequantize: unpack, look up the element's group params, recon, narrow. */
+int kivi_ref_dequant_keys(const uint8_t* packed, const float* scale,
+                          const float* zero, int64_t BH, int64_t S, int64_t D,
+                          int bits, int64_t group, int out_dtype,
+                          uint16_t* out) {
+    if (!shape_ok(BH, S, D, bits, group) || (out_dtype != 0 && out_dtype != 1))
+        return 1;
+    int64_t NG = (S + group - 1) / group;
+    size_t n = (size_t)(BH * S * D);
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    if (!codes) return 1;
+    kivi_ref_unpack(packed, BH * S, D, bits, codes);
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t d = 0; d < D; ++d) {
+                int64_t p = (bh * NG + s / group) * D + d;
+                float r = kivi_ref_recon(codes[(bh * S + s) * D + d], scale[p],
+                                         zero[p]);
+                out[(bh * S + s) * D + d] = narrow(r, out_dtype);
+            }
+    free(codes);
+    return 0;
+}
+
+int kivi_ref_dequant_values(const uint8_t* packed, const float* scale,
+                            const float* zero, int64_t BH, int64_t S,
+                            int64_t D, int bits, int64_t group, int out_dtype,
+                            uint16_t* out) {
+    if (!shape_ok(BH, S, D, bits, group) || (out_dtype != 0 && out_dtype != 1))
+        return 1;
+    int64_t NGD = (D + group - 1) / group;
+    size_t n = (size_t)(BH * S * D);
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    if (!codes) return 1;
+    kivi_ref_unpack(packed, BH * S, D, bits, codes);
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t d = 0; d < D; ++d) {
+                int64_t p = (bh * S + s) * NGD + d / group;
+                float r = kivi_ref_recon(codes[(bh * S + s) * D + d], scale[p],
+                                         zero[p]);
+                out[(bh * S + s) * D + d] = narrow(r, out_dtype);
+            }
+    free(codes);
+    return 0;
+}

@@ -1,0 +1,106 @@
+/*
+ * KIVI reference oracle: plain, slow, obviously correct CPU implementation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the GPU library (kivi.h / libkivi.so); the
+ * product path never calls it.
+ *
+ * What it computes (sources are the VeloxQuant-MLX pages):
+ *   - KIVI blog post on the fused Metal kernels, section "What we're actually
+ *     optimizing": asymmetric min/max group quantization
+ *       zero = min(group), scale = (max - min) / (2^bits - 1),
+ *       q = round((x - zero) / scale), recon = q * scale + zero,
+ *     keys grouped per channel along the token axis, values per token along
+ *     the channel axis.
+ *   - same post, section "The layout problem that shapes everything":
+ *     tensors are [BH, S, D] row-major, element (bh, s, d) at bh*S*D + s*D + d.
+ *   - same post, section "Three ways to be off by one bit": the dequant is a
+ *     multiply then an add (two roundings, no FMA), rounding is half-to-even,
+ *     and a ragged last group is padded by replicating the edge element.
+ *   - VeloxQuant-MLX 0.8.0 release post, section "What KIVI is": codes are
+ *     unsigned integers in [0, 2^bits - 1].
+ *   - TurboQuant Metal kernels post, section "Kernel 1: Bit-Packing", and the
+ *     TurboQuant port overview, section "The Bit-Packing Problem": 8/bits
+ *     codes per byte, element i of a byte at bit offset i*bits (LSB first).
+ *
+ * Arithmetic: every step is one IEEE-754 binary32 operation rounded to nearest
+ * even (the pages' kernels widen each element to float and keep min/max in
+ * float).  The file must be compiled with floating-point contraction off.
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - a group whose computed scale is 0 gets code 0 and reconstructs to zero;
+ *   - a min or max equal to zero is stored as +0 (signed-zero canonical form);
+ *   - codes are packed along D, one layout for keys and values,
+ *     [BH, S, D*bits/8] bytes; scale and zero are fp32, planar,
+ *     keys [BH, ceil(S/G), D], values [BH, S, ceil(D/G)].
+ *
+ * dtype: 0 = IEEE binary16 (fp16), 1 = bfloat16.  Tensors are passed as raw
+ * 16-bit patterns.
+ */
+#ifndef KIVI_ORACLE_H
+#define KIVI_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status: 0 ok, 1 bad argument */
+
+/* Exact widening and round-to-nearest-even narrowing of the 16-bit types. */
+float    kivi_ref_half_to_float(uint16_t h);
+uint16_t kivi_ref_float_to_half(float f);
+float    kivi_ref_bf16_to_float(uint16_t h);
+uint16_t kivi_ref_float_to_bf16(float f);
+
+/* Array forms of the four conversions above (dtype 0 fp16, 1 bf16). */
+int kivi_ref_widen_array(const uint16_t* in, int64_t n, int dtype, float* out);
+int kivi_ref_narrow_array(const float* in, int64_t n, int dtype, uint16_t* out);
+
+/* One group: n fp32 values -> (scale, zero). */
+int   kivi_ref_group_params(const float* vals, int64_t n, int bits,
+                            float* scale, float* zero);
+/* One element -> its code, given its group's (scale, zero). */
+int   kivi_ref_code(float f, float scale, float zero, int bits);
+/* One code -> fp32 reconstruction (multiply, then add). */
+float kivi_ref_recon(int code, float scale, float zero);
+
+/* Unpacked codes (one per byte, [BH,S,D]) plus planar params. */
+int kivi_ref_quant_keys_unpacked(const uint16_t* x, int dtype, int64_t BH,
+                                 int64_t S, int64_t D, int bits, int64_t group,
+                                 uint8_t* codes, float* scale, float* zero);
+int kivi_ref_quant_values_unpacked(const uint16_t* x, int dtype, int64_t BH,
+                                   int64_t S, int64_t D, int bits,
+                                   int64_t group, uint8_t* codes, float* scale,
+                                   float* zero);
+
+/* Bit packing of [rows, D] codes into [rows, D*bits/8] bytes and back. */
+int kivi_ref_pack(const uint8_t* codes, int64_t rows, int64_t D, int bits,
+                  uint8_t* packed);
+int kivi_ref_unpack(const uint8_t* packed, int64_t rows, int64_t D, int bits,
+                    uint8_t* codes);
+
+/* Full quantize: packed codes [BH,S,D*bits/8] plus params. */
+int kivi_ref_quant_keys(const uint16_t* x, int dtype, int64_t BH, int64_t S,
+                        int64_t D, int bits, int64_t group, uint8_t* packed,
+                        float* scale, float* zero);
+int kivi_ref_quant_values(const uint16_t* x, int dtype, int64_t BH, int64_t S,
+                          int64_t D, int bits, int64_t group, uint8_t* packed,
+                          float* scale, float* zero);
+
+/* Dequantize packed codes + params into out_dtype 16-bit patterns [BH,S,D]. */
+int kivi_ref_dequant_keys(const uint8_t* packed, const float* scale,
+                          const float* zero, int64_t BH, int64_t S, int64_t D,
+                          int bits, int64_t group, int out_dtype,
+                          uint16_t* out);
+int kivi_ref_dequant_values(const uint8_t* packed, const float* scale,
+                            const float* zero, int64_t BH, int64_t S,
+                            int64_t D, int bits, int64_t group, int out_dtype,
+                            uint16_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,488 @@
+"""Pins that tie the KIVI oracle to something other than itself.
+
+Each `pin_*` function takes an oracle object (oracle.Oracle) and raises
+AssertionError when the oracle disagrees with what the VeloxQuant-MLX pages
+or the mathematics fix:
+
+  - hand-worked groups and packing bytes (tests/golden/worked_examples.json,
+    each case with its citation and derivation);
+  - exhaustive / boundary checks of the 16-bit conversions against numpy
+    (fp16) and torch on the CPU (bf16);
+  - exact rational arithmetic: the fp32 division is a correctly rounded
+    quotient (not a reciprocal product), the code is the nearest grid point;
+  - invariants: code range, min -> code 0, max -> top code, reconstruction
+    error within scale/2, constant groups, grid-exact round trips,
+    determinism;
+  - equivalences: a ragged group equals the pages' edge-replicate padding;
+    per-channel keys equal per-token values of the transposed tensor;
+  - the pages' statistic: 2-bit reconstruction cosine about 0.93 on
+    unit-norm Gaussian keys (KIVI release post, "Honest limitations"; PyPI
+    page, KIVI section), 4-bit above 0.995 (PyPI page, ZipCache section).
+
+tests/test_oracle_pins.py runs them on the real oracle;
+tests/test_oracle_mutants.py runs them on broken copies and requires each
+copy to fail at least one.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from exact import F, bits32, from_bits32, rn32, round_half_even
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FP16, BF16 = 0, 1
+
+
+def golden():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        return json.load(f)
+
+
+def _expect_f32(case, key):
+    if key + "_bits" in case:
+        return from_bits32(int(case[key + "_bits"], 16))
+    return np.float32(case[key])
+
+
+def _f16_bits(vals):
+    return np.asarray(vals, np.float32).astype(np.float16).view(np.uint16)
+
+
+# --------------------------------------------------------------------------
+# 16-bit conversions
+# --------------------------------------------------------------------------
+
+def pin_fp16_widen_exhaustive(o):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.widen(h, FP16)
+    ref = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _narrow_probe_set(rng, widen_of_all):
+    """fp32 values around every representable 16-bit value: the values, the
+    midpoints between neighbours and one fp32 ulp either side of each."""
+    finite = widen_of_all[np.isfinite(widen_of_all)].astype(np.float64)
+    finite = np.unique(finite)
+    mids = (finite[:-1] + finite[1:]) / 2.0
+    pts = np.concatenate([finite, mids]).astype(np.float32)
+    pts = pts[np.isfinite(pts)]
+    up = np.nextafter(pts, np.float32(np.inf))
+    dn = np.nextafter(pts, np.float32(-np.inf))
+    rnd = rng.integers(0, 2**32, size=400_000, dtype=np.uint64)
+    rnd = rnd.astype(np.uint32).view(np.float32)
+    rnd = rnd[~np.isnan(rnd)]
+    return np.concatenate([pts, up, dn, rnd,
+                           np.array([np.inf, -np.inf, 65504, 65519.996,
+                                     65520, -65520, 1e-8, 2.0**-25,
+                                     2.0**-24, 3 * 2.0**-26], np.float32)])
+
+
+def pin_fp16_narrow_rne(o):
+    rng = np.random.default_rng(11)
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    probes = _narrow_probe_set(rng, h.view(np.float16).astype(np.float32))
+    got = o.narrow(probes, FP16)
+    with np.errstate(over="ignore"):
+        ref = probes.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), int(np.sum(got != ref))
+
+
+def pin_bf16_widen_narrow(o):
+    import torch
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.widen(h, BF16)
+    ref = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).float()
+    ref = ref.numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    rng = np.random.default_rng(12)
+    probes = _narrow_probe_set(rng, ref)
+    probes = probes[np.abs(probes) < 3.0e38]
+    got = o.narrow(probes, BF16)
+    refn = torch.from_numpy(probes).to(torch.bfloat16).view(torch.int16)
+    refn = refn.numpy().view(np.uint16)
+    assert np.array_equal(got, refn), int(np.sum(got != refn))
+
+
+# --------------------------------------------------------------------------
+# Worked examples from the golden file
+# --------------------------------------------------------------------------
+
+def pin_worked_groups(o):
+    for case in golden()["groups"]:
+        vals = np.asarray(case["values"], np.float32)
+        bits = case["bits"]
+        sc, z = o.group_params(vals, bits)
+        name = case["name"]
+        assert bits32(z) == bits32(_expect_f32(case, "zero")), name
+        assert bits32(sc) == bits32(_expect_f32(case, "scale")), name
+        codes = [o.code(v, sc, z, bits) for v in vals]
+        assert codes == case["codes"], (name, codes)
+        if "recon" in case:
+            rec = [float(o.recon(c, sc, z)) for c in codes]
+            assert rec == case["recon"], (name, rec)
+        # the same group through the tensor path, as one value row
+        x = _f16_bits(vals)[None, None, :]
+        if np.array_equal(x.view(np.float16).astype(np.float32)[0, 0], vals) \
+                and (vals.size * bits) % 8 == 0:
+            c2, s2, z2 = o.quant_values_unpacked(x, FP16, bits, vals.size)
+            assert c2[0, 0].tolist() == case["codes"], name
+            assert bits32(s2[0, 0, 0]) == bits32(sc), name
+
+
+def pin_recon_two_roundings(o):
+    c = golden()["recon_two_roundings"]
+    sc = from_bits32(int(c["scale_bits"], 16))
+    z = np.float32(c["zero"])
+    r = o.recon(c["code"], sc, z)
+    assert bits32(r) == int(c["recon_f32_bits"], 16)
+    # through dequant to fp16: one value row of 4 codes (2-bit), code 3 first
+    packed = np.array([[[0x03]]], np.uint8)
+    out = o.dequant_values(packed, np.array([[[sc]]], np.float32),
+                           np.array([[[z]]], np.float32), (1, 1, 4), 2, 4,
+                           FP16)
+    assert int(out[0, 0, 0]) == int(c["recon_fp16_bits"], 16)
+    assert int(out[0, 0, 0]) != int(c["fma_recon_fp16_bits"], 16)
+    out_k = o.dequant_keys(packed, np.full((1, 1, 4), sc, np.float32),
+                           np.full((1, 1, 4), z, np.float32), (1, 1, 4), 2, 1,
+                           FP16)
+    assert int(out_k[0, 0, 0]) == int(c["recon_fp16_bits"], 16)
+
+
+def pin_packing_golden(o):
+    for case in golden()["packing"]["cases"]:
+        bits = case["bits"]
+        codes = np.asarray(case["codes"], np.uint8)[None, :]
+        want = [int(b, 16) for b in case["bytes"]]
+        got = o.pack(codes, bits)[0].tolist()
+        assert got == want, (case, got)
+        back = o.unpack(np.asarray(want, np.uint8)[None, :], codes.shape[1],
+                        bits)
+        assert np.array_equal(back, codes), case
+
+
+def pin_pack_roundtrip_lsb_first(o):
+    rng = np.random.default_rng(3)
+    for bits in (1, 2, 4, 8):
+        D = 64
+        codes = rng.integers(0, 2**bits, size=(5, 7, D), dtype=np.uint8)
+        packed = o.pack(codes, bits)
+        assert packed.shape == (5, 7, D * bits // 8)
+        assert np.array_equal(o.unpack(packed, D, bits), codes)
+        # the rule itself: code i of byte j sits at bits [i*bits, (i+1)*bits)
+        per = 8 // bits
+        for i in range(per):
+            field = (packed.astype(np.uint32) >> (i * bits)) & ((1 << bits) - 1)
+            assert np.array_equal(field, codes[..., i::per])
+
+
+# --------------------------------------------------------------------------
+# Exact arithmetic
+# --------------------------------------------------------------------------
+
+def pin_clip(o):
+    """The chain's clip step (KIVI Metal-kernel post, 'What we're actually
+    optimizing'): an element outside [zero, zero + (2^b - 1) * scale] is
+    clipped to the end codes.  Inside a group it never binds, so it is
+    pinned through the element call."""
+    for bits in (1, 2, 4, 8):
+        top = 2**bits - 1
+        assert o.code(top + 5.0, 1.0, 0.0, bits) == top
+        assert o.code(top + 0.75, 1.0, 0.0, bits) == top
+        assert o.code(-3.0, 1.0, 0.0, bits) == 0
+        assert o.code(-0.75, 0.5, 0.0, bits) == 0
+        assert o.code(top * 0.5, 0.5, 0.0, bits) == top
+
+
+def pin_params_exact(o):
+    """zero = min exactly; scale = RN32(RN32(max - min) / (2^b - 1))."""
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        n = int(rng.integers(1, 70))
+        bits = int(rng.choice([1, 2, 4, 8]))
+        v = (rng.standard_normal(n) * 10.0 ** rng.uniform(-3, 3))
+        v = v.astype(np.float16).astype(np.float32)
+        sc, z = o.group_params(v, bits)
+        mn, mx = v.min(), v.max()
+        want_z = np.float32(0.0) if mn == 0 else mn
+        assert bits32(z) == bits32(want_z)
+        rng_ = rn32(F(mx) - F(mn if mn != 0 else 0.0))
+        want_s = rn32(F(rng_) / (2**bits - 1))
+        assert bits32(sc) == bits32(want_s), (v, bits)
+
+
+def pin_divide_not_reciprocal(o):
+    """Cases where a*RN(1/scale) would round to another code than RN(a/scale):
+    the oracle must give the correctly rounded quotient's code."""
+    rng = np.random.default_rng(17)
+    found = 0
+    for _ in range(200_000):
+        s = np.float32(rng.uniform(0.01, 100.0))
+        y = rn32(Fraction(1) / F(s))
+        k = int(rng.integers(0, 3))
+        a = np.float32((k + 0.5) * float(s))
+        for a_try in (a, np.nextafter(a, np.float32(0)),
+                      np.nextafter(a, np.float32(np.inf))):
+            t_div = rn32(F(a_try) / F(s))
+            t_rcp = rn32(F(a_try) * F(y))
+            c_div = round_half_even(F(t_div))
+            if round_half_even(F(t_rcp)) != c_div:
+                assert o.code(a_try, s, 0.0, 2) == min(max(c_div, 0), 3)
+                found += 1
+        if found >= 20:
+            break
+    assert found >= 20
+
+
+def pin_nearest_code_bruteforce(o):
+    """Brute force over every code: the chosen code is the grid point nearest
+    to x (exact rationals), except within a relative 2^-20 of a midpoint,
+    where either neighbour is acceptable."""
+    rng = np.random.default_rng(23)
+    for trial in range(400):
+        bits = int(rng.choice([1, 2, 4, 8]))
+        n = int(rng.integers(2, 40))
+        v = rng.standard_normal(n) * 10.0 ** rng.uniform(-2, 2)
+        v = v.astype(np.float16).astype(np.float32)
+        sc, z = o.group_params(v, bits)
+        if sc == 0:
+            continue
+        for x in v:
+            c = o.code(x, sc, z, bits)
+            dists = [abs(F(x) - F(z) - j * F(sc)) for j in range(2**bits)]
+            best = min(dists)
+            second = sorted(dists)[1]
+            if second - best > Fraction(1, 2**20) * (abs(F(x) - F(z)) + F(sc)):
+                assert dists[c] == best, (x, c, dists.index(best))
+            else:
+                assert dists[c] in (best, second)
+
+
+# --------------------------------------------------------------------------
+# Invariants on tensors
+# --------------------------------------------------------------------------
+
+def _rand_tensor(rng, BH, S, D, dtype, outliers=True):
+    x = rng.standard_normal((BH, S, D)).astype(np.float32)
+    if outliers:
+        ch = rng.choice(D, size=max(1, D // 32), replace=False)
+        x[:, :, ch] *= 20.0
+    if dtype == FP16:
+        return x.astype(np.float16).view(np.uint16)
+    u = x.view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _out_ulp(vals, dtype):
+    a = np.abs(vals).astype(np.float64)
+    if dtype == FP16:
+        e = np.floor(np.log2(np.maximum(a, 2.0**-14)))
+        return 2.0 ** (e - 10)
+    e = np.floor(np.log2(np.maximum(a, 2.0**-126)))
+    return 2.0 ** (e - 7)
+
+
+def _check_quant_invariants(o, x, dtype, bits, gk, gv):
+    BH, S, D = x.shape
+    f = o.widen(x, dtype).astype(np.float64)
+    maxc = 2**bits - 1
+    for kind in ("keys", "values"):
+        if kind == "keys":
+            codes, sc, z = o.quant_keys_unpacked(x, dtype, bits, gk)
+            gidx = np.arange(S) // gk
+            scx = sc[:, gidx, :].astype(np.float64)
+            zx = z[:, gidx, :].astype(np.float64)
+            packed, sc2, z2 = o.quant_keys(x, dtype, bits, gk)
+            rec = o.dequant_keys(packed, sc2, z2, x.shape, bits, gk, dtype)
+        else:
+            codes, sc, z = o.quant_values_unpacked(x, dtype, bits, gv)
+            gidx = np.arange(D) // gv
+            scx = sc[:, :, gidx].astype(np.float64)
+            zx = z[:, :, gidx].astype(np.float64)
+            packed, sc2, z2 = o.quant_values(x, dtype, bits, gv)
+            rec = o.dequant_values(packed, sc2, z2, x.shape, bits, gv, dtype)
+        assert np.array_equal(sc, sc2) and np.array_equal(z, z2)
+        assert np.array_equal(o.unpack(packed, D, bits), codes)
+        assert codes.max() <= maxc
+        # zero is the group min; every element is >= zero
+        assert np.all(f >= zx)
+        # reconstruction within half a step plus rounding slack
+        r = o.widen(rec, dtype).astype(np.float64)
+        slack = (np.abs(f) + np.abs(zx) + maxc * scx) * 2.0**-22 \
+            + _out_ulp(r, dtype)
+        err = np.abs(r - f)
+        assert np.all(err <= scx / 2 + slack), float((err - scx / 2).max())
+        # group min -> code 0, group max -> top code (when the range > 0)
+        if kind == "keys":
+            for bh in range(BH):
+                for g in range(sc.shape[1]):
+                    blk = f[bh, g * gk:(g + 1) * gk, :]
+                    cb = codes[bh, g * gk:(g + 1) * gk, :]
+                    am = blk.argmin(0)
+                    ax = blk.argmax(0)
+                    d = np.arange(D)
+                    assert np.all(cb[am, d] == 0)
+                    pos = sc[bh, g] > 0
+                    assert np.all(cb[ax, d][pos] == maxc)
+        else:
+            for j in range(sc.shape[2]):
+                blk = f[:, :, j * gv:(j + 1) * gv]
+                cb = codes[:, :, j * gv:(j + 1) * gv]
+                am = blk.argmin(2)[..., None]
+                ax = blk.argmax(2)[..., None]
+                assert np.all(np.take_along_axis(cb, am, 2) == 0)
+                pos = sc[:, :, j] > 0
+                assert np.all(np.take_along_axis(cb, ax, 2)[..., 0][pos]
+                              == maxc)
+
+
+def pin_tensor_invariants(o):
+    rng = np.random.default_rng(29)
+    for (BH, S, D, dtype, bits, gk, gv) in [
+            (2, 64, 64, FP16, 2, 32, 32),
+            (3, 70, 48, FP16, 2, 32, 32),     # ragged S and D groups
+            (2, 40, 128, BF16, 4, 32, 128),
+            (2, 33, 16, FP16, 1, 16, 8),
+            (1, 50, 24, BF16, 8, 7, 5),
+            (2, 96, 64, FP16, 4, 64, 64)]:
+        x = _rand_tensor(rng, BH, S, D, dtype)
+        _check_quant_invariants(o, x, dtype, bits, gk, gv)
+
+
+def pin_constant_groups(o):
+    rng = np.random.default_rng(31)
+    for dtype in (FP16, BF16):
+        x = _rand_tensor(rng, 2, 64, 64, dtype)
+        cval = _f16_bits([0.75])[0] if dtype == FP16 else np.uint16(0x3F40)
+        x[1, 32:64, 5] = cval             # constant key group
+        x[0, 10, 32:64] = cval            # constant value group
+        for kind in ("keys", "values"):
+            if kind == "keys":
+                packed, sc, z = o.quant_keys(x, dtype, 2, 32)
+                codes = o.unpack(packed, 64, 2)
+                assert sc[1, 1, 5] == 0
+                assert bits32(z[1, 1, 5]) == bits32(np.float32(0.75))
+                assert np.all(codes[1, 32:64, 5] == 0)
+                rec = o.dequant_keys(packed, sc, z, x.shape, 2, 32, dtype)
+                assert np.all(rec[1, 32:64, 5] == cval)
+            else:
+                packed, sc, z = o.quant_values(x, dtype, 2, 32)
+                codes = o.unpack(packed, 64, 2)
+                assert sc[0, 10, 1] == 0
+                assert bits32(z[0, 10, 1]) == bits32(np.float32(0.75))
+                assert np.all(codes[0, 10, 32:64] == 0)
+                rec = o.dequant_values(packed, sc, z, x.shape, 2, 32, dtype)
+                assert np.all(rec[0, 10, 32:64] == cval)
+
+
+def pin_ragged_equals_edge_padding(o):
+    """KIVI Metal-kernel post, 'Three ways to be off by one bit', item 3: a
+    ragged last group behaves as if padded with copies of its edge element."""
+    rng = np.random.default_rng(37)
+    for dtype in (FP16, BF16):
+        x = _rand_tensor(rng, 2, 70, 48, dtype)      # S=70: last key group 6
+        G = 32
+        xp = np.concatenate([x, np.repeat(x[:, -1:, :], 96 - 70, axis=1)], 1)
+        c1, s1, z1 = o.quant_keys_unpacked(x, dtype, 2, G)
+        c2, s2, z2 = o.quant_keys_unpacked(xp, dtype, 2, G)
+        assert np.array_equal(s1, s2) and np.array_equal(z1, z2)
+        assert np.array_equal(c1, c2[:, :70, :])
+        # D=48 with G=32: last value group has 16 channels
+        xv = np.concatenate([x, np.repeat(x[:, :, -1:], 64 - 48, axis=2)], 2)
+        c1, s1, z1 = o.quant_values_unpacked(x, dtype, 2, G)
+        c2, s2, z2 = o.quant_values_unpacked(xv, dtype, 2, G)
+        assert np.array_equal(s1, s2) and np.array_equal(z1, z2)
+        assert np.array_equal(c1, c2[:, :, :48])
+
+
+def pin_keys_equal_values_of_transpose(o):
+    """Per-channel keys grouped over tokens are per-token values of the
+    transposed tensor grouped over channels (KIVI Metal-kernel post, 'The
+    layout problem that shapes everything')."""
+    rng = np.random.default_rng(41)
+    x = _rand_tensor(rng, 3, 64, 40, FP16)
+    xt = np.ascontiguousarray(x.transpose(0, 2, 1))
+    for G in (32, 8, 5):
+        ck, sk, zk = o.quant_keys_unpacked(x, FP16, 2, G)
+        cv, sv, zv = o.quant_values_unpacked(xt, FP16, 2, G)
+        assert np.array_equal(ck, cv.transpose(0, 2, 1))
+        assert np.array_equal(sk, sv.transpose(0, 2, 1))
+        assert np.array_equal(zk, zv.transpose(0, 2, 1))
+
+
+def pin_grid_exact_roundtrip(o):
+    """Elements already on a group's grid reconstruct bit-exactly."""
+    rng = np.random.default_rng(43)
+    for bits in (1, 2, 4):
+        maxc = 2**bits - 1
+        z0 = np.float32(-2.0)
+        step = np.float32(0.125)
+        codes = rng.integers(0, maxc + 1, size=(2, 32, 64))
+        codes[:, 0, :] = 0
+        codes[:, 1, :] = maxc           # every key group spans the full range
+        f = (z0 + codes.astype(np.float32) * step).astype(np.float32)
+        x = f.astype(np.float16).view(np.uint16)
+        packed, sc, z = o.quant_keys(x, FP16, bits, 32)
+        assert np.all(sc == step) and np.all(z == z0)
+        assert np.array_equal(o.unpack(packed, 64, bits), codes)
+        rec = o.dequant_keys(packed, sc, z, x.shape, bits, 32, FP16)
+        assert np.array_equal(rec, x)
+
+
+def pin_determinism(o):
+    rng = np.random.default_rng(47)
+    x = _rand_tensor(rng, 2, 64, 64, BF16)
+    a = o.quant_keys(x, BF16, 2, 32)
+    b = o.quant_keys(x, BF16, 2, 32)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+
+
+def pin_invalid_args(o):
+    x = np.zeros((1, 4, 6), np.uint16)
+    for bits, G in ((3, 2), (2, 0)):
+        try:
+            o.quant_keys(x, FP16, bits, G)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("accepted bits=%d group=%d" % (bits, G))
+    try:   # D*bits not a multiple of 8
+        o.quant_values(np.zeros((1, 4, 6), np.uint16), FP16, 1, 2)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("accepted D*bits % 8 != 0")
+
+
+# --------------------------------------------------------------------------
+# The pages' statistic
+# --------------------------------------------------------------------------
+
+def _cosine_unit_norm_keys(o, bits, n_tok=4096, D=128, seed=53):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n_tok, D))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    x = k.astype(np.float16).view(np.uint16)[None]
+    packed, sc, z = o.quant_keys(x, FP16, bits, 32)
+    rec = o.dequant_keys(packed, sc, z, x.shape, bits, 32, FP16)
+    r = rec[0].view(np.float16).astype(np.float64)
+    xf = x[0].view(np.float16).astype(np.float64)
+    cos = (r * xf).sum(1) / (np.linalg.norm(r, axis=1)
+                             * np.linalg.norm(xf, axis=1))
+    return float(cos.mean())
+
+
+def pin_cosine_statistics(o):
+    c2 = _cosine_unit_norm_keys(o, 2)
+    assert 0.92 <= c2 <= 0.94, c2        # pages: "around 0.93"
+    c4 = _cosine_unit_norm_keys(o, 4)
+    assert c4 > 0.995, c4                # pages: 4-bit "> 0.995"
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

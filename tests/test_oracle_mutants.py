@@ -1,0 +1,97 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each mutant is a copy of oracle/kivi_oracle.c with one plausible mistake
+(a dropped term, a wrong sign or index, a transposed operand, the wrong
+rounding), built with the same flags into a temporary directory.  The test
+requires at least one pin in tests/oracle_pins.py to fail on every mutant,
+which shows the pins constrain each part of the oracle.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle.build import CMD, LIB, SRC
+from oracle_pins import ALL_PINS
+
+MUTANTS = [
+    ("range_sign", "float range = mx - mn;", "float range = mx + mn;"),
+    ("zero_is_max", "*zero = mn;", "*zero = mx;"),
+    ("levels_off_by_one", "float levels = (float)((1 << bits) - 1);",
+     "float levels = (float)(1 << bits);"),
+    ("round_half_away", "float r = rintf(t);", "float r = roundf(t);"),
+    ("truncate", "float r = rintf(t);", "float r = truncf(t);"),
+    ("reciprocal_multiply", "float t = a / scale;",
+     "float t = a * (1.0f / scale);"),
+    ("fused_recon", "float p = (float)code * scale;\n    float r = p + zero;",
+     "float r = fmaf((float)code, scale, zero);"),
+    ("no_clip_top", "r = fminf(r, maxc);", "(void)maxc;"),
+    ("no_signed_zero_canon", "if (mn == 0.0f) mn = 0.0f;", ""),
+    ("pack_msb_first", "byte |= c << (i * bits);",
+     "byte |= c << ((per - 1 - i) * bits);"),
+    ("unpack_msb_first",
+     "codes[r * D + d] = (uint8_t)((byte >> ((d % per) * bits)) & mask);",
+     "codes[r * D + d] = (uint8_t)((byte >> ((per - 1 - d % per) * bits)) "
+     "& mask);"),
+    ("key_param_transposed",
+     "scale[(bh * NG + g) * D + d] = sc;\n                zero[(bh * NG + g) * D + d] = z;",
+     "scale[(bh * D + d) * NG + g] = sc;\n                zero[(bh * D + d) * NG + g] = z;"),
+    ("key_group_bound_short", "int64_t s1 = s0 + group < S ? s0 + group : S;",
+     "int64_t s1 = s0 + group - 1 < S ? s0 + group - 1 : S;"),
+    ("value_group_bound_short",
+     "int64_t d1 = d0 + group < D ? d0 + group : D;",
+     "int64_t d1 = d0 + group - 1 < D ? d0 + group - 1 : D;"),
+    ("dequant_key_group_index", "int64_t p = (bh * NG + s / group) * D + d;",
+     "int64_t p = (bh * NG + s % NG) * D + d;"),
+    ("dequant_value_group_index", "int64_t p = (bh * S + s) * NGD + d / group;",
+     "int64_t p = (bh * S + s) * NGD + d % NGD;"),
+    ("f16_round_half_up",
+     "if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u;",
+     "if (rem >= 0x1000u) h += 1u;"),
+    ("f16_truncate_subnormal",
+     "if (rem > half || (rem == half && (q & 1u))) q += 1u;", ""),
+    ("f16_overflow_threshold", "if (a >= 0x477ff000u)", "if (a >= 0x477fe000u)"),
+    ("bf16_round_half_up", "uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);",
+     "uint32_t r = u + 0x8000u;"),
+    ("f16_subnormal_scale", "v = ldexpf((float)m, -24);",
+     "v = ldexpf((float)m, -25);"),
+    ("subtract_dropped", "float a = f - zero;", "float a = f;"),
+]
+
+
+def _build_mutant(tmp, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation {name}: anchor not unique"
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    # the header sits next to the real source
+    lib = os.path.join(tmp, f"lib{name}.so")
+    cmd = list(CMD)
+    cmd[cmd.index(LIB)] = lib
+    cmd[cmd.index(SRC)] = path
+    cmd.insert(1, "-I" + os.path.dirname(SRC))
+    subprocess.run(cmd, check=True, capture_output=True)
+    return lib
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mut():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmpdir_mut, name, old, new):
+    lib = _build_mutant(tmpdir_mut, name, old, new)
+    o = oracle.Oracle(lib)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(o)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin catches mutant {name}"

@@ -1,0 +1,149 @@
+"""Seeded synthetic KV-cache inputs for the KIVI flush.
+
+Holds none of the quantizer's arithmetic: it only draws keys and values with
+the shapes and value distributions of the workloads the VeloxQuant-MLX pages
+measure (KIVI blog post on the fused Metal kernels: flushes of 32 decode
+tokens and 2048-token prefill chunks over 28 layers x 8 KV heads x 128;
+release post for KIVI 0.8.0: Llama-3.2-3B, Qwen2.5-7B, Mistral-7B KV
+geometry; keys carry a few channels of consistently large magnitude, values
+are flatter).  Both the GPU path and the oracle are fed from here.
+
+Every tensor is drawn one (bh) slice at a time from numpy's PCG64 seeded with
+(config seed, tensor id, bh, pool index), so any slice can be regenerated on
+its own; fp16 casts use numpy (round to nearest even), bf16 casts use torch
+on the CPU (round to nearest even).  Tensors are returned as uint16 bit
+patterns [BH, S, D].
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+FP16 = 0
+BF16 = 1
+
+_TENSOR_ID = {"K": 1, "V": 2}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    BH: int
+    S: int
+    D: int
+    dtype: int        # FP16 or BF16
+    bits: int
+    group_k: int      # tokens per key group (per-channel quantization)
+    group_v: int      # channels per value group (per-token quantization)
+    seed: int
+    key_kind: str     # recipe for K
+    value_kind: str   # recipe for V
+    desc: str
+
+    @property
+    def elems(self):
+        return self.BH * self.S * self.D
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("tiny", 4, 64, 64, FP16, 2, 32, 32, 1, "tiny", "tiny",
+                 "tiny 2-bit flush, K/V fp16 [4,64,64], one constant group "
+                 "per tensor"),
+        Workload("decode", 224, 32, 128, FP16, 2, 32, 32, 2, "outlier15",
+                 "normal",
+                 "decode-time flush, 28 layers x 8 KV heads, 32 residual "
+                 "tokens, D=128, fp16, 2-bit"),
+        Workload("prefill", 112, 32768, 128, FP16, 2, 32, 32, 3, "prefill",
+                 "normal05",
+                 "prefill quantize, 28 layers x 4 KV heads, S=32768, D=128, "
+                 "fp16, 2-bit"),
+        Workload("serve", 128, 8192, 128, BF16, 4, 32, 128, 4, "prefill",
+                 "student_t4",
+                 "batched serving flush, 16 x 8 KV heads, S=8192, D=128, "
+                 "bf16, 4-bit, value group = whole head"),
+        Workload("roundtrip", 256, 4096, 128, FP16, 2, 32, 32, 5, "outlier15",
+                 "normal",
+                 "quantize + dequantize round trip, 32 x 8 KV heads, S=4096, "
+                 "D=128, fp16, 2-bit"),
+    ]
+}
+
+
+def _rng(w, tensor, bh, pool):
+    return np.random.default_rng([w.seed, _TENSOR_ID[tensor], bh, pool])
+
+
+def _to_bits(f32, dtype):
+    if dtype == FP16:
+        return f32.astype(np.float16).view(np.uint16)
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _tiny_key_channels(w, pool):
+    r = np.random.default_rng([w.seed, 99, pool])
+    return r.choice(w.D, size=4, replace=False)
+
+
+def slice_f32(w, tensor, bh, pool=0):
+    """fp32 draw of one [S, D] slice before the cast to the tensor dtype."""
+    r = _rng(w, tensor, bh, pool)
+    S, D = w.S, w.D
+    kind = w.key_kind if tensor == "K" else w.value_kind
+    if kind == "tiny":
+        x = r.standard_normal((S, D), dtype=np.float32)
+        if tensor == "K":
+            x[:, _tiny_key_channels(w, pool)] *= np.float32(20.0)
+            if bh == 1:   # one constant key group: channel 5, tokens 32..63
+                x[32:64, 5] = np.float32(0.75)
+        elif bh == 2:     # one constant value group: token 10, channels 32..63
+            x[10, 32:64] = np.float32(-1.25)
+        return x
+    if kind == "normal":
+        return r.standard_normal((S, D), dtype=np.float32)
+    if kind == "normal05":
+        return r.standard_normal((S, D), dtype=np.float32) * np.float32(0.5)
+    if kind == "outlier15":
+        x = r.standard_normal((S, D), dtype=np.float32)
+        ch = r.choice(D, size=4, replace=False)
+        x[:, ch] *= np.float32(15.0)
+        return x
+    if kind == "prefill":
+        # ~3% of channels scaled by U(10, 30), every channel shifted by a
+        # per-channel mean offset U(-2, 2).
+        n_out = max(1, int(round(0.03 * D)))
+        ch = r.choice(D, size=n_out, replace=False)
+        f = np.ones(D, np.float32)
+        f[ch] = r.uniform(10.0, 30.0, size=n_out).astype(np.float32)
+        off = r.uniform(-2.0, 2.0, size=D).astype(np.float32)
+        z = r.standard_normal((S, D), dtype=np.float32)
+        return z * f[None, :] + off[None, :]
+    if kind == "student_t4":
+        return r.standard_t(4.0, size=(S, D)).astype(np.float32)
+    raise ValueError(kind)
+
+
+def gen_slice(w, tensor, bh, pool=0):
+    """uint16 bit patterns of one [S, D] slice."""
+    return _to_bits(slice_f32(w, tensor, bh, pool), w.dtype)
+
+
+def gen_tensor(w, tensor, bhs=None, pool=0):
+    """uint16 [len(bhs), S, D]; bhs defaults to every slice."""
+    if bhs is None:
+        bhs = range(w.BH)
+    bhs = list(bhs)
+    out = np.empty((len(bhs), w.S, w.D), np.uint16)
+    for i, bh in enumerate(bhs):
+        out[i] = gen_slice(w, tensor, bh, pool)
+    return out
+
+
+def sample_bhs(w, n, seed=0):
+    """A deterministic spread of n slice indices: first, last and random."""
+    if w.BH <= n:
+        return list(range(w.BH))
+    r = np.random.default_rng([w.seed, 7, seed])
+    mid = r.choice(np.arange(1, w.BH - 1), size=n - 2, replace=False)
+    return sorted({0, w.BH - 1, *mid.tolist()})
