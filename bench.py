@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""KIVI flush benchmark on one MI355X: effective HBM GB/s of the whole path.
+
+A step is one pass of every kernel of the path over one batch of synthetic
+KV: quantize keys (per channel) and values (per token), dequantize both, and
+the fused quantize->dequantize of both.  Default workload: the dequantize
+round trip, BH = 32 x 8 KV heads, S = 4096, D = 128, fp16, 2-bit, groups of
+32 tokens (keys) and 32 channels (values).
+
+value = algorithmic bytes of the step (each input read once, each output
+written once) / measured step time, with inputs resident in HBM; inputs
+rotate over a pool of distinct tensors larger than the 256 MB MALL so no
+step is served from cache.  Per-kernel durations come from HIP events
+recorded on the launch stream inside the timed region; the dominant kernel's
+achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
+baseline is the plain C oracle (single thread) timed on a bounded sample of
+the same workload.
+
+Prints ONE JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
+          "flush/dequant")
+KERNEL_SOURCES = ["kivi_device.h", "quant_keys.hip", "quant_values.hip",
+                  "dequant.hip"]
+
+
+def bytes_per_elem(op, bits, group, dtype_bytes=2):
+    """Algorithmic bytes per element: input once, every output once.
+    quant: x + codes + fp32 scale and zero per group."""
+    codes = bits / 8.0
+    params = 8.0 / group
+    if op == "quant":
+        return dtype_bytes + codes + params
+    if op == "dequant":
+        return codes + params + dtype_bytes
+    if op == "fused":
+        return dtype_bytes + codes + params + dtype_bytes
+    raise ValueError(op)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kv_cache_quantization_kivi_amd",
+                               "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters (committed in
+    profiles/), used only while the kernel sources are unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(f"{kernel}@{workload}")
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def make_steps(K, w, pool_inputs, torch):
+    """Pre-allocated outputs and the list of (name, op, bytes, launch fn)
+    that make one step.  Every launch goes to torch's current stream."""
+    E = w.elems
+    dev = pool_inputs[0][0].device
+    bits, gk, gv = w.bits, w.group_k, w.group_v
+    NG = (w.S + gk - 1) // gk
+    NGD = (w.D + gv - 1) // gv
+    shp = (w.BH, w.S, w.D)
+
+    def qbufs(keys):
+        c = torch.empty((w.BH, w.S, w.D * bits // 8), dtype=torch.uint8,
+                        device=dev)
+        p = (w.BH, NG, w.D) if keys else (w.BH, w.S, NGD)
+        return (c, torch.empty(p, dtype=torch.float32, device=dev),
+                torch.empty(p, dtype=torch.float32, device=dev))
+
+    qk, qv = qbufs(True), qbufs(False)
+    fk, fv = qbufs(True), qbufs(False)
+    dt = pool_inputs[0][0].dtype
+    dk = torch.empty(shp, dtype=dt, device=dev)
+    dv = torch.empty(shp, dtype=dt, device=dev)
+    rk = torch.empty(shp, dtype=dt, device=dev)
+    rv = torch.empty(shp, dtype=dt, device=dev)
+
+    steps = [
+        ("quant_keys", "quant", gk,
+         lambda kv: K.kivi_quant_keys(kv[0], bits, gk, *qk)),
+        ("quant_values", "quant", gv,
+         lambda kv: K.kivi_quant_values(kv[1], bits, gv, *qv)),
+    ]
+    if w.name in ("tiny", "decode", "roundtrip"):
+        steps += [
+            ("dequant_keys", "dequant", gk,
+             lambda kv: K.kivi_dequant_keys(*qk, bits, gk, out_dtype=dt,
+                                            out=dk)),
+            ("dequant_values", "dequant", gv,
+             lambda kv: K.kivi_dequant_values(*qv, bits, gv, out_dtype=dt,
+                                              out=dv)),
+            ("quant_dequant_keys", "fused", gk,
+             lambda kv: K.kivi_quant_dequant_keys(kv[0], bits, gk, True, rk,
+                                                  *fk)),
+            ("quant_dequant_values", "fused", gv,
+             lambda kv: K.kivi_quant_dequant_values(kv[1], bits, gv, True,
+                                                    rv, *fv)),
+        ]
+    out = []
+    for name, op, g, fn in steps:
+        out.append((name, op, bytes_per_elem(op, bits, g) * E, fn))
+    return out
+
+
+def cpu_baseline(w, n_bh, steps_desc):
+    """The oracle as it stands, single-threaded, on n_bh slices of the same
+    workload: every row of the step (the fused row is the oracle's quantize
+    followed by its dequantize)."""
+    import oracle
+    O = oracle.default()
+    bhs = list(range(n_bh))
+    k = W.gen_tensor(w, "K", bhs)
+    v = W.gen_tensor(w, "V", bhs)
+    E = k.size
+    byts = 0.0
+    t0 = time.perf_counter()
+    names = [s[0] for s in steps_desc]
+    ck = cv = None
+    for name in names:
+        if name == "quant_keys":
+            ck = O.quant_keys(k, w.dtype, w.bits, w.group_k)
+        elif name == "quant_values":
+            cv = O.quant_values(v, w.dtype, w.bits, w.group_v)
+        elif name == "dequant_keys":
+            O.dequant_keys(*ck, k.shape, w.bits, w.group_k, w.dtype)
+        elif name == "dequant_values":
+            O.dequant_values(*cv, v.shape, w.bits, w.group_v, w.dtype)
+        elif name == "quant_dequant_keys":
+            q = O.quant_keys(k, w.dtype, w.bits, w.group_k)
+            O.dequant_keys(*q, k.shape, w.bits, w.group_k, w.dtype)
+        elif name == "quant_dequant_values":
+            q = O.quant_values(v, w.dtype, w.bits, w.group_v)
+            O.dequant_values(*q, v.shape, w.bits, w.group_v, w.dtype)
+    dt = time.perf_counter() - t0
+    for name, op, b, _ in steps_desc:
+        byts += b / w.elems * E
+    return {
+        "value": round(byts / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{n_bh} of {w.BH} (bh) slices of the same workload "
+                   f"({E} elements per tensor), every row of the step, "
+                   f"{dt:.2f} s single-threaded"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="roundtrip",
+                    choices=sorted(W.WORKLOADS))
+    ap.add_argument("--pool", type=int, default=0,
+                    help="distinct input sets (0: enough to exceed 1 GB)")
+    ap.add_argument("--cpu-sample-bh", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus},"
+              f" WORLD_SIZE {world}); the KIVI flush needs no collectives and "
+              "this build runs on a single GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kv_cache_quantization_kivi_amd as K
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    tdt = torch.float16 if w.dtype == W.FP16 else torch.bfloat16
+
+    in_bytes = 2 * w.elems * 2
+    pool = args.pool or max(2, int(np.ceil(1.0e9 / in_bytes)))
+    pool = min(pool, 64)
+    inputs = []
+    for p in range(pool):
+        kv = []
+        for tensor in ("K", "V"):
+            x = W.gen_tensor(w, tensor, pool=p)
+            kv.append(torch.from_numpy(x.view(np.int16)).view(tdt).to(dev))
+        inputs.append(tuple(kv))
+
+    steps = make_steps(K, w, inputs, torch)
+    step_bytes = sum(s[2] for s in steps)
+    stream = torch.cuda.current_stream(dev)
+
+    for i in range(args.warmup):
+        for _, _, _, fn in steps:
+            fn(inputs[i % pool])
+    torch.cuda.synchronize()
+
+    n_k = len(steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k + 1)]
+           for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        e = evs[i]
+        kv = inputs[i % pool]
+        e[0].record(stream)
+        for j, (_, _, _, fn) in enumerate(steps):
+            fn(kv)
+            e[j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    per_kernel = {}
+    for j, (name, op, b, _) in enumerate(steps):
+        d = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+        avg = float(np.mean(d))
+        per_kernel[name] = {
+            "avg_us": round(avg * 1e3, 3),
+            "median_us": round(float(np.median(d)) * 1e3, 3),
+            "min_us": round(float(np.min(d)) * 1e3, 3),
+            "max_us": round(float(np.max(d)) * 1e3, 3),
+            "algorithmic_bytes": int(b),
+            "gbs": round(b / (avg * 1e-3) / 1e9, 1),
+        }
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"])
+    dk = per_kernel[dom]
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(dom, w.name, src_hash)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{w.name}: {w.desc}; K and V [BH={w.BH}, S={w.S}, "
+                         f"D={w.D}] {'fp16' if w.dtype == 0 else 'bf16'}, "
+                         f"bits={w.bits}, key group={w.group_k} tokens, "
+                         f"value group={w.group_v} channels; step = "
+                         + " + ".join(s[0] for s in steps)),
+            "step_algorithmic_bytes": int(step_bytes),
+            "input_pool": pool,
+            "wall_s": round(t_wall, 4),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": dom,
+            "bound": "hbm",
+            "achieved": dk["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+        "per_kernel": per_kernel,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        n_bh = min(args.cpu_sample_bh, w.BH)
+        result["cpu_baseline"] = cpu_baseline(w, n_bh, steps)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * kivi.h -- C ABI of libkivi.so, the KIVI KV-cache flush for MI355X (gfx950).
+ *
+ * The method (VeloxQuant-MLX pages; KIVI blog post on the fused Metal
+ * kernels, section "What we're actually optimizing", and the 0.8.0 release
+ * post, section "What KIVI is"): asymmetric min/max group quantization,
+ *     zero  = min(group)
+ *     scale = (max(group) - min(group)) / (2^bits - 1)
+ *     code  = clip(round_half_even((x - zero) / scale), 0, 2^bits - 1)
+ *     recon = code * scale + zero          (multiply rounded, then add)
+ * with keys grouped per channel over `group` consecutive tokens and values
+ * grouped per token over `group` consecutive channels.  Every step is one
+ * IEEE binary32 operation rounded to nearest even ("Three ways to be off by
+ * one bit": two roundings in the dequant, half-to-even rounding; a ragged
+ * last group behaves as if padded with its edge element, i.e. its min/max
+ * are over its real elements).  A group whose scale is 0 (constant group)
+ * gets code 0 and reconstructs to `zero`; a min or max equal to zero is
+ * stored as +0.
+ *
+ * Layouts (section "The layout problem that shapes everything"):
+ *   x, recon, out : [BH, S, D] row-major 16-bit floats, element (bh, s, d)
+ *                   at bh*S*D + s*D + d (batch and heads flattened into BH).
+ *   codes         : [BH, S, D*bits/8] bytes; along D, 8/bits codes per byte,
+ *                   code i of a byte in bits [i*bits, (i+1)*bits) (the
+ *                   TurboQuant Metal kernels post, section "Kernel 1:
+ *                   Bit-Packing").  One layout for keys and values.
+ *   key params    : scale, zero fp32 [BH, ceil(S/group), D] (planar).
+ *   value params  : scale, zero fp32 [BH, S, ceil(D/group)] (planar).
+ *
+ * Ownership and execution: every pointer is caller-owned device memory
+ * (e.g. allocated by PyTorch); the library never allocates, frees or
+ * synchronises and keeps no state between calls; calls are re-entrant.
+ * Work is enqueued on `stream` (0 = the null stream) and runs
+ * asynchronously; outputs are valid once the stream has reached the call.
+ * Inputs and outputs must not overlap.
+ *
+ * Errors: every argument is checked before anything is launched; on an
+ * error nothing is written and nothing is launched.  Rules:
+ *   bits in {1, 2, 4, 8}                                   else KIVI_ERR_BITS
+ *   group >= 1                                             else KIVI_ERR_GROUP
+ *   BH, S, D >= 0, D*bits % 8 == 0, BH*S*D*2 fits int64    else KIVI_ERR_SHAPE
+ *   dtype is KIVI_FP16 or KIVI_BF16                        else KIVI_ERR_DTYPE
+ *   every pointer that must be written or read is non-NULL else KIVI_ERR_NULL
+ *   every pointer is 16-byte aligned                       else KIVI_ERR_ALIGN
+ * An empty tensor (BH, S or D equal to 0) is valid and launches nothing.
+ * A failed launch returns KIVI_ERR_LAUNCH.  Results for NaN or infinite
+ * inputs, or for groups whose max - min overflows binary32, are unspecified.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KIVI_OK = 0,
+    KIVI_ERR_NULL = 1,
+    KIVI_ERR_SHAPE = 2,
+    KIVI_ERR_BITS = 3,
+    KIVI_ERR_GROUP = 4,
+    KIVI_ERR_DTYPE = 5,
+    KIVI_ERR_ALIGN = 6,
+    KIVI_ERR_LAUNCH = 7
+} kivi_status;
+
+typedef enum { KIVI_FP16 = 0, KIVI_BF16 = 1 } kivi_dtype;
+
+/*
+ * Quantize keys per channel (KIVI blog post on the fused Metal kernels,
+ * section "Kernel A -- per-channel keys"): for every (bh, token group g,
+ * channel d) the group is tokens [g*group, min(g*group + group, S)) of
+ * channel d, read along the strided S axis.
+ *   k      in : [BH, S, D] of dtype `dt`
+ *   codes out : [BH, S, D*bits/8] bytes
+ *   scale, zero out : fp32 [BH, ceil(S/group), D]
+ */
+kivi_status kivi_quant_keys(const void* k, kivi_dtype dt, int64_t BH,
+                            int64_t S, int64_t D, int bits, int64_t group,
+                            uint8_t* codes, float* scale, float* zero,
+                            hipStream_t stream);
+
+/*
+ * Quantize values per token (same post, section "Kernel B -- per-token
+ * values"): for every (bh, token s, channel group j) the group is channels
+ * [j*group, min(j*group + group, D)) of token s, along the contiguous D axis.
+ *   v      in : [BH, S, D] of dtype `dt`
+ *   codes out : [BH, S, D*bits/8] bytes
+ *   scale, zero out : fp32 [BH, S, ceil(D/group)]
+ */
+kivi_status kivi_quant_values(const void* v, kivi_dtype dt, int64_t BH,
+                              int64_t S, int64_t D, int bits, int64_t group,
+                              uint8_t* codes, float* scale, float* zero,
+                              hipStream_t stream);
+
+/*
+ * Dequantize keys (section "What we're actually optimizing", recon =
+ * code * scale + zero, and "Three ways to be off by one bit", item 1: the
+ * product is rounded before the add): codes and key params as produced by
+ * kivi_quant_keys with the same bits and group -> out [BH, S, D] of
+ * `out_dt`, each recon rounded to nearest even in that type.
+ */
+kivi_status kivi_dequant_keys(const uint8_t* codes, const float* scale,
+                              const float* zero, int64_t BH, int64_t S,
+                              int64_t D, int bits, int64_t group,
+                              kivi_dtype out_dt, void* out,
+                              hipStream_t stream);
+
+/* Dequantize values: as kivi_dequant_keys with value params
+ * [BH, S, ceil(D/group)]. */
+kivi_status kivi_dequant_values(const uint8_t* codes, const float* scale,
+                                const float* zero, int64_t BH, int64_t S,
+                                int64_t D, int bits, int64_t group,
+                                kivi_dtype out_dt, void* out,
+                                hipStream_t stream);
+
+/*
+ * Fused quantize -> dequantize of keys in one pass: the operation the
+ * pages' own Metal kernels perform (section "Three ways to be off by one
+ * bit", item 1, and "So why does the kernel ship?": the cache quantizes and
+ * immediately expands back to the input type).  Writes recon [BH, S, D] in
+ * dtype `dt`, bit-identical to kivi_quant_keys followed by
+ * kivi_dequant_keys.  codes, scale and zero are either all non-NULL (they
+ * are written as by kivi_quant_keys) or all NULL (recon only).
+ */
+kivi_status kivi_quant_dequant_keys(const void* k, kivi_dtype dt, int64_t BH,
+                                    int64_t S, int64_t D, int bits,
+                                    int64_t group, uint8_t* codes,
+                                    float* scale, float* zero, void* recon,
+                                    hipStream_t stream);
+
+/* Fused quantize -> dequantize of values; as kivi_quant_dequant_keys. */
+kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
+                                      int64_t BH, int64_t S, int64_t D,
+                                      int bits, int64_t group, uint8_t* codes,
+                                      float* scale, float* zero, void* recon,
+                                      hipStream_t stream);
+
+/* Sizes: bytes of packed codes, and element counts of each params array
+ * (scale and zero each), for a [BH, S, D] tensor.  Return -1 on invalid
+ * arguments (same rules as above). */
+int64_t kivi_codes_bytes(int64_t BH, int64_t S, int64_t D, int bits);
+int64_t kivi_key_param_count(int64_t BH, int64_t S, int64_t D,
+                             int64_t group);
+int64_t kivi_value_param_count(int64_t BH, int64_t S, int64_t D,
+                               int64_t group);
+
+/* A static, human-readable name for a status code. */
+const char* kivi_status_string(kivi_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

@@ -1,0 +1,267 @@
+"""KIVI KV-cache flush for MI355X: Python binding of libkivi.so.
+
+Argument marshalling only: every step of quantization and dequantization
+runs in the HIP kernels behind the C ABI declared in include/kivi.h.  Torch
+tensors supply device memory and the current HIP stream; outputs that are
+not passed in are allocated with torch on the input's device.  Importing
+this package fails loudly if the library has not been built (there is no
+fallback of any kind).
+
+Functions (same names as the C ABI):
+    kivi_quant_keys(k, bits, group)      -> (codes, scale, zero)
+    kivi_quant_values(v, bits, group)    -> (codes, scale, zero)
+    kivi_dequant_keys(codes, scale, zero, bits, group, out_dtype) -> out
+    kivi_dequant_values(codes, scale, zero, bits, group, out_dtype) -> out
+    kivi_quant_dequant_keys(k, bits, group, with_codes=True)
+        -> (recon, codes, scale, zero) or recon when with_codes=False
+    kivi_quant_dequant_values(...)       likewise
+    kivi_codes_bytes, kivi_key_param_count, kivi_value_param_count,
+    kivi_status_string
+Tensors are [BH, S, D] (or [B, H, S, D], flattened to BH = B*H), contiguous,
+float16 or bfloat16; codes are uint8 [..., S, D*bits/8]; key params are
+float32 [..., ceil(S/group), D]; value params float32 [..., S, ceil(D/group)].
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkivi.so")
+
+KIVI_FP16 = 0
+KIVI_BF16 = 1
+
+STATUS = {
+    0: "KIVI_OK", 1: "KIVI_ERR_NULL", 2: "KIVI_ERR_SHAPE", 3: "KIVI_ERR_BITS",
+    4: "KIVI_ERR_GROUP", 5: "KIVI_ERR_DTYPE", 6: "KIVI_ERR_ALIGN",
+    7: "KIVI_ERR_LAUNCH",
+}
+
+
+class KiviError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} "
+                         f"({_C.kivi_status_string(status).decode()})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m "
+            "kv_cache_quantization_kivi_amd.build` (or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I = ctypes.c_int
+    quant = [P, I, I64, I64, I64, I, I64, P, P, P, P]
+    L.kivi_quant_keys.argtypes = quant
+    L.kivi_quant_values.argtypes = quant
+    fused = [P, I, I64, I64, I64, I, I64, P, P, P, P, P]
+    L.kivi_quant_dequant_keys.argtypes = fused
+    L.kivi_quant_dequant_values.argtypes = fused
+    dq = [P, P, P, I64, I64, I64, I, I64, I, P, P]
+    L.kivi_dequant_keys.argtypes = dq
+    L.kivi_dequant_values.argtypes = dq
+    for name in ("kivi_quant_keys", "kivi_quant_values",
+                 "kivi_quant_dequant_keys", "kivi_quant_dequant_values",
+                 "kivi_dequant_keys", "kivi_dequant_values"):
+        getattr(L, name).restype = I
+    L.kivi_codes_bytes.argtypes = [I64, I64, I64, I]
+    L.kivi_codes_bytes.restype = I64
+    L.kivi_key_param_count.argtypes = [I64, I64, I64, I64]
+    L.kivi_key_param_count.restype = I64
+    L.kivi_value_param_count.argtypes = [I64, I64, I64, I64]
+    L.kivi_value_param_count.restype = I64
+    L.kivi_status_string.argtypes = [I]
+    L.kivi_status_string.restype = ctypes.c_char_p
+    return L
+
+
+_C = _load()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _dtype_code(dt):
+    if dt == torch.float16:
+        return KIVI_FP16
+    if dt == torch.bfloat16:
+        return KIVI_BF16
+    raise TypeError(f"KIVI tensors are float16 or bfloat16, got {dt}")
+
+
+def _torch_dtype(code):
+    return torch.float16 if code == KIVI_FP16 else torch.bfloat16
+
+
+def _bsd(x):
+    """Leading dims flattened into BH; returns (BH, S, D, lead_shape)."""
+    if x.dim() < 2:
+        raise ValueError("expected a [..., S, D] tensor")
+    if not x.is_contiguous():
+        raise ValueError("KIVI tensors must be contiguous")
+    S, D = x.shape[-2], x.shape[-1]
+    lead = tuple(x.shape[:-2])
+    BH = 1
+    for n in lead:
+        BH *= n
+    return BH, S, D, lead
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(st, what):
+    if st != 0:
+        raise KiviError(st, what)
+
+
+def _ngroups(n, g):
+    return (n + g - 1) // g
+
+
+def _alloc_quant(x, keys, bits, group, codes, scale, zero):
+    BH, S, D, lead = _bsd(x)
+    if codes is None:
+        codes = torch.empty(lead + (S, D * bits // 8), dtype=torch.uint8,
+                            device=x.device)
+    pshape = lead + ((_ngroups(S, group), D) if keys
+                     else (S, _ngroups(D, group)))
+    if scale is None:
+        scale = torch.empty(pshape, dtype=torch.float32, device=x.device)
+    if zero is None:
+        zero = torch.empty(pshape, dtype=torch.float32, device=x.device)
+    return codes, scale, zero
+
+
+# --------------------------------------------------------------------------
+# the C ABI, tensor level
+# --------------------------------------------------------------------------
+
+def _quant(name, keys, x, bits, group, codes, scale, zero, stream):
+    BH, S, D, _ = _bsd(x)
+    if group < 1:
+        _check(4, name)
+    codes, scale, zero = _alloc_quant(x, keys, bits, group, codes, scale, zero)
+    st = getattr(_C, name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
+                           group, _ptr(codes), _ptr(scale), _ptr(zero),
+                           _stream(x.device, stream))
+    _check(st, name)
+    return codes, scale, zero
+
+
+def kivi_quant_keys(k, bits=2, group=32, codes=None, scale=None, zero=None,
+                    stream=None):
+    """Per-channel key quantization -> (codes, scale, zero)."""
+    return _quant("kivi_quant_keys", True, k, bits, group, codes, scale, zero,
+                  stream)
+
+
+def kivi_quant_values(v, bits=2, group=32, codes=None, scale=None, zero=None,
+                      stream=None):
+    """Per-token value quantization -> (codes, scale, zero)."""
+    return _quant("kivi_quant_values", False, v, bits, group, codes, scale,
+                  zero, stream)
+
+
+def _fused(name, keys, x, bits, group, with_codes, recon, codes, scale, zero,
+           stream):
+    BH, S, D, _ = _bsd(x)
+    if group < 1:
+        _check(4, name)
+    if recon is None:
+        recon = torch.empty_like(x)
+    if with_codes:
+        codes, scale, zero = _alloc_quant(x, keys, bits, group, codes, scale,
+                                          zero)
+    else:
+        codes = scale = zero = None
+    st = getattr(_C, name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
+                           group, _ptr(codes), _ptr(scale), _ptr(zero),
+                           _ptr(recon), _stream(x.device, stream))
+    _check(st, name)
+    return (recon, codes, scale, zero) if with_codes else recon
+
+
+def kivi_quant_dequant_keys(k, bits=2, group=32, with_codes=True, recon=None,
+                            codes=None, scale=None, zero=None, stream=None):
+    """Fused key quantize -> dequantize in one pass."""
+    return _fused("kivi_quant_dequant_keys", True, k, bits, group, with_codes,
+                  recon, codes, scale, zero, stream)
+
+
+def kivi_quant_dequant_values(v, bits=2, group=32, with_codes=True,
+                              recon=None, codes=None, scale=None, zero=None,
+                              stream=None):
+    """Fused value quantize -> dequantize in one pass."""
+    return _fused("kivi_quant_dequant_values", False, v, bits, group,
+                  with_codes, recon, codes, scale, zero, stream)
+
+
+def _dequant(name, keys, codes, scale, zero, bits, group, out_dtype, out,
+             stream):
+    if codes.dim() < 2 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous [..., S, D*bits/8] tensor")
+    lead = tuple(codes.shape[:-2])
+    S = codes.shape[-2]
+    D = codes.shape[-1] * 8 // bits if bits in (1, 2, 4, 8) else 0
+    BH = 1
+    for n in lead:
+        BH *= n
+    if out is None:
+        out = torch.empty(lead + (S, D), dtype=out_dtype, device=codes.device)
+    st = getattr(_C, name)(_ptr(codes), _ptr(scale), _ptr(zero), BH, S, D,
+                           bits, group, _dtype_code(out.dtype), _ptr(out),
+                           _stream(codes.device, stream))
+    _check(st, name)
+    return out
+
+
+def kivi_dequant_keys(codes, scale, zero, bits=2, group=32,
+                      out_dtype=torch.float16, out=None, stream=None):
+    """Key dequantization -> [..., S, D] of out_dtype."""
+    return _dequant("kivi_dequant_keys", True, codes, scale, zero, bits,
+                    group, out_dtype, out, stream)
+
+
+def kivi_dequant_values(codes, scale, zero, bits=2, group=32,
+                        out_dtype=torch.float16, out=None, stream=None):
+    """Value dequantization -> [..., S, D] of out_dtype."""
+    return _dequant("kivi_dequant_values", False, codes, scale, zero, bits,
+                    group, out_dtype, out, stream)
+
+
+def kivi_codes_bytes(BH, S, D, bits):
+    return _C.kivi_codes_bytes(BH, S, D, bits)
+
+
+def kivi_key_param_count(BH, S, D, group):
+    return _C.kivi_key_param_count(BH, S, D, group)
+
+
+def kivi_value_param_count(BH, S, D, group):
+    return _C.kivi_value_param_count(BH, S, D, group)
+
+
+def kivi_status_string(status):
+    return _C.kivi_status_string(status).decode()
+
+
+def library_path():
+    return LIB_PATH
+
+
+def raw():
+    """The ctypes handle of libkivi.so (pointer-level calls)."""
+    return _C

@@ -1,0 +1,188 @@
+// C ABI of libkivi.so (declared in include/kivi.h): argument validation and
+// dispatch to the HIP kernel launchers.  Everything is checked before any
+// launch, so an invalid call writes nothing and enqueues nothing.
+#include "kivi.h"
+
+#include <stdint.h>
+
+#include "kivi_launch.h"
+
+namespace {
+
+bool bits_ok(int bits) {
+    return bits == 1 || bits == 2 || bits == 4 || bits == 8;
+}
+
+bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Shape rules shared by every entry point.
+kivi_status check_shape(int64_t BH, int64_t S, int64_t D, int bits,
+                        int64_t group) {
+    if (!bits_ok(bits)) return KIVI_ERR_BITS;
+    if (group < 1) return KIVI_ERR_GROUP;
+    if (BH < 0 || S < 0 || D < 0) return KIVI_ERR_SHAPE;
+    if (D > (INT64_MAX / 8)) return KIVI_ERR_SHAPE;
+    if ((D * bits) % 8 != 0) return KIVI_ERR_SHAPE;
+    int64_t n = 0;
+    if (__builtin_mul_overflow(BH, S, &n)) return KIVI_ERR_SHAPE;
+    if (__builtin_mul_overflow(n, D, &n)) return KIVI_ERR_SHAPE;
+    if (__builtin_mul_overflow(n, (int64_t)2, &n)) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+bool empty(int64_t BH, int64_t S, int64_t D) {
+    return BH == 0 || S == 0 || D == 0;
+}
+
+bool dtype_ok(int dt) { return dt == KIVI_FP16 || dt == KIVI_BF16; }
+
+kivi_status launched(hipError_t e) {
+    return e == hipSuccess ? KIVI_OK : KIVI_ERR_LAUNCH;
+}
+
+// Common checks of the quantize family.  need_q: codes/scale/zero must be
+// given; need_r: recon must be given; q_optional: codes/scale/zero may be
+// all NULL or all non-NULL.
+kivi_status check_quant(const void* x, int dt, int64_t BH, int64_t S,
+                        int64_t D, int bits, int64_t group,
+                        const uint8_t* codes, const float* scale,
+                        const float* zero, const void* recon, bool need_q,
+                        bool need_r, bool q_optional, bool* is_empty) {
+    kivi_status st = check_shape(BH, S, D, bits, group);
+    if (st != KIVI_OK) return st;
+    if (!dtype_ok(dt)) return KIVI_ERR_DTYPE;
+    *is_empty = empty(BH, S, D);
+    if (*is_empty) return KIVI_OK;
+    const int nq = (codes != nullptr) + (scale != nullptr) + (zero != nullptr);
+    if (x == nullptr) return KIVI_ERR_NULL;
+    if (need_q && nq != 3) return KIVI_ERR_NULL;
+    if (q_optional && nq != 0 && nq != 3) return KIVI_ERR_NULL;
+    if (need_r && recon == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) ||
+        !aligned16(zero) || !aligned16(recon))
+        return KIVI_ERR_ALIGN;
+    return KIVI_OK;
+}
+
+kivi_status quant(bool keys, const void* x, kivi_dtype dt, int64_t BH,
+                  int64_t S, int64_t D, int bits, int64_t group,
+                  uint8_t* codes, float* scale, float* zero, void* recon,
+                  bool fused, hipStream_t stream) {
+    bool is_empty = false;
+    kivi_status st = check_quant(x, dt, BH, S, D, bits, group, codes, scale,
+                                 zero, recon, !fused, fused, fused, &is_empty);
+    if (st != KIVI_OK || is_empty) return st;
+    kivi::QuantJob j{x, (int)dt, BH, S, D, bits, group, codes, scale, zero,
+                     fused ? recon : nullptr, stream};
+    return launched(keys ? kivi::launch_quant_keys(j)
+                         : kivi::launch_quant_values(j));
+}
+
+kivi_status dequant(bool keys, const uint8_t* codes, const float* scale,
+                    const float* zero, int64_t BH, int64_t S, int64_t D,
+                    int bits, int64_t group, kivi_dtype out_dt, void* out,
+                    hipStream_t stream) {
+    kivi_status st = check_shape(BH, S, D, bits, group);
+    if (st != KIVI_OK) return st;
+    if (!dtype_ok(out_dt)) return KIVI_ERR_DTYPE;
+    if (empty(BH, S, D)) return KIVI_OK;
+    if (!codes || !scale || !zero || !out) return KIVI_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(scale) || !aligned16(zero) ||
+        !aligned16(out))
+        return KIVI_ERR_ALIGN;
+    kivi::DequantJob j{codes, scale, zero, BH, S, D, bits, group,
+                       (int)out_dt, out, stream};
+    return launched(keys ? kivi::launch_dequant_keys(j)
+                         : kivi::launch_dequant_values(j));
+}
+
+}  // namespace
+
+extern "C" {
+
+kivi_status kivi_quant_keys(const void* k, kivi_dtype dt, int64_t BH,
+                            int64_t S, int64_t D, int bits, int64_t group,
+                            uint8_t* codes, float* scale, float* zero,
+                            hipStream_t stream) {
+    return quant(true, k, dt, BH, S, D, bits, group, codes, scale, zero,
+                 nullptr, false, stream);
+}
+
+kivi_status kivi_quant_values(const void* v, kivi_dtype dt, int64_t BH,
+                              int64_t S, int64_t D, int bits, int64_t group,
+                              uint8_t* codes, float* scale, float* zero,
+                              hipStream_t stream) {
+    return quant(false, v, dt, BH, S, D, bits, group, codes, scale, zero,
+                 nullptr, false, stream);
+}
+
+kivi_status kivi_quant_dequant_keys(const void* k, kivi_dtype dt, int64_t BH,
+                                    int64_t S, int64_t D, int bits,
+                                    int64_t group, uint8_t* codes,
+                                    float* scale, float* zero, void* recon,
+                                    hipStream_t stream) {
+    return quant(true, k, dt, BH, S, D, bits, group, codes, scale, zero,
+                 recon, true, stream);
+}
+
+kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
+                                      int64_t BH, int64_t S, int64_t D,
+                                      int bits, int64_t group, uint8_t* codes,
+                                      float* scale, float* zero, void* recon,
+                                      hipStream_t stream) {
+    return quant(false, v, dt, BH, S, D, bits, group, codes, scale, zero,
+                 recon, true, stream);
+}
+
+kivi_status kivi_dequant_keys(const uint8_t* codes, const float* scale,
+                              const float* zero, int64_t BH, int64_t S,
+                              int64_t D, int bits, int64_t group,
+                              kivi_dtype out_dt, void* out,
+                              hipStream_t stream) {
+    return dequant(true, codes, scale, zero, BH, S, D, bits, group, out_dt,
+                   out, stream);
+}
+
+kivi_status kivi_dequant_values(const uint8_t* codes, const float* scale,
+                                const float* zero, int64_t BH, int64_t S,
+                                int64_t D, int bits, int64_t group,
+                                kivi_dtype out_dt, void* out,
+                                hipStream_t stream) {
+    return dequant(false, codes, scale, zero, BH, S, D, bits, group, out_dt,
+                   out, stream);
+}
+
+int64_t kivi_codes_bytes(int64_t BH, int64_t S, int64_t D, int bits) {
+    if (check_shape(BH, S, D, bits, 1) != KIVI_OK) return -1;
+    return BH * S * (D * bits / 8);
+}
+
+int64_t kivi_key_param_count(int64_t BH, int64_t S, int64_t D,
+                             int64_t group) {
+    if (check_shape(BH, S, D, 8, group) != KIVI_OK) return -1;
+    return BH * ((S + group - 1) / group) * D;
+}
+
+int64_t kivi_value_param_count(int64_t BH, int64_t S, int64_t D,
+                               int64_t group) {
+    if (check_shape(BH, S, D, 8, group) != KIVI_OK) return -1;
+    return BH * S * ((D + group - 1) / group);
+}
+
+const char* kivi_status_string(kivi_status status) {
+    switch (status) {
+        case KIVI_OK: return "ok";
+        case KIVI_ERR_NULL: return "a required pointer is NULL";
+        case KIVI_ERR_SHAPE: return "invalid shape (negative, overflowing, or D*bits not a multiple of 8)";
+        case KIVI_ERR_BITS: return "bits must be 1, 2, 4 or 8";
+        case KIVI_ERR_GROUP: return "group must be >= 1";
+        case KIVI_ERR_DTYPE: return "dtype must be KIVI_FP16 or KIVI_BF16";
+        case KIVI_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case KIVI_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

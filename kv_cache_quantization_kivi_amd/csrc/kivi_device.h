@@ -1,0 +1,302 @@
+// Device-side building blocks shared by the KIVI kernels (gfx950).
+//
+// Arithmetic contract: every step of the quantizer is one IEEE binary32
+// operation rounded to nearest even, exactly as the KIVI blog post on the
+// fused Metal kernels states it (sections "What we're actually optimizing"
+// and "Three ways to be off by one bit"): zero = min, scale = (max - min) /
+// (2^bits - 1), code = clip(round_half_even((x - zero) / scale)), recon =
+// (code * scale) + zero with the product rounded first.  This file is built
+// with -ffp-contract=off so no multiply-add is ever fused behind our back;
+// the only fused operations are the explicit __builtin_fmaf calls of the
+// division below.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kivi {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+__device__ __forceinline__ h2_t as_h2(uint32_t w) {
+    return __builtin_bit_cast(h2_t, w);
+}
+
+// Element k (0..7) of an 8-element chunk held as 4 dwords, widened to fp32
+// (exact for both 16-bit formats).
+template <int DT>
+__device__ __forceinline__ float elem(const uint32_t (&w)[4], int k) {
+    const uint32_t word = w[k >> 1];
+    if constexpr (DT == DT_F16) {
+        const uint16_t h = (k & 1) ? (uint16_t)(word >> 16) : (uint16_t)word;
+        return (float)__builtin_bit_cast(_Float16, h);
+    } else {
+        return __uint_as_float((k & 1) ? (word & 0xffff0000u) : (word << 16));
+    }
+}
+
+// Two fp32 values -> one dword of two 16-bit values, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
+    if constexpr (DT == DT_F16) {
+        h2_t v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        b2_t v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+__device__ __forceinline__ uint4 load16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+__device__ __forceinline__ void words(const uint4& v, uint32_t (&w)[4]) {
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
+}
+
+// IEEE 754-2019 minimum/maximum.  On gfx950 these map to v_[pk_]minimum3 /
+// v_[pk_]maximum3, which need no NaN-quieting of their inputs (minNum/maxNum
+// under the IEEE mode bit do) and fold two new operands per instruction.
+// They order -0 below +0; the group min/max is canonicalised afterwards.
+__device__ __forceinline__ h2_t vmin(h2_t a, h2_t b) {
+    return __builtin_elementwise_minimum(a, b);
+}
+__device__ __forceinline__ h2_t vmax(h2_t a, h2_t b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+__device__ __forceinline__ float vmin(float a, float b) {
+    return __builtin_elementwise_minimum(a, b);
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+    return __builtin_elementwise_maximum(a, b);
+}
+
+// Running min/max of one 8-element chunk position across rows.
+template <int DT>
+struct MinMax8 {
+    // fp16: packed pairs (exact: min/max only select).
+    // bf16: fp32 of each element, except that the high element of a dword
+    // is taken as the raw dword: its low 16 bits perturb it by less than one
+    // bf16 ulp toward larger magnitude, which keeps the order of distinct
+    // bf16 values, so the min/max dword carries the min/max bf16 in its high
+    // half (zeros of either sign may come out as tiny values of either sign;
+    // get() masks the low half and make_params canonicalises the zero).
+    h2_t mn2[4], mx2[4];
+    float mn[8], mx[8];
+
+    __device__ __forceinline__ void init(const uint4& v) {
+        uint32_t w[4];
+        words(v, w);
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mn2[j] = mx2[j] = as_h2(w[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mn[2 * j] = mx[2 * j] = __uint_as_float(w[j] << 16);
+                mn[2 * j + 1] = mx[2 * j + 1] = __uint_as_float(w[j]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void add(const uint4& v) {
+        uint32_t w[4];
+        words(v, w);
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mn2[j] = vmin(mn2[j], as_h2(w[j]));
+                mx2[j] = vmax(mx2[j], as_h2(w[j]));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lo = __uint_as_float(w[j] << 16);
+                const float hi = __uint_as_float(w[j]);
+                mn[2 * j] = vmin(mn[2 * j], lo);
+                mx[2 * j] = vmax(mx[2 * j], lo);
+                mn[2 * j + 1] = vmin(mn[2 * j + 1], hi);
+                mx[2 * j + 1] = vmax(mx[2 * j + 1], hi);
+            }
+        }
+    }
+
+    // Per-channel min and max as fp32.
+    __device__ __forceinline__ void get(float (&lo)[8], float (&hi)[8]) const {
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lo[2 * j] = (float)mn2[j].x;
+                lo[2 * j + 1] = (float)mn2[j].y;
+                hi[2 * j] = (float)mx2[j].x;
+                hi[2 * j + 1] = (float)mx2[j].y;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                lo[k] = (k & 1) ? __uint_as_float(__float_as_uint(mn[k]) & 0xffff0000u)
+                                : mn[k];
+                hi[k] = (k & 1) ? __uint_as_float(__float_as_uint(mx[k]) & 0xffff0000u)
+                                : mx[k];
+            }
+        }
+    }
+};
+
+// Group parameters from the group's fp32 min and max.
+//   zero  = min (stored as +0 when it compares equal to 0)
+//   scale = RN(RN(max - min) / (2^bits - 1)), a correctly rounded division
+//   y     = RN(1 / scale), used by the division below (0 when scale == 0)
+//   fast  = whether the reciprocal-based division is exact for this scale
+struct Params {
+    float zero, scale, y;
+    bool fast;
+};
+
+__device__ __forceinline__ Params make_params(float mn, float mx,
+                                              float levels) {
+    Params p;
+    mn = (mn == 0.0f) ? 0.0f : mn;
+    mx = (mx == 0.0f) ? 0.0f : mx;
+    const float range = mx - mn;
+    p.zero = mn;
+    p.scale = range / levels;
+    p.y = (p.scale == 0.0f) ? 0.0f : 1.0f / p.scale;
+    // The correction step needs no underflow or overflow in its residual;
+    // any 16-bit input group keeps scale inside these bounds except bf16
+    // groups with extreme magnitudes, which take the exact division.
+    p.fast = (p.scale == 0.0f) ||
+             (p.scale >= 0x1p-64f && p.scale <= 0x1p64f);
+    return p;
+}
+
+// RN(a / scale) from y = RN(1 / scale) (Markstein, IBM J. Res. Dev. 34(1),
+// 1990; Muller et al., Handbook of Floating-Point Arithmetic, "Newton-Raphson
+// based division with an FMA"): q0 = RN(a*y) is within an ulp of a/scale,
+// the residual a - q0*scale is exact in one fused multiply-add, and one more
+// fused multiply-add gives the correctly rounded quotient.  With scale == 0
+// (so y == 0 and a == 0) it returns 0.
+__device__ __forceinline__ float div_fast(float a, float scale, float y) {
+    const float q0 = a * y;
+    const float r = __builtin_fmaf(-q0, scale, a);
+    return __builtin_fmaf(r, y, q0);
+}
+
+// Code of quotient t = RN(a/scale): round half to even and clip to
+// [0, maxc]; maxNum/minNum send a NaN quotient to 0.
+__device__ __forceinline__ uint32_t code_exact(float t, float maxc) {
+    float r = __builtin_rintf(t);
+    r = fmaxf(r, 0.0f);
+    r = fminf(r, maxc);
+    return (uint32_t)r;
+}
+
+// The slow path: true IEEE division (scale == 0 gives code 0).
+__device__ __forceinline__ uint32_t code_slow(float f, const Params& p,
+                                              float maxc) {
+    if (p.scale == 0.0f) return 0u;
+    const float a = f - p.zero;
+    return code_exact(a / p.scale, maxc);
+}
+
+// The fast path.  For an element of its own group, a = RN(f - zero) lies in
+// [0, RN(max - min)], so t = RN(a / scale) lies in [0, maxc * (1 + 2^-23)]
+// and round-half-even never leaves [0, maxc]: the clip cannot bind.  Adding
+// 2^23 rounds t to an integer (ties to even) in the low mantissa bits.
+__device__ __forceinline__ uint32_t code_fast(float f, const Params& p) {
+    const float a = f - p.zero;
+    const float t = div_fast(a, p.scale, p.y);
+    return __float_as_uint(t + 0x1p23f) - 0x4b000000u;
+}
+
+// recon = RN(RN(code * scale) + zero): two roundings, never fused.
+__device__ __forceinline__ float recon(uint32_t code, float scale, float zero) {
+    const float prod = (float)code * scale;
+    return prod + zero;
+}
+
+// Store the 8*BITS bits of one chunk's codes (BITS bytes) at p.
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* p, uint64_t bits) {
+    if constexpr (BITS == 1) {
+        *p = (uint8_t)bits;
+    } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)bits;
+    } else if constexpr (BITS == 4) {
+        *reinterpret_cast<uint32_t*>(p) = (uint32_t)bits;
+    } else {
+        *reinterpret_cast<uint2*>(p) =
+            make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ uint64_t load_codes(const uint8_t* p) {
+    if constexpr (BITS == 1) {
+        return *p;
+    } else if constexpr (BITS == 2) {
+        return *reinterpret_cast<const uint16_t*>(p);
+    } else if constexpr (BITS == 4) {
+        return *reinterpret_cast<const uint32_t*>(p);
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        return (uint64_t)v.x | ((uint64_t)v.y << 32);
+    }
+}
+
+// Quantize one 8-element chunk against 8 per-element parameter sets
+// (pk[k] for element k).  Returns the packed codes (code k at bits
+// [k*BITS, (k+1)*BITS)) and, if wanted, the reconstruction as 4 dwords.
+template <int DT, int BITS, bool FAST, bool WR>
+__device__ __forceinline__ uint64_t quant_chunk(const uint4& v,
+                                                const Params* pk,
+                                                uint4* rec) {
+    constexpr float maxc = (float)((1 << BITS) - 1);
+    uint32_t w[4];
+    words(v, w);
+    uint64_t packed = 0;
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float f = elem<DT>(w, k);
+        const uint32_t c = FAST ? code_fast(f, pk[k]) : code_slow(f, pk[k], maxc);
+        packed |= (uint64_t)c << (k * BITS);
+        if constexpr (WR) r[k] = recon(c, pk[k].scale, pk[k].zero);
+    }
+    if constexpr (WR) {
+        rec->x = narrow2<DT>(r[0], r[1]);
+        rec->y = narrow2<DT>(r[2], r[3]);
+        rec->z = narrow2<DT>(r[4], r[5]);
+        rec->w = narrow2<DT>(r[6], r[7]);
+    }
+    return packed;
+}
+
+// Dequantize one chunk of 8 packed codes.
+template <int DT, int BITS>
+__device__ __forceinline__ uint4 dequant_chunk(uint64_t packed,
+                                               const float (&sc)[8],
+                                               const float (&z)[8]) {
+    constexpr uint32_t mask = (1u << BITS) - 1u;
+    float r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t c = (uint32_t)(packed >> (k * BITS)) & mask;
+        r[k] = recon(c, sc[k], z[k]);
+    }
+    uint4 o;
+    o.x = narrow2<DT>(r[0], r[1]);
+    o.y = narrow2<DT>(r[2], r[3]);
+    o.z = narrow2<DT>(r[4], r[5]);
+    o.w = narrow2<DT>(r[6], r[7]);
+    return o;
+}
+
+}  // namespace kivi

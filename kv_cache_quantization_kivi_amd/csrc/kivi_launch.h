@@ -1,0 +1,49 @@
+// Internal interface between the C ABI (kivi_api.cpp) and the kernel
+// launchers.  Arguments are validated by the caller; launchers only choose a
+// kernel and a grid and enqueue it on the given stream.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace kivi {
+
+struct QuantJob {
+    const void* x;        // [BH, S, D] 16-bit input
+    int dtype;            // 0 fp16, 1 bf16
+    int64_t BH, S, D;
+    int bits;
+    int64_t group;
+    uint8_t* codes;       // may be null only when recon-only
+    float* scale;
+    float* zero;
+    void* recon;          // null unless fused; same dtype as x
+    hipStream_t stream;
+};
+
+struct DequantJob {
+    const uint8_t* codes;
+    const float* scale;
+    const float* zero;
+    int64_t BH, S, D;
+    int bits;
+    int64_t group;
+    int out_dtype;
+    void* out;
+    hipStream_t stream;
+};
+
+hipError_t launch_quant_keys(const QuantJob& j);
+hipError_t launch_quant_values(const QuantJob& j);
+hipError_t launch_dequant_keys(const DequantJob& j);
+hipError_t launch_dequant_values(const DequantJob& j);
+
+// Fallback kernels for shapes the fast kernels do not cover (keys with
+// D % 8 != 0 or group > 32; values with D % 8 != 0, D > 512 or a group that
+// is not 8 times a power of two; dequant with D % 8 != 0 or, for values,
+// group % 8 != 0).
+hipError_t launch_generic_quant_keys(const QuantJob& j);
+hipError_t launch_generic_quant_values(const QuantJob& j);
+hipError_t launch_generic_dequant(const DequantJob& j, bool keys);
+
+}  // namespace kivi

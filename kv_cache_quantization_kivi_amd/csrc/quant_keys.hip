@@ -1,0 +1,175 @@
+// KIVI per-channel key quantization for gfx950.
+//
+// KIVI blog post on the fused Metal kernels, section "Kernel A -- per-channel
+// keys": the group of channel d runs along the strided token axis, so a
+// thread owning whole groups needs no cross-thread reduction.  Here one lane
+// owns a chunk of 8 adjacent channels of one (bh, token group) tile: every
+// step of its token loop is one 128-bit load, and the 16 lanes covering a
+// 128-channel row read 256 contiguous bytes, so a wave's loads stay fully
+// coalesced without a transpose (the post's discarded transposing variant).
+// The whole group (up to 32 tokens x 8 channels) stays in registers, so the
+// input is read from HBM exactly once: min/max, then codes, from the same
+// registers.
+#include "kivi_device.h"
+#include "kivi_launch.h"
+
+namespace kivi {
+
+constexpr int kKeyGMax = 32;   // largest group held in registers
+
+// Quantize and store the GMAX tokens of a whole group from registers.
+template <int DT, int BITS, bool WQ, bool WR, int GMAX>
+__device__ __forceinline__ void emit_full(const uint4 (&v)[GMAX],
+                                          const Params (&pk)[8], uint8_t* dst,
+                                          int64_t row_bytes, uint16_t* rdst,
+                                          int64_t D) {
+#pragma unroll
+    for (int t = 0; t < GMAX; ++t) {
+        uint4 r;
+        const uint64_t q = quant_chunk<DT, BITS, true, WR>(v[t], pk, &r);
+        if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
+        if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+    }
+}
+
+// The rare cases (a ragged last group, or a scale outside the fast
+// division's range): a rolled loop that reloads each token (an L2 hit), so
+// the unrolled register path above is the only large code in the kernel.
+template <int DT, int BITS, bool WQ, bool WR, bool FAST>
+__device__ __forceinline__ void emit_rolled(const uint16_t* src,
+                                         const Params (&pk)[8], int32_t n,
+                                         uint8_t* dst, int64_t row_bytes,
+                                         uint16_t* rdst, int64_t D) {
+#pragma unroll 1
+    for (int32_t t = 0; t < n; ++t) {
+        const uint4 v = load16(src + (int64_t)t * D);
+        uint4 r;
+        const uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v, pk, &r);
+        if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
+        if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+    }
+}
+
+// Work item = (bh, token group g, channel chunk c), flattened with c fastest
+// so consecutive lanes take consecutive 16-byte chunks of the same rows.
+// GMAX >= group size; a ragged last group loads its last token again in the
+// missing slots, which is the pages' edge-replicate padding and leaves the
+// min/max unchanged, so the loads and the min/max carry no guards.
+// WQ: write codes + params.  WR: write the reconstruction (fused path).
+template <int DT, int BITS, int GMAX, bool WQ, bool WR>
+__global__ __launch_bounds__(256) void quant_keys_kernel(
+    const uint16_t* __restrict__ x, uint32_t n_items, uint32_t D8,
+    uint32_t NG, int32_t S, int32_t G, uint8_t* __restrict__ codes,
+    float* __restrict__ scale, float* __restrict__ zero,
+    uint16_t* __restrict__ recon) {
+    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
+    if (item >= n_items) return;
+    const uint32_t c = item % D8;
+    const uint32_t tile = item / D8;
+    const uint32_t g = tile % NG;
+    const uint32_t bh = tile / NG;
+    const int32_t s0 = (int32_t)g * G;
+    const int32_t nt = min(G, S - s0);
+    const int64_t D = (int64_t)D8 * 8;
+    const int64_t row0 = (int64_t)bh * S + s0;
+    const uint16_t* src = x + row0 * D + (int64_t)c * 8;
+
+    uint4 v[GMAX];
+    if (nt == GMAX) {
+#pragma unroll
+        for (int t = 0; t < GMAX; ++t) v[t] = load16(src + t * D);
+    } else {
+#pragma unroll
+        for (int t = 0; t < GMAX; ++t) v[t] = load16(src + min(t, nt - 1) * D);
+    }
+
+    MinMax8<DT> mm;
+    mm.init(v[0]);
+#pragma unroll
+    for (int t = 1; t < GMAX; ++t) mm.add(v[t]);
+    float lo[8], hi[8];
+    mm.get(lo, hi);
+
+    constexpr float levels = (float)((1 << BITS) - 1);
+    Params pk[8];
+    bool fast = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        pk[k] = make_params(lo[k], hi[k], levels);
+        fast = fast && pk[k].fast;
+    }
+
+    if constexpr (WQ) {
+        const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
+        float4* ps = reinterpret_cast<float4*>(scale + p);
+        float4* pz = reinterpret_cast<float4*>(zero + p);
+        ps[0] = make_float4(pk[0].scale, pk[1].scale, pk[2].scale, pk[3].scale);
+        ps[1] = make_float4(pk[4].scale, pk[5].scale, pk[6].scale, pk[7].scale);
+        pz[0] = make_float4(pk[0].zero, pk[1].zero, pk[2].zero, pk[3].zero);
+        pz[1] = make_float4(pk[4].zero, pk[5].zero, pk[6].zero, pk[7].zero);
+    }
+
+    const int64_t row_bytes = (int64_t)D8 * BITS;   // D * BITS / 8
+    uint8_t* dst = WQ ? codes + row0 * row_bytes + (int64_t)c * BITS : nullptr;
+    uint16_t* rdst = WR ? recon + row0 * D + (int64_t)c * 8 : nullptr;
+    if (fast && nt == GMAX)
+        emit_full<DT, BITS, WQ, WR, GMAX>(v, pk, dst, row_bytes, rdst, D);
+    else if (fast)
+        emit_rolled<DT, BITS, WQ, WR, true>(src, pk, nt, dst, row_bytes, rdst, D);
+    else
+        emit_rolled<DT, BITS, WQ, WR, false>(src, pk, nt, dst, row_bytes, rdst, D);
+}
+
+template <int DT, int BITS, int GMAX, bool WQ, bool WR>
+static hipError_t launch_keys_t(const QuantJob& j) {
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
+    const uint64_t n_items = (uint64_t)j.BH * NG * D8;
+    const uint32_t blocks = (uint32_t)((n_items + 255) / 256);
+    hipLaunchKernelGGL((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>), dim3(blocks),
+                       dim3(256), 0, j.stream,
+                       static_cast<const uint16_t*>(j.x), (uint32_t)n_items, D8,
+                       NG, (int32_t)j.S, (int32_t)j.group, j.codes, j.scale,
+                       j.zero, static_cast<uint16_t*>(j.recon));
+    return hipGetLastError();
+}
+
+template <int DT, int BITS, int GMAX>
+static hipError_t launch_keys_mode(const QuantJob& j) {
+    const bool wq = j.codes != nullptr;
+    const bool wr = j.recon != nullptr;
+    if (wq && wr) return launch_keys_t<DT, BITS, GMAX, true, true>(j);
+    if (wq) return launch_keys_t<DT, BITS, GMAX, true, false>(j);
+    return launch_keys_t<DT, BITS, GMAX, false, true>(j);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_keys_gmax(const QuantJob& j) {
+    if (j.group <= 8) return launch_keys_mode<DT, BITS, 8>(j);
+    if (j.group <= 16) return launch_keys_mode<DT, BITS, 16>(j);
+    return launch_keys_mode<DT, BITS, 32>(j);
+}
+
+template <int DT>
+static hipError_t launch_keys_bits(const QuantJob& j) {
+    switch (j.bits) {
+        case 1: return launch_keys_gmax<DT, 1>(j);
+        case 2: return launch_keys_gmax<DT, 2>(j);
+        case 4: return launch_keys_gmax<DT, 4>(j);
+        default: return launch_keys_gmax<DT, 8>(j);
+    }
+}
+
+hipError_t launch_quant_keys(const QuantJob& j) {
+    // Register-resident fast path: whole 8-channel chunks, groups <= 32
+    // tokens, and an item count that fits 32-bit indexing.
+    const int64_t NG = (j.S + j.group - 1) / j.group;
+    const bool fits = (uint64_t)j.BH * NG * (j.D / 8) < (1ull << 31) &&
+                      j.S < (1ll << 31) && j.D < (1ll << 28);
+    if (j.D % 8 != 0 || j.group > kKeyGMax || !fits)
+        return launch_generic_quant_keys(j);
+    return j.dtype == DT_F16 ? launch_keys_bits<DT_F16>(j)
+                             : launch_keys_bits<DT_BF16>(j);
+}
+
+}  // namespace kivi

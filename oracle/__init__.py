@@ -15,7 +15,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, build
+from .build_oracle import LIB, build
 
 FP16 = 0
 BF16 = 1

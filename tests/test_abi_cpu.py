@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol,
+and rejects invalid arguments before touching the GPU (no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kivi.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import kv_cache_quantization_kivi_amd as K
+    return K
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("kivi_quant_keys", "kivi_quant_values", "kivi_dequant_keys",
+              "kivi_dequant_values", "kivi_quant_dequant_keys",
+              "kivi_quant_dequant_values", "kivi_codes_bytes",
+              "kivi_key_param_count", "kivi_value_param_count",
+              "kivi_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(K):
+    lib = ctypes.CDLL(K.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    # the python binding carries the same names
+    for n in declared_functions():
+        assert hasattr(K, n), n
+
+
+def test_size_helpers(K):
+    assert K.kivi_codes_bytes(224, 32, 128, 2) == 224 * 32 * 32
+    assert K.kivi_codes_bytes(4, 70, 48, 4) == 4 * 70 * 24
+    assert K.kivi_key_param_count(112, 32768, 128, 32) == 112 * 1024 * 128
+    assert K.kivi_key_param_count(3, 70, 48, 32) == 3 * 3 * 48
+    assert K.kivi_value_param_count(128, 8192, 128, 128) == 128 * 8192
+    assert K.kivi_value_param_count(3, 70, 48, 32) == 3 * 70 * 2
+    assert K.kivi_codes_bytes(1, 1, 6, 1) == -1        # D*bits % 8 != 0
+    assert K.kivi_codes_bytes(1, 1, 8, 3) == -1        # bits
+    assert K.kivi_key_param_count(1, 1, 8, 0) == -1    # group
+    assert K.kivi_codes_bytes(-1, 1, 8, 2) == -1
+    assert K.kivi_codes_bytes(1 << 40, 1 << 20, 1 << 10, 2) == -1  # overflow
+    assert K.kivi_codes_bytes(0, 5, 8, 2) == 0
+
+
+def test_status_strings(K):
+    for s in range(8):
+        assert K.kivi_status_string(s)
+    assert K.kivi_status_string(0) == "ok"
+
+
+def _raw_quant(K, name, x=0x1000, dt=0, BH=2, S=64, D=64, bits=2, G=32,
+               codes=0x2000, scale=0x3000, zero=0x4000):
+    fn = getattr(K.raw(), name)
+    return fn(ctypes.c_void_p(x), dt, BH, S, D, bits, G, ctypes.c_void_p(codes),
+              ctypes.c_void_p(scale), ctypes.c_void_p(zero), None)
+
+
+@pytest.mark.parametrize("name", ["kivi_quant_keys", "kivi_quant_values"])
+def test_quant_argument_errors(K, name):
+    # Every call below fails validation before any HIP call: the fake
+    # pointers are never dereferenced.
+    assert _raw_quant(K, name, bits=3) == 3
+    assert _raw_quant(K, name, bits=0) == 3
+    assert _raw_quant(K, name, G=0) == 4
+    assert _raw_quant(K, name, G=-5) == 4
+    assert _raw_quant(K, name, D=6, bits=1) == 2      # D*bits % 8
+    assert _raw_quant(K, name, BH=-1) == 2
+    assert _raw_quant(K, name, BH=1 << 40, S=1 << 20, D=1 << 8) == 2
+    assert _raw_quant(K, name, dt=2) == 5
+    assert _raw_quant(K, name, x=0) == 1
+    assert _raw_quant(K, name, codes=0) == 1
+    assert _raw_quant(K, name, scale=0) == 1
+    assert _raw_quant(K, name, zero=0) == 1
+    assert _raw_quant(K, name, x=0x1008) == 6          # misaligned
+    assert _raw_quant(K, name, zero=0x4004) == 6
+    # empty tensors are valid no-ops, even with NULL pointers
+    assert _raw_quant(K, name, BH=0, x=0, codes=0, scale=0, zero=0) == 0
+    assert _raw_quant(K, name, S=0, x=0, codes=0, scale=0, zero=0) == 0
+
+
+@pytest.mark.parametrize("name", ["kivi_quant_dequant_keys",
+                                  "kivi_quant_dequant_values"])
+def test_fused_argument_errors(K, name):
+    fn = getattr(K.raw(), name)
+    P = ctypes.c_void_p
+    # recon is required
+    assert fn(P(0x1000), 0, 2, 64, 64, 2, 32, P(0x2000), P(0x3000), P(0x4000),
+              None, None) == 1
+    # codes/scale/zero: all or none
+    assert fn(P(0x1000), 0, 2, 64, 64, 2, 32, P(0x2000), None, P(0x4000),
+              P(0x5000), None) == 1
+    assert fn(P(0x1000), 0, 2, 64, 64, 2, 32, None, None, None, P(0x5008),
+              None) == 6
+    assert fn(P(0x1000), 0, 2, 64, 64, 3, 32, None, None, None, P(0x5000),
+              None) == 3
+
+
+@pytest.mark.parametrize("name", ["kivi_dequant_keys", "kivi_dequant_values"])
+def test_dequant_argument_errors(K, name):
+    fn = getattr(K.raw(), name)
+    P = ctypes.c_void_p
+
+    def call(codes=0x1000, scale=0x2000, zero=0x3000, BH=2, S=64, D=64,
+             bits=2, G=32, dt=0, out=0x4000):
+        return fn(P(codes), P(scale), P(zero), BH, S, D, bits, G, dt, P(out),
+                  None)
+    assert call(bits=5) == 3
+    assert call(G=0) == 4
+    assert call(D=4, bits=1) == 2
+    assert call(dt=7) == 5
+    assert call(out=0) == 1
+    assert call(codes=0) == 1
+    assert call(scale=0x2002) == 6
+    assert call(S=0, codes=0, scale=0, zero=0, out=0) == 0
+
+
+def test_binding_rejects_bad_tensors(K):
+    import torch
+    x = torch.zeros(2, 8, 8, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        K.kivi_quant_keys(x)
+    y = torch.zeros(2, 8, 16, dtype=torch.float16)[:, :, :8]
+    with pytest.raises(ValueError):
+        K.kivi_quant_keys(y)

@@ -13,7 +13,7 @@ import tempfile
 import pytest
 
 import oracle
-from oracle.build import CMD, LIB, SRC
+from oracle.build_oracle import CMD, LIB, SRC
 from oracle_pins import ALL_PINS
 
 MUTANTS = [

@@ -14,6 +14,8 @@ its own; fp16 casts use numpy (round to nearest even), bf16 casts use torch
 on the CPU (round to nearest even).  Tensors are returned as uint16 bit
 patterns [BH, S, D].
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -129,14 +131,24 @@ def gen_slice(w, tensor, bh, pool=0):
     return _to_bits(slice_f32(w, tensor, bh, pool), w.dtype)
 
 
-def gen_tensor(w, tensor, bhs=None, pool=0):
-    """uint16 [len(bhs), S, D]; bhs defaults to every slice."""
+def gen_tensor(w, tensor, bhs=None, pool=0, threads=None):
+    """uint16 [len(bhs), S, D]; bhs defaults to every slice.  Slices are
+    independent draws, so they are generated on a thread pool."""
     if bhs is None:
         bhs = range(w.BH)
     bhs = list(bhs)
     out = np.empty((len(bhs), w.S, w.D), np.uint16)
-    for i, bh in enumerate(bhs):
-        out[i] = gen_slice(w, tensor, bh, pool)
+
+    def one(i):
+        out[i] = gen_slice(w, tensor, bhs[i], pool)
+
+    n = threads or min(16, os.cpu_count() or 1)
+    if n <= 1 or len(bhs) <= 2:
+        for i in range(len(bhs)):
+            one(i)
+    else:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(one, range(len(bhs))))
     return out
 
 
