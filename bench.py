@@ -171,6 +171,37 @@ def cpu_baseline(w, n_bh, steps_desc):
     }
 
 
+def calibrate_copy(torch, dev, mb, reps):
+    """A plain copy of known size: reads and writes exactly n bytes per
+    launch; its rocprofv3 FETCH_SIZE / WRITE_SIZE give the counter scale."""
+    n = mb * 1000 * 1000
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    big = torch.empty(4 * n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 * n),
+                             ("read_sum", lambda: src.view(torch.int32).sum(),
+                              n)):
+        for _ in range(3):
+            big.fill_(0)          # evict the operands from the caches
+            fn()
+        ts = []
+        for _ in range(reps):
+            big.fill_(0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        med = float(np.median(ts))
+        res[name] = {"bytes_per_launch": nbytes, "median_us": round(med * 1e3, 2),
+                     "gbs": round(nbytes / (med * 1e-3) / 1e9, 1)}
+    print(json.dumps({"calibration": res, "size_bytes": n}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,7 +211,11 @@ def main():
                     choices=sorted(W.WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
-    ap.add_argument("--cpu-sample-bh", type=int, default=96)
+    ap.add_argument("--cpu-sample-bh", type=int, default=256)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="instead of the benchmark, time a plain device copy "
+                         "of MB megabytes (the reference kernel used to scale "
+                         "rocprofv3 byte counters) and a plain read (sum)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -198,6 +233,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
+        return
     w = W.WORKLOADS[args.workload]
     tdt = torch.float16 if w.dtype == W.FP16 else torch.bfloat16
 

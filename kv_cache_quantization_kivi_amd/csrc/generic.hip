@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void generic_quant_keys_kernel(
     Params p[per];
 #pragma unroll
     for (int k = 0; k < per; ++k) {
-        p[k] = make_params(mn[k], mx[k], levels);
+        p[k] = make_params<BITS>(mn[k], mx[k]);
         if constexpr (WQ) {
             scale[(bh * NG + g) * D + d0 + k] = p[k].scale;
             zero[(bh * NG + g) * D + d0 + k] = p[k].zero;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void generic_quant_values_kernel(
             mn = fminf(mn, f);
             mx = fmaxf(mx, f);
         }
-        const Params p = make_params(mn, mx, levels);
+        const Params p = make_params<BITS>(mn, mx);
         if constexpr (WQ) {
             scale[row * NGD + j] = p.scale;
             zero[row * NGD + j] = p.zero;

@@ -54,6 +54,16 @@ __device__ __forceinline__ uint4 load16(const void* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 128-bit load: the input of a flush is read exactly once, so it
+// is marked non-temporal and does not displace reusable lines in the caches.
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+    const u32x4_t q =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(q.x, q.y, q.z, q.w);
+}
+
 __device__ __forceinline__ void words(const uint4& v, uint32_t (&w)[4]) {
     w[0] = v.x;
     w[1] = v.y;
@@ -152,28 +162,46 @@ struct MinMax8 {
 
 // Group parameters from the group's fp32 min and max.
 //   zero  = min (stored as +0 when it compares equal to 0)
-//   scale = RN(RN(max - min) / (2^bits - 1)), a correctly rounded division
+//   scale = RN(RN(max - min) / (2^bits - 1))
 //   y     = RN(1 / scale), used by the division below (0 when scale == 0)
 //   fast  = whether the reciprocal-based division is exact for this scale
+//
+// Both divisions are computed exactly without the IEEE division sequence:
+//  - x + 0.0 turns -0 into +0 and leaves every other value unchanged;
+//  - scale: the quotient by the constant L = 2^bits - 1 with Markstein's
+//    correction from c = RN(1/L): q0 = RN(range*c), r = range - q0*L (exact
+//    in one FMA), scale = RN(q0 + r*c).  Checked against IEEE division for
+//    every significand, L in {1, 3, 15, 255}, range in [2^-100, 2^101);
+//  - y: the hardware reciprocal estimate (within one ulp) plus one Newton
+//    step, y = RN(y0 + y0*(1 - scale*y0)), equals RN(1/scale) for every
+//    significand at every exponent of the fast range on gfx950; the library
+//    carries a self-test of exactly this (kivi_selftest_division).
+// Groups whose range falls outside [2^-56, 2^56] (possible only for bf16
+// inputs of extreme magnitude) are marked slow: their scale is recomputed
+// with IEEE division and their codes take the IEEE-division path.
 struct Params {
     float zero, scale, y;
     bool fast;
 };
 
-__device__ __forceinline__ Params make_params(float mn, float mx,
-                                              float levels) {
+template <int BITS>
+__device__ __forceinline__ Params make_params(float mn, float mx) {
+    constexpr float L = (float)((1 << BITS) - 1);
+    constexpr float inv_L = 1.0f / L;   // RN(1/L), folded at compile time
     Params p;
-    mn = (mn == 0.0f) ? 0.0f : mn;
-    mx = (mx == 0.0f) ? 0.0f : mx;
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
     const float range = mx - mn;
     p.zero = mn;
-    p.scale = range / levels;
-    p.y = (p.scale == 0.0f) ? 0.0f : 1.0f / p.scale;
-    // The correction step needs no underflow or overflow in its residual;
-    // any 16-bit input group keeps scale inside these bounds except bf16
-    // groups with extreme magnitudes, which take the exact division.
-    p.fast = (p.scale == 0.0f) ||
-             (p.scale >= 0x1p-64f && p.scale <= 0x1p64f);
+    const float q0 = range * inv_L;
+    const float r = __builtin_fmaf(-q0, L, range);
+    p.scale = __builtin_fmaf(r, inv_L, q0);
+    const float y0 = __builtin_amdgcn_rcpf(p.scale);
+    const float e = __builtin_fmaf(-p.scale, y0, 1.0f);
+    const float y = __builtin_fmaf(e, y0, y0);
+    p.y = (range == 0.0f) ? 0.0f : y;
+    p.fast = (range == 0.0f) || (range >= 0x1p-56f && range <= 0x1p56f);
+    if (!p.fast) p.scale = range / L;
     return p;
 }
 
@@ -206,14 +234,61 @@ __device__ __forceinline__ uint32_t code_slow(float f, const Params& p,
     return code_exact(a / p.scale, maxc);
 }
 
+// f - zero for element k of a chunk, rounded once to fp32.  For fp16 the
+// widening is folded into the subtraction: v_fma_mix_f32 reads the 16-bit
+// half selected by op_sel, and fma(h, 1.0, -zero) = RN(h - zero) exactly.
+template <int DT>
+__device__ __forceinline__ float sub_zero(const uint32_t (&w)[4], int k,
+                                          float zero) {
+    if constexpr (DT == DT_F16) {
+        float r;
+        if (k & 1)
+            asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                : "=v"(r) : "v"(w[k >> 1]), "v"(zero));
+        else
+            asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,0]"
+                : "=v"(r) : "v"(w[k >> 1]), "v"(zero));
+        return r;
+    } else {
+        return elem<DT>(w, k) - zero;
+    }
+}
+
 // The fast path.  For an element of its own group, a = RN(f - zero) lies in
 // [0, RN(max - min)], so t = RN(a / scale) lies in [0, maxc * (1 + 2^-23)]
 // and round-half-even never leaves [0, maxc]: the clip cannot bind.  Adding
 // 2^23 rounds t to an integer (ties to even) in the low mantissa bits.
-__device__ __forceinline__ uint32_t code_fast(float f, const Params& p) {
-    const float a = f - p.zero;
+// Returns the bits of t + 2^23: the code sits in the low mantissa bits and
+// every mantissa bit above it is 0 (the exponent field holds 0x4b).
+__device__ __forceinline__ uint32_t code_fast_bits(float a, const Params& p) {
     const float t = div_fast(a, p.scale, p.y);
-    return __float_as_uint(t + 0x1p23f) - 0x4b000000u;
+    return __float_as_uint(t + 0x1p23f);
+}
+
+// Pack 8 codes: m[k] has code k in its low BITS bits, zeros above it up to
+// bit 22 and garbage only from bit 23 on (bits of t + 2^23, or plain codes).
+// Shifts and ORs keep the garbage above the packed field; v_perm_b32 picks
+// bytes where it would not.
+template <int BITS>
+__device__ __forceinline__ uint64_t pack8(const uint32_t (&m)[8]) {
+    if constexpr (BITS == 1 || BITS == 2) {
+        const uint32_t n01 = (m[1] << BITS) | m[0], n23 = (m[3] << BITS) | m[2];
+        const uint32_t n45 = (m[5] << BITS) | m[4], n67 = (m[7] << BITS) | m[6];
+        const uint32_t q0 = (n23 << (2 * BITS)) | n01;
+        const uint32_t q1 = (n67 << (2 * BITS)) | n45;
+        return ((q1 << (4 * BITS)) | q0) & ((1u << (8 * BITS)) - 1u);
+    } else if constexpr (BITS == 4) {
+        const uint32_t n01 = (m[1] << 4) | m[0], n23 = (m[3] << 4) | m[2];
+        const uint32_t n45 = (m[5] << 4) | m[4], n67 = (m[7] << 4) | m[6];
+        const uint32_t p0 = (n23 << 8) | n01, p1 = (n67 << 8) | n45;
+        return __builtin_amdgcn_perm(p1, p0, 0x05040100u);
+    } else {
+        const uint32_t p01 = __builtin_amdgcn_perm(m[1], m[0], 0x0c0c0400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(m[3], m[2], 0x04000c0cu);
+        const uint32_t p45 = __builtin_amdgcn_perm(m[5], m[4], 0x0c0c0400u);
+        const uint32_t p67 = __builtin_amdgcn_perm(m[7], m[6], 0x04000c0cu);
+        return (uint64_t)(p01 | p23) | ((uint64_t)(p45 | p67) << 32);
+    }
 }
 
 // recon = RN(RN(code * scale) + zero): two roundings, never fused.
@@ -261,13 +336,18 @@ __device__ __forceinline__ uint64_t quant_chunk(const uint4& v,
     constexpr float maxc = (float)((1 << BITS) - 1);
     uint32_t w[4];
     words(v, w);
-    uint64_t packed = 0;
+    uint32_t m[8];
     float r[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const float f = elem<DT>(w, k);
-        const uint32_t c = FAST ? code_fast(f, pk[k]) : code_slow(f, pk[k], maxc);
-        packed |= (uint64_t)c << (k * BITS);
+        uint32_t c;
+        if constexpr (FAST) {
+            m[k] = code_fast_bits(sub_zero<DT>(w, k, pk[k].zero), pk[k]);
+            c = m[k] - 0x4b000000u;
+        } else {
+            c = code_slow(elem<DT>(w, k), pk[k], maxc);
+            m[k] = c;
+        }
         if constexpr (WR) r[k] = recon(c, pk[k].scale, pk[k].zero);
     }
     if constexpr (WR) {
@@ -276,7 +356,7 @@ __device__ __forceinline__ uint64_t quant_chunk(const uint4& v,
         rec->z = narrow2<DT>(r[4], r[5]);
         rec->w = narrow2<DT>(r[6], r[7]);
     }
-    return packed;
+    return pack8<BITS>(m);
 }
 
 // Dequantize one chunk of 8 packed codes.

@@ -10,6 +10,12 @@
 // The whole group (up to 32 tokens x 8 channels) stays in registers, so the
 // input is read from HBM exactly once: min/max, then codes, from the same
 // registers.
+//
+// Code stores: a lane's codes for one token are only BITS bytes, one per
+// row of the tile.  When the wave holds whole tiles (64 % (D/8) == 0) of full
+// groups, the tiles' codes form one contiguous block; the wave writes its
+// codes into LDS and stores the block with 16-byte stores instead of 2-byte
+// ones.  Other waves store directly from each lane.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -32,14 +38,15 @@ __device__ __forceinline__ void emit_full(const uint4 (&v)[GMAX],
     }
 }
 
-// The rare cases (a ragged last group, or a scale outside the fast
-// division's range): a rolled loop that reloads each token (an L2 hit), so
-// the unrolled register path above is the only large code in the kernel.
+// The rare cases (a ragged last group, a group size below the register
+// capacity, or a scale outside the fast division's range): a rolled loop
+// that reloads each token (an L2 hit), so the unrolled register path is the
+// only large code in the kernel.
 template <int DT, int BITS, bool WQ, bool WR, bool FAST>
 __device__ __forceinline__ void emit_rolled(const uint16_t* src,
-                                         const Params (&pk)[8], int32_t n,
-                                         uint8_t* dst, int64_t row_bytes,
-                                         uint16_t* rdst, int64_t D) {
+                                            const Params (&pk)[8], int32_t n,
+                                            uint8_t* dst, int64_t row_bytes,
+                                            uint16_t* rdst, int64_t D) {
 #pragma unroll 1
     for (int32_t t = 0; t < n; ++t) {
         const uint4 v = load16(src + (int64_t)t * D);
@@ -50,20 +57,38 @@ __device__ __forceinline__ void emit_rolled(const uint16_t* src,
     }
 }
 
+// LDS bytes per wave for the staged code block: tiles of GMAX rows padded
+// by up to 16 bytes each (bank spreading), at most 64 tiles.
+template <int GMAX, int BITS>
+struct KeyStage {
+    static constexpr int kWaveBytes = 64 * GMAX * BITS + 64 * 16;
+    static constexpr bool kUsed = BITS <= 4;
+};
+
 // Work item = (bh, token group g, channel chunk c), flattened with c fastest
 // so consecutive lanes take consecutive 16-byte chunks of the same rows.
+// A lane past the last item mirrors the last item's loads (in bounds) and
+// stores nothing, so every lane reaches the wave-wide steps.
 // GMAX >= group size; a ragged last group loads its last token again in the
 // missing slots, which is the pages' edge-replicate padding and leaves the
-// min/max unchanged, so the loads and the min/max carry no guards.
+// min/max unchanged, so the min/max carries no guards.
 // WQ: write codes + params.  WR: write the reconstruction (fused path).
+// stage: the host's verdict that whole waves hold whole tiles and that a
+// lane's share of the block is whole 16-byte chunks (64 % D8 == 0,
+// group == GMAX, GMAX*BITS % 16 == 0).
 template <int DT, int BITS, int GMAX, bool WQ, bool WR>
 __global__ __launch_bounds__(256) void quant_keys_kernel(
     const uint16_t* __restrict__ x, uint32_t n_items, uint32_t D8,
     uint32_t NG, int32_t S, int32_t G, uint8_t* __restrict__ codes,
     float* __restrict__ scale, float* __restrict__ zero,
-    uint16_t* __restrict__ recon) {
-    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
-    if (item >= n_items) return;
+    uint16_t* __restrict__ recon, int32_t stage) {
+    using Stage = KeyStage<GMAX, BITS>;
+    __shared__ __attribute__((aligned(16)))
+    uint8_t lds[Stage::kUsed ? 4 * Stage::kWaveBytes : 16];
+
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    const bool valid = gid < n_items;
+    const uint32_t item = valid ? gid : n_items - 1u;
     const uint32_t c = item % D8;
     const uint32_t tile = item / D8;
     const uint32_t g = tile % NG;
@@ -73,14 +98,15 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
     const int64_t D = (int64_t)D8 * 8;
     const int64_t row0 = (int64_t)bh * S + s0;
     const uint16_t* src = x + row0 * D + (int64_t)c * 8;
+    const bool full = nt == GMAX;
 
     uint4 v[GMAX];
-    if (nt == GMAX) {
+    if (full) {
 #pragma unroll
-        for (int t = 0; t < GMAX; ++t) v[t] = load16(src + t * D);
+        for (int t = 0; t < GMAX; ++t) v[t] = load16_nt(src + t * D);
     } else {
 #pragma unroll
-        for (int t = 0; t < GMAX; ++t) v[t] = load16(src + min(t, nt - 1) * D);
+        for (int t = 0; t < GMAX; ++t) v[t] = load16_nt(src + min(t, nt - 1) * D);
     }
 
     MinMax8<DT> mm;
@@ -90,16 +116,15 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
     float lo[8], hi[8];
     mm.get(lo, hi);
 
-    constexpr float levels = (float)((1 << BITS) - 1);
     Params pk[8];
     bool fast = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        pk[k] = make_params(lo[k], hi[k], levels);
+        pk[k] = make_params<BITS>(lo[k], hi[k]);
         fast = fast && pk[k].fast;
     }
 
-    if constexpr (WQ) {
+    if (WQ && valid) {
         const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
         float4* ps = reinterpret_cast<float4*>(scale + p);
         float4* pz = reinterpret_cast<float4*>(zero + p);
@@ -112,7 +137,52 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
     const int64_t row_bytes = (int64_t)D8 * BITS;   // D * BITS / 8
     uint8_t* dst = WQ ? codes + row0 * row_bytes + (int64_t)c * BITS : nullptr;
     uint16_t* rdst = WR ? recon + row0 * D + (int64_t)c * 8 : nullptr;
-    if (fast && nt == GMAX)
+
+    if constexpr (WQ && Stage::kUsed) {
+        // Wave-uniform choice: every lane valid, full and fast.
+        if (stage && __all(valid && full && fast)) {
+            const uint32_t lane = threadIdx.x & 63u;
+            uint8_t* L = lds + (threadIdx.x >> 6) * Stage::kWaveBytes;
+            const uint32_t tile_bytes = GMAX * D8 * BITS;
+            const uint32_t pad = (D8 * BITS + 15u) & ~15u;
+            const uint32_t ts = tile_bytes + pad;   // padded tile stride
+            uint8_t* mine = L + (lane / D8) * ts + c * BITS;
+#pragma unroll
+            for (int t = 0; t < GMAX; ++t) {
+                uint4 r;
+                const uint64_t q = quant_chunk<DT, BITS, true, WR>(v[t], pk, &r);
+                if constexpr (BITS == 1) mine[t * row_bytes] = (uint8_t)q;
+                else if constexpr (BITS == 2)
+                    *reinterpret_cast<uint16_t*>(mine + t * row_bytes) = (uint16_t)q;
+                else
+                    *reinterpret_cast<uint32_t*>(mine + t * row_bytes) = (uint32_t)q;
+                if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Lane 0 holds chunk 0 of the wave's first tile; the wave's
+            // tiles are consecutive token groups, i.e. consecutive rows.
+            const uint32_t b_lo = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)row0 & 0xffffffffu));
+            const uint32_t b_hi = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)row0 >> 32));
+            const int64_t wrow0 = (int64_t)(((uint64_t)b_hi << 32) | b_lo);
+            uint8_t* wdst = codes + wrow0 * row_bytes;
+            constexpr int kChunks = GMAX * BITS / 16;   // 16-byte chunks per lane
+#pragma unroll
+            for (int k = 0; k < kChunks; ++k) {
+                const uint32_t off = (k * 64u + lane) * 16u;   // in the block
+                const uint32_t t_idx = off / tile_bytes;
+                const uint4 q = *reinterpret_cast<const uint4*>(
+                    L + t_idx * ts + (off - t_idx * tile_bytes));
+                *reinterpret_cast<uint4*>(wdst + off) = q;
+            }
+            return;
+        }
+    }
+    if (!valid) return;
+    if (fast && full)
         emit_full<DT, BITS, WQ, WR, GMAX>(v, pk, dst, row_bytes, rdst, D);
     else if (fast)
         emit_rolled<DT, BITS, WQ, WR, true>(src, pk, nt, dst, row_bytes, rdst, D);
@@ -126,11 +196,14 @@ static hipError_t launch_keys_t(const QuantJob& j) {
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_items = (uint64_t)j.BH * NG * D8;
     const uint32_t blocks = (uint32_t)((n_items + 255) / 256);
-    hipLaunchKernelGGL((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>), dim3(blocks),
-                       dim3(256), 0, j.stream,
-                       static_cast<const uint16_t*>(j.x), (uint32_t)n_items, D8,
-                       NG, (int32_t)j.S, (int32_t)j.group, j.codes, j.scale,
-                       j.zero, static_cast<uint16_t*>(j.recon));
+    const int32_t stage = KeyStage<GMAX, BITS>::kUsed && WQ && 64 % D8 == 0 &&
+                          j.group == GMAX && (GMAX * BITS) % 16 == 0;
+    hipLaunchKernelGGL((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>),
+                       dim3(blocks), dim3(256), 0, j.stream,
+                       static_cast<const uint16_t*>(j.x), (uint32_t)n_items,
+                       D8, NG, (int32_t)j.S, (int32_t)j.group, j.codes,
+                       j.scale, j.zero, static_cast<uint16_t*>(j.recon),
+                       stage);
     return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
     for (int i = 0; i < kValRows; ++i) {
         const int64_t row = row_base + (int64_t)i * rpp;
         valid[i] = cvalid && row < n_rows;
-        v[i] = valid[i] ? load16(x + row * D + (int64_t)c * 8)
+        v[i] = valid[i] ? load16_nt(x + row * D + (int64_t)c * 8)
                         : make_uint4(0, 0, 0, 0);
     }
 
@@ -117,14 +117,13 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
 #pragma unroll
     for (int i = 0; i < kValRows; ++i) block_minmax(mn[i], mx[i], red);
 
-    constexpr float levels = (float)((1 << BITS) - 1);
     const int64_t row_bytes = (int64_t)D8 * BITS;
     const bool writes_params = (c & ((1u << lcpg) - 1u)) == 0;
 #pragma unroll
     for (int i = 0; i < kValRows; ++i) {
         if (!valid[i]) continue;
         const int64_t row = row_base + (int64_t)i * rpp;
-        Params p = make_params(mn[i], mx[i], levels);
+        Params p = make_params<BITS>(mn[i], mx[i]);
         if constexpr (WQ) {
             if (writes_params) {
                 const int64_t pi = row * NGD + (c >> lcpg);
