@@ -9,10 +9,12 @@ round trip, BH = 32 x 8 KV heads, S = 4096, D = 128, fp16, 2-bit, groups of
 
 value = algorithmic bytes of the step (each input read once, each output
 written once) / measured step time, with inputs resident in HBM; inputs
-rotate over a pool of distinct tensors larger than the 256 MB MALL so no
-step is served from cache.  Per-kernel durations come from HIP events
-recorded on the launch stream inside the timed region; the dominant kernel's
-achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
+rotate over a pool of distinct tensors larger than the 256 MB MALL, and the
+dequantizers read codes written two steps earlier (see make_steps), so no
+kernel's input is served from a cache.  Per-kernel durations come from HIP events
+recorded at each kernel's own dispatch start and end (hipExtLaunchKernel,
+armed through kivi_time_next_launch) inside the timed region; the dominant
+kernel's achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
 baseline is the plain C oracle (single thread) timed on a bounded sample of
 the same workload.
 
@@ -76,15 +78,30 @@ def load_traffic(kernel, workload, src_hash):
     return ent.get("hbm_bytes_per_launch")
 
 
+N_CODE_SETS = 4   # rotating code/param sets (see make_steps)
+
+
 def make_steps(K, w, pool_inputs, torch):
     """Pre-allocated outputs and the list of (name, op, bytes, launch fn)
-    that make one step.  Every launch goes to torch's current stream."""
+    that make one step.  Every launch goes to torch's current stream and
+    takes the step index i.
+
+    Cache hygiene, so that every input byte of every kernel comes from HBM:
+    the quantizers of step i read input set i % P and write code/param set
+    (i + 2) % 4; the fused kernels read the other input set (i + 1) % P; the
+    dequantizers read code set i % 4, written two steps (over 0.5 GB of
+    plain stores) earlier, after the MALL (256 MB) has turned over.  Without
+    this a dequantizer would read codes written microseconds before and
+    still resident in the memory-side cache.
+    """
     E = w.elems
     dev = pool_inputs[0][0].device
+    P = len(pool_inputs)
     bits, gk, gv = w.bits, w.group_k, w.group_v
     NG = (w.S + gk - 1) // gk
     NGD = (w.D + gv - 1) // gv
     shp = (w.BH, w.S, w.D)
+    dt = pool_inputs[0][0].dtype
 
     def qbufs(keys):
         c = torch.empty((w.BH, w.S, w.D * bits // 8), dtype=torch.uint8,
@@ -93,34 +110,45 @@ def make_steps(K, w, pool_inputs, torch):
         return (c, torch.empty(p, dtype=torch.float32, device=dev),
                 torch.empty(p, dtype=torch.float32, device=dev))
 
-    qk, qv = qbufs(True), qbufs(False)
+    qk = [qbufs(True) for _ in range(N_CODE_SETS)]
+    qv = [qbufs(False) for _ in range(N_CODE_SETS)]
+    for s in range(N_CODE_SETS):   # every set holds real codes before timing
+        K.kivi_quant_keys(pool_inputs[s % P][0], bits, gk, *qk[s])
+        K.kivi_quant_values(pool_inputs[s % P][1], bits, gv, *qv[s])
     fk, fv = qbufs(True), qbufs(False)
-    dt = pool_inputs[0][0].dtype
     dk = torch.empty(shp, dtype=dt, device=dev)
     dv = torch.empty(shp, dtype=dt, device=dev)
     rk = torch.empty(shp, dtype=dt, device=dev)
     rv = torch.empty(shp, dtype=dt, device=dev)
 
+    def ws(i):
+        return (i + 2) % N_CODE_SETS
+
+    def rs(i):
+        return i % N_CODE_SETS
+
     steps = [
         ("quant_keys", "quant", gk,
-         lambda kv: K.kivi_quant_keys(kv[0], bits, gk, *qk)),
+         lambda i: K.kivi_quant_keys(pool_inputs[i % P][0], bits, gk,
+                                     *qk[ws(i)])),
         ("quant_values", "quant", gv,
-         lambda kv: K.kivi_quant_values(kv[1], bits, gv, *qv)),
+         lambda i: K.kivi_quant_values(pool_inputs[i % P][1], bits, gv,
+                                       *qv[ws(i)])),
     ]
     if w.name in ("tiny", "decode", "roundtrip"):
         steps += [
-            ("dequant_keys", "dequant", gk,
-             lambda kv: K.kivi_dequant_keys(*qk, bits, gk, out_dtype=dt,
-                                            out=dk)),
-            ("dequant_values", "dequant", gv,
-             lambda kv: K.kivi_dequant_values(*qv, bits, gv, out_dtype=dt,
-                                              out=dv)),
             ("quant_dequant_keys", "fused", gk,
-             lambda kv: K.kivi_quant_dequant_keys(kv[0], bits, gk, True, rk,
-                                                  *fk)),
+             lambda i: K.kivi_quant_dequant_keys(
+                 pool_inputs[(i + 1) % P][0], bits, gk, True, rk, *fk)),
             ("quant_dequant_values", "fused", gv,
-             lambda kv: K.kivi_quant_dequant_values(kv[1], bits, gv, True,
-                                                    rv, *fv)),
+             lambda i: K.kivi_quant_dequant_values(
+                 pool_inputs[(i + 1) % P][1], bits, gv, True, rv, *fv)),
+            ("dequant_keys", "dequant", gk,
+             lambda i: K.kivi_dequant_keys(*qk[rs(i)], bits, gk, out_dtype=dt,
+                                           out=dk)),
+            ("dequant_values", "dequant", gv,
+             lambda i: K.kivi_dequant_values(*qv[rs(i)], bits, gv,
+                                             out_dtype=dt, out=dv)),
         ]
     out = []
     for name, op, g, fn in steps:
@@ -241,6 +269,8 @@ def main():
 
     in_bytes = 2 * w.elems * 2
     pool = args.pool or max(2, int(np.ceil(1.0e9 / in_bytes)))
+    if pool % 2:
+        pool += 1   # fused kernels read the set the quantizers do not
     pool = min(pool, 64)
     inputs = []
     for p in range(pool):
@@ -256,24 +286,30 @@ def main():
 
     for i in range(args.warmup):
         for _, _, _, fn in steps:
-            fn(inputs[i % pool])
+            fn(i)
     torch.cuda.synchronize()
 
+    # Per-kernel durations: every launch of the timed region records its own
+    # start/stop event pair at dispatch (kivi_time_next_launch), so the
+    # durations exclude the dispatch gaps between kernels; the step time is
+    # taken between two events around the whole region and includes them.
     n_k = len(steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k + 1)]
+    kev = [[(torch.cuda.Event(enable_timing=True),
+             torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
            for _ in range(args.steps)]
+    for row in kev:              # torch creates its events on first record
+        for a, b in row:
+            a.record(stream)
+            b.record(stream)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        e = evs[i]
-        kv = inputs[i % pool]
-        e[0].record(stream)
         for j, (_, _, _, fn) in enumerate(steps):
-            fn(kv)
-            e[j + 1].record(stream)
+            K.kivi_time_next_launch(*kev[i][j])
+            fn(args.warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -282,7 +318,7 @@ def main():
 
     per_kernel = {}
     for j, (name, op, b, _) in enumerate(steps):
-        d = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+        d = [kev[i][j][0].elapsed_time(kev[i][j][1]) for i in range(args.steps)]
         avg = float(np.mean(d))
         per_kernel[name] = {
             "avg_us": round(avg * 1e3, 3),

@@ -29,7 +29,8 @@
  *
  * Ownership and execution: every pointer is caller-owned device memory
  * (e.g. allocated by PyTorch); the library never allocates, frees or
- * synchronises and keeps no state between calls; calls are re-entrant.
+ * synchronises and keeps no state between calls (apart from the per-thread
+ * profiling events of kivi_time_next_launch); calls are re-entrant.
  * Work is enqueued on `stream` (0 = the null stream) and runs
  * asynchronously; outputs are valid once the stream has reached the call.
  * Inputs and outputs must not overlap.
@@ -139,6 +140,34 @@ kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
                                       int bits, int64_t group, uint8_t* codes,
                                       float* scale, float* zero, void* recon,
                                       hipStream_t stream);
+
+/*
+ * Profiling aid: the next kernel that a kivi_* call made by this thread
+ * launches records `start` when it begins executing and `stop` when it ends
+ * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is that kernel's
+ * duration alone, without the dispatch gap that events recorded between
+ * launches include.  Both events must be created by the caller (e.g.
+ * hipEventCreate) and outlive the launch.  The pair is consumed by the next
+ * launch (every compute call launches exactly one kernel; calls that launch
+ * nothing -- errors, empty tensors -- leave it armed); passing NULL for
+ * either disarms it.  This thread-local pair is the library's only state.
+ */
+void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
+/*
+ * Self-test of the division shortcuts the quantizers use on this GPU.  The
+ * pages prescribe IEEE division for the scale and for every code's quotient
+ * (section "What we're actually optimizing": subtract, divide, round, clip);
+ * the kernels reach the same correctly rounded results with (1) Markstein's
+ * quotient by the constant 2^bits - 1 and (2) the hardware reciprocal
+ * refined by one Newton step.  This call checks both against IEEE division
+ * for every significand at every exponent where the kernels use them, and
+ * adds the number of mismatches to *mismatches (one device-memory
+ * unsigned long long, 8-byte aligned, zeroed by the caller).  Zero
+ * mismatches is what every quantizer result relies on.
+ */
+kivi_status kivi_selftest_division(unsigned long long* mismatches,
+                                   hipStream_t stream);
 
 /* Sizes: bytes of packed codes, and element counts of each params array
  * (scale and zero each), for a [BH, S, D] tensor.  Return -1 on invalid

@@ -68,6 +68,10 @@ def _load():
                  "kivi_quant_dequant_keys", "kivi_quant_dequant_values",
                  "kivi_dequant_keys", "kivi_dequant_values"):
         getattr(L, name).restype = I
+    L.kivi_time_next_launch.argtypes = [P, P]
+    L.kivi_time_next_launch.restype = None
+    L.kivi_selftest_division.argtypes = [P, P]
+    L.kivi_selftest_division.restype = I
     L.kivi_codes_bytes.argtypes = [I64, I64, I64, I]
     L.kivi_codes_bytes.restype = I64
     L.kivi_key_param_count.argtypes = [I64, I64, I64, I64]
@@ -240,6 +244,28 @@ def kivi_dequant_values(codes, scale, zero, bits=2, group=32,
     """Value dequantization -> [..., S, D] of out_dtype."""
     return _dequant("kivi_dequant_values", False, codes, scale, zero, bits,
                     group, out_dtype, out, stream)
+
+
+def kivi_time_next_launch(start, stop):
+    """Arm a pair of recorded torch.cuda.Event objects (or raw hipEvent_t
+    handles) to time the next kernel this thread launches through the
+    library; None disarms."""
+    def h(e):
+        if e is None:
+            return None
+        return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event")
+                               else int(e))
+    _C.kivi_time_next_launch(h(start), h(stop))
+
+
+def kivi_selftest_division(device="cuda", stream=None):
+    """Number of mismatches of the kernels' exact division shortcuts
+    against IEEE division on this GPU (0 is required)."""
+    dev = torch.device(device)
+    cnt = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = _C.kivi_selftest_division(_ptr(cnt), _stream(dev, stream))
+    _check(st, "kivi_selftest_division")
+    return int(cnt.item())
 
 
 def kivi_codes_bytes(BH, S, D, bits):

@@ -3,27 +3,70 @@
 // fused Metal kernels, section "What we're actually optimizing", and "Three
 // ways to be off by one bit", item 1: the product is rounded before the add).
 //
+// Both kernels move whole 16-byte pieces with non-temporal accesses: the
+// codes and params are read once and the reconstruction is written once, so
+// none of it should displace reusable lines or linger as dirty lines for the
+// next kernel to evict.  Where the natural per-lane access would be narrow
+// or strided, a wave moves its contiguous block through LDS instead.
+//
 // Keys: one lane owns an 8-channel chunk of one (bh, token group) tile, so
 // its 8 scales and 8 zeros are loaded once (four 128-bit loads) and reused
-// for every token of the group; each token then costs one BITS-byte code
-// load and one 128-bit store.
-// Values: one lane owns an 8-channel chunk of one row; the chunk lies in one
-// group (group % 8 == 0), so it needs one scale and one zero.
+// for every token of the group.  A lane's codes are BITS bytes per token
+// (one per row); when the wave holds whole tiles of full groups, the tiles'
+// codes are one contiguous block that the wave reads with 16-byte loads into
+// LDS, and each lane then picks its codes from LDS.
+// Values: one lane owns 32 consecutive channels of a row (as in the value
+// quantizer): one 4*BITS-byte code load, one (scale, zero) per group it
+// touches, and 64 bytes of recon, which go out through LDS as 1 KiB
+// contiguous stores when rows tile the lanes exactly.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
 namespace kivi {
 
-constexpr int kDqTokUnroll = 8;   // code loads in flight per lane (keys)
-constexpr int kDqValItems = 4;    // chunks per lane (values)
+constexpr int kDqTokUnroll = 8;   // tokens per step of the keys' token loop
 
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float4 load_f4_nt(const float* p) {
+    const u32x4_t q =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_float4(__uint_as_float(q.x), __uint_as_float(q.y),
+                       __uint_as_float(q.z), __uint_as_float(q.w));
+}
+
+// Codes of one token of a chunk from LDS (BITS bytes).
+template <int BITS>
+__device__ __forceinline__ uint64_t lds_codes(const uint8_t* p) {
+    if constexpr (BITS == 1) return *p;
+    else if constexpr (BITS == 2) return *reinterpret_cast<const uint16_t*>(p);
+    else return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// Staged key codes: at most 32 tokens per group and BITS <= 4, so a wave's
+// block is at most 64 * 32 * 4 bytes (plus up to 16 bytes of padding per
+// tile, at most 64 tiles).
+constexpr int kDqKeyWaveBytes = 64 * 32 * 4 + 64 * 16;
+
+// stage: the host's verdict that a wave of full tiles has one contiguous
+// code block of whole 16-byte pieces per lane (64 % D8 == 0, group <= 32,
+// group * BITS % 16 == 0, BITS <= 4).
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void dequant_keys_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
     const float* __restrict__ zero, uint32_t n_items, uint32_t D8,
-    uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out) {
-    const uint32_t item = blockIdx.x * 256u + threadIdx.x;
-    if (item >= n_items) return;
+    uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out,
+    int32_t stage) {
+    __shared__ __attribute__((aligned(16)))
+    uint8_t lds[BITS <= 4 ? 4 * kDqKeyWaveBytes : 16];
+
+    const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+    const bool valid = gid < n_items;
+    const uint32_t item = valid ? gid : n_items - 1u;
     const uint32_t c = item % D8;
     const uint32_t tile = item / D8;
     const uint32_t g = tile % NG;
@@ -34,16 +77,54 @@ __global__ __launch_bounds__(256) void dequant_keys_kernel(
     const int64_t row0 = (int64_t)bh * S + s0;
 
     const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
-    const float4 s_a = reinterpret_cast<const float4*>(scale + p)[0];
-    const float4 s_b = reinterpret_cast<const float4*>(scale + p)[1];
-    const float4 z_a = reinterpret_cast<const float4*>(zero + p)[0];
-    const float4 z_b = reinterpret_cast<const float4*>(zero + p)[1];
+    const float4 s_a = load_f4_nt(scale + p);
+    const float4 s_b = load_f4_nt(scale + p + 4);
+    const float4 z_a = load_f4_nt(zero + p);
+    const float4 z_b = load_f4_nt(zero + p + 4);
     const float sc[8] = {s_a.x, s_a.y, s_a.z, s_a.w, s_b.x, s_b.y, s_b.z, s_b.w};
     const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
 
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    const uint8_t* src = codes + row0 * row_bytes + (int64_t)c * BITS;
     uint16_t* dst = out + row0 * D + (int64_t)c * 8;
+
+    if constexpr (BITS <= 4) {
+        if (stage && __all(valid && nt == G)) {
+            const uint32_t lane = threadIdx.x & 63u;
+            uint8_t* L = lds + (threadIdx.x >> 6) * kDqKeyWaveBytes;
+            const uint32_t tile_bytes = (uint32_t)G * D8 * BITS;
+            const uint32_t ts = tile_bytes + ((D8 * BITS + 15u) & ~15u);
+            // Lane 0 holds chunk 0 of the wave's first tile; the wave's
+            // tiles are consecutive token groups, i.e. consecutive rows.
+            const uint32_t b_lo = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)row0 & 0xffffffffu));
+            const uint32_t b_hi = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)row0 >> 32));
+            const uint8_t* wsrc =
+                codes + (int64_t)(((uint64_t)b_hi << 32) | b_lo) * row_bytes;
+            const uint32_t n16 = (uint32_t)G * BITS / 16;   // pieces per lane
+            uint4 t4[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k)
+                if (k < n16) t4[k] = load16_nt(wsrc + (k * 64u + lane) * 16u);
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) {
+                if (k < n16) {
+                    const uint32_t off = (k * 64u + lane) * 16u;
+                    const uint32_t ti = off / tile_bytes;
+                    *reinterpret_cast<uint4*>(L + ti * ts + (off - ti * tile_bytes)) = t4[k];
+                }
+            }
+            lds_sync();
+            const uint8_t* mine = L + (lane / D8) * ts + c * BITS;
+#pragma unroll kDqTokUnroll
+            for (int32_t t = 0; t < G; ++t)
+                store16_nt(dst + (int64_t)t * D,
+                           dequant_chunk<DT, BITS>(lds_codes<BITS>(mine + t * row_bytes), sc, z));
+            return;
+        }
+    }
+    if (!valid) return;
+    const uint8_t* src = codes + row0 * row_bytes + (int64_t)c * BITS;
     for (int32_t t0 = 0; t0 < nt; t0 += kDqTokUnroll) {
         uint64_t q[kDqTokUnroll];
 #pragma unroll
@@ -52,45 +133,116 @@ __global__ __launch_bounds__(256) void dequant_keys_kernel(
 #pragma unroll
         for (int u = 0; u < kDqTokUnroll; ++u)
             if (t0 + u < nt)
-                *reinterpret_cast<uint4*>(dst + (int64_t)(t0 + u) * D) =
-                    dequant_chunk<DT, BITS>(q[u], sc, z);
+                store16_nt(dst + (int64_t)(t0 + u) * D,
+                           dequant_chunk<DT, BITS>(q[u], sc, z));
     }
 }
 
-template <int DT, int BITS>
+// Recon staging layout, as in the value quantizer: chunk j of a wave's
+// 4 KiB block at LDS byte (j + j/4) * 16 (lane stride 80 bytes).
+constexpr int kDqRecLaneStride = 80;
+constexpr int kDqRecWaveBytes = 64 * kDqRecLaneStride;
+
+// GPL: groups per lane (4: G = 8, 2: G = 16, 1: G a multiple of 32, so a
+// lane's 4 chunks, which start at a multiple of 4 chunks, share one group).
+// lp: log2 of lanes per row P; vec: D % 32 == 0 (a lane's codes are one
+// naturally aligned load); tile: D / 32 is a power of two (a wave's recon is
+// one contiguous 4 KiB block).
+template <int DT, int BITS, int GPL>
 __global__ __launch_bounds__(256) void dequant_values_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-    const float* __restrict__ zero, uint64_t n_items, uint32_t D8,
-    uint32_t G8, uint32_t NGD, uint16_t* __restrict__ out) {
-    // Items (row, chunk) with the chunk fastest; a block covers
-    // kDqValItems * 256 consecutive items, 256 per step, so each wave-wide
-    // load and store is contiguous.
-    const uint64_t base = (uint64_t)blockIdx.x * (256u * kDqValItems) +
-                          threadIdx.x;
-    uint64_t q[kDqValItems];
-    float sc[kDqValItems], z[kDqValItems];
+    const float* __restrict__ zero, int64_t n_rows, uint32_t D8, uint32_t lp,
+    uint32_t G8, uint32_t NGD, int32_t vec, int32_t tile,
+    uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDqRecWaveBytes];
+    const uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+    const uint32_t c = (uint32_t)(u & ((1u << lp) - 1u));
+    const int64_t row = (int64_t)(u >> lp);
+    const bool row_ok = row < n_rows;
+    const int32_t ch0 = (int32_t)c * 4;
+    const int32_t nch = min(4, (int32_t)D8 - ch0);
+    const bool staged = tile && __all(row_ok);
+    if (!staged && (!row_ok || nch <= 0)) return;
+
+    const int64_t row_bytes = (int64_t)D8 * BITS;
+    const uint8_t* csrc = codes + row * row_bytes + (int64_t)ch0 * BITS;
+    uint64_t q[4];
+    if (vec && nch == 4) {
+        if constexpr (BITS == 1) {
+            const uint32_t w = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t*>(csrc));
 #pragma unroll
-    for (int i = 0; i < kDqValItems; ++i) {
-        const uint64_t item = base + (uint64_t)i * 256u;
-        if (item < n_items) {
-            const uint64_t row = item / D8;
-            const uint32_t c = (uint32_t)(item - row * D8);
-            q[i] = load_codes<BITS>(codes + item * BITS);
-            const uint64_t pi = row * NGD + c / G8;
-            sc[i] = scale[pi];
-            z[i] = zero[pi];
+            for (int k = 0; k < 4; ++k) q[k] = (w >> (8 * k)) & 0xffu;
+        } else if constexpr (BITS == 2) {
+            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t w = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x2_t*>(csrc));
+            q[0] = w.x & 0xffffu;
+            q[1] = w.x >> 16;
+            q[2] = w.y & 0xffffu;
+            q[3] = w.y >> 16;
+        } else if constexpr (BITS == 4) {
+            const uint4 w = load16_nt(csrc);
+            q[0] = w.x;
+            q[1] = w.y;
+            q[2] = w.z;
+            q[3] = w.w;
+        } else {
+            const uint4 a = load16_nt(csrc);
+            const uint4 b = load16_nt(csrc + 16);
+            q[0] = (uint64_t)a.x | ((uint64_t)a.y << 32);
+            q[1] = (uint64_t)a.z | ((uint64_t)a.w << 32);
+            q[2] = (uint64_t)b.x | ((uint64_t)b.y << 32);
+            q[3] = (uint64_t)b.z | ((uint64_t)b.w << 32);
         }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            q[k] = k < nch ? load_codes<BITS>(csrc + k * BITS) : 0;
     }
+
+    // Params: in-lane group t starts at chunk ch0 + t*CPG and lies in row
+    // group (ch0 + t*CPG) / G8; a group past the row's end reads the lane's
+    // first group instead (its result is never stored).
+    constexpr int CPG = 4 / GPL;
+    float gs[GPL], gz[GPL];
 #pragma unroll
-    for (int i = 0; i < kDqValItems; ++i) {
-        const uint64_t item = base + (uint64_t)i * 256u;
-        if (item < n_items) {
-            const float s8[8] = {sc[i], sc[i], sc[i], sc[i],
-                                 sc[i], sc[i], sc[i], sc[i]};
-            const float z8[8] = {z[i], z[i], z[i], z[i], z[i], z[i], z[i], z[i]};
-            *reinterpret_cast<uint4*>(out + item * 8) =
-                dequant_chunk<DT, BITS>(q[i], s8, z8);
+    for (int t = 0; t < GPL; ++t) {
+        const int32_t ch = ch0 + t * CPG;
+        const int64_t pi =
+            row * NGD + (uint32_t)(ch < (int32_t)D8 ? ch : ch0) / G8;
+        gs[t] = __builtin_nontemporal_load(scale + pi);
+        gz[t] = __builtin_nontemporal_load(zero + pi);
+    }
+
+    uint4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float s = gs[k / CPG], zz = gz[k / CPG];
+        const float s8[8] = {s, s, s, s, s, s, s, s};
+        const float z8[8] = {zz, zz, zz, zz, zz, zz, zz, zz};
+        r[k] = dequant_chunk<DT, BITS>(q[k], s8, z8);
+    }
+
+    if (staged) {
+        const uint32_t lane = threadIdx.x & 63u;
+        uint8_t* L = lds + (threadIdx.x >> 6) * kDqRecWaveBytes;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            *reinterpret_cast<uint4*>(L + lane * kDqRecLaneStride + k * 16) = r[k];
+        lds_sync();
+        uint8_t* wdst = reinterpret_cast<uint8_t*>(out + (u - lane) * 32);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t off = k * 1024u + lane * 16u;
+            store16_nt(wdst + off, *reinterpret_cast<const uint4*>(
+                                       L + (off >> 6) * kDqRecLaneStride + (off & 63u)));
         }
+    } else {
+        uint16_t* dst = out + row * ((int64_t)D8 * 8) + (int64_t)ch0 * 8;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < nch) store16_nt(dst + k * 8, r[k]);
     }
 }
 
@@ -100,25 +252,36 @@ static hipError_t launch_dq_keys_t(const DequantJob& j) {
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_items = (uint64_t)j.BH * NG * D8;
     const uint32_t blocks = (uint32_t)((n_items + 255) / 256);
-    hipLaunchKernelGGL((dequant_keys_kernel<DT, BITS>), dim3(blocks),
+    const int32_t stage = BITS <= 4 && 64 % D8 == 0 && j.group <= 32 &&
+                          (j.group * BITS) % 16 == 0;
+    return launch_kernel((dequant_keys_kernel<DT, BITS>), dim3(blocks),
                        dim3(256), 0, j.stream, j.codes, j.scale, j.zero,
                        (uint32_t)n_items, D8, NG, (int32_t)j.S,
-                       (int32_t)j.group, static_cast<uint16_t*>(j.out));
-    return hipGetLastError();
+                       (int32_t)j.group, static_cast<uint16_t*>(j.out), stage);
+}
+
+template <int DT, int BITS, int GPL>
+static hipError_t launch_dq_values_gpl(const DequantJob& j) {
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
+    const int64_t n_rows = j.BH * j.S;
+    const uint64_t lanes = (uint64_t)n_rows << lp;
+    const uint32_t blocks = (uint32_t)((lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const int32_t tile = vec && (1u << lp) == lpr;
+    return launch_kernel((dequant_values_kernel<DT, BITS, GPL>), dim3(blocks),
+                       dim3(256), 0, j.stream, j.codes, j.scale, j.zero,
+                       n_rows, D8, lp, (uint32_t)(j.group / 8), NGD, vec, tile,
+                       static_cast<uint16_t*>(j.out));
 }
 
 template <int DT, int BITS>
 static hipError_t launch_dq_values_t(const DequantJob& j) {
-    const uint32_t D8 = (uint32_t)(j.D / 8);
-    const uint64_t n_items = (uint64_t)j.BH * j.S * D8;
-    const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
-    const uint64_t per_block = 256u * kDqValItems;
-    const uint32_t blocks = (uint32_t)((n_items + per_block - 1) / per_block);
-    hipLaunchKernelGGL((dequant_values_kernel<DT, BITS>), dim3(blocks),
-                       dim3(256), 0, j.stream, j.codes, j.scale, j.zero,
-                       n_items, D8, (uint32_t)(j.group / 8), NGD,
-                       static_cast<uint16_t*>(j.out));
-    return hipGetLastError();
+    if (j.group == 8) return launch_dq_values_gpl<DT, BITS, 4>(j);
+    if (j.group == 16) return launch_dq_values_gpl<DT, BITS, 2>(j);
+    return launch_dq_values_gpl<DT, BITS, 1>(j);
 }
 
 #define KIVI_DISPATCH_DQ(NAME, J)                                       \
@@ -149,7 +312,11 @@ hipError_t launch_dequant_keys(const DequantJob& j) {
 }
 
 hipError_t launch_dequant_values(const DequantJob& j) {
-    if (j.D % 8 != 0 || j.group % 8 != 0) return launch_generic_dequant(j, false);
+    // A lane's chunks map onto whole groups (group 8, 16 or a multiple of
+    // 32); rows of at most 64 lanes (D <= 2048).
+    const bool grp_ok = j.group == 8 || j.group == 16 || j.group % 32 == 0;
+    if (j.D % 8 != 0 || !grp_ok || j.D > 2048 || j.BH * j.S >= (1ll << 40))
+        return launch_generic_dequant(j, false);
     KIVI_DISPATCH_DQ(launch_dq_values_t, j);
 }
 

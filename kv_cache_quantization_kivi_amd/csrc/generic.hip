@@ -152,24 +152,22 @@ static hipError_t gk_t(const QuantJob& j) {
     constexpr int per = 8 / BITS;
     const int64_t NG = (j.S + j.group - 1) / j.group;
     const uint64_t n = (uint64_t)j.BH * NG * (j.D / per);
-    hipLaunchKernelGGL((generic_quant_keys_kernel<DT, BITS, WQ, WR>),
+    return launch_kernel((generic_quant_keys_kernel<DT, BITS, WQ, WR>),
                        dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
                        j.stream, static_cast<const uint16_t*>(j.x), n, j.S,
                        j.D, j.group, NG, j.codes, j.scale, j.zero,
                        static_cast<uint16_t*>(j.recon));
-    return hipGetLastError();
 }
 
 template <int DT, int BITS, bool WQ, bool WR>
 static hipError_t gv_t(const QuantJob& j) {
     const int64_t NGD = (j.D + j.group - 1) / j.group;
     const int64_t n = j.BH * j.S;
-    hipLaunchKernelGGL((generic_quant_values_kernel<DT, BITS, WQ, WR>),
+    return launch_kernel((generic_quant_values_kernel<DT, BITS, WQ, WR>),
                        dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
                        j.stream, static_cast<const uint16_t*>(j.x), n, j.D,
                        j.group, NGD, j.codes, j.scale, j.zero,
                        static_cast<uint16_t*>(j.recon));
-    return hipGetLastError();
 }
 
 template <int DT, int BITS>
@@ -177,12 +175,11 @@ static hipError_t gdq_t(const DequantJob& j, bool keys) {
     const uint64_t n = (uint64_t)j.BH * j.S * j.D;
     const int64_t NG = (j.S + j.group - 1) / j.group;
     const int64_t NGD = (j.D + j.group - 1) / j.group;
-    hipLaunchKernelGGL((generic_dequant_kernel<DT, BITS>),
+    return launch_kernel((generic_dequant_kernel<DT, BITS>),
                        dim3((uint32_t)((n + 255) / 256)), dim3(256), 0,
                        j.stream, j.codes, j.scale, j.zero, n, j.S, j.D,
                        j.group, NG, NGD, keys ? 1 : 0,
                        static_cast<uint16_t*>(j.out));
-    return hipGetLastError();
 }
 
 template <int DT, int BITS>

@@ -7,6 +7,22 @@
 
 #include "kivi_launch.h"
 
+namespace kivi {
+
+namespace {
+thread_local hipEvent_t g_start = nullptr;
+thread_local hipEvent_t g_stop = nullptr;
+}  // namespace
+
+void take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+    *start = g_start;
+    *stop = g_stop;
+    g_start = nullptr;
+    g_stop = nullptr;
+}
+
+}  // namespace kivi
+
 namespace {
 
 bool bits_ok(int bits) {
@@ -152,6 +168,19 @@ kivi_status kivi_dequant_values(const uint8_t* codes, const float* scale,
                                 hipStream_t stream) {
     return dequant(false, codes, scale, zero, BH, S, D, bits, group, out_dt,
                    out, stream);
+}
+
+void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+    kivi::g_start = start;
+    kivi::g_stop = stop;
+}
+
+kivi_status kivi_selftest_division(unsigned long long* mismatches,
+                                   hipStream_t stream) {
+    if (mismatches == nullptr) return KIVI_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(mismatches) & 7u) != 0)
+        return KIVI_ERR_ALIGN;
+    return launched(kivi::launch_selftest_division(mismatches, stream));
 }
 
 int64_t kivi_codes_bytes(int64_t BH, int64_t S, int64_t D, int bits) {

@@ -50,11 +50,13 @@ __device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
     }
 }
 
-__device__ __forceinline__ uint4 load16(const void* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
-
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// One 128-bit load (through a native vector type, so it is never split).
+__device__ __forceinline__ uint4 load16(const void* p) {
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
+    return make_uint4(q.x, q.y, q.z, q.w);
+}
 
 // Streaming 128-bit load: the input of a flush is read exactly once, so it
 // is marked non-temporal and does not displace reusable lines in the caches.
@@ -62,6 +64,15 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
     const u32x4_t q =
         __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
     return make_uint4(q.x, q.y, q.z, q.w);
+}
+
+// Streaming 128-bit store for whole 16-byte pieces of a fresh output
+// (reconstructions): written once and not read back by this kernel, so it
+// is marked non-temporal and does not leave dirty lines in the caches for
+// the next kernel to evict.
+__device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
+    const u32x4_t q = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(p));
 }
 
 __device__ __forceinline__ void words(const uint4& v, uint32_t (&w)[4]) {

@@ -34,7 +34,7 @@ __device__ __forceinline__ void emit_full(const uint4 (&v)[GMAX],
         uint4 r;
         const uint64_t q = quant_chunk<DT, BITS, true, WR>(v[t], pk, &r);
         if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
-        if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+        if constexpr (WR) store16_nt(rdst + t * D, r);
     }
 }
 
@@ -53,7 +53,7 @@ __device__ __forceinline__ void emit_rolled(const uint16_t* src,
         uint4 r;
         const uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v, pk, &r);
         if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
-        if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+        if constexpr (WR) store16_nt(rdst + t * D, r);
     }
 }
 
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
                     *reinterpret_cast<uint16_t*>(mine + t * row_bytes) = (uint16_t)q;
                 else
                     *reinterpret_cast<uint32_t*>(mine + t * row_bytes) = (uint32_t)q;
-                if constexpr (WR) *reinterpret_cast<uint4*>(rdst + t * D) = r;
+                if constexpr (WR) store16_nt(rdst + t * D, r);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -198,13 +198,12 @@ static hipError_t launch_keys_t(const QuantJob& j) {
     const uint32_t blocks = (uint32_t)((n_items + 255) / 256);
     const int32_t stage = KeyStage<GMAX, BITS>::kUsed && WQ && 64 % D8 == 0 &&
                           j.group == GMAX && (GMAX * BITS) % 16 == 0;
-    hipLaunchKernelGGL((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>),
+    return launch_kernel((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>),
                        dim3(blocks), dim3(256), 0, j.stream,
                        static_cast<const uint16_t*>(j.x), (uint32_t)n_items,
                        D8, NG, (int32_t)j.S, (int32_t)j.group, j.codes,
                        j.scale, j.zero, static_cast<uint16_t*>(j.recon),
                        stage);
-    return hipGetLastError();
 }
 
 template <int DT, int BITS, int GMAX>

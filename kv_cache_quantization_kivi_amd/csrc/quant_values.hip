@@ -1,22 +1,26 @@
 // KIVI per-token value quantization for gfx950.
 //
 // KIVI blog post on the fused Metal kernels, section "Kernel B -- per-token
-// values": the group runs along the contiguous channel axis, so lanes split
-// a group and reduce across lanes.  Here a row of D channels is spread over
-// P = next_pow2(D/8) lanes, 8 channels (one 128-bit load) per lane, so one
-// wave covers 64/P rows per load and every load is a contiguous 1 KiB of the
-// tensor.  A group of G = 8*2^k channels sits on an aligned block of 2^k
-// lanes; its min/max is an xor-butterfly over those lanes using DPP row
-// permutes (quad xor 1, quad xor 2, half-row mirror, row mirror) and, only
-// for blocks wider than 16 lanes, a cross-row lane shuffle.  The post's rule
-// carries over: every lane of the wave reaches the reduction (no lane exits
-// early), so the permutes never read a retired lane.
+// values": the group runs along the contiguous channel axis.  Here one lane
+// owns 32 consecutive channels of a row (four 128-bit loads, 64 contiguous
+// bytes), so
+//   - a group of 8, 16 or 32 channels lies inside one lane: no cross-lane
+//     step at all, one (scale, zero) computation per group, and the lane's
+//     codes are one contiguous 4*BITS-byte store;
+//   - a group of 32*2^k channels spans an aligned block of 2^k lanes: the
+//     block's min/max is an xor-butterfly over DPP row permutes (quad xor 1,
+//     quad xor 2, half-row mirror, row mirror) and, beyond 16 lanes, a
+//     cross-row lane shuffle.
+// A row of D channels takes ceil(D/32) lanes, padded to P = next_pow2 so
+// rows start on aligned lane blocks.  The post's rule for its SIMD-group
+// butterfly carries over: every lane reaches the reduction (no lane exits
+// early); lanes past the row's end or past the last row load an in-bounds
+// copy of a chunk of the same group, which leaves every min/max unchanged,
+// and store nothing.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
 namespace kivi {
-
-constexpr int kValRows = 4;   // rows per lane per launch slot
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -29,174 +33,276 @@ __device__ __forceinline__ float dpp_f(float v) {
 __device__ __forceinline__ void block_minmax(float& mn, float& mx,
                                              uint32_t red) {
     if (red > 1) {
-        mn = fminf(mn, dpp_f<0xB1>(mn));   // quad_perm [1,0,3,2]
-        mx = fmaxf(mx, dpp_f<0xB1>(mx));
+        mn = vmin(mn, dpp_f<0xB1>(mn));   // quad_perm [1,0,3,2]
+        mx = vmax(mx, dpp_f<0xB1>(mx));
     }
     if (red > 2) {
-        mn = fminf(mn, dpp_f<0x4E>(mn));   // quad_perm [2,3,0,1]
-        mx = fmaxf(mx, dpp_f<0x4E>(mx));
+        mn = vmin(mn, dpp_f<0x4E>(mn));   // quad_perm [2,3,0,1]
+        mx = vmax(mx, dpp_f<0x4E>(mx));
     }
     if (red > 4) {
-        mn = fminf(mn, dpp_f<0x141>(mn));  // row_half_mirror
-        mx = fmaxf(mx, dpp_f<0x141>(mx));
+        mn = vmin(mn, dpp_f<0x141>(mn));  // row_half_mirror
+        mx = vmax(mx, dpp_f<0x141>(mx));
     }
     if (red > 8) {
-        mn = fminf(mn, dpp_f<0x140>(mn));  // row_mirror
-        mx = fmaxf(mx, dpp_f<0x140>(mx));
+        mn = vmin(mn, dpp_f<0x140>(mn));  // row_mirror
+        mx = vmax(mx, dpp_f<0x140>(mx));
     }
     if (red > 16) {
-        mn = fminf(mn, __shfl_xor(mn, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mn = vmin(mn, __shfl_xor(mn, 16));
+        mx = vmax(mx, __shfl_xor(mx, 16));
     }
     if (red > 32) {
-        mn = fminf(mn, __shfl_xor(mn, 32));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = vmin(mn, __shfl_xor(mn, 32));
+        mx = vmax(mx, __shfl_xor(mx, 32));
     }
 }
 
-// Min and max of the 8 elements of one chunk, as fp32.
-template <int DT>
-__device__ __forceinline__ void chunk_minmax(const uint4& v, float& mn,
-                                             float& mx) {
-    uint32_t w[4];
-    words(v, w);
-    if constexpr (DT == DT_F16) {
-        const h2_t a = __builtin_elementwise_min(as_h2(w[0]), as_h2(w[1]));
-        const h2_t b = __builtin_elementwise_min(as_h2(w[2]), as_h2(w[3]));
-        const h2_t m = __builtin_elementwise_min(a, b);
-        const h2_t A = __builtin_elementwise_max(as_h2(w[0]), as_h2(w[1]));
-        const h2_t B = __builtin_elementwise_max(as_h2(w[2]), as_h2(w[3]));
-        const h2_t M = __builtin_elementwise_max(A, B);
-        mn = fminf((float)m.x, (float)m.y);
-        mx = fmaxf((float)M.x, (float)M.y);
-    } else {
-        mn = mx = elem<DT>(w, 0);
+// Min and max over chunks [k0, k0 + n) of the lane's four, as fp32.
+template <int DT, int N>
+__device__ __forceinline__ void chunks_minmax(const uint4 (&v)[4], int k0,
+                                              float& mn, float& mx) {
+    MinMax8<DT> mm;
+    mm.init(v[k0]);
 #pragma unroll
-        for (int k = 1; k < 8; ++k) {
-            const float f = elem<DT>(w, k);
-            mn = fminf(mn, f);
-            mx = fmaxf(mx, f);
-        }
+    for (int k = 1; k < N; ++k) mm.add(v[k0 + k]);
+    float lo[8], hi[8];
+    mm.get(lo, hi);
+    mn = lo[0];
+    mx = hi[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+        mn = vmin(mn, lo[k]);
+        mx = vmax(mx, hi[k]);
     }
 }
 
-template <int DT, int BITS, bool WQ, bool WR>
+// LDS staging.  A lane's 64 bytes of input (and of recon) are contiguous
+// but lanes are 64 bytes apart, so direct 16-byte accesses are strided:
+// each 128-byte line is touched by four instructions, which defeats
+// non-temporal loads (a streamed line is fetched again by every touch) and
+// leaves plain loads allocating lines that evict the previous kernel's
+// dirty output.  When rows tile the lanes exactly, a wave's input (and
+// recon) is one contiguous 4 KiB block: the wave loads it with
+// 1 KiB-contiguous non-temporal 16-byte loads, passes it through LDS so
+// that every lane gets its own four consecutive chunks, and stores recon
+// back the same way.  Chunk j of the block sits at LDS byte (j + j/4) * 16,
+// i.e. lane stride 80 bytes, which spreads 8 consecutive lanes over
+// distinct banks.
+constexpr int kRecLaneStride = 80;
+constexpr int kRecWaveBytes = 64 * kRecLaneStride;
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// GPL: groups per lane (4: G = 8, 2: G = 16, 1: G >= 32).
+// lp: log2 of lanes per row P; red: lanes per group block (GPL == 1);
+// gl: log2 of lanes per group (GPL == 1, may exceed lp when G > D);
+// vec: D % 32 == 0, so a lane's codes are one naturally aligned store;
+// tile: D / 32 is a power of two, so lane unit u covers elements
+// [32u, 32u + 32) of the tensor and a wave's input and recon are contiguous.
+template <int DT, int BITS, int GPL, bool WQ, bool WR>
 __global__ __launch_bounds__(256) void quant_values_kernel(
-    const uint16_t* __restrict__ x, int64_t n_rows, uint32_t D8,
-    uint32_t lp, uint32_t red, uint32_t lcpg, uint32_t NGD,
+    const uint16_t* __restrict__ x, int64_t n_rows, uint32_t D8, uint32_t lp,
+    uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
     uint8_t* __restrict__ codes, float* __restrict__ scale,
     float* __restrict__ zero, uint16_t* __restrict__ recon) {
-    const uint32_t lane = threadIdx.x & 63u;
-    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-    const uint32_t c = lane & ((1u << lp) - 1u);   // chunk within its row
-    const uint32_t rw = lane >> lp;                // row within a pass
-    const uint32_t rpp = 64u >> lp;                // rows per pass
-    const int64_t row_base = wave * (int64_t)(rpp * kValRows) + rw;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
+    constexpr int CPG = 4 / GPL;   // chunks per in-lane group
+    const uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+    const uint32_t c = (uint32_t)(u & ((1u << lp) - 1u));   // lane in its row
+    const int64_t row = (int64_t)(u >> lp);
+    const bool row_ok = row < n_rows;
+    const int64_t lrow = row_ok ? row : n_rows - 1;
     const int64_t D = (int64_t)D8 * 8;
-    const bool cvalid = c < D8;
+    const int32_t ch0 = (int32_t)c * 4;                  // first chunk
+    const int32_t nch = min(4, (int32_t)D8 - ch0);       // real chunks (<= 0: pad lane)
+    const uint16_t* rsrc = x + lrow * D;
 
-    uint4 v[kValRows];
-    bool valid[kValRows];
+    // Wave-uniform: a whole wave of real rows in a tiled layout.
+    const bool staged = tile && __all(row_ok);
+    const uint32_t lane = threadIdx.x & 63u;
+    uint8_t* L = lds + (threadIdx.x >> 6) * kRecWaveBytes;
+    uint4 v[4];
+    if (staged) {
+        const uint16_t* wsrc = x + (u - lane) * 32;   // the wave's 4 KiB
+        uint4 t[4];
 #pragma unroll
-    for (int i = 0; i < kValRows; ++i) {
-        const int64_t row = row_base + (int64_t)i * rpp;
-        valid[i] = cvalid && row < n_rows;
-        v[i] = valid[i] ? load16_nt(x + row * D + (int64_t)c * 8)
-                        : make_uint4(0, 0, 0, 0);
-    }
-
-    float mn[kValRows], mx[kValRows];
+        for (int k = 0; k < 4; ++k) t[k] = load16_nt(wsrc + (k * 64 + lane) * 8);
 #pragma unroll
-    for (int i = 0; i < kValRows; ++i) {
-        chunk_minmax<DT>(v[i], mn[i], mx[i]);
-        if (!valid[i]) {   // identity elements for lanes past the row end
-            mn[i] = __builtin_inff();
-            mx[i] = -__builtin_inff();
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t j = k * 64u + lane;
+            *reinterpret_cast<uint4*>(L + (j + (j >> 2)) * 16) = t[k];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            v[m] = *reinterpret_cast<const uint4*>(L + lane * kRecLaneStride + m * 16);
+    } else {
+        // Chunk k of this lane; a missing chunk of a partial lane loads the
+        // lane's last real chunk (same lane, so the same group, or a group
+        // with no real chunk that is never stored); a pad lane loads the
+        // row's last chunk, which belongs to the row's last group -- the
+        // only group a pad lane's reduction block can share.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int32_t ch = nch <= 0 ? (int32_t)D8 - 1
+                                        : ch0 + (k < nch ? k : nch - 1);
+            v[k] = load16(rsrc + (int64_t)ch * 8);
         }
     }
-#pragma unroll
-    for (int i = 0; i < kValRows; ++i) block_minmax(mn[i], mx[i], red);
 
-    const int64_t row_bytes = (int64_t)D8 * BITS;
-    const bool writes_params = (c & ((1u << lcpg) - 1u)) == 0;
+    float mn[GPL], mx[GPL];
 #pragma unroll
-    for (int i = 0; i < kValRows; ++i) {
-        if (!valid[i]) continue;
-        const int64_t row = row_base + (int64_t)i * rpp;
-        Params p = make_params<BITS>(mn[i], mx[i]);
-        if constexpr (WQ) {
-            if (writes_params) {
-                const int64_t pi = row * NGD + (c >> lcpg);
-                scale[pi] = p.scale;
-                zero[pi] = p.zero;
+    for (int t = 0; t < GPL; ++t) chunks_minmax<DT, CPG>(v, t * CPG, mn[t], mx[t]);
+    if constexpr (GPL == 1) block_minmax(mn[0], mx[0], red);
+
+    if (!staged && (!row_ok || nch <= 0)) return;
+
+    Params pg[GPL];
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) pg[t] = make_params<BITS>(mn[t], mx[t]);
+
+    if constexpr (WQ) {
+        if constexpr (GPL == 1) {
+            if ((c & ((1u << gl) - 1u)) == 0) {
+                const int64_t pi = row * NGD + (c >> gl);
+                scale[pi] = pg[0].scale;
+                zero[pi] = pg[0].zero;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < GPL; ++t) {
+                if (t * CPG < nch) {
+                    const int64_t pi = row * NGD + (ch0 / CPG) + t;
+                    scale[pi] = pg[t].scale;
+                    zero[pi] = pg[t].zero;
+                }
             }
         }
+    }
+
+    bool fast = true;
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) fast = fast && pg[t].fast;
+    const int64_t row_bytes = (int64_t)D8 * BITS;
+    uint8_t* cdst = WQ ? codes + row * row_bytes + (int64_t)ch0 * BITS : nullptr;
+    uint16_t* rdst = WR ? recon + row * D + (int64_t)ch0 * 8 : nullptr;
+    uint64_t q[4];
+    uint4 r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
         Params pk[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pk[k] = p;
-        uint4 r;
-        const uint64_t q = p.fast
-            ? quant_chunk<DT, BITS, true, WR>(v[i], pk, &r)
-            : quant_chunk<DT, BITS, false, WR>(v[i], pk, &r);
-        if constexpr (WQ)
-            store_codes<BITS>(codes + row * row_bytes + (int64_t)c * BITS, q);
-        if constexpr (WR)
-            *reinterpret_cast<uint4*>(recon + row * D + (int64_t)c * 8) = r;
+        for (int e = 0; e < 8; ++e) pk[e] = pg[k / CPG];
+        q[k] = fast ? quant_chunk<DT, BITS, true, WR>(v[k], pk, &r[k])
+                    : quant_chunk<DT, BITS, false, WR>(v[k], pk, &r[k]);
+    }
+    if constexpr (WR) {
+        if (staged) {
+            wave_lds_sync();   // every lane has read its input chunks
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint4*>(L + lane * kRecLaneStride + k * 16) = r[k];
+            wave_lds_sync();
+            uint8_t* wdst = reinterpret_cast<uint8_t*>(recon + (u - lane) * 32);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t off = k * 1024u + lane * 16u;
+                store16_nt(wdst + off, *reinterpret_cast<const uint4*>(
+                                           L + (off >> 6) * kRecLaneStride + (off & 63u)));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < nch) store16_nt(rdst + k * 8, r[k]);
+        }
+    }
+    if constexpr (WQ) {
+        if (vec && nch == 4) {
+            if constexpr (BITS == 1) {
+                *reinterpret_cast<uint32_t*>(cdst) =
+                    (uint32_t)(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24));
+            } else if constexpr (BITS == 2) {
+                *reinterpret_cast<uint2*>(cdst) = make_uint2(
+                    (uint32_t)(q[0] | (q[1] << 16)), (uint32_t)(q[2] | (q[3] << 16)));
+            } else if constexpr (BITS == 4) {
+                *reinterpret_cast<uint4*>(cdst) =
+                    make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2],
+                               (uint32_t)q[3]);
+            } else {
+                uint4* d4 = reinterpret_cast<uint4*>(cdst);
+                d4[0] = make_uint4((uint32_t)q[0], (uint32_t)(q[0] >> 32),
+                                   (uint32_t)q[1], (uint32_t)(q[1] >> 32));
+                d4[1] = make_uint4((uint32_t)q[2], (uint32_t)(q[2] >> 32),
+                                   (uint32_t)q[3], (uint32_t)(q[3] >> 32));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (k < nch) store_codes<BITS>(cdst + k * BITS, q[k]);
+        }
     }
 }
 
-static uint32_t log2_ceil(uint64_t n) {
-    uint32_t l = 0;
-    while ((1ull << l) < n) ++l;
-    return l;
-}
-
-template <int DT, int BITS, bool WQ, bool WR>
+template <int DT, int BITS, int GPL, bool WQ, bool WR>
 static hipError_t launch_values_t(const QuantJob& j) {
     const uint32_t D8 = (uint32_t)(j.D / 8);
-    const uint32_t lp = log2_ceil(D8);                 // lanes per row = 2^lp
-    const uint32_t lcpg = log2_ceil((uint64_t)(j.group / 8));
-    const uint32_t red = 1u << (lcpg < lp ? lcpg : lp);
+    const uint32_t lpr = (D8 + 3) / 4;                 // real lanes per row
+    const uint32_t lp = log2_ceil(lpr);                // P = 2^lp
+    const uint32_t gl = GPL == 1 ? log2_ceil((uint64_t)(j.group / 32)) : 0;
+    const uint32_t red = 1u << (gl < lp ? gl : lp);
     const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
     const int64_t n_rows = j.BH * j.S;
-    const int64_t rows_per_wave = (int64_t)(64u >> lp) * kValRows;
-    const int64_t waves = (n_rows + rows_per_wave - 1) / rows_per_wave;
-    const uint32_t blocks = (uint32_t)((waves + 3) / 4);
-    hipLaunchKernelGGL((quant_values_kernel<DT, BITS, WQ, WR>), dim3(blocks),
-                       dim3(256), 0, j.stream,
+    const uint64_t lanes = (uint64_t)n_rows << lp;
+    const uint32_t blocks = (uint32_t)((lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const int32_t tile = vec && (1u << lp) == lpr;
+    return launch_kernel((quant_values_kernel<DT, BITS, GPL, WQ, WR>),
+                       dim3(blocks), dim3(256), 0, j.stream,
                        static_cast<const uint16_t*>(j.x), n_rows, D8, lp, red,
-                       lcpg, NGD, j.codes, j.scale, j.zero,
+                       gl, NGD, vec, tile, j.codes, j.scale, j.zero,
                        static_cast<uint16_t*>(j.recon));
-    return hipGetLastError();
 }
 
-template <int DT, int BITS>
+template <int DT, int BITS, int GPL>
 static hipError_t launch_values_mode(const QuantJob& j) {
     const bool wq = j.codes != nullptr;
     const bool wr = j.recon != nullptr;
-    if (wq && wr) return launch_values_t<DT, BITS, true, true>(j);
-    if (wq) return launch_values_t<DT, BITS, true, false>(j);
-    return launch_values_t<DT, BITS, false, true>(j);
+    if (wq && wr) return launch_values_t<DT, BITS, GPL, true, true>(j);
+    if (wq) return launch_values_t<DT, BITS, GPL, true, false>(j);
+    return launch_values_t<DT, BITS, GPL, false, true>(j);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_values_gpl(const QuantJob& j) {
+    if (j.group == 8) return launch_values_mode<DT, BITS, 4>(j);
+    if (j.group == 16) return launch_values_mode<DT, BITS, 2>(j);
+    return launch_values_mode<DT, BITS, 1>(j);
 }
 
 template <int DT>
 static hipError_t launch_values_bits(const QuantJob& j) {
     switch (j.bits) {
-        case 1: return launch_values_mode<DT, 1>(j);
-        case 2: return launch_values_mode<DT, 2>(j);
-        case 4: return launch_values_mode<DT, 4>(j);
-        default: return launch_values_mode<DT, 8>(j);
+        case 1: return launch_values_gpl<DT, 1>(j);
+        case 2: return launch_values_gpl<DT, 2>(j);
+        case 4: return launch_values_gpl<DT, 4>(j);
+        default: return launch_values_gpl<DT, 8>(j);
     }
 }
 
 hipError_t launch_quant_values(const QuantJob& j) {
-    // Fast path: whole 8-channel chunks, a row within one wave, and groups
-    // of 8 * 2^k channels (each group then sits on an aligned lane block).
-    const int64_t cpg = j.group / 8;
-    const bool pow2 = cpg >= 1 && (cpg & (cpg - 1)) == 0 && j.group % 8 == 0;
+    // Fast path: whole 8-channel chunks, rows of at most 64 lanes
+    // (D <= 2048), and groups of 8, 16 or 32 * 2^k channels.
+    const int64_t g32 = j.group / 32;
+    const bool grp_ok = j.group == 8 || j.group == 16 ||
+                        (j.group % 32 == 0 && (g32 & (g32 - 1)) == 0);
     const int64_t n_rows = j.BH * j.S;
-    const bool fits = n_rows < (1ll << 40) / 64;
-    if (j.D % 8 != 0 || j.D > 512 || !pow2 || !fits)
+    const bool fits = n_rows < (1ll << 40);
+    if (j.D % 8 != 0 || j.D > 2048 || !grp_ok || !fits)
         return launch_generic_quant_values(j);
     return j.dtype == DT_F16 ? launch_values_bits<DT_F16>(j)
                              : launch_values_bits<DT_BF16>(j);

@@ -176,6 +176,10 @@ DIRECTED = [
     (2, 16, 1024, FP16, 2, 32, 32),    # D > 512: generic values
     (1, 1, 8, FP16, 2, 32, 8),         # one token
     (3, 64, 128, FP16, 2, 256, 512),   # group larger than S / D
+    (2, 16, 1024, BF16, 4, 32, 1024),  # 32-lane value groups (cross-row)
+    (1, 8, 2048, FP16, 2, 16, 2048),   # 64-lane value groups
+    (2, 24, 96, FP16, 2, 32, 64),      # 3 lanes per row padded to 4
+    (2, 24, 2056, FP16, 2, 32, 32),    # D > 2048: generic values
 ]
 
 
@@ -301,3 +305,30 @@ def test_more_than_2_31_elements(K, O):
         assert_recon_equal(bits16(r[sel]), want, f"max size {kind} dequant")
         del c, s_, z, r
         torch.cuda.empty_cache()
+
+
+def test_selftest_division(K):
+    """The exact-division shortcuts hold on this GPU for every significand
+    at every exponent the kernels use them."""
+    assert K.kivi_selftest_division() == 0
+
+
+def test_time_next_launch(K):
+    """kivi_time_next_launch times exactly the next kernel: a positive
+    duration no longer than the events around the whole call, and the pair
+    is disarmed after one launch."""
+    w = W.WORKLOADS["decode"]
+    x = to_dev(W.gen_tensor(w, "K"), w.dtype)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    o1, o2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for e in (a, b):
+        e.record()
+    torch.cuda.synchronize()
+    o1.record()
+    K.kivi_time_next_launch(a, b)
+    K.kivi_quant_keys(x, 2, 32)
+    o2.record()
+    K.kivi_quant_keys(x, 2, 32)          # not timed: the pair was consumed
+    torch.cuda.synchronize()
+    dt = a.elapsed_time(b)
+    assert 0.0 < dt <= o1.elapsed_time(o2)
