@@ -15,8 +15,8 @@ kernel's input is served from a cache.  Per-kernel durations come from HIP event
 recorded at each kernel's own dispatch start and end (hipExtLaunchKernel,
 armed through kivi_time_next_launch) inside the timed region; the dominant
 kernel's achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
-baseline is the plain C oracle (single thread) timed on a bounded sample of
-the same workload.
+baseline is the plain C oracle timed on a bounded sample of the same workload,
+on the host's threads (value) and on one thread.
 
 Prints ONE JSON line.
 """
@@ -156,19 +156,9 @@ def make_steps(K, w, pool_inputs, torch):
     return out
 
 
-def cpu_baseline(w, n_bh, steps_desc):
-    """The oracle as it stands, single-threaded, on n_bh slices of the same
-    workload: every row of the step (the fused row is the oracle's quantize
-    followed by its dequantize)."""
-    import oracle
-    O = oracle.default()
-    bhs = list(range(n_bh))
-    k = W.gen_tensor(w, "K", bhs)
-    v = W.gen_tensor(w, "V", bhs)
-    E = k.size
-    byts = 0.0
-    t0 = time.perf_counter()
-    names = [s[0] for s in steps_desc]
+def _oracle_step(O, w, k, v, names):
+    """Every row of the step on one block of bh slices, through the oracle as
+    it stands (the fused row is its quantize followed by its dequantize)."""
     ck = cv = None
     for name in names:
         if name == "quant_keys":
@@ -185,17 +175,47 @@ def cpu_baseline(w, n_bh, steps_desc):
         elif name == "quant_dequant_values":
             q = O.quant_values(v, w.dtype, w.bits, w.group_v)
             O.dequant_values(*q, v.shape, w.bits, w.group_v, w.dtype)
-    dt = time.perf_counter() - t0
-    for name, op, b, _ in steps_desc:
-        byts += b / w.elems * E
+
+
+def cpu_baseline(w, n_bh, steps_desc, threads):
+    """The oracle as it stands on n_bh slices of the same workload, timed
+    twice: on one thread, then on `threads` threads that each run the whole
+    step over a contiguous block of the slices (the oracle's C calls release
+    the GIL, so the blocks run in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    O = oracle.default()
+    bhs = list(range(n_bh))
+    k = W.gen_tensor(w, "K", bhs)
+    v = W.gen_tensor(w, "V", bhs)
+    E = k.size
+    names = [s[0] for s in steps_desc]
+    byts = sum(b / w.elems * E for _, _, b, _ in steps_desc)
+
+    t0 = time.perf_counter()
+    _oracle_step(O, w, k, v, names)
+    dt1 = time.perf_counter() - t0
+
+    threads = max(1, min(threads, n_bh))
+    cuts = np.linspace(0, n_bh, threads + 1).astype(int)
+    blocks = [(np.ascontiguousarray(k[a:b]), np.ascontiguousarray(v[a:b]))
+              for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    with ThreadPoolExecutor(max_workers=len(blocks)) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda kv: _oracle_step(O, w, kv[0], kv[1], names),
+                    blocks))
+        dtn = time.perf_counter() - t0
     return {
-        "value": round(byts / dt / 1e9, 4),
+        "value": round(byts / dtn / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": len(blocks),
         "kind": "oracle",
         "sample": (f"{n_bh} of {w.BH} (bh) slices of the same workload "
-                   f"({E} elements per tensor), every row of the step, "
-                   f"{dt:.2f} s single-threaded"),
+                   f"({E} elements per tensor), every row of the step: "
+                   f"{dtn:.2f} s on {len(blocks)} threads (value); "
+                   f"{dt1:.2f} s on 1 thread"),
+        "single_thread_value": round(byts / dt1 / 1e9, 4),
     }
 
 
@@ -239,7 +259,12 @@ def main():
                     choices=sorted(W.WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
-    ap.add_argument("--cpu-sample-bh", type=int, default=256)
+    ap.add_argument("--cpu-sample-bh", type=int, default=0,
+                    help="bh slices of the CPU-baseline sample (0: enough "
+                         "for about 2^27 elements per tensor)")
+    ap.add_argument("--cpu-threads", type=int,
+                    default=min(16, os.cpu_count() or 1),
+                    help="threads of the multi-threaded oracle timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="instead of the benchmark, time a plain device copy "
                          "of MB megabytes (the reference kernel used to scale "
@@ -371,8 +396,10 @@ def main():
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:
-        n_bh = min(args.cpu_sample_bh, w.BH)
-        result["cpu_baseline"] = cpu_baseline(w, n_bh, steps)
+        n_bh = args.cpu_sample_bh or max(1, (1 << 27) // (w.S * w.D))
+        n_bh = min(n_bh, w.BH)
+        result["cpu_baseline"] = cpu_baseline(w, n_bh, steps,
+                                              args.cpu_threads)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -103,12 +103,17 @@ __device__ __forceinline__ float vmax(float a, float b) {
 template <int DT>
 struct MinMax8 {
     // fp16: packed pairs (exact: min/max only select).
-    // bf16: fp32 of each element, except that the high element of a dword
-    // is taken as the raw dword: its low 16 bits perturb it by less than one
-    // bf16 ulp toward larger magnitude, which keeps the order of distinct
-    // bf16 values, so the min/max dword carries the min/max bf16 in its high
-    // half (zeros of either sign may come out as tiny values of either sign;
+    // bf16: each element is compared as a raw fp32 dword that holds it in
+    // its high half: the dword itself for the high element, the dword
+    // rotated by 16 bits for the low one.  The other element then sits in
+    // the low 16 bits and perturbs the value by less than one bf16 ulp
+    // toward larger magnitude, which keeps the order of distinct bf16
+    // values, so the min/max dword carries the min/max bf16 in its high half
+    // (zeros of either sign may come out as tiny values of either sign;
     // get() masks the low half and make_params canonicalises the zero).
+    // The rotate is one instruction like the plain widening shift, but it
+    // is not merged with the code pass's widening, which would keep every
+    // token's widened low half live across both passes.
     h2_t mn2[4], mx2[4];
     float mn[8], mx[8];
 
@@ -121,7 +126,8 @@ struct MinMax8 {
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                mn[2 * j] = mx[2 * j] = __uint_as_float(w[j] << 16);
+                mn[2 * j] = mx[2 * j] =
+                    __uint_as_float(__builtin_amdgcn_alignbit(w[j], w[j], 16));
                 mn[2 * j + 1] = mx[2 * j + 1] = __uint_as_float(w[j]);
             }
         }
@@ -139,7 +145,8 @@ struct MinMax8 {
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float lo = __uint_as_float(w[j] << 16);
+                const float lo =
+                    __uint_as_float(__builtin_amdgcn_alignbit(w[j], w[j], 16));
                 const float hi = __uint_as_float(w[j]);
                 mn[2 * j] = vmin(mn[2 * j], lo);
                 mx[2 * j] = vmax(mx[2 * j], lo);
@@ -162,10 +169,8 @@ struct MinMax8 {
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                lo[k] = (k & 1) ? __uint_as_float(__float_as_uint(mn[k]) & 0xffff0000u)
-                                : mn[k];
-                hi[k] = (k & 1) ? __uint_as_float(__float_as_uint(mx[k]) & 0xffff0000u)
-                                : mx[k];
+                lo[k] = __uint_as_float(__float_as_uint(mn[k]) & 0xffff0000u);
+                hi[k] = __uint_as_float(__float_as_uint(mx[k]) & 0xffff0000u);
             }
         }
     }
