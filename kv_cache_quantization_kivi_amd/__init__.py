@@ -4,8 +4,10 @@ Argument marshalling only: every step of quantization and dequantization
 runs in the HIP kernels behind the C ABI declared in include/kivi.h.  Torch
 tensors supply device memory and the current HIP stream; outputs that are
 not passed in are allocated with torch on the input's device.  Importing
-this package fails loudly if the library has not been built (there is no
-fallback of any kind).
+this package works without the library (so that its `build` submodule can
+run from a clean checkout), but the first call of any function below fails
+loudly with ImportError if the library has not been built: there is no
+fallback of any kind.
 
 Functions (same names as the C ABI):
     kivi_quant_keys(k, bits, group)      -> (codes, scale, zero)
@@ -43,7 +45,7 @@ class KiviError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
         super().__init__(f"{what}: {STATUS.get(status, status)} "
-                         f"({_C.kivi_status_string(status).decode()})")
+                         f"({_lib().kivi_status_string(status).decode()})")
 
 
 def _load():
@@ -83,7 +85,15 @@ def _load():
     return L
 
 
-_C = _load()
+_C = None
+
+
+def _lib():
+    """The loaded libkivi.so (loaded on first use; ImportError if absent)."""
+    global _C
+    if _C is None:
+        _C = _load()
+    return _C
 
 
 # --------------------------------------------------------------------------
@@ -158,7 +168,7 @@ def _quant(name, keys, x, bits, group, codes, scale, zero, stream):
     if group < 1:
         _check(4, name)
     codes, scale, zero = _alloc_quant(x, keys, bits, group, codes, scale, zero)
-    st = getattr(_C, name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
+    st = getattr(_lib(), name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
                            group, _ptr(codes), _ptr(scale), _ptr(zero),
                            _stream(x.device, stream))
     _check(st, name)
@@ -191,7 +201,7 @@ def _fused(name, keys, x, bits, group, with_codes, recon, codes, scale, zero,
                                           zero)
     else:
         codes = scale = zero = None
-    st = getattr(_C, name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
+    st = getattr(_lib(), name)(_ptr(x), _dtype_code(x.dtype), BH, S, D, bits,
                            group, _ptr(codes), _ptr(scale), _ptr(zero),
                            _ptr(recon), _stream(x.device, stream))
     _check(st, name)
@@ -225,7 +235,7 @@ def _dequant(name, keys, codes, scale, zero, bits, group, out_dtype, out,
         BH *= n
     if out is None:
         out = torch.empty(lead + (S, D), dtype=out_dtype, device=codes.device)
-    st = getattr(_C, name)(_ptr(codes), _ptr(scale), _ptr(zero), BH, S, D,
+    st = getattr(_lib(), name)(_ptr(codes), _ptr(scale), _ptr(zero), BH, S, D,
                            bits, group, _dtype_code(out.dtype), _ptr(out),
                            _stream(codes.device, stream))
     _check(st, name)
@@ -255,7 +265,7 @@ def kivi_time_next_launch(start, stop):
             return None
         return ctypes.c_void_p(e.cuda_event if hasattr(e, "cuda_event")
                                else int(e))
-    _C.kivi_time_next_launch(h(start), h(stop))
+    _lib().kivi_time_next_launch(h(start), h(stop))
 
 
 def kivi_selftest_division(device="cuda", stream=None):
@@ -263,25 +273,25 @@ def kivi_selftest_division(device="cuda", stream=None):
     against IEEE division on this GPU (0 is required)."""
     dev = torch.device(device)
     cnt = torch.zeros(1, dtype=torch.int64, device=dev)
-    st = _C.kivi_selftest_division(_ptr(cnt), _stream(dev, stream))
+    st = _lib().kivi_selftest_division(_ptr(cnt), _stream(dev, stream))
     _check(st, "kivi_selftest_division")
     return int(cnt.item())
 
 
 def kivi_codes_bytes(BH, S, D, bits):
-    return _C.kivi_codes_bytes(BH, S, D, bits)
+    return _lib().kivi_codes_bytes(BH, S, D, bits)
 
 
 def kivi_key_param_count(BH, S, D, group):
-    return _C.kivi_key_param_count(BH, S, D, group)
+    return _lib().kivi_key_param_count(BH, S, D, group)
 
 
 def kivi_value_param_count(BH, S, D, group):
-    return _C.kivi_value_param_count(BH, S, D, group)
+    return _lib().kivi_value_param_count(BH, S, D, group)
 
 
 def kivi_status_string(status):
-    return _C.kivi_status_string(status).decode()
+    return _lib().kivi_status_string(status).decode()
 
 
 def library_path():
@@ -290,4 +300,4 @@ def library_path():
 
 def raw():
     """The ctypes handle of libkivi.so (pointer-level calls)."""
-    return _C
+    return _lib()

@@ -26,12 +26,6 @@ namespace kivi {
 
 constexpr int kDqTokUnroll = 8;   // tokens per step of the keys' token loop
 
-__device__ __forceinline__ void lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 __device__ __forceinline__ float4 load_f4_nt(const float* p) {
     const u32x4_t q =
         __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -48,21 +42,28 @@ __device__ __forceinline__ uint64_t lds_codes(const uint8_t* p) {
 }
 
 // Staged key codes: at most 32 tokens per group and BITS <= 4, so a wave's
-// block is at most 64 * 32 * 4 bytes (plus up to 16 bytes of padding per
+// block is at most 64 * 32 * BITS bytes (plus up to 16 bytes of padding per
 // tile, at most 64 tiles).
-constexpr int kDqKeyWaveBytes = 64 * 32 * 4 + 64 * 16;
+template <int BITS>
+struct DqKeyStage {
+    static constexpr int kWaveBytes = BITS <= 4 ? 64 * 32 * BITS + 64 * 16 : 0;
+};
 
 // stage: the host's verdict that a wave of full tiles has one contiguous
 // code block of whole 16-byte pieces per lane (64 % D8 == 0, group <= 32,
 // group * BITS % 16 == 0, BITS <= 4).
+// (Gathering a few tokens of reconstruction in LDS so that every store
+// instruction writes a contiguous KiB measured 3-4% slower than the direct
+// 16-byte stores below, and was left out.)
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void dequant_keys_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
     const float* __restrict__ zero, uint32_t n_items, uint32_t D8,
     uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out,
     int32_t stage) {
+    constexpr int kWaveBytes = DqKeyStage<BITS>::kWaveBytes;
     __shared__ __attribute__((aligned(16)))
-    uint8_t lds[BITS <= 4 ? 4 * kDqKeyWaveBytes : 16];
+    uint8_t lds[BITS <= 4 ? 4 * kWaveBytes : 16];
 
     const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
     const bool valid = gid < n_items;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void dequant_keys_kernel(
     if constexpr (BITS <= 4) {
         if (stage && __all(valid && nt == G)) {
             const uint32_t lane = threadIdx.x & 63u;
-            uint8_t* L = lds + (threadIdx.x >> 6) * kDqKeyWaveBytes;
+            uint8_t* L = lds + (threadIdx.x >> 6) * kWaveBytes;
             const uint32_t tile_bytes = (uint32_t)G * D8 * BITS;
             const uint32_t ts = tile_bytes + ((D8 * BITS + 15u) & ~15u);
             // Lane 0 holds chunk 0 of the wave's first tile; the wave's
@@ -99,8 +100,8 @@ __global__ __launch_bounds__(256) void dequant_keys_kernel(
                 (uint32_t)((uint64_t)row0 & 0xffffffffu));
             const uint32_t b_hi = __builtin_amdgcn_readfirstlane(
                 (uint32_t)((uint64_t)row0 >> 32));
-            const uint8_t* wsrc =
-                codes + (int64_t)(((uint64_t)b_hi << 32) | b_lo) * row_bytes;
+            const int64_t wrow0 = (int64_t)(((uint64_t)b_hi << 32) | b_lo);
+            const uint8_t* wsrc = codes + wrow0 * row_bytes;
             const uint32_t n16 = (uint32_t)G * BITS / 16;   // pieces per lane
             uint4 t4[8];
 #pragma unroll
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(256) void dequant_keys_kernel(
                     *reinterpret_cast<uint4*>(L + ti * ts + (off - ti * tile_bytes)) = t4[k];
                 }
             }
-            lds_sync();
+            wave_lds_sync();
             const uint8_t* mine = L + (lane / D8) * ts + c * BITS;
 #pragma unroll kDqTokUnroll
             for (int32_t t = 0; t < G; ++t)
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void dequant_values_kernel(
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             *reinterpret_cast<uint4*>(L + lane * kDqRecLaneStride + k * 16) = r[k];
-        lds_sync();
+        wave_lds_sync();
         uint8_t* wdst = reinterpret_cast<uint8_t*>(out + (u - lane) * 32);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -246,9 +247,74 @@ __global__ __launch_bounds__(256) void dequant_values_kernel(
     }
 }
 
+// Small dequantizations (a decode-time flush) have too few (bh, group,
+// chunk) items to fill the GPU, and one lane storing a whole group is then
+// the latency.  Here each item is split over SPLIT lanes that take
+// ceil(G / SPLIT) consecutive tokens each (lanes: chunk fastest, then part);
+// they share the item's scale and zero and need no communication.
+constexpr int kDqKeySplit = 4;
+constexpr uint64_t kDqKeySplitBelow = 256ull * 256ull;
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(64) void dequant_keys_split_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+    const float* __restrict__ zero, uint32_t n_lanes, uint32_t D8,
+    uint32_t NG, int32_t S, int32_t G, int32_t TPL,
+    uint16_t* __restrict__ out) {
+    const uint32_t lid = blockIdx.x * 64u + threadIdx.x;
+    if (lid >= n_lanes) return;
+    const uint32_t c = lid % D8;
+    const uint32_t part = (lid / D8) % kDqKeySplit;
+    const uint32_t tile = lid / (D8 * kDqKeySplit);
+    const uint32_t g = tile % NG;
+    const uint32_t bh = tile / NG;
+    const int32_t s0 = (int32_t)g * G;
+    const int32_t nt = min(G, S - s0);
+    const int32_t t_lo = (int32_t)part * TPL;
+    const int32_t t_hi = min(t_lo + TPL, nt);
+    if (t_lo >= t_hi) return;
+    const int64_t D = (int64_t)D8 * 8;
+    const int64_t row0 = (int64_t)bh * S + s0;
+
+    const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
+    const float4 s_a = load_f4_nt(scale + p);
+    const float4 s_b = load_f4_nt(scale + p + 4);
+    const float4 z_a = load_f4_nt(zero + p);
+    const float4 z_b = load_f4_nt(zero + p + 4);
+    const float sc[8] = {s_a.x, s_a.y, s_a.z, s_a.w, s_b.x, s_b.y, s_b.z, s_b.w};
+    const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
+
+    const int64_t row_bytes = (int64_t)D8 * BITS;
+    const uint8_t* src = codes + row0 * row_bytes + (int64_t)c * BITS;
+    uint16_t* dst = out + row0 * D + (int64_t)c * 8;
+    for (int32_t t0 = t_lo; t0 < t_hi; t0 += kDqTokUnroll) {
+        uint64_t q[kDqTokUnroll];
+#pragma unroll
+        for (int u = 0; u < kDqTokUnroll; ++u)
+            if (t0 + u < t_hi) q[u] = load_codes<BITS>(src + (t0 + u) * row_bytes);
+#pragma unroll
+        for (int u = 0; u < kDqTokUnroll; ++u)
+            if (t0 + u < t_hi)
+                store16_nt(dst + (int64_t)(t0 + u) * D,
+                           dequant_chunk<DT, BITS>(q[u], sc, z));
+    }
+}
+
 template <int DT, int BITS>
 static hipError_t launch_dq_keys_t(const DequantJob& j) {
     const uint32_t D8 = (uint32_t)(j.D / 8);
+    if ((uint64_t)j.BH * ((j.S + j.group - 1) / j.group) * D8 <
+        kDqKeySplitBelow) {
+        const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
+        const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * kDqKeySplit;
+        const int32_t tpl = (int32_t)((j.group + kDqKeySplit - 1) / kDqKeySplit);
+        return launch_kernel((dequant_keys_split_kernel<DT, BITS>),
+                             dim3((uint32_t)((n_lanes + 63) / 64)), dim3(64), 0,
+                             j.stream, j.codes, j.scale, j.zero,
+                             (uint32_t)n_lanes, D8, NG, (int32_t)j.S,
+                             (int32_t)j.group, tpl,
+                             static_cast<uint16_t*>(j.out));
+    }
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_items = (uint64_t)j.BH * NG * D8;
     const uint32_t blocks = (uint32_t)((n_items + 255) / 256);

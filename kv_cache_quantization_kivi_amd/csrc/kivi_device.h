@@ -75,6 +75,14 @@ __device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
     __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t*>(p));
 }
 
+// Make one wave's LDS writes visible to the other lanes of the same wave
+// (the waits for its outstanding LDS operations plus a wave barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ void words(const uint4& v, uint32_t (&w)[4]) {
     w[0] = v.x;
     w[1] = v.y;
@@ -156,6 +164,26 @@ struct MinMax8 {
         }
     }
 
+    // Fold in the running min/max of the lane `mask` lanes away (an xor
+    // partner in the same wave; every lane of the wave must take part).
+    __device__ __forceinline__ void combine_xor(int mask) {
+        if constexpr (DT == DT_F16) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int a = __shfl_xor(__builtin_bit_cast(int, mn2[j]), mask);
+                const int b = __shfl_xor(__builtin_bit_cast(int, mx2[j]), mask);
+                mn2[j] = vmin(mn2[j], __builtin_bit_cast(h2_t, a));
+                mx2[j] = vmax(mx2[j], __builtin_bit_cast(h2_t, b));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mn[k] = vmin(mn[k], __shfl_xor(mn[k], mask));
+                mx[k] = vmax(mx[k], __shfl_xor(mx[k], mask));
+            }
+        }
+    }
+
     // Per-channel min and max as fp32.
     __device__ __forceinline__ void get(float (&lo)[8], float (&hi)[8]) const {
         if constexpr (DT == DT_F16) {
@@ -217,7 +245,12 @@ __device__ __forceinline__ Params make_params(float mn, float mx) {
     const float y = __builtin_fmaf(e, y0, y0);
     p.y = (range == 0.0f) ? 0.0f : y;
     p.fast = (range == 0.0f) || (range >= 0x1p-56f && range <= 0x1p56f);
-    if (!p.fast) p.scale = range / L;
+    // Ranges outside the fast window are rare; a wave-uniform branch keeps
+    // the IEEE division sequence off the common path (a per-lane select
+    // would execute it for every group).
+    if (__any(!p.fast)) {
+        if (!p.fast) p.scale = range / L;
+    }
     return p;
 }
 

@@ -58,11 +58,12 @@ __device__ __forceinline__ void emit_rolled(const uint16_t* src,
 }
 
 // LDS bytes per wave for the staged code block: tiles of GMAX rows padded
-// by up to 16 bytes each (bank spreading), at most 64 tiles.
+// by up to 16 bytes each (bank spreading), at most 64 tiles.  Used when a
+// lane's share of the block is whole 16-byte pieces.
 template <int GMAX, int BITS>
 struct KeyStage {
-    static constexpr int kWaveBytes = 64 * GMAX * BITS + 64 * 16;
-    static constexpr bool kUsed = BITS <= 4;
+    static constexpr bool kUsed = BITS <= 4 && (GMAX * BITS) % 16 == 0;
+    static constexpr int kWaveBytes = kUsed ? 64 * GMAX * BITS + 64 * 16 : 0;
 };
 
 // Work item = (bh, token group g, channel chunk c), flattened with c fastest
@@ -73,9 +74,11 @@ struct KeyStage {
 // missing slots, which is the pages' edge-replicate padding and leaves the
 // min/max unchanged, so the min/max carries no guards.
 // WQ: write codes + params.  WR: write the reconstruction (fused path).
-// stage: the host's verdict that whole waves hold whole tiles and that a
-// lane's share of the block is whole 16-byte chunks (64 % D8 == 0,
-// group == GMAX, GMAX*BITS % 16 == 0).
+// stage: the host's verdict that whole waves hold whole tiles (64 % D8 == 0,
+// group == GMAX), so that a wave's codes are one contiguous block.
+// (Staging the fused path's reconstruction the same way, so that each store
+// instruction writes a contiguous KiB, measured 1-2% slower than the direct
+// 16-byte stores below, and was left out.)
 template <int DT, int BITS, int GMAX, bool WQ, bool WR>
 __global__ __launch_bounds__(256) void quant_keys_kernel(
     const uint16_t* __restrict__ x, uint32_t n_items, uint32_t D8,
@@ -83,8 +86,9 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
     float* __restrict__ scale, float* __restrict__ zero,
     uint16_t* __restrict__ recon, int32_t stage) {
     using Stage = KeyStage<GMAX, BITS>;
+    constexpr bool kStaged = WQ && Stage::kUsed;
     __shared__ __attribute__((aligned(16)))
-    uint8_t lds[Stage::kUsed ? 4 * Stage::kWaveBytes : 16];
+    uint8_t lds[kStaged ? 4 * Stage::kWaveBytes : 16];
 
     const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
     const bool valid = gid < n_items;
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
     uint8_t* dst = WQ ? codes + row0 * row_bytes + (int64_t)c * BITS : nullptr;
     uint16_t* rdst = WR ? recon + row0 * D + (int64_t)c * 8 : nullptr;
 
-    if constexpr (WQ && Stage::kUsed) {
+    if constexpr (kStaged) {
         // Wave-uniform choice: every lane valid, full and fast.
         if (stage && __all(valid && full && fast)) {
             const uint32_t lane = threadIdx.x & 63u;
@@ -158,9 +162,7 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
                     *reinterpret_cast<uint32_t*>(mine + t * row_bytes) = (uint32_t)q;
                 if constexpr (WR) store16_nt(rdst + t * D, r);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_lds_sync();
             // Lane 0 holds chunk 0 of the wave's first tile; the wave's
             // tiles are consecutive token groups, i.e. consecutive rows.
             const uint32_t b_lo = __builtin_amdgcn_readfirstlane(
@@ -190,14 +192,124 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
         emit_rolled<DT, BITS, WQ, WR, false>(src, pk, nt, dst, row_bytes, rdst, D);
 }
 
+// Small flushes (a decode-time flush of a few dozen tokens per head) have
+// too few (bh, token group, chunk) items to fill the GPU, and one lane
+// working through a whole group is then the latency.  This variant gives the
+// chunk of a group to SPLIT lanes of one wave, TPL = GMAX / SPLIT tokens
+// each: lanes are laid out channel chunk fastest, then token part, so the
+// SPLIT lanes of a group are D8 lanes apart and their min/max meet through
+// xor shuffles; then every lane codes its own tokens.  A lane's token
+// index is clamped to the group's last token (the edge padding), so lanes
+// of a ragged group load in bounds and store only real tokens.  Lanes past
+// the end mirror the last lane; items come in whole groups of D8*SPLIT
+// lanes aligned inside the wave, so they only ever meet each other.
+template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL>
+__device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
+                                           const Params (&pk)[8], int32_t n,
+                                           uint8_t* dst, int64_t row_bytes,
+                                           uint16_t* rdst, int64_t D) {
+#pragma unroll
+    for (int t = 0; t < TPL; ++t) {
+        if (t < n) {
+            uint4 r;
+            const uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v[t], pk, &r);
+            if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
+            if constexpr (WR) store16_nt(rdst + t * D, r);
+        }
+    }
+}
+
+template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR>
+__global__ __launch_bounds__(64) void quant_keys_split_kernel(
+    const uint16_t* __restrict__ x, uint32_t n_lanes, uint32_t D8,
+    uint32_t NG, int32_t S, int32_t G, uint8_t* __restrict__ codes,
+    float* __restrict__ scale, float* __restrict__ zero,
+    uint16_t* __restrict__ recon) {
+    const uint32_t gid = blockIdx.x * 64u + threadIdx.x;
+    const bool valid = gid < n_lanes;
+    const uint32_t lid = valid ? gid : n_lanes - 1u;
+    const uint32_t c = lid % D8;
+    const uint32_t part = (lid / D8) % SPLIT;
+    const uint32_t tile = lid / (D8 * SPLIT);
+    const uint32_t g = tile % NG;
+    const uint32_t bh = tile / NG;
+    const int32_t s0 = (int32_t)g * G;
+    const int32_t nt = min(G, S - s0);
+    const int32_t t0 = (int32_t)part * TPL;   // first token of this lane
+    const int64_t D = (int64_t)D8 * 8;
+    const int64_t row0 = (int64_t)bh * S + s0;
+    const uint16_t* src = x + row0 * D + (int64_t)c * 8;
+
+    uint4 v[TPL];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t)
+        v[t] = load16_nt(src + min(t0 + t, nt - 1) * D);
+
+    MinMax8<DT> mm;
+    mm.init(v[0]);
+#pragma unroll
+    for (int t = 1; t < TPL; ++t) mm.add(v[t]);
+#pragma unroll
+    for (int k = 1; k < SPLIT; k <<= 1) mm.combine_xor((int)D8 * k);
+    float lo[8], hi[8];
+    mm.get(lo, hi);
+
+    Params pk[8];
+    bool fast = true;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        pk[k] = make_params<BITS>(lo[k], hi[k]);
+        fast = fast && pk[k].fast;
+    }
+    if (!valid) return;
+
+    if (WQ && part == 0) {
+        const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
+        float4* ps = reinterpret_cast<float4*>(scale + p);
+        float4* pz = reinterpret_cast<float4*>(zero + p);
+        ps[0] = make_float4(pk[0].scale, pk[1].scale, pk[2].scale, pk[3].scale);
+        ps[1] = make_float4(pk[4].scale, pk[5].scale, pk[6].scale, pk[7].scale);
+        pz[0] = make_float4(pk[0].zero, pk[1].zero, pk[2].zero, pk[3].zero);
+        pz[1] = make_float4(pk[4].zero, pk[5].zero, pk[6].zero, pk[7].zero);
+    }
+    const int32_t n = nt - t0;   // real tokens of this lane (may be <= 0)
+    const int64_t row_bytes = (int64_t)D8 * BITS;
+    uint8_t* dst = WQ ? codes + (row0 + t0) * row_bytes + (int64_t)c * BITS
+                      : nullptr;
+    uint16_t* rdst = WR ? recon + (row0 + t0) * D + (int64_t)c * 8 : nullptr;
+    if (fast)
+        emit_split<DT, BITS, WQ, WR, true, TPL>(v, pk, n, dst, row_bytes, rdst, D);
+    else
+        emit_split<DT, BITS, WQ, WR, false, TPL>(v, pk, n, dst, row_bytes, rdst, D);
+}
+
+// Lanes below which a flush takes the split kernel: one lane per
+// (bh, group, chunk) item would leave most of the GPU's 256 CUs idle.
+constexpr uint64_t kKeySplitBelow = 256ull * 256ull;
+constexpr int kKeySplit = 4;
+
+template <int DT, int BITS, int GMAX, bool WQ, bool WR>
+static hipError_t launch_keys_split_t(const QuantJob& j) {
+    constexpr int TPL = GMAX / kKeySplit;
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
+    const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * kKeySplit;
+    const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
+    return launch_kernel(
+        (quant_keys_split_kernel<DT, BITS, TPL, kKeySplit, WQ, WR>),
+        dim3(blocks), dim3(64), 0, j.stream,
+        static_cast<const uint16_t*>(j.x), (uint32_t)n_lanes, D8, NG,
+        (int32_t)j.S, (int32_t)j.group, j.codes, j.scale, j.zero,
+        static_cast<uint16_t*>(j.recon));
+}
+
 template <int DT, int BITS, int GMAX, bool WQ, bool WR>
 static hipError_t launch_keys_t(const QuantJob& j) {
     const uint32_t D8 = (uint32_t)(j.D / 8);
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_items = (uint64_t)j.BH * NG * D8;
     const uint32_t blocks = (uint32_t)((n_items + 255) / 256);
-    const int32_t stage = KeyStage<GMAX, BITS>::kUsed && WQ && 64 % D8 == 0 &&
-                          j.group == GMAX && (GMAX * BITS) % 16 == 0;
+    const int32_t stage = 64 % D8 == 0 && j.group == GMAX;
     return launch_kernel((quant_keys_kernel<DT, BITS, GMAX, WQ, WR>),
                        dim3(blocks), dim3(256), 0, j.stream,
                        static_cast<const uint16_t*>(j.x), (uint32_t)n_items,
@@ -210,6 +322,15 @@ template <int DT, int BITS, int GMAX>
 static hipError_t launch_keys_mode(const QuantJob& j) {
     const bool wq = j.codes != nullptr;
     const bool wr = j.recon != nullptr;
+    const uint64_t D8 = (uint64_t)(j.D / 8);
+    const uint64_t NG = (uint64_t)((j.S + j.group - 1) / j.group);
+    const bool split = (uint64_t)j.BH * NG * D8 < kKeySplitBelow &&
+                       64 % (D8 * kKeySplit) == 0;
+    if (split) {
+        if (wq && wr) return launch_keys_split_t<DT, BITS, GMAX, true, true>(j);
+        if (wq) return launch_keys_split_t<DT, BITS, GMAX, true, false>(j);
+        return launch_keys_split_t<DT, BITS, GMAX, false, true>(j);
+    }
     if (wq && wr) return launch_keys_t<DT, BITS, GMAX, true, true>(j);
     if (wq) return launch_keys_t<DT, BITS, GMAX, true, false>(j);
     return launch_keys_t<DT, BITS, GMAX, false, true>(j);

@@ -92,12 +92,6 @@ __device__ __forceinline__ void chunks_minmax(const uint4 (&v)[4], int k0,
 constexpr int kRecLaneStride = 80;
 constexpr int kRecWaveBytes = 64 * kRecLaneStride;
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // GPL: groups per lane (4: G = 8, 2: G = 16, 1: G >= 32).
 // lp: log2 of lanes per row P; red: lanes per group block (GPL == 1);
 // gl: log2 of lanes per group (GPL == 1, may exceed lp when G > D);

@@ -136,3 +136,30 @@ def test_binding_rejects_bad_tensors(K):
     y = torch.zeros(2, 8, 16, dtype=torch.float16)[:, :, :8]
     with pytest.raises(ValueError):
         K.kivi_quant_keys(y)
+
+
+def test_missing_library_fails_loudly_but_build_module_imports(tmp_path):
+    """From a checkout where libkivi.so is not built, the package and its
+    `build` submodule import (so the build can run), and the first call
+    raises ImportError naming the missing library: there is no fallback."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "kv_cache_quantization_kivi_amd")
+    dst = tmp_path / "kv_cache_quantization_kivi_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns(
+        "*.so", "_build", "__pycache__"))
+    code = (
+        "import kv_cache_quantization_kivi_amd.build as b\n"
+        "import kv_cache_quantization_kivi_amd as K\n"
+        "assert callable(b.build)\n"
+        "try:\n"
+        "    K.kivi_codes_bytes(1, 1, 8, 2)\n"
+        "except ImportError as e:\n"
+        "    assert 'libkivi.so' in str(e)\n"
+        "    print('loud')\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=tmp_path,
+                         capture_output=True, text=True, timeout=120,
+                         env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "loud"

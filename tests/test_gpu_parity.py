@@ -173,7 +173,7 @@ DIRECTED = [
     (1, 37, 20, BF16, 2, 3, 5),        # generic, groups straddle code bytes
     (2, 32, 512, FP16, 2, 32, 256),    # 64 lanes per row, cross-row reduce
     (1, 32, 512, BF16, 2, 32, 512),
-    (2, 16, 1024, FP16, 2, 32, 32),    # D > 512: generic values
+    (2, 16, 1024, FP16, 2, 32, 32),    # 32 lanes per row, in-lane groups
     (1, 1, 8, FP16, 2, 32, 8),         # one token
     (3, 64, 128, FP16, 2, 256, 512),   # group larger than S / D
     (2, 16, 1024, BF16, 4, 32, 1024),  # 32-lane value groups (cross-row)
@@ -190,6 +190,63 @@ def test_directed(K, O, case):
     tag = "directed " + "x".join(map(str, case))
     got = run_all(K, to_dev(x, dtype), dtype, bits, gk, gv, tag)
     compare(O, got, x, dtype, bits, gk, gv, tag)
+
+
+# The key quantizer and dequantizer each have two kernels: below 65536
+# (bh, token group, 8-channel chunk) items each group is split over four
+# lanes (the decode-time flush; for the quantizer only when D/8 is a power
+# of two up to 16); above it one lane owns a whole group.  Each shape runs
+# once with the BH given (split kernels) and once with BH raised past the
+# threshold (one-lane kernels).
+KEY_PATHS = [
+    # (BH, S, D, dtype, bits, gk)
+    (2, 33, 64, FP16, 1, 8),      # ragged: the last group has one token
+    (2, 50, 64, BF16, 8, 5),      # group 5 over 4 lanes of 2 tokens
+    (2, 48, 128, FP16, 4, 16),
+    (1, 1, 8, FP16, 2, 32),       # one token, D8 = 1
+    (3, 70, 32, BF16, 2, 32),     # ragged 32-token group
+    (2, 64, 16, FP16, 4, 32),
+    (2, 64, 256, FP16, 2, 32),    # D8 = 32: two tiles per wave
+    (2, 64, 512, BF16, 4, 32),    # D8 = 64: one tile per wave
+    (2, 96, 64, FP16, 2, 48),     # group > 32: generic quantizer, direct dequant
+]
+KEY_SPLIT_BELOW = 65536
+
+
+def _key_path_bh(S, D, gk, split):
+    if split:
+        return None
+    items = ((S + gk - 1) // gk) * (D // 8)
+    return -(-KEY_SPLIT_BELOW // items)
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one_lane"])
+@pytest.mark.parametrize("case", KEY_PATHS,
+                         ids=lambda c: "x".join(map(str, c)))
+def test_key_kernel_paths(K, O, case, split):
+    BH, S, D, dtype, bits, gk = case
+    BH = _key_path_bh(S, D, gk, split) or BH
+    tag = f"keys {'split' if split else 'one-lane'} BH={BH} " + \
+        "x".join(map(str, case[1:]))
+    x = _rand(hash(case) % (2**31), BH, S, D, dtype)
+    xd = to_dev(x, dtype)
+    say(f"[{tag}] quant / fused / dequant")
+    ck, sk, zk = K.kivi_quant_keys(xd, bits, gk)
+    rk = K.kivi_dequant_keys(ck, sk, zk, bits, gk, out_dtype=xd.dtype)
+    fk, fck, fsk, fzk = K.kivi_quant_dequant_keys(xd, bits, gk)
+    fk2 = K.kivi_quant_dequant_keys(xd, bits, gk, with_codes=False)
+    torch.cuda.synchronize()
+    eck, esk, ezk = O.quant_keys(x, dtype, bits, gk)
+    erk = O.dequant_keys(eck, esk, ezk, x.shape, bits, gk, dtype)
+    for got, exp, what in ((ck, eck, "codes"), (fck, eck, "fused codes")):
+        assert_codes_equal(host(got), exp, f"{tag} {what}")
+    for got, exp, what in ((sk, esk, "scale"), (zk, ezk, "zero"),
+                           (fsk, esk, "fused scale"),
+                           (fzk, ezk, "fused zero")):
+        assert_f32_bits_equal(host(got), exp, f"{tag} {what}")
+    for got, what in ((rk, "dequant"), (fk, "fused recon"),
+                      (fk2, "recon-only")):
+        assert_recon_equal(bits16(got), erk, f"{tag} {what}")
 
 
 def test_constant_and_signed_zero_groups(K, O):
