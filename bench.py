@@ -13,9 +13,10 @@ rotate over a pool of distinct tensors larger than the 256 MB MALL, and the
 dequantizers read codes written two steps earlier (see make_steps), so no
 kernel's input is served from a cache.  Per-kernel durations come from HIP events
 recorded at each kernel's own dispatch (hipExtLaunchKernel, armed through
-kivi_time_next_launch): every launch of one pass of K steps gives the
-per-kernel table, then the timed region of K steps arms only the dominant
-kernel, whose achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
+kivi_time_next_launch) over a second pass of K steps, after the timed
+region: the markers HIP queues for such events cost a few microseconds per
+launch, so the step itself is timed without them.  The dominant kernel's
+achieved bandwidth is reported against MI355X's 8 TB/s peak.  The CPU
 baseline is the plain C oracle timed on a bounded sample of the same workload,
 on the host's threads (value) and on one thread.
 
@@ -271,6 +272,12 @@ def main():
                          "of MB megabytes (the reference kernel used to scale "
                          "rocprofv3 byte counters) and a plain read (sum)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", choices=("auto", "graphs", "eager"),
+                    default="auto",
+                    help="timed steps as HIP graph replays or eager launches; "
+                         "auto: graphs for launch-bound steps (under 256 MB "
+                         "of traffic), eager otherwise (graph replays add "
+                         "1-4%% to long steps)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -334,15 +341,56 @@ def main():
             b.record(stream)
         return ev
 
-    # Pass 1, per-kernel durations: every launch records its own start/stop
-    # event pair at its dispatch (kivi_time_next_launch), on the launch's
-    # stream.  HIP puts each pair in the queue as marker packets around the
-    # kernel, which costs a few microseconds of dispatch per armed launch,
-    # so this pass is not the one that times the step.
+    # Pass 1, the timed region: exactly K steps between two events on the
+    # launch stream, with nothing else in the queue.  A launch-bound step
+    # (a decode-time flush) is one HIP graph replay: the step's launches
+    # depend only on the step index modulo `period` (input sets and code
+    # sets rotate), so one graph per phase is captured once, before timing,
+    # and replayed in order; kernels and arguments are exactly those of the
+    # eager calls.
+    period = int(np.lcm(pool, N_CODE_SETS))
+    use_graphs = (args.launch == "graphs" or
+                  (args.launch == "auto" and step_bytes < 256e6))
+    graphs = None
+    if use_graphs:
+        graphs = []
+        cap = torch.cuda.Stream(device=dev)
+        for ph in range(period):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for _, _, _, fn in steps:
+                    fn(ph)
+            graphs.append(g)
+        for ph in range(period):      # first replays happen outside the timing
+            graphs[ph].replay()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    base = args.warmup
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        if graphs is not None:
+            graphs[(base + i) % period].replay()
+        else:
+            for _, _, _, fn in steps:
+                fn(base + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    # Pass 2, kernel durations: K more steps in which every launch records
+    # its own start/stop event pair at its dispatch (kivi_time_next_launch,
+    # hipExtLaunchKernel), on the launch's stream.  HIP queues each pair as
+    # marker packets around the kernel, which adds a few microseconds of
+    # dispatch per armed launch; that is why the step is timed in a pass of
+    # its own.  The dominant kernel (longest average) gives the roofline.
     n_k = len(steps)
     kev = [event_pairs(n_k) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    base = args.warmup
+    base = args.warmup + args.steps
     for i in range(args.steps):
         for jj, (_, _, _, fn) in enumerate(steps):
             K.kivi_time_next_launch(*kev[i][jj])
@@ -354,30 +402,7 @@ def main():
              for i in range(args.steps)]
         per_kernel[name] = stats(name, op, b, d)
     dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"])
-    jdom = [s_[0] for s_ in steps].index(dom)
-
-    # Pass 2, the timed region: exactly K steps between two events; only
-    # the dominant kernel's launches are armed, which gives its duration
-    # over the timed region itself for the roofline.
-    dev_ev = event_pairs(args.steps)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    base = args.warmup + args.steps
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        for jj, (_, _, _, fn) in enumerate(steps):
-            if jj == jdom:
-                K.kivi_time_next_launch(*dev_ev[i])
-            fn(base + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    name, op, b, _ = steps[jdom]
-    dk = stats(name, op, b, [a.elapsed_time(z) for a, z in dev_ev])
+    dk = per_kernel[dom]
 
     src_hash = kernel_source_hash()
     traffic = load_traffic(dom, w.name, src_hash)
@@ -404,6 +429,8 @@ def main():
                          + " + ".join(s[0] for s in steps)),
             "step_algorithmic_bytes": int(step_bytes),
             "input_pool": pool,
+            "launch": (f"one HIP graph replay per step ({period} phases)"
+                       if use_graphs else "eager"),
             "wall_s": round(t_wall, 4),
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -418,10 +445,10 @@ def main():
             "traffic": traffic,
         },
         "per_kernel": per_kernel,
-        "per_kernel_note": ("per_kernel: every launch of a separate pass of "
-                            "K steps armed with events; roofline: the "
-                            "dominant kernel's launches inside the timed "
-                            "region"),
+        "per_kernel_note": ("value: K steps with no per-launch events; "
+                            "per_kernel and roofline: a second pass of K "
+                            "steps, every launch timed by HIP events at its "
+                            "own dispatch"),
         "kernel_source_hash": src_hash,
     }
     if not args.no_cpu_baseline:

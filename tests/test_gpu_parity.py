@@ -323,6 +323,51 @@ def test_deterministic_and_stream(K):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
+@pytest.mark.parametrize("shape", [(224, 32, 128), (512, 256, 128)],
+                         ids=["decode_split", "one_lane"])
+def test_graph_capture_replays(K, shape):
+    """Every compute entry point captured in one HIP graph (as the benchmark
+    replays a launch-bound step): three replays, each after eager work that
+    scribbles over the outputs and a synchronisation, must reproduce the
+    eager results bit for bit."""
+    BH, S, D = shape
+    bits, g = 2, 32
+    x = to_dev(_rand(11, BH, S, D, FP16), FP16)
+    ck, sk, zk = K.kivi_quant_keys(x, bits, g)
+    cv, sv, zv = K.kivi_quant_values(x, bits, g)
+    rk = K.kivi_dequant_keys(ck, sk, zk, bits, g, out_dtype=x.dtype)
+    rv = K.kivi_dequant_values(cv, sv, zv, bits, g, out_dtype=x.dtype)
+    fk = K.kivi_quant_dequant_keys(x, bits, g)
+    fv = K.kivi_quant_dequant_values(x, bits, g)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (ck, sk, zk, cv, sv, zv, rk, rv, *fk, *fv)]
+    outs = [torch.empty_like(t) for t in eager]
+    (gck, gsk, gzk, gcv, gsv, gzv, grk, grv,
+     gfk, gfck, gfsk, gfzk, gfv, gfcv, gfsv, gfzv) = outs
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        K.kivi_quant_keys(x, bits, g, gck, gsk, gzk)
+        K.kivi_quant_values(x, bits, g, gcv, gsv, gzv)
+        K.kivi_dequant_keys(eager[0], eager[1], eager[2], bits, g,
+                            out_dtype=x.dtype, out=grk)
+        K.kivi_dequant_values(eager[3], eager[4], eager[5], bits, g,
+                              out_dtype=x.dtype, out=grv)
+        K.kivi_quant_dequant_keys(x, bits, g, True, gfk, gfck, gfsk, gfzk)
+        K.kivi_quant_dequant_values(x, bits, g, True, gfv, gfcv, gfsv, gfzv)
+    for rep in range(3):
+        say(f"[graph {shape}] replay {rep}")
+        for t in outs:                     # eager work between replays
+            t.view(torch.uint8).fill_(0xA5 + rep)
+        K.kivi_quant_keys(x, bits, g)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(outs, eager)):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                f"replay {rep}, output {i}"
+
+
 def test_more_than_2_31_elements(K, O):
     """A [520, 32768, 128] fp16 tensor (2.2e9 elements, 4.4 GB): 64-bit
     offsets throughout.  Built by tiling 8 seeded slices; the oracle checks
