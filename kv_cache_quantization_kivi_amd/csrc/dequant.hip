@@ -249,9 +249,10 @@ __global__ __launch_bounds__(256) void dequant_values_kernel(
 
 // Small dequantizations (a decode-time flush) have too few (bh, group,
 // chunk) items to fill the GPU, and one lane storing a whole group is then
-// the latency.  Here each item is split over SPLIT lanes that take
-// ceil(G / SPLIT) consecutive tokens each (lanes: chunk fastest, then part);
-// they share the item's scale and zero and need no communication.
+// the latency.  Here each item is split over SPLIT lanes, interleaved: part
+// p takes tokens p, p + SPLIT, ... (lanes: chunk fastest, then part, so one
+// store instruction covers SPLIT consecutive rows); the lanes share the
+// item's scale and zero and need no communication.
 constexpr int kDqKeySplit = 4;
 constexpr uint64_t kDqKeySplitBelow = 256ull * 256ull;
 
@@ -259,8 +260,7 @@ template <int DT, int BITS>
 __global__ __launch_bounds__(64) void dequant_keys_split_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
     const float* __restrict__ zero, uint32_t n_lanes, uint32_t D8,
-    uint32_t NG, int32_t S, int32_t G, int32_t TPL,
-    uint16_t* __restrict__ out) {
+    uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out) {
     const uint32_t lid = blockIdx.x * 64u + threadIdx.x;
     if (lid >= n_lanes) return;
     const uint32_t c = lid % D8;
@@ -270,9 +270,9 @@ __global__ __launch_bounds__(64) void dequant_keys_split_kernel(
     const uint32_t bh = tile / NG;
     const int32_t s0 = (int32_t)g * G;
     const int32_t nt = min(G, S - s0);
-    const int32_t t_lo = (int32_t)part * TPL;
-    const int32_t t_hi = min(t_lo + TPL, nt);
-    if (t_lo >= t_hi) return;
+    // tokens part + SPLIT * t < nt
+    const int32_t n = (nt - (int32_t)part + kDqKeySplit - 1) / kDqKeySplit;
+    if (n <= 0) return;
     const int64_t D = (int64_t)D8 * 8;
     const int64_t row0 = (int64_t)bh * S + s0;
 
@@ -285,17 +285,19 @@ __global__ __launch_bounds__(64) void dequant_keys_split_kernel(
     const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
 
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    const uint8_t* src = codes + row0 * row_bytes + (int64_t)c * BITS;
-    uint16_t* dst = out + row0 * D + (int64_t)c * 8;
-    for (int32_t t0 = t_lo; t0 < t_hi; t0 += kDqTokUnroll) {
+    const int64_t cs = kDqKeySplit * row_bytes;   // code row stride
+    const int64_t rs = kDqKeySplit * D;           // recon row stride
+    const uint8_t* src = codes + (row0 + part) * row_bytes + (int64_t)c * BITS;
+    uint16_t* dst = out + (row0 + part) * D + (int64_t)c * 8;
+    for (int32_t t0 = 0; t0 < n; t0 += kDqTokUnroll) {
         uint64_t q[kDqTokUnroll];
 #pragma unroll
         for (int u = 0; u < kDqTokUnroll; ++u)
-            if (t0 + u < t_hi) q[u] = load_codes<BITS>(src + (t0 + u) * row_bytes);
+            if (t0 + u < n) q[u] = load_codes<BITS>(src + (t0 + u) * cs);
 #pragma unroll
         for (int u = 0; u < kDqTokUnroll; ++u)
-            if (t0 + u < t_hi)
-                store16_nt(dst + (int64_t)(t0 + u) * D,
+            if (t0 + u < n)
+                store16_nt(dst + (int64_t)(t0 + u) * rs,
                            dequant_chunk<DT, BITS>(q[u], sc, z));
     }
 }
@@ -307,13 +309,11 @@ static hipError_t launch_dq_keys_t(const DequantJob& j) {
         kDqKeySplitBelow) {
         const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
         const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * kDqKeySplit;
-        const int32_t tpl = (int32_t)((j.group + kDqKeySplit - 1) / kDqKeySplit);
         return launch_kernel((dequant_keys_split_kernel<DT, BITS>),
                              dim3((uint32_t)((n_lanes + 63) / 64)), dim3(64), 0,
                              j.stream, j.codes, j.scale, j.zero,
                              (uint32_t)n_lanes, D8, NG, (int32_t)j.S,
-                             (int32_t)j.group, tpl,
-                             static_cast<uint16_t*>(j.out));
+                             (int32_t)j.group, static_cast<uint16_t*>(j.out));
     }
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_items = (uint64_t)j.BH * NG * D8;

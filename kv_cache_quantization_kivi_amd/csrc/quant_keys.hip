@@ -196,30 +196,34 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
 // too few (bh, token group, chunk) items to fill the GPU, and one lane
 // working through a whole group is then the latency.  This variant gives the
 // chunk of a group to SPLIT lanes of one wave, TPL = GMAX / SPLIT tokens
-// each: lanes are laid out channel chunk fastest, then token part, so the
-// SPLIT lanes of a group are D8 lanes apart and their min/max meet through
-// xor shuffles; then every lane codes its own tokens.  A lane's token
-// index is clamped to the group's last token (the edge padding), so lanes
-// of a ragged group load in bounds and store only real tokens.  Lanes past
-// the end mirror the last lane; items come in whole groups of D8*SPLIT
-// lanes aligned inside the wave, so they only ever meet each other.
+// each, interleaved: lane part p takes tokens p, p + SPLIT, p + 2 SPLIT, ...
+// Lanes are laid out channel chunk fastest, then part, so one load or store
+// instruction covers SPLIT consecutive rows of a tile, and the SPLIT lanes
+// of a group are D8 lanes apart, where their min/max meet through xor
+// shuffles; then every lane codes its own tokens.  A lane's token index is
+// clamped to the group's last token (the edge padding), so lanes of a
+// ragged group load in bounds and store only real tokens.  Lanes past the
+// end mirror the last lane; items come in whole groups of D8*SPLIT lanes
+// aligned inside the wave, so they only ever meet each other.
+// Code and store a lane's first n tokens; token t's code row is at
+// dst + t * cstride bytes and its recon row at rdst + t * rstride elements.
 template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL>
 __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
                                            const Params (&pk)[8], int32_t n,
-                                           uint8_t* dst, int64_t row_bytes,
-                                           uint16_t* rdst, int64_t D) {
+                                           uint8_t* dst, int64_t cstride,
+                                           uint16_t* rdst, int64_t rstride) {
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
         if (t < n) {
             uint4 r;
             const uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v[t], pk, &r);
-            if constexpr (WQ) store_codes<BITS>(dst + t * row_bytes, q);
-            if constexpr (WR) store16_nt(rdst + t * D, r);
+            if constexpr (WQ) store_codes<BITS>(dst + t * cstride, q);
+            if constexpr (WR) store16_nt(rdst + t * rstride, r);
         }
     }
 }
 
-template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR>
+template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV>
 __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const uint16_t* __restrict__ x, uint32_t n_lanes, uint32_t D8,
     uint32_t NG, int32_t S, int32_t G, uint8_t* __restrict__ codes,
@@ -235,7 +239,6 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const uint32_t bh = tile / NG;
     const int32_t s0 = (int32_t)g * G;
     const int32_t nt = min(G, S - s0);
-    const int32_t t0 = (int32_t)part * TPL;   // first token of this lane
     const int64_t D = (int64_t)D8 * 8;
     const int64_t row0 = (int64_t)bh * S + s0;
     const uint16_t* src = x + row0 * D + (int64_t)c * 8;
@@ -243,7 +246,8 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     uint4 v[TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t)
-        v[t] = load16_nt(src + min(t0 + t, nt - 1) * D);
+        v[t] = load16_nt(src + min(ILV ? (int32_t)part + SPLIT * t
+                                       : (int32_t)part * TPL + t, nt - 1) * D);
 
     MinMax8<DT> mm;
     mm.init(v[0]);
@@ -272,35 +276,54 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
         pz[0] = make_float4(pk[0].zero, pk[1].zero, pk[2].zero, pk[3].zero);
         pz[1] = make_float4(pk[4].zero, pk[5].zero, pk[6].zero, pk[7].zero);
     }
-    const int32_t n = nt - t0;   // real tokens of this lane (may be <= 0)
+    // real tokens of this lane: part + SPLIT * t < nt (interleaved), or
+    // part * TPL + t < nt (blocked)
+    const int32_t n = ILV ? ((int32_t)nt - (int32_t)part + SPLIT - 1) / SPLIT
+                          : (int32_t)nt - (int32_t)part * TPL;
+    const int32_t first = ILV ? (int32_t)part : (int32_t)part * TPL;
+    const int32_t step = ILV ? SPLIT : 1;
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    uint8_t* dst = WQ ? codes + (row0 + t0) * row_bytes + (int64_t)c * BITS
+    uint8_t* dst = WQ ? codes + (row0 + first) * row_bytes + (int64_t)c * BITS
                       : nullptr;
-    uint16_t* rdst = WR ? recon + (row0 + t0) * D + (int64_t)c * 8 : nullptr;
+    uint16_t* rdst = WR ? recon + (row0 + first) * D + (int64_t)c * 8 : nullptr;
     if (fast)
-        emit_split<DT, BITS, WQ, WR, true, TPL>(v, pk, n, dst, row_bytes, rdst, D);
+        emit_split<DT, BITS, WQ, WR, true, TPL>(v, pk, n, dst, step * row_bytes,
+                                                rdst, step * D);
     else
-        emit_split<DT, BITS, WQ, WR, false, TPL>(v, pk, n, dst, row_bytes, rdst, D);
+        emit_split<DT, BITS, WQ, WR, false, TPL>(v, pk, n, dst, step * row_bytes,
+                                                 rdst, step * D);
 }
 
-// Lanes below which a flush takes the split kernel: one lane per
-// (bh, group, chunk) item would leave most of the GPU's 256 CUs idle.
+// Lanes per group.  Below kKeySplitBelow (bh, group, chunk) items (a
+// decode-time flush) one lane per item would leave most of the GPU's 256
+// CUs idle, so each group takes 4 lanes; above it 2 lanes per group, which
+// measured 3-13% faster than one lane per group on the large workloads (half
+// the registers per lane, so more waves in flight, for one xor shuffle and
+// one repeated parameter computation per group).
 constexpr uint64_t kKeySplitBelow = 256ull * 256ull;
-constexpr int kKeySplit = 4;
 
-template <int DT, int BITS, int GMAX, bool WQ, bool WR>
+template <int DT, int BITS, int GMAX, int SPLIT, bool WQ, bool WR>
 static hipError_t launch_keys_split_t(const QuantJob& j) {
-    constexpr int TPL = GMAX / kKeySplit;
+    constexpr int TPL = GMAX / SPLIT;
     const uint32_t D8 = (uint32_t)(j.D / 8);
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
-    const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * kKeySplit;
+    const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * SPLIT;
     const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
     return launch_kernel(
-        (quant_keys_split_kernel<DT, BITS, TPL, kKeySplit, WQ, WR>),
+        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true>),
         dim3(blocks), dim3(64), 0, j.stream,
         static_cast<const uint16_t*>(j.x), (uint32_t)n_lanes, D8, NG,
         (int32_t)j.S, (int32_t)j.group, j.codes, j.scale, j.zero,
         static_cast<uint16_t*>(j.recon));
+}
+
+template <int DT, int BITS, int GMAX, int SPLIT>
+static hipError_t launch_keys_split_mode(const QuantJob& j) {
+    const bool wq = j.codes != nullptr;
+    const bool wr = j.recon != nullptr;
+    if (wq && wr) return launch_keys_split_t<DT, BITS, GMAX, SPLIT, true, true>(j);
+    if (wq) return launch_keys_split_t<DT, BITS, GMAX, SPLIT, true, false>(j);
+    return launch_keys_split_t<DT, BITS, GMAX, SPLIT, false, true>(j);
 }
 
 template <int DT, int BITS, int GMAX, bool WQ, bool WR>
@@ -324,13 +347,12 @@ static hipError_t launch_keys_mode(const QuantJob& j) {
     const bool wr = j.recon != nullptr;
     const uint64_t D8 = (uint64_t)(j.D / 8);
     const uint64_t NG = (uint64_t)((j.S + j.group - 1) / j.group);
-    const bool split = (uint64_t)j.BH * NG * D8 < kKeySplitBelow &&
-                       64 % (D8 * kKeySplit) == 0;
-    if (split) {
-        if (wq && wr) return launch_keys_split_t<DT, BITS, GMAX, true, true>(j);
-        if (wq) return launch_keys_split_t<DT, BITS, GMAX, true, false>(j);
-        return launch_keys_split_t<DT, BITS, GMAX, false, true>(j);
-    }
+    const uint64_t items = (uint64_t)j.BH * NG * D8;
+    // n_lanes = items * SPLIT must fit the kernel's 32-bit lane index
+    if (items < kKeySplitBelow && 64 % (D8 * 4) == 0)
+        return launch_keys_split_mode<DT, BITS, GMAX, 4>(j);
+    if (items < (1ull << 31) && 64 % (D8 * 2) == 0)
+        return launch_keys_split_mode<DT, BITS, GMAX, 2>(j);
     if (wq && wr) return launch_keys_t<DT, BITS, GMAX, true, true>(j);
     if (wq) return launch_keys_t<DT, BITS, GMAX, true, false>(j);
     return launch_keys_t<DT, BITS, GMAX, false, true>(j);

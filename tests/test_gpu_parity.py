@@ -192,12 +192,12 @@ def test_directed(K, O, case):
     compare(O, got, x, dtype, bits, gk, gv, tag)
 
 
-# The key quantizer and dequantizer each have two kernels: below 65536
-# (bh, token group, 8-channel chunk) items each group is split over four
-# lanes (the decode-time flush; for the quantizer only when D/8 is a power
-# of two up to 16); above it one lane owns a whole group.  Each shape runs
-# once with the BH given (split kernels) and once with BH raised past the
-# threshold (one-lane kernels).
+# The key quantizer splits each (bh, token group, 8-channel chunk) item
+# over 4 lanes below 65536 items (the decode-time flush) and over 2 lanes
+# above it, when D/8 allows (a power of two up to 16, resp. 32); other
+# shapes take one lane per item.  The key dequantizer splits items over 4
+# lanes below 65536 items and uses one lane per item above.  Each shape runs
+# once with the BH given and once with BH raised past the threshold.
 KEY_PATHS = [
     # (BH, S, D, dtype, bits, gk)
     (2, 33, 64, FP16, 1, 8),      # ragged: the last group has one token
@@ -206,8 +206,8 @@ KEY_PATHS = [
     (1, 1, 8, FP16, 2, 32),       # one token, D8 = 1
     (3, 70, 32, BF16, 2, 32),     # ragged 32-token group
     (2, 64, 16, FP16, 4, 32),
-    (2, 64, 256, FP16, 2, 32),    # D8 = 32: two tiles per wave
-    (2, 64, 512, BF16, 4, 32),    # D8 = 64: one tile per wave
+    (2, 64, 256, FP16, 2, 32),    # D8 = 32: one lane (small), two (large)
+    (2, 64, 512, BF16, 4, 32),    # D8 = 64: one lane per item, staged codes
     (2, 96, 64, FP16, 2, 48),     # group > 32: generic quantizer, direct dequant
 ]
 KEY_SPLIT_BELOW = 65536
@@ -220,13 +220,13 @@ def _key_path_bh(S, D, gk, split):
     return -(-KEY_SPLIT_BELOW // items)
 
 
-@pytest.mark.parametrize("split", [True, False], ids=["split", "one_lane"])
+@pytest.mark.parametrize("split", [True, False], ids=["small", "large"])
 @pytest.mark.parametrize("case", KEY_PATHS,
                          ids=lambda c: "x".join(map(str, c)))
 def test_key_kernel_paths(K, O, case, split):
     BH, S, D, dtype, bits, gk = case
     BH = _key_path_bh(S, D, gk, split) or BH
-    tag = f"keys {'split' if split else 'one-lane'} BH={BH} " + \
+    tag = f"keys {'small' if split else 'large'} BH={BH} " + \
         "x".join(map(str, case[1:]))
     x = _rand(hash(case) % (2**31), BH, S, D, dtype)
     xd = to_dev(x, dtype)
@@ -324,7 +324,7 @@ def test_deterministic_and_stream(K):
 
 
 @pytest.mark.parametrize("shape", [(224, 32, 128), (512, 256, 128)],
-                         ids=["decode_split", "one_lane"])
+                         ids=["small", "large"])
 def test_graph_capture_replays(K, shape):
     """Every compute entry point captured in one HIP graph (as the benchmark
     replays a launch-bound step): three replays, each after eager work that
