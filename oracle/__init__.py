@@ -177,6 +177,66 @@ class Oracle:
         return self._dequant("kivi_ref_dequant_values", packed, scale, zero,
                              shape, bits, group, out_dtype)
 
+    def cache(self, BH, D, S_max, R, G_k, G_v, bits, dtype):
+        """A residual-window cache (kivi_ref_cache) over numpy arrays."""
+        return OracleCache(self, BH, D, S_max, R, G_k, G_v, bits, dtype)
+
+
+class _RefCache(ctypes.Structure):
+    _fields_ = [("BH", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("S_max", ctypes.c_int64), ("R", ctypes.c_int64),
+                ("G_k", ctypes.c_int64), ("G_v", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+                ("T", ctypes.c_int64), ("Q", ctypes.c_int64)]
+
+
+class OracleCache:
+    """kivi_ref_cache with its arrays held here: append(k_new, v_new) with
+    [BH, n, D] uint16 patterns; T, Q; the compressed store and the history
+    as numpy arrays (k_codes, k_scale, ..., k, v)."""
+
+    def __init__(self, oracle, BH, D, S_max, R, G_k, G_v, bits, dtype):
+        self.o = oracle
+        NG = n_groups(S_max, G_k)
+        NGD = n_groups(D, G_v)
+        rb = D * bits // 8
+        self.k = np.zeros((BH, S_max, D), np.uint16)
+        self.v = np.zeros((BH, S_max, D), np.uint16)
+        self.k_codes = np.zeros((BH, S_max, rb), np.uint8)
+        self.v_codes = np.zeros((BH, S_max, rb), np.uint8)
+        self.k_scale = np.zeros((BH, NG, D), np.float32)
+        self.k_zero = np.zeros((BH, NG, D), np.float32)
+        self.v_scale = np.zeros((BH, S_max, NGD), np.float32)
+        self.v_zero = np.zeros((BH, S_max, NGD), np.float32)
+        self.c = _RefCache(BH, D, S_max, R, G_k, G_v, bits, dtype,
+                           *[a.ctypes.data for a in (
+                               self.k, self.v, self.k_codes, self.v_codes,
+                               self.k_scale, self.k_zero, self.v_scale,
+                               self.v_zero)], 0, 0)
+        oracle.L.kivi_ref_cache_append.argtypes = [
+            ctypes.POINTER(_RefCache), ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64]
+
+    @property
+    def T(self):
+        return self.c.T
+
+    @property
+    def Q(self):
+        return self.c.Q
+
+    def append(self, k_new, v_new):
+        k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
+        v_new = np.ascontiguousarray(v_new, dtype=np.uint16)
+        n = k_new.shape[1] if k_new.ndim == 3 else 0
+        self.o._check(self.o.L.kivi_ref_cache_append(
+            ctypes.byref(self.c), _ptr(k_new), _ptr(v_new), n),
+            "cache_append")
+
 
 _default = None
 

@@ -369,3 +369,54 @@ int kivi_ref_dequant_values(const uint8_t* packed, const float* scale,
     free(codes);
     return 0;
 }
+
+/* One flush: the G_k oldest unquantized tokens [Q, Q + G_k) of every bh,
+ * which form exactly one key group, go through the plain quantizers above,
+ * writing straight into the compressed store at their own offsets. */
+static int cache_flush_group(kivi_ref_cache* c) {
+    const int64_t D = c->D, G = c->G_k, S = c->S_max;
+    const int64_t row_bytes = D * c->bits / 8;
+    const int64_t NG = (S + G - 1) / G;
+    const int64_t NGD = (D + c->G_v - 1) / c->G_v;
+    for (int64_t bh = 0; bh < c->BH; ++bh) {
+        const int64_t row = bh * S + c->Q;
+        int st = kivi_ref_quant_keys(c->k + row * D, c->dtype, 1, G, D,
+                                     c->bits, G, c->k_codes + row * row_bytes,
+                                     c->k_scale + (bh * NG + c->Q / G) * D,
+                                     c->k_zero + (bh * NG + c->Q / G) * D);
+        if (st == 0)
+            st = kivi_ref_quant_values(c->v + row * D, c->dtype, 1, G, D,
+                                       c->bits, c->G_v,
+                                       c->v_codes + row * row_bytes,
+                                       c->v_scale + row * NGD,
+                                       c->v_zero + row * NGD);
+        if (st != 0) return st;
+    }
+    c->Q += G;
+    return 0;
+}
+
+int kivi_ref_cache_append(kivi_ref_cache* c, const uint16_t* k_new,
+                          const uint16_t* v_new, int64_t n) {
+    if (!c || n < 0 || c->R < 0 || c->G_k < 1 || c->G_v < 1 ||
+        c->T < 0 || c->Q < 0 || c->Q > c->T ||
+        !shape_ok(c->BH, c->S_max, c->D, c->bits, c->G_k) ||
+        (c->dtype != 0 && c->dtype != 1) || n > c->S_max - c->T)
+        return 1;
+    if (n > 0 && (!k_new || !v_new)) return 1;
+    const int64_t D = c->D;
+    for (int64_t i = 0; i < n; ++i) {
+        for (int64_t bh = 0; bh < c->BH; ++bh) {
+            memcpy(c->k + (bh * c->S_max + c->T) * D, k_new + (bh * n + i) * D,
+                   (size_t)D * sizeof(uint16_t));
+            memcpy(c->v + (bh * c->S_max + c->T) * D, v_new + (bh * n + i) * D,
+                   (size_t)D * sizeof(uint16_t));
+        }
+        c->T += 1;
+        while (c->T - c->Q >= c->R + c->G_k) {
+            int st = cache_flush_group(c);
+            if (st != 0) return st;
+        }
+    }
+    return 0;
+}

@@ -100,6 +100,43 @@ int kivi_ref_dequant_values(const uint8_t* packed, const float* scale,
                             int64_t D, int bits, int64_t group, int out_dtype,
                             uint16_t* out);
 
+/* Residual-window cache (KIVI blog post on the fused Metal kernels, section
+ * "What we're actually optimizing": the most recent residual_length tokens
+ * stay in 16-bit floats and, once enough fresh tokens have accumulated, are
+ * quantized as a batch -- a flush; the 0.8.0 release post, section "What
+ * KIVI is": the last R tokens are held exactly and tokens are quantized as
+ * they age out of that window).  Reading: tokens arrive one at a time; after
+ * each, while at least R + G_k tokens are unquantized, the oldest G_k of them
+ * (one whole key group, group-aligned) are quantized -- keys per channel
+ * over those G_k tokens, values per token -- into the compressed store at
+ * their own token offset.  Every appended token is also kept in k / v, so a
+ * test can read back the tokens [Q, T) that are still unquantized.
+ * The caller allocates every array:
+ *   k, v              [BH, S_max, D] 16-bit patterns
+ *   k_codes, v_codes  [BH, S_max, D*bits/8]
+ *   k_scale, k_zero   [BH, ceil(S_max/G_k), D]
+ *   v_scale, v_zero   [BH, S_max, ceil(D/G_v)]
+ * and sets T = Q = 0 before the first append. */
+typedef struct {
+    int64_t BH, D, S_max, R, G_k, G_v;
+    int32_t bits, dtype;
+    uint16_t* k;
+    uint16_t* v;
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    float* k_scale;
+    float* k_zero;
+    float* v_scale;
+    float* v_zero;
+    int64_t T, Q;   /* tokens appended, tokens quantized */
+} kivi_ref_cache;
+
+/* Append n tokens of every bh (k_new, v_new [BH, n, D]); flush as above.
+ * Returns 1 (and appends nothing) if the cache would exceed S_max or an
+ * argument is invalid. */
+int kivi_ref_cache_append(kivi_ref_cache* c, const uint16_t* k_new,
+                          const uint16_t* v_new, int64_t n);
+
 #ifdef __cplusplus
 }
 #endif

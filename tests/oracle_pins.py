@@ -15,6 +15,10 @@ or the mathematics fix:
     determinism;
   - equivalences: a ragged group equals the pages' edge-replicate padding;
     per-channel keys equal per-token values of the transposed tensor;
+  - the residual-window cache: the pages' flush counts (prompts of 559,
+    2059, 8209 tokens flush 512, 2016, 8160; 240 decode tokens make 7
+    flushes), the window invariant, and group-by-group flushing equal to
+    quantizing the flushed prefix at once;
   - the pages' statistic: 2-bit reconstruction cosine about 0.93 on
     unit-norm Gaussian keys (KIVI release post, "Honest limitations"; PyPI
     page, KIVI section), 4-bit above 0.995 (PyPI page, ZipCache section).
@@ -483,6 +487,120 @@ def pin_cosine_statistics(o):
     assert 0.92 <= c2 <= 0.94, c2        # pages: "around 0.93"
     c4 = _cosine_unit_norm_keys(o, 4)
     assert c4 > 0.995, c4                # pages: 4-bit "> 0.995"
+
+
+# --------------------------------------------------------------------------
+# The residual-window cache (flush scheduling)
+# --------------------------------------------------------------------------
+
+def _tokens(seed, BH, n, D):
+    r = np.random.default_rng(seed)
+    return (r.standard_normal((BH, n, D)) * 2).astype(np.float16).view(
+        np.uint16)
+
+
+def pin_cache_flush_counts_from_pages(o):
+    """KIVI blog post on the fused Metal kernels, "The full end-to-end
+    record", Generation 1: with residual_length = group = 32, prompts of
+    559, 2059 and 8209 tokens flush 512, 2016 and 8160 tokens per layer.
+    The same counts whether the prompt arrives at once, in prefill chunks of
+    2048 tokens (the chunking the post names) or token by token."""
+    for prompt, flushed in ((559, 512), (2059, 2016), (8209, 8160)):
+        x = _tokens(prompt, 1, prompt, 8)
+        for chunk in (prompt, 2048, 1):
+            c = o.cache(1, 8, 8320, 32, 32, 32, 2, FP16)
+            for a in range(0, prompt, chunk):
+                c.append(x[:, a:a + chunk], x[:, a:a + chunk])
+            assert (c.T, c.Q) == (prompt, flushed), (prompt, chunk, c.Q)
+
+
+def pin_cache_decode_flush_cadence(o):
+    """Same post, "Four benchmarks that lied", Lie #2: 240 decode tokens
+    after a 2k prompt make 7 flushes (R = G = 32; the 2059-token prompt of
+    Generation 1)."""
+    c = o.cache(1, 8, 2400, 32, 32, 32, 2, FP16)
+    x = _tokens(7, 1, 2059 + 240, 8)
+    c.append(x[:, :2059], x[:, :2059])
+    events = 0
+    for t in range(2059, 2059 + 240):
+        q = c.Q
+        c.append(x[:, t:t + 1], x[:, t:t + 1])
+        assert c.Q in (q, q + 32)
+        events += c.Q != q
+    assert events == 7, events
+
+
+def pin_cache_window_invariant(o):
+    """After every append the unquantized tail holds the R most recent
+    tokens and fewer than R + G in all: Q is a multiple of G, and
+    R <= T - Q < R + G once T >= R + G (before that nothing is flushed);
+    with R = 0 every whole group is flushed at once."""
+    for R, G in ((32, 32), (0, 8), (5, 16), (40, 32)):
+        c = o.cache(2, 16, 600, R, G, 16, 4, BF16)
+        rng = np.random.default_rng(R + G)
+        x = _tokens(3, 2, 600, 16)
+        t = 0
+        while t < 560:
+            n = min(int(rng.choice([1, 1, 2, 7, 31, 64])), 600 - t)
+            c.append(x[:, t:t + n], x[:, t:t + n])
+            t += n
+            assert c.T == t and c.Q % G == 0
+            if t < R + G:
+                assert c.Q == 0, (R, G, t, c.Q)
+            else:
+                assert R <= t - c.Q < R + G, (R, G, t, c.Q)
+
+
+def pin_cache_equals_prefix_quantization(o):
+    """Flushing group by group as tokens age out is the same as quantizing
+    the whole flushed prefix at once (key groups are aligned at token 0 and
+    independent; values are per token): codes and params of tokens [0, Q)
+    equal the plain quantizers on the history prefix, untouched storage past
+    Q stays zero, and the history holds every appended token."""
+    for dtype, bits, Gk, Gv, R in ((FP16, 2, 32, 32, 32), (BF16, 4, 16, 64, 7),
+                                   (FP16, 1, 8, 8, 0)):
+        BH, D, S_max = 3, 64, 300
+        c = o.cache(BH, D, S_max, R, Gk, Gv, bits, dtype)
+        x = _tokens(11 + bits, BH, S_max, D)
+        y = _tokens(12 + bits, BH, S_max, D)
+        t = 0
+        for n in (1, 5, 40, 1, 1, 70, 33, 2, 90, 3):
+            c.append(x[:, t:t + n], y[:, t:t + n])
+            t += n
+        Q = c.Q
+        assert Q > 0 and np.array_equal(c.k[:, :t], x[:, :t]) \
+            and np.array_equal(c.v[:, :t], y[:, :t])
+        ck, sk, zk = o.quant_keys(np.ascontiguousarray(x[:, :Q]), dtype, bits,
+                                  Gk)
+        cv, sv, zv = o.quant_values(np.ascontiguousarray(y[:, :Q]), dtype,
+                                    bits, Gv)
+        assert np.array_equal(c.k_codes[:, :Q], ck)
+        assert np.array_equal(c.k_scale[:, :Q // Gk].view(np.uint32),
+                              sk.view(np.uint32))
+        assert np.array_equal(c.k_zero[:, :Q // Gk].view(np.uint32),
+                              zk.view(np.uint32))
+        assert np.array_equal(c.v_codes[:, :Q], cv)
+        assert np.array_equal(c.v_scale[:, :Q].view(np.uint32),
+                              sv.view(np.uint32))
+        assert np.array_equal(c.v_zero[:, :Q].view(np.uint32),
+                              zv.view(np.uint32))
+        assert not c.k_codes[:, Q:].any() and not c.v_codes[:, Q:].any()
+        assert not c.k_scale[:, Q // Gk:].any() and not c.v_scale[:, Q:].any()
+
+
+def pin_cache_rejects_overflow(o):
+    """An append past S_max is refused and leaves the cache unchanged."""
+    c = o.cache(1, 8, 64, 8, 8, 8, 2, FP16)
+    x = _tokens(1, 1, 70, 8)
+    c.append(x[:, :60], x[:, :60])
+    T, Q = c.T, c.Q
+    try:
+        c.append(x[:, 60:70], x[:, 60:70])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("append past S_max accepted")
+    assert (c.T, c.Q) == (T, Q)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -58,6 +58,19 @@ MUTANTS = [
     ("f16_subnormal_scale", "v = ldexpf((float)m, -24);",
      "v = ldexpf((float)m, -25);"),
     ("subtract_dropped", "float a = f - zero;", "float a = f;"),
+    ("cache_flush_early", "while (c->T - c->Q >= c->R + c->G_k) {",
+     "while (c->T - c->Q >= c->R) {"),
+    ("cache_flush_late", "while (c->T - c->Q >= c->R + c->G_k) {",
+     "while (c->T - c->Q > c->R + c->G_k) {"),
+    ("cache_key_group_slot",
+     "c->k_scale + (bh * NG + c->Q / G) * D,",
+     "c->k_scale + (bh * NG + c->T / G) * D,"),
+    ("cache_value_rows_shifted",
+     "c->v_codes + row * row_bytes,",
+     "c->v_codes + (row + 1) * row_bytes,"),
+    ("cache_history_overwrite",
+     "memcpy(c->k + (bh * c->S_max + c->T) * D, k_new + (bh * n + i) * D,",
+     "memcpy(c->k + (bh * c->S_max + c->Q) * D, k_new + (bh * n + i) * D,"),
 ]
 
 
