@@ -39,8 +39,8 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
-KERNEL_SOURCES = ["kivi_device.h", "quant_keys.hip", "quant_values.hip",
-                  "dequant.hip"]
+KERNEL_SOURCES = ["kivi_device.h", "kivi_rows.h", "quant_keys.hip", "quant_values.hip",
+                  "dequant.hip", "cache.hip"]
 
 
 def bytes_per_elem(op, bits, group, dtype_bytes=2):

@@ -142,15 +142,82 @@ kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
                                       hipStream_t stream);
 
 /*
+ * Residual-window cache (KIVI blog post on the fused Metal kernels, section
+ * "What we're actually optimizing": the most recent residual_length tokens
+ * stay in 16-bit floats and, once enough fresh tokens have accumulated, are
+ * quantized as a batch -- a flush -- and folded into the compressed store;
+ * the 0.8.0 release post, section "What KIVI is": the last R tokens are held
+ * exactly and tokens are quantized as they age out of that window).
+ *
+ * After an append brings the cache to T tokens, the first
+ *     Q = G_k * floor((T - R) / G_k)     (0 while T < R)
+ * tokens are quantized, in whole key groups aligned at token 0, and tokens
+ * [Q, T) -- at least min(T, R) and fewer than R + G_k of them -- are held
+ * in 16-bit ring buffers.  The compressed store then equals kivi_quant_keys
+ * / kivi_quant_values of tokens [0, Q) at their own offsets (keys grouped
+ * per channel over G_k tokens, values per token over G_v channels).
+ *
+ * The struct carries the geometry, caller-owned device buffers and the two
+ * counters:
+ *   k_ring, v_ring    [BH, ring, D] 16-bit (dtype); token s in [Q, T) is
+ *                     in slot s % ring.  ring: a multiple of G_k, >= R + G_k
+ *   k_codes, v_codes  [BH, S_max, D*bits/8] bytes (layout as kivi_quant_*)
+ *   k_scale, k_zero   fp32 [BH, ceil(S_max/G_k), D]
+ *   v_scale, v_zero   fp32 [BH, S_max, ceil(D/G_v)]
+ *   T, Q              tokens appended / quantized; 0 and 0 for an empty cache
+ * Storage past Q (codes, params) and ring slots of other tokens are not
+ * written.
+ */
+typedef struct {
+    int64_t BH, D, S_max, R, G_k, G_v, ring;
+    int32_t bits;
+    int32_t dtype;            /* kivi_dtype */
+    void* k_ring;
+    void* v_ring;
+    uint8_t* k_codes;
+    uint8_t* v_codes;
+    float* k_scale;
+    float* k_zero;
+    float* v_scale;
+    float* v_zero;
+    int64_t T, Q;
+} kivi_cache;
+
+/*
+ * Append n tokens of every bh: k_new, v_new [BH, n, D] of the cache's dtype
+ * (device memory, read before the call's work completes).  Enqueues on
+ * `stream`: the flush of tokens [Q, Q_new) (from the ring and from the new
+ * tokens) into the compressed store, then the copy of the new tokens that
+ * stay unquantized into their ring slots; then sets cache->T and cache->Q
+ * to their new values (they describe the state once the stream has reached
+ * this call).  Calls on one cache must be ordered on one stream.
+ * Errors (nothing is enqueued and the struct is unchanged):
+ *   cache == NULL, a NULL buffer, or k_new/v_new NULL with n > 0 KIVI_ERR_NULL
+ *   bits not 1, 2, 4, 8                                       KIVI_ERR_BITS
+ *   G_k not in [1, 32], or G_v not 8, 16 or a multiple of 32  KIVI_ERR_GROUP
+ *   dtype invalid                                             KIVI_ERR_DTYPE
+ *   D not 8, 16, 32, 64, 128 or 256; BH, R, S_max or n < 0; ring not a
+ *   multiple of G_k or < R + G_k; S_max or ring >= 2^31; BH*S_max*D/2
+ *   >= 2^32; an inconsistent state (not 0 <= Q <= T <= S_max,
+ *   Q % G_k == 0, T - Q < ring); T + n > S_max                 KIVI_ERR_SHAPE
+ *   a pointer not 16-byte aligned                             KIVI_ERR_ALIGN
+ */
+kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
+                              const void* v_new, int64_t n,
+                              hipStream_t stream);
+
+/*
  * Profiling aid: the next kernel that a kivi_* call made by this thread
  * launches records `start` when it begins executing and `stop` when it ends
  * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is that kernel's
  * duration alone, without the dispatch gap that events recorded between
  * launches include.  Both events must be created by the caller (e.g.
  * hipEventCreate) and outlive the launch.  The pair is consumed by the next
- * launch (every compute call launches exactly one kernel; calls that launch
- * nothing -- errors, empty tensors -- leave it armed); passing NULL for
- * either disarms it.  This thread-local pair is the library's only state.
+ * launch: every quantize or dequantize call launches exactly one kernel,
+ * kivi_cache_append up to four (the pair times the first), and calls that
+ * launch nothing -- errors, empty tensors -- leave it armed.  Passing NULL
+ * for either disarms it.  This thread-local pair is the library's only
+ * state.
  */
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop);
 

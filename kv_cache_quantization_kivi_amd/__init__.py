@@ -19,6 +19,9 @@ Functions (same names as the C ABI):
     kivi_quant_dequant_values(...)       likewise
     kivi_codes_bytes, kivi_key_param_count, kivi_value_param_count,
     kivi_status_string
+    KiviCache(BH, D, S_max, R, G_k, G_v, bits, dtype), kivi_cache_append
+        the residual-window cache (recent tokens kept exact, whole key
+        groups flushed into packed storage as they age out)
 Tensors are [BH, S, D] (or [B, H, S, D], flattened to BH = B*H), contiguous,
 float16 or bfloat16; codes are uint8 [..., S, D*bits/8]; key params are
 float32 [..., ceil(S/group), D]; value params float32 [..., S, ceil(D/group)].
@@ -254,6 +257,87 @@ def kivi_dequant_values(codes, scale, zero, bits=2, group=32,
     """Value dequantization -> [..., S, D] of out_dtype."""
     return _dequant("kivi_dequant_values", False, codes, scale, zero, bits,
                     group, out_dtype, out, stream)
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("BH", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("S_max", ctypes.c_int64), ("R", ctypes.c_int64),
+                ("G_k", ctypes.c_int64), ("G_v", ctypes.c_int64),
+                ("ring", ctypes.c_int64), ("bits", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k_ring", ctypes.c_void_p),
+                ("v_ring", ctypes.c_void_p), ("k_codes", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("k_zero", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("v_zero", ctypes.c_void_p), ("T", ctypes.c_int64),
+                ("Q", ctypes.c_int64)]
+
+
+class KiviCache:
+    """A residual-window KIVI cache (kivi_cache / kivi_cache_append): the
+    device buffers are torch tensors held here, the counters live in the C
+    struct.  append(k_new, v_new) takes [BH, n, D] (or [..., n, D]) tensors
+    of the cache's dtype on its device and enqueues on the current stream.
+    Attributes: k_ring, v_ring [BH, ring, D]; k_codes, v_codes
+    [BH, S_max, D*bits/8]; k_scale, k_zero [BH, ceil(S_max/G_k), D];
+    v_scale, v_zero [BH, S_max, ceil(D/G_v)]; T, Q."""
+
+    def __init__(self, BH, D, S_max, R=32, G_k=32, G_v=32, bits=2,
+                 dtype=torch.float16, device="cuda", ring=None):
+        if ring is None:
+            ring = ((R + G_k) + G_k - 1) // G_k * G_k
+        dev = torch.device(device)
+        rb = D * bits // 8
+        self.k_ring = torch.empty((BH, ring, D), dtype=dtype, device=dev)
+        self.v_ring = torch.empty((BH, ring, D), dtype=dtype, device=dev)
+        self.k_codes = torch.zeros((BH, S_max, rb), dtype=torch.uint8,
+                                   device=dev)
+        self.v_codes = torch.zeros((BH, S_max, rb), dtype=torch.uint8,
+                                   device=dev)
+        ng = _ngroups(S_max, G_k) if G_k > 0 else 0
+        ngd = _ngroups(D, G_v) if G_v > 0 else 0
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.k_scale = torch.zeros((BH, ng, D), **f32)
+        self.k_zero = torch.zeros((BH, ng, D), **f32)
+        self.v_scale = torch.zeros((BH, S_max, ngd), **f32)
+        self.v_zero = torch.zeros((BH, S_max, ngd), **f32)
+        self.dtype = dtype
+        self.c = _Cache(BH, D, S_max, R, G_k, G_v, ring, bits,
+                        _dtype_code(dtype), *[t.data_ptr() for t in (
+                            self.k_ring, self.v_ring, self.k_codes,
+                            self.v_codes, self.k_scale, self.k_zero,
+                            self.v_scale, self.v_zero)], 0, 0)
+
+    @property
+    def T(self):
+        return self.c.T
+
+    @property
+    def Q(self):
+        return self.c.Q
+
+    def append(self, k_new, v_new, stream=None):
+        """Append n tokens of every bh and flush what ages out."""
+        for t in (k_new, v_new):
+            if t.dtype != self.dtype or not t.is_contiguous():
+                raise ValueError("k_new, v_new: contiguous tensors of the "
+                                 "cache's dtype")
+        n = k_new.shape[-2]
+        if v_new.shape != k_new.shape:
+            raise ValueError("k_new and v_new differ in shape")
+        L = _lib()
+        L.kivi_cache_append.argtypes = [ctypes.POINTER(_Cache),
+                                        ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+        L.kivi_cache_append.restype = ctypes.c_int
+        st = L.kivi_cache_append(ctypes.byref(self.c), _ptr(k_new),
+                                 _ptr(v_new), n,
+                                 _stream(k_new.device, stream))
+        _check(st, "kivi_cache_append")
+
+
+def kivi_cache_append(cache, k_new, v_new, stream=None):
+    """C-ABI name: append to a KiviCache."""
+    cache.append(k_new, v_new, stream)
 
 
 def kivi_time_next_launch(start, stop):

@@ -114,6 +114,48 @@ kivi_status dequant(bool keys, const uint8_t* codes, const float* scale,
                          : kivi::launch_dequant_values(j));
 }
 
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+// Every rule of kivi_cache_append's contract (include/kivi.h), checked
+// before anything is enqueued.
+kivi_status check_cache(const kivi_cache* c, const void* k_new,
+                        const void* v_new, int64_t n) {
+    if (c == nullptr) return KIVI_ERR_NULL;
+    if (!bits_ok(c->bits)) return KIVI_ERR_BITS;
+    if (c->G_k < 1 || c->G_k > 32) return KIVI_ERR_GROUP;
+    if (!(c->G_v == 8 || c->G_v == 16 || (c->G_v >= 32 && c->G_v % 32 == 0)))
+        return KIVI_ERR_GROUP;
+    if (!dtype_ok(c->dtype)) return KIVI_ERR_DTYPE;
+    const int64_t D = c->D;
+    if (!(D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256))
+        return KIVI_ERR_SHAPE;
+    if (c->BH < 0 || c->R < 0 || c->S_max < 0 || n < 0) return KIVI_ERR_SHAPE;
+    if (c->S_max >= (1ll << 31) || c->ring >= (1ll << 31) ||
+        c->ring % c->G_k != 0 || c->ring < c->R + c->G_k)
+        return KIVI_ERR_SHAPE;
+    int64_t cells = 0;   // bounds the kernels' 32-bit lane and row indices
+    if (!mul_ok(c->BH, c->S_max, &cells) || !mul_ok(cells, D / 2, &cells) ||
+        cells >= (1ll << 32))
+        return KIVI_ERR_SHAPE;
+    if (!mul_ok(c->BH, c->ring, &cells) || !mul_ok(cells, D, &cells))
+        return KIVI_ERR_SHAPE;
+    if (c->Q < 0 || c->Q > c->T || c->T > c->S_max || c->Q % c->G_k != 0 ||
+        c->T - c->Q >= c->ring)
+        return KIVI_ERR_SHAPE;
+    if (n > c->S_max - c->T) return KIVI_ERR_SHAPE;
+    const void* bufs[] = {c->k_ring, c->v_ring, c->k_codes, c->v_codes,
+                          c->k_scale, c->k_zero, c->v_scale, c->v_zero};
+    for (const void* b : bufs)
+        if (b == nullptr) return KIVI_ERR_NULL;
+    if (n > 0 && (k_new == nullptr || v_new == nullptr)) return KIVI_ERR_NULL;
+    for (const void* b : bufs)
+        if (!aligned16(b)) return KIVI_ERR_ALIGN;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_ERR_ALIGN;
+    return KIVI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,6 +210,47 @@ kivi_status kivi_dequant_values(const uint8_t* codes, const float* scale,
                                 hipStream_t stream) {
     return dequant(false, codes, scale, zero, BH, S, D, bits, group, out_dt,
                    out, stream);
+}
+
+kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
+                              const void* v_new, int64_t n,
+                              hipStream_t stream) {
+    kivi_status st = check_cache(c, k_new, v_new, n);
+    if (st != KIVI_OK) return st;
+    const int64_t T_new = c->T + n;
+    const int64_t Q_new =
+        T_new >= c->R ? c->G_k * ((T_new - c->R) / c->G_k) : 0;
+    const int64_t Q_to = Q_new > c->Q ? Q_new : c->Q;
+    if (c->BH > 0 && Q_to > c->Q) {
+        // flush tokens [Q, Q_to): keys per channel, values per token
+        kivi::CacheFlushJob f{c->k_ring, k_new, (int)c->dtype, c->BH, c->D,
+                              c->ring, n, c->T, c->Q, Q_to - c->Q, c->S_max,
+                              (int)c->bits, c->G_k, c->G_k, c->k_codes,
+                              c->k_scale, c->k_zero, stream};
+        if (kivi::launch_cache_flush_keys(f) != hipSuccess)
+            return KIVI_ERR_LAUNCH;
+        f.ring = c->v_ring;
+        f.in = v_new;
+        f.group = c->G_v;
+        f.codes = c->v_codes;
+        f.scale = c->v_scale;
+        f.zero = c->v_zero;
+        if (kivi::launch_cache_flush_values(f) != hipSuccess)
+            return KIVI_ERR_LAUNCH;
+    }
+    // the new tokens that stay unquantized go to their ring slots (after the
+    // flush has read the slots they may reuse: same stream, in order)
+    const int64_t s_first = Q_to > c->T ? Q_to : c->T;
+    if (c->BH > 0 && T_new > s_first) {
+        if (kivi::launch_ring_store(k_new, c->k_ring, c->BH, c->D, n, c->T,
+                                    s_first, c->ring, stream) != hipSuccess ||
+            kivi::launch_ring_store(v_new, c->v_ring, c->BH, c->D, n, c->T,
+                                    s_first, c->ring, stream) != hipSuccess)
+            return KIVI_ERR_LAUNCH;
+    }
+    c->T = T_new;
+    c->Q = Q_to;
+    return KIVI_OK;
 }
 
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop) {

@@ -62,15 +62,42 @@ struct DequantJob {
     hipStream_t stream;
 };
 
+// One flush of a residual-window cache: tokens [Q, Q + F) of every bh, where
+// token s < T sits in ring slot s % ring_len of [BH, ring_len, D] and token
+// s >= T is row s - T of the appended [BH, n_in, D]; codes and params go to
+// the compressed store ([BH, S_max, ...]) at the tokens' own offsets.  Q and
+// F are multiples of the key group G_k; D / 8 is a power of two <= 32.
+struct CacheFlushJob {
+    const void* ring;
+    const void* in;
+    int dtype;
+    int64_t BH, D, ring_len, n_in, T, Q, F, S_max;
+    int bits;
+    int64_t G_k;          // key group (the flush unit)
+    int64_t group;        // this tensor's group: G_k for keys, G_v for values
+    uint8_t* codes;
+    float* scale;
+    float* zero;
+    hipStream_t stream;
+};
+
 hipError_t launch_quant_keys(const QuantJob& j);
 hipError_t launch_quant_values(const QuantJob& j);
 hipError_t launch_dequant_keys(const DequantJob& j);
 hipError_t launch_dequant_values(const DequantJob& j);
+hipError_t launch_cache_flush_keys(const CacheFlushJob& j);
+hipError_t launch_cache_flush_values(const CacheFlushJob& j);
+// Copy tokens [s_first, T + n_in) of the appended block into their ring
+// slots (both tensors of one dtype, 16-byte chunks).
+hipError_t launch_ring_store(const void* in, void* ring, int64_t BH,
+                             int64_t D, int64_t n_in, int64_t T,
+                             int64_t s_first, int64_t ring_len,
+                             hipStream_t stream);
 
 // Fallback kernels for shapes the fast kernels do not cover (keys with
-// D % 8 != 0 or group > 32; values with D % 8 != 0, D > 512 or a group that
-// is not 8 times a power of two; dequant with D % 8 != 0 or, for values,
-// group % 8 != 0).
+// D % 8 != 0 or group > 32; values with D % 8 != 0, D > 2048 or a group
+// other than 8, 16 or a multiple of 32; dequant with D % 8 != 0 or, for
+// values, such a group).
 hipError_t launch_generic_quant_keys(const QuantJob& j);
 hipError_t launch_generic_quant_values(const QuantJob& j);
 hipError_t launch_generic_dequant(const DequantJob& j, bool keys);

@@ -1,0 +1,77 @@
+// Where the quantizers find token rows and where they put a token's
+// outputs.  Two layouts share the kernels:
+//   DenseRows - one [BH, S, D] tensor, outputs at the same (bh, token);
+//   CacheRows - a flush of tokens [Q, Q + F) of a residual-window cache:
+//               token s < T is in its ring slot s % ring_len of
+//               [BH, ring_len, D], token s >= T is row s - T of the appended
+//               [BH, n_in, D]; outputs go to the cache's compressed store at
+//               token s of [BH, S_max, ...] (key groups counted from 0).
+// Token indices are 32-bit: the launchers only use these layouts for
+// tensors of fewer than 2^31 tokens per bh.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kivi {
+
+struct DenseRows {
+    const uint16_t* x;
+    int32_t S;      // tokens per bh
+    uint32_t NG;    // key groups per bh (input = output)
+    int32_t G;      // key group size
+
+    // key tiles: group g of bh
+    __device__ int32_t first(uint32_t g) const { return (int32_t)g * G; }
+    __device__ int32_t count(int32_t s0) const { return min(G, S - s0); }
+    __device__ const uint16_t* row(uint32_t bh, int32_t s, int64_t D) const {
+        return x + ((int64_t)bh * S + s) * D;
+    }
+    __device__ int64_t out_row(uint32_t bh, int32_t s) const {
+        return (int64_t)bh * S + s;
+    }
+    __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
+        return (int64_t)bh * NG + g;
+    }
+    // value rows: row r of the flattened [BH * S] rows
+    static constexpr bool kContiguous = true;
+    __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
+        return x + r * D;
+    }
+    __device__ int64_t vout(int64_t r) const { return r; }
+};
+
+struct CacheRows {
+    const uint16_t* ring;   // [BH, ring_len, D]
+    const uint16_t* in;     // [BH, n_in, D]
+    int32_t ring_len, n_in, T, Q, F, S_max;
+    uint32_t NG_out;        // key groups per bh in the compressed store
+    int32_t G;              // key group size (the flush unit)
+
+    __device__ const uint16_t* token(uint32_t bh, int32_t s, int64_t D) const {
+        return s < T ? ring + ((int64_t)bh * ring_len + s % ring_len) * D
+                     : in + ((int64_t)bh * n_in + (s - T)) * D;
+    }
+    __device__ int32_t first(uint32_t g) const { return Q + (int32_t)g * G; }
+    __device__ int32_t count(int32_t) const { return G; }
+    __device__ const uint16_t* row(uint32_t bh, int32_t s, int64_t D) const {
+        return token(bh, s, D);
+    }
+    __device__ int64_t out_row(uint32_t bh, int32_t s) const {
+        return (int64_t)bh * S_max + s;
+    }
+    __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
+        return (int64_t)bh * NG_out + (uint32_t)(Q / G) + g;
+    }
+    static constexpr bool kContiguous = false;
+    __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
+        const uint32_t bh = (uint32_t)r / (uint32_t)F;
+        return token(bh, Q + (int32_t)((uint32_t)r - bh * (uint32_t)F), D);
+    }
+    __device__ int64_t vout(int64_t r) const {
+        const uint32_t bh = (uint32_t)r / (uint32_t)F;
+        return (int64_t)bh * S_max + Q + ((uint32_t)r - bh * (uint32_t)F);
+    }
+};
+
+}  // namespace kivi

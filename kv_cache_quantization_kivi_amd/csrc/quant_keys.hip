@@ -18,6 +18,7 @@
 // ones.  Other waves store directly from each lane.
 #include "kivi_device.h"
 #include "kivi_launch.h"
+#include "kivi_rows.h"
 
 namespace kivi {
 
@@ -223,12 +224,14 @@ __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
     }
 }
 
-template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV>
+// IO: the row layout (DenseRows or CacheRows, kivi_rows.h); NG here is the
+// number of groups per bh that this launch quantizes.
+template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV,
+          typename IO>
 __global__ __launch_bounds__(64) void quant_keys_split_kernel(
-    const uint16_t* __restrict__ x, uint32_t n_lanes, uint32_t D8,
-    uint32_t NG, int32_t S, int32_t G, uint8_t* __restrict__ codes,
-    float* __restrict__ scale, float* __restrict__ zero,
-    uint16_t* __restrict__ recon) {
+    IO io, uint32_t n_lanes, uint32_t D8, uint32_t NG,
+    uint8_t* __restrict__ codes, float* __restrict__ scale,
+    float* __restrict__ zero, uint16_t* __restrict__ recon) {
     const uint32_t gid = blockIdx.x * 64u + threadIdx.x;
     const bool valid = gid < n_lanes;
     const uint32_t lid = valid ? gid : n_lanes - 1u;
@@ -237,17 +240,17 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const uint32_t tile = lid / (D8 * SPLIT);
     const uint32_t g = tile % NG;
     const uint32_t bh = tile / NG;
-    const int32_t s0 = (int32_t)g * G;
-    const int32_t nt = min(G, S - s0);
+    const int32_t s0 = io.first(g);
+    const int32_t nt = io.count(s0);
     const int64_t D = (int64_t)D8 * 8;
-    const int64_t row0 = (int64_t)bh * S + s0;
-    const uint16_t* src = x + row0 * D + (int64_t)c * 8;
 
     uint4 v[TPL];
 #pragma unroll
-    for (int t = 0; t < TPL; ++t)
-        v[t] = load16_nt(src + min(ILV ? (int32_t)part + SPLIT * t
-                                       : (int32_t)part * TPL + t, nt - 1) * D);
+    for (int t = 0; t < TPL; ++t) {
+        const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
+                                   : (int32_t)part * TPL + t, nt - 1);
+        v[t] = load16_nt(io.row(bh, s0 + tt, D) + (int64_t)c * 8);
+    }
 
     MinMax8<DT> mm;
     mm.init(v[0]);
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     if (!valid) return;
 
     if (WQ && part == 0) {
-        const int64_t p = ((int64_t)bh * NG + g) * D + (int64_t)c * 8;
+        const int64_t p = io.out_group(bh, g) * D + (int64_t)c * 8;
         float4* ps = reinterpret_cast<float4*>(scale + p);
         float4* pz = reinterpret_cast<float4*>(zero + p);
         ps[0] = make_float4(pk[0].scale, pk[1].scale, pk[2].scale, pk[3].scale);
@@ -283,9 +286,9 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const int32_t first = ILV ? (int32_t)part : (int32_t)part * TPL;
     const int32_t step = ILV ? SPLIT : 1;
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    uint8_t* dst = WQ ? codes + (row0 + first) * row_bytes + (int64_t)c * BITS
-                      : nullptr;
-    uint16_t* rdst = WR ? recon + (row0 + first) * D + (int64_t)c * 8 : nullptr;
+    const int64_t orow = io.out_row(bh, s0 + first);
+    uint8_t* dst = WQ ? codes + orow * row_bytes + (int64_t)c * BITS : nullptr;
+    uint16_t* rdst = WR ? recon + orow * D + (int64_t)c * 8 : nullptr;
     if (fast)
         emit_split<DT, BITS, WQ, WR, true, TPL>(v, pk, n, dst, step * row_bytes,
                                                 rdst, step * D);
@@ -309,12 +312,12 @@ static hipError_t launch_keys_split_t(const QuantJob& j) {
     const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
     const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * SPLIT;
     const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
+    const DenseRows io{static_cast<const uint16_t*>(j.x), (int32_t)j.S, NG,
+                       (int32_t)j.group};
     return launch_kernel(
-        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true>),
-        dim3(blocks), dim3(64), 0, j.stream,
-        static_cast<const uint16_t*>(j.x), (uint32_t)n_lanes, D8, NG,
-        (int32_t)j.S, (int32_t)j.group, j.codes, j.scale, j.zero,
-        static_cast<uint16_t*>(j.recon));
+        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true, DenseRows>),
+        dim3(blocks), dim3(64), 0, j.stream, io, (uint32_t)n_lanes, D8, NG,
+        j.codes, j.scale, j.zero, static_cast<uint16_t*>(j.recon));
 }
 
 template <int DT, int BITS, int GMAX, int SPLIT>
@@ -373,6 +376,59 @@ static hipError_t launch_keys_bits(const QuantJob& j) {
         case 4: return launch_keys_gmax<DT, 4>(j);
         default: return launch_keys_gmax<DT, 8>(j);
     }
+}
+
+template <int DT, int BITS, int GMAX, int SPLIT>
+static hipError_t launch_cache_keys_t(const CacheFlushJob& j) {
+    constexpr int TPL = GMAX / SPLIT;
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t NG = (uint32_t)(j.F / j.G_k);      // groups flushed per bh
+    const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * SPLIT;
+    const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
+    const CacheRows io{static_cast<const uint16_t*>(j.ring),
+                       static_cast<const uint16_t*>(j.in), (int32_t)j.ring_len,
+                       (int32_t)j.n_in, (int32_t)j.T, (int32_t)j.Q,
+                       (int32_t)j.F, (int32_t)j.S_max,
+                       (uint32_t)((j.S_max + j.G_k - 1) / j.G_k),
+                       (int32_t)j.G_k};
+    return launch_kernel(
+        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, true, false, true,
+                                 CacheRows>),
+        dim3(blocks), dim3(64), 0, j.stream, io, (uint32_t)n_lanes, D8, NG,
+        j.codes, j.scale, j.zero, (uint16_t*)nullptr);
+}
+
+template <int DT, int BITS, int GMAX>
+static hipError_t launch_cache_keys_gmax(const CacheFlushJob& j) {
+    const uint64_t D8 = (uint64_t)(j.D / 8);
+    const uint64_t items = (uint64_t)j.BH * (j.F / j.G_k) * D8;
+    if (items < kKeySplitBelow && 64 % (D8 * 4) == 0)
+        return launch_cache_keys_t<DT, BITS, GMAX, 4>(j);
+    return launch_cache_keys_t<DT, BITS, GMAX, 2>(j);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_cache_keys_bits(const CacheFlushJob& j) {
+    if (j.G_k <= 8) return launch_cache_keys_gmax<DT, BITS, 8>(j);
+    if (j.G_k <= 16) return launch_cache_keys_gmax<DT, BITS, 16>(j);
+    return launch_cache_keys_gmax<DT, BITS, 32>(j);
+}
+
+template <int DT>
+static hipError_t launch_cache_keys_dt(const CacheFlushJob& j) {
+    switch (j.bits) {
+        case 1: return launch_cache_keys_bits<DT, 1>(j);
+        case 2: return launch_cache_keys_bits<DT, 2>(j);
+        case 4: return launch_cache_keys_bits<DT, 4>(j);
+        default: return launch_cache_keys_bits<DT, 8>(j);
+    }
+}
+
+// The caller guarantees: D / 8 a power of two <= 32, G_k <= 32, F a
+// multiple of G_k, and fewer than 2^31 lanes.
+hipError_t launch_cache_flush_keys(const CacheFlushJob& j) {
+    return j.dtype == DT_F16 ? launch_cache_keys_dt<DT_F16>(j)
+                             : launch_cache_keys_dt<DT_BF16>(j);
 }
 
 hipError_t launch_quant_keys(const QuantJob& j) {

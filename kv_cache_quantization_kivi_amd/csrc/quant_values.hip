@@ -19,6 +19,7 @@
 // and store nothing.
 #include "kivi_device.h"
 #include "kivi_launch.h"
+#include "kivi_rows.h"
 
 namespace kivi {
 
@@ -98,9 +99,11 @@ constexpr int kRecWaveBytes = 64 * kRecLaneStride;
 // vec: D % 32 == 0, so a lane's codes are one naturally aligned store;
 // tile: D / 32 is a power of two, so lane unit u covers elements
 // [32u, 32u + 32) of the tensor and a wave's input and recon are contiguous.
-template <int DT, int BITS, int GPL, bool WQ, bool WR>
+// IO: the row layout (DenseRows or CacheRows, kivi_rows.h); the staged
+// (tiled) path needs contiguous rows.
+template <int DT, int BITS, int GPL, bool WQ, bool WR, typename IO>
 __global__ __launch_bounds__(256) void quant_values_kernel(
-    const uint16_t* __restrict__ x, int64_t n_rows, uint32_t D8, uint32_t lp,
+    IO io, int64_t n_rows, uint32_t D8, uint32_t lp,
     uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
     uint8_t* __restrict__ codes, float* __restrict__ scale,
     float* __restrict__ zero, uint16_t* __restrict__ recon) {
@@ -114,15 +117,15 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
     const int64_t D = (int64_t)D8 * 8;
     const int32_t ch0 = (int32_t)c * 4;                  // first chunk
     const int32_t nch = min(4, (int32_t)D8 - ch0);       // real chunks (<= 0: pad lane)
-    const uint16_t* rsrc = x + lrow * D;
+    const uint16_t* rsrc = io.vrow(lrow, D);
 
     // Wave-uniform: a whole wave of real rows in a tiled layout.
-    const bool staged = tile && __all(row_ok);
+    const bool staged = IO::kContiguous && tile && __all(row_ok);
     const uint32_t lane = threadIdx.x & 63u;
     uint8_t* L = lds + (threadIdx.x >> 6) * kRecWaveBytes;
     uint4 v[4];
     if (staged) {
-        const uint16_t* wsrc = x + (u - lane) * 32;   // the wave's 4 KiB
+        const uint16_t* wsrc = io.vrow(0, D) + (u - lane) * 32;   // the wave's 4 KiB
         uint4 t[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) t[k] = load16_nt(wsrc + (k * 64 + lane) * 8);
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
     if constexpr (GPL == 1) block_minmax(mn[0], mx[0], red);
 
     if (!staged && (!row_ok || nch <= 0)) return;
+    const int64_t orow = io.vout(row);   // output row of this lane's row
 
     Params pg[GPL];
 #pragma unroll
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
     if constexpr (WQ) {
         if constexpr (GPL == 1) {
             if ((c & ((1u << gl) - 1u)) == 0) {
-                const int64_t pi = row * NGD + (c >> gl);
+                const int64_t pi = orow * NGD + (c >> gl);
                 scale[pi] = pg[0].scale;
                 zero[pi] = pg[0].zero;
             }
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
 #pragma unroll
             for (int t = 0; t < GPL; ++t) {
                 if (t * CPG < nch) {
-                    const int64_t pi = row * NGD + (ch0 / CPG) + t;
+                    const int64_t pi = orow * NGD + (ch0 / CPG) + t;
                     scale[pi] = pg[t].scale;
                     zero[pi] = pg[t].zero;
                 }
@@ -183,8 +187,8 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
 #pragma unroll
     for (int t = 0; t < GPL; ++t) fast = fast && pg[t].fast;
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    uint8_t* cdst = WQ ? codes + row * row_bytes + (int64_t)ch0 * BITS : nullptr;
-    uint16_t* rdst = WR ? recon + row * D + (int64_t)ch0 * 8 : nullptr;
+    uint8_t* cdst = WQ ? codes + orow * row_bytes + (int64_t)ch0 * BITS : nullptr;
+    uint16_t* rdst = WR ? recon + orow * D + (int64_t)ch0 * 8 : nullptr;
     uint64_t q[4];
     uint4 r[4];
 #pragma unroll
@@ -255,10 +259,10 @@ static hipError_t launch_values_t(const QuantJob& j) {
     const uint32_t blocks = (uint32_t)((lanes + 255) / 256);
     const int32_t vec = (D8 % 4) == 0;
     const int32_t tile = vec && (1u << lp) == lpr;
-    return launch_kernel((quant_values_kernel<DT, BITS, GPL, WQ, WR>),
-                       dim3(blocks), dim3(256), 0, j.stream,
-                       static_cast<const uint16_t*>(j.x), n_rows, D8, lp, red,
-                       gl, NGD, vec, tile, j.codes, j.scale, j.zero,
+    const DenseRows io{static_cast<const uint16_t*>(j.x), 0, 0, 1};   // rows only
+    return launch_kernel((quant_values_kernel<DT, BITS, GPL, WQ, WR, DenseRows>),
+                       dim3(blocks), dim3(256), 0, j.stream, io, n_rows, D8,
+                       lp, red, gl, NGD, vec, tile, j.codes, j.scale, j.zero,
                        static_cast<uint16_t*>(j.recon));
 }
 
@@ -286,6 +290,54 @@ static hipError_t launch_values_bits(const QuantJob& j) {
         case 4: return launch_values_gpl<DT, 4>(j);
         default: return launch_values_gpl<DT, 8>(j);
     }
+}
+
+template <int DT, int BITS, int GPL>
+static hipError_t launch_cache_values_t(const CacheFlushJob& j) {
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t gl = GPL == 1 ? log2_ceil((uint64_t)(j.group / 32)) : 0;
+    const uint32_t red = 1u << (gl < lp ? gl : lp);
+    const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
+    const int64_t n_rows = j.BH * j.F;
+    const uint64_t lanes = (uint64_t)n_rows << lp;
+    const uint32_t blocks = (uint32_t)((lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const CacheRows io{static_cast<const uint16_t*>(j.ring),
+                       static_cast<const uint16_t*>(j.in), (int32_t)j.ring_len,
+                       (int32_t)j.n_in, (int32_t)j.T, (int32_t)j.Q,
+                       (int32_t)j.F, (int32_t)j.S_max,
+                       (uint32_t)((j.S_max + j.G_k - 1) / j.G_k),
+                       (int32_t)j.G_k};
+    return launch_kernel(
+        (quant_values_kernel<DT, BITS, GPL, true, false, CacheRows>),
+        dim3(blocks), dim3(256), 0, j.stream, io, n_rows, D8, lp, red, gl, NGD,
+        vec, (int32_t)0, j.codes, j.scale, j.zero, (uint16_t*)nullptr);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_cache_values_bits(const CacheFlushJob& j) {
+    if (j.group == 8) return launch_cache_values_t<DT, BITS, 4>(j);
+    if (j.group == 16) return launch_cache_values_t<DT, BITS, 2>(j);
+    return launch_cache_values_t<DT, BITS, 1>(j);
+}
+
+template <int DT>
+static hipError_t launch_cache_values_dt(const CacheFlushJob& j) {
+    switch (j.bits) {
+        case 1: return launch_cache_values_bits<DT, 1>(j);
+        case 2: return launch_cache_values_bits<DT, 2>(j);
+        case 4: return launch_cache_values_bits<DT, 4>(j);
+        default: return launch_cache_values_bits<DT, 8>(j);
+    }
+}
+
+// The caller guarantees: D / 8 a power of two <= 32 (so D <= 256), a value
+// group of 8, 16 or a multiple of 32, and fewer than 2^31 rows.
+hipError_t launch_cache_flush_values(const CacheFlushJob& j) {
+    return j.dtype == DT_F16 ? launch_cache_values_dt<DT_F16>(j)
+                             : launch_cache_values_dt<DT_BF16>(j);
 }
 
 hipError_t launch_quant_values(const QuantJob& j) {

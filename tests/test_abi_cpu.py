@@ -163,3 +163,54 @@ def test_missing_library_fails_loudly_but_build_module_imports(tmp_path):
                          env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "loud"
+
+
+def test_cache_append_rejects_before_any_launch(K):
+    """kivi_cache_append validates the whole struct and its arguments first:
+    every case below returns its status without a HIP call (fake aligned
+    pointers) and leaves the counters as they were; a valid append that
+    flushes nothing and copies nothing (n = 0) returns OK."""
+    C = K._Cache
+    L = K.raw()
+    L.kivi_cache_append.argtypes = [ctypes.POINTER(C), ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]
+    L.kivi_cache_append.restype = ctypes.c_int
+
+    def cache(**kw):
+        f = dict(BH=2, D=128, S_max=256, R=32, G_k=32, G_v=32, ring=64,
+                 bits=2, dtype=0, k_ring=0x10000, v_ring=0x20000,
+                 k_codes=0x30000, v_codes=0x40000, k_scale=0x50000,
+                 k_zero=0x60000, v_scale=0x70000, v_zero=0x80000, T=0, Q=0)
+        f.update(kw)
+        return C(*[f[name] for name, _ in C._fields_])
+
+    def call(c, n=1, k=0x90000, v=0xA0000):
+        T, Q = c.T, c.Q
+        st = L.kivi_cache_append(ctypes.byref(c), k, v, n, None)
+        assert (c.T, c.Q) == (T, Q) or st == 0
+        return st
+
+    OK, NULL, SHAPE, BITS, GROUP, DTYPE, ALIGN = 0, 1, 2, 3, 4, 5, 6
+    assert L.kivi_cache_append(None, 0x90000, 0xA0000, 1, None) == NULL
+    assert call(cache(), n=0) == OK
+    assert call(cache(bits=3)) == BITS
+    assert call(cache(G_k=0)) == GROUP
+    assert call(cache(G_k=33, ring=66)) == GROUP
+    assert call(cache(G_v=24)) == GROUP
+    assert call(cache(dtype=2)) == DTYPE
+    assert call(cache(D=96)) == SHAPE
+    assert call(cache(D=512)) == SHAPE
+    assert call(cache(ring=48)) == SHAPE            # not a multiple of G_k
+    assert call(cache(ring=32)) == SHAPE            # < R + G_k
+    assert call(cache(R=-1)) == SHAPE
+    assert call(cache(S_max=1 << 31)) == SHAPE
+    assert call(cache(BH=1 << 20, S_max=1 << 20)) == SHAPE   # 32-bit lanes
+    assert call(cache(T=10, Q=32)) == SHAPE         # Q > T
+    assert call(cache(T=40, Q=8)) == SHAPE          # Q not group-aligned
+    assert call(cache(T=100, Q=0)) == SHAPE         # T - Q >= ring
+    assert call(cache(T=250, Q=224), n=7) == SHAPE  # past S_max
+    assert call(cache(k_codes=0)) == NULL
+    assert call(cache(), k=0) == NULL
+    assert call(cache(v_zero=0x80004)) == ALIGN
+    assert call(cache(), v=0xA0008) == ALIGN
