@@ -252,13 +252,257 @@ def calibrate_copy(torch, dev, mb, reps):
     print(json.dumps({"calibration": res, "size_bytes": n}), flush=True)
 
 
+# --------------------------------------------------------------------------
+# residual-window cache workloads (kivi_cache_append)
+# --------------------------------------------------------------------------
+
+def flush_plan(cw):
+    """The appends of one step, as the cache's rule schedules them: per
+    append (T before, Q before, n, tokens flushed F, tokens stored in the
+    ring), per bh.  Q = G_k * floor((T - R) / G_k)."""
+    def q_of(t):
+        return cw.group_k * ((t - cw.R) // cw.group_k) if t >= cw.R else 0
+    T, Q = cw.T0, q_of(cw.T0)
+    plan = []
+    for _ in range(cw.appends):
+        Tn = T + cw.n
+        Qn = max(q_of(Tn), Q)
+        plan.append((T, Q, cw.n, Qn - Q, Tn - max(Qn, T)))
+        T, Q = Tn, Qn
+    return plan
+
+
+def cache_bytes(cw, F, copy, keys_flush_only=False):
+    """Algorithmic bytes of one append: the F flushed tokens of K and V read
+    once, their codes and params written once, and the tokens that stay
+    unquantized read once and written once to the ring."""
+    D = cw.D
+    kf = F * D * 2 + F * D * cw.bits // 8 + (F // cw.group_k) * D * 8
+    if keys_flush_only:
+        return kf * cw.BH
+    vf = F * D * 2 + F * D * cw.bits // 8 + F * (-(-D // cw.group_v)) * 8
+    ring = 2 * copy * D * 2 * 2
+    return (kf + vf + ring) * cw.BH
+
+
+def cache_cpu_baseline(cw, threads, plan, step_bytes):
+    """The oracle's cache (token-by-token scheduler) on a sample of whole bh
+    slices: the same appends from the same starting state, timed on
+    `threads` threads (a cache per contiguous block of slices) and on one."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    O = oracle.default()
+    tw = cw.tokens()
+    n_bh = min(cw.BH, max(1, threads))
+    k = W.gen_tensor(tw, "K", range(n_bh))
+    v = W.gen_tensor(tw, "V", range(n_bh))
+    S_max = cw.T0 + cw.n * cw.appends
+    pw = W.Workload(cw.name, cw.BH, max(cw.T0, 1), cw.D, cw.dtype, cw.bits,
+                    cw.group_k, cw.group_v, cw.seed + 100, tw.key_kind,
+                    tw.value_kind, cw.desc)
+    pk = W.gen_tensor(pw, "K", range(n_bh))[:, :cw.T0]
+    pv = W.gen_tensor(pw, "V", range(n_bh))[:, :cw.T0]
+
+    def run(a, b, timed):
+        c = O.cache(b - a, cw.D, S_max, cw.R, cw.group_k, cw.group_v,
+                    cw.bits, cw.dtype)
+        c.append(np.ascontiguousarray(pk[a:b]), np.ascontiguousarray(pv[a:b]))
+        t0 = time.perf_counter()
+        for i in range(cw.appends):
+            sl = slice(i * cw.n, (i + 1) * cw.n)
+            c.append(np.ascontiguousarray(k[a:b, sl]),
+                     np.ascontiguousarray(v[a:b, sl]))
+        return time.perf_counter() - t0
+
+    dt1 = run(0, 1, True)
+    cuts = np.linspace(0, n_bh, n_bh + 1).astype(int)
+    with ThreadPoolExecutor(max_workers=n_bh) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda ab: run(ab[0], ab[1], True),
+                    zip(cuts[:-1], cuts[1:])))
+        dtn = time.perf_counter() - t0
+    per_bh = step_bytes / cw.BH
+    return {
+        "value": round(per_bh * n_bh / dtn / 1e9, 4),
+        "unit": "GB/s",
+        "cores": n_bh,
+        "kind": "oracle",
+        "sample": (f"{n_bh} of {cw.BH} (bh) slices, one step ({cw.appends} "
+                   f"append(s) of {cw.n} token(s) from T = {cw.T0}): "
+                   f"{dtn:.3f} s on {n_bh} threads, one slice per thread "
+                   f"(value); {dt1:.3f} s for one slice on 1 thread; the "
+                   "cache's setup appends are not timed"),
+        "single_thread_value": round(per_bh / dt1 / 1e9, 4),
+    }
+
+
+def cache_bench(args, cw, K, torch, dev):
+    """One step = `appends` calls of kivi_cache_append on a cache reset to
+    T0 tokens (counters only; the ring and the store keep real data from
+    a setup append).  Launch-bound steps are one HIP graph replay."""
+    tdt = torch.float16 if cw.dtype == W.FP16 else torch.bfloat16
+    tw = cw.tokens()
+    plan = flush_plan(cw)
+    step_bytes = sum(cache_bytes(cw, F, cp) for _, _, _, F, cp in plan)
+    S_max = cw.T0 + cw.n * cw.appends
+    cache = K.KiviCache(cw.BH, cw.D, S_max, cw.R, cw.group_k, cw.group_v,
+                        cw.bits, tdt, dev)
+    if cw.T0:
+        pw = W.Workload(cw.name, cw.BH, cw.T0, cw.D, cw.dtype, cw.bits,
+                        cw.group_k, cw.group_v, cw.seed + 100, tw.key_kind,
+                        tw.value_kind, cw.desc)
+        pk = torch.from_numpy(W.gen_tensor(pw, "K").view(np.int16)).view(tdt)
+        pv = torch.from_numpy(W.gen_tensor(pw, "V").view(np.int16)).view(tdt)
+        for a in range(0, cw.T0, 2048):
+            cache.append(pk[:, a:a + 2048].contiguous().to(dev),
+                         pv[:, a:a + 2048].contiguous().to(dev))
+    T0, Q0 = cache.T, cache.Q
+    set_bytes = 2 * cw.BH * cw.n * cw.appends * cw.D * 2
+    P = args.pool or max(2, min(64, int(np.ceil(1.0e9 / set_bytes))))
+    pool = []
+    for p in range(P):
+        kv = []
+        for tensor in ("K", "V"):
+            x = torch.from_numpy(W.gen_tensor(tw, tensor, pool=p).view(
+                np.int16)).view(tdt)
+            kv.append([x[:, i * cw.n:(i + 1) * cw.n].contiguous().to(dev)
+                       for i in range(cw.appends)])
+        pool.append(kv)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, arm=None):
+        cache.c.T, cache.c.Q = T0, Q0
+        ks, vs = pool[i % P]
+        for a in range(cw.appends):
+            if arm is not None:
+                K.kivi_time_next_launch(*arm[a])
+            cache.append(ks[a], vs[a])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    use_graphs = (args.launch == "graphs" or
+                  (args.launch == "auto" and step_bytes < 256e6))
+    graphs = None
+    if use_graphs:
+        graphs = []
+        cap = torch.cuda.Stream(device=dev)
+        for ph in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(ph)
+            graphs.append(g)
+            g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        if graphs is not None:
+            graphs[(args.warmup + i) % P].replay()
+        else:
+            step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # kernel durations: the first kernel of every append (the key flush when
+    # the append flushes, else the ring store of keys and values), eagerly,
+    # K more steps
+    def pairs():
+        ev = [(torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True))
+              for _ in range(cw.appends)]
+        for a, b in ev:
+            a.record(stream)
+            b.record(stream)
+        return ev
+    arms = [pairs() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, arms[i])
+    torch.cuda.synchronize()
+    kinds = {}
+    for a, (_, _, n, F, cp) in enumerate(plan):
+        name = "cache_flush_keys" if F else "cache_ring_store"
+        b = (cache_bytes(cw, F, cp, keys_flush_only=True) if F
+             else cw.BH * cp * cw.D * 2 * 2 * 2)
+        d = [arms[i][a][0].elapsed_time(arms[i][a][1])
+             for i in range(args.steps)]
+        kinds.setdefault(name, (b, []))[1].extend(d)
+    per_kernel = {}
+    for name, (b, d) in kinds.items():
+        avg = float(np.mean(d))
+        per_kernel[name] = {
+            "avg_us": round(avg * 1e3, 3),
+            "median_us": round(float(np.median(d)) * 1e3, 3),
+            "min_us": round(float(np.min(d)) * 1e3, 3),
+            "max_us": round(float(np.max(d)) * 1e3, 3),
+            "algorithmic_bytes": int(b),
+            "gbs": round(b / (avg * 1e-3) / 1e9, 1),
+        }
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"])
+    dk = per_kernel[dom]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens = cw.BH * cw.n * cw.appends
+    result = {
+        "metric": METRIC + " (residual-window cache append)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cw.name}: {cw.desc}; step = {cw.appends} "
+                         f"kivi_cache_append call(s) of {cw.n} token(s) x "
+                         f"BH={cw.BH} from T={T0} (Q={Q0})"),
+            "step_algorithmic_bytes": int(step_bytes),
+            "tokens_per_step": tokens,
+            "us_per_append": round(ms_per_step * 1e3 / cw.appends, 3),
+            "input_pool": P,
+            "launch": (f"one HIP graph replay per step ({P} phases)"
+                       if graphs is not None else "eager"),
+            "wall_s": round(t_wall, 4),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": dom,
+            "avg_us": dk["avg_us"],
+            "bound": "hbm",
+            "achieved": dk["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(dom, cw.name, kernel_source_hash()),
+        },
+        "per_kernel": per_kernel,
+        "per_kernel_note": ("value: K steps with no per-launch events; "
+                            "per_kernel: the first kernel of every append of "
+                            "a second pass of K eager steps"),
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": (None if args.no_cpu_baseline else
+                         cache_cpu_baseline(cw, args.cpu_threads, plan,
+                                            step_bytes)),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="roundtrip",
-                    choices=sorted(W.WORKLOADS))
+                    choices=sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
     ap.add_argument("--cpu-sample-bh", type=int, default=0,
@@ -296,6 +540,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
+        return
+    if args.workload in W.CACHE_WORKLOADS:
+        cache_bench(args, W.CACHE_WORKLOADS[args.workload], K, torch, dev)
         return
     w = W.WORKLOADS[args.workload]
     tdt = torch.float16 if w.dtype == W.FP16 else torch.bfloat16

@@ -214,7 +214,7 @@ kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
  * launches include.  Both events must be created by the caller (e.g.
  * hipEventCreate) and outlive the launch.  The pair is consumed by the next
  * launch: every quantize or dequantize call launches exactly one kernel,
- * kivi_cache_append up to four (the pair times the first), and calls that
+ * kivi_cache_append up to three (the pair times the first), and calls that
  * launch nothing -- errors, empty tensors -- leave it armed.  Passing NULL
  * for either disarms it.  This thread-local pair is the library's only
  * state.

@@ -242,10 +242,9 @@ kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
     // flush has read the slots they may reuse: same stream, in order)
     const int64_t s_first = Q_to > c->T ? Q_to : c->T;
     if (c->BH > 0 && T_new > s_first) {
-        if (kivi::launch_ring_store(k_new, c->k_ring, c->BH, c->D, n, c->T,
-                                    s_first, c->ring, stream) != hipSuccess ||
-            kivi::launch_ring_store(v_new, c->v_ring, c->BH, c->D, n, c->T,
-                                    s_first, c->ring, stream) != hipSuccess)
+        if (kivi::launch_ring_store(k_new, v_new, c->k_ring, c->v_ring, c->BH,
+                                    c->D, n, c->T, s_first, c->ring,
+                                    stream) != hipSuccess)
             return KIVI_ERR_LAUNCH;
     }
     c->T = T_new;

@@ -87,11 +87,11 @@ hipError_t launch_dequant_keys(const DequantJob& j);
 hipError_t launch_dequant_values(const DequantJob& j);
 hipError_t launch_cache_flush_keys(const CacheFlushJob& j);
 hipError_t launch_cache_flush_values(const CacheFlushJob& j);
-// Copy tokens [s_first, T + n_in) of the appended block into their ring
-// slots (both tensors of one dtype, 16-byte chunks).
-hipError_t launch_ring_store(const void* in, void* ring, int64_t BH,
-                             int64_t D, int64_t n_in, int64_t T,
-                             int64_t s_first, int64_t ring_len,
+// Copy tokens [s_first, T + n_in) of the appended keys and values into
+// their ring slots, both tensors in one launch (16-byte chunks).
+hipError_t launch_ring_store(const void* k_in, const void* v_in, void* k_ring,
+                             void* v_ring, int64_t BH, int64_t D, int64_t n_in,
+                             int64_t T, int64_t s_first, int64_t ring_len,
                              hipStream_t stream);
 
 // Fallback kernels for shapes the fast kernels do not cover (keys with

@@ -15,6 +15,17 @@
 
 namespace kivi {
 
+// The rows of one key tile (the tokens s0, s0 + 1, ... of one bh): row t is
+// at a + t * D for t < split, else at b + (t - split) * D.
+struct TileRows {
+    const uint16_t* a;
+    const uint16_t* b;
+    int32_t split;
+    __device__ const uint16_t* row(int32_t t, int64_t D) const {
+        return t < split ? a + t * D : b + (t - split) * D;
+    }
+};
+
 struct DenseRows {
     const uint16_t* x;
     int32_t S;      // tokens per bh
@@ -24,8 +35,9 @@ struct DenseRows {
     // key tiles: group g of bh
     __device__ int32_t first(uint32_t g) const { return (int32_t)g * G; }
     __device__ int32_t count(int32_t s0) const { return min(G, S - s0); }
-    __device__ const uint16_t* row(uint32_t bh, int32_t s, int64_t D) const {
-        return x + ((int64_t)bh * S + s) * D;
+    __device__ TileRows tile(uint32_t bh, int32_t s0, int64_t D) const {
+        const uint16_t* a = x + ((int64_t)bh * S + s0) * D;
+        return TileRows{a, a, 0x7fffffff};
     }
     __device__ int64_t out_row(uint32_t bh, int32_t s) const {
         return (int64_t)bh * S + s;
@@ -54,8 +66,13 @@ struct CacheRows {
     }
     __device__ int32_t first(uint32_t g) const { return Q + (int32_t)g * G; }
     __device__ int32_t count(int32_t) const { return G; }
-    __device__ const uint16_t* row(uint32_t bh, int32_t s, int64_t D) const {
-        return token(bh, s, D);
+    // A group is G-aligned and the ring a multiple of G long, so the tile's
+    // ring slots are consecutive; a tile may continue into the new tokens.
+    __device__ TileRows tile(uint32_t bh, int32_t s0, int64_t D) const {
+        const uint16_t* nb = in + ((int64_t)bh * n_in + (s0 - T)) * D;
+        if (s0 >= T) return TileRows{nb, nb, 0x7fffffff};
+        return TileRows{ring + ((int64_t)bh * ring_len + s0 % ring_len) * D,
+                        in + (int64_t)bh * n_in * D, T - s0};
     }
     __device__ int64_t out_row(uint32_t bh, int32_t s) const {
         return (int64_t)bh * S_max + s;

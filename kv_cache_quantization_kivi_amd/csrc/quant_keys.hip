@@ -244,12 +244,13 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const int32_t nt = io.count(s0);
     const int64_t D = (int64_t)D8 * 8;
 
+    const TileRows rows = io.tile(bh, s0, D);
     uint4 v[TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
         const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
                                    : (int32_t)part * TPL + t, nt - 1);
-        v[t] = load16_nt(io.row(bh, s0 + tt, D) + (int64_t)c * 8);
+        v[t] = load16_nt(rows.row(tt, D) + (int64_t)c * 8);
     }
 
     MinMax8<DT> mm;

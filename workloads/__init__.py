@@ -71,6 +71,51 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class CacheWorkload:
+    """A residual-window cache workload: a step appends `appends` blocks of
+    `n` tokens to a cache that starts the step holding T0 tokens (the
+    counters are reset before every step)."""
+    name: str
+    BH: int
+    D: int
+    dtype: int
+    bits: int
+    group_k: int
+    group_v: int
+    R: int
+    T0: int
+    n: int
+    appends: int
+    seed: int
+    key_kind: str
+    value_kind: str
+    desc: str
+
+    def tokens(self):
+        """The Workload that draws this step's new tokens ([BH, n*appends,
+        D] of the same recipes)."""
+        return Workload(self.name, self.BH, self.n * self.appends, self.D,
+                        self.dtype, self.bits, self.group_k, self.group_v,
+                        self.seed, self.key_kind, self.value_kind, self.desc)
+
+
+CACHE_WORKLOADS = {
+    w.name: w for w in [
+        CacheWorkload("cache-prefill", 112, 128, FP16, 2, 32, 32, 32, 0, 2048,
+                      1, 6, "prefill", "normal05",
+                      "prefill chunk of 2048 tokens into an empty residual-"
+                      "window cache (R = 32): flush 2016 tokens, keep 32; "
+                      "28 layers x 4 KV heads, D=128, fp16, 2-bit"),
+        CacheWorkload("cache-decode", 224, 128, FP16, 2, 32, 32, 32, 2059, 1,
+                      32, 7, "outlier15", "normal",
+                      "32 decode tokens appended one at a time after a "
+                      "2059-token prompt (R = 32): one flush of 32 tokens; "
+                      "28 layers x 8 KV heads, D=128, fp16, 2-bit"),
+    ]
+}
+
+
 def _rng(w, tensor, bh, pool):
     return np.random.default_rng([w.seed, _TENSOR_ID[tensor], bh, pool])
 
