@@ -229,6 +229,44 @@ class OracleCache:
     def Q(self):
         return self.c.Q
 
+    def dequantized(self, which):
+        """The cache as the pages' attention sees it: tokens [0, Q)
+        dequantized (to the cache's 16-bit type, exactly as the dequantizers
+        produce them) followed by the exact tokens [Q, T); [BH, T, D] uint16
+        patterns."""
+        c = self.c
+        Q, T = c.Q, c.T
+        if which == "K":
+            deq = self.o.dequant_keys(
+                np.ascontiguousarray(self.k_codes[:, :Q]),
+                np.ascontiguousarray(self.k_scale[:, :Q // c.G_k]),
+                np.ascontiguousarray(self.k_zero[:, :Q // c.G_k]),
+                (c.BH, Q, c.D), c.bits, c.G_k, c.dtype)
+            tail = self.k[:, Q:T]
+        else:
+            deq = self.o.dequant_values(
+                np.ascontiguousarray(self.v_codes[:, :Q]),
+                np.ascontiguousarray(self.v_scale[:, :Q]),
+                np.ascontiguousarray(self.v_zero[:, :Q]),
+                (c.BH, Q, c.D), c.bits, c.G_v, c.dtype)
+            tail = self.v[:, Q:T]
+        return np.concatenate([deq, tail], axis=1)
+
+    def attend(self, q, sm_scale):
+        """Decode attention of q [BH, n_q, D] (16-bit patterns; n_q query
+        heads share each KV head) over all T cached tokens, in float64:
+        softmax(sm_scale * q K^T) V with K, V from dequantized().  Returns
+        float64 [BH, n_q, D]."""
+        dt = self.c.dtype
+        Kf = self.o.widen(self.dequantized("K"), dt).astype(np.float64)
+        Vf = self.o.widen(self.dequantized("V"), dt).astype(np.float64)
+        qf = self.o.widen(np.ascontiguousarray(q), dt).astype(np.float64)
+        s = np.einsum("bjd,btd->bjt", qf, Kf) * float(sm_scale)
+        s -= s.max(axis=2, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=2, keepdims=True)
+        return np.einsum("bjt,btd->bjd", p, Vf)
+
     def append(self, k_new, v_new):
         k_new = np.ascontiguousarray(k_new, dtype=np.uint16)
         v_new = np.ascontiguousarray(v_new, dtype=np.uint16)

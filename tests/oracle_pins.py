@@ -603,4 +603,69 @@ def pin_cache_rejects_overflow(o):
     assert (c.T, c.Q) == (T, Q)
 
 
+# --------------------------------------------------------------------------
+# Decode attention over the cache (reading the compressed store)
+# --------------------------------------------------------------------------
+
+def _sdpa_f64(q, k, v, sm_scale):
+    """torch's scaled_dot_product_attention on the CPU in float64 (a library
+    routine independent of the oracle's own softmax)."""
+    import torch
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, None], torch.from_numpy(k)[:, None],
+        torch.from_numpy(v)[:, None], scale=float(sm_scale))
+    return out[:, 0].numpy()
+
+
+def pin_attend_matches_library_sdpa(o):
+    """KIVI blog post on the fused Metal kernels, "So why does the kernel
+    ship?": attention that reads the packed codes must equal attention over
+    the dequantized cache.  The oracle's attend() against torch's SDPA
+    (float64, CPU) on the K, V that the plain dequantizers give for tokens
+    [0, Q) and the exact tokens [Q, T); with several query heads per KV
+    head, and with nothing quantized yet (T < R + G)."""
+    for T, R in ((300, 32), (40, 32)):
+        c = o.cache(3, 64, 320, R, 32, 32, 2, FP16)
+        k, v = _tokens(21, 3, T, 64), _tokens(22, 3, T, 64)
+        c.append(k, v)
+        q = _tokens(23, 3, 4, 64)
+        sm = 1.0 / 8.0
+        got = c.attend(q, sm)
+        K = o.widen(c.dequantized("K"), FP16).astype(np.float64)
+        V = o.widen(c.dequantized("V"), FP16).astype(np.float64)
+        Qf = o.widen(q, FP16).astype(np.float64)
+        ref = _sdpa_f64(Qf, K, V, sm)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (T, R)
+        # the quantized part really is the dequantized store ...
+        Qn = c.Q
+        deq = o.dequant_keys(c.k_codes[:, :Qn], c.k_scale[:, :Qn // 32],
+                             c.k_zero[:, :Qn // 32], (3, Qn, 64), 2, 32, FP16)
+        assert np.array_equal(c.dequantized("K")[:, :Qn], deq)
+        # ... and the rest the exact tokens
+        assert np.array_equal(c.dequantized("V")[:, Qn:], v[:, Qn:T])
+
+
+def pin_attend_closed_forms(o):
+    """q = 0 gives equal weights, so the output is the mean of the V rows;
+    a single cached token gives that token's V; the output is a convex
+    combination of V rows (within their per-channel min and max)."""
+    c = o.cache(2, 32, 64, 4, 8, 8, 4, BF16)
+    k, v = _tokens(31, 2, 50, 32), _tokens(32, 2, 50, 32)
+    c.append(k, v)
+    V = o.widen(c.dequantized("V"), BF16).astype(np.float64)
+    zero_q = np.zeros((2, 3, 32), np.uint16)
+    got = c.attend(zero_q, 0.2)
+    assert np.allclose(got, V.mean(axis=1)[:, None, :].repeat(3, 1),
+                       rtol=1e-12, atol=1e-12)
+    q = _tokens(33, 2, 3, 32)
+    got = c.attend(q, 0.2)
+    assert (got <= V.max(axis=1)[:, None, :] + 1e-12).all()
+    assert (got >= V.min(axis=1)[:, None, :] - 1e-12).all()
+    one = o.cache(1, 32, 8, 4, 8, 8, 2, FP16)
+    one.append(k[:1, :1], v[:1, :1])
+    got = one.attend(q[:1], 0.2)
+    vf = o.widen(v[:1, :1], FP16).astype(np.float64)
+    assert np.allclose(got, vf.repeat(3, 1), rtol=0, atol=0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
