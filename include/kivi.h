@@ -207,6 +207,39 @@ kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
                               hipStream_t stream);
 
 /*
+ * Decode attention over a residual-window cache, reading the compressed
+ * store directly (KIVI blog post on the fused Metal kernels, section "So
+ * why does the kernel ship?": the memory and speed win needs packed storage
+ * and attention that expands the codes in registers, never in memory).
+ * For every bh and query head j < n_q (n_q query heads share each KV head):
+ *     out[bh, j] = softmax_t(sm_scale * q[bh, j] . K[bh, t]) V[bh, t]
+ * over the cache's T tokens, where K, V of tokens t < Q are the codes
+ * reconstructed with their group's params -- keys RN(RN(code * scale) +
+ * zero) in fp32, values exactly as kivi_dequant_values gives them -- and
+ * tokens t >= Q are the exact tokens in the rings.  fp32 scores, softmax
+ * and accumulation; out is rounded to the cache's dtype.
+ *   q    in  : [BH, n_q, D] of the cache's dtype
+ *   out  out : [BH, n_q, D] of the cache's dtype
+ *   work     : device scratch of at least kivi_cache_attend_work_bytes
+ *              bytes (16-byte aligned); its contents are not used after
+ *              the call
+ * Uses the cache's counters at the time of the call; launches two kernels.
+ * Errors (nothing is launched): any kivi_cache_append rule on the struct;
+ * D not 64 or 128, G_k not 8, 16 or 32, T < 1 or BH >= 65536
+ * (KIVI_ERR_SHAPE / KIVI_ERR_GROUP); n_q not in [1, 8] (KIVI_ERR_SHAPE);
+ * a NULL pointer (KIVI_ERR_NULL); a misaligned one (KIVI_ERR_ALIGN);
+ * work_bytes too small (KIVI_ERR_SHAPE).
+ */
+kivi_status kivi_cache_attend(const kivi_cache* cache, const void* q,
+                              int64_t n_q, float sm_scale, void* out,
+                              void* work, int64_t work_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes kivi_cache_attend needs for this cache (at its current T)
+ * and n_q; -1 if the arguments are invalid. */
+int64_t kivi_cache_attend_work_bytes(const kivi_cache* cache, int64_t n_q);
+
+/*
  * Profiling aid: the next kernel that a kivi_* call made by this thread
  * launches records `start` when it begins executing and `stop` when it ends
  * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is that kernel's
@@ -214,7 +247,8 @@ kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
  * launches include.  Both events must be created by the caller (e.g.
  * hipEventCreate) and outlive the launch.  The pair is consumed by the next
  * launch: every quantize or dequantize call launches exactly one kernel,
- * kivi_cache_append up to three (the pair times the first), and calls that
+ * kivi_cache_append up to three and kivi_cache_attend two (the pair times
+ * the first), and calls that
  * launch nothing -- errors, empty tensors -- leave it armed.  Passing NULL
  * for either disarms it.  This thread-local pair is the library's only
  * state.

@@ -335,6 +335,52 @@ class KiviCache:
         _check(st, "kivi_cache_append")
 
 
+    def attend(self, q, sm_scale, out=None, work=None, stream=None):
+        """Decode attention of q [BH, n_q, D] (the cache's dtype) over the
+        cache's T tokens, reading the packed store (kivi_cache_attend);
+        returns out [BH, n_q, D].  `work` (uint8 device tensor) is allocated
+        if not given."""
+        if q.dtype != self.dtype or not q.is_contiguous():
+            raise ValueError("q: a contiguous tensor of the cache's dtype")
+        n_q = q.shape[-2]
+        L = _lib()
+        L.kivi_cache_attend_work_bytes.argtypes = [ctypes.POINTER(_Cache),
+                                                   ctypes.c_int64]
+        L.kivi_cache_attend_work_bytes.restype = ctypes.c_int64
+        L.kivi_cache_attend.argtypes = [
+            ctypes.POINTER(_Cache), ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p]
+        L.kivi_cache_attend.restype = ctypes.c_int
+        nb = L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
+        if out is None:
+            out = torch.empty_like(q)
+        if work is None:
+            work = torch.empty(max(nb, 16), dtype=torch.uint8,
+                               device=q.device)
+        st = L.kivi_cache_attend(ctypes.byref(self.c), _ptr(q), n_q,
+                                 float(sm_scale), _ptr(out), _ptr(work),
+                                 work.numel(), _stream(q.device, stream))
+        _check(st, "kivi_cache_attend")
+        return out
+
+    def attend_work_bytes(self, n_q):
+        L = _lib()
+        L.kivi_cache_attend_work_bytes.argtypes = [ctypes.POINTER(_Cache),
+                                                   ctypes.c_int64]
+        L.kivi_cache_attend_work_bytes.restype = ctypes.c_int64
+        return L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
+
+
+def kivi_cache_attend(cache, q, sm_scale, out=None, work=None, stream=None):
+    """C-ABI name: decode attention over a KiviCache."""
+    return cache.attend(q, sm_scale, out, work, stream)
+
+
+def kivi_cache_attend_work_bytes(cache, n_q):
+    return cache.attend_work_bytes(n_q)
+
+
 def kivi_cache_append(cache, k_new, v_new, stream=None):
     """C-ABI name: append to a KiviCache."""
     cache.append(k_new, v_new, stream)

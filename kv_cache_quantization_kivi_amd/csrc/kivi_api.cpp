@@ -156,6 +156,16 @@ kivi_status check_cache(const kivi_cache* c, const void* k_new,
     return KIVI_OK;
 }
 
+// kivi_cache_attend's extra rules on top of a valid cache struct.
+kivi_status check_attend(const kivi_cache* c, int64_t n_q) {
+    kivi_status st = check_cache(c, nullptr, nullptr, 0);
+    if (st != KIVI_OK) return st;
+    if (!(c->D == 64 || c->D == 128)) return KIVI_ERR_SHAPE;
+    if (!(c->G_k == 8 || c->G_k == 16 || c->G_k == 32)) return KIVI_ERR_GROUP;
+    if (n_q < 1 || n_q > 8 || c->T < 1 || c->BH >= 65536) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -250,6 +260,35 @@ kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
     c->T = T_new;
     c->Q = Q_to;
     return KIVI_OK;
+}
+
+int64_t kivi_cache_attend_work_bytes(const kivi_cache* c, int64_t n_q) {
+    if (check_attend(c, n_q) != KIVI_OK) return -1;
+    return kivi::attend_work_floats(c->BH, c->T, c->D, n_q) * 4;
+}
+
+kivi_status kivi_cache_attend(const kivi_cache* c, const void* q, int64_t n_q,
+                              float sm_scale, void* out, void* work,
+                              int64_t work_bytes, hipStream_t stream) {
+    kivi_status st = check_attend(c, n_q);
+    if (st != KIVI_OK) return st;
+    if (q == nullptr || out == nullptr || work == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(work))
+        return KIVI_ERR_ALIGN;
+    if (work_bytes < kivi::attend_work_floats(c->BH, c->T, c->D, n_q) * 4)
+        return KIVI_ERR_SHAPE;
+    if (c->BH == 0) return KIVI_OK;
+    kivi::AttendArgs a{
+        c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
+        static_cast<const uint16_t*>(c->k_ring),
+        static_cast<const uint16_t*>(c->v_ring),
+        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+        static_cast<float*>(work), (int32_t)c->D, (int32_t)c->S_max,
+        (int32_t)c->ring, (int32_t)c->G_k, (int32_t)c->G_v,
+        (int32_t)((c->S_max + c->G_k - 1) / c->G_k),
+        (int32_t)((c->D + c->G_v - 1) / c->G_v), (int32_t)c->T, (int32_t)c->Q,
+        (int32_t)n_q, (int32_t)kivi::attend_chunks(c->T), sm_scale};
+    return launched(kivi::launch_attend(a, c->BH, c->dtype, c->bits, stream));
 }
 
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop) {

@@ -81,6 +81,29 @@ struct CacheFlushJob {
     hipStream_t stream;
 };
 
+// Decode attention over a residual-window cache (attend.hip); the caller has
+// checked D in {64, 128}, G_k in {8, 16, 32}, 1 <= n_q <= 8, T >= 1,
+// BH < 65536 and the workspace size (attend_work_floats floats).
+struct AttendArgs {
+    const uint8_t* k_codes;
+    const float* k_scale;
+    const float* k_zero;
+    const uint8_t* v_codes;
+    const float* v_scale;
+    const float* v_zero;
+    const uint16_t* k_ring;
+    const uint16_t* v_ring;
+    const uint16_t* q;     // [BH, n_q, D]
+    uint16_t* out;         // [BH, n_q, D]
+    float* work;
+    int32_t D, S_max, ring, G_k, G_v, NG, NGD, T, Q, n_q, n_chunks;
+    float sm_scale;
+};
+int64_t attend_chunks(int64_t T);
+int64_t attend_work_floats(int64_t BH, int64_t T, int64_t D, int64_t n_q);
+hipError_t launch_attend(const AttendArgs& a, int64_t BH, int dtype, int bits,
+                         hipStream_t stream);
+
 hipError_t launch_quant_keys(const QuantJob& j);
 hipError_t launch_quant_values(const QuantJob& j);
 hipError_t launch_dequant_keys(const DequantJob& j);
