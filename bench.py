@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
 KERNEL_SOURCES = ["kivi_device.h", "kivi_rows.h", "quant_keys.hip", "quant_values.hip",
-                  "dequant.hip", "cache.hip"]
+                  "dequant.hip", "cache.hip", "attend.hip"]
 
 
 def bytes_per_elem(op, bits, group, dtype_bytes=2):
@@ -496,13 +496,176 @@ def cache_bench(args, cw, K, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+# --------------------------------------------------------------------------
+# decode attention over the packed cache (kivi_cache_attend)
+# --------------------------------------------------------------------------
+
+def attend_bytes(aw, Q):
+    """Algorithmic bytes of one attention call: the packed store of tokens
+    [0, Q) (codes and params of K and V), the exact tokens [Q, T) of K and
+    V, and the queries read once; the outputs written once."""
+    D, T = aw.D, aw.T
+    per_bh = (2 * Q * D * aw.bits // 8 + (Q // aw.group_k) * D * 8
+              + Q * (-(-D // aw.group_v)) * 8 + 2 * (T - Q) * D * 2
+              + aw.n_q * D * 2)
+    out = aw.n_q * D * 2
+    return (per_bh + out) * aw.BH, out * aw.BH
+
+
+def attend_bench(args, aw, K, torch, dev):
+    """One step = one kivi_cache_attend call; the caches rotate over a pool
+    whose packed stores exceed the 256 MB MALL together."""
+    tdt = torch.float16 if aw.dtype == W.FP16 else torch.bfloat16
+    q_of = aw.group_k * ((aw.T - aw.R) // aw.group_k) if aw.T >= aw.R else 0
+    step_bytes, out_bytes = attend_bytes(aw, q_of)
+    P = args.pool or max(2, min(16, int(np.ceil(600e6 / step_bytes))))
+    tw = aw.tokens()
+    caches, qs = [], []
+    for p in range(P):
+        c = K.KiviCache(aw.BH, aw.D, aw.T, aw.R, aw.group_k, aw.group_v,
+                        aw.bits, tdt, dev)
+        kx = torch.from_numpy(W.gen_tensor(tw, "K", pool=p).view(np.int16)).view(tdt)
+        vx = torch.from_numpy(W.gen_tensor(tw, "V", pool=p).view(np.int16)).view(tdt)
+        for a in range(0, aw.T, 2048):
+            c.append(kx[:, a:a + 2048].contiguous().to(dev),
+                     vx[:, a:a + 2048].contiguous().to(dev))
+        assert c.Q == q_of
+        caches.append(c)
+        r = np.random.default_rng([aw.seed, 77, p])
+        qx = (r.standard_normal((aw.BH, aw.n_q, aw.D)) * 0.5).astype(np.float32)
+        qs.append(torch.from_numpy(qx).to(tdt).to(dev))
+    out = torch.empty((aw.BH, aw.n_q, aw.D), dtype=tdt, device=dev)
+    work = torch.empty(max(16, caches[0].attend_work_bytes(aw.n_q)),
+                       dtype=torch.uint8, device=dev)
+    sm = 1.0 / float(np.sqrt(aw.D))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        caches[i % P].attend(qs[i % P], sm, out=out, work=work)
+
+    for i in range(args.warmup):
+        step(i)
+    use_graphs = (args.launch == "graphs" or
+                  (args.launch == "auto" and step_bytes < 256e6))
+    graphs = None
+    if use_graphs:
+        graphs = []
+        cap = torch.cuda.Stream(device=dev)
+        for ph in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(ph)
+            graphs.append(g)
+            g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        if graphs is not None:
+            graphs[(args.warmup + i) % P].replay()
+        else:
+            step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # the attention kernel proper (the first of the call's two launches)
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in ev:
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        K.kivi_time_next_launch(*ev[i])
+        step(args.warmup + args.steps + i)
+    torch.cuda.synchronize()
+    d = [a_.elapsed_time(b_) for a_, b_ in ev]
+    kb = step_bytes - out_bytes
+    avg = float(np.mean(d))
+    pk = {"attend_partial": {
+        "avg_us": round(avg * 1e3, 3),
+        "median_us": round(float(np.median(d)) * 1e3, 3),
+        "min_us": round(float(np.min(d)) * 1e3, 3),
+        "max_us": round(float(np.max(d)) * 1e3, 3),
+        "algorithmic_bytes": int(kb),
+        "gbs": round(kb / (avg * 1e-3) / 1e9, 1)}}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    fp16_bytes = aw.BH * (2 * aw.T * aw.D * 2 + 2 * aw.n_q * aw.D * 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        O = oracle.default()
+        n_bh = min(aw.BH, 16)
+        oc = O.cache(n_bh, aw.D, aw.T, aw.R, aw.group_k, aw.group_v,
+                     aw.bits, aw.dtype)
+        kx = W.gen_tensor(tw, "K", range(n_bh))
+        vx = W.gen_tensor(tw, "V", range(n_bh))
+        oc.append(kx, vx)
+        qx = qs[0][:n_bh].cpu().view(torch.int16).numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oc.attend(qx, sm)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(step_bytes / aw.BH * n_bh / dt / 1e9, 4),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": (f"{n_bh} of {aw.BH} (bh) slices, one attention "
+                          f"call: {dt:.3f} s on 1 thread (float64 numpy; the "
+                          "cache's setup appends are not timed)")}
+    result = {
+        "metric": METRIC + " (decode attention over the packed cache)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{aw.name}: {aw.desc}; step = one "
+                         "kivi_cache_attend call"),
+            "step_algorithmic_bytes": int(step_bytes),
+            "fp16_cache_bytes_same_attention": int(fp16_bytes),
+            "us_per_call": round(ms_per_step * 1e3, 3),
+            "input_pool": P,
+            "launch": (f"one HIP graph replay per step ({P} phases)"
+                       if graphs is not None else "eager"),
+            "wall_s": round(t_wall, 4),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": "attend_partial",
+            "avg_us": pk["attend_partial"]["avg_us"],
+            "bound": "hbm",
+            "achieved": pk["attend_partial"]["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(pk["attend_partial"]["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic("attend_partial", aw.name,
+                                    kernel_source_hash()),
+        },
+        "per_kernel": pk,
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="roundtrip",
-                    choices=sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS))
+                    choices=sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS)
+                    + sorted(W.ATTEND_WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
     ap.add_argument("--cpu-sample-bh", type=int, default=0,
@@ -540,6 +703,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         calibrate_copy(torch, dev, args.calibrate_copy, args.steps)
+        return
+    if args.workload in W.ATTEND_WORKLOADS:
+        attend_bench(args, W.ATTEND_WORKLOADS[args.workload], K, torch, dev)
         return
     if args.workload in W.CACHE_WORKLOADS:
         cache_bench(args, W.CACHE_WORKLOADS[args.workload], K, torch, dev)

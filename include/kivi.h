@@ -225,7 +225,8 @@ kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
  *              the call
  * Uses the cache's counters at the time of the call; launches two kernels.
  * Errors (nothing is launched): any kivi_cache_append rule on the struct;
- * D not 64 or 128, G_k not 8, 16 or 32, T < 1 or BH >= 65536
+ * D not 64 or 128, D * bits < 128, G_k not 8, 16 or 32, T < 1 or
+ * BH >= 65536
  * (KIVI_ERR_SHAPE / KIVI_ERR_GROUP); n_q not in [1, 8] (KIVI_ERR_SHAPE);
  * a NULL pointer (KIVI_ERR_NULL); a misaligned one (KIVI_ERR_ALIGN);
  * work_bytes too small (KIVI_ERR_SHAPE).

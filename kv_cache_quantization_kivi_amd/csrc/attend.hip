@@ -21,8 +21,6 @@
 namespace kivi {
 
 constexpr int kAttChunk = 128;   // tokens per block (one per thread)
-constexpr int kAttMaxQ = 8;      // query heads per KV head
-constexpr int kAttMaxD = 128;    // head dimension
 constexpr int kAttMaxGroups = kAttChunk / 8;   // key groups in a chunk (G_k >= 8)
 
 __device__ __forceinline__ float block_reduce_max(float v, float* red) {
@@ -58,29 +56,52 @@ __device__ __forceinline__ float widen16(uint16_t h) {
 // Workspace per (bh, chunk, query head): m, l, then D partial outputs.
 __host__ __device__ inline int64_t att_slot(int64_t D) { return D + 2; }
 
-template <int DT, int BITS>
+// The 8 codes (8 * BITS bits) of channel chunk c8 from a token's code row
+// held as 32-bit words.
+template <int BITS>
+__device__ __forceinline__ uint64_t row_chunk(const uint32_t* w, int c8) {
+    if constexpr (BITS == 8) {
+        return (uint64_t)w[2 * c8] | ((uint64_t)w[2 * c8 + 1] << 32);
+    } else if constexpr (BITS == 4) {
+        return w[c8];
+    } else {   // 8 or 16 bits inside one word
+        const int bit = c8 * BITS * 8;
+        return (w[bit >> 5] >> (bit & 31)) & ((1u << (8 * BITS)) - 1u);
+    }
+}
+
+// D: head dimension (64 or 128); NQ: query heads per KV head rounded up to
+// 1, 2, 4 or 8 (rows past n_q are zeros and never stored).  One block of
+// kAttChunk threads per (chunk, bh); the caller guarantees D * BITS >= 128
+// (whole 16-byte code rows), G_k in {8, 16, 32} (chunks are group-aligned)
+// and n_q <= NQ.
+template <int DT, int BITS, int D, int NQ>
 __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a) {
-    __shared__ float q_s[kAttMaxQ][kAttMaxD];
-    __shared__ float ks_s[kAttMaxGroups][kAttMaxD + 4];   // key scale, zero
-    __shared__ float kz_s[kAttMaxGroups][kAttMaxD + 4];
-    __shared__ float p_s[kAttMaxQ][kAttChunk];
-    __shared__ __attribute__((aligned(16))) uint16_t v_s[kAttChunk][kAttMaxD];
+    constexpr int D8 = D / 8;
+    constexpr int kRowWords = D * BITS / 32;      // code row as 32-bit words
+    constexpr int PARTS = kAttChunk / D8;         // token parts in phase 3
+    __shared__ __attribute__((aligned(16))) float q_s[NQ][D];
+    __shared__ __attribute__((aligned(16))) float ks_s[kAttMaxGroups][D + 4];
+    __shared__ __attribute__((aligned(16))) float kz_s[kAttMaxGroups][D + 4];
+    __shared__ __attribute__((aligned(16))) float p_s[NQ][kAttChunk];
+    __shared__ __attribute__((aligned(16))) float acc_s[NQ][D];
     __shared__ float red[2];
 
     const int chunk = blockIdx.x;
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
-    const int D = a.D, D8 = a.D / 8, nq = a.n_q;
+    const int nq = a.n_q;
     const int t0 = chunk * kAttChunk;
     const int nt = min(kAttChunk, a.T - t0);           // tokens in this chunk
     const int nq_tok = max(0, min(nt, a.Q - t0));      // of them quantized
-    const int64_t row_bytes = (int64_t)D8 * BITS;
+    constexpr int64_t row_bytes = (int64_t)D8 * BITS;
 
-    // query heads (widened once)
-    for (int i = tid; i < nq * D; i += kAttChunk)
+    // query heads (widened once; padded rows are zero) and the key params
+    // of the chunk's quantized groups
+    for (int i = tid; i < NQ * D; i += kAttChunk)
         q_s[i / D][i % D] =
-            widen16<DT>(a.q[((int64_t)bh * nq + i / D) * D + i % D]);
-    // key params of the chunk's quantized groups (chunks are group-aligned)
+            i / D < nq ? widen16<DT>(a.q[((int64_t)bh * nq + i / D) * D + i % D])
+                       : 0.0f;
     const int g0 = t0 / a.G_k;
     const int ng = (nq_tok + a.G_k - 1) / a.G_k;
     for (int i = tid; i < ng * D; i += kAttChunk) {
@@ -90,16 +111,26 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     }
     __syncthreads();
 
-    // ---- scores: one token per thread ----
-    float sc[kAttMaxQ];
+    // ---- scores: one token per thread, its whole row loaded up front ----
+    float sc[NQ];
 #pragma unroll
-    for (int j = 0; j < kAttMaxQ; ++j) sc[j] = 0.0f;
+    for (int j = 0; j < NQ; ++j) sc[j] = 0.0f;
     const int t = t0 + tid;
     if (tid < nq_tok) {
         const uint8_t* crow = a.k_codes + ((int64_t)bh * a.S_max + t) * row_bytes;
+        uint32_t w[kRowWords];
+#pragma unroll
+        for (int k = 0; k < kRowWords / 4; ++k) {
+            const uint4 x = load16_nt(crow + k * 16);
+            w[4 * k] = x.x;
+            w[4 * k + 1] = x.y;
+            w[4 * k + 2] = x.z;
+            w[4 * k + 3] = x.w;
+        }
         const int g = t / a.G_k - g0;   // this token's group in ks_s / kz_s
+#pragma unroll
         for (int c8 = 0; c8 < D8; ++c8) {
-            const uint64_t packed = load_codes<BITS>(crow + c8 * BITS);
+            const uint64_t packed = row_chunk<BITS>(w, c8);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int d = c8 * 8 + e;
@@ -107,33 +138,35 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
                     (uint32_t)(packed >> (e * BITS)) & ((1u << BITS) - 1u);
                 const float k = recon(code, ks_s[g][d], kz_s[g][d]);
 #pragma unroll
-                for (int j = 0; j < kAttMaxQ; ++j)
-                    if (j < nq) sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
+                for (int j = 0; j < NQ; ++j)
+                    sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
             }
         }
     } else if (tid < nt) {
         const uint16_t* krow =
             a.k_ring + ((int64_t)bh * a.ring + t % a.ring) * D;
+        uint4 x[D8];
+#pragma unroll
+        for (int k = 0; k < D8; ++k) x[k] = load16(krow + k * 8);
+#pragma unroll
         for (int c8 = 0; c8 < D8; ++c8) {
-            const uint4 w = load16(krow + c8 * 8);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            const uint32_t ws[4] = {x[c8].x, x[c8].y, x[c8].z, x[c8].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int d = c8 * 8 + e;
                 const uint16_t h = (uint16_t)(ws[e >> 1] >> ((e & 1) * 16));
                 const float k = widen16<DT>(h);
 #pragma unroll
-                for (int j = 0; j < kAttMaxQ; ++j)
-                    if (j < nq) sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
+                for (int j = 0; j < NQ; ++j)
+                    sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
             }
         }
     }
 
     // ---- softmax partial of the chunk, per query head ----
-    float m[kAttMaxQ], l[kAttMaxQ];
+    float m[NQ], l[NQ];
 #pragma unroll
-    for (int j = 0; j < kAttMaxQ; ++j) {
-        if (j >= nq) break;
+    for (int j = 0; j < NQ; ++j) {
         const float s = tid < nt ? sc[j] * a.sm_scale : -__builtin_huge_valf();
         m[j] = block_reduce_max(s, red);
         const float p = tid < nt ? __expf(s - m[j]) : 0.0f;
@@ -141,59 +174,71 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
         l[j] = block_reduce_sum(p, red);
     }
 
-    // ---- the chunk's values, as 16-bit recon, into LDS ----
-    for (int i = tid; i < nt * D8; i += kAttChunk) {
-        const int tt = i / D8, c8 = i % D8;
+    // ---- partial outputs: thread (channel chunk c8, token part) reads its
+    // tokens' value codes straight from memory (consecutive threads take
+    // consecutive chunks of a row), reconstructs them exactly as the value
+    // dequantizer does, and accumulates p * v; the parts are then summed
+    // with lane shuffles (inside a wave) and LDS (across the two waves).
+    const int c8 = tid % D8, part = tid / D8;
+    float o[NQ][8];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] = 0.0f;
+    const int gv = (c8 * 8) / a.G_v;
+#pragma unroll 4
+    for (int tt = part; tt < nt; tt += PARTS) {
         const int ts = t0 + tt;
         uint4 v;
         if (tt < nq_tok) {
-            const int64_t r = (int64_t)bh * a.S_max + ts;
-            const uint64_t packed = load_codes<BITS>(a.v_codes + r * row_bytes + c8 * BITS);
-            const int64_t p = r * a.NGD + (c8 * 8) / a.G_v;
-            const float s = a.v_scale[p], z = a.v_zero[p];
-            const float sv[8] = {s, s, s, s, s, s, s, s};
-            const float zv[8] = {z, z, z, z, z, z, z, z};
-            v = dequant_chunk<DT, BITS>(packed, sv, zv);
+            const int64_t row = (int64_t)bh * a.S_max + ts;
+            const uint64_t pc = load_codes<BITS>(a.v_codes + row * row_bytes + c8 * BITS);
+            const int64_t p = row * a.NGD + gv;
+            const float sv = a.v_scale[p], zv = a.v_zero[p];
+            const float s8[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
+            const float z8[8] = {zv, zv, zv, zv, zv, zv, zv, zv};
+            v = dequant_chunk<DT, BITS>(pc, s8, z8);
         } else {
             v = load16(a.v_ring + ((int64_t)bh * a.ring + ts % a.ring) * D + c8 * 8);
         }
-        *reinterpret_cast<uint4*>(&v_s[tt][c8 * 8]) = v;
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
+        float pj[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) pj[j] = p_s[j][tt];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = widen16<DT>((uint16_t)(ws[e >> 1] >> ((e & 1) * 16)));
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) o[j][e] = __builtin_fmaf(pj[j], x, o[j][e]);
+        }
     }
+    // parts inside a wave: lanes D8, 2 D8, ... apart
+#pragma unroll
+    for (int msk = D8; msk < 64; msk <<= 1)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[j][e] += __shfl_xor(o[j][e], msk);
+    // the second wave's sum into LDS, the first wave adds it and stores
+    const int lane = tid & 63, wave = tid >> 6;
+    if (wave == 1 && lane < D8)
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc_s[j][c8 * 8 + e] = o[j][e];
     __syncthreads();
-
-    // ---- partial outputs: threads split (channel, token stride) ----
-    const int per = kAttChunk / D;            // threads per channel (1 or 2)
-    const int d = tid % D, part = tid / D;
-    float o[kAttMaxQ];
-#pragma unroll
-    for (int j = 0; j < kAttMaxQ; ++j) o[j] = 0.0f;
-    for (int tt = part; tt < nt; tt += per) {
-        const float v = widen16<DT>(v_s[tt][d]);
-#pragma unroll
-        for (int j = 0; j < kAttMaxQ; ++j)
-            if (j < nq) o[j] = __builtin_fmaf(p_s[j][tt], v, o[j]);
-    }
+    if (wave == 1 || lane >= D8) return;
     float* w = a.work + ((int64_t)bh * a.n_chunks + chunk) * nq * att_slot(D);
-    if (per > 1) {
-        // fold the second half of the threads into the first, through LDS
-        __syncthreads();
-        float* acc = reinterpret_cast<float*>(&v_s[0][0]);   // reuse
-        if (part == 1)
 #pragma unroll
-            for (int j = 0; j < kAttMaxQ; ++j)
-                if (j < nq) acc[j * D + d] = o[j];
-        __syncthreads();
-        if (part == 1) return;
-#pragma unroll
-        for (int j = 0; j < kAttMaxQ; ++j)
-            if (j < nq) o[j] += acc[j * D + d];
-    }
-#pragma unroll
-    for (int j = 0; j < kAttMaxQ; ++j) {
+    for (int j = 0; j < NQ; ++j) {
         if (j >= nq) break;
         float* wj = w + j * att_slot(D);
-        if (d == 0) { wj[0] = m[j]; wj[1] = l[j]; }
-        wj[2 + d] = o[j];
+        if (c8 == 0) {
+            wj[0] = m[j];
+            wj[1] = l[j];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wj[2 + c8 * 8 + e] = o[j][e] + acc_s[j][c8 * 8 + e];
     }
 }
 
@@ -226,12 +271,28 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a) {
     }
 }
 
+template <int DT, int BITS, int D, int NQ>
+static hipError_t launch_partial(const AttendArgs& a, int64_t BH,
+                                 hipStream_t stream) {
+    return launch_kernel((attend_partial_kernel<DT, BITS, D, NQ>),
+                         dim3((uint32_t)a.n_chunks, (uint32_t)BH),
+                         dim3(kAttChunk), 0, stream, a);
+}
+
+template <int DT, int BITS, int D>
+static hipError_t launch_partial_nq(const AttendArgs& a, int64_t BH,
+                                    hipStream_t stream) {
+    if (a.n_q <= 1) return launch_partial<DT, BITS, D, 1>(a, BH, stream);
+    if (a.n_q <= 2) return launch_partial<DT, BITS, D, 2>(a, BH, stream);
+    if (a.n_q <= 4) return launch_partial<DT, BITS, D, 4>(a, BH, stream);
+    return launch_partial<DT, BITS, D, 8>(a, BH, stream);
+}
+
 template <int DT, int BITS>
 static hipError_t launch_attend_t(const AttendArgs& a, int64_t BH,
                                   hipStream_t stream) {
-    hipError_t e = launch_kernel((attend_partial_kernel<DT, BITS>),
-                                 dim3((uint32_t)a.n_chunks, (uint32_t)BH),
-                                 dim3(kAttChunk), 0, stream, a);
+    hipError_t e = a.D == 64 ? launch_partial_nq<DT, BITS, 64>(a, BH, stream)
+                             : launch_partial_nq<DT, BITS, 128>(a, BH, stream);
     if (e != hipSuccess) return e;
     return launch_kernel((attend_merge_kernel<DT>), dim3((uint32_t)BH),
                          dim3(128), 0, stream, a);

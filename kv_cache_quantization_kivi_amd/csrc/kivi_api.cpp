@@ -160,7 +160,8 @@ kivi_status check_cache(const kivi_cache* c, const void* k_new,
 kivi_status check_attend(const kivi_cache* c, int64_t n_q) {
     kivi_status st = check_cache(c, nullptr, nullptr, 0);
     if (st != KIVI_OK) return st;
-    if (!(c->D == 64 || c->D == 128)) return KIVI_ERR_SHAPE;
+    if (!(c->D == 64 || c->D == 128) || c->D * c->bits < 128)
+        return KIVI_ERR_SHAPE;
     if (!(c->G_k == 8 || c->G_k == 16 || c->G_k == 32)) return KIVI_ERR_GROUP;
     if (n_q < 1 || n_q > 8 || c->T < 1 || c->BH >= 65536) return KIVI_ERR_SHAPE;
     return KIVI_OK;

@@ -82,8 +82,9 @@ struct CacheFlushJob {
 };
 
 // Decode attention over a residual-window cache (attend.hip); the caller has
-// checked D in {64, 128}, G_k in {8, 16, 32}, 1 <= n_q <= 8, T >= 1,
-// BH < 65536 and the workspace size (attend_work_floats floats).
+// checked D in {64, 128}, D * bits >= 128, G_k in {8, 16, 32},
+// 1 <= n_q <= 8, T >= 1, BH < 65536 and the workspace size
+// (attend_work_floats floats).
 struct AttendArgs {
     const uint8_t* k_codes;
     const float* k_scale;

@@ -116,6 +116,42 @@ CACHE_WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class AttendWorkload:
+    """Decode attention over a cache holding T tokens (R of them exact):
+    n_q query heads per KV head, one decode position each."""
+    name: str
+    BH: int
+    D: int
+    dtype: int
+    bits: int
+    group_k: int
+    group_v: int
+    R: int
+    T: int
+    n_q: int
+    seed: int
+    key_kind: str
+    value_kind: str
+    desc: str
+
+    def tokens(self):
+        return Workload(self.name, self.BH, self.T, self.D, self.dtype,
+                        self.bits, self.group_k, self.group_v, self.seed,
+                        self.key_kind, self.value_kind, self.desc)
+
+
+ATTEND_WORKLOADS = {
+    w.name: w for w in [
+        AttendWorkload("attend-decode", 224, 128, FP16, 2, 32, 32, 32, 2059,
+                       3, 8, "outlier15", "normal",
+                       "decode attention of 3 query heads per KV head over "
+                       "a 2059-token KIVI cache (2016 tokens packed, 43 "
+                       "exact), 28 layers x 8 KV heads, D=128, fp16, 2-bit"),
+    ]
+}
+
+
 def _rng(w, tensor, bh, pool):
     return np.random.default_rng([w.seed, _TENSOR_ID[tensor], bh, pool])
 
