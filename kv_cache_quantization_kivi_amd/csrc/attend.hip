@@ -10,11 +10,11 @@
 // output o = sum_t exp(s_t - m) v_t, and writes (m, l, o) to the workspace;
 // a second kernel merges the chunks of each bh.
 //
-// Keys of tokens t < Q are reconstructed from codes and their group's
-// params as the dequantizer does, RN(RN(code * scale) + zero), in fp32 (no
-// narrowing to 16 bits); values of tokens t < Q are reconstructed and
-// narrowed exactly as kivi_dequant_values produces them; tokens t >= Q come
-// from the ring as stored.  Scores and the softmax are fp32.
+// Tokens t < Q are used through their codes and params without being
+// rounded to the 16-bit type: a key enters a score as
+// sum_d (q_d scale_d) code_d + sum_d q_d zero_d, a value enters the output as
+// (p scale) code + p zero, both in fp32; tokens t >= Q come from the ring as
+// stored.  Scores, the softmax and all sums are fp32.
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -81,8 +81,18 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     constexpr int kRowWords = D * BITS / 32;      // code row as 32-bit words
     constexpr int PARTS = kAttChunk / D8;         // token parts in phase 3
     __shared__ __attribute__((aligned(16))) float q_s[NQ][D];
-    __shared__ __attribute__((aligned(16))) float ks_s[kAttMaxGroups][D + 4];
-    __shared__ __attribute__((aligned(16))) float kz_s[kAttMaxGroups][D + 4];
+    // Key params of the chunk's groups, as scale / zero rows (ks, kz) or,
+    // when they fit (groups * NQ <= kQsRows), as the scaled queries
+    // qs[g][j][d] = q[j][d] * scale[g][d] with bias[g][j] = sum_d q[j][d] *
+    // zero[g][d], so that a score is sum_d qs * code + bias.
+    constexpr int kKpStride = D + 4;
+    constexpr int kQsRows = 16;
+    __shared__ __attribute__((aligned(16))) float kp_s[2 * kAttMaxGroups * kKpStride];
+    float (*ks_s)[kKpStride] = reinterpret_cast<float (*)[kKpStride]>(kp_s);
+    float (*kz_s)[kKpStride] =
+        reinterpret_cast<float (*)[kKpStride]>(kp_s + kAttMaxGroups * kKpStride);
+    float (*qs_s)[D] = reinterpret_cast<float (*)[D]>(kp_s);
+    float* bias_s = kp_s + kQsRows * D;
     __shared__ __attribute__((aligned(16))) float p_s[NQ][kAttChunk];
     __shared__ __attribute__((aligned(16))) float acc_s[NQ][D];
     __shared__ float red[2];
@@ -104,10 +114,31 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
                        : 0.0f;
     const int g0 = t0 / a.G_k;
     const int ng = (nq_tok + a.G_k - 1) / a.G_k;
-    for (int i = tid; i < ng * D; i += kAttChunk) {
-        const int64_t p = ((int64_t)bh * a.NG + g0 + i / D) * D + i % D;
-        ks_s[i / D][i % D] = a.k_scale[p];
-        kz_s[i / D][i % D] = a.k_zero[p];
+    const bool scaled_q = ng * NQ <= kQsRows;     // block-uniform
+    __syncthreads();                             // q_s complete
+    if (scaled_q) {
+        float* z_s = bias_s + kQsRows;   // the groups' zeros, [ng][D]
+        for (int i = tid; i < ng * NQ * D; i += kAttChunk) {
+            const int row = i / D, d = i % D;    // row = g * NQ + j
+            const int64_t p = ((int64_t)bh * a.NG + g0 + row / NQ) * D + d;
+            qs_s[row][d] = q_s[row % NQ][d] * a.k_scale[p];
+        }
+        for (int i = tid; i < ng * D; i += kAttChunk)
+            z_s[i] = a.k_zero[((int64_t)bh * a.NG + g0 + i / D) * D + i % D];
+        __syncthreads();
+        // bias[g][j]: one thread per (g, j), a plain sum over d
+        if (tid < ng * NQ) {
+            const int g = tid / NQ, j = tid % NQ;
+            float b = 0.0f;
+            for (int d = 0; d < D; ++d) b = __builtin_fmaf(q_s[j][d], z_s[g * D + d], b);
+            bias_s[tid] = b;
+        }
+    } else {
+        for (int i = tid; i < ng * D; i += kAttChunk) {
+            const int64_t p = ((int64_t)bh * a.NG + g0 + i / D) * D + i % D;
+            ks_s[i / D][i % D] = a.k_scale[p];
+            kz_s[i / D][i % D] = a.k_zero[p];
+        }
     }
     __syncthreads();
 
@@ -127,19 +158,37 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
             w[4 * k + 2] = x.z;
             w[4 * k + 3] = x.w;
         }
-        const int g = t / a.G_k - g0;   // this token's group in ks_s / kz_s
+        const int g = t / a.G_k - g0;   // this token's group in the chunk
+        if (scaled_q) {
 #pragma unroll
-        for (int c8 = 0; c8 < D8; ++c8) {
-            const uint64_t packed = row_chunk<BITS>(w, c8);
+            for (int c8 = 0; c8 < D8; ++c8) {
+                const uint64_t packed = row_chunk<BITS>(w, c8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = c8 * 8 + e;
-                const uint32_t code =
-                    (uint32_t)(packed >> (e * BITS)) & ((1u << BITS) - 1u);
-                const float k = recon(code, ks_s[g][d], kz_s[g][d]);
+                for (int e = 0; e < 8; ++e) {
+                    const int d = c8 * 8 + e;
+                    const float code = (float)((uint32_t)(packed >> (e * BITS)) &
+                                               ((1u << BITS) - 1u));
 #pragma unroll
-                for (int j = 0; j < NQ; ++j)
-                    sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
+                    for (int j = 0; j < NQ; ++j)
+                        sc[j] = __builtin_fmaf(qs_s[g * NQ + j][d], code, sc[j]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) sc[j] += bias_s[g * NQ + j];
+        } else {
+#pragma unroll
+            for (int c8 = 0; c8 < D8; ++c8) {
+                const uint64_t packed = row_chunk<BITS>(w, c8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int d = c8 * 8 + e;
+                    const uint32_t code =
+                        (uint32_t)(packed >> (e * BITS)) & ((1u << BITS) - 1u);
+                    const float k = recon(code, ks_s[g][d], kz_s[g][d]);
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j)
+                        sc[j] = __builtin_fmaf(q_s[j][d], k, sc[j]);
+                }
             }
         }
     } else if (tid < nt) {
@@ -185,31 +234,48 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     for (int j = 0; j < NQ; ++j)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[j][e] = 0.0f;
+    // A quantized value is code * scale + zero with one (scale, zero) per
+    // (token, value group), so its share of the output is taken as
+    // (p * scale) * code plus p * zero, summed separately (zb).
     const int gv = (c8 * 8) / a.G_v;
-#pragma unroll 4
-    for (int tt = part; tt < nt; tt += PARTS) {
-        const int ts = t0 + tt;
-        uint4 v;
-        if (tt < nq_tok) {
-            const int64_t row = (int64_t)bh * a.S_max + ts;
-            const uint64_t pc = load_codes<BITS>(a.v_codes + row * row_bytes + c8 * BITS);
-            const int64_t p = row * a.NGD + gv;
-            const float sv = a.v_scale[p], zv = a.v_zero[p];
-            const float s8[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
-            const float z8[8] = {zv, zv, zv, zv, zv, zv, zv, zv};
-            v = dequant_chunk<DT, BITS>(pc, s8, z8);
-        } else {
-            v = load16(a.v_ring + ((int64_t)bh * a.ring + ts % a.ring) * D + c8 * 8);
-        }
-        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
-        float pj[NQ];
+    float zb[NQ];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) pj[j] = p_s[j][tt];
+    for (int j = 0; j < NQ; ++j) zb[j] = 0.0f;
+#pragma unroll 4
+    for (int tt = part; tt < nq_tok; tt += PARTS) {
+        const int64_t row = (int64_t)bh * a.S_max + t0 + tt;
+        const uint64_t pc = load_codes<BITS>(a.v_codes + row * row_bytes + c8 * BITS);
+        const int64_t p = row * a.NGD + gv;
+        const float sv = a.v_scale[p], zv = a.v_zero[p];
+        float ws[NQ];
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const float pj = p_s[j][tt];
+            ws[j] = pj * sv;
+            zb[j] = __builtin_fmaf(pj, zv, zb[j]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = (float)((uint32_t)(pc >> (e * BITS)) & ((1u << BITS) - 1u));
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) o[j][e] = __builtin_fmaf(ws[j], x, o[j][e]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] += zb[j];
+    // the exact tokens of the ring
+    for (int tt = max(part, nq_tok + ((part - nq_tok) % PARTS + PARTS) % PARTS);
+         tt < nt; tt += PARTS) {
+        const uint4 v = load16(a.v_ring + ((int64_t)bh * a.ring + (t0 + tt) % a.ring) * D +
+                               c8 * 8);
+        const uint32_t ws[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = widen16<DT>((uint16_t)(ws[e >> 1] >> ((e & 1) * 16)));
 #pragma unroll
-            for (int j = 0; j < NQ; ++j) o[j][e] = __builtin_fmaf(pj[j], x, o[j][e]);
+            for (int j = 0; j < NQ; ++j) o[j][e] = __builtin_fmaf(p_s[j][tt], x, o[j][e]);
         }
     }
     // parts inside a wave: lanes D8, 2 D8, ... apart
@@ -242,32 +308,45 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     }
 }
 
-// Merge the chunks of each bh: out = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c.
+// Merge the chunks of each bh: out = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
+// with M = max_c m_c.  One block per bh; M and L are block reductions over
+// the chunks, then each thread sums one channel (D = 64: two threads per
+// channel, each taking every other chunk).
 template <int DT>
 __global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a) {
-    const int bh = blockIdx.x;
-    const int D = a.D, nq = a.n_q;
-    for (int i = threadIdx.x; i < nq * D; i += 128) {
-        const int j = i / D, d = i % D;
-        const float* w = a.work + (int64_t)bh * a.n_chunks * nq * att_slot(D) +
-                         j * att_slot(D);
-        float M = -__builtin_huge_valf();
-        for (int c = 0; c < a.n_chunks; ++c)
-            M = fmaxf(M, w[(int64_t)c * nq * att_slot(D)]);
-        float L = 0.0f, O = 0.0f;
-        for (int c = 0; c < a.n_chunks; ++c) {
-            const float* wc = w + (int64_t)c * nq * att_slot(D);
-            const float f = __expf(wc[0] - M);
-            L = __builtin_fmaf(f, wc[1], L);
-            O = __builtin_fmaf(f, wc[2 + d], O);
+    __shared__ float red[2];
+    __shared__ float half_s[64];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int D = a.D, nq = a.n_q, nc = a.n_chunks;
+    const int64_t cs = (int64_t)nq * att_slot(D);   // chunk stride
+    const int per = 128 / D, d = tid % D, part = tid / D;
+    for (int j = 0; j < nq; ++j) {
+        const float* w = a.work + (int64_t)bh * nc * cs + j * att_slot(D);
+        float mx = -__builtin_huge_valf();
+        for (int c = tid; c < nc; c += 128) mx = fmaxf(mx, w[c * cs]);
+        const float M = block_reduce_max(mx, red);
+        float ls = 0.0f;
+        for (int c = tid; c < nc; c += 128) ls += __expf(w[c * cs] - M) * w[c * cs + 1];
+        const float L = block_reduce_sum(ls, red);
+        float O = 0.0f;
+#pragma unroll 4
+        for (int c = part; c < nc; c += per)
+            O = __builtin_fmaf(__expf(w[c * cs] - M), w[c * cs + 2 + d], O);
+        if (per > 1) {
+            if (part == 1) half_s[d] = O;
+            __syncthreads();
+            if (part == 0) O += half_s[d];
+            __syncthreads();
         }
-        const float r = O / L;
-        uint16_t h;
-        if constexpr (DT == DT_F16)
-            h = __builtin_bit_cast(uint16_t, (_Float16)r);
-        else
-            h = __builtin_bit_cast(uint16_t, (__bf16)r);
-        a.out[((int64_t)bh * nq + j) * D + d] = h;
+        if (part == 0) {
+            const float r = O / L;
+            uint16_t h;
+            if constexpr (DT == DT_F16)
+                h = __builtin_bit_cast(uint16_t, (_Float16)r);
+            else
+                h = __builtin_bit_cast(uint16_t, (__bf16)r);
+            a.out[((int64_t)bh * nq + j) * D + d] = h;
+        }
     }
 }
 

@@ -2,16 +2,25 @@
 (kivi_cache_attend, reading the packed store) against the oracle's float64
 attention over the dequantized cache (oracle.OracleCache.attend).
 
-Tolerance, derived from the arithmetic (u = 2^-11 for fp16, 2^-8 for bf16):
-the kernel keeps key reconstructions in fp32 where the oracle rounds them to
-the 16-bit type, so a score moves by at most
-    ds_t = sm * u * sum_d |q_d| |k_td|
-(plus fp32 accumulation, far smaller); the softmax weights then move by at
-most 2 * max_t ds_t in total variation (for small ds), which moves the
-output by at most that times max |V|; the result is rounded once to the
-16-bit type (u * |o|).  The test bound is
-    2 * max_t ds_t * max|V| * 1.25 + u * |o_ref| + 2^-20 * max|V|
-per element, with max taken per (bh, query head)."""
+Tolerance, derived from the arithmetic (u = 2^-11 for fp16, 2^-8 for bf16,
+e = 2^-24 for fp32):
+ * keys: the kernel forms a score of a quantized token as
+   sum_d (q_d scale_d) code_d + sum_d q_d zero_d in fp32, never rounding the
+   key to the 16-bit type as the oracle's dequantized cache does; the score
+   moves by at most
+       ds_t = sm * (u * sum_d |q_d| |k_td| + e (D + 4) sum_d |q_d| (|k_td| + 2 |z_td|))
+   (|code * scale| <= |k| + |z|, an fp32 sum of D + 2 terms), and the
+   softmax weights then move by at most 2 max_t ds_t in total variation,
+   which moves the output by that times max |V|;
+ * values: likewise summed as sum_t (p_t scale_t) code_t + sum_t p_t zero_t in
+   fp32 without the 16-bit rounding: at most u max|V| from the rounding, plus
+   e n_acc (max|V| + 2 max|z_v|) for fp32 sums of depth at most
+   n_acc = 128 + chunks + 8 (tokens of a chunk, the chunk merge, the shuffle
+   tree);
+ * the result is rounded once to the 16-bit type (u |o|), and 2^-20 max|V|
+   covers the fp32 exponentials.
+The test bound is the sum of these terms, the first two times 1.25, per
+element, with the maxima taken per (bh, query head)."""
 import numpy as np
 import pytest
 
@@ -57,12 +66,23 @@ def _widen(O, x, dtype):
 
 def _bound(O, oc, q, sm, ref, dtype):
     u = 2.0 ** -11 if dtype == FP16 else 2.0 ** -8
+    e = 2.0 ** -24
     Kf = _widen(O, oc.dequantized("K"), dtype)
     Vf = _widen(O, oc.dequantized("V"), dtype)
     qf = _widen(O, q, dtype)
-    ds = sm * u * np.einsum("bjd,btd->bjt", np.abs(qf), np.abs(Kf))
+    BH, T, D = Kf.shape
+    Q, G_k = oc.Q, oc.c.G_k
+    zk = np.zeros((BH, T, D))
+    zk[:, :Q] = np.repeat(oc.k_zero[:, :Q // G_k].astype(np.float64), G_k, axis=1)
+    aq = np.abs(qf)
+    ds = sm * (u * np.einsum("bjd,btd->bjt", aq, np.abs(Kf))
+               + e * (D + 4) * np.einsum("bjd,btd->bjt", aq, np.abs(Kf) + 2 * np.abs(zk)))
     vmax = np.abs(Vf).max(axis=(1, 2))[:, None, None]
-    return (2.0 * ds.max(axis=2)[:, :, None] * vmax * 1.25
+    zv = np.abs(oc.v_zero[:, :Q].astype(np.float64))
+    zvmax = (zv.max(axis=(1, 2)) if Q else np.zeros(BH))[:, None, None]
+    n_acc = 128 + (T + 127) // 128 + 8
+    vterm = u * vmax + e * n_acc * (vmax + 2 * zvmax)
+    return (1.25 * (2.0 * ds.max(axis=2)[:, :, None] * vmax + vterm)
             + u * np.abs(ref) + 2.0 ** -20 * vmax)
 
 
