@@ -58,6 +58,14 @@ class Oracle:
         L.kivi_ref_unpack.argtypes = [P, I64, I64, I, P]
         for name in ("kivi_ref_dequant_keys", "kivi_ref_dequant_values"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I64, I, I64, I, P]
+        L.kivi_ref_sink_scores.argtypes = [P, I, I64, I64, I64, I64, P]
+        L.kivi_ref_sink_select.argtypes = [P, I64, I64, I64, P]
+        for name in ("kivi_ref_quant_keys_sink_unpacked",
+                     "kivi_ref_quant_keys_sink"):
+            getattr(L, name).argtypes = [P, I, I64, I64, I64, I64, I, I64, P,
+                                         I64, P, P, P]
+        L.kivi_ref_sink_gather.argtypes = [P, I64, I64, I64, I64, P, I64, P]
+        L.kivi_ref_sink_restore.argtypes = [P, I64, I64, I64, I64, P, I64, P]
         self.L = L
         self.path = path
 
@@ -176,6 +184,77 @@ class Oracle:
                        out_dtype):
         return self._dequant("kivi_ref_dequant_values", packed, scale, zero,
                              shape, bits, group, out_dtype)
+
+    # KIVI-Sink --------------------------------------------------------------
+    def sink_scores(self, k, dtype, H):
+        """k [B*H, S, D] -> float32 [B, S]: mean over heads of key L2 norms."""
+        k = np.ascontiguousarray(k, dtype=np.uint16)
+        BH, S, D = k.shape
+        out = np.zeros((BH // H, S), np.float32)
+        self._check(self.L.kivi_ref_sink_scores(_ptr(k), dtype, BH // H, H, S,
+                                                D, _ptr(out)), "sink_scores")
+        return out
+
+    def sink_select(self, score, n_sink):
+        """score [B, S] -> int32 [B, n_sink], highest first."""
+        score = np.ascontiguousarray(score, dtype=np.float32)
+        B, S = score.shape
+        idx = np.zeros((B, n_sink), np.int32)
+        self._check(self.L.kivi_ref_sink_select(_ptr(score), B, S, n_sink,
+                                                _ptr(idx)), "sink_select")
+        return idx
+
+    def _quant_sink(self, name, x, dtype, H, bits, group, idx, packed):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        BH, S, D = x.shape
+        n_sink = idx.shape[1] if idx.ndim == 2 else 0
+        sc = np.zeros((BH, n_groups(S, group), D), np.float32)
+        z = np.zeros_like(sc)
+        codes = np.zeros((BH, S, D * bits // 8 if packed else D), np.uint8)
+        self._check(getattr(self.L, name)(_ptr(x), dtype, BH // H, H, S, D,
+                                          bits, group, _ptr(idx), n_sink,
+                                          _ptr(codes), _ptr(sc), _ptr(z)), name)
+        return codes, sc, z
+
+    def quant_keys_sink(self, x, dtype, H, bits, group, idx):
+        """-> (packed codes, scale [BH,NG,D], zero [BH,NG,D]); idx [B, n_sink]"""
+        return self._quant_sink("kivi_ref_quant_keys_sink", x, dtype, H, bits,
+                                group, idx, True)
+
+    def quant_keys_sink_unpacked(self, x, dtype, H, bits, group, idx):
+        return self._quant_sink("kivi_ref_quant_keys_sink_unpacked", x, dtype,
+                                H, bits, group, idx, False)
+
+    def sink_gather(self, x, H, idx):
+        """x [B*H, S, D] -> [B*H, n_sink, D] rows of the sinks."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        BH, S, D = x.shape
+        out = np.zeros((BH, idx.shape[1], D), np.uint16)
+        self._check(self.L.kivi_ref_sink_gather(_ptr(x), BH // H, H, S, D,
+                                                _ptr(idx), idx.shape[1],
+                                                _ptr(out)), "sink_gather")
+        return out
+
+    def sink_restore(self, x_sink, H, idx, out):
+        """Copy the sink rows back into out [B*H, S, D]; returns a new array."""
+        x_sink = np.ascontiguousarray(x_sink, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        out = np.array(out, dtype=np.uint16, copy=True, order="C")
+        BH, S, D = out.shape
+        self._check(self.L.kivi_ref_sink_restore(_ptr(x_sink), BH // H, H, S,
+                                                 D, _ptr(idx), idx.shape[1],
+                                                 _ptr(out)), "sink_restore")
+        return out
+
+    def sink_recon(self, x, dtype, H, bits, group, idx):
+        """Plain-KIVI-with-sinks reconstruction of keys x: quantize with the
+        sinks left out of calibration, dequantize, put the sink rows back."""
+        BH, S, D = x.shape
+        codes, sc, z = self.quant_keys_sink(x, dtype, H, bits, group, idx)
+        deq = self.dequant_keys(codes, sc, z, (BH, S, D), bits, group, dtype)
+        return self.sink_restore(self.sink_gather(x, H, idx), H, idx, deq)
 
     def cache(self, BH, D, S_max, R, G_k, G_v, bits, dtype):
         """A residual-window cache (kivi_ref_cache) over numpy arrays."""

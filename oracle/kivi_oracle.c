@@ -420,3 +420,184 @@ int kivi_ref_cache_append(kivi_ref_cache* c, const uint16_t* k_new,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* KIVI-Sink (VeloxQuant-MLX 0.24.1 package page, section "KVSink-adapted   */
+/* sink protection"): per sequence, the n_sink token positions whose keys   */
+/* have the largest L2 norm (averaged over the KV heads) are sinks.  Sinks  */
+/* are kept in 16-bit floats and take no part in the min/max of their key   */
+/* groups; every other token is quantized as plain KIVI.                    */
+/* Tensors are [B*H, S, D] with the H heads of sequence b at rows           */
+/* b*H .. b*H + H - 1; sink lists are [B, n_sink] token positions.          */
+/* ------------------------------------------------------------------------ */
+
+static int sink_shape_ok(int64_t B, int64_t H, int64_t S, int64_t D,
+                         int64_t n_sink) {
+    return B >= 0 && H >= 1 && S >= 0 && D >= 0 && n_sink >= 0 && n_sink <= S;
+}
+
+/*
+ * Score of token s of sequence b: the mean over the H heads of the key's L2
+ * norm.  Reading of the silent arithmetic: per head the squares are summed in
+ * channel order with one rounding per step (ss = fma(x, x, ss)), the norm is
+ * the correctly rounded square root, the H norms are summed in head order and
+ * the sum is divided by H once.  (The square of a 16-bit float is exact in
+ * fp32 unless a bf16 square underflows, so a separate multiply and add gives
+ * the same sums.)
+ */
+int kivi_ref_sink_scores(const uint16_t* k, int dtype, int64_t B, int64_t H,
+                         int64_t S, int64_t D, float* score) {
+    if (!sink_shape_ok(B, H, S, D, 0) || (dtype != 0 && dtype != 1)) return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t s = 0; s < S; ++s) {
+            float total = 0.0f;
+            for (int64_t h = 0; h < H; ++h) {
+                const uint16_t* row = k + ((b * H + h) * S + s) * D;
+                float ss = 0.0f;
+                for (int64_t d = 0; d < D; ++d) {
+                    float x = widen(row[d], dtype);
+                    ss = fmaf(x, x, ss);
+                }
+                total = total + sqrtf(ss);
+            }
+            score[b * S + s] = total / (float)H;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The sinks of each sequence: the n_sink positions of highest score, taken
+ * one at a time, highest first.  Reading where the pages are silent: of equal
+ * scores the lower position is taken first.
+ */
+int kivi_ref_sink_select(const float* score, int64_t B, int64_t S,
+                         int64_t n_sink, int32_t* idx) {
+    if (!sink_shape_ok(B, 1, S, 0, n_sink)) return 1;
+    unsigned char* taken = (unsigned char*)calloc((size_t)(S > 0 ? S : 1), 1);
+    if (!taken) return 1;
+    for (int64_t b = 0; b < B; ++b) {
+        memset(taken, 0, (size_t)(S > 0 ? S : 1));
+        for (int64_t r = 0; r < n_sink; ++r) {
+            int64_t best = -1;
+            for (int64_t s = 0; s < S; ++s) {
+                if (taken[s]) continue;
+                if (best < 0 || score[b * S + s] > score[b * S + best]) best = s;
+            }
+            taken[best] = 1;
+            idx[b * n_sink + r] = (int32_t)best;
+        }
+    }
+    free(taken);
+    return 0;
+}
+
+/* Whether position s is one of the sinks of sequence b (positions outside
+ * [0, S) in a list match nothing). */
+static int is_sink(const int32_t* idx, int64_t n_sink, int64_t b, int64_t s) {
+    for (int64_t i = 0; i < n_sink; ++i)
+        if ((int64_t)idx[b * n_sink + i] == s) return 1;
+    return 0;
+}
+
+/*
+ * Keys with sinks: as kivi_ref_quant_keys_unpacked, except that a group's min
+ * and max run over its tokens that are not sinks of the row's sequence
+ * (b = bh / H), and a sink's code is 0 (the sink is kept in 16-bit form, so
+ * it has no code).  Readings: a group made only of sinks has scale 0 and
+ * zero 0; the per-token value groups need no change, since a value group
+ * holds a single token and excluding a sink from calibration cannot touch
+ * any other token.
+ */
+int kivi_ref_quant_keys_sink_unpacked(const uint16_t* x, int dtype, int64_t B,
+                                      int64_t H, int64_t S, int64_t D,
+                                      int bits, int64_t group,
+                                      const int32_t* idx, int64_t n_sink,
+                                      uint8_t* codes, float* scale,
+                                      float* zero) {
+    if (!sink_shape_ok(B, H, S, D, n_sink) ||
+        !shape_ok(B * H, S, D, bits, group) || (dtype != 0 && dtype != 1))
+        return 1;
+    int64_t NG = (S + group - 1) / group;
+    float* vals = (float*)malloc((size_t)group * sizeof(float));
+    unsigned char* sink = (unsigned char*)malloc((size_t)group);
+    if (!vals || !sink) {
+        free(vals);
+        free(sink);
+        return 1;
+    }
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H;
+        for (int64_t g = 0; g < NG; ++g) {
+            int64_t s0 = g * group;
+            int64_t s1 = s0 + group < S ? s0 + group : S;
+            for (int64_t s = s0; s < s1; ++s) sink[s - s0] = (unsigned char)is_sink(idx, n_sink, b, s);
+            for (int64_t d = 0; d < D; ++d) {
+                int64_t n = 0;
+                for (int64_t s = s0; s < s1; ++s)
+                    if (!sink[s - s0]) vals[n++] = widen(x[(bh * S + s) * D + d], dtype);
+                float sc = 0.0f, z = 0.0f;
+                if (n > 0) kivi_ref_group_params(vals, n, bits, &sc, &z);
+                scale[(bh * NG + g) * D + d] = sc;
+                zero[(bh * NG + g) * D + d] = z;
+                for (int64_t s = s0; s < s1; ++s) {
+                    float f = widen(x[(bh * S + s) * D + d], dtype);
+                    codes[(bh * S + s) * D + d] =
+                        sink[s - s0] ? 0 : (uint8_t)kivi_ref_code(f, sc, z, bits);
+                }
+            }
+        }
+    }
+    free(vals);
+    free(sink);
+    return 0;
+}
+
+int kivi_ref_quant_keys_sink(const uint16_t* x, int dtype, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int bits,
+                             int64_t group, const int32_t* idx, int64_t n_sink,
+                             uint8_t* packed, float* scale, float* zero) {
+    if (!sink_shape_ok(B, H, S, D, n_sink) || !shape_ok(B * H, S, D, bits, group))
+        return 1;
+    size_t n = (size_t)(B * H * S * D);
+    uint8_t* codes = (uint8_t*)malloc(n ? n : 1);
+    if (!codes) return 1;
+    int st = kivi_ref_quant_keys_sink_unpacked(x, dtype, B, H, S, D, bits,
+                                               group, idx, n_sink, codes,
+                                               scale, zero);
+    if (st == 0) st = kivi_ref_pack(codes, B * H * S, D, bits, packed);
+    free(codes);
+    return st;
+}
+
+/* The sinks' rows kept in 16-bit form: x_sink[bh, i, :] = x[bh, idx[b, i], :]
+ * (a position outside [0, S) leaves its row of x_sink untouched). */
+int kivi_ref_sink_gather(const uint16_t* x, int64_t B, int64_t H, int64_t S,
+                         int64_t D, const int32_t* idx, int64_t n_sink,
+                         uint16_t* x_sink) {
+    if (!sink_shape_ok(B, H, S, D, n_sink)) return 1;
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t i = 0; i < n_sink; ++i) {
+            int64_t s = idx[(bh / H) * n_sink + i];
+            if (s < 0 || s >= S) continue;
+            memcpy(x_sink + (bh * n_sink + i) * D, x + (bh * S + s) * D,
+                   (size_t)D * sizeof(uint16_t));
+        }
+    return 0;
+}
+
+/* The reconstruction with sinks: each sink row copied back into the
+ * dequantized tensor, out[bh, idx[b, i], :] = x_sink[bh, i, :]. */
+int kivi_ref_sink_restore(const uint16_t* x_sink, int64_t B, int64_t H,
+                          int64_t S, int64_t D, const int32_t* idx,
+                          int64_t n_sink, uint16_t* out) {
+    if (!sink_shape_ok(B, H, S, D, n_sink)) return 1;
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t i = 0; i < n_sink; ++i) {
+            int64_t s = idx[(bh / H) * n_sink + i];
+            if (s < 0 || s >= S) continue;
+            memcpy(out + (bh * S + s) * D, x_sink + (bh * n_sink + i) * D,
+                   (size_t)D * sizeof(uint16_t));
+        }
+    return 0;
+}

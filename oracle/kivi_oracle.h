@@ -137,6 +137,40 @@ typedef struct {
 int kivi_ref_cache_append(kivi_ref_cache* c, const uint16_t* k_new,
                           const uint16_t* v_new, int64_t n);
 
+/* KIVI-Sink (VeloxQuant-MLX 0.24.1 package page, section "KVSink-adapted
+ * sink protection").  Keys are [B*H, S, D] with the H KV heads of sequence b
+ * at rows b*H .. b*H + H - 1; a sink list is [B, n_sink] positions.
+ *   sink_scores: score[b, s] = mean over heads of the key's L2 norm
+ *                (per head fma-accumulated squares in channel order, fp32
+ *                square root, head-order sum, one division by H);
+ *   sink_select: the n_sink highest scores per sequence, highest first, the
+ *                lower position first among equal scores (0 <= n_sink <= S);
+ *   quant_keys_sink: per-channel key quantization whose group min/max skip
+ *                the sinks; a sink's code is 0; an all-sink group has scale
+ *                0 and zero 0;
+ *   sink_gather / sink_restore: copy the sinks' rows to / from
+ *                [B*H, n_sink, D] (positions outside [0, S) are skipped). */
+int kivi_ref_sink_scores(const uint16_t* k, int dtype, int64_t B, int64_t H,
+                         int64_t S, int64_t D, float* score);
+int kivi_ref_sink_select(const float* score, int64_t B, int64_t S,
+                         int64_t n_sink, int32_t* idx);
+int kivi_ref_quant_keys_sink_unpacked(const uint16_t* x, int dtype, int64_t B,
+                                      int64_t H, int64_t S, int64_t D,
+                                      int bits, int64_t group,
+                                      const int32_t* idx, int64_t n_sink,
+                                      uint8_t* codes, float* scale,
+                                      float* zero);
+int kivi_ref_quant_keys_sink(const uint16_t* x, int dtype, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int bits,
+                             int64_t group, const int32_t* idx, int64_t n_sink,
+                             uint8_t* packed, float* scale, float* zero);
+int kivi_ref_sink_gather(const uint16_t* x, int64_t B, int64_t H, int64_t S,
+                         int64_t D, const int32_t* idx, int64_t n_sink,
+                         uint16_t* x_sink);
+int kivi_ref_sink_restore(const uint16_t* x_sink, int64_t B, int64_t H,
+                          int64_t S, int64_t D, const int32_t* idx,
+                          int64_t n_sink, uint16_t* out);
+
 #ifdef __cplusplus
 }
 #endif

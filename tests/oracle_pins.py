@@ -19,6 +19,11 @@ or the mathematics fix:
     2059, 8209 tokens flush 512, 2016, 8160; 240 decode tokens make 7
     flushes), the window invariant, and group-by-group flushing equal to
     quantizing the flushed prefix at once;
+  - KIVI-Sink: the key-norm score re-derived bit-exactly with numpy and
+    3-4-5 rows, selection equal to numpy's stable argsort, a hand-worked
+    spike group, brute-force masked group params and codes, n_sink = 0
+    equal to plain KIVI, and the pages' claims on planted-sink data (sinks
+    bit-exact, lower MSE than plain KIVI and than keeping the first n);
   - the pages' statistic: 2-bit reconstruction cosine about 0.93 on
     unit-norm Gaussian keys (KIVI release post, "Honest limitations"; PyPI
     page, KIVI section), 4-bit above 0.995 (PyPI page, ZipCache section).
@@ -666,6 +671,208 @@ def pin_attend_closed_forms(o):
     got = one.attend(q[:1], 0.2)
     vf = o.widen(v[:1, :1], FP16).astype(np.float64)
     assert np.allclose(got, vf.repeat(3, 1), rtol=0, atol=0)
+
+
+# --------------------------------------------------------------------------
+# KIVI-Sink (PyPI page of VeloxQuant-MLX 0.24.1, section "KVSink-adapted
+# sink protection")
+# --------------------------------------------------------------------------
+
+def _sink_scores_numpy(o, k, dtype, H):
+    """The score written out with numpy: per head the squares accumulated in
+    channel order with one rounding per step, the fp32 square root, the
+    head-order sum and one division by H.  x*x is exact in float64 and a
+    float64 sum or square root rounded again to float32 equals the single
+    float32 rounding (53 >= 2*24 + 2), so this is bit-exact."""
+    f = o.widen(k, dtype).astype(np.float64)
+    BH, S, D = f.shape
+    ss = np.zeros((BH, S), np.float32)
+    for d in range(D):
+        ss = (f[:, :, d] * f[:, :, d] + ss.astype(np.float64)).astype(np.float32)
+    norm = np.sqrt(ss.astype(np.float64)).astype(np.float32).reshape(BH // H, H, S)
+    total = np.zeros((BH // H, S), np.float32)
+    for h in range(H):
+        total = total + norm[:, h]
+    return total / np.float32(H)
+
+
+def _planted_sinks(seed, B, H, S, D, positions, factor=30.0, dtype=FP16):
+    """Keys N(0,1) whose sink positions (per sequence) carry keys `factor`
+    times larger in every head."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, H, S, D)).astype(np.float32)
+    for b in range(B):
+        x[b, :, positions[b]] *= factor
+    x = x.reshape(B * H, S, D)
+    if dtype == FP16:
+        return x.astype(np.float16).view(np.uint16)
+    u = x.view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def pin_sink_scores(o):
+    """The score is the mean over heads of the key's L2 norm: Pythagorean
+    rows give exact norms (3-4-5: heads of norm 5 and 10 average to 7.5),
+    and on random fp16 / bf16 keys the oracle equals the numpy
+    re-derivation bit for bit."""
+    rows = np.zeros((2, 1, 8), np.float32)      # B = 1, H = 2, S = 1, D = 8
+    rows[0, 0, :2] = (3.0, 4.0)
+    rows[1, 0, 5:7] = (6.0, 8.0)
+    got = o.sink_scores(_f16_bits(rows), FP16, 2)
+    assert got.shape == (1, 1) and got[0, 0] == np.float32(7.5), got
+    r = np.random.default_rng(71)
+    for dtype in (FP16, BF16):
+        k = _rand_tensor(r, 6, 37, 24, dtype)
+        for H in (1, 3):
+            got = o.sink_scores(k, dtype, H)
+            exp = _sink_scores_numpy(o, k, dtype, H)
+            assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), (dtype, H)
+            # and close to the float64 definition
+            f = o.widen(k, dtype).astype(np.float64).reshape(6 // H, H, 37, 24)
+            ref = np.sqrt((f * f).sum(axis=3)).mean(axis=1)
+            assert np.allclose(got, ref, rtol=2.0**-24 * (24 + H + 4), atol=0)
+
+
+def pin_sink_select(o):
+    """Selection equals numpy's stable descending argsort (the lower position
+    first among equal scores): random scores, planted ties, n_sink = 0 and
+    n_sink = S."""
+    r = np.random.default_rng(72)
+    sc = r.random((3, 50)).astype(np.float32)
+    sc[1, [4, 9, 30]] = np.float32(2.0)         # a three-way tie at the top
+    sc[2, 10:20] = np.float32(0.5)              # a run of ties in the middle
+    for n in (0, 1, 3, 7, 50):
+        got = o.sink_select(sc, n)
+        exp = np.argsort(-sc, axis=1, kind="stable")[:, :n].astype(np.int32)
+        assert np.array_equal(got, exp), n
+    assert np.array_equal(o.sink_select(sc, 3)[1], [4, 9, 30])
+    try:
+        o.sink_select(sc, 51)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("n_sink > S accepted")
+
+
+def pin_sink_worked_group(o):
+    """A spike among small keys (one channel, a group of four tokens
+    [0, 1, 0.5, 100], 2 bits).  Plain KIVI: scale 100/3, codes [0, 0, 0, 3],
+    so every neighbour reconstructs to 0.  With the spike as a sink: zero 0,
+    scale RN(1/3) = 0x3EAAAAAB, codes [0, 3, 2, 0] (0.5 / RN(1/3) rounds to
+    1.5 in fp32, then to the even 2), reconstruction [0, 1, 0.6666667] and
+    the spike itself bit-exact."""
+    x = _f16_bits(np.array([0.0, 1.0, 0.5, 100.0], np.float32).reshape(1, 4, 1)
+                  .repeat(8, axis=2))
+    idx = np.array([[3]], np.int32)
+    codes, sc, z = o.quant_keys_sink_unpacked(x, FP16, 1, 2, 4, idx)
+    assert codes[0, :, 0].tolist() == [0, 3, 2, 0], codes[0, :, 0]
+    assert sc[0, 0, 0].view(np.uint32) == 0x3EAAAAAB and z[0, 0, 0] == 0.0
+    plain, psc, _ = o.quant_keys_unpacked(x, FP16, 2, 4)
+    assert plain[0, :, 0].tolist() == [0, 0, 0, 3]
+    assert psc[0, 0, 0] == np.float32(100.0) / np.float32(3.0)
+    rec = o.widen(o.sink_recon(x, FP16, 1, 2, 4, idx), FP16)[0, :, 0]
+    assert rec.tolist() == [0.0, 1.0, float(np.float16(np.float32(2) * np.float32(1 / 3))), 100.0]
+
+
+def pin_sink_quant_bruteforce(o):
+    """Keys with sinks on ragged shapes against numpy float32: each group's
+    zero and scale are numpy's min, max and (max - min) / (2^b - 1) over the
+    group's non-sink tokens (+0 for a zero min or max), codes are
+    rint((x - zero) / scale) clipped (0 when scale is 0) and a sink's code is
+    0; a group of sinks only has scale 0 and zero 0.  Sink lists name each
+    sequence's own tokens (H = 2 heads per sequence)."""
+    r = np.random.default_rng(73)
+    B, H, S, D, G, bits = 2, 2, 19, 8, 4, 2
+    x = _rand_tensor(r, B * H, S, D, FP16)
+    idx = np.array([[0, 1, 2, 3, 9, 18], [17, 5, 6, 40, -1, 6]], np.int32)
+    codes, sc, z = o.quant_keys_sink_unpacked(x, FP16, H, bits, G, idx)
+    f = o.widen(x, FP16)
+    L = np.float32(2**bits - 1)
+    for bh in range(B * H):
+        sinks = set(int(s) for s in idx[bh // H])
+        for g in range((S + G - 1) // G):
+            toks = [s for s in range(g * G, min(g * G + G, S))]
+            keep = [s for s in toks if s not in sinks]
+            for d in range(D):
+                if keep:
+                    v = f[bh, keep, d]
+                    mn, mx = np.float32(v.min()) + np.float32(0), np.float32(v.max()) + np.float32(0)
+                    es, ez = np.float32(mx - mn) / L, mn
+                else:
+                    es, ez = np.float32(0), np.float32(0)
+                assert sc[bh, g, d].view(np.uint32) == es.view(np.uint32), (bh, g, d)
+                assert z[bh, g, d].view(np.uint32) == ez.view(np.uint32), (bh, g, d)
+                for s in toks:
+                    if s in sinks or es == 0:
+                        e = 0
+                    else:
+                        t = np.float32(np.float32(f[bh, s, d] - ez) / es)
+                        e = int(min(max(np.rint(t), 0), 2**bits - 1))
+                    assert codes[bh, s, d] == e, (bh, s, d, codes[bh, s, d], e)
+    # the second sequence's group 1 is tokens 4..7 with sinks 5 and 6; its
+    # first group has none; the first sequence's group 0 is all sinks
+    assert (sc[:2, 0] == 0).all() and (z[:2, 0] == 0).all()
+
+
+def pin_sink_zero_is_plain_kivi(o):
+    """With no sinks the variant is plain KIVI bit for bit (PyPI page,
+    KVSink section: n_sink_tokens = 0 reproduces plain KIVI)."""
+    r = np.random.default_rng(74)
+    for dtype, bits, G in ((FP16, 2, 32), (BF16, 4, 8)):
+        x = _rand_tensor(r, 4, 70, 16, dtype)
+        got = o.quant_keys_sink(x, dtype, 2, bits, G, np.zeros((2, 0), np.int32))
+        exp = o.quant_keys(x, dtype, bits, G)
+        for a, b in zip(got, exp):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def pin_sink_claims(o):
+    """The pages' evidence for the variant on planted-sink data: sinks come
+    back bit-exact while the others are quantized; the sink-protected MSE is
+    below plain KIVI's at the same bit width; and with sinks away from the
+    front, dynamic selection beats keeping the first n tokens at the same
+    fp16 budget.  Also gather then restore is the identity on sink rows."""
+    B, H, S, D, n = 2, 4, 256, 32, 4
+    pos = [np.array([40, 97, 150, 201]), np.array([3, 64, 130, 250])]
+    x = _planted_sinks(75, B, H, S, D, pos)
+    idx = o.sink_select(o.sink_scores(x, FP16, H), n)
+    for b in range(B):
+        assert sorted(idx[b].tolist()) == sorted(pos[b].tolist()), idx[b]
+    f = o.widen(x, FP16).astype(np.float64)
+
+    def mse(rec):
+        return float(((o.widen(rec, FP16) - f) ** 2).mean())
+
+    rec = o.sink_recon(x, FP16, H, 2, 32, idx)
+    for bh in range(B * H):
+        assert np.array_equal(rec[bh, idx[bh // H]], x[bh, idx[bh // H]])
+    plain_codes, psc, pz = o.quant_keys(x, FP16, 2, 32)
+    plain = o.dequant_keys(plain_codes, psc, pz, x.shape, 2, 32, FP16)
+    first = np.tile(np.arange(n, dtype=np.int32), (B, 1))
+    front = o.sink_recon(x, FP16, H, 2, 32, first)
+    assert mse(rec) < 0.5 * mse(plain), (mse(rec), mse(plain))
+    assert mse(rec) < mse(front), (mse(rec), mse(front))
+    assert not np.array_equal(rec, x)
+    # gather / restore
+    xs = o.sink_gather(x, H, idx)
+    for bh in range(B * H):
+        assert np.array_equal(xs[bh], x[bh, idx[bh // H]])
+    back = o.sink_restore(xs, H, idx, np.zeros_like(x))
+    mask = np.zeros(x.shape[:2], bool)
+    for bh in range(B * H):
+        mask[bh, idx[bh // H]] = True
+    assert np.array_equal(back[mask], x[mask]) and not back[~mask].any()
+    # positions outside [0, S) leave their rows alone (the input sits in a
+    # larger buffer, so a row read past the end stays inside it)
+    big = np.concatenate([x, np.ones((1, S, D), np.uint16)])
+    odd_g = np.array([[S, int(idx[0, 0])], [-1, S]], np.int32)
+    xs2 = o.sink_gather(big[:B * H], H, odd_g)
+    assert not xs2[:, 0].any() and not xs2[H:, 1].any()
+    for bh in range(H):
+        assert np.array_equal(xs2[bh, 1], x[bh, idx[0, 0]])
+    odd = np.array([[-1, S], [S + 5, -7]], np.int32)     # nothing in range
+    assert not o.sink_restore(np.ones((B * H, 2, D), np.uint16), H, odd,
+                              np.zeros_like(x)).any()
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

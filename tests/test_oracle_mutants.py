@@ -71,6 +71,29 @@ MUTANTS = [
     ("cache_history_overwrite",
      "memcpy(c->k + (bh * c->S_max + c->T) * D, k_new + (bh * n + i) * D,",
      "memcpy(c->k + (bh * c->S_max + c->Q) * D, k_new + (bh * n + i) * D,"),
+    ("sink_in_minmax",
+     "if (!sink[s - s0]) vals[n++] = widen(x[(bh * S + s) * D + d], dtype);",
+     "vals[n++] = widen(x[(bh * S + s) * D + d], dtype);"),
+    ("sink_code_not_zero",
+     "sink[s - s0] ? 0 : (uint8_t)kivi_ref_code(f, sc, z, bits);",
+     "(uint8_t)kivi_ref_code(f, sc, z, bits);"),
+    ("sink_wrong_sequence", "int64_t b = bh / H;", "int64_t b = bh % H;"),
+    ("sink_tie_higher_position",
+     "if (best < 0 || score[b * S + s] > score[b * S + best]) best = s;",
+     "if (best < 0 || score[b * S + s] >= score[b * S + best]) best = s;"),
+    ("sink_select_repeats", "taken[best] = 1;", "(void)taken;"),
+    ("sink_score_no_sqrt", "total = total + sqrtf(ss);", "total = total + ss;"),
+    ("sink_score_no_mean", "score[b * S + s] = total / (float)H;",
+     "score[b * S + s] = total;"),
+    ("sink_score_head_stride",
+     "const uint16_t* row = k + ((b * H + h) * S + s) * D;",
+     "const uint16_t* row = k + ((b * H + h) * S + s) * D + (h > 0);"),
+    ("sink_restore_row",
+     "memcpy(out + (bh * S + s) * D, x_sink + (bh * n_sink + i) * D,",
+     "memcpy(out + (bh * S + s) * D, x_sink + (bh * n_sink) * D,"),
+    ("sink_gather_range",
+     "if (s < 0 || s >= S) continue;\n            memcpy(x_sink",
+     "if (s < 0 || s > S) continue;\n            memcpy(x_sink"),
 ]
 
 
