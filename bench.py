@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
 KERNEL_SOURCES = ["kivi_device.h", "kivi_rows.h", "quant_keys.hip", "quant_values.hip",
-                  "dequant.hip", "cache.hip", "attend.hip"]
+                  "dequant.hip", "cache.hip", "attend.hip", "sink.hip"]
 
 
 def bytes_per_elem(op, bits, group, dtype_bytes=2):
@@ -658,6 +658,174 @@ def attend_bench(args, aw, K, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+# --------------------------------------------------------------------------
+# KIVI-Sink over a prompt (kivi_sink_select, kivi_quant_keys_sink, ...)
+# --------------------------------------------------------------------------
+
+def sink_bytes(sw):
+    """Algorithmic bytes of one KIVI-Sink pass, per kernel: the scores read
+    every key once and write one fp32 per token; the selection reads the
+    scores once; the key quantizer reads the keys again (the sinks must be
+    known before any key group's min/max) and writes codes and params; the
+    value quantizer is plain KIVI; the two gathers copy the sinks' K and V
+    rows."""
+    E = sw.B * sw.H * sw.S * sw.D
+    tok = sw.B * sw.S * 4
+    kq = E * bytes_per_elem("quant", sw.bits, sw.group_k)
+    vq = E * bytes_per_elem("quant", sw.bits, sw.group_v)
+    gather = sw.B * sw.H * sw.n_sink * sw.D * 2 * 2
+    return {"sink_score": E * 2 + tok, "sink_select": tok,
+            "quant_keys_sink": int(kq), "quant_values": int(vq),
+            "sink_gather_k": gather, "sink_gather_v": gather}
+
+
+def sink_bench(args, sw, K, torch, dev):
+    """One step = the KIVI-Sink pass over one prompt: select the sinks,
+    quantize the keys without them, quantize the values, keep the sinks' K
+    and V rows.  Inputs rotate over a pool of prompts larger than the MALL."""
+    tdt = torch.float16 if sw.dtype == W.FP16 else torch.bfloat16
+    w = sw.tokens()
+    B, H, S, D = sw.B, sw.H, sw.S, sw.D
+    nb = sink_bytes(sw)
+    step_bytes = sum(nb.values())
+    P = args.pool or 2
+    inputs = []
+    for p in range(P):
+        kv = []
+        for tensor in ("K", "V"):
+            x = W.gen_tensor(w, tensor, pool=p)
+            kv.append(torch.from_numpy(x.view(np.int16)).view(tdt).to(dev)
+                      .view(B, H, S, D))
+        inputs.append(tuple(kv))
+    kc, ks, kz = K.kivi_quant_keys_sink(inputs[0][0], torch.zeros(
+        (B, sw.n_sink), dtype=torch.int32, device=dev), sw.bits, sw.group_k)
+    vc, vs, vz = K.kivi_quant_values(inputs[0][1], sw.bits, sw.group_v)
+    idx = torch.empty((B, sw.n_sink), dtype=torch.int32, device=dev)
+    score = torch.empty((B, S), dtype=torch.float32, device=dev)
+    k_keep = torch.empty((B, H, sw.n_sink, D), dtype=tdt, device=dev)
+    v_keep = torch.empty_like(k_keep)
+    stream = torch.cuda.current_stream(dev)
+    names = ["sink_score", "quant_keys_sink", "quant_values", "sink_gather_k",
+             "sink_gather_v"]
+
+    def step(i, arm=None):
+        k, v = inputs[i % P]
+        if arm == 0:
+            K.kivi_time_next_launch(*ev)
+        K.kivi_sink_select(k, sw.n_sink, score=score, idx=idx)
+        if arm == 1:
+            K.kivi_time_next_launch(*ev)
+        K.kivi_quant_keys_sink(k, idx, sw.bits, sw.group_k, codes=kc,
+                               scale=ks, zero=kz)
+        if arm == 2:
+            K.kivi_time_next_launch(*ev)
+        K.kivi_quant_values(v, sw.bits, sw.group_v, codes=vc, scale=vs, zero=vz)
+        if arm == 3:
+            K.kivi_time_next_launch(*ev)
+        K.kivi_sink_gather(k, idx, out=k_keep)
+        if arm == 4:
+            K.kivi_time_next_launch(*ev)
+        K.kivi_sink_gather(v, idx, out=v_keep)
+
+    ev = None
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    pk = {}
+    base = args.warmup + args.steps
+    for a, name in enumerate(names):
+        d = []
+        for i in range(args.steps):
+            ev = (torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True))
+            step(base + i, arm=a)
+            torch.cuda.synchronize()
+            d.append(ev[0].elapsed_time(ev[1]))
+        base += args.steps
+        avg = float(np.mean(d))
+        b = nb[name]
+        pk[name] = {"avg_us": round(avg * 1e3, 3),
+                    "median_us": round(float(np.median(d)) * 1e3, 3),
+                    "min_us": round(float(np.min(d)) * 1e3, 3),
+                    "max_us": round(float(np.max(d)) * 1e3, 3),
+                    "algorithmic_bytes": int(b),
+                    "gbs": round(b / (avg * 1e-3) / 1e9, 1)}
+    ev = None
+    dom = max(("sink_score", "quant_keys_sink"), key=lambda n: pk[n]["avg_us"])
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        O = oracle.default()
+        one = W.SinkWorkload(sw.name, 1, H, S, D, sw.dtype, sw.bits,
+                             sw.group_k, sw.group_v, sw.n_sink, sw.seed,
+                             sw.key_kind, sw.value_kind, sw.desc)
+        kx = W.gen_tensor(w, "K", range(H))
+        vx = W.gen_tensor(w, "V", range(H))
+        t0 = time.perf_counter()
+        sc = O.sink_scores(kx, sw.dtype, H)
+        ix = O.sink_select(sc, sw.n_sink)
+        O.quant_keys_sink(kx, sw.dtype, H, sw.bits, sw.group_k, ix)
+        O.quant_values(vx, sw.dtype, sw.bits, sw.group_v)
+        O.sink_gather(kx, H, ix)
+        O.sink_gather(vx, H, ix)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(sum(sink_bytes(one).values()) / dt / 1e9, 4),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": (f"1 of {B} sequences ({H} heads x {S} tokens), the "
+                          f"whole pass: {dt:.2f} s on 1 thread")}
+    result = {
+        "metric": METRIC + " (KIVI-Sink pass)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{sw.name}: {sw.desc}; step = kivi_sink_select + "
+                         "kivi_quant_keys_sink + kivi_quant_values + two "
+                         "kivi_sink_gather calls"),
+            "step_algorithmic_bytes": int(step_bytes),
+            "input_pool": P,
+            "launch": "eager",
+            "wall_s": round(t_wall, 4),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": dom,
+            "avg_us": pk[dom]["avg_us"],
+            "bound": "hbm",
+            "achieved": pk[dom]["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(pk[dom]["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(dom, sw.name, kernel_source_hash()),
+        },
+        "per_kernel": pk,
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -665,7 +833,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="roundtrip",
                     choices=sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS)
-                    + sorted(W.ATTEND_WORKLOADS))
+                    + sorted(W.ATTEND_WORKLOADS) + sorted(W.SINK_WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
     ap.add_argument("--cpu-sample-bh", type=int, default=0,
@@ -709,6 +877,9 @@ def main():
         return
     if args.workload in W.CACHE_WORKLOADS:
         cache_bench(args, W.CACHE_WORKLOADS[args.workload], K, torch, dev)
+        return
+    if args.workload in W.SINK_WORKLOADS:
+        sink_bench(args, W.SINK_WORKLOADS[args.workload], K, torch, dev)
         return
     w = W.WORKLOADS[args.workload]
     tdt = torch.float16 if w.dtype == W.FP16 else torch.bfloat16

@@ -214,10 +214,12 @@ kivi_status kivi_cache_append(kivi_cache* cache, const void* k_new,
  * For every bh and query head j < n_q (n_q query heads share each KV head):
  *     out[bh, j] = softmax_t(sm_scale * q[bh, j] . K[bh, t]) V[bh, t]
  * over the cache's T tokens, where K, V of tokens t < Q are the codes
- * reconstructed with their group's params -- keys RN(RN(code * scale) +
- * zero) in fp32, values exactly as kivi_dequant_values gives them -- and
- * tokens t >= Q are the exact tokens in the rings.  fp32 scores, softmax
- * and accumulation; out is rounded to the cache's dtype.
+ * reconstructed with their group's params, code * scale + zero, used in
+ * fp32 without rounding to the 16-bit type (a key through
+ * sum_d (q_d scale_d) code_d + sum_d q_d zero_d, a value through
+ * (p scale) code + p zero), and tokens t >= Q are the exact tokens in the
+ * rings.  fp32 scores, softmax and accumulation; out is rounded to the
+ * cache's dtype.
  *   q    in  : [BH, n_q, D] of the cache's dtype
  *   out  out : [BH, n_q, D] of the cache's dtype
  *   work     : device scratch of at least kivi_cache_attend_work_bytes
@@ -241,6 +243,68 @@ kivi_status kivi_cache_attend(const kivi_cache* cache, const void* q,
 int64_t kivi_cache_attend_work_bytes(const kivi_cache* cache, int64_t n_q);
 
 /*
+ * KIVI-Sink (VeloxQuant-MLX 0.24.1 package page, section "KVSink-adapted
+ * sink protection"): per sequence, the n_sink token positions whose keys
+ * have the largest L2 norm averaged over the KV heads are sinks; they are
+ * kept in 16-bit form and left out of the min/max of their key groups, so a
+ * high-magnitude sink does not stretch its neighbours' scale.
+ *
+ * Layout: keys and values [B*H, S, D] (the [BH, S, D] layout above with the
+ * H KV heads of sequence b at rows b*H .. b*H + H - 1); a sink list is
+ * int32 [B, n_sink] token positions; a sink store is [B*H, n_sink, D] of the
+ * tensor's 16-bit type, row (bh, i) holding token idx[bh / H, i].
+ * Common rules (else nothing is launched): B, H, S >= 1 and D >= 8
+ * (KIVI_ERR_SHAPE), 0 <= n_sink <= min(S, 64) (KIVI_ERR_SHAPE), B*H*S*D
+ * < 2^40 and B*S < 2^31 (KIVI_ERR_SHAPE), dtype as above, pointers non-NULL
+ * (KIVI_ERR_NULL) and 16-byte aligned (KIVI_ERR_ALIGN; 4-byte for idx and
+ * score).  Positions outside [0, S) in a list given by the caller are
+ * ignored.  n_sink == 0 launches nothing (kivi_sink_select still writes the
+ * scores).
+ */
+
+/* Scores and selection.  score[b, s] (fp32 [B, S], written) is the mean
+ * over the H heads of the L2 norm of key row (b*H + h, s): per head the
+ * squares summed in channel order with one rounding per step, the correctly
+ * rounded square root, the head-order sum divided once by H.  idx (int32
+ * [B, n_sink], written) gets each sequence's n_sink highest scores, highest
+ * first; of equal scores the lower position comes first.  D must be a power
+ * of two in [8, 256] (KIVI_ERR_SHAPE).  Launches two kernels (one when
+ * n_sink == 0). */
+kivi_status kivi_sink_select(const void* k, kivi_dtype dt, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int64_t n_sink,
+                             float* score, int32_t* idx, hipStream_t stream);
+
+/* Per-channel key quantization with sinks: as kivi_quant_keys (codes
+ * [B*H, S, D*bits/8], params [B*H, ceil(S/group), D]), except that each
+ * group's min and max run over its tokens that are not sinks of the row's
+ * sequence; a sink's code is 0, and a group made only of sinks gets scale 0
+ * and zero 0.  recon, if non-NULL ([B*H, S, D], the input's dtype), gets the
+ * reconstruction with every sink row equal to its input row (the dequant of
+ * the codes followed by kivi_sink_restore).  codes, scale and zero are all
+ * given or all NULL; at least one output (KIVI_ERR_NULL).  D % 8 == 0
+ * (KIVI_ERR_SHAPE); 1 <= group <= 32 (KIVI_ERR_GROUP).  One kernel. */
+kivi_status kivi_quant_keys_sink(const void* k, kivi_dtype dt, int64_t B,
+                                 int64_t H, int64_t S, int64_t D, int bits,
+                                 int64_t group, const int32_t* idx,
+                                 int64_t n_sink, uint8_t* codes, float* scale,
+                                 float* zero, void* recon, hipStream_t stream);
+
+/* Keep the sinks' rows: x_sink[bh, i, :] = x[bh, idx[bh / H, i], :].
+ * Values need nothing more than this: a value group is one token, so the
+ * plain kivi_quant_values already leaves every other token untouched by a
+ * sink.  D % 8 == 0 (KIVI_ERR_SHAPE).  One kernel. */
+kivi_status kivi_sink_gather(const void* x, int64_t B, int64_t H, int64_t S,
+                             int64_t D, const int32_t* idx, int64_t n_sink,
+                             void* x_sink, hipStream_t stream);
+
+/* Put the sinks' rows back into a dequantized tensor:
+ * out[bh, idx[bh / H, i], :] = x_sink[bh, i, :].  D % 8 == 0
+ * (KIVI_ERR_SHAPE).  One kernel. */
+kivi_status kivi_sink_restore(const void* x_sink, int64_t B, int64_t H,
+                              int64_t S, int64_t D, const int32_t* idx,
+                              int64_t n_sink, void* out, hipStream_t stream);
+
+/*
  * Profiling aid: the next kernel that a kivi_* call made by this thread
  * launches records `start` when it begins executing and `stop` when it ends
  * (hipExtLaunchKernel), so hipEventElapsedTime(start, stop) is that kernel's
@@ -248,8 +312,8 @@ int64_t kivi_cache_attend_work_bytes(const kivi_cache* cache, int64_t n_q);
  * launches include.  Both events must be created by the caller (e.g.
  * hipEventCreate) and outlive the launch.  The pair is consumed by the next
  * launch: every quantize or dequantize call launches exactly one kernel,
- * kivi_cache_append up to three and kivi_cache_attend two (the pair times
- * the first), and calls that
+ * kivi_cache_append up to three, kivi_cache_attend and kivi_sink_select
+ * two (the pair times the first), and calls that
  * launch nothing -- errors, empty tensors -- leave it armed.  Passing NULL
  * for either disarms it.  This thread-local pair is the library's only
  * state.

@@ -21,7 +21,12 @@ Functions (same names as the C ABI):
     kivi_status_string
     KiviCache(BH, D, S_max, R, G_k, G_v, bits, dtype), kivi_cache_append
         the residual-window cache (recent tokens kept exact, whole key
-        groups flushed into packed storage as they age out)
+        groups flushed into packed storage as they age out), and
+        kivi_cache_attend, decode attention reading the packed store
+    kivi_sink_select, kivi_quant_keys_sink, kivi_sink_gather,
+    kivi_sink_restore
+        KIVI-Sink: the highest key-norm tokens kept in 16-bit form and left
+        out of the key groups' min/max
 Tensors are [BH, S, D] (or [B, H, S, D], flattened to BH = B*H), contiguous,
 float16 or bfloat16; codes are uint8 [..., S, D*bits/8]; key params are
 float32 [..., ceil(S/group), D]; value params float32 [..., S, ceil(D/group)].
@@ -83,6 +88,15 @@ def _load():
     L.kivi_key_param_count.restype = I64
     L.kivi_value_param_count.argtypes = [I64, I64, I64, I64]
     L.kivi_value_param_count.restype = I64
+    L.kivi_sink_select.argtypes = [P, I, I64, I64, I64, I64, I64, P, P, P]
+    L.kivi_quant_keys_sink.argtypes = [P, I, I64, I64, I64, I64, I, I64, P,
+                                       I64, P, P, P, P, P]
+    copy = [P, I64, I64, I64, I64, P, I64, P, P]
+    L.kivi_sink_gather.argtypes = copy
+    L.kivi_sink_restore.argtypes = copy
+    for name in ("kivi_sink_select", "kivi_quant_keys_sink",
+                 "kivi_sink_gather", "kivi_sink_restore"):
+        getattr(L, name).restype = I
     L.kivi_status_string.argtypes = [I]
     L.kivi_status_string.restype = ctypes.c_char_p
     return L
@@ -257,6 +271,97 @@ def kivi_dequant_values(codes, scale, zero, bits=2, group=32,
     """Value dequantization -> [..., S, D] of out_dtype."""
     return _dequant("kivi_dequant_values", False, codes, scale, zero, bits,
                     group, out_dtype, out, stream)
+
+
+# --------------------------------------------------------------------------
+# KIVI-Sink
+# --------------------------------------------------------------------------
+
+def _bhsd(x, H):
+    """(B, H, S, D) of a [B, H, S, D] tensor, or of [..., S, D] with the
+    given H heads per sequence (the flattened rows must be B*H)."""
+    BH, S, D, lead = _bsd(x)
+    if x.dim() == 4 and H is None:
+        H = x.shape[1]
+    if H is None or H < 1 or BH % H:
+        raise ValueError(f"cannot split {BH} rows into sequences of H={H} heads")
+    return BH // H, H, S, D
+
+
+def _idx_arg(idx):
+    if idx.dtype != torch.int32 or idx.dim() != 2 or not idx.is_contiguous():
+        raise ValueError("sink lists are contiguous int32 [B, n_sink] tensors")
+    return idx.shape[1]
+
+
+def kivi_sink_select(k, n_sink, H=None, score=None, idx=None, stream=None):
+    """Per-sequence sinks of keys [B, H, S, D] -> (idx int32 [B, n_sink],
+    score float32 [B, S]): the n_sink highest mean key L2 norms, highest
+    first."""
+    B, H, S, D = _bhsd(k, H)
+    if score is None:
+        score = torch.empty((B, S), dtype=torch.float32, device=k.device)
+    if idx is None:
+        idx = torch.empty((B, max(n_sink, 0)), dtype=torch.int32, device=k.device)
+    st = _lib().kivi_sink_select(_ptr(k), _dtype_code(k.dtype), B, H, S, D,
+                                 n_sink, _ptr(score), _ptr(idx),
+                                 _stream(k.device, stream))
+    _check(st, "kivi_sink_select")
+    return idx, score
+
+
+def kivi_quant_keys_sink(k, idx, bits=2, group=32, H=None, with_codes=True,
+                         with_recon=False, codes=None, scale=None, zero=None,
+                         recon=None, stream=None):
+    """Per-channel key quantization with the sinks idx [B, n_sink] left out
+    of every group's min/max.  Returns (codes, scale, zero), with the
+    reconstruction first when with_recon, or the reconstruction alone when
+    not with_codes."""
+    B, H, S, D = _bhsd(k, H)
+    n_sink = _idx_arg(idx)
+    if group < 1:
+        _check(4, "kivi_quant_keys_sink")
+    if not with_codes:
+        with_recon = True
+    if with_recon and recon is None:
+        recon = torch.empty_like(k)
+    if with_codes:
+        codes, scale, zero = _alloc_quant(k, True, bits, group, codes, scale,
+                                          zero)
+    else:
+        codes = scale = zero = None
+    st = _lib().kivi_quant_keys_sink(
+        _ptr(k), _dtype_code(k.dtype), B, H, S, D, bits, group, _ptr(idx),
+        n_sink, _ptr(codes), _ptr(scale), _ptr(zero),
+        _ptr(recon) if with_recon else None, _stream(k.device, stream))
+    _check(st, "kivi_quant_keys_sink")
+    if not with_codes:
+        return recon
+    return (recon, codes, scale, zero) if with_recon else (codes, scale, zero)
+
+
+def kivi_sink_gather(x, idx, H=None, out=None, stream=None):
+    """The sinks' rows of x [B, H, S, D] -> [B, H, n_sink, D]."""
+    B, H, S, D = _bhsd(x, H)
+    n_sink = _idx_arg(idx)
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-2]) + (n_sink, D), dtype=x.dtype,
+                          device=x.device)
+    st = _lib().kivi_sink_gather(_ptr(x), B, H, S, D, _ptr(idx), n_sink,
+                                 _ptr(out), _stream(x.device, stream))
+    _check(st, "kivi_sink_gather")
+    return out
+
+
+def kivi_sink_restore(x_sink, idx, out, H=None, stream=None):
+    """Write the sink rows x_sink [B, H, n_sink, D] back into out
+    [B, H, S, D] (in place); returns out."""
+    B, H, S, D = _bhsd(out, H)
+    n_sink = _idx_arg(idx)
+    st = _lib().kivi_sink_restore(_ptr(x_sink), B, H, S, D, _ptr(idx), n_sink,
+                                  _ptr(out), _stream(out.device, stream))
+    _check(st, "kivi_sink_restore")
+    return out
 
 
 class _Cache(ctypes.Structure):

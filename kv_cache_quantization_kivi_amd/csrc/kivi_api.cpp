@@ -167,9 +167,96 @@ kivi_status check_attend(const kivi_cache* c, int64_t n_q) {
     return KIVI_OK;
 }
 
+// Rules shared by the KIVI-Sink entry points (include/kivi.h).
+kivi_status check_sink(int64_t B, int64_t H, int64_t S, int64_t D,
+                       int64_t n_sink) {
+    if (B < 1 || H < 1 || S < 1 || D < 8) return KIVI_ERR_SHAPE;
+    if (n_sink < 0 || n_sink > 64 || n_sink > S) return KIVI_ERR_SHAPE;
+    int64_t n = 0;
+    if (!mul_ok(B, H, &n) || !mul_ok(n, S, &n) || !mul_ok(n, D, &n) ||
+        n >= (1ll << 40))
+        return KIVI_ERR_SHAPE;
+    if (!mul_ok(B, S, &n) || n >= (1ll << 31)) return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
+bool aligned4(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
+}
+
+kivi_status sink_copy(bool gather, const void* src, int64_t B, int64_t H,
+                      int64_t S, int64_t D, const int32_t* idx,
+                      int64_t n_sink, void* dst, hipStream_t stream) {
+    kivi_status st = check_sink(B, H, S, D, n_sink);
+    if (st != KIVI_OK) return st;
+    if (D % 8 != 0 || B * H * n_sink * (D / 8) >= (1ll << 32))
+        return KIVI_ERR_SHAPE;
+    if (n_sink == 0) return KIVI_OK;
+    if (!src || !dst || !idx) return KIVI_ERR_NULL;
+    if (!aligned16(src) || !aligned16(dst) || !aligned4(idx))
+        return KIVI_ERR_ALIGN;
+    return launched(kivi::launch_sink_copy(gather, src, dst, B, H, S, D, idx,
+                                           n_sink, stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+kivi_status kivi_sink_select(const void* k, kivi_dtype dt, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int64_t n_sink,
+                             float* score, int32_t* idx, hipStream_t stream) {
+    kivi_status st = check_sink(B, H, S, D, n_sink);
+    if (st != KIVI_OK) return st;
+    if (!(D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256))
+        return KIVI_ERR_SHAPE;
+    if (!dtype_ok(dt)) return KIVI_ERR_DTYPE;
+    if (!k || !score || (n_sink > 0 && !idx)) return KIVI_ERR_NULL;
+    if (!aligned16(k) || !aligned4(score) || !aligned4(idx))
+        return KIVI_ERR_ALIGN;
+    if (kivi::launch_sink_scores(k, (int)dt, B, H, S, D, score, stream) !=
+        hipSuccess)
+        return KIVI_ERR_LAUNCH;
+    if (n_sink == 0) return KIVI_OK;
+    return launched(kivi::launch_sink_select(score, B, S, n_sink, idx, stream));
+}
+
+kivi_status kivi_quant_keys_sink(const void* k, kivi_dtype dt, int64_t B,
+                                 int64_t H, int64_t S, int64_t D, int bits,
+                                 int64_t group, const int32_t* idx,
+                                 int64_t n_sink, uint8_t* codes, float* scale,
+                                 float* zero, void* recon, hipStream_t stream) {
+    if (!bits_ok(bits)) return KIVI_ERR_BITS;
+    if (group < 1 || group > 32) return KIVI_ERR_GROUP;
+    kivi_status st = check_sink(B, H, S, D, n_sink);
+    if (st != KIVI_OK) return st;
+    if (D % 8 != 0) return KIVI_ERR_SHAPE;
+    if (B * H * ((S + group - 1) / group) * (D / 8) >= (1ll << 32))
+        return KIVI_ERR_SHAPE;
+    if (!dtype_ok(dt)) return KIVI_ERR_DTYPE;
+    const int nq = (codes != nullptr) + (scale != nullptr) + (zero != nullptr);
+    if (!k || (nq != 0 && nq != 3) || (nq == 0 && !recon) ||
+        (n_sink > 0 && !idx))
+        return KIVI_ERR_NULL;
+    if (!aligned16(k) || !aligned16(codes) || !aligned16(scale) ||
+        !aligned16(zero) || !aligned16(recon) || !aligned4(idx))
+        return KIVI_ERR_ALIGN;
+    kivi::SinkQuantJob j{k, (int)dt, B, H, S, D, bits, group, idx, n_sink,
+                         codes, scale, zero, recon, stream};
+    return launched(kivi::launch_quant_keys_sink(j));
+}
+
+kivi_status kivi_sink_gather(const void* x, int64_t B, int64_t H, int64_t S,
+                             int64_t D, const int32_t* idx, int64_t n_sink,
+                             void* x_sink, hipStream_t stream) {
+    return sink_copy(true, x, B, H, S, D, idx, n_sink, x_sink, stream);
+}
+
+kivi_status kivi_sink_restore(const void* x_sink, int64_t B, int64_t H,
+                              int64_t S, int64_t D, const int32_t* idx,
+                              int64_t n_sink, void* out, hipStream_t stream) {
+    return sink_copy(false, x_sink, B, H, S, D, idx, n_sink, out, stream);
+}
 
 kivi_status kivi_quant_keys(const void* k, kivi_dtype dt, int64_t BH,
                             int64_t S, int64_t D, int bits, int64_t group,

@@ -105,6 +105,36 @@ int64_t attend_work_floats(int64_t BH, int64_t T, int64_t D, int64_t n_q);
 hipError_t launch_attend(const AttendArgs& a, int64_t BH, int dtype, int bits,
                          hipStream_t stream);
 
+// KIVI-Sink (sink.hip).  Keys are [B*H, S, D] with the H heads of
+// sequence b at rows b*H .. b*H + H - 1; sink lists are [B, n_sink].  The
+// caller has checked D in {8, ..., 256} (a power of two) for the scores,
+// D % 8 == 0 and 1 <= group <= 32 for the keys, 1 <= n_sink <= 64 for the
+// selection and the copies, and sizes that keep lane indices in 32 bits.
+struct SinkQuantJob {
+    const void* k;
+    int dtype;
+    int64_t B, H, S, D;
+    int bits;
+    int64_t group;
+    const int32_t* idx;
+    int64_t n_sink;
+    uint8_t* codes;       // codes/scale/zero all null or all given
+    float* scale;
+    float* zero;
+    void* recon;          // may be null
+    hipStream_t stream;
+};
+hipError_t launch_sink_scores(const void* k, int dtype, int64_t B, int64_t H,
+                              int64_t S, int64_t D, float* score,
+                              hipStream_t stream);
+hipError_t launch_sink_select(const float* score, int64_t B, int64_t S,
+                              int64_t n_sink, int32_t* idx, hipStream_t stream);
+hipError_t launch_quant_keys_sink(const SinkQuantJob& j);
+hipError_t launch_sink_copy(bool gather, const void* src, void* dst, int64_t B,
+                            int64_t H, int64_t S, int64_t D,
+                            const int32_t* idx, int64_t n_sink,
+                            hipStream_t stream);
+
 hipError_t launch_quant_keys(const QuantJob& j);
 hipError_t launch_quant_values(const QuantJob& j);
 hipError_t launch_dequant_keys(const DequantJob& j);

@@ -214,3 +214,49 @@ def test_cache_append_rejects_before_any_launch(K):
     assert call(cache(), k=0) == NULL
     assert call(cache(v_zero=0x80004)) == ALIGN
     assert call(cache(), v=0xA0008) == ALIGN
+
+
+def test_sink_entry_points_reject_before_any_launch(K):
+    """KIVI-Sink argument rules (include/kivi.h): every call below fails
+    validation, so the fake pointers are never dereferenced."""
+    L = K.raw()
+    P = ctypes.c_void_p
+    k, sc, idx, out = P(0x1000), P(0x2000), P(0x3000), P(0x4000)
+
+    def select(B=2, H=4, S=64, D=128, n=5, dt=0, k=k, sc=sc, idx=idx):
+        return L.kivi_sink_select(k, dt, B, H, S, D, n, sc, idx, None)
+
+    assert select(n=65, S=100) == 2        # n_sink > 64
+    assert select(n=9, S=8) == 2           # n_sink > S
+    assert select(n=-1) == 2
+    assert select(D=48) == 2               # not a power of two in [8, 256]
+    assert select(D=512) == 2
+    assert select(B=0) == 2 and select(H=0) == 2 and select(S=0) == 2
+    assert select(B=1 << 20, S=1 << 12, H=1, D=8) == 2   # B*S >= 2^31
+    assert select(dt=2) == 5
+    assert select(k=None) == 1 and select(sc=None) == 1
+    assert select(idx=None) == 1 and select(n=0, idx=None, k=P(0x1001)) == 6
+    assert select(k=P(0x1008)) == 6                     # k not 16-byte aligned
+    assert select(sc=P(0x2002)) == 6
+
+    def qks(bits=2, G=32, D=128, n=5, codes=P(0x5000), scale=P(0x6000),
+            zero=P(0x7000), recon=None, idx=idx, S=64):
+        return L.kivi_quant_keys_sink(k, 0, 2, 4, S, D, bits, G, idx, n,
+                                      codes, scale, zero, recon, None)
+
+    assert qks(bits=3) == 3
+    assert qks(G=0) == 4 and qks(G=33) == 4
+    assert qks(D=12) == 2
+    assert qks(codes=None) == 1                          # partial q outputs
+    assert qks(codes=None, scale=None, zero=None) == 1   # no output at all
+    assert qks(idx=None) == 1
+    assert qks(recon=P(0x8004)) == 6
+    assert qks(n=70, S=100) == 2
+
+    for name in ("kivi_sink_gather", "kivi_sink_restore"):
+        fn = getattr(L, name)
+        assert fn(k, 2, 4, 64, 12, idx, 5, out, None) == 2      # D % 8
+        assert fn(k, 2, 4, 64, 128, idx, 65, out, None) == 2
+        assert fn(k, 2, 4, 64, 128, None, 5, out, None) == 1
+        assert fn(k, 2, 4, 64, 128, idx, 5, P(0x4008), None) == 6
+        assert fn(None, 2, 4, 64, 128, idx, 0, None, None) == 0  # nothing to do

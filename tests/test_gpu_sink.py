@@ -1,0 +1,179 @@
+"""GPU parity of KIVI-Sink (kivi_sink_select, kivi_quant_keys_sink,
+kivi_sink_gather, kivi_sink_restore) against the oracle: bit-exact scores,
+sink lists, codes, fp32 params and reconstructions.
+
+Small cases span several key groups, ragged last groups, ties, positions
+outside [0, S), groups made only of sinks and n_sink = 0; the full-size
+prompt (14 sequences x 8 KV heads x 32768 tokens) runs in the launch shape
+the benchmark times and is compared on tokens and key groups the oracle
+computes one by one."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle                                              # noqa: E402
+import workloads as W                                      # noqa: E402
+from gpu_util import (FP16, BF16, TORCH_DT, assert_codes_equal,   # noqa: E402
+                      assert_f32_bits_equal, assert_recon_equal, bits16,
+                      host, say, to_dev, to_dev_raw)
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_cache_quantization_kivi_amd as K
+    return K
+
+
+@pytest.fixture(scope="module")
+def O():
+    return oracle.default()
+
+
+def _keys(seed, B, H, S, D, dtype, planted=(), factor=8.0):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((B, H, S, D)).astype(np.float32)
+    x[..., r.choice(D, size=max(1, D // 32), replace=False)] *= 10.0
+    for b, pos in planted:
+        x[b, :, pos] *= factor
+    x = x.reshape(B * H, S, D)
+    if dtype == FP16:
+        return x.astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16)
+    return t.numpy().view(np.uint16)
+
+
+SELECT_CASES = [
+    # (B, H, S, D, n_sink, dtype)
+    (2, 4, 300, 128, 5, FP16),
+    (3, 1, 77, 64, 7, BF16),
+    (1, 8, 1000, 256, 64, FP16),
+    (4, 2, 33, 8, 33, BF16),         # every token a sink
+    (2, 3, 50, 32, 0, FP16),         # scores only
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_select_matches_oracle(K, O, case):
+    B, H, S, D, n, dtype = case
+    say(f"[sink select {case}]")
+    x = _keys(61, B, H, S, D, dtype, planted=[(0, [3, S - 1]), (B - 1, [S // 2])])
+    idx, score = K.kivi_sink_select(to_dev(x, dtype).view(B, H, S, D), n)
+    torch.cuda.synchronize()
+    want_s = O.sink_scores(x, dtype, H)
+    assert_f32_bits_equal(host(score), want_s, "scores")
+    assert np.array_equal(host(idx), O.sink_select(want_s, n)), "sink lists"
+
+
+def test_select_ties_take_lower_position(K, O):
+    """Rows repeated across positions have equal scores: the lower position
+    must win (and the GPU's block-wide reduction must agree)."""
+    B, H, S, D = 2, 2, 700, 64
+    x = _keys(62, B, H, S, D, FP16).reshape(B, H, S, D)
+    for b in range(B):
+        for p in (5, 260, 517, 699):        # four copies of row 5, all large
+            x[b, :, p] = x[b, :, 5]
+        x[b, :, 5] = (np.float16(4.0) * x[b, :, 5].view(np.float16)).view(np.uint16)
+        for p in (260, 517, 699):
+            x[b, :, p] = x[b, :, 5]
+    x = x.reshape(B * H, S, D)
+    idx, score = K.kivi_sink_select(to_dev(x, FP16), 3, H=H)
+    torch.cuda.synchronize()
+    want = O.sink_select(O.sink_scores(x, FP16, H), 3)
+    assert np.array_equal(host(idx), want)
+    assert host(idx)[0].tolist() == [5, 260, 517]
+
+
+QUANT_CASES = [
+    # (B, H, S, D, bits, G, dtype, sink lists (None = select n))
+    (2, 4, 300, 128, 2, 32, FP16, 5),
+    (3, 2, 70, 64, 4, 8, BF16, 6),
+    (1, 3, 47, 16, 8, 5, FP16, [[0, 1, 2, 3, 4, 46, 40, 100, -3]]),  # all-sink group, ragged
+    (2, 1, 129, 128, 1, 32, BF16, [[128, 128, 0, 31], [64, 65, 66, 67]]),  # duplicates
+    (2, 2, 64, 128, 2, 32, FP16, 0),                          # plain KIVI
+    (1, 2, 40, 24, 2, 1, FP16, [[7, 39]]),                    # G = 1
+]
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=lambda c: "x".join(map(str, c[:7])))
+def test_quant_keys_sink_matches_oracle(K, O, case):
+    B, H, S, D, bits, G, dtype, sinks = case
+    say(f"[sink quant {case[:7]}]")
+    x = _keys(63, B, H, S, D, dtype, planted=[(0, [1, S // 3])])
+    xd = to_dev(x, dtype)
+    if isinstance(sinks, int):
+        idx_d, _ = K.kivi_sink_select(xd, sinks, H=H)
+        torch.cuda.synchronize()
+        idx = host(idx_d)
+    else:
+        idx = np.array(sinks, np.int32)
+        idx_d = to_dev_raw(idx)
+    recon, codes, scale, zero = K.kivi_quant_keys_sink(
+        xd, idx_d, bits, G, H=H, with_recon=True)
+    only = K.kivi_quant_keys_sink(xd, idx_d, bits, G, H=H, with_codes=False)
+    torch.cuda.synchronize()
+    wc, ws, wz = O.quant_keys_sink(x, dtype, H, bits, G, idx)
+    assert_codes_equal(host(codes), wc, "codes")
+    assert_f32_bits_equal(host(scale), ws, "scale")
+    assert_f32_bits_equal(host(zero), wz, "zero")
+    want_r = O.sink_recon(x, dtype, H, bits, G, idx)
+    assert_recon_equal(bits16(recon), want_r, "recon")
+    assert_recon_equal(bits16(only), want_r, "recon-only")
+    # gather + dequant + restore on the GPU gives the same reconstruction
+    # rows of positions outside [0, S) are left as they were: start at zero
+    kept = K.kivi_sink_gather(xd, idx_d, H=H, out=torch.zeros(
+        (B * H, idx.shape[1], D), dtype=TORCH_DT[dtype], device="cuda"))
+    deq = K.kivi_dequant_keys(codes, scale, zero, bits, G, out_dtype=TORCH_DT[dtype])
+    K.kivi_sink_restore(kept, idx_d, deq, H=H)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(kept), O.sink_gather(x, H, idx))
+    assert_recon_equal(bits16(deq), want_r, "dequant + restore")
+    if idx.shape[1] == 0:
+        pc, ps, pz = K.kivi_quant_keys(xd, bits, G)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pc), host(codes))
+        assert np.array_equal(host(ps).view(np.uint32), host(scale).view(np.uint32))
+
+
+def test_sink_full_size_sampled(K, O):
+    """The benchmark's prompt in the benchmark's launch shape: scores on
+    sampled tokens, the sink lists (the top of the GPU's own scores, which
+    are checked exactly where sampled, and the planted tokens), and codes,
+    params and values of sampled key groups against the oracle."""
+    sw = W.SINK_WORKLOADS["sink-prefill"]
+    w = sw.tokens()
+    B, H, S, D, n = sw.B, sw.H, sw.S, sw.D, sw.n_sink
+    say(f"[sink full size {sw.name}]")
+    x = W.gen_tensor(w, "K")
+    xd = to_dev(x, w.dtype)
+    idx_d, score_d = K.kivi_sink_select(xd, n, H=H)
+    codes, scale, zero = K.kivi_quant_keys_sink(xd, idx_d, w.bits, w.group_k, H=H)
+    torch.cuda.synchronize()
+    idx, score = host(idx_d), host(score_d)
+    r = np.random.default_rng(5)
+    for b in (0, 6, B - 1):
+        toks = np.sort(np.concatenate([r.choice(S, 40, replace=False), idx[b]]))
+        sub = np.ascontiguousarray(x[b * H:(b + 1) * H][:, toks])
+        assert_f32_bits_equal(score[b, toks], O.sink_scores(sub, w.dtype, H)[0],
+                              f"scores of sequence {b}")
+        assert np.array_equal(idx[b], np.argsort(-score[b], kind="stable")[:n])
+        assert sorted(idx[b].tolist()) == W.planted_positions(w, b).tolist()
+    NG = S // w.group_k
+    rb = D * w.bits // 8
+    for bh in (0, 17, B * H - 1):
+        b = bh // H
+        groups = sorted({0, NG - 1, *(int(s) // w.group_k for s in idx[b]),
+                         *r.choice(NG, 6, replace=False).tolist()})
+        for g in groups:
+            s0 = g * w.group_k
+            tile = np.ascontiguousarray(x[bh:bh + 1, s0:s0 + w.group_k])
+            local = (idx[b:b + 1] - s0).astype(np.int32)
+            wc, ws, wz = O.quant_keys_sink(tile, w.dtype, 1, w.bits, w.group_k, local)
+            assert_codes_equal(host(codes[bh, s0:s0 + w.group_k]), wc[0], f"codes {bh},{g}")
+            assert_f32_bits_equal(host(scale[bh, g]), ws[0, 0], f"scale {bh},{g}")
+            assert_f32_bits_equal(host(zero[bh, g]), wz[0, 0], f"zero {bh},{g}")
+    assert codes.shape == (B * H, S, rb)

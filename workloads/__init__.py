@@ -40,6 +40,8 @@ class Workload:
     key_kind: str     # recipe for K
     value_kind: str   # recipe for V
     desc: str
+    heads: int = 1    # KV heads per sequence (rows b*heads .. of BH)
+    n_planted: int = 0   # planted high-norm key tokens per sequence
 
     @property
     def elems(self):
@@ -152,6 +154,55 @@ ATTEND_WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class SinkWorkload:
+    """KIVI-Sink over a prompt: B sequences of H KV heads ([B*H, S, D]),
+    keys with n_planted tokens per sequence whose rows (in every head) are
+    scaled up, so that they stand out by key norm the way attention sinks
+    do; n_sink tokens per sequence are selected and kept."""
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: int
+    bits: int
+    group_k: int
+    group_v: int
+    n_sink: int
+    seed: int
+    key_kind: str
+    value_kind: str
+    desc: str
+
+    def tokens(self):
+        return Workload(self.name, self.B * self.H, self.S, self.D, self.dtype,
+                        self.bits, self.group_k, self.group_v, self.seed,
+                        self.key_kind, self.value_kind, self.desc,
+                        heads=self.H, n_planted=self.n_sink)
+
+
+SINK_WORKLOADS = {
+    w.name: w for w in [
+        SinkWorkload("sink-prefill", 14, 8, 32768, 128, FP16, 2, 32, 32, 5, 9,
+                     "prefill", "normal05",
+                     "KIVI-Sink over a 32768-token prompt: 14 layers x 8 KV "
+                     "heads, D=128, fp16, 2-bit, 5 sinks per layer (token 0 "
+                     "and 4 seeded positions carry 6x keys)"),
+    ]
+}
+
+PLANT_FACTOR = 6.0
+
+
+def planted_positions(w, b):
+    """The planted high-norm tokens of sequence b: token 0 and n_planted - 1
+    further distinct positions drawn from (seed, b)."""
+    r = np.random.default_rng([w.seed, 11, b])
+    rest = r.choice(np.arange(1, w.S), size=w.n_planted - 1, replace=False)
+    return np.sort(np.concatenate([[0], rest])).astype(np.int64)
+
+
 def _rng(w, tensor, bh, pool):
     return np.random.default_rng([w.seed, _TENSOR_ID[tensor], bh, pool])
 
@@ -209,7 +260,10 @@ def slice_f32(w, tensor, bh, pool=0):
 
 def gen_slice(w, tensor, bh, pool=0):
     """uint16 bit patterns of one [S, D] slice."""
-    return _to_bits(slice_f32(w, tensor, bh, pool), w.dtype)
+    x = slice_f32(w, tensor, bh, pool)
+    if tensor == "K" and w.n_planted > 0:
+        x[planted_positions(w, bh // w.heads)] *= np.float32(PLANT_FACTOR)
+    return _to_bits(x, w.dtype)
 
 
 def gen_tensor(w, tensor, bhs=None, pool=0, threads=None):
