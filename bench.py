@@ -749,6 +749,8 @@ def sink_bench(args, sw, K, torch, dev):
         for i in range(args.steps):
             ev = (torch.cuda.Event(enable_timing=True),
                   torch.cuda.Event(enable_timing=True))
+            ev[0].record(stream)   # torch times only events it has recorded;
+            ev[1].record(stream)   # the armed launch then re-records both
             step(base + i, arm=a)
             torch.cuda.synchronize()
             d.append(ev[0].elapsed_time(ev[1]))
