@@ -66,6 +66,14 @@ class Oracle:
                                          I64, P, P, P]
         L.kivi_ref_sink_gather.argtypes = [P, I64, I64, I64, I64, P, I64, P]
         L.kivi_ref_sink_restore.argtypes = [P, I64, I64, I64, I64, P, I64, P]
+        L.kivi_ref_partition_top.argtypes = [P, I64, I64, I64, P, P]
+        for name in ("kivi_ref_quant_keys_rows", "kivi_ref_quant_values_rows"):
+            getattr(L, name).argtypes = [P, I, I64, I64, I64, I64, I, I64, P,
+                                         I64, P, P, P]
+        for name in ("kivi_ref_dequant_keys_rows",
+                     "kivi_ref_dequant_values_rows"):
+            getattr(L, name).argtypes = [P, P, P, I64, I64, I64, I64, I, I64,
+                                         P, I64, I, P]
         self.L = L
         self.path = path
 
@@ -255,6 +263,83 @@ class Oracle:
         codes, sc, z = self.quant_keys_sink(x, dtype, H, bits, group, idx)
         deq = self.dequant_keys(codes, sc, z, (BH, S, D), bits, group, dtype)
         return self.sink_restore(self.sink_gather(x, H, idx), H, idx, deq)
+
+    # per-token mixed precision -------------------------------------------
+    def partition_top(self, score, n_hi):
+        """score [B, S] -> (pos_hi [B, n_hi], pos_lo [B, S - n_hi]), int32,
+        each ascending."""
+        score = np.ascontiguousarray(score, dtype=np.float32)
+        B, S = score.shape
+        hi = np.zeros((B, n_hi), np.int32)
+        lo = np.zeros((B, S - n_hi), np.int32)
+        self._check(self.L.kivi_ref_partition_top(_ptr(score), B, S, n_hi,
+                                                  _ptr(hi), _ptr(lo)),
+                    "partition_top")
+        return hi, lo
+
+    def _quant_rows(self, name, x, dtype, H, bits, group, pos, keys):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        BH, S, D = x.shape
+        n = pos.shape[1]
+        pshape = (BH, n_groups(n, group), D) if keys else (BH, n, n_groups(D, group))
+        sc = np.zeros(pshape, np.float32)
+        z = np.zeros(pshape, np.float32)
+        codes = np.zeros((BH, n, D * bits // 8), np.uint8)
+        self._check(getattr(self.L, name)(_ptr(x), dtype, BH // H, H, S, D,
+                                          bits, group, _ptr(pos), n,
+                                          _ptr(codes), _ptr(sc), _ptr(z)), name)
+        return codes, sc, z
+
+    def quant_keys_rows(self, x, dtype, H, bits, group, pos):
+        return self._quant_rows("kivi_ref_quant_keys_rows", x, dtype, H, bits,
+                                group, pos, True)
+
+    def quant_values_rows(self, x, dtype, H, bits, group, pos):
+        return self._quant_rows("kivi_ref_quant_values_rows", x, dtype, H,
+                                bits, group, pos, False)
+
+    def _dequant_rows(self, name, codes, scale, zero, shape, H, bits, group,
+                      pos, out_dtype, out):
+        BH, S, D = shape
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        out = (np.zeros(shape, np.uint16) if out is None
+               else np.array(out, dtype=np.uint16, copy=True, order="C"))
+        args = [np.ascontiguousarray(a) for a in (codes, scale, zero)]
+        self._check(getattr(self.L, name)(_ptr(args[0]), _ptr(args[1]),
+                                          _ptr(args[2]), BH // H, H, S, D,
+                                          bits, group, _ptr(pos), pos.shape[1],
+                                          out_dtype, _ptr(out)), name)
+        return out
+
+    def dequant_keys_rows(self, codes, scale, zero, shape, H, bits, group,
+                          pos, out_dtype, out=None):
+        return self._dequant_rows("kivi_ref_dequant_keys_rows", codes, scale,
+                                  zero, shape, H, bits, group, pos, out_dtype,
+                                  out)
+
+    def dequant_values_rows(self, codes, scale, zero, shape, H, bits, group,
+                            pos, out_dtype, out=None):
+        return self._dequant_rows("kivi_ref_dequant_values_rows", codes, scale,
+                                  zero, shape, H, bits, group, pos, out_dtype,
+                                  out)
+
+    def mixed_recon(self, x, dtype, H, n_hi, hi_bits, lo_bits, group, keys):
+        """The mixed-precision reconstruction of keys (keys=True, per-channel
+        groups over each set's tokens) or values: the n_hi highest key-norm
+        tokens of each sequence at hi_bits, the rest at lo_bits.  The ranking
+        always comes from the keys, so for values pass the keys as `keys`."""
+        kx = x if keys is True else keys
+        hi, lo = self.partition_top(self.sink_scores(kx, dtype, H), n_hi)
+        out = np.zeros(x.shape, np.uint16)
+        q = self.quant_keys_rows if keys is True else self.quant_values_rows
+        dq = self.dequant_keys_rows if keys is True else self.dequant_values_rows
+        for pos, bits in ((hi, hi_bits), (lo, lo_bits)):
+            if pos.shape[1] == 0:
+                continue
+            c, sc, z = q(x, dtype, H, bits, group, pos)
+            out = dq(c, sc, z, x.shape, H, bits, group, pos, dtype, out)
+        return out
 
     def cache(self, BH, D, S_max, R, G_k, G_v, bits, dtype):
         """A residual-window cache (kivi_ref_cache) over numpy arrays."""

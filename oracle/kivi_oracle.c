@@ -530,17 +530,18 @@ int kivi_ref_quant_keys_sink_unpacked(const uint16_t* x, int dtype, int64_t B,
         int64_t b = bh / H;
         for (int64_t g = 0; g < NG; ++g) {
             int64_t s0 = g * group;
-            int64_t s1 = s0 + group < S ? s0 + group : S;
-            for (int64_t s = s0; s < s1; ++s) sink[s - s0] = (unsigned char)is_sink(idx, n_sink, b, s);
+            int64_t s_end = s0 + group < S ? s0 + group : S;
+            for (int64_t s = s0; s < s_end; ++s) sink[s - s0] = (unsigned char)is_sink(idx, n_sink, b, s);
             for (int64_t d = 0; d < D; ++d) {
                 int64_t n = 0;
-                for (int64_t s = s0; s < s1; ++s)
+                for (int64_t s = s0; s < s_end; ++s)
                     if (!sink[s - s0]) vals[n++] = widen(x[(bh * S + s) * D + d], dtype);
                 float sc = 0.0f, z = 0.0f;
                 if (n > 0) kivi_ref_group_params(vals, n, bits, &sc, &z);
-                scale[(bh * NG + g) * D + d] = sc;
-                zero[(bh * NG + g) * D + d] = z;
-                for (int64_t s = s0; s < s1; ++s) {
+                int64_t pi = (bh * NG + g) * D + d;
+                scale[pi] = sc;
+                zero[pi] = z;
+                for (int64_t s = s0; s < s_end; ++s) {
                     float f = widen(x[(bh * S + s) * D + d], dtype);
                     codes[(bh * S + s) * D + d] =
                         sink[s - s0] ? 0 : (uint8_t)kivi_ref_code(f, sc, z, bits);
@@ -600,4 +601,145 @@ int kivi_ref_sink_restore(const uint16_t* x_sink, int64_t B, int64_t H,
                    (size_t)D * sizeof(uint16_t));
         }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-token mixed precision (VeloxQuant-MLX 0.24.1 package page, section   */
+/* "ZipCache-adapted -- saliency-adaptive per-token mixed precision"): the  */
+/* tokens with the highest key norm are quantized at hi_bits, the rest at   */
+/* lo_bits, both with the KIVI group quantizer.  Reading: the two token     */
+/* sets are quantized as two tensors -- the listed tokens of every head in  */
+/* position order -- so a key group is `group` consecutive tokens of a set. */
+/* ------------------------------------------------------------------------ */
+
+static const float* g_part_score;   /* the scores being ranked by qsort */
+
+/* Rank order: higher score first; of equal scores the lower position. */
+static int rank_cmp(const void* a, const void* b) {
+    int32_t i = *(const int32_t*)a, j = *(const int32_t*)b;
+    float si = g_part_score[i], sj = g_part_score[j];
+    if (si > sj) return -1;
+    if (si < sj) return 1;
+    return (i > j) - (i < j);
+}
+
+/* pos_hi [B, n_hi]: positions of the n_hi first tokens in rank order, listed
+ * in ascending position; pos_lo [B, S - n_hi]: all other positions, ascending. */
+int kivi_ref_partition_top(const float* score, int64_t B, int64_t S,
+                           int64_t n_hi, int32_t* pos_hi, int32_t* pos_lo) {
+    if (B < 0 || S < 0 || n_hi < 0 || n_hi > S) return 1;
+    int32_t* order = (int32_t*)malloc((size_t)(S > 0 ? S : 1) * sizeof(int32_t));
+    unsigned char* hi = (unsigned char*)malloc((size_t)(S > 0 ? S : 1));
+    if (!order || !hi) {
+        free(order);
+        free(hi);
+        return 1;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+        for (int64_t s = 0; s < S; ++s) order[s] = (int32_t)s;
+        g_part_score = score + b * S;
+        qsort(order, (size_t)S, sizeof(int32_t), rank_cmp);
+        memset(hi, 0, (size_t)(S > 0 ? S : 1));
+        for (int64_t r = 0; r < n_hi; ++r) hi[order[r]] = 1;
+        int64_t nh = 0, nl = 0;
+        for (int64_t s = 0; s < S; ++s) {
+            if (hi[s]) pos_hi[b * n_hi + nh++] = (int32_t)s;
+            else pos_lo[b * (S - n_hi) + nl++] = (int32_t)s;
+        }
+    }
+    free(order);
+    free(hi);
+    return 0;
+}
+
+/* The listed tokens of every head as one tensor: out[bh, j, :] =
+ * x[bh, pos[bh / H, j], :]. */
+static uint16_t* gather_rows(const uint16_t* x, int64_t B, int64_t H,
+                             int64_t S, int64_t D, const int32_t* pos,
+                             int64_t n) {
+    uint16_t* out = (uint16_t*)malloc((size_t)(B * H * n * D + 1) * sizeof(uint16_t));
+    if (!out) return NULL;
+    for (int64_t bh = 0; bh < B * H; ++bh)
+        for (int64_t j = 0; j < n; ++j)
+            memcpy(out + (bh * n + j) * D, x + (bh * S + pos[(bh / H) * n + j]) * D,
+                   (size_t)D * sizeof(uint16_t));
+    return out;
+}
+
+static int rows_ok(int64_t B, int64_t H, int64_t S, int64_t D,
+                   const int32_t* pos, int64_t n) {
+    if (B < 0 || H < 1 || S < 0 || D < 0 || n < 0 || n > S) return 0;
+    for (int64_t i = 0; i < B * n; ++i)
+        if (pos[i] < 0 || pos[i] >= S) return 0;
+    return 1;
+}
+
+/* Keys of the listed tokens: kivi_ref_quant_keys of the gathered
+ * [B*H, n, D] tensor (codes [B*H, n, D*bits/8], params [B*H, ceil(n/group), D]). */
+int kivi_ref_quant_keys_rows(const uint16_t* x, int dtype, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int bits,
+                             int64_t group, const int32_t* pos, int64_t n,
+                             uint8_t* packed, float* scale, float* zero) {
+    if (!rows_ok(B, H, S, D, pos, n)) return 1;
+    uint16_t* g = gather_rows(x, B, H, S, D, pos, n);
+    if (!g) return 1;
+    int st = kivi_ref_quant_keys(g, dtype, B * H, n, D, bits, group, packed,
+                                 scale, zero);
+    free(g);
+    return st;
+}
+
+/* Values of the listed tokens: kivi_ref_quant_values of the gathered tensor
+ * (params [B*H, n, ceil(D/group)]). */
+int kivi_ref_quant_values_rows(const uint16_t* x, int dtype, int64_t B,
+                               int64_t H, int64_t S, int64_t D, int bits,
+                               int64_t group, const int32_t* pos, int64_t n,
+                               uint8_t* packed, float* scale, float* zero) {
+    if (!rows_ok(B, H, S, D, pos, n)) return 1;
+    uint16_t* g = gather_rows(x, B, H, S, D, pos, n);
+    if (!g) return 1;
+    int st = kivi_ref_quant_values(g, dtype, B * H, n, D, bits, group, packed,
+                                   scale, zero);
+    free(g);
+    return st;
+}
+
+/* Dequantize a listed set and write its rows back to their positions:
+ * out[bh, pos[bh / H, j], :] = recon[bh, j, :]; other rows are untouched. */
+static int dequant_rows(int keys, const uint8_t* packed, const float* scale,
+                        const float* zero, int64_t B, int64_t H, int64_t S,
+                        int64_t D, int bits, int64_t group, const int32_t* pos,
+                        int64_t n, int out_dtype, uint16_t* out) {
+    if (!rows_ok(B, H, S, D, pos, n)) return 1;
+    uint16_t* r = (uint16_t*)malloc((size_t)(B * H * n * D + 1) * sizeof(uint16_t));
+    if (!r) return 1;
+    int st = keys ? kivi_ref_dequant_keys(packed, scale, zero, B * H, n, D,
+                                          bits, group, out_dtype, r)
+                  : kivi_ref_dequant_values(packed, scale, zero, B * H, n, D,
+                                            bits, group, out_dtype, r);
+    if (st == 0)
+        for (int64_t bh = 0; bh < B * H; ++bh)
+            for (int64_t j = 0; j < n; ++j)
+                memcpy(out + (bh * S + pos[(bh / H) * n + j]) * D, r + (bh * n + j) * D,
+                       (size_t)D * sizeof(uint16_t));
+    free(r);
+    return st;
+}
+
+int kivi_ref_dequant_keys_rows(const uint8_t* packed, const float* scale,
+                               const float* zero, int64_t B, int64_t H,
+                               int64_t S, int64_t D, int bits, int64_t group,
+                               const int32_t* pos, int64_t n, int out_dtype,
+                               uint16_t* out) {
+    return dequant_rows(1, packed, scale, zero, B, H, S, D, bits, group, pos,
+                        n, out_dtype, out);
+}
+
+int kivi_ref_dequant_values_rows(const uint8_t* packed, const float* scale,
+                                 const float* zero, int64_t B, int64_t H,
+                                 int64_t S, int64_t D, int bits, int64_t group,
+                                 const int32_t* pos, int64_t n, int out_dtype,
+                                 uint16_t* out) {
+    return dequant_rows(0, packed, scale, zero, B, H, S, D, bits, group, pos,
+                        n, out_dtype, out);
 }

@@ -171,6 +171,38 @@ int kivi_ref_sink_restore(const uint16_t* x_sink, int64_t B, int64_t H,
                           int64_t S, int64_t D, const int32_t* idx,
                           int64_t n_sink, uint16_t* out);
 
+/* Per-token mixed precision (VeloxQuant-MLX 0.24.1 package page, section
+ * "ZipCache-adapted -- saliency-adaptive per-token mixed precision"): the
+ * n_hi tokens of highest key-norm score per sequence at hi_bits, the rest at
+ * lo_bits.  The two sets are quantized as two tensors of the listed tokens.
+ *   partition_top: pos_hi [B, n_hi] the n_hi first positions in the order
+ *       (score descending, position ascending), listed ascending; pos_lo
+ *       [B, S - n_hi] the others, ascending;
+ *   quant_{keys,values}_rows: the plain quantizers applied to the tensor
+ *       [B*H, n, D] of rows x[bh, pos[bh / H, j]] (positions in [0, S));
+ *   dequant_{keys,values}_rows: the plain dequantizers, each row written
+ *       back to out[bh, pos[bh / H, j]]. */
+int kivi_ref_partition_top(const float* score, int64_t B, int64_t S,
+                           int64_t n_hi, int32_t* pos_hi, int32_t* pos_lo);
+int kivi_ref_quant_keys_rows(const uint16_t* x, int dtype, int64_t B,
+                             int64_t H, int64_t S, int64_t D, int bits,
+                             int64_t group, const int32_t* pos, int64_t n,
+                             uint8_t* packed, float* scale, float* zero);
+int kivi_ref_quant_values_rows(const uint16_t* x, int dtype, int64_t B,
+                               int64_t H, int64_t S, int64_t D, int bits,
+                               int64_t group, const int32_t* pos, int64_t n,
+                               uint8_t* packed, float* scale, float* zero);
+int kivi_ref_dequant_keys_rows(const uint8_t* packed, const float* scale,
+                               const float* zero, int64_t B, int64_t H,
+                               int64_t S, int64_t D, int bits, int64_t group,
+                               const int32_t* pos, int64_t n, int out_dtype,
+                               uint16_t* out);
+int kivi_ref_dequant_values_rows(const uint8_t* packed, const float* scale,
+                                 const float* zero, int64_t B, int64_t H,
+                                 int64_t S, int64_t D, int bits, int64_t group,
+                                 const int32_t* pos, int64_t n, int out_dtype,
+                                 uint16_t* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,10 @@ or the mathematics fix:
     spike group, brute-force masked group params and codes, n_sink = 0
     equal to plain KIVI, and the pages' claims on planted-sink data (sinks
     bit-exact, lower MSE than plain KIVI and than keeping the first n);
+  - per-token mixed precision: the partition equals numpy's stable argsort,
+    listed rows equal numpy-gathered tensors through the plain quantizers,
+    and the page's evidence (cosine above 0.995 at 4 bits and 0.8 at 2,
+    all-hi beats all-lo, mixed in between in error and bytes);
   - the pages' statistic: 2-bit reconstruction cosine about 0.93 on
     unit-norm Gaussian keys (KIVI release post, "Honest limitations"; PyPI
     page, KIVI section), 4-bit above 0.995 (PyPI page, ZipCache section).
@@ -873,6 +877,134 @@ def pin_sink_claims(o):
     odd = np.array([[-1, S], [S + 5, -7]], np.int32)     # nothing in range
     assert not o.sink_restore(np.ones((B * H, 2, D), np.uint16), H, odd,
                               np.zeros_like(x)).any()
+
+
+# --------------------------------------------------------------------------
+# Per-token mixed precision (PyPI page of VeloxQuant-MLX 0.24.1, section
+# "ZipCache-adapted -- saliency-adaptive per-token mixed precision")
+# --------------------------------------------------------------------------
+
+def pin_mixed_partition(o):
+    """The hi set is the first n_hi positions in the order (score
+    descending, position ascending), i.e. numpy's stable descending argsort;
+    both lists ascending and together a permutation of the positions; ties,
+    n_hi = 0 and n_hi = S included."""
+    r = np.random.default_rng(81)
+    sc = r.random((3, 90)).astype(np.float32)
+    sc[1, 10:40] = np.float32(0.7)               # a long run of ties
+    sc[2] = np.float32(0.25)                      # everything tied
+    for n in (0, 1, 17, 45, 89, 90):
+        hi, lo = o.partition_top(sc, n)
+        exp = np.sort(np.argsort(-sc, axis=1, kind="stable")[:, :n], axis=1)
+        assert np.array_equal(hi, exp), n
+        for b in range(3):
+            assert np.array_equal(np.sort(np.concatenate([hi[b], lo[b]])),
+                                  np.arange(90))
+            assert (np.diff(lo[b]) > 0).all()
+    assert o.partition_top(sc, 5)[0][2].tolist() == [0, 1, 2, 3, 4]
+
+
+def pin_mixed_rows_are_gathered_tensors(o):
+    """Quantizing listed rows equals quantizing the tensor numpy gathers
+    (x[bh, pos[bh // H]]) with the plain quantizers; listing every position
+    is plain KIVI; the row dequantizers write exactly the listed rows, each
+    equal to the plain dequant of the gathered tensor."""
+    r = np.random.default_rng(82)
+    B, H, S, D = 2, 3, 61, 24
+    x = _rand_tensor(r, B * H, S, D, FP16)
+    pos = np.sort(np.stack([r.choice(S, 23, replace=False) for _ in range(B)]),
+                  axis=1).astype(np.int32)
+    g = np.stack([x[bh, pos[bh // H]] for bh in range(B * H)])
+    for keys, bits, G in ((True, 4, 8), (False, 2, 8), (True, 2, 32), (False, 4, 16)):
+        q = o.quant_keys_rows if keys else o.quant_values_rows
+        pq = o.quant_keys if keys else o.quant_values
+        got = q(x, FP16, H, bits, G, pos)
+        exp = pq(g, FP16, bits, G)
+        for a, b in zip(got, exp):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (keys, bits, G)
+        allpos = np.tile(np.arange(S, dtype=np.int32), (B, 1))
+        for a, b in zip(q(x, FP16, H, bits, G, allpos), pq(x, FP16, bits, G)):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+        dq = o.dequant_keys_rows if keys else o.dequant_values_rows
+        pdq = o.dequant_keys if keys else o.dequant_values
+        base = np.full(x.shape, 0x7777, np.uint16)
+        out = dq(*got, x.shape, H, bits, G, pos, FP16, base)
+        rec = pdq(*exp, g.shape, bits, G, FP16)
+        want = base.copy()
+        for bh in range(B * H):
+            want[bh, pos[bh // H]] = rec[bh]
+        assert np.array_equal(out, want), (keys, bits, G)
+    bad = pos.copy()
+    bad[1, 3] = S
+    try:
+        o.quant_keys_rows(x, FP16, H, 2, 8, bad)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("position outside [0, S) accepted")
+
+
+def pin_mixed_claims(o):
+    """The page's evidence for the variant: the saliency mask is the top
+    fraction by key norm; 4-bit per-channel quantization of unit-norm
+    Gaussian keys has cosine > 0.995 and 2-bit > 0.8; hi_fraction 1 beats
+    hi_fraction 0; mixed bits sit between all-lo and all-hi in error and in
+    bytes (compressed <= fp16, mixed >= all-lo), with average bits in
+    [lo_bits, hi_bits]."""
+    r = np.random.default_rng(83)
+    B, H, S, D, G = 2, 2, 320, 64, 32
+    f = r.standard_normal((B * H, S, D)).astype(np.float32)
+    f /= np.linalg.norm(f, axis=2, keepdims=True)
+    f *= r.uniform(0.5, 3.0, size=(B, 1, S, 1)).repeat(H, 1).reshape(B * H, S, 1).astype(np.float32)
+    x = f.astype(np.float16).view(np.uint16)
+    fx = o.widen(x, FP16).astype(np.float64)
+    norms = np.sqrt((fx ** 2).sum(axis=2)).reshape(B, H, S).mean(axis=1)
+    n_hi = int(0.2 * S)
+    hi, lo = o.partition_top(o.sink_scores(x, FP16, H), n_hi)
+    for b in range(B):
+        assert np.array_equal(hi[b], np.sort(np.argsort(-norms[b])[:n_hi]))
+
+    def err(rec):
+        e = o.widen(rec, FP16).astype(np.float64) - fx
+        return float((e ** 2).mean())
+
+    def cos(rec):
+        y = o.widen(rec, FP16).astype(np.float64)
+        return float(((y * fx).sum(2) / np.linalg.norm(y, axis=2)
+                      / np.linalg.norm(fx, axis=2)).mean())
+
+    # the page's cosines are for unit-norm Gaussian keys
+    u = (f / np.linalg.norm(f, axis=2, keepdims=True)).astype(np.float16).view(np.uint16)
+    fu = o.widen(u, FP16).astype(np.float64)
+
+    def cos_u(rec):
+        y = o.widen(rec, FP16).astype(np.float64)
+        return float(((y * fu).sum(2) / np.linalg.norm(y, axis=2)
+                      / np.linalg.norm(fu, axis=2)).mean())
+
+    c4 = cos_u(o.mixed_recon(u, FP16, H, S, 4, 2, G, True))
+    c2 = cos_u(o.mixed_recon(u, FP16, H, 0, 4, 2, G, True))
+    assert c4 > 0.995 and c2 > 0.8, (c4, c2)
+    rec4 = o.mixed_recon(x, FP16, H, S, 4, 2, G, True)        # all hi
+    rec2 = o.mixed_recon(x, FP16, H, 0, 4, 2, G, True)        # all lo
+    mix = o.mixed_recon(x, FP16, H, n_hi, 4, 2, G, True)
+    assert err(rec4) < err(mix) < err(rec2)
+    assert cos(rec4) > cos(mix) > cos(rec2)
+    # plain KIVI at one width is the mixed variant with an empty other set
+    pc, psc, pz = o.quant_keys(x, FP16, 4, G)
+    assert np.array_equal(rec4, o.dequant_keys(pc, psc, pz, x.shape, 4, G, FP16))
+
+    def nbytes(n, bits):
+        if n == 0:
+            return 0
+        c, sc, z = o.quant_keys_rows(x, FP16, H, bits, G, np.tile(
+            np.arange(n, dtype=np.int32), (B, 1)))
+        return c.nbytes + sc.nbytes + z.nbytes
+
+    mixed = nbytes(n_hi, 4) + nbytes(S - n_hi, 2)
+    assert nbytes(S, 2) <= mixed <= nbytes(S, 4) <= x.nbytes
+    avg = (n_hi * 4 + (S - n_hi) * 2) / S
+    assert 2 <= avg <= 4
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -94,6 +94,21 @@ MUTANTS = [
     ("sink_gather_range",
      "if (s < 0 || s >= S) continue;\n            memcpy(x_sink",
      "if (s < 0 || s > S) continue;\n            memcpy(x_sink"),
+    ("partition_tie_higher_first", "return (i > j) - (i < j);",
+     "return (i < j) - (i > j);"),
+    ("partition_lowest_scores", "    if (si > sj) return -1;\n    if (si < sj) return 1;",
+     "    if (si > sj) return 1;\n    if (si < sj) return -1;"),
+    ("partition_rank_from_bottom", "for (int64_t r = 0; r < n_hi; ++r) hi[order[r]] = 1;",
+     "for (int64_t r = 0; r < n_hi; ++r) hi[order[S - 1 - r]] = 1;"),
+    ("rows_gather_first_sequence",
+     "memcpy(out + (bh * n + j) * D, x + (bh * S + pos[(bh / H) * n + j]) * D,",
+     "memcpy(out + (bh * n + j) * D, x + (bh * S + pos[j]) * D,"),
+    ("rows_scatter_shifted",
+     "memcpy(out + (bh * S + pos[(bh / H) * n + j]) * D, r + (bh * n + j) * D,",
+     "memcpy(out + (bh * S + pos[(bh / H) * n + j]) * D, r + (bh * n) * D,"),
+    ("rows_values_group_doubled",
+     "    int st = kivi_ref_quant_values(g, dtype, B * H, n, D, bits, group, packed,",
+     "    int st = kivi_ref_quant_values(g, dtype, B * H, n, D, bits, group * 2, packed,"),
 ]
 
 
