@@ -40,7 +40,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
 KERNEL_SOURCES = ["kivi_device.h", "kivi_rows.h", "quant_keys.hip", "quant_values.hip",
-                  "dequant.hip", "cache.hip", "attend.hip", "sink.hip"]
+                  "dequant.hip", "cache.hip", "attend.hip", "sink.hip", "rows.hip"]
 
 
 def bytes_per_elem(op, bits, group, dtype_bytes=2):
@@ -828,6 +828,184 @@ def sink_bench(args, sw, K, torch, dev):
     print(json.dumps(result), flush=True)
 
 
+# --------------------------------------------------------------------------
+# per-token mixed precision over a prompt
+# --------------------------------------------------------------------------
+
+def mixed_bytes(mw):
+    """Algorithmic bytes of one mixed-precision round trip, per launch: the
+    scores read every key once; the partition reads the scores and writes
+    both position lists; each set's quantizer reads its rows and writes
+    codes and params; each dequantizer reads them back and writes the rows."""
+    BH, S, D = mw.B * mw.H, mw.S, mw.D
+    E = BH * S * D
+    out = {"key_scores": E * 2 + mw.B * S * 4, "partition": mw.B * S * 8}
+    for name, n, bits in (("hi", mw.n_hi, mw.hi_bits),
+                          ("lo", S - mw.n_hi, mw.lo_bits)):
+        kp = BH * (-(-n // mw.group_k)) * D * 8
+        vp = BH * n * (-(-D // mw.group_v)) * 8
+        rows = BH * n * D
+        out[f"quant_keys_{name}"] = rows * 2 + rows * bits // 8 + kp
+        out[f"quant_values_{name}"] = rows * 2 + rows * bits // 8 + vp
+        out[f"dequant_keys_{name}"] = rows * bits // 8 + kp + rows * 2
+        out[f"dequant_values_{name}"] = rows * bits // 8 + vp + rows * 2
+    return out
+
+
+def mixed_bench(args, mw, K, torch, dev):
+    """One step = the mixed-precision round trip over one prompt: key-norm
+    scores, the partition, both sets of keys and values quantized, and both
+    sets dequantized back into full tensors.  Inputs rotate over a pool of
+    prompts larger than the MALL."""
+    tdt = torch.float16 if mw.dtype == W.FP16 else torch.bfloat16
+    w = mw.tokens()
+    B, H, S, D = mw.B, mw.H, mw.S, mw.D
+    nb = mixed_bytes(mw)
+    step_bytes = sum(nb.values())
+    P = args.pool or 2
+    inputs = []
+    for p in range(P):
+        kv = []
+        for tensor in ("K", "V"):
+            x = W.gen_tensor(w, tensor, pool=p)
+            kv.append(torch.from_numpy(x.view(np.int16)).view(tdt).to(dev)
+                      .view(B, H, S, D))
+        inputs.append(tuple(kv))
+    score = K.kivi_key_scores(inputs[0][0])
+    hi, lo = K.kivi_partition_top(score, mw.n_hi)
+    sets = [("hi", hi, mw.hi_bits), ("lo", lo, mw.lo_bits)]
+    bufs = {}
+    for name, pos, bits in sets:
+        bufs["k" + name] = K.kivi_quant_keys_rows(inputs[0][0], pos, bits, mw.group_k)
+        bufs["v" + name] = K.kivi_quant_values_rows(inputs[0][1], pos, bits, mw.group_v)
+    k_out = torch.empty((B, H, S, D), dtype=tdt, device=dev)
+    v_out = torch.empty_like(k_out)
+    stream = torch.cuda.current_stream(dev)
+    calls = [("key_scores", lambda k, v: K.kivi_key_scores(k, score=score)),
+             ("partition", lambda k, v: K.kivi_partition_top(
+                 score, mw.n_hi, pos_hi=hi, pos_lo=lo))]
+    for name, pos, bits in sets:
+        kb, vb = bufs["k" + name], bufs["v" + name]
+        calls.append((f"quant_keys_{name}", lambda k, v, pos=pos, bits=bits, kb=kb:
+                      K.kivi_quant_keys_rows(k, pos, bits, mw.group_k, codes=kb[0],
+                                             scale=kb[1], zero=kb[2])))
+        calls.append((f"quant_values_{name}", lambda k, v, pos=pos, bits=bits, vb=vb:
+                      K.kivi_quant_values_rows(v, pos, bits, mw.group_v, codes=vb[0],
+                                               scale=vb[1], zero=vb[2])))
+    for name, pos, bits in sets:
+        kb, vb = bufs["k" + name], bufs["v" + name]
+        calls.append((f"dequant_keys_{name}", lambda k, v, pos=pos, bits=bits, kb=kb:
+                      K.kivi_dequant_keys_rows(*kb, pos, k_out, bits, mw.group_k)))
+        calls.append((f"dequant_values_{name}", lambda k, v, pos=pos, bits=bits, vb=vb:
+                      K.kivi_dequant_values_rows(*vb, pos, v_out, bits, mw.group_v)))
+
+    def step(i, arm=None):
+        k, v = inputs[i % P]
+        for a, (_, fn) in enumerate(calls):
+            if a == arm:
+                K.kivi_time_next_launch(*ev)
+            fn(k, v)
+
+    ev = None
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    pk = {}
+    base = args.warmup + args.steps
+    n_time = max(5, args.steps // 4)
+    for a, (name, _) in enumerate(calls):
+        d = []
+        for i in range(n_time):
+            ev = (torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True))
+            ev[0].record(stream)   # torch times only events it has recorded;
+            ev[1].record(stream)   # the armed launch then re-records both
+            step(base + i, arm=a)
+            torch.cuda.synchronize()
+            d.append(ev[0].elapsed_time(ev[1]))
+        base += n_time
+        avg = float(np.mean(d))
+        pk[name] = {"avg_us": round(avg * 1e3, 3),
+                    "median_us": round(float(np.median(d)) * 1e3, 3),
+                    "algorithmic_bytes": int(nb[name]),
+                    "gbs": round(nb[name] / (avg * 1e-3) / 1e9, 1)}
+    ev = None
+    dom = max(pk, key=lambda n: pk[n]["avg_us"])
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        O = oracle.default()
+        one = W.MixedWorkload(mw.name, 1, H, S, D, mw.dtype, mw.hi_bits,
+                              mw.lo_bits, mw.group_k, mw.group_v,
+                              mw.hi_fraction, mw.seed, mw.key_kind,
+                              mw.value_kind, mw.desc)
+        kx = W.gen_tensor(w, "K", range(H))
+        vx = W.gen_tensor(w, "V", range(H))
+        t0 = time.perf_counter()
+        ohi, olo = O.partition_top(O.sink_scores(kx, mw.dtype, H), mw.n_hi)
+        for pos, bits in ((ohi, mw.hi_bits), (olo, mw.lo_bits)):
+            kq = O.quant_keys_rows(kx, mw.dtype, H, bits, mw.group_k, pos)
+            vq = O.quant_values_rows(vx, mw.dtype, H, bits, mw.group_v, pos)
+            O.dequant_keys_rows(*kq, kx.shape, H, bits, mw.group_k, pos, mw.dtype)
+            O.dequant_values_rows(*vq, vx.shape, H, bits, mw.group_v, pos, mw.dtype)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(sum(mixed_bytes(one).values()) / dt / 1e9, 4),
+               "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": (f"1 of {B} sequences ({H} heads x {S} tokens), the "
+                          f"whole round trip: {dt:.2f} s on 1 thread")}
+    result = {
+        "metric": METRIC + " (per-token mixed precision round trip)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{mw.name}: {mw.desc}; step = key scores + "
+                         "partition + 4 set quantizers + 4 set dequantizers"),
+            "n_hi": mw.n_hi,
+            "step_algorithmic_bytes": int(step_bytes),
+            "input_pool": P,
+            "launch": "eager",
+            "wall_s": round(t_wall, 4),
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": dom,
+            "avg_us": pk[dom]["avg_us"],
+            "bound": "hbm",
+            "achieved": pk[dom]["gbs"],
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(pk[dom]["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic(dom, mw.name, kernel_source_hash()),
+        },
+        "per_kernel": pk,
+        "kernel_source_hash": kernel_source_hash(),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -835,7 +1013,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="roundtrip",
                     choices=sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS)
-                    + sorted(W.ATTEND_WORKLOADS) + sorted(W.SINK_WORKLOADS))
+                    + sorted(W.ATTEND_WORKLOADS) + sorted(W.SINK_WORKLOADS)
+                    + sorted(W.MIXED_WORKLOADS))
     ap.add_argument("--pool", type=int, default=0,
                     help="distinct input sets (0: enough to exceed 1 GB)")
     ap.add_argument("--cpu-sample-bh", type=int, default=0,
@@ -882,6 +1061,9 @@ def main():
         return
     if args.workload in W.SINK_WORKLOADS:
         sink_bench(args, W.SINK_WORKLOADS[args.workload], K, torch, dev)
+        return
+    if args.workload in W.MIXED_WORKLOADS:
+        mixed_bench(args, W.MIXED_WORKLOADS[args.workload], K, torch, dev)
         return
     w = W.WORKLOADS[args.workload]
     tdt = torch.float16 if w.dtype == W.FP16 else torch.bfloat16

@@ -194,7 +194,7 @@ typedef struct {
  * Errors (nothing is enqueued and the struct is unchanged):
  *   cache == NULL, a NULL buffer, or k_new/v_new NULL with n > 0 KIVI_ERR_NULL
  *   bits not 1, 2, 4, 8                                       KIVI_ERR_BITS
- *   G_k not in [1, 32], or G_v not 8, 16 or a multiple of 32  KIVI_ERR_GROUP
+ *   G_k not in [1, 32], or G_v not 8, 16 or 32 * 2^k          KIVI_ERR_GROUP
  *   dtype invalid                                             KIVI_ERR_DTYPE
  *   D not 8, 16, 32, 64, 128 or 256; BH, R, S_max or n < 0; ring not a
  *   multiple of G_k or < R + G_k; S_max or ring >= 2^31; BH*S_max*D/2
@@ -303,6 +303,67 @@ kivi_status kivi_sink_gather(const void* x, int64_t B, int64_t H, int64_t S,
 kivi_status kivi_sink_restore(const void* x_sink, int64_t B, int64_t H,
                               int64_t S, int64_t D, const int32_t* idx,
                               int64_t n_sink, void* out, hipStream_t stream);
+
+/*
+ * Per-token mixed precision (VeloxQuant-MLX 0.24.1 package page, section
+ * "ZipCache-adapted -- saliency-adaptive per-token mixed precision"): the
+ * tokens of highest key-norm score (kivi_sink_select with n_sink = 0 gives
+ * the scores) are quantized at hi_bits and the rest at lo_bits, both with
+ * the KIVI group quantizer.  The two token sets are position lists shared
+ * by the H heads of a sequence; each set is quantized as its own tensor of
+ * the listed rows, so a key group is `group` consecutive tokens of a set.
+ *
+ * Layout: x and out [B*H, S, D] as for KIVI-Sink; a list is int32 [B, n]
+ * positions in [0, S), distinct within a sequence (ascending, as
+ * kivi_partition_top writes them, keeps a key group's tokens in order); a
+ * set's codes [B*H, n, D*bits/8], key params [B*H, ceil(n/group), D],
+ * value params [B*H, n, ceil(D/group)].  A position outside [0, S) is read
+ * clamped into range by the quantizers (its results are unspecified) and
+ * is never written by the dequantizers.
+ * Rules (else nothing is launched): bits in {1, 2, 4, 8} (KIVI_ERR_BITS);
+ * key group in [1, 32], value group 8, 16 or 32 * 2^k (KIVI_ERR_GROUP);
+ * B, H, S >= 1, D in {8, 16, 32, 64, 128, 256}, 0 <= n <= S, B*H*n < 2^31,
+ * B*H*S*D < 2^40 (KIVI_ERR_SHAPE); dtype (KIVI_ERR_DTYPE); non-NULL
+ * (KIVI_ERR_NULL) and 16-byte aligned pointers, 4-byte for lists
+ * (KIVI_ERR_ALIGN).  n == 0 launches nothing.  One kernel per call.
+ */
+
+/* pos_hi [B, n_hi] gets the n_hi first positions of each sequence in the
+ * order (score descending, position ascending), listed in ascending
+ * position; pos_lo [B, S - n_hi] the other positions, ascending.  score is
+ * fp32 [B, S] (NaN scores: unspecified).  0 <= n_hi <= S < 2^31, B >= 1;
+ * pos_hi may be NULL when n_hi == 0 and pos_lo when n_hi == S. */
+kivi_status kivi_partition_top(const float* score, int64_t B, int64_t S,
+                               int64_t n_hi, int32_t* pos_hi, int32_t* pos_lo,
+                               hipStream_t stream);
+
+/* Quantize the listed rows as one [B*H, n, D] tensor: keys per channel over
+ * groups of `group` consecutive listed tokens, values per token. */
+kivi_status kivi_quant_keys_rows(const void* k, kivi_dtype dt, int64_t B,
+                                 int64_t H, int64_t S, int64_t D, int bits,
+                                 int64_t group, const int32_t* pos, int64_t n,
+                                 uint8_t* codes, float* scale, float* zero,
+                                 hipStream_t stream);
+kivi_status kivi_quant_values_rows(const void* v, kivi_dtype dt, int64_t B,
+                                   int64_t H, int64_t S, int64_t D, int bits,
+                                   int64_t group, const int32_t* pos,
+                                   int64_t n, uint8_t* codes, float* scale,
+                                   float* zero, hipStream_t stream);
+
+/* Dequantize a set and write each row j of head bh to
+ * out[bh, pos[bh / H, j], :]; rows of out not listed are untouched. */
+kivi_status kivi_dequant_keys_rows(const uint8_t* codes, const float* scale,
+                                   const float* zero, int64_t B, int64_t H,
+                                   int64_t S, int64_t D, int bits,
+                                   int64_t group, const int32_t* pos,
+                                   int64_t n, kivi_dtype out_dt, void* out,
+                                   hipStream_t stream);
+kivi_status kivi_dequant_values_rows(const uint8_t* codes, const float* scale,
+                                     const float* zero, int64_t B, int64_t H,
+                                     int64_t S, int64_t D, int bits,
+                                     int64_t group, const int32_t* pos,
+                                     int64_t n, kivi_dtype out_dt, void* out,
+                                     hipStream_t stream);
 
 /*
  * Profiling aid: the next kernel that a kivi_* call made by this thread

@@ -27,6 +27,10 @@ Functions (same names as the C ABI):
     kivi_sink_restore
         KIVI-Sink: the highest key-norm tokens kept in 16-bit form and left
         out of the key groups' min/max
+    kivi_key_scores, kivi_partition_top, kivi_quant_{keys,values}_rows,
+    kivi_dequant_{keys,values}_rows
+        per-token mixed precision: the highest key-norm tokens at hi_bits,
+        the rest at lo_bits, each set quantized as its own tensor
 Tensors are [BH, S, D] (or [B, H, S, D], flattened to BH = B*H), contiguous,
 float16 or bfloat16; codes are uint8 [..., S, D*bits/8]; key params are
 float32 [..., ceil(S/group), D]; value params float32 [..., S, ceil(D/group)].
@@ -96,6 +100,17 @@ def _load():
     L.kivi_sink_restore.argtypes = copy
     for name in ("kivi_sink_select", "kivi_quant_keys_sink",
                  "kivi_sink_gather", "kivi_sink_restore"):
+        getattr(L, name).restype = I
+    L.kivi_partition_top.argtypes = [P, I64, I64, I64, P, P, P]
+    qrows = [P, I, I64, I64, I64, I64, I, I64, P, I64, P, P, P, P]
+    L.kivi_quant_keys_rows.argtypes = qrows
+    L.kivi_quant_values_rows.argtypes = qrows
+    drows = [P, P, P, I64, I64, I64, I64, I, I64, P, I64, I, P, P]
+    L.kivi_dequant_keys_rows.argtypes = drows
+    L.kivi_dequant_values_rows.argtypes = drows
+    for name in ("kivi_partition_top", "kivi_quant_keys_rows",
+                 "kivi_quant_values_rows", "kivi_dequant_keys_rows",
+                 "kivi_dequant_values_rows"):
         getattr(L, name).restype = I
     L.kivi_status_string.argtypes = [I]
     L.kivi_status_string.restype = ctypes.c_char_p
@@ -362,6 +377,97 @@ def kivi_sink_restore(x_sink, idx, out, H=None, stream=None):
                                   _ptr(out), _stream(out.device, stream))
     _check(st, "kivi_sink_restore")
     return out
+
+
+# --------------------------------------------------------------------------
+# per-token mixed precision
+# --------------------------------------------------------------------------
+
+def kivi_key_scores(k, H=None, score=None, stream=None):
+    """Mean key L2 norm over the heads of each sequence, float32 [B, S]
+    (kivi_sink_select with n_sink = 0)."""
+    B, H, S, D = _bhsd(k, H)
+    _, score = kivi_sink_select(k, 0, H=H, score=score, stream=stream)
+    return score
+
+
+def kivi_partition_top(score, n_hi, pos_hi=None, pos_lo=None, stream=None):
+    """score float32 [B, S] -> (pos_hi int32 [B, n_hi], pos_lo [B, S - n_hi]):
+    the n_hi highest scores' positions and the rest, each ascending."""
+    if score.dtype != torch.float32 or score.dim() != 2 or not score.is_contiguous():
+        raise ValueError("score must be a contiguous float32 [B, S] tensor")
+    B, S = score.shape
+    if pos_hi is None:
+        pos_hi = torch.empty((B, max(n_hi, 0)), dtype=torch.int32, device=score.device)
+    if pos_lo is None:
+        pos_lo = torch.empty((B, max(S - n_hi, 0)), dtype=torch.int32,
+                             device=score.device)
+    st = _lib().kivi_partition_top(_ptr(score), B, S, n_hi, _ptr(pos_hi),
+                                   _ptr(pos_lo), _stream(score.device, stream))
+    _check(st, "kivi_partition_top")
+    return pos_hi, pos_lo
+
+
+def _quant_rows(name, keys, x, pos, bits, group, H, codes, scale, zero,
+                stream):
+    B, H, S, D = _bhsd(x, H)
+    n = _idx_arg(pos)
+    lead = (B, H) if x.dim() == 4 else (B * H,)
+    if codes is None:
+        codes = torch.empty(lead + (n, D * bits // 8), dtype=torch.uint8,
+                            device=x.device)
+    pshape = lead + ((_ngroups(n, max(group, 1)), D) if keys
+                     else (n, _ngroups(D, max(group, 1))))
+    if scale is None:
+        scale = torch.empty(pshape, dtype=torch.float32, device=x.device)
+    if zero is None:
+        zero = torch.empty(pshape, dtype=torch.float32, device=x.device)
+    st = getattr(_lib(), name)(_ptr(x), _dtype_code(x.dtype), B, H, S, D, bits,
+                               group, _ptr(pos), n, _ptr(codes), _ptr(scale),
+                               _ptr(zero), _stream(x.device, stream))
+    _check(st, name)
+    return codes, scale, zero
+
+
+def kivi_quant_keys_rows(k, pos, bits=2, group=32, H=None, codes=None,
+                         scale=None, zero=None, stream=None):
+    """Per-channel key quantization of the listed tokens pos [B, n] as one
+    tensor -> (codes [.., n, D*bits/8], scale, zero [.., ceil(n/group), D])."""
+    return _quant_rows("kivi_quant_keys_rows", True, k, pos, bits, group, H,
+                       codes, scale, zero, stream)
+
+
+def kivi_quant_values_rows(v, pos, bits=2, group=32, H=None, codes=None,
+                           scale=None, zero=None, stream=None):
+    """Per-token value quantization of the listed tokens -> (codes, scale,
+    zero [.., n, ceil(D/group)])."""
+    return _quant_rows("kivi_quant_values_rows", False, v, pos, bits, group, H,
+                       codes, scale, zero, stream)
+
+
+def _dequant_rows(name, codes, scale, zero, pos, out, bits, group, H, stream):
+    B, H, S, D = _bhsd(out, H)
+    n = _idx_arg(pos)
+    st = getattr(_lib(), name)(_ptr(codes), _ptr(scale), _ptr(zero), B, H, S,
+                               D, bits, group, _ptr(pos), n,
+                               _dtype_code(out.dtype), _ptr(out),
+                               _stream(out.device, stream))
+    _check(st, name)
+    return out
+
+
+def kivi_dequant_keys_rows(codes, scale, zero, pos, out, bits=2, group=32,
+                           H=None, stream=None):
+    """Dequantize a listed key set into its rows of out [B, H, S, D]."""
+    return _dequant_rows("kivi_dequant_keys_rows", codes, scale, zero, pos,
+                         out, bits, group, H, stream)
+
+
+def kivi_dequant_values_rows(codes, scale, zero, pos, out, bits=2, group=32,
+                             H=None, stream=None):
+    """Dequantize a listed value set into its rows of out [B, H, S, D]."""
+    return _dequant_rows("kivi_dequant_values_rows", codes, scale, zero, pos,
+                         out, bits, group, H, stream)
 
 
 class _Cache(ctypes.Structure):

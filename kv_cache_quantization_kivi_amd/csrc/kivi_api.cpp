@@ -118,6 +118,36 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
     return !__builtin_mul_overflow(a, b, out);
 }
 
+// Value groups the register-resident value kernel handles: 8 or 16
+// channels, or 32 * 2^k (whole lanes of 32 channels combined by butterflies).
+bool value_group_ok(int64_t g) {
+    if (g == 8 || g == 16) return true;
+    if (g < 32 || g % 32 != 0) return false;
+    const int64_t m = g / 32;
+    return (m & (m - 1)) == 0;
+}
+
+bool pow2_d(int64_t D) {
+    return D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256;
+}
+
+// Rules of the listed-set entry points (include/kivi.h).
+kivi_status check_list(int64_t B, int64_t H, int64_t S, int64_t D, int bits,
+                       int64_t group, int64_t n, bool keys) {
+    if (!bits_ok(bits)) return KIVI_ERR_BITS;
+    if (keys ? (group < 1 || group > 32) : !value_group_ok(group))
+        return KIVI_ERR_GROUP;
+    if (B < 1 || H < 1 || S < 1 || !pow2_d(D) || n < 0 || n > S)
+        return KIVI_ERR_SHAPE;
+    int64_t m = 0;
+    if (!mul_ok(B, H, &m) || !mul_ok(m, n, &m) || m >= (1ll << 31))
+        return KIVI_ERR_SHAPE;
+    if (!mul_ok(B, H, &m) || !mul_ok(m, S, &m) || !mul_ok(m, D, &m) ||
+        m >= (1ll << 40) || S >= (1ll << 31))
+        return KIVI_ERR_SHAPE;
+    return KIVI_OK;
+}
+
 // Every rule of kivi_cache_append's contract (include/kivi.h), checked
 // before anything is enqueued.
 kivi_status check_cache(const kivi_cache* c, const void* k_new,
@@ -125,8 +155,7 @@ kivi_status check_cache(const kivi_cache* c, const void* k_new,
     if (c == nullptr) return KIVI_ERR_NULL;
     if (!bits_ok(c->bits)) return KIVI_ERR_BITS;
     if (c->G_k < 1 || c->G_k > 32) return KIVI_ERR_GROUP;
-    if (!(c->G_v == 8 || c->G_v == 16 || (c->G_v >= 32 && c->G_v % 32 == 0)))
-        return KIVI_ERR_GROUP;
+    if (!value_group_ok(c->G_v)) return KIVI_ERR_GROUP;
     if (!dtype_ok(c->dtype)) return KIVI_ERR_DTYPE;
     const int64_t D = c->D;
     if (!(D == 8 || D == 16 || D == 32 || D == 64 || D == 128 || D == 256))
@@ -199,9 +228,99 @@ kivi_status sink_copy(bool gather, const void* src, int64_t B, int64_t H,
                                            n_sink, stream));
 }
 
+kivi_status quant_rows(bool keys, const void* x, kivi_dtype dt, int64_t B,
+                       int64_t H, int64_t S, int64_t D, int bits,
+                       int64_t group, const int32_t* pos, int64_t n,
+                       uint8_t* codes, float* scale, float* zero,
+                       hipStream_t stream) {
+    kivi_status st = check_list(B, H, S, D, bits, group, n, keys);
+    if (st != KIVI_OK) return st;
+    if (!dtype_ok(dt)) return KIVI_ERR_DTYPE;
+    if (n == 0) return KIVI_OK;
+    if (!x || !pos || !codes || !scale || !zero) return KIVI_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) ||
+        !aligned16(zero) || !aligned4(pos))
+        return KIVI_ERR_ALIGN;
+    kivi::ListJob j{x, (int)dt, B, H, S, D, bits, group, pos, n, codes, scale,
+                    zero, stream};
+    return launched(keys ? kivi::launch_list_quant_keys(j)
+                         : kivi::launch_list_quant_values(j));
+}
+
+kivi_status dequant_rows(bool keys, const uint8_t* codes, const float* scale,
+                         const float* zero, int64_t B, int64_t H, int64_t S,
+                         int64_t D, int bits, int64_t group,
+                         const int32_t* pos, int64_t n, kivi_dtype out_dt,
+                         void* out, hipStream_t stream) {
+    kivi_status st = check_list(B, H, S, D, bits, group, n, keys);
+    if (st != KIVI_OK) return st;
+    if (!dtype_ok(out_dt)) return KIVI_ERR_DTYPE;
+    if (n == 0) return KIVI_OK;
+    if (!codes || !scale || !zero || !pos || !out) return KIVI_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(scale) || !aligned16(zero) ||
+        !aligned16(out) || !aligned4(pos))
+        return KIVI_ERR_ALIGN;
+    kivi::ListJob j{nullptr, (int)out_dt, B, H, S, D, bits, group, pos, n,
+                    const_cast<uint8_t*>(codes), const_cast<float*>(scale),
+                    const_cast<float*>(zero), stream};
+    return launched(kivi::launch_list_dequant(j, keys, out));
+}
+
 }  // namespace
 
 extern "C" {
+
+kivi_status kivi_partition_top(const float* score, int64_t B, int64_t S,
+                               int64_t n_hi, int32_t* pos_hi, int32_t* pos_lo,
+                               hipStream_t stream) {
+    if (B < 1 || S < 1 || S >= (1ll << 31) || B >= (1ll << 31) || n_hi < 0 ||
+        n_hi > S)
+        return KIVI_ERR_SHAPE;
+    if (!score || (n_hi > 0 && !pos_hi) || (n_hi < S && !pos_lo))
+        return KIVI_ERR_NULL;
+    if (!aligned4(score) || !aligned4(pos_hi) || !aligned4(pos_lo))
+        return KIVI_ERR_ALIGN;
+    return launched(kivi::launch_partition_top(score, B, S, n_hi, pos_hi,
+                                               pos_lo, stream));
+}
+
+kivi_status kivi_quant_keys_rows(const void* k, kivi_dtype dt, int64_t B,
+                                 int64_t H, int64_t S, int64_t D, int bits,
+                                 int64_t group, const int32_t* pos, int64_t n,
+                                 uint8_t* codes, float* scale, float* zero,
+                                 hipStream_t stream) {
+    return quant_rows(true, k, dt, B, H, S, D, bits, group, pos, n, codes,
+                      scale, zero, stream);
+}
+
+kivi_status kivi_quant_values_rows(const void* v, kivi_dtype dt, int64_t B,
+                                   int64_t H, int64_t S, int64_t D, int bits,
+                                   int64_t group, const int32_t* pos,
+                                   int64_t n, uint8_t* codes, float* scale,
+                                   float* zero, hipStream_t stream) {
+    return quant_rows(false, v, dt, B, H, S, D, bits, group, pos, n, codes,
+                      scale, zero, stream);
+}
+
+kivi_status kivi_dequant_keys_rows(const uint8_t* codes, const float* scale,
+                                   const float* zero, int64_t B, int64_t H,
+                                   int64_t S, int64_t D, int bits,
+                                   int64_t group, const int32_t* pos,
+                                   int64_t n, kivi_dtype out_dt, void* out,
+                                   hipStream_t stream) {
+    return dequant_rows(true, codes, scale, zero, B, H, S, D, bits, group, pos,
+                        n, out_dt, out, stream);
+}
+
+kivi_status kivi_dequant_values_rows(const uint8_t* codes, const float* scale,
+                                     const float* zero, int64_t B, int64_t H,
+                                     int64_t S, int64_t D, int bits,
+                                     int64_t group, const int32_t* pos,
+                                     int64_t n, kivi_dtype out_dt, void* out,
+                                     hipStream_t stream) {
+    return dequant_rows(false, codes, scale, zero, B, H, S, D, bits, group,
+                        pos, n, out_dt, out, stream);
+}
 
 kivi_status kivi_sink_select(const void* k, kivi_dtype dt, int64_t B,
                              int64_t H, int64_t S, int64_t D, int64_t n_sink,

@@ -135,6 +135,36 @@ hipError_t launch_sink_copy(bool gather, const void* src, void* dst, int64_t B,
                             const int32_t* idx, int64_t n_sink,
                             hipStream_t stream);
 
+// Listed token sets (per-token mixed precision, rows.hip and the list
+// launchers of the quantizers).  Keys/values [B*H, S, D]; a list is
+// [B, n] positions shared by the H heads of a sequence; outputs are the
+// set's rows [B*H, n, ...].  The caller has checked D / 8 a power of two
+// <= 32, 1 <= n <= S, B*H*n < 2^31, key groups <= 32 and value groups of
+// 8, 16 or a multiple of 32.
+struct ListJob {
+    const void* x;        // quantize: [B*H, S, D] input
+    int dtype;
+    int64_t B, H, S, D;
+    int bits;
+    int64_t group;
+    const int32_t* pos;
+    int64_t n;
+    uint8_t* codes;       // [B*H, n, D*bits/8]
+    float* scale;
+    float* zero;
+    hipStream_t stream;
+};
+hipError_t launch_list_quant_keys(const ListJob& j);
+hipError_t launch_list_quant_values(const ListJob& j);
+// Dequantize a set and write each row to its position of out [B*H, S, D]
+// (rows listed outside [0, S) are not written).
+hipError_t launch_list_dequant(const ListJob& j, bool keys, void* out);
+// pos_hi [B, n_hi] and pos_lo [B, S - n_hi], each ascending: the n_hi first
+// positions in the order (score descending, position ascending) and the rest.
+hipError_t launch_partition_top(const float* score, int64_t B, int64_t S,
+                                int64_t n_hi, int32_t* pos_hi, int32_t* pos_lo,
+                                hipStream_t stream);
+
 hipError_t launch_quant_keys(const QuantJob& j);
 hipError_t launch_quant_values(const QuantJob& j);
 hipError_t launch_dequant_keys(const DequantJob& j);

@@ -1,11 +1,14 @@
 // Where the quantizers find token rows and where they put a token's
-// outputs.  Two layouts share the kernels:
+// outputs.  Three layouts share the kernels:
 //   DenseRows - one [BH, S, D] tensor, outputs at the same (bh, token);
 //   CacheRows - a flush of tokens [Q, Q + F) of a residual-window cache:
 //               token s < T is in its ring slot s % ring_len of
 //               [BH, ring_len, D], token s >= T is row s - T of the appended
 //               [BH, n_in, D]; outputs go to the cache's compressed store at
-//               token s of [BH, S_max, ...] (key groups counted from 0).
+//               token s of [BH, S_max, ...] (key groups counted from 0);
+//   ListRows  - a listed token set: row j of head bh is token
+//               pos[bh / H][j] of [BH, S, D] (the H heads of a sequence share
+//               one list); outputs are the set's own rows [BH, n, ...].
 // Token indices are 32-bit: the launchers only use these layouts for
 // tensors of fewer than 2^31 tokens per bh.
 #pragma once
@@ -89,6 +92,49 @@ struct CacheRows {
         const uint32_t bh = (uint32_t)r / (uint32_t)F;
         return (int64_t)bh * S_max + Q + ((uint32_t)r - bh * (uint32_t)F);
     }
+};
+
+// Rows of one key tile of a listed set: row t is token pos[t] of the bh's
+// [S, D] rows.  A position outside [0, S) is clamped, so a bad list reads
+// in bounds (its results are unspecified).
+struct ListTile {
+    const uint16_t* x;     // the bh's token 0
+    const int32_t* pos;    // the tile's first list entry
+    int32_t S;
+    __device__ const uint16_t* row(int32_t t, int64_t D) const {
+        const int32_t p = min(max(pos[t], 0), S - 1);
+        return x + (int64_t)p * D;
+    }
+};
+
+struct ListRows {
+    const uint16_t* x;     // [BH, S, D]
+    const int32_t* pos;    // [BH / H, n]
+    int32_t S, n, H;
+    uint32_t NG;           // key groups of the set per bh
+    int32_t G;
+
+    __device__ int32_t first(uint32_t g) const { return (int32_t)g * G; }
+    __device__ int32_t count(int32_t s0) const { return min(G, n - s0); }
+    __device__ ListTile tile(uint32_t bh, int32_t s0, int64_t D) const {
+        return ListTile{x + (int64_t)bh * S * D,
+                        pos + (int64_t)(bh / (uint32_t)H) * n + s0, S};
+    }
+    __device__ int64_t out_row(uint32_t bh, int32_t s) const {
+        return (int64_t)bh * n + s;
+    }
+    __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
+        return (int64_t)bh * NG + g;
+    }
+    // value rows: row r of the flattened [BH * n] set rows (fewer than 2^31)
+    static constexpr bool kContiguous = false;
+    __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
+        const uint32_t bh = (uint32_t)r / (uint32_t)n;
+        const int32_t j = (int32_t)((uint32_t)r - bh * (uint32_t)n);
+        const int32_t p = min(max(pos[(int64_t)(bh / (uint32_t)H) * n + j], 0), S - 1);
+        return x + ((int64_t)bh * S + p) * D;
+    }
+    __device__ int64_t vout(int64_t r) const { return r; }
 };
 
 }  // namespace kivi

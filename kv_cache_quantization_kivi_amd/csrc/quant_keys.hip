@@ -224,7 +224,7 @@ __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
     }
 }
 
-// IO: the row layout (DenseRows or CacheRows, kivi_rows.h); NG here is the
+// IO: the row layout (DenseRows, CacheRows or ListRows, kivi_rows.h); NG here is the
 // number of groups per bh that this launch quantizes.
 template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV,
           typename IO>
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     const int32_t nt = io.count(s0);
     const int64_t D = (int64_t)D8 * 8;
 
-    const TileRows rows = io.tile(bh, s0, D);
+    const auto rows = io.tile(bh, s0, D);
     uint4 v[TPL];
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
@@ -423,6 +423,53 @@ static hipError_t launch_cache_keys_dt(const CacheFlushJob& j) {
         case 4: return launch_cache_keys_bits<DT, 4>(j);
         default: return launch_cache_keys_bits<DT, 8>(j);
     }
+}
+
+template <int DT, int BITS, int GMAX, int SPLIT>
+static hipError_t launch_list_keys_t(const ListJob& j) {
+    constexpr int TPL = GMAX / SPLIT;
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t NG = (uint32_t)((j.n + j.group - 1) / j.group);
+    const uint64_t n_lanes = (uint64_t)j.B * j.H * NG * D8 * SPLIT;
+    const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
+    const ListRows io{static_cast<const uint16_t*>(j.x), j.pos, (int32_t)j.S,
+                      (int32_t)j.n, (int32_t)j.H, NG, (int32_t)j.group};
+    return launch_kernel(
+        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, true, false, true,
+                                 ListRows>),
+        dim3(blocks), dim3(64), 0, j.stream, io, (uint32_t)n_lanes, D8, NG,
+        j.codes, j.scale, j.zero, (uint16_t*)nullptr);
+}
+
+template <int DT, int BITS, int GMAX>
+static hipError_t launch_list_keys_gmax(const ListJob& j) {
+    const uint64_t D8 = (uint64_t)(j.D / 8);
+    const uint64_t items = (uint64_t)j.B * j.H * ((j.n + j.group - 1) / j.group) * D8;
+    if (items < kKeySplitBelow && 64 % (D8 * 4) == 0)
+        return launch_list_keys_t<DT, BITS, GMAX, 4>(j);
+    return launch_list_keys_t<DT, BITS, GMAX, 2>(j);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_list_keys_bits(const ListJob& j) {
+    if (j.group <= 8) return launch_list_keys_gmax<DT, BITS, 8>(j);
+    if (j.group <= 16) return launch_list_keys_gmax<DT, BITS, 16>(j);
+    return launch_list_keys_gmax<DT, BITS, 32>(j);
+}
+
+template <int DT>
+static hipError_t launch_list_keys_dt(const ListJob& j) {
+    switch (j.bits) {
+        case 1: return launch_list_keys_bits<DT, 1>(j);
+        case 2: return launch_list_keys_bits<DT, 2>(j);
+        case 4: return launch_list_keys_bits<DT, 4>(j);
+        default: return launch_list_keys_bits<DT, 8>(j);
+    }
+}
+
+hipError_t launch_list_quant_keys(const ListJob& j) {
+    return j.dtype == DT_F16 ? launch_list_keys_dt<DT_F16>(j)
+                             : launch_list_keys_dt<DT_BF16>(j);
 }
 
 // The caller guarantees: D / 8 a power of two <= 32, G_k <= 32, F a

@@ -333,6 +333,48 @@ static hipError_t launch_cache_values_dt(const CacheFlushJob& j) {
     }
 }
 
+template <int DT, int BITS, int GPL>
+static hipError_t launch_list_values_t(const ListJob& j) {
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t gl = GPL == 1 ? log2_ceil((uint64_t)(j.group / 32)) : 0;
+    const uint32_t red = 1u << (gl < lp ? gl : lp);
+    const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
+    const int64_t n_rows = j.B * j.H * j.n;
+    const uint64_t lanes = (uint64_t)n_rows << lp;
+    const uint32_t blocks = (uint32_t)((lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const ListRows io{static_cast<const uint16_t*>(j.x), j.pos, (int32_t)j.S,
+                      (int32_t)j.n, (int32_t)j.H, 0u, 1};
+    return launch_kernel(
+        (quant_values_kernel<DT, BITS, GPL, true, false, ListRows>),
+        dim3(blocks), dim3(256), 0, j.stream, io, n_rows, D8, lp, red, gl, NGD,
+        vec, (int32_t)0, j.codes, j.scale, j.zero, (uint16_t*)nullptr);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_list_values_bits(const ListJob& j) {
+    if (j.group == 8) return launch_list_values_t<DT, BITS, 4>(j);
+    if (j.group == 16) return launch_list_values_t<DT, BITS, 2>(j);
+    return launch_list_values_t<DT, BITS, 1>(j);
+}
+
+template <int DT>
+static hipError_t launch_list_values_dt(const ListJob& j) {
+    switch (j.bits) {
+        case 1: return launch_list_values_bits<DT, 1>(j);
+        case 2: return launch_list_values_bits<DT, 2>(j);
+        case 4: return launch_list_values_bits<DT, 4>(j);
+        default: return launch_list_values_bits<DT, 8>(j);
+    }
+}
+
+hipError_t launch_list_quant_values(const ListJob& j) {
+    return j.dtype == DT_F16 ? launch_list_values_dt<DT_F16>(j)
+                             : launch_list_values_dt<DT_BF16>(j);
+}
+
 // The caller guarantees: D / 8 a power of two <= 32 (so D <= 256), a value
 // group of 8, 16 or a multiple of 32, and fewer than 2^31 rows.
 hipError_t launch_cache_flush_values(const CacheFlushJob& j) {

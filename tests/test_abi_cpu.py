@@ -198,6 +198,8 @@ def test_cache_append_rejects_before_any_launch(K):
     assert call(cache(G_k=0)) == GROUP
     assert call(cache(G_k=33, ring=66)) == GROUP
     assert call(cache(G_v=24)) == GROUP
+    assert call(cache(G_v=96)) == GROUP             # not 32 * 2^k
+    assert call(cache(G_v=64), n=0) == OK
     assert call(cache(dtype=2)) == DTYPE
     assert call(cache(D=96)) == SHAPE
     assert call(cache(D=512)) == SHAPE
@@ -260,3 +262,46 @@ def test_sink_entry_points_reject_before_any_launch(K):
         assert fn(k, 2, 4, 64, 128, None, 5, out, None) == 1
         assert fn(k, 2, 4, 64, 128, idx, 5, P(0x4008), None) == 6
         assert fn(None, 2, 4, 64, 128, idx, 0, None, None) == 0  # nothing to do
+
+
+def test_mixed_precision_entry_points_reject_before_any_launch(K):
+    """Listed-set rules (include/kivi.h); fake pointers, never dereferenced."""
+    L = K.raw()
+    P = ctypes.c_void_p
+    x, pos, c, s, z = P(0x1000), P(0x2000), P(0x3000), P(0x4000), P(0x5000)
+    part = L.kivi_partition_top
+    assert part(s, 2, 100, 101, pos, pos, None) == 2          # n_hi > S
+    assert part(s, 2, 100, -1, pos, pos, None) == 2
+    assert part(s, 0, 100, 5, pos, pos, None) == 2
+    assert part(None, 2, 100, 5, pos, pos, None) == 1
+    assert part(s, 2, 100, 5, None, pos, None) == 1
+    assert part(s, 2, 100, 100, None, pos, None) == 1          # all hi needs pos_hi
+    assert part(s, 2, 100, 5, pos, P(0x2002), None) == 6
+
+    for name, keys in (("kivi_quant_keys_rows", True),
+                       ("kivi_quant_values_rows", False)):
+        fn = getattr(L, name)
+
+        def q(bits=2, G=32, D=128, n=40, S=64, dt=0, x=x, pos=pos, codes=c):
+            return fn(x, dt, 2, 4, S, D, bits, G, pos, n, codes, s, z, None)
+
+        assert q(bits=3) == 3
+        assert q(G=0) == 4
+        assert q(G=48) == 4 and q(G=96) == 4                    # not 32 * 2^k
+        if keys:
+            assert q(G=33) == 4 and q(G=5) != 4
+        else:
+            assert q(G=5) == 4 and q(G=64) != 4
+        assert q(D=48) == 2 and q(D=512) == 2
+        assert q(n=65) == 2 and q(n=-1) == 2
+        assert q(dt=3) == 5
+        assert q(x=None) == 1 and q(pos=None) == 1 and q(codes=None) == 1
+        assert q(x=P(0x1004)) == 6 and q(pos=P(0x2001)) == 6
+        assert q(n=0, x=None) == 0                              # nothing to do
+
+    for name in ("kivi_dequant_keys_rows", "kivi_dequant_values_rows"):
+        fn = getattr(L, name)
+        assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 65, 0, x, None) == 2
+        assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 0, None, None) == 1
+        assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 0, P(0x1008), None) == 6
+        assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 7, x, None) == 5

@@ -192,6 +192,49 @@ SINK_WORKLOADS = {
     ]
 }
 
+@dataclass(frozen=True)
+class MixedWorkload:
+    """Per-token mixed precision over a prompt: B sequences of H KV heads
+    ([B*H, S, D]); the floor(hi_fraction * S) tokens of highest key norm
+    per sequence at hi_bits, the rest at lo_bits."""
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: int
+    hi_bits: int
+    lo_bits: int
+    group_k: int
+    group_v: int
+    hi_fraction: float
+    seed: int
+    key_kind: str
+    value_kind: str
+    desc: str
+
+    @property
+    def n_hi(self):
+        return int(self.hi_fraction * self.S)
+
+    def tokens(self):
+        return Workload(self.name, self.B * self.H, self.S, self.D, self.dtype,
+                        self.lo_bits, self.group_k, self.group_v, self.seed,
+                        self.key_kind, self.value_kind, self.desc,
+                        heads=self.H)
+
+
+MIXED_WORKLOADS = {
+    w.name: w for w in [
+        MixedWorkload("mixed-prefill", 14, 8, 32768, 128, FP16, 4, 2, 32, 32,
+                      0.2, 10, "prefill", "normal05",
+                      "per-token mixed precision over a 32768-token prompt: "
+                      "14 layers x 8 KV heads, D=128, fp16; the 20% of tokens "
+                      "with the highest key norm at 4 bits, the rest at 2 "
+                      "bits, groups of 32"),
+    ]
+}
+
 PLANT_FACTOR = 6.0
 
 
