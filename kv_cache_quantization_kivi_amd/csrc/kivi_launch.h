@@ -130,6 +130,8 @@ hipError_t launch_sink_scores(const void* k, int dtype, int64_t B, int64_t H,
 hipError_t launch_sink_select(const float* score, int64_t B, int64_t S,
                               int64_t n_sink, int32_t* idx, hipStream_t stream);
 hipError_t launch_quant_keys_sink(const SinkQuantJob& j);
+// The same on the split key kernel (quant_keys.hip); D / 8 a power of two.
+hipError_t launch_split_quant_keys_sink(const SinkQuantJob& j);
 hipError_t launch_sink_copy(bool gather, const void* src, void* dst, int64_t B,
                             int64_t H, int64_t S, int64_t D,
                             const int32_t* idx, int64_t n_sink,

@@ -48,6 +48,9 @@ struct DenseRows {
     __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
         return (int64_t)bh * NG + g;
     }
+    // no sinks: every token takes part in its group's min/max
+    static constexpr bool kSinks = false;
+    __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     // value rows: row r of the flattened [BH * S] rows
     static constexpr bool kContiguous = true;
     __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
@@ -83,6 +86,8 @@ struct CacheRows {
     __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
         return (int64_t)bh * NG_out + (uint32_t)(Q / G) + g;
     }
+    static constexpr bool kSinks = false;
+    __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     static constexpr bool kContiguous = false;
     __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
         const uint32_t bh = (uint32_t)r / (uint32_t)F;
@@ -126,6 +131,8 @@ struct ListRows {
     __device__ int64_t out_group(uint32_t bh, uint32_t g) const {
         return (int64_t)bh * NG + g;
     }
+    static constexpr bool kSinks = false;
+    __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     // value rows: row r of the flattened [BH * n] set rows (fewer than 2^31)
     static constexpr bool kContiguous = false;
     __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
@@ -135,6 +142,25 @@ struct ListRows {
         return x + ((int64_t)bh * S + p) * D;
     }
     __device__ int64_t vout(int64_t r) const { return r; }
+};
+
+// KIVI-Sink: dense [BH, S, D] keys whose sinks (a list of n_sink positions
+// per sequence of H heads, [BH / H, n_sink]) take no part in their group's
+// min/max.  sink_mask(bh, s0, nt): bit t set when token s0 + t is a sink
+// (t < nt <= 32); positions outside [0, S) match nothing.
+struct SinkRows : DenseRows {
+    const int32_t* idx;
+    int32_t n_sink, H;
+    static constexpr bool kSinks = true;
+    __device__ uint32_t sink_mask(uint32_t bh, int32_t s0, int32_t nt) const {
+        const int32_t* l = idx + (int64_t)(bh / (uint32_t)H) * n_sink;
+        uint32_t m = 0u;
+        for (int32_t i = 0; i < n_sink; ++i) {
+            const int32_t t = l[i] - s0;
+            if ((uint32_t)t < (uint32_t)nt) m |= 1u << t;
+        }
+        return m;
+    }
 };
 
 }  // namespace kivi

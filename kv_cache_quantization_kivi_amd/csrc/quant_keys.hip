@@ -208,16 +208,25 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
 // aligned inside the wave, so they only ever meet each other.
 // Code and store a lane's first n tokens; token t's code row is at
 // dst + t * cstride bytes and its recon row at rdst + t * rstride elements.
-template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL>
+// With SINKS, bit t of `sinks` marks the lane's token t as a sink: code 0,
+// and its own row as the reconstruction.
+template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL, bool SINKS>
 __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
                                            const Params (&pk)[8], int32_t n,
                                            uint8_t* dst, int64_t cstride,
-                                           uint16_t* rdst, int64_t rstride) {
+                                           uint16_t* rdst, int64_t rstride,
+                                           uint32_t sinks) {
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
         if (t < n) {
             uint4 r;
-            const uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v[t], pk, &r);
+            uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v[t], pk, &r);
+            if constexpr (SINKS) {
+                if ((sinks >> t) & 1u) {
+                    q = 0;
+                    r = v[t];
+                }
+            }
             if constexpr (WQ) store_codes<BITS>(dst + t * cstride, q);
             if constexpr (WR) store16_nt(rdst + t * rstride, r);
         }
@@ -246,17 +255,35 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
 
     const auto rows = io.tile(bh, s0, D);
     uint4 v[TPL];
+    uint32_t lane_sinks = 0;   // bit t: this lane's token t is a sink
+    uint32_t group_sinks = 0;  // bit t: token s0 + t is a sink
+    if constexpr (IO::kSinks) group_sinks = io.sink_mask(bh, s0, nt);
 #pragma unroll
     for (int t = 0; t < TPL; ++t) {
         const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
                                    : (int32_t)part * TPL + t, nt - 1);
         v[t] = load16_nt(rows.row(tt, D) + (int64_t)c * 8);
+        if constexpr (IO::kSinks) lane_sinks |= ((group_sinks >> tt) & 1u) << t;
     }
 
+    // A sink takes no part in the min/max: it is replaced there by the
+    // group's first token that is not a sink (a duplicate changes neither).
+    uint4 fill = v[0];
+    bool no_tokens = false;    // every token of the group is a sink
+    if constexpr (IO::kSinks) {
+        const uint32_t live = ~group_sinks & (nt < 32 ? (1u << nt) - 1u : ~0u);
+        no_tokens = live == 0u;
+        if (lane_sinks != 0u && !no_tokens)
+            fill = load16_nt(rows.row(__builtin_ctz(live), D) + (int64_t)c * 8);
+    }
+    const auto tok = [&](int t) -> uint4 {
+        if constexpr (IO::kSinks) return ((lane_sinks >> t) & 1u) ? fill : v[t];
+        return v[t];
+    };
     MinMax8<DT> mm;
-    mm.init(v[0]);
+    mm.init(tok(0));
 #pragma unroll
-    for (int t = 1; t < TPL; ++t) mm.add(v[t]);
+    for (int t = 1; t < TPL; ++t) mm.add(tok(t));
 #pragma unroll
     for (int k = 1; k < SPLIT; k <<= 1) mm.combine_xor((int)D8 * k);
     float lo[8], hi[8];
@@ -266,7 +293,7 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     bool fast = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        pk[k] = make_params<BITS>(lo[k], hi[k]);
+        pk[k] = make_params<BITS>(no_tokens ? 0.0f : lo[k], no_tokens ? 0.0f : hi[k]);
         fast = fast && pk[k].fast;
     }
     if (!valid) return;
@@ -291,11 +318,11 @@ __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     uint8_t* dst = WQ ? codes + orow * row_bytes + (int64_t)c * BITS : nullptr;
     uint16_t* rdst = WR ? recon + orow * D + (int64_t)c * 8 : nullptr;
     if (fast)
-        emit_split<DT, BITS, WQ, WR, true, TPL>(v, pk, n, dst, step * row_bytes,
-                                                rdst, step * D);
+        emit_split<DT, BITS, WQ, WR, true, TPL, IO::kSinks>(
+            v, pk, n, dst, step * row_bytes, rdst, step * D, lane_sinks);
     else
-        emit_split<DT, BITS, WQ, WR, false, TPL>(v, pk, n, dst, step * row_bytes,
-                                                 rdst, step * D);
+        emit_split<DT, BITS, WQ, WR, false, TPL, IO::kSinks>(
+            v, pk, n, dst, step * row_bytes, rdst, step * D, lane_sinks);
 }
 
 // Lanes per group.  Below kKeySplitBelow (bh, group, chunk) items (a
@@ -465,6 +492,68 @@ static hipError_t launch_list_keys_dt(const ListJob& j) {
         case 4: return launch_list_keys_bits<DT, 4>(j);
         default: return launch_list_keys_bits<DT, 8>(j);
     }
+}
+
+template <int DT, int BITS, int GMAX, int SPLIT, bool WQ, bool WR>
+static hipError_t launch_sink_keys_t(const SinkQuantJob& j) {
+    constexpr int TPL = GMAX / SPLIT;
+    const uint32_t D8 = (uint32_t)(j.D / 8);
+    const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
+    const uint64_t n_lanes = (uint64_t)j.B * j.H * NG * D8 * SPLIT;
+    const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
+    SinkRows io{};
+    io.x = static_cast<const uint16_t*>(j.k);
+    io.S = (int32_t)j.S;
+    io.NG = NG;
+    io.G = (int32_t)j.group;
+    io.idx = j.idx;
+    io.n_sink = (int32_t)j.n_sink;
+    io.H = (int32_t)j.H;
+    return launch_kernel(
+        (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true, SinkRows>),
+        dim3(blocks), dim3(64), 0, j.stream, io, (uint32_t)n_lanes, D8, NG,
+        j.codes, j.scale, j.zero, static_cast<uint16_t*>(j.recon));
+}
+
+template <int DT, int BITS, int GMAX, int SPLIT>
+static hipError_t launch_sink_keys_mode(const SinkQuantJob& j) {
+    const bool wq = j.codes != nullptr, wr = j.recon != nullptr;
+    if (wq && wr) return launch_sink_keys_t<DT, BITS, GMAX, SPLIT, true, true>(j);
+    if (wq) return launch_sink_keys_t<DT, BITS, GMAX, SPLIT, true, false>(j);
+    return launch_sink_keys_t<DT, BITS, GMAX, SPLIT, false, true>(j);
+}
+
+template <int DT, int BITS, int GMAX>
+static hipError_t launch_sink_keys_gmax(const SinkQuantJob& j) {
+    const uint64_t D8 = (uint64_t)(j.D / 8);
+    const uint64_t items = (uint64_t)j.B * j.H * ((j.S + j.group - 1) / j.group) * D8;
+    if (items < kKeySplitBelow && 64 % (D8 * 4) == 0)
+        return launch_sink_keys_mode<DT, BITS, GMAX, 4>(j);
+    return launch_sink_keys_mode<DT, BITS, GMAX, 2>(j);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_sink_keys_bits(const SinkQuantJob& j) {
+    if (j.group <= 8) return launch_sink_keys_gmax<DT, BITS, 8>(j);
+    if (j.group <= 16) return launch_sink_keys_gmax<DT, BITS, 16>(j);
+    return launch_sink_keys_gmax<DT, BITS, 32>(j);
+}
+
+template <int DT>
+static hipError_t launch_sink_keys_dt(const SinkQuantJob& j) {
+    switch (j.bits) {
+        case 1: return launch_sink_keys_bits<DT, 1>(j);
+        case 2: return launch_sink_keys_bits<DT, 2>(j);
+        case 4: return launch_sink_keys_bits<DT, 4>(j);
+        default: return launch_sink_keys_bits<DT, 8>(j);
+    }
+}
+
+// KIVI-Sink keys on the split kernel; the caller guarantees D / 8 a power
+// of two <= 32, group <= 32 and fewer than 2^31 lanes.
+hipError_t launch_split_quant_keys_sink(const SinkQuantJob& j) {
+    return j.dtype == DT_F16 ? launch_sink_keys_dt<DT_F16>(j)
+                             : launch_sink_keys_dt<DT_BF16>(j);
 }
 
 hipError_t launch_list_quant_keys(const ListJob& j) {

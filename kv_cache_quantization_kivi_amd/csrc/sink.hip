@@ -6,9 +6,9 @@
 // neighbours' scale.
 //
 // Three steps, each one launch:
-//   scores  - one lane per (sequence b, token s) reads the token's key row in
-//             every head (16-byte loads of a whole row, consecutive lanes on
-//             consecutive rows) and forms the mean norm in a fixed order:
+//   scores  - one lane per (sequence b, token s) walks the token's key row
+//             in every head (rows staged through LDS by coalesced wave
+//             loads) and forms the mean norm in a fixed order:
 //             per head fma-accumulated squares in channel order, the
 //             correctly rounded square root, the head-order sum, one division
 //             by H;
@@ -31,25 +31,51 @@ namespace kivi {
 
 // ---- scores -------------------------------------------------------------
 
+// One wave per (sequence b, tile of 64 tokens).  The tile's rows of one
+// head are contiguous, so the wave reads them with fully coalesced 16-byte
+// loads (consecutive lanes on consecutive 16-byte pieces), parks them in
+// LDS, and each lane then walks its own token's row from LDS in channel
+// order.  The next head's rows are loaded into registers while the current
+// head is summed.  Rows are padded by 16 bytes in LDS, so the 16 lanes that
+// read at once hit 16 different 4-bank groups.
 template <int DT, int D8>
-__global__ __launch_bounds__(256) void sink_score_kernel(
-    const uint16_t* __restrict__ k, int32_t H, int32_t S, int64_t n_tok,
+__global__ __launch_bounds__(64) void sink_score_kernel(
+    const uint16_t* __restrict__ k, int32_t H, int32_t S, int32_t n_tiles,
     float* __restrict__ score) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // b * S + s
-    if (i >= n_tok) return;
-    const int64_t b = i / S, s = i - b * S;
+    constexpr int RS = D8 * 16 + 16;          // padded LDS row bytes
+    __shared__ __attribute__((aligned(16))) uint8_t rows_s[64 * RS];
+    const int32_t tile = (int32_t)(blockIdx.x % (uint32_t)n_tiles);
+    const int64_t b = blockIdx.x / (uint32_t)n_tiles;
+    const int32_t s0 = tile * 64;
+    const int32_t nv = min(64, S - s0);       // real tokens of the tile
+    const int lane = threadIdx.x;
     constexpr int D = D8 * 8;
+    uint4 pre[D8];                            // 64 * D8 pieces, D8 per lane
+    const auto load_head = [&](int32_t h) {
+        const uint16_t* base = k + ((b * H + h) * S + s0) * D;
+#pragma unroll
+        for (int q = 0; q < D8; ++q) {
+            const int piece = q * 64 + lane;
+            const int row = min(piece / D8, nv - 1);
+            pre[q] = load16_nt(base + row * D + (piece % D8) * 8);
+        }
+    };
+    load_head(0);
     float total = 0.0f;
     for (int32_t h = 0; h < H; ++h) {
-        const uint16_t* row = k + ((b * H + h) * S + s) * D;
-        uint4 x[D8];
 #pragma unroll
-        for (int c = 0; c < D8; ++c) x[c] = load16_nt(row + c * 8);
+        for (int q = 0; q < D8; ++q) {
+            const int piece = q * 64 + lane;
+            *reinterpret_cast<uint4*>(rows_s + (piece / D8) * RS + (piece % D8) * 16) = pre[q];
+        }
+        wave_lds_sync();
+        if (h + 1 < H) load_head(h + 1);
         float ss = 0.0f;
 #pragma unroll
         for (int c = 0; c < D8; ++c) {
+            const uint4 x = *reinterpret_cast<const uint4*>(rows_s + lane * RS + c * 16);
             uint32_t w[4];
-            words(x[c], w);
+            words(x, w);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = elem<DT>(w, e);
@@ -58,24 +84,26 @@ __global__ __launch_bounds__(256) void sink_score_kernel(
         }
         // correctly rounded (built with -fhip-fp32-correctly-rounded-divide-sqrt)
         total = total + __builtin_sqrtf(ss);
+        wave_lds_sync();                      // every lane has read its row
     }
-    score[i] = total / (float)H;
+    if (lane < nv) score[b * S + s0 + lane] = total / (float)H;
 }
 
 template <int DT>
 static hipError_t launch_scores_dt(const void* k, int64_t B, int64_t H,
                                    int64_t S, int64_t D, float* score,
                                    hipStream_t st) {
-    const int64_t n = B * S;
-    const dim3 grid((uint32_t)((n + 255) / 256)), block(256);
+    const int32_t n_tiles = (int32_t)((S + 63) / 64);
+    const dim3 grid((uint32_t)(B * n_tiles)), block(64);
     const uint16_t* x = static_cast<const uint16_t*>(k);
+    const int32_t h = (int32_t)H, s = (int32_t)S;
     switch (D) {
-        case 8: return launch_kernel(sink_score_kernel<DT, 1>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
-        case 16: return launch_kernel(sink_score_kernel<DT, 2>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
-        case 32: return launch_kernel(sink_score_kernel<DT, 4>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
-        case 64: return launch_kernel(sink_score_kernel<DT, 8>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
-        case 128: return launch_kernel(sink_score_kernel<DT, 16>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
-        default: return launch_kernel(sink_score_kernel<DT, 32>, grid, block, 0, st, x, (int32_t)H, (int32_t)S, n, score);
+        case 8: return launch_kernel(sink_score_kernel<DT, 1>, grid, block, 0, st, x, h, s, n_tiles, score);
+        case 16: return launch_kernel(sink_score_kernel<DT, 2>, grid, block, 0, st, x, h, s, n_tiles, score);
+        case 32: return launch_kernel(sink_score_kernel<DT, 4>, grid, block, 0, st, x, h, s, n_tiles, score);
+        case 64: return launch_kernel(sink_score_kernel<DT, 8>, grid, block, 0, st, x, h, s, n_tiles, score);
+        case 128: return launch_kernel(sink_score_kernel<DT, 16>, grid, block, 0, st, x, h, s, n_tiles, score);
+        default: return launch_kernel(sink_score_kernel<DT, 32>, grid, block, 0, st, x, h, s, n_tiles, score);
     }
 }
 
@@ -315,6 +343,13 @@ hipError_t launch_sink_select(const float* score, int64_t B, int64_t S,
 }
 
 hipError_t launch_quant_keys_sink(const SinkQuantJob& j) {
+    // Head dimensions whose 8-channel chunks tile a wave go to the split key
+    // kernel (two or four lanes per group, the plain quantizer's fast path);
+    // others to the one-lane kernel above.
+    const int64_t D8 = j.D / 8;
+    const int64_t lanes = j.B * j.H * ((j.S + j.group - 1) / j.group) * D8 * 4;
+    if ((D8 & (D8 - 1)) == 0 && D8 <= 32 && lanes < (1ll << 31))
+        return launch_split_quant_keys_sink(j);
     return j.dtype == DT_F16 ? launch_keys_sink_dt<DT_F16>(j)
                              : launch_keys_sink_dt<DT_BF16>(j);
 }
