@@ -157,37 +157,97 @@ __global__ __launch_bounds__(256) void list_dequant_keys_kernel(
     const uint8_t* src = codes + ((int64_t)bh * n + j0) * row_bytes + (int64_t)c * BITS;
     const int32_t* lp = pos + (int64_t)(bh / (uint32_t)H) * n + j0;
     uint16_t* dst = out + (int64_t)bh * S * D + (int64_t)c * 8;
-    for (int32_t t = 0; t < nt; ++t) {
-        const int32_t s = lp[t];
-        const uint4 r = dequant_chunk<DT, BITS>(load_codes<BITS>(src + t * row_bytes), sc, z);
-        if (s >= 0 && s < S) store16_nt(dst + (int64_t)s * D, r);
+    // tokens in batches of 8: every load of a batch is issued before its
+    // first store
+    for (int32_t t0 = 0; t0 < nt; t0 += 8) {
+        uint64_t q[8];
+        int32_t sp[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int32_t t = min(t0 + u, nt - 1);
+            q[u] = load_codes<BITS>(src + t * row_bytes);
+            sp[u] = lp[t];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int32_t s = sp[u];
+            if (t0 + u < nt && s >= 0 && s < S)
+                store16_nt(dst + (int64_t)s * D, dequant_chunk<DT, BITS>(q[u], sc, z));
+        }
     }
 }
 
-// Values: one lane per (row of the set, 8-channel chunk); a chunk lies in
-// one value group (groups are multiples of 8 channels).
-template <int DT, int BITS>
+// Values: one lane per (row of the set, CPL consecutive 8-channel chunks):
+// one CPL * BITS-byte code load and one (scale, zero) load per value group
+// it touches (groups are multiples of 8 channels).  The reconstruction goes
+// out through LDS: a wave's rows are parked there and stored with one lane
+// per 16-byte chunk, so each store instruction writes whole rows.
+constexpr int kLdvWaveRowsMax = 64;
+
+template <int DT, int BITS, int CPL, int D8>
 __global__ __launch_bounds__(256) void list_dequant_values_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-    const float* __restrict__ zero, uint64_t n_items, uint32_t D8,
-    uint32_t NGD, int32_t S, int32_t n, int32_t H, int32_t G,
-    const int32_t* __restrict__ pos, uint16_t* __restrict__ out) {
+    const float* __restrict__ zero, uint64_t n_items, uint32_t NGD, int32_t S,
+    int32_t n, int32_t H, int32_t G, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ out) {
+    constexpr int UNITS = D8 / CPL;                  // lanes per row
+    constexpr int WROWS = 64 / UNITS;                // rows per wave
+    constexpr int RS = D8 * 16 + 16;                 // padded LDS row bytes
+    constexpr int64_t D = D8 * 8;
+    __shared__ __attribute__((aligned(16))) uint8_t rec_s[4][WROWS * RS];
+    __shared__ int64_t row_s[4][WROWS];              // output row, or -1
+    const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
     const uint64_t gid = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-    if (gid >= n_items) return;
-    const uint32_t c = (uint32_t)(gid % D8);
-    const uint32_t r = (uint32_t)(gid / D8);          // bh * n + j
+    const bool valid = gid < n_items;
+    const uint64_t item = valid ? gid : n_items - 1u;
+    const uint32_t u = (uint32_t)(item % UNITS);
+    const uint32_t r = (uint32_t)(item / UNITS);     // bh * n + j
     const uint32_t bh = r / (uint32_t)n;
     const int32_t j = (int32_t)(r - bh * (uint32_t)n);
     const int32_t s = pos[(int64_t)(bh / (uint32_t)H) * n + j];
-    if (s < 0 || s >= S) return;
-    const int64_t D = (int64_t)D8 * 8;
-    const int64_t pi = (int64_t)r * NGD + (int64_t)(c * 8) / G;
-    const float sv = scale[pi], zv = zero[pi];
-    const float sc[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
-    const float z[8] = {zv, zv, zv, zv, zv, zv, zv, zv};
-    const uint64_t q = load_codes<BITS>(codes + (int64_t)r * D8 * BITS + (int64_t)c * BITS);
-    store16_nt(out + ((int64_t)bh * S + s) * D + (int64_t)c * 8,
-               dequant_chunk<DT, BITS>(q, sc, z));
+    const uint8_t* cp = codes + (int64_t)r * D8 * BITS + (int64_t)u * CPL * BITS;
+    uint64_t q[CPL];
+    if constexpr (CPL * BITS == 8) {
+        const uint2 wd = *reinterpret_cast<const uint2*>(cp);
+        const uint64_t all = (uint64_t)wd.x | ((uint64_t)wd.y << 32);
+        if constexpr (CPL == 1) {
+            q[0] = all;
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                q[i] = (all >> (i * 8 * BITS)) & ((1ull << (8 * BITS)) - 1ull);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) q[i] = load_codes<BITS>(cp + i * BITS);
+    }
+    const float* sr = scale + (int64_t)r * NGD;
+    const float* zr = zero + (int64_t)r * NGD;
+    // The LDS slot comes from the lane, not the item: a lane past the end
+    // mirrors the last item, but its slot (and the row index its wave row
+    // gets, -1) must still be its own, so that every wave row is written.
+    const uint32_t wrow = lane / UNITS, ul = lane % UNITS;
+    uint8_t* mine = rec_s[w] + wrow * RS + ul * CPL * 16;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int32_t gv = (int32_t)((u * CPL + i) * 8) / G;
+        const float sv = sr[gv], zv = zr[gv];
+        const float sc[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
+        const float z[8] = {zv, zv, zv, zv, zv, zv, zv, zv};
+        *reinterpret_cast<uint4*>(mine + i * 16) = dequant_chunk<DT, BITS>(q[i], sc, z);
+    }
+    if (ul == 0)
+        row_s[w][wrow] = (valid && s >= 0 && s < S) ? (int64_t)bh * S + s : -1;
+    wave_lds_sync();
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+        const uint32_t piece = k * 64u + lane;       // chunk of the wave's rows
+        const uint32_t pr = piece / D8, pc = piece % D8;
+        const int64_t orow = row_s[w][pr];
+        if (orow >= 0)
+            store16_nt(out + orow * D + pc * 8,
+                       *reinterpret_cast<const uint4*>(rec_s[w] + pr * RS + pc * 16));
+    }
 }
 
 template <int DT, int BITS>
@@ -204,12 +264,24 @@ static hipError_t launch_list_dq_t(const ListJob& j, bool keys, void* out) {
                              j.pos, o);
     }
     const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
-    const uint64_t n = (uint64_t)j.B * j.H * j.n * D8;
-    return launch_kernel((list_dequant_values_kernel<DT, BITS>),
-                         dim3((uint32_t)((n + 255u) / 256u)), dim3(256), 0,
-                         j.stream, j.codes, j.scale, j.zero, n, D8, NGD,
-                         (int32_t)j.S, (int32_t)j.n, (int32_t)j.H,
-                         (int32_t)j.group, j.pos, o);
+    const uint32_t cpl = D8 < 4 ? D8 : 4;              // D8 is a power of two
+    // whole waves of lanes: n_items rounded up to a multiple of 64 lanes is
+    // not needed, lanes past the end mirror the last item and store nothing
+    const uint64_t n = (uint64_t)j.B * j.H * j.n * (D8 / cpl);
+    const dim3 grid((uint32_t)((n + 255u) / 256u)), block(256);
+    const auto go = [&](auto kern) {
+        return launch_kernel(kern, grid, block, 0, j.stream, j.codes, j.scale,
+                             j.zero, n, NGD, (int32_t)j.S, (int32_t)j.n,
+                             (int32_t)j.H, (int32_t)j.group, j.pos, o);
+    };
+    switch (D8) {
+        case 1: return go(list_dequant_values_kernel<DT, BITS, 1, 1>);
+        case 2: return go(list_dequant_values_kernel<DT, BITS, 2, 2>);
+        case 4: return go(list_dequant_values_kernel<DT, BITS, 4, 4>);
+        case 8: return go(list_dequant_values_kernel<DT, BITS, 4, 8>);
+        case 16: return go(list_dequant_values_kernel<DT, BITS, 4, 16>);
+        default: return go(list_dequant_values_kernel<DT, BITS, 4, 32>);
+    }
 }
 
 template <int DT>
