@@ -23,26 +23,38 @@ namespace kivi {
 constexpr int kAttChunk = 128;   // tokens per block (one per thread)
 constexpr int kAttMaxGroups = kAttChunk / 8;   // key groups in a chunk (G_k >= 8)
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red) {
+// Max and sum over the block's two waves of N values at once (one pair of
+// barriers for all N); red holds 2 * N floats.
+template <int N>
+__device__ __forceinline__ void block_max_n(float (&v)[N], float* red) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v[j] = fmaxf(v[j], __shfl_xor(v[j], o));
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int j = 0; j < N; ++j) red[w * N + j] = v[j];
     __syncthreads();
-    v = fmaxf(red[0], red[1]);
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = fmaxf(red[j], red[N + j]);
     __syncthreads();
-    return v;
 }
 
-__device__ __forceinline__ float block_reduce_sum(float v, float* red) {
+template <int N>
+__device__ __forceinline__ void block_sum_n(float (&v)[N], float* red) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v[j] += __shfl_xor(v[j], o);
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int j = 0; j < N; ++j) red[w * N + j] = v[j];
     __syncthreads();
-    v = red[0] + red[1];
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] = red[j] + red[N + j];
     __syncthreads();
-    return v;
 }
 
 template <int DT>
@@ -71,7 +83,7 @@ __device__ __forceinline__ uint64_t row_chunk(const uint32_t* w, int c8) {
 }
 
 // D: head dimension (64 or 128); NQ: query heads per KV head rounded up to
-// 1, 2, 4 or 8 (rows past n_q are zeros and never stored).  One block of
+// 1, 2, 3, 4, 6 or 8 (rows past n_q are zeros and never stored).  One block of
 // kAttChunk threads per (chunk, bh); the caller guarantees D * BITS >= 128
 // (whole 16-byte code rows), G_k in {8, 16, 32} (chunks are group-aligned)
 // and n_q <= NQ.
@@ -95,7 +107,7 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     float* bias_s = kp_s + kQsRows * D;
     __shared__ __attribute__((aligned(16))) float p_s[NQ][kAttChunk];
     __shared__ __attribute__((aligned(16))) float acc_s[NQ][D];
-    __shared__ float red[2];
+    __shared__ float red[2 * NQ];
 
     const int chunk = blockIdx.x;
     const int bh = blockIdx.y;
@@ -212,16 +224,21 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
         }
     }
 
-    // ---- softmax partial of the chunk, per query head ----
+    // ---- softmax partial of the chunk, every query head at once ----
     float m[NQ], l[NQ];
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-        const float s = tid < nt ? sc[j] * a.sm_scale : -__builtin_huge_valf();
-        m[j] = block_reduce_max(s, red);
-        const float p = tid < nt ? __expf(s - m[j]) : 0.0f;
-        p_s[j][tid] = p;
-        l[j] = block_reduce_sum(p, red);
+        sc[j] = tid < nt ? sc[j] * a.sm_scale : -__builtin_huge_valf();
+        m[j] = sc[j];
     }
+    block_max_n<NQ>(m, red);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+        const float p = tid < nt ? __expf(sc[j] - m[j]) : 0.0f;
+        p_s[j][tid] = p;
+        l[j] = p;
+    }
+    block_sum_n<NQ>(l, red);
 
     // ---- partial outputs: thread (channel chunk c8, token part) reads its
     // tokens' value codes straight from memory (consecutive threads take
@@ -308,45 +325,48 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     }
 }
 
-// Merge the chunks of each bh: out = sum_c e^{m_c - M} o_c / sum_c e^{m_c - M} l_c
-// with M = max_c m_c.  One block per bh; M and L are block reductions over
-// the chunks, then each thread sums one channel (D = 64: two threads per
-// channel, each taking every other chunk).
-template <int DT>
-__global__ __launch_bounds__(128) void attend_merge_kernel(AttendArgs a) {
-    __shared__ float red[2];
-    __shared__ float half_s[64];
-    const int bh = blockIdx.x, tid = threadIdx.x;
-    const int D = a.D, nq = a.n_q, nc = a.n_chunks;
-    const int64_t cs = (int64_t)nq * att_slot(D);   // chunk stride
-    const int per = 128 / D, d = tid % D, part = tid / D;
-    for (int j = 0; j < nq; ++j) {
-        const float* w = a.work + (int64_t)bh * nc * cs + j * att_slot(D);
-        float mx = -__builtin_huge_valf();
-        for (int c = tid; c < nc; c += 128) mx = fmaxf(mx, w[c * cs]);
-        const float M = block_reduce_max(mx, red);
-        float ls = 0.0f;
-        for (int c = tid; c < nc; c += 128) ls += __expf(w[c * cs] - M) * w[c * cs + 1];
-        const float L = block_reduce_sum(ls, red);
-        float O = 0.0f;
+// Merge the chunks of each (bh, query head): out = sum_c e^{m_c - M} o_c /
+// sum_c e^{m_c - M} l_c with M = max_c m_c.  One wave per (bh, head), four
+// per block: the lanes take the chunks for M and the denominator (wave
+// reductions, no barrier), then the channels for the numerator.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
+                                                           int32_t n_pairs) {
+    const int32_t pair = (int32_t)blockIdx.x * 4 + (int32_t)(threadIdx.x >> 6);
+    if (pair >= n_pairs) return;                 // the whole wave
+    const int lane = threadIdx.x & 63;
+    const int nq = a.n_q, nc = a.n_chunks;
+    const int bh = pair / nq, j = pair - bh * nq;
+    const int64_t cs = (int64_t)nq * att_slot(D);        // chunk stride
+    const float* w = a.work + (int64_t)bh * nc * cs + (int64_t)j * att_slot(D);
+    float mx = -__builtin_huge_valf();
+    for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, w[c * cs]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    float ls = 0.0f;
+    for (int c = lane; c < nc; c += 64) ls += __expf(w[c * cs] - mx) * w[c * cs + 1];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
+    constexpr int PER = D / 64;                  // channels per lane
+    float O[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) O[i] = 0.0f;
 #pragma unroll 4
-        for (int c = part; c < nc; c += per)
-            O = __builtin_fmaf(__expf(w[c * cs] - M), w[c * cs + 2 + d], O);
-        if (per > 1) {
-            if (part == 1) half_s[d] = O;
-            __syncthreads();
-            if (part == 0) O += half_s[d];
-            __syncthreads();
-        }
-        if (part == 0) {
-            const float r = O / L;
-            uint16_t h;
-            if constexpr (DT == DT_F16)
-                h = __builtin_bit_cast(uint16_t, (_Float16)r);
-            else
-                h = __builtin_bit_cast(uint16_t, (__bf16)r);
-            a.out[((int64_t)bh * nq + j) * D + d] = h;
-        }
+    for (int c = 0; c < nc; ++c) {
+        const float e = __expf(w[c * cs] - mx);
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            O[i] = __builtin_fmaf(e, w[c * cs + 2 + lane + 64 * i], O[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const float r = O[i] / ls;
+        uint16_t h;
+        if constexpr (DT == DT_F16)
+            h = __builtin_bit_cast(uint16_t, (_Float16)r);
+        else
+            h = __builtin_bit_cast(uint16_t, (__bf16)r);
+        a.out[((int64_t)bh * nq + j) * D + lane + 64 * i] = h;
     }
 }
 
@@ -361,10 +381,15 @@ static hipError_t launch_partial(const AttendArgs& a, int64_t BH,
 template <int DT, int BITS, int D>
 static hipError_t launch_partial_nq(const AttendArgs& a, int64_t BH,
                                     hipStream_t stream) {
-    if (a.n_q <= 1) return launch_partial<DT, BITS, D, 1>(a, BH, stream);
-    if (a.n_q <= 2) return launch_partial<DT, BITS, D, 2>(a, BH, stream);
-    if (a.n_q <= 4) return launch_partial<DT, BITS, D, 4>(a, BH, stream);
-    return launch_partial<DT, BITS, D, 8>(a, BH, stream);
+    switch (a.n_q) {
+        case 1: return launch_partial<DT, BITS, D, 1>(a, BH, stream);
+        case 2: return launch_partial<DT, BITS, D, 2>(a, BH, stream);
+        case 3: return launch_partial<DT, BITS, D, 3>(a, BH, stream);
+        case 4: return launch_partial<DT, BITS, D, 4>(a, BH, stream);
+        case 5:
+        case 6: return launch_partial<DT, BITS, D, 6>(a, BH, stream);
+        default: return launch_partial<DT, BITS, D, 8>(a, BH, stream);
+    }
 }
 
 template <int DT, int BITS>
@@ -373,8 +398,11 @@ static hipError_t launch_attend_t(const AttendArgs& a, int64_t BH,
     hipError_t e = a.D == 64 ? launch_partial_nq<DT, BITS, 64>(a, BH, stream)
                              : launch_partial_nq<DT, BITS, 128>(a, BH, stream);
     if (e != hipSuccess) return e;
-    return launch_kernel((attend_merge_kernel<DT>), dim3((uint32_t)BH),
-                         dim3(128), 0, stream, a);
+    const int32_t pairs = (int32_t)(BH * a.n_q);
+    const dim3 grid((uint32_t)((pairs + 3) / 4)), block(256);
+    return a.D == 64
+        ? launch_kernel((attend_merge_kernel<DT, 64>), grid, block, 0, stream, a, pairs)
+        : launch_kernel((attend_merge_kernel<DT, 128>), grid, block, 0, stream, a, pairs);
 }
 
 int64_t attend_chunks(int64_t T) { return (T + kAttChunk - 1) / kAttChunk; }
