@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["quant_keys.hip", "quant_values.hip", "dequant.hip", "generic.hip",
-           "cache.hip", "attend.hip", "sink.hip", "rows.hip",
+           "cache.hip", "attend.hip", "attend_mfma.hip", "sink.hip", "rows.hip",
            "selftest.hip", "kivi_api.cpp"]
 
 FLAGS = [

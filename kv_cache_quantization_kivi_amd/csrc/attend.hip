@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     // zero[g][d], so that a score is sum_d qs * code + bias.
     constexpr int kKpStride = D + 4;
     constexpr int kQsRows = 16;
+    static_assert(kQsRows * 8 == kAttChunk, "bias: eight lanes per row");
     __shared__ __attribute__((aligned(16))) float kp_s[2 * kAttMaxGroups * kKpStride];
     float (*ks_s)[kKpStride] = reinterpret_cast<float (*)[kKpStride]>(kp_s);
     float (*kz_s)[kKpStride] =
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
     __shared__ __attribute__((aligned(16))) float acc_s[NQ][D];
     __shared__ float red[2 * NQ];
 
-    const int chunk = blockIdx.x;
+    const int chunk = (int)blockIdx.x + a.chunk0;
     const int bh = blockIdx.y;
     const int tid = threadIdx.x;
     const int nq = a.n_q;
@@ -138,12 +139,21 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
         for (int i = tid; i < ng * D; i += kAttChunk)
             z_s[i] = a.k_zero[((int64_t)bh * a.NG + g0 + i / D) * D + i % D];
         __syncthreads();
-        // bias[g][j]: one thread per (g, j), a plain sum over d
-        if (tid < ng * NQ) {
-            const int g = tid / NQ, j = tid % NQ;
+        // bias[g][j] = sum_d q[j][d] * zero[g][d]: eight lanes per (g, j)
+        // (kQsRows * 8 == kAttChunk), each summing every eighth channel,
+        // then three xor shuffles inside the eight
+        {
+            const int row = tid >> 3, part = tid & 7;
             float b = 0.0f;
-            for (int d = 0; d < D; ++d) b = __builtin_fmaf(q_s[j][d], z_s[g * D + d], b);
-            bias_s[tid] = b;
+            if (row < ng * NQ) {
+                const int g = row / NQ, j = row % NQ;
+#pragma unroll 4
+                for (int d = part; d < D; d += 8)
+                    b = __builtin_fmaf(q_s[j][d], z_s[g * D + d], b);
+            }
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) b += __shfl_xor(b, o);
+            if (part == 0 && row < ng * NQ) bias_s[row] = b;
         }
     } else {
         for (int i = tid; i < ng * D; i += kAttChunk) {
@@ -371,33 +381,48 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
 }
 
 template <int DT, int BITS, int D, int NQ>
-static hipError_t launch_partial(const AttendArgs& a, int64_t BH,
+static hipError_t launch_partial(const AttendArgs& a, int64_t BH, int64_t nc,
                                  hipStream_t stream) {
     return launch_kernel((attend_partial_kernel<DT, BITS, D, NQ>),
-                         dim3((uint32_t)a.n_chunks, (uint32_t)BH),
+                         dim3((uint32_t)nc, (uint32_t)BH),
                          dim3(kAttChunk), 0, stream, a);
 }
 
 template <int DT, int BITS, int D>
 static hipError_t launch_partial_nq(const AttendArgs& a, int64_t BH,
-                                    hipStream_t stream) {
+                                    int64_t nc, hipStream_t stream) {
     switch (a.n_q) {
-        case 1: return launch_partial<DT, BITS, D, 1>(a, BH, stream);
-        case 2: return launch_partial<DT, BITS, D, 2>(a, BH, stream);
-        case 3: return launch_partial<DT, BITS, D, 3>(a, BH, stream);
-        case 4: return launch_partial<DT, BITS, D, 4>(a, BH, stream);
+        case 1: return launch_partial<DT, BITS, D, 1>(a, BH, nc, stream);
+        case 2: return launch_partial<DT, BITS, D, 2>(a, BH, nc, stream);
+        case 3: return launch_partial<DT, BITS, D, 3>(a, BH, nc, stream);
+        case 4: return launch_partial<DT, BITS, D, 4>(a, BH, nc, stream);
         case 5:
-        case 6: return launch_partial<DT, BITS, D, 6>(a, BH, stream);
-        default: return launch_partial<DT, BITS, D, 8>(a, BH, stream);
+        case 6: return launch_partial<DT, BITS, D, 6>(a, BH, nc, stream);
+        default: return launch_partial<DT, BITS, D, 8>(a, BH, nc, stream);
     }
 }
 
 template <int DT, int BITS>
-static hipError_t launch_attend_t(const AttendArgs& a, int64_t BH,
+static hipError_t launch_attend_t(const AttendArgs& a0, int64_t BH,
                                   hipStream_t stream) {
-    hipError_t e = a.D == 64 ? launch_partial_nq<DT, BITS, 64>(a, BH, stream)
-                             : launch_partial_nq<DT, BITS, 128>(a, BH, stream);
-    if (e != hipSuccess) return e;
+    // Every chunk goes to the matrix-core kernel when its shape rules hold
+    // (it takes the ring's exact tokens on the vector units); otherwise all
+    // go to the token-per-thread kernel.
+    AttendArgs a = a0;
+    a.chunk0 = 0;
+    const bool mfma = BITS <= 4 && (a.G_k == 16 || a.G_k == 32) && a.G_v >= 16;
+    const int n_full = mfma ? a.n_chunks : 0;
+    if (n_full > 0) {
+        hipError_t e = launch_attend_mfma(a, BH, n_full, DT, BITS, stream);
+        if (e != hipSuccess) return e;
+        a.chunk0 = n_full;
+    }
+    if (a.chunk0 < a.n_chunks) {
+        const int64_t nc = a.n_chunks - a.chunk0;
+        hipError_t e = a.D == 64 ? launch_partial_nq<DT, BITS, 64>(a, BH, nc, stream)
+                                 : launch_partial_nq<DT, BITS, 128>(a, BH, nc, stream);
+        if (e != hipSuccess) return e;
+    }
     const int32_t pairs = (int32_t)(BH * a.n_q);
     const dim3 grid((uint32_t)((pairs + 3) / 4)), block(256);
     return a.D == 64

@@ -99,11 +99,17 @@ struct AttendArgs {
     float* work;
     int32_t D, S_max, ring, G_k, G_v, NG, NGD, T, Q, n_q, n_chunks;
     float sm_scale;
+    int32_t chunk0;        // first chunk of the token-per-thread kernel
 };
 int64_t attend_chunks(int64_t T);
 int64_t attend_work_floats(int64_t BH, int64_t T, int64_t D, int64_t n_q);
 hipError_t launch_attend(const AttendArgs& a, int64_t BH, int dtype, int bits,
                          hipStream_t stream);
+// The matrix-core kernel (attend_mfma.hip) over chunks [0, n_full) of every
+// bh; the caller has checked D in {64, 128}, bits <= 4, G_k in {16, 32} and
+// a value group of at least 16.
+hipError_t launch_attend_mfma(const AttendArgs& a, int64_t BH, int n_full,
+                              int dtype, int bits, hipStream_t stream);
 
 // KIVI-Sink (sink.hip).  Keys are [B*H, S, D] with the H heads of
 // sequence b at rows b*H .. b*H + H - 1; sink lists are [B, n_sink].  The

@@ -18,7 +18,13 @@ e = 2^-24 for fp32):
    n_acc = 128 + chunks + 8 (tokens of a chunk, the chunk merge, the shuffle
    tree);
  * the result is rounded once to the 16-bit type (u |o|), and 2^-20 max|V|
-   covers the fp32 exponentials.
+   covers the fp32 exponentials;
+ * the matrix-core kernel feeds q * scale and p * vscale to f16 operands as
+   hi + lo after a power-of-two scaling bounded by qmax * smax (vmax for
+   values): relative error 2^-22 (inside the terms above) plus, where lo
+   falls below f16's normal range, an absolute 2^-38 of the bound per
+   operand: at most sm 2^-34 D qmax smax on a score and 2^-34 T vmax on
+   the output.
 The test bound is the sum of these terms, the first two times 1.25, per
 element, with the maxima taken per (bh, query head)."""
 import numpy as np
@@ -81,7 +87,14 @@ def _bound(O, oc, q, sm, ref, dtype):
     zv = np.abs(oc.v_zero[:, :Q].astype(np.float64))
     zvmax = (zv.max(axis=(1, 2)) if Q else np.zeros(BH))[:, None, None]
     n_acc = 128 + (T + 127) // 128 + 8
-    vterm = u * vmax + e * n_acc * (vmax + 2 * zvmax)
+    if Q:
+        skmax = np.abs(oc.k_scale[:, :Q // G_k]).max(axis=(1, 2))[:, None]
+        svmax = np.abs(oc.v_scale[:, :Q]).max(axis=(1, 2))[:, None, None]
+    else:
+        skmax = np.zeros((BH, 1))
+        svmax = np.zeros((BH, 1, 1))
+    ds = ds + sm * 2.0 ** -34 * D * aq.max(axis=2)[:, :, None] * skmax[:, :, None]
+    vterm = u * vmax + e * n_acc * (vmax + 2 * zvmax) + 2.0 ** -34 * T * svmax
     return (1.25 * (2.0 * ds.max(axis=2)[:, :, None] * vmax + vterm)
             + u * np.abs(ref) + 2.0 ** -20 * vmax)
 
@@ -95,6 +108,11 @@ CASES = [
     (2, 64, 0, 8, 8, 8, BF16, 2, [256]),             # everything quantized
     (3, 128, 5, 32, 64, 1, FP16, 8, [1000, 3]),
     (2, 128, 32, 32, 32, 2, FP16, 4, [1]),           # a single token
+    # chunks of 128 fully quantized tokens take the matrix-core kernel
+    (3, 128, 32, 16, 16, 4, BF16, 6, [700]),
+    (2, 64, 32, 32, 64, 2, FP16, 2, [500, 9]),
+    (2, 64, 16, 16, 32, 2, BF16, 3, [290]),
+    (1, 128, 0, 32, 128, 2, FP16, 5, [512]),         # every chunk full
 ]
 
 
