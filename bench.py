@@ -586,7 +586,7 @@ def attend_bench(args, aw, K, torch, dev):
     d = [a_.elapsed_time(b_) for a_, b_ in ev]
     kb = step_bytes - out_bytes
     avg = float(np.mean(d))
-    pk = {"attend_partial": {
+    pk = {"attend_chunks": {
         "avg_us": round(avg * 1e3, 3),
         "median_us": round(float(np.median(d)) * 1e3, 3),
         "min_us": round(float(np.min(d)) * 1e3, 3),
@@ -641,14 +641,14 @@ def attend_bench(args, aw, K, torch, dev):
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "roofline": {
-            "kernel": "attend_partial",
-            "avg_us": pk["attend_partial"]["avg_us"],
+            "kernel": "attend_chunks",
+            "avg_us": pk["attend_chunks"]["avg_us"],
             "bound": "hbm",
-            "achieved": pk["attend_partial"]["gbs"],
+            "achieved": pk["attend_chunks"]["gbs"],
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(pk["attend_partial"]["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic("attend_partial", aw.name,
+            "frac": round(pk["attend_chunks"]["gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": load_traffic("attend_chunks", aw.name,
                                     kernel_source_hash()),
         },
         "per_kernel": pk,
