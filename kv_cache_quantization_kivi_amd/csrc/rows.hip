@@ -25,15 +25,19 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix count of `flag` over the block in thread order, plus the
-// block's total.  Lanes of a wave count with their ballot mask; the waves'
-// totals meet in LDS.
-__device__ __forceinline__ uint32_t block_rank(bool flag, uint32_t* wsum,
+// Exclusive prefix sum of `v` over the block in thread order, plus the
+// block's total: an inclusive scan inside each wave (shuffles), the waves'
+// totals through LDS.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum,
                                                uint32_t* total) {
     const uint32_t lane = threadIdx.x & 63u, w = threadIdx.x >> 6;
-    const uint64_t m = __ballot(flag);
-    const uint32_t below = (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[w] = (uint32_t)__popcll(m);
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(incl, o);
+        if (lane >= (uint32_t)o) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
     uint32_t before = 0, all = 0;
     for (int i = 0; i < kPartWaves; ++i) {
@@ -43,32 +47,75 @@ __device__ __forceinline__ uint32_t block_rank(bool flag, uint32_t* wsum,
     }
     __syncthreads();
     *total = all;
-    return before + below;
+    return before + incl - v;
 }
+
+// Elements per thread per round: thread t owns positions
+// [round * kPartThreads * kPartPer + t * kPartPer, + kPartPer).
+constexpr int kPartPer = 32;
+constexpr int kPartRound = kPartThreads * kPartPer;
 
 // One block per sequence.  The n_hi-th largest key is found digit by digit
 // (four 8-bit radix passes over the scores, counting only the scores that
-// share the digits fixed so far); then one pass in position order marks the
-// scores above it and, of the scores equal to it, the lowest positions still
-// needed, and writes both lists in ascending position.
+// share the digits fixed so far; in the first pass, where most scores share
+// their top byte, a wave adds each distinct digit once through a ballot).
+// Then each thread walks its own run of positions in order: the scores above
+// the threshold and, of those equal to it, the lowest positions still
+// needed, are hi; block prefix sums of the per-thread counts give every
+// thread its place in both lists, which stay in ascending position.
 __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
     const float* __restrict__ score, int32_t S, int32_t n_hi,
     int32_t* __restrict__ pos_hi, int32_t* __restrict__ pos_lo) {
     __shared__ uint32_t hist[256];
     __shared__ uint32_t wsum[kPartWaves];
     __shared__ uint32_t pick[2];
+    // a round's keys, element p at p + p / 32: the block loads them with
+    // coalesced reads, and the 64 lanes reading element i of their runs
+    // (stride 33 words) hit 64 different banks
+    __shared__ uint32_t stage_s[kPartRound + kPartRound / 32];
     const int32_t b = blockIdx.x, tid = threadIdx.x;
+    const int lane = tid & 63;
     const float* sc = score + (int64_t)b * S;
+    const int n_rounds = (S + kPartRound - 1) / kPartRound;
+    uint32_t key[kPartPer];                    // this thread's run (one round)
+    const auto load_run = [&](int r) {         // every thread, barriers inside
+        __syncthreads();
+        for (int i = tid; i < kPartRound; i += kPartThreads) {
+            const int32_t p = r * kPartRound + i;
+            stage_s[i + i / 32] = p < S ? order_key(sc[p]) : 0u;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPartPer; ++i) key[i] = stage_s[tid * (kPartPer + 1) + i];
+    };
+    if (n_rounds == 1) load_run(0);
     uint32_t prefix = 0, need = (uint32_t)n_hi;   // keys above prefix still to take
     if (n_hi > 0 && n_hi < S) {
         for (int shift = 24; shift >= 0; shift -= 8) {
             for (int i = tid; i < 256; i += kPartThreads) hist[i] = 0u;
             __syncthreads();
             const uint32_t hmask = shift == 24 ? 0u : ~0u << (shift + 8);
-            for (int32_t s = tid; s < S; s += kPartThreads) {
-                const uint32_t k = order_key(sc[s]);
-                if ((k & hmask) == (prefix & hmask))
-                    atomicAdd(&hist[(k >> shift) & 255u], 1u);
+            for (int r = 0; r < n_rounds; ++r) {
+                if (n_rounds > 1) load_run(r);
+                const int32_t s0 = r * kPartRound + tid * kPartPer;
+#pragma unroll
+                for (int i = 0; i < kPartPer; ++i) {
+                    const bool in = s0 + i < S && (key[i] & hmask) == (prefix & hmask);
+                    const uint32_t d = (key[i] >> shift) & 255u;
+                    if (shift == 24) {
+                        // each distinct digit of the wave once
+                        uint64_t left = __ballot(in);
+                        while (left) {
+                            const int ld = __ffsll((unsigned long long)left) - 1;
+                            const uint32_t dd = __shfl(d, ld);
+                            const uint64_t same = __ballot(in && d == dd) & left;
+                            if (lane == ld) atomicAdd(&hist[dd], (uint32_t)__popcll(same));
+                            left &= ~same;
+                        }
+                    } else if (in) {
+                        atomicAdd(&hist[d], 1u);
+                    }
+                }
             }
             __syncthreads();
             // wave 0: lane l holds digits 255-4l .. 252-4l (descending), an
@@ -110,20 +157,64 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
     // in position order
     const bool all_hi = n_hi == S, none_hi = n_hi == 0;
     uint32_t eq_base = 0, hi_base = 0;
-    for (int32_t s0 = 0; s0 < S; s0 += kPartThreads) {
-        const int32_t s = s0 + tid;
-        const bool real = s < S;
-        const uint32_t k = real ? order_key(sc[s]) : 0u;
-        const bool eq = real && !all_hi && !none_hi && k == prefix;
-        uint32_t n_eq, n_h;
-        const uint32_t eq_rank = eq_base + block_rank(eq, wsum, &n_eq);
-        const bool hi = real && (all_hi || (!none_hi && (k > prefix ||
-                                                         (eq && eq_rank < need))));
-        const uint32_t hi_rank = hi_base + block_rank(hi, wsum, &n_h);
-        if (hi) pos_hi[(int64_t)b * n_hi + hi_rank] = s;
-        else if (real) pos_lo[(int64_t)b * (S - n_hi) + (s - (int32_t)hi_rank)] = s;
-        eq_base += n_eq;
-        hi_base += n_h;
+    for (int r = 0; r < n_rounds; ++r) {
+        if (n_rounds > 1) load_run(r);
+        const int32_t s0 = r * kPartRound + tid * kPartPer;
+        uint32_t n_eq = 0;
+#pragma unroll
+        for (int i = 0; i < kPartPer; ++i)
+            n_eq += (s0 + i < S && !all_hi && !none_hi && key[i] == prefix) ? 1u : 0u;
+        uint32_t eq_all, hi_all;
+        uint32_t eq_rank = eq_base + block_scan(n_eq, wsum, &eq_all);
+        uint32_t hi_here = 0;
+        uint32_t mark = 0;                     // bit i: position s0 + i is hi
+#pragma unroll
+        for (int i = 0; i < kPartPer; ++i) {
+            const bool real = s0 + i < S;
+            const bool eq = real && !all_hi && !none_hi && key[i] == prefix;
+            const bool hi = real && (all_hi || (!none_hi && (key[i] > prefix ||
+                                                             (eq && eq_rank < need))));
+            eq_rank += eq ? 1u : 0u;
+            hi_here += hi ? 1u : 0u;
+            mark |= (hi ? 1u : 0u) << i;
+        }
+        uint32_t hi_rank = hi_base + block_scan(hi_here, wsum, &hi_all);
+        if (n_rounds == 1) {
+            // one round: both lists are assembled in LDS (the keys are
+            // already in registers) and leave with coalesced stores
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kPartPer; ++i) {
+                const int32_t s = s0 + i;
+                if (s >= S) break;
+                if ((mark >> i) & 1u) {
+                    stage_s[hi_rank] = (uint32_t)s;
+                    ++hi_rank;
+                } else {
+                    stage_s[n_hi + (s - (int32_t)hi_rank)] = (uint32_t)s;
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < S; i += kPartThreads) {
+                const int32_t v = (int32_t)stage_s[i];
+                if (i < n_hi) pos_hi[(int64_t)b * n_hi + i] = v;
+                else pos_lo[(int64_t)b * (S - n_hi) + (i - n_hi)] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kPartPer; ++i) {
+                const int32_t s = s0 + i;
+                if (s >= S) break;
+                if ((mark >> i) & 1u) {
+                    pos_hi[(int64_t)b * n_hi + hi_rank] = s;
+                    ++hi_rank;
+                } else {
+                    pos_lo[(int64_t)b * (S - n_hi) + (s - (int32_t)hi_rank)] = s;
+                }
+            }
+        }
+        eq_base += eq_all;
+        hi_base += hi_all;
     }
 }
 
