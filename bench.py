@@ -39,8 +39,18 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
-KERNEL_SOURCES = ["kivi_device.h", "kivi_rows.h", "quant_keys.hip", "quant_values.hip",
-                  "dequant.hip", "cache.hip", "attend.hip", "sink.hip", "rows.hip"]
+# The kernel sources behind each family of workloads: the traffic measured
+# for a workload stays valid while these files are unchanged.
+_COMMON = ["kivi_device.h", "kivi_launch.h", "kivi_rows.h"]
+KERNEL_SOURCES = {
+    "flush": _COMMON + ["quant_keys.hip", "quant_values.hip", "dequant.hip",
+                        "generic.hip"],
+    "cache": _COMMON + ["quant_keys.hip", "quant_values.hip", "cache.hip"],
+    "attend": _COMMON + ["attend.hip", "attend_mfma.hip"],
+    "sink": _COMMON + ["sink.hip", "quant_keys.hip", "quant_values.hip"],
+    "mixed": _COMMON + ["sink.hip", "rows.hip", "quant_keys.hip",
+                        "quant_values.hip"],
+}
 
 
 def bytes_per_elem(op, bits, group, dtype_bytes=2):
@@ -57,9 +67,9 @@ def bytes_per_elem(op, bits, group, dtype_bytes=2):
     raise ValueError(op)
 
 
-def kernel_source_hash():
+def kernel_source_hash(family="flush"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(ROOT, "kv_cache_quantization_kivi_amd",
                                "csrc", f), "rb") as fh:
             h.update(fh.read())
@@ -482,13 +492,13 @@ def cache_bench(args, cw, K, torch, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(dk["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(dom, cw.name, kernel_source_hash()),
+            "traffic": load_traffic(dom, cw.name, kernel_source_hash("cache")),
         },
         "per_kernel": per_kernel,
         "per_kernel_note": ("value: K steps with no per-launch events; "
                             "per_kernel: the first kernel of every append of "
                             "a second pass of K eager steps"),
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("cache"),
         "cpu_baseline": (None if args.no_cpu_baseline else
                          cache_cpu_baseline(cw, args.cpu_threads, plan,
                                             step_bytes)),
@@ -649,10 +659,10 @@ def attend_bench(args, aw, K, torch, dev):
             "unit": "GB/s",
             "frac": round(pk["attend_chunks"]["gbs"] / PEAK_HBM_GBS, 4),
             "traffic": load_traffic("attend_chunks", aw.name,
-                                    kernel_source_hash()),
+                                    kernel_source_hash("attend")),
         },
         "per_kernel": pk,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("attend"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -819,10 +829,10 @@ def sink_bench(args, sw, K, torch, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(pk[dom]["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(dom, sw.name, kernel_source_hash()),
+            "traffic": load_traffic(dom, sw.name, kernel_source_hash("sink")),
         },
         "per_kernel": pk,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("sink"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -997,10 +1007,10 @@ def mixed_bench(args, mw, K, torch, dev):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(pk[dom]["gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": load_traffic(dom, mw.name, kernel_source_hash()),
+            "traffic": load_traffic(dom, mw.name, kernel_source_hash("mixed")),
         },
         "per_kernel": pk,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("mixed"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -115,55 +115,94 @@ __device__ __forceinline__ bool ranks_before(float sa, int32_t pa, float sb,
     return sa > sb || (sa == sb && pa < pb);
 }
 
-constexpr int kSelThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 32;   // scores per thread when a sequence fits in registers
 
+// One pick: the best (score, position) that ranks after the previous pick.
+// best starts as (-inf, INT_MAX), which every non-NaN score outranks and
+// which itself outranks nothing, so it doubles as "nothing yet"; a NaN
+// score ranks neither before nor after anything and is never picked.
+__device__ __forceinline__ void consider(float prev_s, int32_t prev_p, float v,
+                                         int32_t s, float& best_s,
+                                         int32_t& best_p) {
+    if (ranks_before(prev_s, prev_p, v, s) && ranks_before(v, s, best_s, best_p)) {
+        best_s = v;
+        best_p = s;
+    }
+}
+
+// One block per sequence, n_sink rounds of a block-wide argmax in (score
+// desc, position asc) order, each round restricted to what ranks after the
+// previous round's pick.  RESIDENT: the sequence's scores (S <= 32768) are
+// loaded once into registers, thread t holding positions t + 1024 i;
+// otherwise every round streams them again.
+template <bool RESIDENT>
 __global__ __launch_bounds__(kSelThreads) void sink_select_kernel(
     const float* __restrict__ score, int32_t S, int32_t n_sink,
     int32_t* __restrict__ idx) {
-    __shared__ float red_s[kSelThreads / 64];
-    __shared__ int32_t red_p[kSelThreads / 64];
+    constexpr int NW = kSelThreads / 64;
+    // two buffers, so one barrier per round suffices: a round writes the
+    // buffer the round before it did not read
+    __shared__ float red_s[2][NW];
+    __shared__ int32_t red_p[2][NW];
     const int32_t b = blockIdx.x, tid = threadIdx.x;
     const float* sc = score + (int64_t)b * S;
-    // the previous round's pick; the first round has none
-    float prev_s = __builtin_huge_valf();
+    float v[RESIDENT ? kSelPer : 1];
+    if constexpr (RESIDENT) {
+#pragma unroll
+        for (int i = 0; i < kSelPer; ++i) {
+            const int32_t s = tid + i * kSelThreads;
+            v[i] = s < S ? sc[s] : __builtin_nanf("");
+        }
+    }
+    float prev_s = __builtin_huge_valf();   // the first round has no pick before it
     int32_t prev_p = -1;
     for (int32_t r = 0; r < n_sink; ++r) {
         float best_s = -__builtin_huge_valf();
-        int32_t best_p = 0x7fffffff;   // nothing yet
-        for (int32_t s = tid; s < S; s += kSelThreads) {
-            const float v = sc[s];
-            if (ranks_before(prev_s, prev_p, v, s) &&
-                (best_p == 0x7fffffff || ranks_before(v, s, best_s, best_p))) {
-                best_s = v;
-                best_p = s;
+        int32_t best_p = 0x7fffffff;
+        if constexpr (RESIDENT) {
+#pragma unroll
+            for (int i = 0; i < kSelPer; ++i)
+                consider(prev_s, prev_p, v[i], tid + i * kSelThreads, best_s, best_p);
+        } else {
+            // 64-bit positions: S may come within a batch of 2^31
+            for (int64_t s0 = 0; s0 < S; s0 += 8 * kSelThreads) {
+                float w[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int64_t s = s0 + tid + i * kSelThreads;
+                    w[i] = s < S ? sc[s] : __builtin_nanf("");
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    consider(prev_s, prev_p, w[i], (int32_t)(s0 + tid + i * kSelThreads),
+                             best_s, best_p);
             }
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
             const float os = __shfl_xor(best_s, o);
             const int32_t op = __shfl_xor(best_p, o);
-            if (op != 0x7fffffff &&
-                (best_p == 0x7fffffff || ranks_before(os, op, best_s, best_p))) {
+            if (ranks_before(os, op, best_s, best_p)) {
                 best_s = os;
                 best_p = op;
             }
         }
+        const int buf = r & 1;
         if ((tid & 63) == 0) {
-            red_s[tid >> 6] = best_s;
-            red_p[tid >> 6] = best_p;
+            red_s[buf][tid >> 6] = best_s;
+            red_p[buf][tid >> 6] = best_p;
         }
         __syncthreads();
-        best_s = red_s[0];
-        best_p = red_p[0];
+        best_s = red_s[buf][0];
+        best_p = red_p[buf][0];
 #pragma unroll
-        for (int w = 1; w < kSelThreads / 64; ++w)
-            if (red_p[w] != 0x7fffffff &&
-                (best_p == 0x7fffffff || ranks_before(red_s[w], red_p[w], best_s, best_p))) {
-                best_s = red_s[w];
-                best_p = red_p[w];
+        for (int w = 1; w < NW; ++w)
+            if (ranks_before(red_s[buf][w], red_p[buf][w], best_s, best_p)) {
+                best_s = red_s[buf][w];
+                best_p = red_p[buf][w];
             }
-        __syncthreads();
-        // only a NaN score can leave a round empty; such a round stores -1
+        // only NaN scores can leave a round empty; such a round stores -1
         if (tid == 0) idx[(int64_t)b * n_sink + r] = best_p == 0x7fffffff ? -1 : best_p;
         prev_s = best_s;
         prev_p = best_p;
@@ -338,8 +377,13 @@ hipError_t launch_sink_scores(const void* k, int dtype, int64_t B, int64_t H,
 
 hipError_t launch_sink_select(const float* score, int64_t B, int64_t S,
                               int64_t n_sink, int32_t* idx, hipStream_t stream) {
-    return launch_kernel(sink_select_kernel, dim3((uint32_t)B), dim3(kSelThreads),
-                         0, stream, score, (int32_t)S, (int32_t)n_sink, idx);
+    if (S <= (int64_t)kSelThreads * kSelPer)
+        return launch_kernel(sink_select_kernel<true>, dim3((uint32_t)B),
+                             dim3(kSelThreads), 0, stream, score, (int32_t)S,
+                             (int32_t)n_sink, idx);
+    return launch_kernel(sink_select_kernel<false>, dim3((uint32_t)B),
+                         dim3(kSelThreads), 0, stream, score, (int32_t)S,
+                         (int32_t)n_sink, idx);
 }
 
 hipError_t launch_quant_keys_sink(const SinkQuantJob& j) {

@@ -54,6 +54,8 @@ SELECT_CASES = [
     (1, 8, 1000, 256, 64, FP16),
     (4, 2, 33, 8, 33, BF16),         # every token a sink
     (2, 3, 50, 32, 0, FP16),         # scores only
+    (2, 1, 32768, 8, 64, FP16),      # longest sequence held in registers
+    (2, 1, 40000, 8, 64, BF16),      # longer: scores streamed every round
 ]
 
 
@@ -69,23 +71,24 @@ def test_select_matches_oracle(K, O, case):
     assert np.array_equal(host(idx), O.sink_select(want_s, n)), "sink lists"
 
 
-def test_select_ties_take_lower_position(K, O):
+@pytest.mark.parametrize("S", [700, 50000])
+def test_select_ties_take_lower_position(K, O, S):
     """Rows repeated across positions have equal scores: the lower position
-    must win (and the GPU's block-wide reduction must agree)."""
-    B, H, S, D = 2, 2, 700, 64
+    must win (and the GPU's block-wide reduction must agree), with the
+    scores in registers (S = 700) and streamed (S = 50000)."""
+    B, H, D = 2, 2, 64 if S < 1000 else 8
+    copies = (5, S // 3 + 1, S // 2 + 7, S - 1)
     x = _keys(62, B, H, S, D, FP16).reshape(B, H, S, D)
     for b in range(B):
-        for p in (5, 260, 517, 699):        # four copies of row 5, all large
-            x[b, :, p] = x[b, :, 5]
-        x[b, :, 5] = (np.float16(4.0) * x[b, :, 5].view(np.float16)).view(np.uint16)
-        for p in (260, 517, 699):
+        x[b, :, 5] = (np.float16(16.0) * x[b, :, 5].view(np.float16)).view(np.uint16)
+        for p in copies[1:]:                 # four copies of row 5, all large
             x[b, :, p] = x[b, :, 5]
     x = x.reshape(B * H, S, D)
     idx, score = K.kivi_sink_select(to_dev(x, FP16), 3, H=H)
     torch.cuda.synchronize()
     want = O.sink_select(O.sink_scores(x, FP16, H), 3)
     assert np.array_equal(host(idx), want)
-    assert host(idx)[0].tolist() == [5, 260, 517]
+    assert host(idx)[0].tolist() == list(copies[:3])
 
 
 QUANT_CASES = [
