@@ -323,7 +323,7 @@ kivi_status kivi_sink_restore(const void* x_sink, int64_t B, int64_t H,
  * Rules (else nothing is launched): bits in {1, 2, 4, 8} (KIVI_ERR_BITS);
  * key group in [1, 32], value group 8, 16 or 32 * 2^k (KIVI_ERR_GROUP);
  * B, H, S >= 1, D in {8, 16, 32, 64, 128, 256}, 0 <= n <= S, B*H*n < 2^31,
- * B*H*S*D < 2^40 (KIVI_ERR_SHAPE); dtype (KIVI_ERR_DTYPE); non-NULL
+ * B*H*S*D < 2^40, for keys B*H*ceil(n/group)*D < 2^33 (KIVI_ERR_SHAPE); dtype (KIVI_ERR_DTYPE); non-NULL
  * (KIVI_ERR_NULL) and 16-byte aligned pointers, 4-byte for lists
  * (KIVI_ERR_ALIGN).  n == 0 launches nothing.  One kernel per call.
  */

@@ -145,6 +145,10 @@ kivi_status check_list(int64_t B, int64_t H, int64_t S, int64_t D, int bits,
     if (!mul_ok(B, H, &m) || !mul_ok(m, S, &m) || !mul_ok(m, D, &m) ||
         m >= (1ll << 40) || S >= (1ll << 31))
         return KIVI_ERR_SHAPE;
+    // key kernels: up to 4 lanes per (bh, group, 8 channels), 32-bit counts
+    if (keys && (!mul_ok(B * H, (n + group - 1) / group, &m) ||
+                 !mul_ok(m, D, &m) || m >= (1ll << 33)))
+        return KIVI_ERR_SHAPE;
     return KIVI_OK;
 }
 

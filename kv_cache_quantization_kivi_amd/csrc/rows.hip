@@ -222,16 +222,44 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
 
 // Keys: one lane per (bh, group of the set, 8-channel chunk), chunk fastest;
 // the chunk's 8 scales and zeros are loaded once for the group's tokens.
+// stage: the host's verdict that a wave of full groups has one contiguous
+// block of codes made of whole 16-byte pieces per lane (64 % D8 == 0,
+// D8 >= 4, group <= 32, group * BITS % 16 == 0, BITS <= 4); the wave then
+// loads the block with 16-byte loads into LDS (each group's codes padded
+// apart), and its groups' positions beside it, so that the token loop is
+// stores only.  A global load in that loop would make each batch wait for
+// the stores before it, since one counter tracks a wave's outstanding
+// loads and stores together.  The set's codes [BH, n, D*BITS/8] have the
+// row order of the wave's groups, so the block starts at lane 0's first row.
+template <int BITS>
+struct ListDqKeyStage {
+    static constexpr int kWaveBytes = BITS <= 4 ? 64 * 32 * BITS + 64 * 16 : 0;
+    static constexpr int kWavePos = 16 * 32;   // positions: <= 16 groups of <= 32
+};
+
+template <int BITS>
+__device__ __forceinline__ uint64_t lds_key_codes(const uint8_t* p) {
+    if constexpr (BITS == 1) return *p;
+    else if constexpr (BITS == 2) return *reinterpret_cast<const uint16_t*>(p);
+    else return *reinterpret_cast<const uint32_t*>(p);
+}
+
 template <int DT, int BITS>
 __global__ __launch_bounds__(256) void list_dequant_keys_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ scale,
     const float* __restrict__ zero, uint32_t n_items, uint32_t D8, uint32_t NG,
     int32_t S, int32_t n, int32_t H, int32_t G, const int32_t* __restrict__ pos,
-    uint16_t* __restrict__ out) {
+    uint16_t* __restrict__ out, int32_t stage) {
+    constexpr int kWaveBytes = ListDqKeyStage<BITS>::kWaveBytes;
+    constexpr int kWavePos = ListDqKeyStage<BITS>::kWavePos;
+    __shared__ __attribute__((aligned(16)))
+    uint8_t lds[BITS <= 4 ? 4 * kWaveBytes : 16];
+    __shared__ int32_t pos_s[BITS <= 4 ? 4 * kWavePos : 1];
     const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
-    if (gid >= n_items) return;
-    const uint32_t c = gid % D8;
-    const uint32_t tile = gid / D8;
+    const bool valid = gid < n_items;
+    const uint32_t item = valid ? gid : n_items - 1u;
+    const uint32_t c = item % D8;
+    const uint32_t tile = item / D8;
     const uint32_t g = tile % NG;
     const uint32_t bh = tile / NG;
     const int64_t D = (int64_t)D8 * 8;
@@ -245,9 +273,70 @@ __global__ __launch_bounds__(256) void list_dequant_keys_kernel(
     const float sc[8] = {s_a.x, s_a.y, s_a.z, s_a.w, s_b.x, s_b.y, s_b.z, s_b.w};
     const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
     const int64_t row_bytes = (int64_t)D8 * BITS;
-    const uint8_t* src = codes + ((int64_t)bh * n + j0) * row_bytes + (int64_t)c * BITS;
+    const int64_t crow0 = (int64_t)bh * n + j0;      // the group's first code row
     const int32_t* lp = pos + (int64_t)(bh / (uint32_t)H) * n + j0;
     uint16_t* dst = out + (int64_t)bh * S * D + (int64_t)c * 8;
+
+    if constexpr (BITS <= 4) {
+        if (stage && __all(valid && nt == G)) {
+            const uint32_t lane = threadIdx.x & 63u;
+            uint8_t* L = lds + (threadIdx.x >> 6) * kWaveBytes;
+            const uint32_t tile_bytes = (uint32_t)G * D8 * BITS;
+            const uint32_t ts = tile_bytes + ((D8 * BITS + 15u) & ~15u);
+            const uint32_t r_lo = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)crow0 & 0xffffffffu));
+            const uint32_t r_hi = __builtin_amdgcn_readfirstlane(
+                (uint32_t)((uint64_t)crow0 >> 32));
+            const uint8_t* wsrc =
+                codes + (int64_t)(((uint64_t)r_hi << 32) | r_lo) * row_bytes;
+            const uint32_t n16 = (uint32_t)G * BITS / 16;   // pieces per lane
+            uint4 t4[8];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k)
+                if (k < n16) t4[k] = load16_nt(wsrc + (k * 64u + lane) * 16u);
+            // the group's positions: lane c of the group loads t = c + m*D8
+            // (D8 >= 4, so at most 8 each)
+            int32_t pp[8];
+#pragma unroll
+            for (uint32_t m = 0; m < 8; ++m)   // wave-uniform bound, clamped index
+                if (m * D8 < (uint32_t)G) pp[m] = lp[min(c + m * D8, (uint32_t)G - 1u)];
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) {
+                if (k < n16) {
+                    const uint32_t off = (k * 64u + lane) * 16u;
+                    const uint32_t ti = off / tile_bytes;
+                    *reinterpret_cast<uint4*>(L + ti * ts + (off - ti * tile_bytes)) = t4[k];
+                }
+            }
+            int32_t* P = pos_s + (threadIdx.x >> 6) * kWavePos + (lane / D8) * 32;
+#pragma unroll
+            for (uint32_t m = 0; m < 8; ++m) {
+                const uint32_t t = c + m * D8;
+                if (m * D8 < (uint32_t)G && t < (uint32_t)G) P[t] = pp[m];
+            }
+            wave_lds_sync();
+            const uint8_t* mine = L + (lane / D8) * ts + c * BITS;
+            for (int32_t t0 = 0; t0 < G; t0 += 8) {
+                int32_t sp[8];
+                uint64_t q[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {   // every LDS read of a batch first
+                    const int32_t t = min(t0 + u, G - 1);
+                    sp[u] = P[t];
+                    q[u] = lds_key_codes<BITS>(mine + t * row_bytes);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int32_t s = sp[u];
+                    if (t0 + u < G && s >= 0 && s < S)
+                        store16_nt(dst + (int64_t)s * D, dequant_chunk<DT, BITS>(q[u], sc, z));
+                }
+            }
+            return;
+        }
+    }
+    if (!valid) return;
+    const uint8_t* src = codes + crow0 * row_bytes + (int64_t)c * BITS;
     // tokens in batches of 8: every load of a batch is issued before its
     // first store
     for (int32_t t0 = 0; t0 < nt; t0 += 8) {
@@ -348,11 +437,13 @@ static hipError_t launch_list_dq_t(const ListJob& j, bool keys, void* out) {
     if (keys) {
         const uint32_t NG = (uint32_t)((j.n + j.group - 1) / j.group);
         const uint32_t n = (uint32_t)(j.B * j.H) * NG * D8;
+        const int32_t stage = BITS <= 4 && 64 % D8 == 0 && D8 >= 4 &&
+                              j.group <= 32 && (j.group * BITS) % 16 == 0;
         return launch_kernel((list_dequant_keys_kernel<DT, BITS>),
                              dim3((n + 255u) / 256u), dim3(256), 0, j.stream,
                              j.codes, j.scale, j.zero, n, D8, NG, (int32_t)j.S,
                              (int32_t)j.n, (int32_t)j.H, (int32_t)j.group,
-                             j.pos, o);
+                             j.pos, o, stage);
     }
     const uint32_t NGD = (uint32_t)((j.D + j.group - 1) / j.group);
     const uint32_t cpl = D8 < 4 ? D8 : 4;              // D8 is a power of two

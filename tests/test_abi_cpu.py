@@ -298,6 +298,9 @@ def test_mixed_precision_entry_points_reject_before_any_launch(K):
         assert q(x=None) == 1 and q(pos=None) == 1 and q(codes=None) == 1
         assert q(x=P(0x1004)) == 6 and q(pos=P(0x2001)) == 6
         assert q(n=0, x=None) == 0                              # nothing to do
+        if keys:        # 2^30 one-token groups of 128 channels: too many lanes
+            assert fn(x, 0, 1, 1, 1 << 30, 128, 2, 1, pos, (1 << 30) - 1,
+                      c, s, z, None) == 2
 
     for name in ("kivi_dequant_keys_rows", "kivi_dequant_values_rows"):
         fn = getattr(L, name)
@@ -305,3 +308,6 @@ def test_mixed_precision_entry_points_reject_before_any_launch(K):
         assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 0, None, None) == 1
         assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 0, P(0x1008), None) == 6
         assert fn(c, s, z, 2, 4, 64, 128, 2, 32, pos, 40, 7, x, None) == 5
+        if name == "kivi_dequant_keys_rows":
+            assert fn(c, s, z, 1, 1, 1 << 30, 128, 2, 1, pos, (1 << 30) - 1, 0,
+                      x, None) == 2

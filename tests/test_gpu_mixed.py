@@ -45,6 +45,10 @@ def _x(seed, BH, S, D, dtype):
     return t.numpy().view(np.uint16)
 
 
+def _ix(a):
+    return torch.from_numpy(np.asarray(a, np.int64))
+
+
 PART_CASES = [(3, 90, 17), (2, 5000, 1000), (1, 40000, 8000), (4, 1024, 0),
               (2, 777, 777), (2, 1025, 1), (3, 3000, 2999)]
 
@@ -75,6 +79,11 @@ ROW_CASES = [
     (1, 3, 100, 256, 100, 8, 5, 16, FP16),
     (2, 1, 50, 32, 33, 2, 16, 64, BF16),
     (1, 2, 40, 8, 7, 4, 1, 8, FP16),
+    # whole key groups only: every wave of the key dequantizer stages its
+    # codes through LDS (2, 1 and 4 bits; 4, 8 and 2 groups per wave)
+    (2, 4, 300, 128, 256, 2, 32, 32, FP16),
+    (2, 2, 200, 64, 128, 1, 16, 16, BF16),
+    (1, 2, 300, 256, 64, 4, 32, 64, FP16),
 ]
 
 
@@ -130,7 +139,8 @@ def test_mixed_end_to_end(K, O):
 def test_mixed_full_size_sampled(K, O):
     """The benchmark's prompt in the benchmark's launch shape: the lists
     against the oracle's partition of the GPU scores (sampled scores checked
-    exactly), then sampled key groups and value rows of both sets."""
+    exactly), then sampled key groups and value rows of both sets: codes,
+    params, and the rows both sets' dequantizers wrote back."""
     mw = W.MIXED_WORKLOADS["mixed-prefill"]
     w = mw.tokens()
     B, H, S, D, n_hi = mw.B, mw.H, mw.S, mw.D, mw.n_hi
@@ -140,9 +150,13 @@ def test_mixed_full_size_sampled(K, O):
     score = K.kivi_key_scores(kd, H=H)
     hi, lo = K.kivi_partition_top(score, n_hi)
     sets = {}
+    k_out, v_out = torch.zeros_like(kd), torch.zeros_like(kd)
     for name, pos, bits in (("hi", hi, mw.hi_bits), ("lo", lo, mw.lo_bits)):
-        sets[name] = (host(pos), bits, K.kivi_quant_keys_rows(kd, pos, bits, mw.group_k, H=H),
-                      K.kivi_quant_values_rows(kd, pos, bits, mw.group_v, H=H))
+        kq = K.kivi_quant_keys_rows(kd, pos, bits, mw.group_k, H=H)
+        vq = K.kivi_quant_values_rows(kd, pos, bits, mw.group_v, H=H)
+        K.kivi_dequant_keys_rows(*kq, pos, k_out, bits, mw.group_k, H=H)
+        K.kivi_dequant_values_rows(*vq, pos, v_out, bits, mw.group_v, H=H)
+        sets[name] = (host(pos), bits, kq, vq)
     torch.cuda.synchronize()
     sc = host(score)
     ehi, elo = O.partition_top(sc, n_hi)
@@ -164,8 +178,14 @@ def test_mixed_full_size_sampled(K, O):
                 assert_codes_equal(host(kc[bh, j0:j1]), wc[0], f"{name} key codes {bh},{g}")
                 assert_f32_bits_equal(host(ks[bh, g]), ws[0, 0], f"{name} key scale")
                 assert_f32_bits_equal(host(kz[bh, g]), wz[0, 0], f"{name} key zero")
+                want = O.dequant_keys(wc, ws, wz, tile.shape, bits, mw.group_k, w.dtype)
+                assert_recon_equal(bits16(k_out[bh, _ix(pos[b, j0:j1])]), want[0],
+                                   f"{name} key recon {bh},{g}")
             js = r.choice(n, 8, replace=False)
             rows = np.ascontiguousarray(k[bh:bh + 1, pos[b, js]])
             wc, ws, wz = O.quant_values(rows, w.dtype, bits, mw.group_v)
             assert_codes_equal(host(vc[bh, js]), wc[0], f"{name} value codes")
             assert_f32_bits_equal(host(vs[bh, js]), ws[0], f"{name} value scale")
+            want = O.dequant_values(wc, ws, wz, rows.shape, bits, mw.group_v, w.dtype)
+            assert_recon_equal(bits16(v_out[bh, _ix(pos[b, js])]), want[0],
+                               f"{name} value recon {bh}")
