@@ -38,7 +38,36 @@ typedef _Float16 h2x_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMChunk = 128;            // tokens per block, one per thread
-constexpr int kMaxKGroups = kMChunk / 16;
+
+// Sizes of one instantiation.  GK is the smallest key and value group the
+// instantiation serves (16, or 32 when G_k = 32 and G_v >= 32): it bounds
+// the key groups of a chunk and the value groups of a row, and so the LDS
+// that holds their operands.  kWaves: the waves per SIMD that the LDS
+// footprint allows (two waves per block, four SIMDs per CU, 160 KiB of LDS
+// per CU), capped at 5; the launch bounds ask the compiler for registers
+// that allow as many.
+template <int BITS, int D, int NQ, int GK>
+struct MfmaShape {
+    static constexpr int D8 = D / 8;
+    static constexpr int KS = D / 32;                 // k-steps over the channels
+    static constexpr int CPL = D / 4;                 // channels of a lane block
+    static constexpr int LB = CPL * BITS / 8;         // code bytes of a lane block
+    static constexpr int DW = D * BITS / 32;          // code row in dwords
+    static constexpr int MT = D / 16;                 // channel tiles (values)
+    static constexpr int KGROUPS = kMChunk / GK;      // key groups of a chunk
+    static constexpr int MAXGV = D / GK;              // value groups of a row
+    static constexpr int VKS = kMChunk / 32;          // k-steps over the tokens
+    static constexpr int kKOps = KGROUPS * 4 * NQ * KS * 2;   // uint4 key operands
+    static constexpr int kVOps = MAXGV * 4 * NQ * VKS * 2;    // uint4 value operands
+    static constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
+    static constexpr int kZero = 2 * (KS > VKS ? KS : VKS);   // zero block (uint4)
+    static constexpr int kLds =
+        NQ * D * 4 + kOps * 16 + kZero * 16 + 2 * KGROUPS * NQ * 4 +
+        NQ * kMChunk * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
+        MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
+    static constexpr int kBlocks = (160 * 1024) / kLds;
+    static constexpr int kWaves = kBlocks / 2 < 1 ? 1 : (kBlocks / 2 > 5 ? 5 : kBlocks / 2);
+};
 
 __device__ __forceinline__ h8_t as_h8(uint32_t a, uint32_t b, uint32_t c,
                                       uint32_t d) {
@@ -95,6 +124,16 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// The uint4s of operand block bi (N of them, N a power of two) are stored
+// in the order k ^ swz(bi).  A wave reads the blocks of 4 * NQ consecutive
+// bi at once, 128 bytes apart for D = 128: unpermuted, every second (or
+// fourth) block starts on the same LDS bank; with the permutation blocks
+// bi, bi + 4 and bi + 8 of one bank class read distinct 16-byte slots.
+template <int N>
+__device__ __forceinline__ int swz(int bi) {
+    return (bi >> 1) & (N - 1);
+}
+
 // An operand, or zeros when `keep` is false.
 __device__ __forceinline__ h8_t pick_op(uint4 v, bool keep) {
     return as_h8(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
@@ -128,23 +167,18 @@ __device__ __forceinline__ float widen_h(uint16_t h) {
 // 16 * 2^k channels and n_q <= NQ.
 //
 // B operands live in LDS, each lane's operands of one group contiguous:
-// keys [g][kb][j][k-step][hi, lo], values [gv][kb][j][k-step][hi, lo]
+// keys [g][kb][j][k-step][hi, lo], values [gv][kb][j][k-step][hi, lo],
+// the uint4s of each [..][kb][j] block permuted by swz
 // (uint4 = 8 halves each).  Lanes past the query heads read a zero block
 // instead (an LDS address select), so no operand needs masking.
-template <int DT, int BITS, int D, int NQ>
-__global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
-    constexpr int D8 = D / 8;
-    constexpr int KS = D / 32;                 // k-steps over the channels
-    constexpr int CPL = D / 4;                 // channels of a lane block
-    constexpr int LB = CPL * BITS / 8;         // code bytes of a lane block
-    constexpr int DW = D * BITS / 32;          // code row in dwords
-    constexpr int MT = D / 16;                 // channel tiles (values)
-    constexpr int MAXGV = D / 16;              // value groups (>= 16 channels)
-    constexpr int VKS = kMChunk / 32;          // k-steps over the tokens
-    constexpr int kKOps = kMaxKGroups * 4 * NQ * KS * 2;   // uint4 key operands
-    constexpr int kVOps = MAXGV * 4 * NQ * VKS * 2;        // uint4 value operands
-    constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
-    constexpr int kZero = 2 * (KS > VKS ? KS : VKS);       // zero block (uint4)
+template <int DT, int BITS, int D, int NQ, int GK>
+__global__ __launch_bounds__(kMChunk, (MfmaShape<BITS, D, NQ, GK>::kWaves))
+void attend_mfma_kernel(AttendArgs a) {
+    using Sh = MfmaShape<BITS, D, NQ, GK>;
+    constexpr int D8 = Sh::D8, KS = Sh::KS, CPL = Sh::CPL, LB = Sh::LB;
+    constexpr int DW = Sh::DW, MT = Sh::MT, MAXGV = Sh::MAXGV, VKS = Sh::VKS;
+    constexpr int kMaxKGroups = Sh::KGROUPS;
+    constexpr int kOps = Sh::kOps, kZero = Sh::kZero;
     static_assert(NQ * MAXGV * kMChunk <= kOps * 4, "zero-point rows fit");
 
     __shared__ __attribute__((aligned(16))) float q_s[NQ][D];
@@ -283,9 +317,11 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
                     lw[i / 2] = pack_h2(l0, l1);
                 }
                 const int d = kc8 * 8, blk = d / CPL, s = (d % CPL) / 8;
-                const int o = (((kg * 4 + blk) * NQ + j) * KS + s) * 2;
-                ops_s[o] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                ops_s[o + 1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                const int bi = (kg * 4 + blk) * NQ + j;
+                uint4* ob = ops_s + bi * (2 * KS);
+                const int sw = swz<2 * KS>(bi);
+                ob[(2 * s) ^ sw] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                ob[(2 * s + 1) ^ sw] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
                 if (kc8 == 0) {
                     kbias_s[kg][j] = b;
                     kexp_s[kg][j] = e;
@@ -301,7 +337,9 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
         const int tok0 = (wave + 2 * tt) * 16;
         if (tok0 >= nq_tok) break;             // wave-uniform
         const int g = tok0 >> gk_sh;
-        const uint4* bp = m16 < NQ ? ops_s + (((g * 4 + kb) * NQ + m16) * KS) * 2 : zero_s;
+        const int bi = (g * 4 + kb) * NQ + m16;
+        const uint4* bp = m16 < NQ ? ops_s + bi * (2 * KS) : zero_s;
+        const int sw = swz<2 * KS>(bi);
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -311,9 +349,9 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
             if constexpr (SB < 32) bits &= (1u << SB) - 1u;
             const h8_t A = codes8<BITS>(bits);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[(2 * s) ^ sw]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s + 1]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[(2 * s + 1) ^ sw]), acc, 0, 0, 0);
         }
         if (m16 < NQ) {
             const int e = kexp_s[g][m16];
@@ -349,10 +387,16 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
 
     // ---- softmax partial of the chunk: eight lanes per head find the max,
     // then every thread takes its token's p, then eight lanes per head sum
+    // (rows are 512 bytes apart, so each row's lanes start at another eight
+    // banks: lane i of row j reads t = i + 8 ((u + j) mod 16) at step u)
     if (tid < 8 * NQ) {
         const int j = tid >> 3;
         float v = -__builtin_huge_valf();
-        for (int t = tid & 7; t < nt; t += 8) v = fmaxf(v, p_s[j][t] * a.sm_scale);
+#pragma unroll 4
+        for (int u = 0; u < kMChunk / 8; ++u) {
+            const int t = (tid & 7) + 8 * ((u + j) & (kMChunk / 8 - 1));
+            if (t < nt) v = fmaxf(v, p_s[j][t] * a.sm_scale);
+        }
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
         if ((tid & 7) == 0) ml_s[0][j] = v;
@@ -410,13 +454,16 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
         for (int j = 0; j < NQ; ++j) q_s[j][tid] = o[j];
     }
     // eight lanes per row: the sums of p (per head) and of p * zero, and the
-    // maxima of the value scales
+    // maxima of the value scales (rotated starts as above: the eight rows a
+    // wave reads at once sit in distinct banks)
     const int n_sum = NQ + NQ * ngd;
     for (int k = tid >> 3; k < n_sum + ngd; k += kMChunk / 8) {
         if (k < n_sum) {
             const float* row = k < NQ ? p_s[k] : zrows + (k - NQ) * kMChunk;
             float v = 0.0f;
-            for (int t = tid & 7; t < kMChunk; t += 8) v += row[t];
+#pragma unroll 4
+            for (int u = 0; u < kMChunk / 8; ++u)
+                v += row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))];
 #pragma unroll
             for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o);
             if ((tid & 7) == 0) {
@@ -426,7 +473,9 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
         } else {
             const float* row = sv_s[k - n_sum];
             float v = 0.0f;
-            for (int t = tid & 7; t < kMChunk; t += 8) v = fmaxf(v, row[t]);
+#pragma unroll 4
+            for (int u = 0; u < kMChunk / 8; ++u)
+                v = fmaxf(v, row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))]);
 #pragma unroll
             for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
             if ((tid & 7) == 0) vmax_s[k - n_sum] = v;
@@ -445,9 +494,10 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
             for (int j = 0; j < NQ; ++j) {
                 _Float16 hi, lo;
                 split16(__builtin_ldexpf(pt[j] * sv, e), hi, lo);
-                const int o = (((gv * 4 + blk) * NQ + j) * VKS + s4) * 2;
-                vops[o * 8 + i] = hi;
-                vops[(o + 1) * 8 + i] = lo;
+                const int bi = (gv * 4 + blk) * NQ + j, sw = swz<2 * VKS>(bi);
+                _Float16* vb = vops + bi * (2 * VKS) * 8;
+                vb[((2 * s4) ^ sw) * 8 + i] = hi;
+                vb[((2 * s4 + 1) ^ sw) * 8 + i] = lo;
             }
         }
     }
@@ -459,7 +509,9 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
         const int gv = (mt * 16) >> gv_sh;
         const int ch = mt * 16 + m16;                   // this lane's A row
         const int wd = (ch * BITS) / 32, sh = (ch * BITS) % 32;
-        const uint4* bp = m16 < NQ ? ops_s + (((gv * 4 + kb) * NQ + m16) * VKS) * 2 : zero_s;
+        const int bi = (gv * 4 + kb) * NQ + m16;
+        const uint4* bp = m16 < NQ ? ops_s + bi * (2 * VKS) : zero_s;
+        const int sw = swz<2 * VKS>(bi);
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s4 = 0; s4 < VKS; ++s4) {
@@ -474,9 +526,9 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
                 pr[k] = pair_f16(((dw[2 * k] >> sh) & M) | (((dw[2 * k + 1] >> sh) & M) << 16));
             const h8_t A = as_h8(pr[0], pr[1], pr[2], pr[3]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s4]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[(2 * s4) ^ sw]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s4 + 1]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[(2 * s4 + 1) ^ sw]), acc, 0, 0, 0);
         }
         // C: lane (head m16, row block kb) holds channels mt*16 + 4 kb + i
         if (m16 < nq) {
@@ -499,9 +551,12 @@ __global__ __launch_bounds__(kMChunk) void attend_mfma_kernel(AttendArgs a) {
 template <int DT, int BITS, int D, int NQ>
 static hipError_t launch_mfma_t(const AttendArgs& a, int64_t BH, int n_full,
                                 hipStream_t stream) {
-    return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ>),
-                         dim3((uint32_t)n_full, (uint32_t)BH), dim3(kMChunk), 0,
-                         stream, a);
+    const dim3 grid((uint32_t)n_full, (uint32_t)BH), block(kMChunk);
+    if (a.G_k == 32 && a.G_v >= 32)
+        return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 32>), grid,
+                             block, 0, stream, a);
+    return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 16>), grid,
+                         block, 0, stream, a);
 }
 
 template <int DT, int BITS, int D>
