@@ -44,8 +44,8 @@ constexpr int kMChunk = 128;            // tokens per block, one per thread
 // the key groups of a chunk and the value groups of a row, and so the LDS
 // that holds their operands.  kWaves: the waves per SIMD that the LDS
 // footprint allows (two waves per block, four SIMDs per CU, 160 KiB of LDS
-// per CU), capped at 5; the launch bounds ask the compiler for registers
-// that allow as many.
+// per CU), capped at 5 (4 for 4-bit codes); the launch bounds ask the
+// compiler for registers that allow as many.
 template <int BITS, int D, int NQ, int GK>
 struct MfmaShape {
     static constexpr int D8 = D / 8;
@@ -66,7 +66,9 @@ struct MfmaShape {
         NQ * kMChunk * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
-    static constexpr int kWaves = kBlocks / 2 < 1 ? 1 : (kBlocks / 2 > 5 ? 5 : kBlocks / 2);
+    // 4-bit codes hold twice the key code registers: at most 4 waves there
+    static constexpr int kCap = BITS == 4 ? 4 : 5;
+    static constexpr int kWaves = kBlocks / 2 < 1 ? 1 : (kBlocks / 2 > kCap ? kCap : kBlocks / 2);
 };
 
 __device__ __forceinline__ h8_t as_h8(uint32_t a, uint32_t b, uint32_t c,
@@ -110,6 +112,14 @@ __device__ __forceinline__ int op_exp(float P) {
     // which still keeps P * 2^e below 2^14)
     const int lg = (int)((__float_as_uint(P) >> 23) & 0xffu) - 127;
     return 13 - lg;
+}
+
+// (x & m) | c in one instruction, with m and c held in registers (a VOP3
+// instruction here reads at most one scalar or constant operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+    return r;
 }
 
 // x = hi + lo with hi = RN16(x) and lo = RN16(x - hi).
@@ -187,7 +197,12 @@ void attend_mfma_kernel(AttendArgs a) {
     __shared__ float kbias_s[kMaxKGroups][NQ];
     __shared__ int kexp_s[kMaxKGroups][NQ];
     __shared__ __attribute__((aligned(16))) float p_s[NQ][kMChunk];
-    __shared__ __attribute__((aligned(16))) uint32_t vc_s[DW][kMChunk];
+    // value codes by token pair: row q holds, for each pair of tokens
+    // (2P, 2P + 1), the q-th 16 bits of each token's code row, the even
+    // token's in the low half (rows padded to 68 dwords, which keeps the
+    // two writers of a pair off one bank)
+    constexpr int kVpStride = kMChunk / 2 + 4;
+    __shared__ __attribute__((aligned(16))) uint32_t vp_s[2 * DW][kVpStride];
     __shared__ __attribute__((aligned(16))) float sv_s[MAXGV][kMChunk];
     __shared__ float vmax_s[MAXGV];
     __shared__ float zsum_s[NQ * MAXGV];
@@ -401,10 +416,25 @@ void attend_mfma_kernel(AttendArgs a) {
         for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
         if ((tid & 7) == 0) ml_s[0][j] = v;
     }
-    // value codes and value scales of this thread's token, transposed into
-    // LDS
+    // value codes (by token pair) and value scales of this thread's token
+    // into LDS
+    {
+        // the even thread of a pair writes rows of words [0, DW/2), the odd
+        // one rows of words [DW/2, DW); each first swaps with its partner
+        // the words the partner needs (DW >= 4 on this path)
+        const bool even = (tid & 1) == 0;
+        const uint32_t sel_lo = even ? 0x05040100u : 0x01000504u;
+        const uint32_t sel_hi = even ? 0x07060302u : 0x03020706u;
+        uint32_t* row = &vp_s[even ? 0 : DW][tid >> 1];
 #pragma unroll
-    for (int k = 0; k < DW; ++k) vc_s[k][tid] = vw[k];
+        for (int k = 0; k < DW / 2; ++k) {
+            const uint32_t lo_w = vw[k], hi_w = vw[k + DW / 2];   // static indices
+            const uint32_t mine = even ? lo_w : hi_w;
+            const uint32_t other = (uint32_t)__shfl_xor((int)(even ? hi_w : lo_w), 1);
+            row[(2 * k) * kVpStride] = __builtin_amdgcn_perm(other, mine, sel_lo);
+            row[(2 * k + 1) * kVpStride] = __builtin_amdgcn_perm(other, mine, sel_hi);
+        }
+    }
 #pragma unroll
     for (int gv = 0; gv < MAXGV; ++gv)
         if (gv < ngd) sv_s[gv][tid] = svv[gv];
@@ -508,22 +538,27 @@ void attend_mfma_kernel(AttendArgs a) {
     for (int mt = wave; mt < MT; mt += 2) {
         const int gv = (mt * 16) >> gv_sh;
         const int ch = mt * 16 + m16;                   // this lane's A row
-        const int wd = (ch * BITS) / 32, sh = (ch * BITS) % 32;
+        const int q = (ch * BITS) / 16, sh = (ch * BITS) % 16;
+        const uint32_t pmask = ((1u << BITS) - 1u) * 0x10001u;
         const int bi = (gv * 4 + kb) * NQ + m16;
         const uint4* bp = m16 < NQ ? ops_s + bi * (2 * VKS) : zero_s;
         const int sw = swz<2 * VKS>(bi);
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s4 = 0; s4 < VKS; ++s4) {
-            const int T0 = s4 * 32 + kb * 8;
-            const uint4 d0 = *reinterpret_cast<const uint4*>(&vc_s[wd][T0]);
-            const uint4 d1 = *reinterpret_cast<const uint4*>(&vc_s[wd][T0 + 4]);
-            const uint32_t dw[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+            // tokens s4*32 + kb*8 + [0, 8) are pairs P0 .. P0 + 3, each dword
+            // holding this channel's two codes sh bits up in its two halves
+            const int P0 = s4 * 16 + kb * 4;
+            const uint4 d = *reinterpret_cast<const uint4*>(&vp_s[q][P0]);
+            const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
             constexpr uint32_t M = (1u << BITS) - 1u;
+            const h2x_t one_k = {(_Float16)1024.0f, (_Float16)1024.0f};
             uint32_t pr[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                pr[k] = pair_f16(((dw[2 * k] >> sh) & M) | (((dw[2 * k + 1] >> sh) & M) << 16));
+            for (int k = 0; k < 4; ++k) {   // as pair_f16, the mask and 0x6400s in one step
+                const uint32_t f = and_or(dw[k] >> sh, pmask, 0x64006400u);
+                pr[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2x_t, f) - one_k);
+            }
             const h8_t A = as_h8(pr[0], pr[1], pr[2], pr[3]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 A, __builtin_bit_cast(h8_t, bp[(2 * s4) ^ sw]), acc, 0, 0, 0);
