@@ -84,6 +84,14 @@ __device__ __forceinline__ uint32_t pair_f16(uint32_t c01) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// (x & m) | c in one instruction, with m and c held in registers (a VOP3
+// instruction here reads at most one scalar or constant operand).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+    return r;
+}
+
 // 8 codes held LSB-first in the low 8 * BITS bits of `bits` (higher bits
 // zero) as 8 f16 values.
 template <int BITS>
@@ -93,8 +101,12 @@ __device__ __forceinline__ h8_t codes8(uint32_t bits) {
     if constexpr (BITS <= 2) {
         // a second copy 16 - BITS bits up puts code 2k + 1 at bit 16 + 2k BITS
         const uint32_t t = bits | (bits << (16 - BITS));
+        const h2x_t one_k = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) d[k] = pair_f16((t >> (2 * k * BITS)) & (M | (M << 16)));
+        for (int k = 0; k < 4; ++k) {   // pair_f16 with the mask and 0x6400s in one step
+            const uint32_t f = and_or(t >> (2 * k * BITS), M | (M << 16), 0x64006400u);
+            d[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2x_t, f) - one_k);
+        }
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
@@ -112,14 +124,6 @@ __device__ __forceinline__ int op_exp(float P) {
     // which still keeps P * 2^e below 2^14)
     const int lg = (int)((__float_as_uint(P) >> 23) & 0xffu) - 127;
     return 13 - lg;
-}
-
-// (x & m) | c in one instruction, with m and c held in registers (a VOP3
-// instruction here reads at most one scalar or constant operand).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
-    return r;
 }
 
 // x = hi + lo with hi = RN16(x) and lo = RN16(x - hi).
