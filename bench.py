@@ -41,7 +41,7 @@ METRIC = ("effective HBM GB/s (and % of MI355X peak) for KIVI 2-bit K+V "
           "flush/dequant")
 # The kernel sources behind each family of workloads: the traffic measured
 # for a workload stays valid while these files are unchanged.
-_COMMON = ["kivi_device.h", "kivi_launch.h", "kivi_rows.h"]
+_COMMON = ["kivi_device.h", "kivi_launch.h", "kivi_rows.h", "kivi_key_split.h"]
 KERNEL_SOURCES = {
     "flush": _COMMON + ["quant_keys.hip", "quant_values.hip", "dequant.hip",
                         "generic.hip"],
@@ -93,7 +93,12 @@ def load_traffic(kernel, workload, src_hash):
 N_CODE_SETS = 4   # rotating code/param sets (see make_steps)
 
 
-def make_steps(K, w, pool_inputs, torch):
+PAIRED = {"quant_kv": ("quant_keys", "quant_values"),
+          "quant_dequant_kv": ("quant_dequant_keys", "quant_dequant_values"),
+          "dequant_kv": ("dequant_keys", "dequant_values")}
+
+
+def make_steps(K, w, pool_inputs, torch, paired=False):
     """Pre-allocated outputs and the list of (name, op, bytes, launch fn)
     that make one step.  Every launch goes to torch's current stream and
     takes the step index i.
@@ -165,13 +170,31 @@ def make_steps(K, w, pool_inputs, torch):
     out = []
     for name, op, g, fn in steps:
         out.append((name, op, bytes_per_elem(op, bits, g) * E, fn))
-    return out
+    if not paired:
+        return out
+    # the same work through the K+V calls: one launch each at these sizes
+    kv = [
+        ("quant_kv", lambda i: K.kivi_quant_kv(
+            pool_inputs[i % P][0], pool_inputs[i % P][1], bits, gk, gv,
+            qk[ws(i)], qv[ws(i)])),
+        ("quant_dequant_kv", lambda i: K.kivi_quant_dequant_kv(
+            pool_inputs[(i + 1) % P][0], pool_inputs[(i + 1) % P][1], bits, gk,
+            gv, True, rk, rv, fk, fv)),
+        ("dequant_kv", lambda i: K.kivi_dequant_kv(
+            qk[rs(i)], qv[rs(i)], bits, gk, gv, out_dtype=dt, k_out=dk,
+            v_out=dv)),
+    ]
+    byts = {name: b for name, _, b, _ in out}
+    ops = {name: op for name, op, _, _ in out}
+    return [(name, ops[PAIRED[name][0]], sum(byts[n] for n in PAIRED[name]), fn)
+            for name, fn in kv if PAIRED[name][0] in byts]
 
 
 def _oracle_step(O, w, k, v, names):
     """Every row of the step on one block of bh slices, through the oracle as
     it stands (the fused row is its quantize followed by its dequantize)."""
     ck = cv = None
+    names = [n for name in names for n in PAIRED.get(name, (name,))]
     for name in names:
         if name == "quant_keys":
             ck = O.quant_keys(k, w.dtype, w.bits, w.group_k)
@@ -1038,6 +1061,9 @@ def main():
                          "of MB megabytes (the reference kernel used to scale "
                          "rocprofv3 byte counters) and a plain read (sum)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-calls", action="store_true",
+                    help="decode/tiny: time the separate key and value calls "
+                         "instead of the K+V calls")
     ap.add_argument("--launch", choices=("auto", "graphs", "eager"),
                     default="auto",
                     help="timed steps as HIP graph replays or eager launches; "
@@ -1091,7 +1117,10 @@ def main():
             kv.append(torch.from_numpy(x.view(np.int16)).view(tdt).to(dev))
         inputs.append(tuple(kv))
 
-    steps = make_steps(K, w, inputs, torch)
+    # decode-size flushes go through the K+V calls (one launch per pair of
+    # rows); --single-calls times the separate key and value calls instead
+    paired = w.name in ("tiny", "decode") and not args.single_calls
+    steps = make_steps(K, w, inputs, torch, paired)
     step_bytes = sum(s[2] for s in steps)
     stream = torch.cuda.current_stream(dev)
 

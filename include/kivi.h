@@ -142,6 +142,41 @@ kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
                                       hipStream_t stream);
 
 /*
+ * Keys and values of one flush in one call (the 0.8.0 release post, section
+ * "What KIVI is": a flush quantizes the aged-out keys per channel and the
+ * values per token together; the KIVI blog post on the fused Metal kernels,
+ * section "What we're actually optimizing": at decode sizes the flush is
+ * launch-bound).  Each result is exactly that of the single call on that
+ * tensor (kivi_quant_keys / kivi_quant_values, kivi_quant_dequant_*,
+ * kivi_dequant_*), with group_k for keys and group_v for values.  K and V
+ * share dtype, shape and bits; every argument of both halves is checked by
+ * the single call's rules before anything is launched, and codes/params
+ * must be given for both tensors or (kivi_quant_dequant_kv) for neither.
+ * Small flushes (keys in groups of 17 to 32 tokens with fewer than 65536
+ * (bh, group, 8-channel) items, D/8 dividing 16, value groups of 32 * 2^k
+ * channels, or for the dequantizer any multiple of 32) run as one kernel
+ * launch; otherwise the two single launches are issued, keys first.
+ */
+kivi_status kivi_quant_kv(const void* k, const void* v, kivi_dtype dt,
+                          int64_t BH, int64_t S, int64_t D, int bits,
+                          int64_t group_k, int64_t group_v, uint8_t* k_codes,
+                          float* k_scale, float* k_zero, uint8_t* v_codes,
+                          float* v_scale, float* v_zero, hipStream_t stream);
+kivi_status kivi_quant_dequant_kv(const void* k, const void* v, kivi_dtype dt,
+                                  int64_t BH, int64_t S, int64_t D, int bits,
+                                  int64_t group_k, int64_t group_v,
+                                  uint8_t* k_codes, float* k_scale,
+                                  float* k_zero, uint8_t* v_codes,
+                                  float* v_scale, float* v_zero, void* k_recon,
+                                  void* v_recon, hipStream_t stream);
+kivi_status kivi_dequant_kv(const uint8_t* k_codes, const float* k_scale,
+                            const float* k_zero, const uint8_t* v_codes,
+                            const float* v_scale, const float* v_zero,
+                            int64_t BH, int64_t S, int64_t D, int bits,
+                            int64_t group_k, int64_t group_v, kivi_dtype out_dt,
+                            void* k_out, void* v_out, hipStream_t stream);
+
+/*
  * Residual-window cache (KIVI blog post on the fused Metal kernels, section
  * "What we're actually optimizing": the most recent residual_length tokens
  * stay in 16-bit floats and, once enough fresh tokens have accumulated, are

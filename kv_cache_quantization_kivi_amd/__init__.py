@@ -78,9 +78,13 @@ def _load():
     dq = [P, P, P, I64, I64, I64, I, I64, I, P, P]
     L.kivi_dequant_keys.argtypes = dq
     L.kivi_dequant_values.argtypes = dq
+    L.kivi_quant_kv.argtypes = [P, P, I, I64, I64, I64, I, I64, I64] + [P] * 7
+    L.kivi_quant_dequant_kv.argtypes = [P, P, I, I64, I64, I64, I, I64, I64] + [P] * 9
+    L.kivi_dequant_kv.argtypes = [P] * 6 + [I64, I64, I64, I, I64, I64, I, P, P, P]
     for name in ("kivi_quant_keys", "kivi_quant_values",
                  "kivi_quant_dequant_keys", "kivi_quant_dequant_values",
-                 "kivi_dequant_keys", "kivi_dequant_values"):
+                 "kivi_dequant_keys", "kivi_dequant_values", "kivi_quant_kv",
+                 "kivi_quant_dequant_kv", "kivi_dequant_kv"):
         getattr(L, name).restype = I
     L.kivi_time_next_launch.argtypes = [P, P]
     L.kivi_time_next_launch.restype = None
@@ -286,6 +290,81 @@ def kivi_dequant_values(codes, scale, zero, bits=2, group=32,
     """Value dequantization -> [..., S, D] of out_dtype."""
     return _dequant("kivi_dequant_values", False, codes, scale, zero, bits,
                     group, out_dtype, out, stream)
+
+
+def _same_kv(k, v):
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("keys and values must share shape and dtype")
+
+
+def kivi_quant_kv(k, v, bits=2, group_k=32, group_v=32, k_out=None,
+                  v_out=None, stream=None):
+    """Keys and values of one flush in one call (one launch for small
+    flushes) -> ((k_codes, k_scale, k_zero), (v_codes, v_scale, v_zero)).
+    k_out / v_out: optional preallocated (codes, scale, zero) triples."""
+    _same_kv(k, v)
+    BH, S, D, _ = _bsd(k)
+    if group_k < 1 or group_v < 1:
+        _check(4, "kivi_quant_kv")
+    kq = _alloc_quant(k, True, bits, group_k, *(k_out or (None,) * 3))
+    vq = _alloc_quant(v, False, bits, group_v, *(v_out or (None,) * 3))
+    st = _lib().kivi_quant_kv(_ptr(k), _ptr(v), _dtype_code(k.dtype), BH, S, D,
+                              bits, group_k, group_v, *map(_ptr, kq),
+                              *map(_ptr, vq), _stream(k.device, stream))
+    _check(st, "kivi_quant_kv")
+    return kq, vq
+
+
+def kivi_quant_dequant_kv(k, v, bits=2, group_k=32, group_v=32,
+                          with_codes=True, k_recon=None, v_recon=None,
+                          k_out=None, v_out=None, stream=None):
+    """Fused quantize -> dequantize of keys and values in one call ->
+    (k_recon, v_recon[, (k codes, scale, zero), (v codes, scale, zero)])."""
+    _same_kv(k, v)
+    BH, S, D, _ = _bsd(k)
+    if group_k < 1 or group_v < 1:
+        _check(4, "kivi_quant_dequant_kv")
+    k_recon = torch.empty_like(k) if k_recon is None else k_recon
+    v_recon = torch.empty_like(v) if v_recon is None else v_recon
+    if with_codes:
+        kq = _alloc_quant(k, True, bits, group_k, *(k_out or (None,) * 3))
+        vq = _alloc_quant(v, False, bits, group_v, *(v_out or (None,) * 3))
+    else:
+        kq = vq = (None, None, None)
+    st = _lib().kivi_quant_dequant_kv(
+        _ptr(k), _ptr(v), _dtype_code(k.dtype), BH, S, D, bits, group_k,
+        group_v, *map(_ptr, kq), *map(_ptr, vq), _ptr(k_recon), _ptr(v_recon),
+        _stream(k.device, stream))
+    _check(st, "kivi_quant_dequant_kv")
+    return (k_recon, v_recon, kq, vq) if with_codes else (k_recon, v_recon)
+
+
+def kivi_dequant_kv(kq, vq, bits=2, group_k=32, group_v=32,
+                    out_dtype=torch.float16, k_out=None, v_out=None,
+                    stream=None):
+    """Keys and values dequantized in one call from (codes, scale, zero)
+    triples -> (k, v) of out_dtype."""
+    kc, vc = kq[0], vq[0]
+    if kc.shape != vc.shape or kc.dim() < 2 or not kc.is_contiguous() \
+            or not vc.is_contiguous():
+        raise ValueError("codes must be contiguous [..., S, D*bits/8] tensors "
+                         "of one shape")
+    lead = tuple(kc.shape[:-2])
+    S = kc.shape[-2]
+    D = kc.shape[-1] * 8 // bits if bits in (1, 2, 4, 8) else 0
+    BH = 1
+    for n in lead:
+        BH *= n
+    if k_out is None:
+        k_out = torch.empty(lead + (S, D), dtype=out_dtype, device=kc.device)
+    if v_out is None:
+        v_out = torch.empty(lead + (S, D), dtype=out_dtype, device=kc.device)
+    st = _lib().kivi_dequant_kv(*map(_ptr, kq), *map(_ptr, vq), BH, S, D, bits,
+                                group_k, group_v, _dtype_code(k_out.dtype),
+                                _ptr(k_out), _ptr(v_out),
+                                _stream(kc.device, stream))
+    _check(st, "kivi_dequant_kv")
+    return k_out, v_out
 
 
 # --------------------------------------------------------------------------

@@ -149,14 +149,14 @@ constexpr int kDqRecWaveBytes = 64 * kDqRecLaneStride;
 // lp: log2 of lanes per row P; vec: D % 32 == 0 (a lane's codes are one
 // naturally aligned load); tile: D / 32 is a power of two (a wave's recon is
 // one contiguous 4 KiB block).
+// u: the lane's index over all lanes of the launch (blocks of 256 lanes);
+// lds: the block's 4 * kDqRecWaveBytes staging bytes.
 template <int DT, int BITS, int GPL>
-__global__ __launch_bounds__(256) void dequant_values_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-    const float* __restrict__ zero, int64_t n_rows, uint32_t D8, uint32_t lp,
-    uint32_t G8, uint32_t NGD, int32_t vec, int32_t tile,
-    uint16_t* __restrict__ out) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDqRecWaveBytes];
-    const uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+__device__ __forceinline__ void dequant_values_body(
+    uint64_t u, uint8_t* lds, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, const float* __restrict__ zero,
+    int64_t n_rows, uint32_t D8, uint32_t lp, uint32_t G8, uint32_t NGD,
+    int32_t vec, int32_t tile, uint16_t* __restrict__ out) {
     const uint32_t c = (uint32_t)(u & ((1u << lp) - 1u));
     const int64_t row = (int64_t)(u >> lp);
     const bool row_ok = row < n_rows;
@@ -247,6 +247,18 @@ __global__ __launch_bounds__(256) void dequant_values_kernel(
     }
 }
 
+template <int DT, int BITS, int GPL>
+__global__ __launch_bounds__(256) void dequant_values_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+    const float* __restrict__ zero, int64_t n_rows, uint32_t D8, uint32_t lp,
+    uint32_t G8, uint32_t NGD, int32_t vec, int32_t tile,
+    uint16_t* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDqRecWaveBytes];
+    dequant_values_body<DT, BITS, GPL>((uint64_t)blockIdx.x * 256u + threadIdx.x,
+                                       lds, codes, scale, zero, n_rows, D8, lp,
+                                       G8, NGD, vec, tile, out);
+}
+
 // Small dequantizations (a decode-time flush) have too few (bh, group,
 // chunk) items to fill the GPU, and one lane storing a whole group is then
 // the latency.  Here each item is split over SPLIT lanes, interleaved: part
@@ -256,12 +268,13 @@ __global__ __launch_bounds__(256) void dequant_values_kernel(
 constexpr int kDqKeySplit = 4;
 constexpr uint64_t kDqKeySplitBelow = 256ull * 256ull;
 
+// lid: the lane's index over all lanes of the launch (waves 64-aligned).
 template <int DT, int BITS>
-__global__ __launch_bounds__(64) void dequant_keys_split_kernel(
-    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
-    const float* __restrict__ zero, uint32_t n_lanes, uint32_t D8,
-    uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out) {
-    const uint32_t lid = blockIdx.x * 64u + threadIdx.x;
+__device__ __forceinline__ void dequant_keys_split_body(
+    uint32_t lid, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scale, const float* __restrict__ zero,
+    uint32_t n_lanes, uint32_t D8, uint32_t NG, int32_t S, int32_t G,
+    uint16_t* __restrict__ out) {
     if (lid >= n_lanes) return;
     const uint32_t c = lid % D8;
     const uint32_t part = (lid / D8) % kDqKeySplit;
@@ -300,6 +313,15 @@ __global__ __launch_bounds__(64) void dequant_keys_split_kernel(
                 store16_nt(dst + (int64_t)(t0 + u) * rs,
                            dequant_chunk<DT, BITS>(q[u], sc, z));
     }
+}
+
+template <int DT, int BITS>
+__global__ __launch_bounds__(64) void dequant_keys_split_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+    const float* __restrict__ zero, uint32_t n_lanes, uint32_t D8,
+    uint32_t NG, int32_t S, int32_t G, uint16_t* __restrict__ out) {
+    dequant_keys_split_body<DT, BITS>(blockIdx.x * 64u + threadIdx.x, codes,
+                                      scale, zero, n_lanes, D8, NG, S, G, out);
 }
 
 template <int DT, int BITS>
@@ -384,6 +406,84 @@ hipError_t launch_dequant_values(const DequantJob& j) {
     if (j.D % 8 != 0 || !grp_ok || j.D > 2048 || j.BH * j.S >= (1ll << 40))
         return launch_generic_dequant(j, false);
     KIVI_DISPATCH_DQ(launch_dq_values_t, j);
+}
+
+// ---- keys and values of a small flush in one launch --------------------
+
+// Blocks [0, v_blocks) run the value body (groups of 32 * k channels), the
+// rest the 4-lane split key body on 256 lanes per block.
+template <int DT, int BITS>
+__global__ __launch_bounds__(256) void dequant_kv_kernel(
+    const uint8_t* __restrict__ kc, const float* __restrict__ ks,
+    const float* __restrict__ kz, uint32_t k_lanes, uint32_t D8, uint32_t NG,
+    int32_t S, int32_t G, uint16_t* __restrict__ kout,
+    const uint8_t* __restrict__ vc, const float* __restrict__ vs,
+    const float* __restrict__ vz, int64_t n_rows, uint32_t lp, uint32_t G8,
+    uint32_t NGD, int32_t vec, int32_t tile, uint16_t* __restrict__ vout,
+    uint32_t v_blocks) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kDqRecWaveBytes];
+    if (blockIdx.x < v_blocks)
+        dequant_values_body<DT, BITS, 1>((uint64_t)blockIdx.x * 256u + threadIdx.x,
+                                         lds, vc, vs, vz, n_rows, D8, lp, G8, NGD,
+                                         vec, tile, vout);
+    else
+        dequant_keys_split_body<DT, BITS>((blockIdx.x - v_blocks) * 256u + threadIdx.x,
+                                          kc, ks, kz, k_lanes, D8, NG, S, G, kout);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_dq_kv_t(const DequantJob& k, const DequantJob& v) {
+    const uint32_t D8 = (uint32_t)(k.D / 8);
+    const uint32_t NG = (uint32_t)((k.S + k.group - 1) / k.group);
+    const uint64_t k_lanes = (uint64_t)k.BH * NG * D8 * kDqKeySplit;
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t NGD = (uint32_t)((v.D + v.group - 1) / v.group);
+    const int64_t n_rows = v.BH * v.S;
+    const uint64_t v_lanes = (uint64_t)n_rows << lp;
+    const uint32_t v_blocks = (uint32_t)((v_lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const int32_t tile = vec && (1u << lp) == lpr;
+    const uint32_t blocks = v_blocks + (uint32_t)((k_lanes + 255) / 256);
+    return launch_kernel((dequant_kv_kernel<DT, BITS>), dim3(blocks), dim3(256),
+                         0, k.stream, k.codes, k.scale, k.zero, (uint32_t)k_lanes,
+                         D8, NG, (int32_t)k.S, (int32_t)k.group,
+                         static_cast<uint16_t*>(k.out), v.codes, v.scale, v.zero,
+                         n_rows, lp, (uint32_t)(v.group / 8), NGD, vec, tile,
+                         static_cast<uint16_t*>(v.out), v_blocks);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_dq_kv_pair(const DequantJob& k, const DequantJob& v) {
+    return launch_dq_kv_t<DT, BITS>(k, v);
+}
+
+// The caller has validated both jobs (same shape, bits and output dtype).
+// One launch when the keys take the split kernel and the value groups are
+// multiples of 32 channels; otherwise the two single launches, keys first.
+hipError_t launch_dequant_kv(const DequantJob& k, const DequantJob& v) {
+    const uint64_t D8 = (uint64_t)(k.D / 8);
+    const uint64_t items = (uint64_t)k.BH * ((k.S + k.group - 1) / k.group) * D8;
+    const bool pair = k.D % 8 == 0 && k.D <= 2048 && items < kDqKeySplitBelow &&
+                      k.S < (1ll << 31) && v.group % 32 == 0;
+    if (!pair) {
+        const hipError_t e = launch_dequant_keys(k);
+        return e != hipSuccess ? e : launch_dequant_values(v);
+    }
+    if (k.out_dtype == DT_F16) {
+        switch (k.bits) {
+            case 1: return launch_dq_kv_pair<DT_F16, 1>(k, v);
+            case 2: return launch_dq_kv_pair<DT_F16, 2>(k, v);
+            case 4: return launch_dq_kv_pair<DT_F16, 4>(k, v);
+            default: return launch_dq_kv_pair<DT_F16, 8>(k, v);
+        }
+    }
+    switch (k.bits) {
+        case 1: return launch_dq_kv_pair<DT_BF16, 1>(k, v);
+        case 2: return launch_dq_kv_pair<DT_BF16, 2>(k, v);
+        case 4: return launch_dq_kv_pair<DT_BF16, 4>(k, v);
+        default: return launch_dq_kv_pair<DT_BF16, 8>(k, v);
+    }
 }
 
 }  // namespace kivi

@@ -415,6 +415,78 @@ kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
                  recon, true, stream);
 }
 
+// Both halves of a K+V call checked (each by the single call's rules)
+// before anything is launched.
+static kivi_status quant_kv(const void* k, const void* v, kivi_dtype dt,
+                            int64_t BH, int64_t S, int64_t D, int bits,
+                            int64_t group_k, int64_t group_v, uint8_t* kc,
+                            float* ks, float* kz, uint8_t* vc, float* vs,
+                            float* vz, void* kr, void* vr, bool fused,
+                            hipStream_t stream) {
+    bool ek = false, ev = false;
+    kivi_status st = check_quant(k, dt, BH, S, D, bits, group_k, kc, ks, kz, kr,
+                                 !fused, fused, fused, &ek);
+    if (st != KIVI_OK) return st;
+    st = check_quant(v, dt, BH, S, D, bits, group_v, vc, vs, vz, vr, !fused,
+                     fused, fused, &ev);
+    if (st != KIVI_OK) return st;
+    if ((kc == nullptr) != (vc == nullptr)) return KIVI_ERR_NULL;
+    if (ek) return KIVI_OK;   // same shape: both empty
+    kivi::QuantJob jk{k, (int)dt, BH, S, D, bits, group_k, kc, ks, kz,
+                      fused ? kr : nullptr, stream};
+    kivi::QuantJob jv{v, (int)dt, BH, S, D, bits, group_v, vc, vs, vz,
+                      fused ? vr : nullptr, stream};
+    return launched(kivi::launch_quant_kv(jk, jv));
+}
+
+kivi_status kivi_quant_kv(const void* k, const void* v, kivi_dtype dt,
+                          int64_t BH, int64_t S, int64_t D, int bits,
+                          int64_t group_k, int64_t group_v, uint8_t* k_codes,
+                          float* k_scale, float* k_zero, uint8_t* v_codes,
+                          float* v_scale, float* v_zero, hipStream_t stream) {
+    return quant_kv(k, v, dt, BH, S, D, bits, group_k, group_v, k_codes,
+                    k_scale, k_zero, v_codes, v_scale, v_zero, nullptr, nullptr,
+                    false, stream);
+}
+
+kivi_status kivi_quant_dequant_kv(const void* k, const void* v, kivi_dtype dt,
+                                  int64_t BH, int64_t S, int64_t D, int bits,
+                                  int64_t group_k, int64_t group_v,
+                                  uint8_t* k_codes, float* k_scale,
+                                  float* k_zero, uint8_t* v_codes,
+                                  float* v_scale, float* v_zero, void* k_recon,
+                                  void* v_recon, hipStream_t stream) {
+    return quant_kv(k, v, dt, BH, S, D, bits, group_k, group_v, k_codes,
+                    k_scale, k_zero, v_codes, v_scale, v_zero, k_recon, v_recon,
+                    true, stream);
+}
+
+kivi_status kivi_dequant_kv(const uint8_t* k_codes, const float* k_scale,
+                            const float* k_zero, const uint8_t* v_codes,
+                            const float* v_scale, const float* v_zero,
+                            int64_t BH, int64_t S, int64_t D, int bits,
+                            int64_t group_k, int64_t group_v, kivi_dtype out_dt,
+                            void* k_out, void* v_out, hipStream_t stream) {
+    kivi_status st = check_shape(BH, S, D, bits, group_k);
+    if (st != KIVI_OK) return st;
+    st = check_shape(BH, S, D, bits, group_v);
+    if (st != KIVI_OK) return st;
+    if (!dtype_ok(out_dt)) return KIVI_ERR_DTYPE;
+    if (empty(BH, S, D)) return KIVI_OK;
+    if (!k_codes || !k_scale || !k_zero || !k_out || !v_codes || !v_scale ||
+        !v_zero || !v_out)
+        return KIVI_ERR_NULL;
+    if (!aligned16(k_codes) || !aligned16(k_scale) || !aligned16(k_zero) ||
+        !aligned16(k_out) || !aligned16(v_codes) || !aligned16(v_scale) ||
+        !aligned16(v_zero) || !aligned16(v_out))
+        return KIVI_ERR_ALIGN;
+    kivi::DequantJob jk{k_codes, k_scale, k_zero, BH, S, D, bits, group_k,
+                        (int)out_dt, k_out, stream};
+    kivi::DequantJob jv{v_codes, v_scale, v_zero, BH, S, D, bits, group_v,
+                        (int)out_dt, v_out, stream};
+    return launched(kivi::launch_dequant_kv(jk, jv));
+}
+
 kivi_status kivi_dequant_keys(const uint8_t* codes, const float* scale,
                               const float* zero, int64_t BH, int64_t S,
                               int64_t D, int bits, int64_t group,

@@ -177,6 +177,10 @@ hipError_t launch_quant_keys(const QuantJob& j);
 hipError_t launch_quant_values(const QuantJob& j);
 hipError_t launch_dequant_keys(const DequantJob& j);
 hipError_t launch_dequant_values(const DequantJob& j);
+// Keys and values of one flush (validated, same shape, dtype and bits):
+// one launch for small flushes, else the two single launches.
+hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v);
+hipError_t launch_dequant_kv(const DequantJob& k, const DequantJob& v);
 hipError_t launch_cache_flush_keys(const CacheFlushJob& j);
 hipError_t launch_cache_flush_values(const CacheFlushJob& j);
 // Copy tokens [s_first, T + n_in) of the appended keys and values into

@@ -19,6 +19,7 @@
 #include "kivi_device.h"
 #include "kivi_launch.h"
 #include "kivi_rows.h"
+#include "kivi_key_split.h"
 
 namespace kivi {
 
@@ -193,145 +194,20 @@ __global__ __launch_bounds__(256) void quant_keys_kernel(
         emit_rolled<DT, BITS, WQ, WR, false>(src, pk, nt, dst, row_bytes, rdst, D);
 }
 
-// Small flushes (a decode-time flush of a few dozen tokens per head) have
-// too few (bh, token group, chunk) items to fill the GPU, and one lane
-// working through a whole group is then the latency.  This variant gives the
-// chunk of a group to SPLIT lanes of one wave, TPL = GMAX / SPLIT tokens
-// each, interleaved: lane part p takes tokens p, p + SPLIT, p + 2 SPLIT, ...
-// Lanes are laid out channel chunk fastest, then part, so one load or store
-// instruction covers SPLIT consecutive rows of a tile, and the SPLIT lanes
-// of a group are D8 lanes apart, where their min/max meet through xor
-// shuffles; then every lane codes its own tokens.  A lane's token index is
-// clamped to the group's last token (the edge padding), so lanes of a
-// ragged group load in bounds and store only real tokens.  Lanes past the
-// end mirror the last lane; items come in whole groups of D8*SPLIT lanes
-// aligned inside the wave, so they only ever meet each other.
-// Code and store a lane's first n tokens; token t's code row is at
-// dst + t * cstride bytes and its recon row at rdst + t * rstride elements.
-// With SINKS, bit t of `sinks` marks the lane's token t as a sink: code 0,
-// and its own row as the reconstruction.
-template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL, bool SINKS>
-__device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
-                                           const Params (&pk)[8], int32_t n,
-                                           uint8_t* dst, int64_t cstride,
-                                           uint16_t* rdst, int64_t rstride,
-                                           uint32_t sinks) {
-#pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-        if (t < n) {
-            uint4 r;
-            uint64_t q = quant_chunk<DT, BITS, FAST, WR>(v[t], pk, &r);
-            if constexpr (SINKS) {
-                if ((sinks >> t) & 1u) {
-                    q = 0;
-                    r = v[t];
-                }
-            }
-            if constexpr (WQ) store_codes<BITS>(dst + t * cstride, q);
-            if constexpr (WR) store16_nt(rdst + t * rstride, r);
-        }
-    }
-}
-
-// IO: the row layout (DenseRows, CacheRows or ListRows, kivi_rows.h); NG here is the
-// number of groups per bh that this launch quantizes.
+// The split variant for small flushes (its lane body: kivi_key_split.h).
 template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV,
           typename IO>
 __global__ __launch_bounds__(64) void quant_keys_split_kernel(
     IO io, uint32_t n_lanes, uint32_t D8, uint32_t NG,
     uint8_t* __restrict__ codes, float* __restrict__ scale,
     float* __restrict__ zero, uint16_t* __restrict__ recon) {
-    const uint32_t gid = blockIdx.x * 64u + threadIdx.x;
-    const bool valid = gid < n_lanes;
-    const uint32_t lid = valid ? gid : n_lanes - 1u;
-    const uint32_t c = lid % D8;
-    const uint32_t part = (lid / D8) % SPLIT;
-    const uint32_t tile = lid / (D8 * SPLIT);
-    const uint32_t g = tile % NG;
-    const uint32_t bh = tile / NG;
-    const int32_t s0 = io.first(g);
-    const int32_t nt = io.count(s0);
-    const int64_t D = (int64_t)D8 * 8;
-
-    const auto rows = io.tile(bh, s0, D);
-    uint4 v[TPL];
-    uint32_t lane_sinks = 0;   // bit t: this lane's token t is a sink
-    uint32_t group_sinks = 0;  // bit t: token s0 + t is a sink
-    if constexpr (IO::kSinks) group_sinks = io.sink_mask(bh, s0, nt);
-#pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-        const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
-                                   : (int32_t)part * TPL + t, nt - 1);
-        v[t] = load16_nt(rows.row(tt, D) + (int64_t)c * 8);
-        if constexpr (IO::kSinks) lane_sinks |= ((group_sinks >> tt) & 1u) << t;
-    }
-
-    // A sink takes no part in the min/max: it is replaced there by the
-    // group's first token that is not a sink (a duplicate changes neither).
-    uint4 fill = v[0];
-    bool no_tokens = false;    // every token of the group is a sink
-    if constexpr (IO::kSinks) {
-        const uint32_t live = ~group_sinks & (nt < 32 ? (1u << nt) - 1u : ~0u);
-        no_tokens = live == 0u;
-        if (lane_sinks != 0u && !no_tokens)
-            fill = load16_nt(rows.row(__builtin_ctz(live), D) + (int64_t)c * 8);
-    }
-    const auto tok = [&](int t) -> uint4 {
-        if constexpr (IO::kSinks) return ((lane_sinks >> t) & 1u) ? fill : v[t];
-        return v[t];
-    };
-    MinMax8<DT> mm;
-    mm.init(tok(0));
-#pragma unroll
-    for (int t = 1; t < TPL; ++t) mm.add(tok(t));
-#pragma unroll
-    for (int k = 1; k < SPLIT; k <<= 1) mm.combine_xor((int)D8 * k);
-    float lo[8], hi[8];
-    mm.get(lo, hi);
-
-    Params pk[8];
-    bool fast = true;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        pk[k] = make_params<BITS>(no_tokens ? 0.0f : lo[k], no_tokens ? 0.0f : hi[k]);
-        fast = fast && pk[k].fast;
-    }
-    if (!valid) return;
-
-    if (WQ && part == 0) {
-        const int64_t p = io.out_group(bh, g) * D + (int64_t)c * 8;
-        float4* ps = reinterpret_cast<float4*>(scale + p);
-        float4* pz = reinterpret_cast<float4*>(zero + p);
-        ps[0] = make_float4(pk[0].scale, pk[1].scale, pk[2].scale, pk[3].scale);
-        ps[1] = make_float4(pk[4].scale, pk[5].scale, pk[6].scale, pk[7].scale);
-        pz[0] = make_float4(pk[0].zero, pk[1].zero, pk[2].zero, pk[3].zero);
-        pz[1] = make_float4(pk[4].zero, pk[5].zero, pk[6].zero, pk[7].zero);
-    }
-    // real tokens of this lane: part + SPLIT * t < nt (interleaved), or
-    // part * TPL + t < nt (blocked)
-    const int32_t n = ILV ? ((int32_t)nt - (int32_t)part + SPLIT - 1) / SPLIT
-                          : (int32_t)nt - (int32_t)part * TPL;
-    const int32_t first = ILV ? (int32_t)part : (int32_t)part * TPL;
-    const int32_t step = ILV ? SPLIT : 1;
-    const int64_t row_bytes = (int64_t)D8 * BITS;
-    const int64_t orow = io.out_row(bh, s0 + first);
-    uint8_t* dst = WQ ? codes + orow * row_bytes + (int64_t)c * BITS : nullptr;
-    uint16_t* rdst = WR ? recon + orow * D + (int64_t)c * 8 : nullptr;
-    if (fast)
-        emit_split<DT, BITS, WQ, WR, true, TPL, IO::kSinks>(
-            v, pk, n, dst, step * row_bytes, rdst, step * D, lane_sinks);
-    else
-        emit_split<DT, BITS, WQ, WR, false, TPL, IO::kSinks>(
-            v, pk, n, dst, step * row_bytes, rdst, step * D, lane_sinks);
+    quant_keys_split_body<DT, BITS, TPL, SPLIT, WQ, WR, ILV, IO>(
+        io, blockIdx.x * 64u + threadIdx.x, n_lanes, D8, NG, codes, scale, zero,
+        recon);
 }
 
-// Lanes per group.  Below kKeySplitBelow (bh, group, chunk) items (a
-// decode-time flush) one lane per item would leave most of the GPU's 256
-// CUs idle, so each group takes 4 lanes; above it 2 lanes per group, which
-// measured 3-13% faster than one lane per group on the large workloads (half
-// the registers per lane, so more waves in flight, for one xor shuffle and
-// one repeated parameter computation per group).
-constexpr uint64_t kKeySplitBelow = 256ull * 256ull;
+// Lanes per group: 4 below kKeySplitBelow (bh, group, chunk) items, 2 above
+// (kivi_key_split.h).
 
 template <int DT, int BITS, int GMAX, int SPLIT, bool WQ, bool WR>
 static hipError_t launch_keys_split_t(const QuantJob& j) {

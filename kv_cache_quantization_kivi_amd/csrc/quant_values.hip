@@ -19,6 +19,7 @@
 // and store nothing.
 #include "kivi_device.h"
 #include "kivi_launch.h"
+#include "kivi_key_split.h"
 #include "kivi_rows.h"
 
 namespace kivi {
@@ -101,15 +102,15 @@ constexpr int kRecWaveBytes = 64 * kRecLaneStride;
 // [32u, 32u + 32) of the tensor and a wave's input and recon are contiguous.
 // IO: the row layout (DenseRows or CacheRows, kivi_rows.h); the staged
 // (tiled) path needs contiguous rows.
+// u: the lane's index over all lanes of the launch (blocks of 256 lanes);
+// lds: the block's 4 * kRecWaveBytes staging bytes.
 template <int DT, int BITS, int GPL, bool WQ, bool WR, typename IO>
-__global__ __launch_bounds__(256) void quant_values_kernel(
-    IO io, int64_t n_rows, uint32_t D8, uint32_t lp,
+__device__ __forceinline__ void quant_values_body(
+    IO io, uint64_t u, uint8_t* lds, int64_t n_rows, uint32_t D8, uint32_t lp,
     uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
     uint8_t* __restrict__ codes, float* __restrict__ scale,
     float* __restrict__ zero, uint16_t* __restrict__ recon) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
     constexpr int CPG = 4 / GPL;   // chunks per in-lane group
-    const uint64_t u = (uint64_t)blockIdx.x * 256u + threadIdx.x;
     const uint32_t c = (uint32_t)(u & ((1u << lp) - 1u));   // lane in its row
     const int64_t row = (int64_t)(u >> lp);
     const bool row_ok = row < n_rows;
@@ -246,6 +247,18 @@ __global__ __launch_bounds__(256) void quant_values_kernel(
     }
 }
 
+template <int DT, int BITS, int GPL, bool WQ, bool WR, typename IO>
+__global__ __launch_bounds__(256) void quant_values_kernel(
+    IO io, int64_t n_rows, uint32_t D8, uint32_t lp,
+    uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
+    uint8_t* __restrict__ codes, float* __restrict__ scale,
+    float* __restrict__ zero, uint16_t* __restrict__ recon) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
+    quant_values_body<DT, BITS, GPL, WQ, WR, IO>(
+        io, (uint64_t)blockIdx.x * 256u + threadIdx.x, lds, n_rows, D8, lp, red,
+        gl, NGD, vec, tile, codes, scale, zero, recon);
+}
+
 template <int DT, int BITS, int GPL, bool WQ, bool WR>
 static hipError_t launch_values_t(const QuantJob& j) {
     const uint32_t D8 = (uint32_t)(j.D / 8);
@@ -380,6 +393,99 @@ hipError_t launch_list_quant_values(const ListJob& j) {
 hipError_t launch_cache_flush_values(const CacheFlushJob& j) {
     return j.dtype == DT_F16 ? launch_cache_values_dt<DT_F16>(j)
                              : launch_cache_values_dt<DT_BF16>(j);
+}
+
+// ---- keys and values of a small flush in one launch --------------------
+
+// Blocks [0, v_blocks) run the value body, the rest the 4-lane split key
+// body on 256 lanes per block (its lanes need no block-level step).  A
+// decode-time flush of both tensors is then one launch instead of two:
+// each is a few microseconds of fixed latency at these sizes.
+template <int DT, int BITS, bool WQ, bool WR>
+__global__ __launch_bounds__(256) void quant_kv_kernel(
+    DenseRows kio, uint32_t k_lanes, uint32_t D8, uint32_t NG,
+    uint8_t* __restrict__ kc, float* __restrict__ ks, float* __restrict__ kz,
+    uint16_t* __restrict__ kr, DenseRows vio, int64_t n_rows, uint32_t lp,
+    uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
+    uint8_t* __restrict__ vc, float* __restrict__ vs, float* __restrict__ vz,
+    uint16_t* __restrict__ vr, uint32_t v_blocks) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
+    if (blockIdx.x < v_blocks) {
+        quant_values_body<DT, BITS, 1, WQ, WR, DenseRows>(
+            vio, (uint64_t)blockIdx.x * 256u + threadIdx.x, lds, n_rows, D8, lp,
+            red, gl, NGD, vec, tile, vc, vs, vz, vr);
+    } else {
+        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, WQ, WR, true, DenseRows>(
+            kio, (blockIdx.x - v_blocks) * 256u + threadIdx.x, k_lanes, D8, NG,
+            kc, ks, kz, kr);
+    }
+}
+
+template <int DT, int BITS, bool WQ, bool WR>
+static hipError_t launch_kv_t(const QuantJob& k, const QuantJob& v) {
+    const uint32_t D8 = (uint32_t)(k.D / 8);
+    const uint32_t NG = (uint32_t)((k.S + k.group - 1) / k.group);
+    const uint64_t k_lanes = (uint64_t)k.BH * NG * D8 * 4;
+    const DenseRows kio{static_cast<const uint16_t*>(k.x), (int32_t)k.S, NG,
+                        (int32_t)k.group};
+    // value launch shape, as launch_values_t
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t gl = log2_ceil((uint64_t)(v.group / 32));
+    const uint32_t red = 1u << (gl < lp ? gl : lp);
+    const uint32_t NGD = (uint32_t)((v.D + v.group - 1) / v.group);
+    const int64_t n_rows = v.BH * v.S;
+    const uint64_t v_lanes = (uint64_t)n_rows << lp;
+    const uint32_t v_blocks = (uint32_t)((v_lanes + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const int32_t tile = vec && (1u << lp) == lpr;
+    const DenseRows vio{static_cast<const uint16_t*>(v.x), 0, 0, 1};
+    const uint32_t blocks = v_blocks + (uint32_t)((k_lanes + 255) / 256);
+    return launch_kernel((quant_kv_kernel<DT, BITS, WQ, WR>), dim3(blocks),
+                         dim3(256), 0, k.stream, kio, (uint32_t)k_lanes, D8, NG,
+                         k.codes, k.scale, k.zero, static_cast<uint16_t*>(k.recon),
+                         vio, n_rows, lp, red, gl, NGD, vec, tile, v.codes,
+                         v.scale, v.zero, static_cast<uint16_t*>(v.recon),
+                         v_blocks);
+}
+
+template <int DT, int BITS>
+static hipError_t launch_kv_mode(const QuantJob& k, const QuantJob& v) {
+    const bool wq = k.codes != nullptr;
+    const bool wr = k.recon != nullptr;
+    if (wq && wr) return launch_kv_t<DT, BITS, true, true>(k, v);
+    if (wq) return launch_kv_t<DT, BITS, true, false>(k, v);
+    return launch_kv_t<DT, BITS, false, true>(k, v);
+}
+
+template <int DT>
+static hipError_t launch_kv_bits(const QuantJob& k, const QuantJob& v) {
+    switch (k.bits) {
+        case 1: return launch_kv_mode<DT, 1>(k, v);
+        case 2: return launch_kv_mode<DT, 2>(k, v);
+        case 4: return launch_kv_mode<DT, 4>(k, v);
+        default: return launch_kv_mode<DT, 8>(k, v);
+    }
+}
+
+// The caller has validated both jobs (same dtype, shape, bits and outputs
+// present alike).  One launch when the keys take the 4-lane split kernel
+// with groups of 17 to 32 tokens and the value groups are 32 * 2^k
+// channels; otherwise the two single launches, keys first.
+hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v) {
+    const uint64_t D8 = (uint64_t)(k.D / 8);
+    const uint64_t items = (uint64_t)k.BH * ((k.S + k.group - 1) / k.group) * D8;
+    const int64_t g32 = v.group / 32;
+    const bool pair = k.D % 8 == 0 && items < kKeySplitBelow &&
+                      64 % (D8 * 4) == 0 && k.group > kKeyGMaxPair / 2 &&
+                      k.group <= kKeyGMaxPair && v.group % 32 == 0 &&
+                      (g32 & (g32 - 1)) == 0;
+    if (!pair) {
+        const hipError_t e = launch_quant_keys(k);
+        return e != hipSuccess ? e : launch_quant_values(v);
+    }
+    return k.dtype == DT_F16 ? launch_kv_bits<DT_F16>(k, v)
+                             : launch_kv_bits<DT_BF16>(k, v);
 }
 
 hipError_t launch_quant_values(const QuantJob& j) {

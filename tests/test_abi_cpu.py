@@ -311,3 +311,52 @@ def test_mixed_precision_entry_points_reject_before_any_launch(K):
         if name == "kivi_dequant_keys_rows":
             assert fn(c, s, z, 1, 1, 1 << 30, 128, 2, 1, pos, (1 << 30) - 1, 0,
                       x, None) == 2
+
+
+def test_kv_entry_points_reject_before_any_launch(K):
+    """K+V rules (include/kivi.h): each half by the single call's rules,
+    codes for both tensors or neither; fake pointers, never dereferenced."""
+    L = K.raw()
+    P = ctypes.c_void_p
+    k, v = P(0x1000), P(0x2000)
+    kc, ks, kz, vc, vs, vz = (P(0x10000 * i) for i in range(3, 9))
+    kr, vr = P(0x90000), P(0xa0000)
+
+    def q(bits=2, gk=32, gv=32, dt=0, D=128, **kw):
+        a = dict(k=k, v=v, kc=kc, ks=ks, kz=kz, vc=vc, vs=vs, vz=vz)
+        a.update(kw)
+        return L.kivi_quant_kv(a["k"], a["v"], dt, 4, 32, D, bits, gk, gv,
+                               a["kc"], a["ks"], a["kz"], a["vc"], a["vs"],
+                               a["vz"], None)
+
+    assert q(bits=3) == 3
+    assert q(gk=0) == 4 and q(gv=0) == 4
+    assert q(D=13) == 2                       # D * bits % 8
+    assert q(dt=5) == 5
+    assert q(k=None) == 1 and q(vz=None) == 1
+    assert q(v=P(0x2008)) == 6 and q(kc=P(0x30004)) == 6
+    assert L.kivi_quant_kv(k, v, 0, 0, 32, 128, 2, 32, 32, *([None] * 6),
+                           None) == 0         # empty: nothing to do
+
+    def f(**kw):
+        a = dict(kc=kc, ks=ks, kz=kz, vc=vc, vs=vs, vz=vz, kr=kr, vr=vr)
+        a.update(kw)
+        return L.kivi_quant_dequant_kv(k, v, 0, 4, 32, 128, 2, 32, 32, a["kc"],
+                                       a["ks"], a["kz"], a["vc"], a["vs"],
+                                       a["vz"], a["kr"], a["vr"], None)
+
+    assert f(kr=None) == 1 and f(vr=None) == 1
+    assert f(ks=None) == 1                    # a partial set of outputs
+    assert f(kc=None, ks=None, kz=None) == 1  # codes for one tensor only
+    assert f(vr=P(0xa0002)) == 6
+
+    def d(bits=2, gk=32, gv=32, odt=0, **kw):
+        a = dict(kc=kc, ks=ks, kz=kz, vc=vc, vs=vs, vz=vz, kr=kr, vr=vr)
+        a.update(kw)
+        return L.kivi_dequant_kv(a["kc"], a["ks"], a["kz"], a["vc"], a["vs"],
+                                 a["vz"], 4, 32, 128, bits, gk, gv, odt,
+                                 a["kr"], a["vr"], None)
+
+    assert d(bits=5) == 3 and d(gv=0) == 4 and d(odt=2) == 5
+    assert d(vr=None) == 1 and d(kz=None) == 1
+    assert d(vs=P(0x70004)) == 6
