@@ -113,6 +113,8 @@ CASES = [
     (2, 64, 32, 32, 64, 2, FP16, 2, [500, 9]),
     (2, 64, 16, 16, 32, 2, BF16, 3, [290]),
     (1, 128, 0, 32, 128, 2, FP16, 5, [512]),         # every chunk full
+    (2, 64, 32, 32, 32, 4, FP16, 4, [400]),          # 4-bit value code pairs, D = 64
+    (2, 128, 32, 32, 32, 1, BF16, 2, [600]),         # 1-bit value code pairs
 ]
 
 
