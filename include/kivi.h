@@ -152,10 +152,12 @@ kivi_status kivi_quant_dequant_values(const void* v, kivi_dtype dt,
  * share dtype, shape and bits; every argument of both halves is checked by
  * the single call's rules before anything is launched, and codes/params
  * must be given for both tensors or (kivi_quant_dequant_kv) for neither.
- * Small flushes (keys in groups of 17 to 32 tokens with fewer than 65536
- * (bh, group, 8-channel) items, D/8 dividing 16, value groups of 32 * 2^k
- * channels, or for the dequantizer any multiple of 32) run as one kernel
- * launch; otherwise the two single launches are issued, keys first.
+ * Small flushes run as one kernel launch: for the quantizing calls, D/8
+ * dividing 16, key groups of 17 to 32 tokens, fewer than 65536 (bh, key
+ * group, 8-channel) items and value groups of 32 * 2^k channels; for
+ * kivi_dequant_kv, D a multiple of 8 up to 2048, fewer than 65536 key items
+ * and value groups a multiple of 32.  Otherwise the two single launches
+ * are issued, keys first (a caller timing one launch then sees the keys').
  */
 kivi_status kivi_quant_kv(const void* k, const void* v, kivi_dtype dt,
                           int64_t BH, int64_t S, int64_t D, int bits,

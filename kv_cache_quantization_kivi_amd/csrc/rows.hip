@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
     uint32_t key[kPartPer];                    // this thread's run (one round)
     const auto load_run = [&](int r) {         // every thread, barriers inside
         __syncthreads();
+#pragma unroll 8
         for (int i = tid; i < kPartRound; i += kPartThreads) {
             const int32_t p = r * kPartRound + i;
             stage_s[i + i / 32] = p < S ? order_key(sc[p]) : 0u;
@@ -182,17 +183,20 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
         if (n_rounds == 1) {
             // one round: both lists are assembled in LDS (the keys are
             // already in registers) and leave with coalesced stores
+            // Lane L takes its run's elements in the order i = (t + L) mod
+            // 32, so that the 64 lanes of a wave, whose runs start about 32
+            // words apart, write distinct banks; an element's rank within
+            // the run is the count of hi marks before it.
             __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kPartPer; ++i) {
+#pragma unroll 4
+            for (int t = 0; t < kPartPer; ++t) {
+                const int i = (t + lane) & (kPartPer - 1);
                 const int32_t s = s0 + i;
-                if (s >= S) break;
-                if ((mark >> i) & 1u) {
-                    stage_s[hi_rank] = (uint32_t)s;
-                    ++hi_rank;
-                } else {
-                    stage_s[n_hi + (s - (int32_t)hi_rank)] = (uint32_t)s;
-                }
+                const uint32_t before = (uint32_t)__builtin_popcount(mark & ((1u << i) - 1u));
+                const uint32_t hr = hi_rank + before;
+                if (s < S)
+                    stage_s[((mark >> i) & 1u) ? hr : (uint32_t)n_hi + (uint32_t)s - hr] =
+                        (uint32_t)s;
             }
             __syncthreads();
             for (int i = tid; i < S; i += kPartThreads) {
