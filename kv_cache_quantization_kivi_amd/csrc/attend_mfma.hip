@@ -138,16 +138,6 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// The uint4s of operand block bi (N of them, N a power of two) are stored
-// in the order k ^ swz(bi).  A wave reads the blocks of 4 * NQ consecutive
-// bi at once, 128 bytes apart for D = 128: unpermuted, every second (or
-// fourth) block starts on the same LDS bank; with the permutation blocks
-// bi, bi + 4 and bi + 8 of one bank class read distinct 16-byte slots.
-template <int N>
-__device__ __forceinline__ int swz(int bi) {
-    return (bi >> 1) & (N - 1);
-}
-
 // An operand, or zeros when `keep` is false.
 __device__ __forceinline__ h8_t pick_op(uint4 v, bool keep) {
     return as_h8(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
@@ -181,8 +171,7 @@ __device__ __forceinline__ float widen_h(uint16_t h) {
 // 16 * 2^k channels and n_q <= NQ.
 //
 // B operands live in LDS, each lane's operands of one group contiguous:
-// keys [g][kb][j][k-step][hi, lo], values [gv][kb][j][k-step][hi, lo],
-// the uint4s of each [..][kb][j] block permuted by swz
+// keys [g][kb][j][k-step][hi, lo], values [gv][kb][j][k-step][hi, lo]
 // (uint4 = 8 halves each).  Lanes past the query heads read a zero block
 // instead (an LDS address select), so no operand needs masking.
 template <int DT, int BITS, int D, int NQ, int GK>
@@ -336,11 +325,9 @@ void attend_mfma_kernel(AttendArgs a) {
                     lw[i / 2] = pack_h2(l0, l1);
                 }
                 const int d = kc8 * 8, blk = d / CPL, s = (d % CPL) / 8;
-                const int bi = (kg * 4 + blk) * NQ + j;
-                uint4* ob = ops_s + bi * (2 * KS);
-                const int sw = swz<2 * KS>(bi);
-                ob[(2 * s) ^ sw] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                ob[(2 * s + 1) ^ sw] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                uint4* ob = ops_s + ((kg * 4 + blk) * NQ + j) * (2 * KS);
+                ob[2 * s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                ob[2 * s + 1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
                 if (kc8 == 0) {
                     kbias_s[kg][j] = b;
                     kexp_s[kg][j] = e;
@@ -356,9 +343,7 @@ void attend_mfma_kernel(AttendArgs a) {
         const int tok0 = (wave + 2 * tt) * 16;
         if (tok0 >= nq_tok) break;             // wave-uniform
         const int g = tok0 >> gk_sh;
-        const int bi = (g * 4 + kb) * NQ + m16;
-        const uint4* bp = m16 < NQ ? ops_s + bi * (2 * KS) : zero_s;
-        const int sw = swz<2 * KS>(bi);
+        const uint4* bp = m16 < NQ ? ops_s + ((g * 4 + kb) * NQ + m16) * (2 * KS) : zero_s;
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -368,9 +353,9 @@ void attend_mfma_kernel(AttendArgs a) {
             if constexpr (SB < 32) bits &= (1u << SB) - 1u;
             const h8_t A = codes8<BITS>(bits);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[(2 * s) ^ sw]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[2 * s]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[(2 * s + 1) ^ sw]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[2 * s + 1]), acc, 0, 0, 0);
         }
         if (m16 < NQ) {
             const int e = kexp_s[g][m16];
@@ -528,10 +513,9 @@ void attend_mfma_kernel(AttendArgs a) {
             for (int j = 0; j < NQ; ++j) {
                 _Float16 hi, lo;
                 split16(__builtin_ldexpf(pt[j] * sv, e), hi, lo);
-                const int bi = (gv * 4 + blk) * NQ + j, sw = swz<2 * VKS>(bi);
-                _Float16* vb = vops + bi * (2 * VKS) * 8;
-                vb[((2 * s4) ^ sw) * 8 + i] = hi;
-                vb[((2 * s4 + 1) ^ sw) * 8 + i] = lo;
+                _Float16* vb = vops + ((gv * 4 + blk) * NQ + j) * (2 * VKS) * 8;
+                vb[(2 * s4) * 8 + i] = hi;
+                vb[(2 * s4 + 1) * 8 + i] = lo;
             }
         }
     }
@@ -544,9 +528,7 @@ void attend_mfma_kernel(AttendArgs a) {
         const int ch = mt * 16 + m16;                   // this lane's A row
         const int q = (ch * BITS) / 16, sh = (ch * BITS) % 16;
         const uint32_t pmask = ((1u << BITS) - 1u) * 0x10001u;
-        const int bi = (gv * 4 + kb) * NQ + m16;
-        const uint4* bp = m16 < NQ ? ops_s + bi * (2 * VKS) : zero_s;
-        const int sw = swz<2 * VKS>(bi);
+        const uint4* bp = m16 < NQ ? ops_s + ((gv * 4 + kb) * NQ + m16) * (2 * VKS) : zero_s;
         f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s4 = 0; s4 < VKS; ++s4) {
@@ -565,9 +547,9 @@ void attend_mfma_kernel(AttendArgs a) {
             }
             const h8_t A = as_h8(pr[0], pr[1], pr[2], pr[3]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[(2 * s4) ^ sw]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[2 * s4]), acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[(2 * s4 + 1) ^ sw]), acc, 0, 0, 0);
+                A, __builtin_bit_cast(h8_t, bp[2 * s4 + 1]), acc, 0, 0, 0);
         }
         // C: lane (head m16, row block kb) holds channels mt*16 + 4 kb + i
         if (m16 < nq) {
