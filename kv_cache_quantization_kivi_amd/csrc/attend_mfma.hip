@@ -126,16 +126,15 @@ __device__ __forceinline__ int op_exp(float P) {
     return 13 - lg;
 }
 
-// x = hi + lo with hi = RN16(x) and lo = RN16(x - hi).
-__device__ __forceinline__ void split16(float x, _Float16& hi, _Float16& lo) {
-    hi = (_Float16)x;
-    lo = (_Float16)(x - (float)hi);
-}
-
-// Two f16 values as one dword (a in the low half).
-__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+// x = hi + lo with hi = RN16(x) and lo = RN16(x - hi), for two values at
+// once as packed pairs (x0 in the low halves): one paired conversion for the
+// two hi parts and one for the two lo parts.
+__device__ __forceinline__ void split16x2(float x0, float x1, uint32_t& hi,
+                                          uint32_t& lo) {
+    const h2x_t h = {(_Float16)x0, (_Float16)x1};
+    const h2x_t l = {(_Float16)(x0 - (float)h.x), (_Float16)(x1 - (float)h.y)};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // An operand, or zeros when `keep` is false.
@@ -318,11 +317,8 @@ void attend_mfma_kernel(AttendArgs a) {
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    _Float16 h0, l0, h1, l1;
-                    split16(__builtin_ldexpf(pr[i], e), h0, l0);
-                    split16(__builtin_ldexpf(pr[i + 1], e), h1, l1);
-                    hw[i / 2] = pack_h2(h0, h1);
-                    lw[i / 2] = pack_h2(l0, l1);
+                    split16x2(__builtin_ldexpf(pr[i], e), __builtin_ldexpf(pr[i + 1], e),
+                              hw[i / 2], lw[i / 2]);
                 }
                 const int d = kc8 * 8, blk = d / CPL, s = (d % CPL) / 8;
                 uint4* ob = ops_s + ((kg * 4 + blk) * NQ + j) * (2 * KS);
@@ -509,13 +505,21 @@ void attend_mfma_kernel(AttendArgs a) {
         for (int gv = 0; gv < ngd; ++gv) {
             const int e = op_exp(vmax_s[gv]);
             const float sv = sv_s[gv][tid];   // this token's scale
+            // heads in pairs: one paired conversion per pair for hi and lo
 #pragma unroll
-            for (int j = 0; j < NQ; ++j) {
-                _Float16 hi, lo;
-                split16(__builtin_ldexpf(pt[j] * sv, e), hi, lo);
-                _Float16* vb = vops + ((gv * 4 + blk) * NQ + j) * (2 * VKS) * 8;
-                vb[(2 * s4) * 8 + i] = hi;
-                vb[(2 * s4 + 1) * 8 + i] = lo;
+            for (int j = 0; j < NQ; j += 2) {
+                const float w0 = __builtin_ldexpf(pt[j] * sv, e);
+                const float w1 = j + 1 < NQ ? __builtin_ldexpf(pt[j + 1] * sv, e) : 0.0f;
+                uint32_t hi, lo;
+                split16x2(w0, w1, hi, lo);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    if (j + u < NQ) {
+                        _Float16* vb = vops + ((gv * 4 + blk) * NQ + j + u) * (2 * VKS) * 8;
+                        vb[(2 * s4) * 8 + i] = __builtin_bit_cast(_Float16, (uint16_t)(hi >> (16 * u)));
+                        vb[(2 * s4 + 1) * 8 + i] = __builtin_bit_cast(_Float16, (uint16_t)(lo >> (16 * u)));
+                    }
+                }
             }
         }
     }
