@@ -305,7 +305,17 @@ def flush_plan(cw):
     return plan
 
 
-def cache_bytes(cw, F, copy, keys_flush_only=False):
+def cache_flush_paired(cw, F):
+    """Whether the library flushes F tokens of K and V in one launch (the
+    one-launch rule of the K+V calls, include/kivi.h)."""
+    D8 = cw.D // 8
+    g32 = cw.group_v // 32
+    return (cw.BH * (F // cw.group_k) * D8 < 65536 and 64 % (D8 * 4) == 0
+            and 16 < cw.group_k <= 32 and cw.group_v % 32 == 0
+            and g32 & (g32 - 1) == 0)
+
+
+def cache_bytes(cw, F, copy, keys_flush_only=False, flush_only=False):
     """Algorithmic bytes of one append: the F flushed tokens of K and V read
     once, their codes and params written once, and the tokens that stay
     unquantized read once and written once to the ring."""
@@ -314,6 +324,8 @@ def cache_bytes(cw, F, copy, keys_flush_only=False):
     if keys_flush_only:
         return kf * cw.BH
     vf = F * D * 2 + F * D * cw.bits // 8 + F * (-(-D // cw.group_v)) * 8
+    if flush_only:
+        return (kf + vf) * cw.BH
     ring = 2 * copy * D * 2 * 2
     return (kf + vf + ring) * cw.BH
 
@@ -460,8 +472,13 @@ def cache_bench(args, cw, K, torch, dev):
     torch.cuda.synchronize()
     kinds = {}
     for a, (_, _, n, F, cp) in enumerate(plan):
-        name = "cache_flush_keys" if F else "cache_ring_store"
-        b = (cache_bytes(cw, F, cp, keys_flush_only=True) if F
+        # the first launch of the append: the flush (of K and V together
+        # when it is one launch), else the ring store
+        paired = F and cache_flush_paired(cw, F)
+        name = ("cache_flush_kv" if paired else "cache_flush_keys") if F \
+            else "cache_ring_store"
+        b = (cache_bytes(cw, F, cp, flush_only=True) if paired
+             else cache_bytes(cw, F, cp, keys_flush_only=True) if F
              else cw.BH * cp * cw.D * 2 * 2 * 2)
         d = [arms[i][a][0].elapsed_time(arms[i][a][1])
              for i in range(args.steps)]

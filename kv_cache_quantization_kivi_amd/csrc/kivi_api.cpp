@@ -520,15 +520,14 @@ kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
                               c->ring, n, c->T, c->Q, Q_to - c->Q, c->S_max,
                               (int)c->bits, c->G_k, c->G_k, c->k_codes,
                               c->k_scale, c->k_zero, stream};
-        if (kivi::launch_cache_flush_keys(f) != hipSuccess)
-            return KIVI_ERR_LAUNCH;
-        f.ring = c->v_ring;
-        f.in = v_new;
-        f.group = c->G_v;
-        f.codes = c->v_codes;
-        f.scale = c->v_scale;
-        f.zero = c->v_zero;
-        if (kivi::launch_cache_flush_values(f) != hipSuccess)
+        kivi::CacheFlushJob fv = f;
+        fv.ring = c->v_ring;
+        fv.in = v_new;
+        fv.group = c->G_v;
+        fv.codes = c->v_codes;
+        fv.scale = c->v_scale;
+        fv.zero = c->v_zero;
+        if (kivi::launch_cache_flush_kv(f, fv) != hipSuccess)
             return KIVI_ERR_LAUNCH;
     }
     // the new tokens that stay unquantized go to their ring slots (after the

@@ -401,21 +401,21 @@ hipError_t launch_cache_flush_values(const CacheFlushJob& j) {
 // body on 256 lanes per block (its lanes need no block-level step).  A
 // decode-time flush of both tensors is then one launch instead of two:
 // each is a few microseconds of fixed latency at these sizes.
-template <int DT, int BITS, bool WQ, bool WR>
+template <int DT, int BITS, bool WQ, bool WR, typename IO>
 __global__ __launch_bounds__(256) void quant_kv_kernel(
-    DenseRows kio, uint32_t k_lanes, uint32_t D8, uint32_t NG,
+    IO kio, uint32_t k_lanes, uint32_t D8, uint32_t NG,
     uint8_t* __restrict__ kc, float* __restrict__ ks, float* __restrict__ kz,
-    uint16_t* __restrict__ kr, DenseRows vio, int64_t n_rows, uint32_t lp,
+    uint16_t* __restrict__ kr, IO vio, int64_t n_rows, uint32_t lp,
     uint32_t red, uint32_t gl, uint32_t NGD, int32_t vec, int32_t tile,
     uint8_t* __restrict__ vc, float* __restrict__ vs, float* __restrict__ vz,
     uint16_t* __restrict__ vr, uint32_t v_blocks) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
     if (blockIdx.x < v_blocks) {
-        quant_values_body<DT, BITS, 1, WQ, WR, DenseRows>(
+        quant_values_body<DT, BITS, 1, WQ, WR, IO>(
             vio, (uint64_t)blockIdx.x * 256u + threadIdx.x, lds, n_rows, D8, lp,
             red, gl, NGD, vec, tile, vc, vs, vz, vr);
     } else {
-        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, WQ, WR, true, DenseRows>(
+        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, WQ, WR, true, IO>(
             kio, (blockIdx.x - v_blocks) * 256u + threadIdx.x, k_lanes, D8, NG,
             kc, ks, kz, kr);
     }
@@ -441,7 +441,7 @@ static hipError_t launch_kv_t(const QuantJob& k, const QuantJob& v) {
     const int32_t tile = vec && (1u << lp) == lpr;
     const DenseRows vio{static_cast<const uint16_t*>(v.x), 0, 0, 1};
     const uint32_t blocks = v_blocks + (uint32_t)((k_lanes + 255) / 256);
-    return launch_kernel((quant_kv_kernel<DT, BITS, WQ, WR>), dim3(blocks),
+    return launch_kernel((quant_kv_kernel<DT, BITS, WQ, WR, DenseRows>), dim3(blocks),
                          dim3(256), 0, k.stream, kio, (uint32_t)k_lanes, D8, NG,
                          k.codes, k.scale, k.zero, static_cast<uint16_t*>(k.recon),
                          vio, n_rows, lp, red, gl, NGD, vec, tile, v.codes,
@@ -486,6 +486,62 @@ hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v) {
     }
     return k.dtype == DT_F16 ? launch_kv_bits<DT_F16>(k, v)
                              : launch_kv_bits<DT_BF16>(k, v);
+}
+
+// A residual-window cache's flush of both tensors (CacheRows) in one
+// launch, under the same rule as launch_quant_kv.
+template <int DT, int BITS>
+static hipError_t launch_cache_kv_t(const CacheFlushJob& k, const CacheFlushJob& v) {
+    const uint32_t D8 = (uint32_t)(k.D / 8);
+    const uint32_t NG = (uint32_t)(k.F / k.G_k);          // groups flushed per bh
+    const uint64_t k_lanes = (uint64_t)k.BH * NG * D8 * 4;
+    const uint32_t NG_out = (uint32_t)((k.S_max + k.G_k - 1) / k.G_k);
+    const auto rows = [&](const CacheFlushJob& j) {
+        return CacheRows{static_cast<const uint16_t*>(j.ring),
+                         static_cast<const uint16_t*>(j.in), (int32_t)j.ring_len,
+                         (int32_t)j.n_in, (int32_t)j.T, (int32_t)j.Q,
+                         (int32_t)j.F, (int32_t)j.S_max, NG_out, (int32_t)j.G_k};
+    };
+    const uint32_t lpr = (D8 + 3) / 4;
+    const uint32_t lp = log2_ceil(lpr);
+    const uint32_t gl = log2_ceil((uint64_t)(v.group / 32));
+    const uint32_t red = 1u << (gl < lp ? gl : lp);
+    const uint32_t NGD = (uint32_t)((v.D + v.group - 1) / v.group);
+    const int64_t n_rows = v.BH * v.F;
+    const uint32_t v_blocks = (uint32_t)((((uint64_t)n_rows << lp) + 255) / 256);
+    const int32_t vec = (D8 % 4) == 0;
+    const uint32_t blocks = v_blocks + (uint32_t)((k_lanes + 255) / 256);
+    return launch_kernel((quant_kv_kernel<DT, BITS, true, false, CacheRows>),
+                         dim3(blocks), dim3(256), 0, k.stream, rows(k),
+                         (uint32_t)k_lanes, D8, NG, k.codes, k.scale, k.zero,
+                         (uint16_t*)nullptr, rows(v), n_rows, lp, red, gl, NGD,
+                         vec, (int32_t)0, v.codes, v.scale, v.zero,
+                         (uint16_t*)nullptr, v_blocks);
+}
+
+template <int DT>
+static hipError_t launch_cache_kv_bits(const CacheFlushJob& k, const CacheFlushJob& v) {
+    switch (k.bits) {
+        case 1: return launch_cache_kv_t<DT, 1>(k, v);
+        case 2: return launch_cache_kv_t<DT, 2>(k, v);
+        case 4: return launch_cache_kv_t<DT, 4>(k, v);
+        default: return launch_cache_kv_t<DT, 8>(k, v);
+    }
+}
+
+hipError_t launch_cache_flush_kv(const CacheFlushJob& k, const CacheFlushJob& v) {
+    const uint64_t D8 = (uint64_t)(k.D / 8);
+    const uint64_t items = (uint64_t)k.BH * (k.F / k.G_k) * D8;
+    const int64_t g32 = v.group / 32;
+    const bool pair = items < kKeySplitBelow && 64 % (D8 * 4) == 0 &&
+                      k.G_k > kKeyGMaxPair / 2 && k.G_k <= kKeyGMaxPair &&
+                      v.group % 32 == 0 && (g32 & (g32 - 1)) == 0;
+    if (!pair) {
+        const hipError_t e = launch_cache_flush_keys(k);
+        return e != hipSuccess ? e : launch_cache_flush_values(v);
+    }
+    return k.dtype == DT_F16 ? launch_cache_kv_bits<DT_F16>(k, v)
+                             : launch_cache_kv_bits<DT_BF16>(k, v);
 }
 
 hipError_t launch_quant_values(const QuantJob& j) {

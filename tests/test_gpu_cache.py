@@ -81,6 +81,7 @@ CONFIGS = [
     (5, 8, 160, 40, 32, 8, 1, BF16, [2, 80, 1, 1, 30, 41]),
     (2, 32, 300, 5, 32, 256, 2, FP16, [37, 1, 64, 2, 100]),
     (3, 16, 200, 3, 5, 16, 4, FP16, [1, 2, 3, 50, 4, 7]),
+    (2, 64, 256, 32, 24, 64, 4, BF16, [1, 50, 1, 1, 30, 70, 2]),  # K+V flush in one launch
 ]
 
 
