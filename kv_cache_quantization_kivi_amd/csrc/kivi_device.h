@@ -347,17 +347,30 @@ __device__ __forceinline__ float recon(uint32_t code, float scale, float zero) {
 }
 
 // Store the 8*BITS bits of one chunk's codes (BITS bytes) at p.
-template <int BITS>
+// NT: a non-temporal store (streamed past the caches), for outputs that no
+// later step of the same kernel reads.
+template <int BITS, bool NT = false>
 __device__ __forceinline__ void store_codes(uint8_t* p, uint64_t bits) {
     if constexpr (BITS == 1) {
-        *p = (uint8_t)bits;
+        if constexpr (NT) __builtin_nontemporal_store((uint8_t)bits, p);
+        else *p = (uint8_t)bits;
     } else if constexpr (BITS == 2) {
-        *reinterpret_cast<uint16_t*>(p) = (uint16_t)bits;
+        if constexpr (NT)
+            __builtin_nontemporal_store((uint16_t)bits, reinterpret_cast<uint16_t*>(p));
+        else *reinterpret_cast<uint16_t*>(p) = (uint16_t)bits;
     } else if constexpr (BITS == 4) {
-        *reinterpret_cast<uint32_t*>(p) = (uint32_t)bits;
+        if constexpr (NT)
+            __builtin_nontemporal_store((uint32_t)bits, reinterpret_cast<uint32_t*>(p));
+        else *reinterpret_cast<uint32_t*>(p) = (uint32_t)bits;
     } else {
-        *reinterpret_cast<uint2*>(p) =
-            make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+        if constexpr (NT) {
+            typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+            const u32x2_t w = {(uint32_t)bits, (uint32_t)(bits >> 32)};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+        } else {
+            *reinterpret_cast<uint2*>(p) =
+                make_uint2((uint32_t)bits, (uint32_t)(bits >> 32));
+        }
     }
 }
 

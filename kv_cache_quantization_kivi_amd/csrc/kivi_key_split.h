@@ -50,7 +50,11 @@ __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
                     r = v[t];
                 }
             }
-            if constexpr (WQ) store_codes<BITS>(dst + t * cstride, q);
+            // quantize-only: codes streamed (measured faster for this
+            // kernel and for the kernels after it); the fused form keeps
+            // plain stores (streaming them beside the reconstruction was
+            // slower)
+            if constexpr (WQ) store_codes<BITS, !WR>(dst + t * cstride, q);
             if constexpr (WR) store16_nt(rdst + t * rstride, r);
         }
     }
@@ -123,12 +127,27 @@ __device__ __forceinline__ void quant_keys_split_body(
 
     if (WQ && part == 0) {
         const int64_t p = io.out_group(bh, g) * D + (int64_t)c * 8;
-        float4* ps = reinterpret_cast<float4*>(scale + p);
-        float4* pz = reinterpret_cast<float4*>(zero + p);
-        ps[0] = make_float4(pk[0].scale, pk[1].scale, pk[2].scale, pk[3].scale);
-        ps[1] = make_float4(pk[4].scale, pk[5].scale, pk[6].scale, pk[7].scale);
-        pz[0] = make_float4(pk[0].zero, pk[1].zero, pk[2].zero, pk[3].zero);
-        pz[1] = make_float4(pk[4].zero, pk[5].zero, pk[6].zero, pk[7].zero);
+        const uint4 s0 = make_uint4(__float_as_uint(pk[0].scale), __float_as_uint(pk[1].scale),
+                                    __float_as_uint(pk[2].scale), __float_as_uint(pk[3].scale));
+        const uint4 s1 = make_uint4(__float_as_uint(pk[4].scale), __float_as_uint(pk[5].scale),
+                                    __float_as_uint(pk[6].scale), __float_as_uint(pk[7].scale));
+        const uint4 z0 = make_uint4(__float_as_uint(pk[0].zero), __float_as_uint(pk[1].zero),
+                                    __float_as_uint(pk[2].zero), __float_as_uint(pk[3].zero));
+        const uint4 z1 = make_uint4(__float_as_uint(pk[4].zero), __float_as_uint(pk[5].zero),
+                                    __float_as_uint(pk[6].zero), __float_as_uint(pk[7].zero));
+        if constexpr (!WR) {   // params streamed like the codes
+            store16_nt(scale + p, s0);
+            store16_nt(scale + p + 4, s1);
+            store16_nt(zero + p, z0);
+            store16_nt(zero + p + 4, z1);
+        } else {
+            uint4* ps = reinterpret_cast<uint4*>(scale + p);
+            uint4* pz = reinterpret_cast<uint4*>(zero + p);
+            ps[0] = s0;
+            ps[1] = s1;
+            pz[0] = z0;
+            pz[1] = z1;
+        }
     }
     // real tokens of this lane: part + SPLIT * t < nt (interleaved), or
     // part * TPL + t < nt (blocked)
