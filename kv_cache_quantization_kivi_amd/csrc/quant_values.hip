@@ -79,6 +79,14 @@ __device__ __forceinline__ void chunks_minmax(const uint4 (&v)[4], int k0,
     }
 }
 
+// A group parameter; NT: streamed (quantize-only outputs, which measured
+// faster non-temporal, for this kernel and the ones after it).
+template <bool NT>
+__device__ __forceinline__ void put_param(float* p, float v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 // LDS staging.  A lane's 64 bytes of input (and of recon) are contiguous
 // but lanes are 64 bytes apart, so direct 16-byte accesses are strided:
 // each 128-byte line is touched by four instructions, which defeats
@@ -169,16 +177,16 @@ __device__ __forceinline__ void quant_values_body(
         if constexpr (GPL == 1) {
             if ((c & ((1u << gl) - 1u)) == 0) {
                 const int64_t pi = orow * NGD + (c >> gl);
-                scale[pi] = pg[0].scale;
-                zero[pi] = pg[0].zero;
+                put_param<!WR>(scale + pi, pg[0].scale);
+                put_param<!WR>(zero + pi, pg[0].zero);
             }
         } else {
 #pragma unroll
             for (int t = 0; t < GPL; ++t) {
                 if (t * CPG < nch) {
                     const int64_t pi = orow * NGD + (ch0 / CPG) + t;
-                    scale[pi] = pg[t].scale;
-                    zero[pi] = pg[t].zero;
+                    put_param<!WR>(scale + pi, pg[t].scale);
+                    put_param<!WR>(zero + pi, pg[t].zero);
                 }
             }
         }
@@ -222,27 +230,33 @@ __device__ __forceinline__ void quant_values_body(
     }
     if constexpr (WQ) {
         if (vec && nch == 4) {
+            // the lane's 4 chunks' codes as one store (BITS bytes per chunk)
             if constexpr (BITS == 1) {
-                *reinterpret_cast<uint32_t*>(cdst) =
-                    (uint32_t)(q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24));
+                store_codes<4, !WR>(cdst, q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24));
             } else if constexpr (BITS == 2) {
-                *reinterpret_cast<uint2*>(cdst) = make_uint2(
-                    (uint32_t)(q[0] | (q[1] << 16)), (uint32_t)(q[2] | (q[3] << 16)));
-            } else if constexpr (BITS == 4) {
-                *reinterpret_cast<uint4*>(cdst) =
-                    make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2],
-                               (uint32_t)q[3]);
-            } else {
-                uint4* d4 = reinterpret_cast<uint4*>(cdst);
-                d4[0] = make_uint4((uint32_t)q[0], (uint32_t)(q[0] >> 32),
-                                   (uint32_t)q[1], (uint32_t)(q[1] >> 32));
-                d4[1] = make_uint4((uint32_t)q[2], (uint32_t)(q[2] >> 32),
-                                   (uint32_t)q[3], (uint32_t)(q[3] >> 32));
+                store_codes<8, !WR>(cdst, q[0] | (q[1] << 16) | (q[2] << 32) | (q[3] << 48));
+            } else {   // 16 bytes (4-bit) or 32 bytes (8-bit) of codes
+                constexpr int N = BITS / 4;
+                uint4 w[2];
+                if constexpr (BITS == 4) {
+                    w[0] = make_uint4((uint32_t)q[0], (uint32_t)q[1], (uint32_t)q[2],
+                                      (uint32_t)q[3]);
+                } else {
+                    w[0] = make_uint4((uint32_t)q[0], (uint32_t)(q[0] >> 32),
+                                      (uint32_t)q[1], (uint32_t)(q[1] >> 32));
+                    w[1] = make_uint4((uint32_t)q[2], (uint32_t)(q[2] >> 32),
+                                      (uint32_t)q[3], (uint32_t)(q[3] >> 32));
+                }
+#pragma unroll
+                for (int k = 0; k < N; ++k) {
+                    if constexpr (!WR) store16_nt(cdst + 16 * k, w[k]);
+                    else reinterpret_cast<uint4*>(cdst)[k] = w[k];
+                }
             }
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                if (k < nch) store_codes<BITS>(cdst + k * BITS, q[k]);
+                if (k < nch) store_codes<BITS, !WR>(cdst + k * BITS, q[k]);
         }
     }
 }
