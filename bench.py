@@ -307,10 +307,11 @@ def flush_plan(cw):
 
 def cache_flush_paired(cw, F):
     """Whether the library flushes F tokens of K and V in one launch (the
-    one-launch rule of the K+V calls, include/kivi.h)."""
+    one-launch rule of the K+V calls, include/kivi.h, with a cache flush's
+    item bound of 4 * 65536)."""
     D8 = cw.D // 8
     g32 = cw.group_v // 32
-    return (cw.BH * (F // cw.group_k) * D8 < 65536 and 64 % (D8 * 4) == 0
+    return (cw.BH * (F // cw.group_k) * D8 < 4 * 65536 and 64 % (D8 * 4) == 0
             and 16 < cw.group_k <= 32 and cw.group_v % 32 == 0
             and g32 & (g32 - 1) == 0)
 

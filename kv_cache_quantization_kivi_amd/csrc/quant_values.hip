@@ -503,7 +503,13 @@ hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v) {
 }
 
 // A residual-window cache's flush of both tensors (CacheRows) in one
-// launch, under the same rule as launch_quant_kv.
+// launch, under the rule of launch_quant_kv with a larger item bound: up to
+// kCacheKvPairBelow key items the one launch, with the 4-lane key body, is
+// faster than the two (a 2016-token prefill flush of 112 heads, 112896
+// items: the step 42.2 -> 37.5 us), since each launch's ramp and tail is
+// a third of a key flush that size.
+constexpr uint64_t kCacheKvPairBelow = 4 * kKeySplitBelow;
+
 template <int DT, int BITS>
 static hipError_t launch_cache_kv_t(const CacheFlushJob& k, const CacheFlushJob& v) {
     const uint32_t D8 = (uint32_t)(k.D / 8);
@@ -547,7 +553,7 @@ hipError_t launch_cache_flush_kv(const CacheFlushJob& k, const CacheFlushJob& v)
     const uint64_t D8 = (uint64_t)(k.D / 8);
     const uint64_t items = (uint64_t)k.BH * (k.F / k.G_k) * D8;
     const int64_t g32 = v.group / 32;
-    const bool pair = items < kKeySplitBelow && 64 % (D8 * 4) == 0 &&
+    const bool pair = items < kCacheKvPairBelow && 64 % (D8 * 4) == 0 &&
                       k.G_k > kKeyGMaxPair / 2 && k.G_k <= kKeyGMaxPair &&
                       v.group % 32 == 0 && (g32 & (g32 - 1)) == 0;
     if (!pair) {

@@ -108,12 +108,15 @@ def test_cache_appends_match_oracle(K, O, cfg):
         _compare(c, o, tag)
 
 
-def test_cache_prefill_chunks_then_decode(K, O):
+@pytest.mark.parametrize("BH", [224, 512])
+def test_cache_prefill_chunks_then_decode(K, O, BH):
     """A 2059-token prompt in prefill chunks of 2048, then 240 decode
-    tokens (R = G = 32, 28 layers x 8 KV heads, D = 128): 2016 tokens
-    flushed by the prompt, 7 decode flushes, everything bit-identical to the
-    oracle.  The prompt flush is large enough for the two-lane key kernel."""
-    BH, D, R, G = 224, 128, 32, 32
+    tokens (R = G = 32, D = 128; 28 layers x 8 KV heads, or 512 heads):
+    2016 tokens flushed by the prompt, 7 decode flushes, everything
+    bit-identical to the oracle.  The prompt flush of 224 heads (225792 key
+    items) runs K and V in one launch; that of 512 heads (516096) takes the
+    two launches and the two-lane key kernel."""
+    D, R, G = 128, 32, 32
     S_max = 2059 + 240
     c = K.KiviCache(BH, D, S_max, R, G, G, 2, torch.float16)
     o = O.cache(BH, D, S_max, R, G, G, 2, FP16)
@@ -121,7 +124,7 @@ def test_cache_prefill_chunks_then_decode(K, O):
     v = _tokens(6, BH, S_max, D, FP16)
     for a in (0, 2048):
         b = min(a + 2048, 2059)
-        say(f"[cache prefill chunk {a}:{b}]")
+        say(f"[cache prefill BH={BH} chunk {a}:{b}]")
         kn, vn = np.ascontiguousarray(k[:, a:b]), np.ascontiguousarray(v[:, a:b])
         c.append(_dev(kn, FP16), _dev(vn, FP16))
         o.append(kn, vn)
