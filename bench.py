@@ -1093,8 +1093,10 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus},"
-              f" WORLD_SIZE {world}); the KIVI flush needs no collectives and "
-              "this build runs on a single GPU.", file=sys.stderr)
+              f" WORLD_SIZE {world}); the KIVI flush needs no collectives: "
+              "each GPU quantizes its own heads, so the figure for N GPUs is "
+              "N times the one-GPU figure and is not measured here.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
