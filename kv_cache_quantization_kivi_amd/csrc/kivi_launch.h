@@ -183,8 +183,9 @@ hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v);
 hipError_t launch_dequant_kv(const DequantJob& k, const DequantJob& v);
 hipError_t launch_cache_flush_keys(const CacheFlushJob& j);
 hipError_t launch_cache_flush_values(const CacheFlushJob& j);
-// Both tensors of a flush: one launch for small flushes (the rule of
-// launch_quant_kv), else the key and value launches.
+// Both tensors of a flush: one launch under the rule of launch_quant_kv
+// with four times its item bound (kCacheKvPairBelow), else the key and
+// value launches.
 hipError_t launch_cache_flush_kv(const CacheFlushJob& k, const CacheFlushJob& v);
 // Copy tokens [s_first, T + n_in) of the appended keys and values into
 // their ring slots, both tensors in one launch (16-byte chunks).
