@@ -416,20 +416,65 @@ class OracleCache:
             tail = self.v[:, Q:T]
         return np.concatenate([deq, tail], axis=1)
 
-    def attend(self, q, sm_scale):
-        """Decode attention of q [BH, n_q, D] (16-bit patterns; n_q query
-        heads share each KV head) over all T cached tokens, in float64:
-        softmax(sm_scale * q K^T) V with K, V from dequantized().  Returns
-        float64 [BH, n_q, D]."""
-        dt = self.c.dtype
-        Kf = self.o.widen(self.dequantized("K"), dt).astype(np.float64)
-        Vf = self.o.widen(self.dequantized("V"), dt).astype(np.float64)
-        qf = self.o.widen(np.ascontiguousarray(q), dt).astype(np.float64)
+    def reconstructed(self, which):
+        """The cache as attention over the packed store reads it (the
+        contract of kivi_cache_attend): tokens [0, Q) as code * scale + zero
+        with their group's params, evaluated in float64 (the product is
+        exact, the sum rounded once at 2^-53) and never rounded to fp32 or
+        to the 16-bit type, followed by the exact tokens [Q, T) widened;
+        float64 [BH, T, D]."""
+        c = self.c
+        Q, T, D = c.Q, c.T, c.D
+        if which == "K":
+            codes = self.o.unpack(np.ascontiguousarray(self.k_codes[:, :Q]),
+                                  D, c.bits)
+            sc = np.repeat(self.k_scale[:, :Q // c.G_k], c.G_k, axis=1)
+            z = np.repeat(self.k_zero[:, :Q // c.G_k], c.G_k, axis=1)
+            hist = self.k
+        else:
+            codes = self.o.unpack(np.ascontiguousarray(self.v_codes[:, :Q]),
+                                  D, c.bits)
+            sc = np.repeat(self.v_scale[:, :Q], c.G_v, axis=2)[:, :, :D]
+            z = np.repeat(self.v_zero[:, :Q], c.G_v, axis=2)[:, :, :D]
+            hist = self.v
+        rec = (codes.astype(np.float64) * sc.astype(np.float64)
+               + z.astype(np.float64))
+        tail = self.o.widen(np.ascontiguousarray(hist[:, Q:T]),
+                            c.dtype).astype(np.float64)
+        return np.concatenate([rec, tail], axis=1)
+
+    @staticmethod
+    def _softmax_attend(qf, Kf, Vf, sm_scale):
+        """softmax_t(sm_scale * q . K_t) V_t in float64 for every (bh, query
+        head); qf [BH, n_q, D], Kf and Vf [BH, T, D]."""
         s = np.einsum("bjd,btd->bjt", qf, Kf) * float(sm_scale)
         s -= s.max(axis=2, keepdims=True)
         p = np.exp(s)
         p /= p.sum(axis=2, keepdims=True)
         return np.einsum("bjt,btd->bjd", p, Vf)
+
+    def attend(self, q, sm_scale):
+        """Decode attention of q [BH, n_q, D] (16-bit patterns; n_q query
+        heads share each KV head) over all T cached tokens, in float64:
+        softmax(sm_scale * q K^T) V with K, V from dequantized(), the
+        reading in which the pages' fetch hands attention a dequantized
+        16-bit cache.  Returns float64 [BH, n_q, D]."""
+        dt = self.c.dtype
+        Kf = self.o.widen(self.dequantized("K"), dt).astype(np.float64)
+        Vf = self.o.widen(self.dequantized("V"), dt).astype(np.float64)
+        qf = self.o.widen(np.ascontiguousarray(q), dt).astype(np.float64)
+        return self._softmax_attend(qf, Kf, Vf, sm_scale)
+
+    def attend_exact(self, q, sm_scale):
+        """Decode attention as kivi_cache_attend defines it: as attend(),
+        but over reconstructed() (quantized tokens never rounded to 16 bits)
+        and with sm_scale taken as the fp32 value the call receives.
+        Returns float64 [BH, n_q, D]."""
+        dt = self.c.dtype
+        qf = self.o.widen(np.ascontiguousarray(q), dt).astype(np.float64)
+        sm = float(np.float32(sm_scale))
+        return self._softmax_attend(qf, self.reconstructed("K"),
+                                    self.reconstructed("V"), sm)
 
     def append(self, k_new, v_new):
         k_new = np.ascontiguousarray(k_new, dtype=np.uint16)

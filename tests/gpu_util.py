@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: moving uint16 bit patterns between numpy
 and torch device tensors, and comparing GPU outputs with the oracle's."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -12,6 +14,19 @@ TORCH_DT = {FP16: torch.float16, BF16: torch.bfloat16}
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def by_blocks(n, fn, threads=None):
+    """fn(a, b) over contiguous blocks [a, b) that cover range(n), on a
+    thread pool of up to 16 threads (the oracle's C calls release the GIL,
+    so blocks of slices run in parallel); returns the results in order and
+    re-raises the first failure."""
+    threads = max(1, min(threads or min(16, os.cpu_count() or 1), n))
+    cuts = np.linspace(0, n, threads + 1).astype(int)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        futs = [ex.submit(fn, int(a), int(b))
+                for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+        return [f.result() for f in futs]
 
 
 def to_dev(bits16, dtype, device="cuda"):

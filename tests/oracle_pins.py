@@ -677,6 +677,93 @@ def pin_attend_closed_forms(o):
     assert np.allclose(got, vf.repeat(3, 1), rtol=0, atol=0)
 
 
+def _grid_tokens(rng, BH, n, D, bits, G, keys):
+    """fp16 tokens [BH, n, D] that lie on their quantization groups' grids:
+    every key group (G tokens of one channel; keys=True) or value group
+    (G channels of one token) has its own zero (a multiple of 1/4 in
+    [-4, 4)) and power-of-two step (1/4 .. 1/32), and holds both code 0
+    and code 2^bits - 1, so the quantizer must return exactly that zero and
+    step and the element's own code."""
+    maxc = 2 ** bits - 1
+    codes = rng.integers(0, maxc + 1, size=(BH, n, D))
+    if keys:
+        ng = (n + G - 1) // G
+        codes[:, 0::G, :] = 0
+        codes[:, 1::G, :] = maxc
+        zero = rng.integers(-16, 16, size=(BH, ng, D)) * 0.25
+        step = 2.0 ** -rng.integers(2, 6, size=(BH, ng, D)).astype(float)
+        zero = np.repeat(zero, G, axis=1)[:, :n]
+        step = np.repeat(step, G, axis=1)[:, :n]
+    else:
+        ng = (D + G - 1) // G
+        codes[:, :, 0::G] = 0
+        codes[:, :, 1::G] = maxc
+        zero = rng.integers(-16, 16, size=(BH, n, ng)) * 0.25
+        step = 2.0 ** -rng.integers(2, 6, size=(BH, n, ng)).astype(float)
+        zero = np.repeat(zero, G, axis=2)[:, :, :D]
+        step = np.repeat(step, G, axis=2)[:, :, :D]
+    f = zero + codes * step
+    x = f.astype(np.float16)
+    assert np.array_equal(x.astype(np.float64), f)     # exact in fp16
+    return x.view(np.uint16)
+
+
+def pin_attend_exact_reconstruction(o):
+    """kivi_cache_attend's contract reconstructs a quantized token as
+    code * scale + zero of its own group, never rounded to 16 bits.  On
+    tokens that lie on their groups' grids (each group with its own zero and
+    step) that reconstruction must give back the stored tokens exactly, so
+    the oracle's reconstructed() picks each token's codes and each group's
+    params; and on random tokens, rounded to fp16, it is within one ulp of
+    the plain dequantizers' output (which round once from fp32) and equal
+    to it almost everywhere."""
+    rng = np.random.default_rng(61)
+    BH, D, T = 2, 64, 300
+    for bits, Gk, Gv in ((2, 32, 32), (4, 16, 64), (2, 8, 16)):
+        kg = _grid_tokens(rng, BH, T, D, bits, Gk, keys=True)
+        vg = _grid_tokens(rng, BH, T, D, bits, Gv, keys=False)
+        c = o.cache(BH, D, T, 32, Gk, Gv, bits, FP16)
+        c.append(kg, vg)
+        assert c.Q > 0
+        for which, x in (("K", kg), ("V", vg)):
+            want = o.widen(x[:, :c.T], FP16).astype(np.float64)
+            assert np.array_equal(c.reconstructed(which), want), (bits, which)
+        q = _tokens(62, BH, 3, D)
+        got = c.attend_exact(q, 0.125)
+        ref = _sdpa_f64(o.widen(q, FP16).astype(np.float64),
+                        o.widen(kg, FP16).astype(np.float64),
+                        o.widen(vg, FP16).astype(np.float64), 0.125)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    c = o.cache(3, 64, 320, 32, 32, 32, 2, FP16)
+    c.append(_tokens(63, 3, 300, 64), _tokens(64, 3, 300, 64))
+    for which in ("K", "V"):
+        r16 = c.reconstructed(which).astype(np.float16).view(np.uint16)
+        d = c.dequantized(which)
+        ia = np.where(r16 & 0x8000, 0x8000 - (r16 & 0x7FFF), 0x8000 + r16)
+        ib = np.where(d & 0x8000, 0x8000 - (d & 0x7FFF), 0x8000 + d)
+        diff = np.abs(ia.astype(np.int64) - ib)
+        assert diff.max() <= 1 and (diff == 0).mean() > 0.99, which
+
+
+def pin_attend_exact_matches_library_sdpa(o):
+    """attend_exact() against torch's SDPA (float64, CPU) over
+    reconstructed() keys and values, with sm_scale rounded to fp32 as the
+    call receives it; bf16 and fp16, with and without quantized tokens."""
+    for dtype, T, R, bits, Gk, Gv in ((FP16, 300, 32, 2, 32, 32),
+                                      (BF16, 200, 5, 4, 16, 64),
+                                      (BF16, 40, 32, 2, 32, 32)):
+        c = o.cache(2, 64, 320, R, Gk, Gv, bits, dtype)
+        c.append(_tokens(71, 2, T, 64), _tokens(72, 2, T, 64))
+        q = _tokens(73, 2, 4, 64)
+        sm = 1.0 / np.sqrt(3.0)
+        got = c.attend_exact(q, sm)
+        ref = _sdpa_f64(o.widen(q, dtype).astype(np.float64),
+                        c.reconstructed("K"), c.reconstructed("V"),
+                        float(np.float32(sm)))
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), (dtype, T)
+        assert float(np.float32(sm)) != sm     # the fp32 rounding is real
+
+
 # --------------------------------------------------------------------------
 # KIVI-Sink (PyPI page of VeloxQuant-MLX 0.24.1, section "KVSink-adapted
 # sink protection")

@@ -18,7 +18,7 @@ import oracle                                              # noqa: E402
 import workloads as W                                      # noqa: E402
 from gpu_util import (FP16, BF16, TORCH_DT, assert_codes_equal,   # noqa: E402
                       assert_f32_bits_equal, assert_recon_equal, bits16,
-                      host, say, to_dev, to_dev_raw)
+                      by_blocks, host, say, to_dev, to_dev_raw)
 
 
 @pytest.fixture(scope="module")
@@ -136,56 +136,68 @@ def test_mixed_end_to_end(K, O):
     assert_recon_equal(bits16(outs[1]), O.mixed_recon(v, FP16, H, n_hi, 4, 2, 32, k), "values")
 
 
-def test_mixed_full_size_sampled(K, O):
-    """The benchmark's prompt in the benchmark's launch shape: the lists
-    against the oracle's partition of the GPU scores (sampled scores checked
-    exactly), then sampled key groups and value rows of both sets: codes,
-    params, and the rows both sets' dequantizers wrote back."""
+@pytest.mark.timeout(900)
+def test_mixed_full_size(K, O):
+    """The benchmark's step on the benchmark's prompt, compared in full:
+    every score, both position lists, the codes and params of every key
+    group and value row of both sets (keys from K, values from V), and the
+    key and value tensors both sets' dequantizers wrote back, against the
+    oracle run over blocks of sequences on a thread pool."""
     mw = W.MIXED_WORKLOADS["mixed-prefill"]
     w = mw.tokens()
     B, H, S, D, n_hi = mw.B, mw.H, mw.S, mw.D, mw.n_hi
-    say(f"[mixed full size {mw.name}]")
+    say(f"[mixed full size {mw.name}] generating")
     k = W.gen_tensor(w, "K")
-    kd = to_dev(k, w.dtype)
+    v = W.gen_tensor(w, "V")
+    kd, vd = to_dev(k, w.dtype), to_dev(v, w.dtype)
     score = K.kivi_key_scores(kd, H=H)
     hi, lo = K.kivi_partition_top(score, n_hi)
-    sets = {}
-    k_out, v_out = torch.zeros_like(kd), torch.zeros_like(kd)
+    sets = []
+    k_out, v_out = torch.zeros_like(kd), torch.zeros_like(vd)
     for name, pos, bits in (("hi", hi, mw.hi_bits), ("lo", lo, mw.lo_bits)):
         kq = K.kivi_quant_keys_rows(kd, pos, bits, mw.group_k, H=H)
-        vq = K.kivi_quant_values_rows(kd, pos, bits, mw.group_v, H=H)
+        vq = K.kivi_quant_values_rows(vd, pos, bits, mw.group_v, H=H)
         K.kivi_dequant_keys_rows(*kq, pos, k_out, bits, mw.group_k, H=H)
         K.kivi_dequant_values_rows(*vq, pos, v_out, bits, mw.group_v, H=H)
-        sets[name] = (host(pos), bits, kq, vq)
+        sets.append((name, host(pos), bits, [host(t) for t in kq],
+                     [host(t) for t in vq]))
     torch.cuda.synchronize()
-    sc = host(score)
-    ehi, elo = O.partition_top(sc, n_hi)
-    assert np.array_equal(sets["hi"][0], ehi) and np.array_equal(sets["lo"][0], elo)
-    r = np.random.default_rng(6)
-    for b in (0, B - 1):
-        toks = r.choice(S, 30, replace=False)
-        sub = np.ascontiguousarray(k[b * H:(b + 1) * H][:, toks])
-        assert_f32_bits_equal(sc[b, toks], O.sink_scores(sub, w.dtype, H)[0], "scores")
-    for name, (pos, bits, (kc, ks, kz), (vc, vs, vz)) in sets.items():
-        n = pos.shape[1]
-        NG = -(-n // mw.group_k)
-        for bh in (0, 45, B * H - 1):
-            b = bh // H
-            for g in sorted({0, NG - 1, *r.choice(NG, 4, replace=False).tolist()}):
-                j0, j1 = g * mw.group_k, min(n, g * mw.group_k + mw.group_k)
-                tile = np.ascontiguousarray(k[bh:bh + 1, pos[b, j0:j1]])
-                wc, ws, wz = O.quant_keys(tile, w.dtype, bits, mw.group_k)
-                assert_codes_equal(host(kc[bh, j0:j1]), wc[0], f"{name} key codes {bh},{g}")
-                assert_f32_bits_equal(host(ks[bh, g]), ws[0, 0], f"{name} key scale")
-                assert_f32_bits_equal(host(kz[bh, g]), wz[0, 0], f"{name} key zero")
-                want = O.dequant_keys(wc, ws, wz, tile.shape, bits, mw.group_k, w.dtype)
-                assert_recon_equal(bits16(k_out[bh, _ix(pos[b, j0:j1])]), want[0],
-                                   f"{name} key recon {bh},{g}")
-            js = r.choice(n, 8, replace=False)
-            rows = np.ascontiguousarray(k[bh:bh + 1, pos[b, js]])
-            wc, ws, wz = O.quant_values(rows, w.dtype, bits, mw.group_v)
-            assert_codes_equal(host(vc[bh, js]), wc[0], f"{name} value codes")
-            assert_f32_bits_equal(host(vs[bh, js]), ws[0], f"{name} value scale")
-            want = O.dequant_values(wc, ws, wz, rows.shape, bits, mw.group_v, w.dtype)
-            assert_recon_equal(bits16(v_out[bh, _ix(pos[b, js])]), want[0],
-                               f"{name} value recon {bh}")
+    sc, k_out, v_out = host(score), bits16(k_out), bits16(v_out)
+    del kd, vd
+    torch.cuda.empty_cache()
+    say(f"[mixed full size] oracle over all {B} sequences")
+
+    def rows(a, b):
+        return slice(a * H, b * H)
+
+    want_sc = np.concatenate(by_blocks(B, lambda a, b: O.sink_scores(
+        np.ascontiguousarray(k[rows(a, b)]), w.dtype, H)))
+    assert_f32_bits_equal(sc, want_sc, "scores")
+    ehi, elo = O.partition_top(want_sc, n_hi)
+    assert np.array_equal(sets[0][1], ehi) and np.array_equal(sets[1][1], elo)
+
+    def block(a, b):
+        r = rows(a, b)
+        ks, vs_ = np.ascontiguousarray(k[r]), np.ascontiguousarray(v[r])
+        kr = vr = None
+        for name, pos, bits, (kc, kscale, kz), (vc, vscale, vz) in sets:
+            pb = np.ascontiguousarray(pos[a:b])
+            tag = f"{name} seq[{a}:{b}]"
+            wc, ws, wz = O.quant_keys_rows(ks, w.dtype, H, bits, mw.group_k, pb)
+            assert_codes_equal(kc[r], wc, f"{tag} key codes")
+            assert_f32_bits_equal(kscale[r], ws, f"{tag} key scale")
+            assert_f32_bits_equal(kz[r], wz, f"{tag} key zero")
+            kr = O.dequant_keys_rows(wc, ws, wz, ks.shape, H, bits,
+                                     mw.group_k, pb, w.dtype, kr)
+            wc, ws, wz = O.quant_values_rows(vs_, w.dtype, H, bits,
+                                             mw.group_v, pb)
+            assert_codes_equal(vc[r], wc, f"{tag} value codes")
+            assert_f32_bits_equal(vscale[r], ws, f"{tag} value scale")
+            assert_f32_bits_equal(vz[r], wz, f"{tag} value zero")
+            vr = O.dequant_values_rows(wc, ws, wz, vs_.shape, H, bits,
+                                       mw.group_v, pb, w.dtype, vr)
+        assert_recon_equal(k_out[r], kr, f"key recon seq[{a}:{b}]")
+        assert_recon_equal(v_out[r], vr, f"value recon seq[{a}:{b}]")
+
+    by_blocks(B, block)
+    say("[mixed full size] every score, list, group, row and recon equal")

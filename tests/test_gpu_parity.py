@@ -2,10 +2,10 @@
 
 Codes (packed bytes) and fp32 scale/zero must be bit-exact; reconstructions
 are compared bit-exactly as well (the stated bar is one ulp of the output
-type, the path computes the same IEEE operations as the oracle).  Small
-workloads are compared in full; the full-size workloads run on the GPU at
-their real shape, in the same launch configuration the benchmark times, and
-are compared on sampled (bh) slices that the oracle computes on their own.
+type, the path computes the same IEEE operations as the oracle).  Every
+workload is compared in full: the full-size ones run on the GPU at their
+real shape, in the same launch configuration the benchmark times, and the
+oracle covers every (bh) slice, in contiguous blocks on a thread pool.
 """
 import numpy as np
 import pytest
@@ -18,7 +18,7 @@ import oracle                                              # noqa: E402
 import workloads as W                                      # noqa: E402
 from gpu_util import (FP16, BF16, assert_codes_equal,      # noqa: E402
                       assert_f32_bits_equal, assert_recon_equal, bits16,
-                      host, say, to_dev, to_dev_raw)
+                      by_blocks, host, say, to_dev, to_dev_raw)
 
 
 @pytest.fixture(scope="module")
@@ -125,22 +125,29 @@ def test_tiny_constant_groups_hit(K, O):
     assert np.all(O.unpack(host(cv), 64, 2)[2, 10, 32:64] == 0)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tensor", ["K", "V"])
 @pytest.mark.parametrize("name", ["prefill", "serve", "roundtrip"])
-def test_workload_full_size_sampled(K, O, name):
+def test_workload_full_size(K, O, name, tensor):
+    """Every element of the large workloads: the GPU results of all six
+    entry points on one full-size tensor against the oracle on every (bh)
+    slice."""
     w = W.WORKLOADS[name]
-    bhs = W.sample_bhs(w, 4)
-    for tensor in ("K", "V"):
-        tag = f"{name}/{tensor}"
-        say(f"[{tag}] generating {w.BH}x{w.S}x{w.D}")
-        x = W.gen_tensor(w, tensor)
-        got = run_all(K, to_dev(x, w.dtype), w.dtype, w.bits, w.group_k,
-                      w.group_v, tag)
-        del x
-        xs = W.gen_tensor(w, tensor, bhs)
-        compare(O, got, xs, w.dtype, w.bits, w.group_k, w.group_v,
-                f"{tag} bh={bhs}", sel=bhs)
-        del got
-        torch.cuda.empty_cache()
+    tag = f"{name}/{tensor}"
+    say(f"[{tag}] generating {w.BH}x{w.S}x{w.D}")
+    x = W.gen_tensor(w, tensor)
+    got = run_all(K, to_dev(x, w.dtype), w.dtype, w.bits, w.group_k,
+                  w.group_v, tag)
+    torch.cuda.empty_cache()
+    say(f"[{tag}] oracle over all {w.BH} slices")
+
+    def block(a, b):
+        compare(O, {n: g[a:b] for n, g in got.items()},
+                np.ascontiguousarray(x[a:b]), w.dtype, w.bits, w.group_k,
+                w.group_v, f"{tag} bh[{a}:{b}]")
+
+    by_blocks(w.BH, block)
+    say(f"[{tag}] all {w.BH} slices equal")
 
 
 # --------------------------------------------------------------------------

@@ -18,7 +18,7 @@ import oracle                                              # noqa: E402
 import workloads as W                                      # noqa: E402
 from gpu_util import (FP16, BF16, TORCH_DT, assert_codes_equal,   # noqa: E402
                       assert_f32_bits_equal, assert_recon_equal, bits16,
-                      host, say, to_dev, to_dev_raw)
+                      by_blocks, host, say, to_dev, to_dev_raw)
 
 
 @pytest.fixture(scope="module")
@@ -142,41 +142,59 @@ def test_quant_keys_sink_matches_oracle(K, O, case):
         assert np.array_equal(host(ps).view(np.uint32), host(scale).view(np.uint32))
 
 
-def test_sink_full_size_sampled(K, O):
-    """The benchmark's prompt in the benchmark's launch shape: scores on
-    sampled tokens, the sink lists (the top of the GPU's own scores, which
-    are checked exactly where sampled, and the planted tokens), and codes,
-    params and values of sampled key groups against the oracle."""
+@pytest.mark.timeout(900)
+def test_sink_full_size(K, O):
+    """The benchmark's step on the benchmark's prompt, compared in full:
+    every score, the sink lists, the codes and params of every key group
+    with the sinks left out, the plain value quantization of every row and
+    the kept sink rows of K and V, against the oracle run over blocks of
+    sequences on a thread pool."""
     sw = W.SINK_WORKLOADS["sink-prefill"]
     w = sw.tokens()
     B, H, S, D, n = sw.B, sw.H, sw.S, sw.D, sw.n_sink
-    say(f"[sink full size {sw.name}]")
+    say(f"[sink full size {sw.name}] generating")
     x = W.gen_tensor(w, "K")
-    xd = to_dev(x, w.dtype)
+    v = W.gen_tensor(w, "V")
+    xd, vd = to_dev(x, w.dtype), to_dev(v, w.dtype)
     idx_d, score_d = K.kivi_sink_select(xd, n, H=H)
     codes, scale, zero = K.kivi_quant_keys_sink(xd, idx_d, w.bits, w.group_k, H=H)
+    vc, vs, vz = K.kivi_quant_values(vd, w.bits, w.group_v)
+    k_keep = K.kivi_sink_gather(xd, idx_d, H=H)
+    v_keep = K.kivi_sink_gather(vd, idx_d, H=H)
     torch.cuda.synchronize()
     idx, score = host(idx_d), host(score_d)
-    r = np.random.default_rng(5)
-    for b in (0, 6, B - 1):
-        toks = np.sort(np.concatenate([r.choice(S, 40, replace=False), idx[b]]))
-        sub = np.ascontiguousarray(x[b * H:(b + 1) * H][:, toks])
-        assert_f32_bits_equal(score[b, toks], O.sink_scores(sub, w.dtype, H)[0],
-                              f"scores of sequence {b}")
-        assert np.array_equal(idx[b], np.argsort(-score[b], kind="stable")[:n])
+    codes, scale, zero = host(codes), host(scale), host(zero)
+    vc, vs, vz = host(vc), host(vs), host(vz)
+    k_keep, v_keep = bits16(k_keep), bits16(v_keep)
+    del xd, vd
+    torch.cuda.empty_cache()
+    say(f"[sink full size] oracle over all {B} sequences")
+
+    def rows(a, b):
+        return slice(a * H, b * H)
+
+    want_score = np.concatenate(by_blocks(B, lambda a, b: O.sink_scores(
+        np.ascontiguousarray(x[rows(a, b)]), w.dtype, H)))
+    assert_f32_bits_equal(score, want_score, "scores")
+    assert np.array_equal(idx, O.sink_select(want_score, n))
+    for b in range(B):
         assert sorted(idx[b].tolist()) == W.planted_positions(w, b).tolist()
-    NG = S // w.group_k
-    rb = D * w.bits // 8
-    for bh in (0, 17, B * H - 1):
-        b = bh // H
-        groups = sorted({0, NG - 1, *(int(s) // w.group_k for s in idx[b]),
-                         *r.choice(NG, 6, replace=False).tolist()})
-        for g in groups:
-            s0 = g * w.group_k
-            tile = np.ascontiguousarray(x[bh:bh + 1, s0:s0 + w.group_k])
-            local = (idx[b:b + 1] - s0).astype(np.int32)
-            wc, ws, wz = O.quant_keys_sink(tile, w.dtype, 1, w.bits, w.group_k, local)
-            assert_codes_equal(host(codes[bh, s0:s0 + w.group_k]), wc[0], f"codes {bh},{g}")
-            assert_f32_bits_equal(host(scale[bh, g]), ws[0, 0], f"scale {bh},{g}")
-            assert_f32_bits_equal(host(zero[bh, g]), wz[0, 0], f"zero {bh},{g}")
-    assert codes.shape == (B * H, S, rb)
+
+    def block(a, b):
+        r = rows(a, b)
+        xs = np.ascontiguousarray(x[r])
+        ib = np.ascontiguousarray(idx[a:b])
+        wc, ws, wz = O.quant_keys_sink(xs, w.dtype, H, w.bits, w.group_k, ib)
+        assert_codes_equal(codes[r], wc, f"key codes seq[{a}:{b}]")
+        assert_f32_bits_equal(scale[r], ws, f"key scale seq[{a}:{b}]")
+        assert_f32_bits_equal(zero[r], wz, f"key zero seq[{a}:{b}]")
+        assert np.array_equal(k_keep[r], O.sink_gather(xs, H, ib))
+        vs_ = np.ascontiguousarray(v[r])
+        wc, ws, wz = O.quant_values(vs_, w.dtype, w.bits, w.group_v)
+        assert_codes_equal(vc[r], wc, f"value codes seq[{a}:{b}]")
+        assert_f32_bits_equal(vs[r], ws, f"value scale seq[{a}:{b}]")
+        assert_f32_bits_equal(vz[r], wz, f"value zero seq[{a}:{b}]")
+        assert np.array_equal(v_keep[r], O.sink_gather(vs_, H, ib))
+
+    by_blocks(B, block)
+    say("[sink full size] every score, list, group and row equal")
