@@ -66,7 +66,8 @@ typedef enum {
     KIVI_ERR_GROUP = 4,
     KIVI_ERR_DTYPE = 5,
     KIVI_ERR_ALIGN = 6,
-    KIVI_ERR_LAUNCH = 7
+    KIVI_ERR_LAUNCH = 7,
+    KIVI_ERR_SCRATCH = 8
 } kivi_status;
 
 typedef enum { KIVI_FP16 = 0, KIVI_BF16 = 1 } kivi_dtype;
@@ -278,6 +279,28 @@ kivi_status kivi_cache_attend(const kivi_cache* cache, const void* q,
 /* Workspace bytes kivi_cache_attend needs for this cache (at its current T)
  * and n_q; -1 if the arguments are invalid. */
 int64_t kivi_cache_attend_work_bytes(const kivi_cache* cache, int64_t n_q);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kivi_cache_attend with its chunk workspace in a buffer that the library
+ * itself holds on each device, KIVI_ATTEND_SCRATCH_BYTES (32 MiB) per GPU,
+ * kept until the process ends.  Same arguments, results and errors as
+ * kivi_cache_attend, without work / work_bytes; a call whose workspace
+ * (kivi_cache_attend_work_bytes) exceeds the buffer returns
+ * KIVI_ERR_SCRATCH and launches nothing (e.g. 224 KV heads x 3 query heads
+ * at D = 128 fit up to about 12 000 cached tokens).  The call allocates
+ * nothing and does not synchronise; its first call on a device (the current
+ * device) looks up that device's copy of the buffer.  Nothing in the buffer
+ * needs clearing: every call writes each workspace slot it reads.  All
+ * calls on one GPU share that GPU's buffer, so calls that may overlap in
+ * time (on different streams, or from threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.
+ */
+#define KIVI_ATTEND_SCRATCH_BYTES (32ll << 20)
+kivi_status kivi_cache_attend_noalloc(const kivi_cache* cache, const void* q,
+                                      int64_t n_q, float sm_scale, void* out,
+                                      hipStream_t stream);
 
 /*
  * KIVI-Sink (VeloxQuant-MLX 0.24.1 package page, section "KVSink-adapted

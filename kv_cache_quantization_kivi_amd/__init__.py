@@ -42,6 +42,8 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkivi.so")
+# kivi_cache_attend_noalloc's per-device workspace (include/kivi.h)
+ATTEND_SCRATCH_BYTES = 32 << 20
 
 KIVI_FP16 = 0
 KIVI_BF16 = 1
@@ -49,7 +51,7 @@ KIVI_BF16 = 1
 STATUS = {
     0: "KIVI_OK", 1: "KIVI_ERR_NULL", 2: "KIVI_ERR_SHAPE", 3: "KIVI_ERR_BITS",
     4: "KIVI_ERR_GROUP", 5: "KIVI_ERR_DTYPE", 6: "KIVI_ERR_ALIGN",
-    7: "KIVI_ERR_LAUNCH",
+    7: "KIVI_ERR_LAUNCH", 8: "KIVI_ERR_SCRATCH",
 }
 
 
@@ -654,6 +656,25 @@ class KiviCache:
         _check(st, "kivi_cache_attend")
         return out
 
+    def attend_noalloc(self, q, sm_scale, out, stream=None):
+        """As attend(), through kivi_cache_attend_noalloc: the workspace is
+        the library's own per-device buffer and nothing is allocated (out
+        must be given)."""
+        if q.dtype != self.dtype or not q.is_contiguous():
+            raise ValueError("q: a contiguous tensor of the cache's dtype")
+        if out is None or out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out: a tensor shaped and typed like q")
+        L = _lib()
+        L.kivi_cache_attend_noalloc.argtypes = [
+            ctypes.POINTER(_Cache), ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+        L.kivi_cache_attend_noalloc.restype = ctypes.c_int
+        st = L.kivi_cache_attend_noalloc(ctypes.byref(self.c), _ptr(q),
+                                         q.shape[-2], float(sm_scale),
+                                         _ptr(out), _stream(q.device, stream))
+        _check(st, "kivi_cache_attend_noalloc")
+        return out
+
     def attend_work_bytes(self, n_q):
         L = _lib()
         L.kivi_cache_attend_work_bytes.argtypes = [ctypes.POINTER(_Cache),
@@ -665,6 +686,12 @@ class KiviCache:
 def kivi_cache_attend(cache, q, sm_scale, out=None, work=None, stream=None):
     """C-ABI name: decode attention over a KiviCache."""
     return cache.attend(q, sm_scale, out, work, stream)
+
+
+def kivi_cache_attend_noalloc(cache, q, sm_scale, out, stream=None):
+    """C-ABI name: decode attention over a KiviCache with the library's own
+    workspace (allocates nothing)."""
+    return cache.attend_noalloc(q, sm_scale, out, stream)
 
 
 def kivi_cache_attend_work_bytes(cache, n_q):

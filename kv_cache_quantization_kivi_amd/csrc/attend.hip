@@ -15,6 +15,8 @@
 // sum_d (q_d scale_d) code_d + sum_d q_d zero_d, a value enters the output as
 // (p scale) code + p zero, both in fp32; tokens t >= Q come from the ring as
 // stored.  Scores, the softmax and all sums are fp32.
+#include <mutex>
+
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -428,6 +430,37 @@ static hipError_t launch_attend_t(const AttendArgs& a0, int64_t BH,
     return a.D == 64
         ? launch_kernel((attend_merge_kernel<DT, 64>), grid, block, 0, stream, a, pairs)
         : launch_kernel((attend_merge_kernel<DT, 128>), grid, block, 0, stream, a, pairs);
+}
+
+// The workspace of kivi_cache_attend_noalloc: a file-scope device array,
+// one copy per GPU.  Host code never passes the array's own name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address that hipGetSymbolAddress returns for the current device.
+constexpr int64_t kScratchBytes = 32ll << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) float scratch[kScratchBytes / 4];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+int64_t attend_scratch_bytes() { return kScratchBytes; }
+
+hipError_t attend_scratch(float** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<float*>(p);
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
 }
 
 int64_t attend_chunks(int64_t T) { return (T + kAttChunk - 1) / kAttChunk; }

@@ -549,6 +549,26 @@ int64_t kivi_cache_attend_work_bytes(const kivi_cache* c, int64_t n_q) {
     return kivi::attend_work_floats(c->BH, c->T, c->D, n_q) * 4;
 }
 
+namespace {
+
+kivi_status attend_launch(const kivi_cache* c, const void* q, int64_t n_q,
+                          float sm_scale, void* out, float* work,
+                          hipStream_t stream) {
+    kivi::AttendArgs a{
+        c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
+        static_cast<const uint16_t*>(c->k_ring),
+        static_cast<const uint16_t*>(c->v_ring),
+        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
+        work, (int32_t)c->D, (int32_t)c->S_max,
+        (int32_t)c->ring, (int32_t)c->G_k, (int32_t)c->G_v,
+        (int32_t)((c->S_max + c->G_k - 1) / c->G_k),
+        (int32_t)((c->D + c->G_v - 1) / c->G_v), (int32_t)c->T, (int32_t)c->Q,
+        (int32_t)n_q, (int32_t)kivi::attend_chunks(c->T), sm_scale};
+    return launched(kivi::launch_attend(a, c->BH, c->dtype, c->bits, stream));
+}
+
+}  // namespace
+
 kivi_status kivi_cache_attend(const kivi_cache* c, const void* q, int64_t n_q,
                               float sm_scale, void* out, void* work,
                               int64_t work_bytes, hipStream_t stream) {
@@ -560,17 +580,24 @@ kivi_status kivi_cache_attend(const kivi_cache* c, const void* q, int64_t n_q,
     if (work_bytes < kivi::attend_work_floats(c->BH, c->T, c->D, n_q) * 4)
         return KIVI_ERR_SHAPE;
     if (c->BH == 0) return KIVI_OK;
-    kivi::AttendArgs a{
-        c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
-        static_cast<const uint16_t*>(c->k_ring),
-        static_cast<const uint16_t*>(c->v_ring),
-        static_cast<const uint16_t*>(q), static_cast<uint16_t*>(out),
-        static_cast<float*>(work), (int32_t)c->D, (int32_t)c->S_max,
-        (int32_t)c->ring, (int32_t)c->G_k, (int32_t)c->G_v,
-        (int32_t)((c->S_max + c->G_k - 1) / c->G_k),
-        (int32_t)((c->D + c->G_v - 1) / c->G_v), (int32_t)c->T, (int32_t)c->Q,
-        (int32_t)n_q, (int32_t)kivi::attend_chunks(c->T), sm_scale};
-    return launched(kivi::launch_attend(a, c->BH, c->dtype, c->bits, stream));
+    return attend_launch(c, q, n_q, sm_scale, out, static_cast<float*>(work),
+                         stream);
+}
+
+kivi_status kivi_cache_attend_noalloc(const kivi_cache* c, const void* q,
+                                      int64_t n_q, float sm_scale, void* out,
+                                      hipStream_t stream) {
+    kivi_status st = check_attend(c, n_q);
+    if (st != KIVI_OK) return st;
+    if (q == nullptr || out == nullptr) return KIVI_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return KIVI_ERR_ALIGN;
+    if (kivi::attend_work_floats(c->BH, c->T, c->D, n_q) * 4 >
+        kivi::attend_scratch_bytes())
+        return KIVI_ERR_SCRATCH;
+    if (c->BH == 0) return KIVI_OK;
+    float* work = nullptr;
+    if (kivi::attend_scratch(&work) != hipSuccess) return KIVI_ERR_LAUNCH;
+    return attend_launch(c, q, n_q, sm_scale, out, work, stream);
 }
 
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop) {
@@ -613,6 +640,7 @@ const char* kivi_status_string(kivi_status status) {
         case KIVI_ERR_DTYPE: return "dtype must be KIVI_FP16 or KIVI_BF16";
         case KIVI_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case KIVI_ERR_LAUNCH: return "kernel launch failed";
+        case KIVI_ERR_SCRATCH: return "the call needs more workspace than the library's fixed per-device buffer (KIVI_ATTEND_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

@@ -103,6 +103,11 @@ struct AttendArgs {
 };
 int64_t attend_chunks(int64_t T);
 int64_t attend_work_floats(int64_t BH, int64_t T, int64_t D, int64_t n_q);
+// The library-held attention workspace of the current device
+// (attend_scratch_bytes bytes): its device address, looked up on the
+// device's first call.
+hipError_t attend_scratch(float** ptr);
+int64_t attend_scratch_bytes();
 hipError_t launch_attend(const AttendArgs& a, int64_t BH, int dtype, int bits,
                          hipStream_t stream);
 // The matrix-core kernel (attend_mfma.hip) over chunks [0, n_full) of every

@@ -57,7 +57,7 @@ def test_size_helpers(K):
 
 
 def test_status_strings(K):
-    for s in range(8):
+    for s in range(9):
         assert K.kivi_status_string(s)
     assert K.kivi_status_string(0) == "ok"
 
@@ -216,6 +216,47 @@ def test_cache_append_rejects_before_any_launch(K):
     assert call(cache(), k=0) == NULL
     assert call(cache(v_zero=0x80004)) == ALIGN
     assert call(cache(), v=0xA0008) == ALIGN
+
+
+def test_attend_noalloc_rejects_before_any_launch(K):
+    """kivi_cache_attend_noalloc checks the struct, the pointers and the
+    workspace size against the library's fixed buffer before any HIP call
+    (fake aligned pointers): too large a workspace is KIVI_ERR_SCRATCH."""
+    C = K._Cache
+    L = K.raw()
+    L.kivi_cache_attend_noalloc.argtypes = [
+        ctypes.POINTER(C), ctypes.c_void_p, ctypes.c_int64, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p]
+    L.kivi_cache_attend_noalloc.restype = ctypes.c_int
+
+    def cache(**kw):
+        f = dict(BH=224, D=128, S_max=40000, R=32, G_k=32, G_v=32, ring=64,
+                 bits=2, dtype=0, k_ring=0x10000, v_ring=0x20000,
+                 k_codes=0x30000, v_codes=0x40000, k_scale=0x50000,
+                 k_zero=0x60000, v_scale=0x70000, v_zero=0x80000, T=2059,
+                 Q=2016)
+        f.update(kw)
+        return C(*[f[name] for name, _ in C._fields_])
+
+    def call(c, n_q=3, q=0x90000, out=0xA0000):
+        return L.kivi_cache_attend_noalloc(ctypes.byref(c), q, n_q, 0.1, out,
+                                           None)
+
+    NULL, SHAPE, GROUP, ALIGN, SCRATCH = 1, 2, 4, 6, 8
+    assert L.kivi_cache_attend_noalloc(None, 0x90000, 1, 0.1, 0xA0000,
+                                       None) == NULL
+    assert call(cache(), q=0) == NULL
+    assert call(cache(), out=0) == NULL
+    assert call(cache(), out=0xA0008) == ALIGN
+    assert call(cache(), n_q=9) == SHAPE
+    assert call(cache(T=0, Q=0)) == SHAPE
+    assert call(cache(G_k=16, ring=64, D=256)) == SHAPE
+    # workspace = BH * chunks * n_q * (D + 2) * 4 bytes
+    big = cache(T=32000, Q=31968)
+    need = 224 * ((32000 + 127) // 128) * 3 * 130 * 4
+    assert need > K.ATTEND_SCRATCH_BYTES
+    assert call(big) == SCRATCH
+    assert K.kivi_status_string(SCRATCH).startswith("the call needs more")
 
 
 def test_sink_entry_points_reject_before_any_launch(K):
