@@ -324,11 +324,84 @@ __global__ __launch_bounds__(64) void dequant_keys_split_kernel(
                                       scale, zero, n_lanes, D8, NG, S, G, out);
 }
 
+// Large calls of whole groups: the split layout above (four lanes per
+// chunk with interleaved tokens, so that every store instruction writes four
+// consecutive rows of a tile: 1 KiB at D = 128), with the codes read the way
+// the one-lane kernel reads them: the wave's tiles are consecutive rows, so
+// their codes are one contiguous block of 16 * G * BITS bytes, loaded once
+// with 16-byte loads into LDS, from where each lane picks its own.  A wave
+// with lanes past the end takes the unstaged split body.
+template <int DT, int BITS>
+__global__ __launch_bounds__(64) void dequant_keys_staged_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+    const float* __restrict__ zero, uint32_t n_lanes, uint32_t D8,
+    uint32_t NG, int32_t G, uint16_t* __restrict__ out) {
+    static_assert(BITS <= 4, "a wave's block is at most 2 KiB");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[16 * 32 * BITS];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t lid = blockIdx.x * 64u + lane;
+    const int32_t S = (int32_t)NG * G;
+    if (!__all(lid < n_lanes)) {
+        dequant_keys_split_body<DT, BITS>(lid, codes, scale, zero, n_lanes, D8,
+                                          NG, S, G, out);
+        return;
+    }
+    const uint32_t c = lid % D8;
+    const uint32_t part = (lid / D8) % kDqKeySplit;
+    const uint32_t tile = lid / (D8 * kDqKeySplit);
+    const uint32_t tile0 = (blockIdx.x * 64u) / (D8 * kDqKeySplit);
+    const int64_t D = (int64_t)D8 * 8;
+    const int64_t row_bytes = (int64_t)D8 * BITS;
+
+    // the wave's code block: tiles tile0.. are rows tile0 * G.. (S = NG * G)
+    const uint8_t* wsrc = codes + (int64_t)tile0 * G * row_bytes;
+    const uint32_t n16 = (uint32_t)G * BITS;          // 16-byte pieces
+    uint4 t4[2];
+#pragma unroll
+    for (uint32_t k = 0; k < 2; ++k)
+        if (k * 64u + lane < n16) t4[k] = load16_nt(wsrc + (k * 64u + lane) * 16u);
+    const int64_t p = (int64_t)tile * D + (int64_t)c * 8;   // tile = bh * NG + g
+    const float4 s_a = load_f4_nt(scale + p);
+    const float4 s_b = load_f4_nt(scale + p + 4);
+    const float4 z_a = load_f4_nt(zero + p);
+    const float4 z_b = load_f4_nt(zero + p + 4);
+#pragma unroll
+    for (uint32_t k = 0; k < 2; ++k)
+        if (k * 64u + lane < n16)
+            *reinterpret_cast<uint4*>(lds + (k * 64u + lane) * 16u) = t4[k];
+    wave_lds_sync();
+    const float sc[8] = {s_a.x, s_a.y, s_a.z, s_a.w, s_b.x, s_b.y, s_b.z, s_b.w};
+    const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
+
+    const uint8_t* mine = lds + ((tile - tile0) * G + part) * row_bytes + c * BITS;
+    uint16_t* dst = out + ((int64_t)tile * G + part) * D + (int64_t)c * 8;
+    const int32_t n = (G - (int32_t)part + kDqKeySplit - 1) / kDqKeySplit;
+#pragma unroll
+    for (int32_t i = 0; i < 32 / kDqKeySplit; ++i)
+        if (i < n)
+            store16_nt(dst + (int64_t)i * kDqKeySplit * D,
+                       dequant_chunk<DT, BITS>(
+                           lds_codes<BITS>(mine + i * kDqKeySplit * row_bytes), sc, z));
+}
+
 template <int DT, int BITS>
 static hipError_t launch_dq_keys_t(const DequantJob& j) {
     const uint32_t D8 = (uint32_t)(j.D / 8);
-    if ((uint64_t)j.BH * ((j.S + j.group - 1) / j.group) * D8 <
-        kDqKeySplitBelow) {
+    const uint64_t items = (uint64_t)j.BH * ((j.S + j.group - 1) / j.group) * D8;
+    if constexpr (BITS <= 4) {
+        if (items >= kDqKeySplitBelow && 64 % (D8 * kDqKeySplit) == 0 &&
+            j.group <= 32 && j.S % j.group == 0 &&
+            items * kDqKeySplit < (1ull << 32)) {
+            const uint32_t NG = (uint32_t)(j.S / j.group);
+            const uint64_t n_lanes = items * kDqKeySplit;
+            return launch_kernel((dequant_keys_staged_kernel<DT, BITS>),
+                                 dim3((uint32_t)((n_lanes + 63) / 64)), dim3(64),
+                                 0, j.stream, j.codes, j.scale, j.zero,
+                                 (uint32_t)n_lanes, D8, NG, (int32_t)j.group,
+                                 static_cast<uint16_t*>(j.out));
+        }
+    }
+    if (items < kDqKeySplitBelow) {
         const uint32_t NG = (uint32_t)((j.S + j.group - 1) / j.group);
         const uint64_t n_lanes = (uint64_t)j.BH * NG * D8 * kDqKeySplit;
         return launch_kernel((dequant_keys_split_kernel<DT, BITS>),
