@@ -98,6 +98,83 @@ PAIRED = {"quant_kv": ("quant_keys", "quant_values"),
           "dequant_kv": ("dequant_keys", "dequant_values")}
 
 
+class Dispatches:
+    """The library's kernel dispatches in the order the GPU runs them,
+    counted with kivi_launch_count, so that a profiler's dispatch trace can
+    be split into this run's phases: an eager launch dispatches once, a
+    launch recorded into a graph under capture dispatches at every replay."""
+
+    def __init__(self, K):
+        self.K = K
+        self.mark = K.kivi_launch_count()
+        self.n = self.mark          # every earlier launch was eager
+
+    def eager(self):
+        c = self.K.kivi_launch_count()
+        self.n += c - self.mark
+        self.mark = c
+
+    def captured(self):
+        """Launches recorded into a graph since the last call: their number
+        (nothing is dispatched)."""
+        c = self.K.kivi_launch_count()
+        k = c - self.mark
+        self.mark = c
+        return k
+
+    def replayed(self, k):
+        self.n += k
+
+
+def launch_labels(K, calls):
+    """Run calls = [(name, fn)] once, in order, and label every kernel they
+    launch: a call that launches n kernels gives name, name#2, ... name#n
+    (the first is the one its per-kernel timing arms)."""
+    labels = []
+    for name, fn in calls:
+        c0 = K.kivi_launch_count()
+        fn()
+        n = K.kivi_launch_count() - c0
+        labels += [name] + [f"{name}#{k}" for k in range(2, n + 1)]
+    return labels
+
+
+def profile_layout(before, timed, labels):
+    return {"dispatches_before_timed": int(before),
+            "timed_dispatches": int(timed), "step_launches": labels}
+
+
+def launch_bound(args, step_bytes, launches):
+    """Whether the timed steps are HIP graph replays: asked for, or (auto) a
+    launch-bound step, under 16 MB of traffic per launch (a decode-time
+    flush, one-token cache appends).  Longer launches are issued eagerly: the
+    host then stays ahead of the GPU, and a replay costs several
+    microseconds more than it saves (a 2048-token cache append: 27.4 us a
+    step eagerly, 32.8 us replayed)."""
+    if args.launch != "auto":
+        return args.launch == "graphs"
+    return step_bytes / max(1, launches) < 16e6
+
+
+def call_intervals(torch, stream, step, n_calls, n_steps, base):
+    """Per call of a step, its duration in each of n_steps more steps
+    launched as in the timed region, with a plain event recorded on the
+    launch stream before the step and after every call
+    (step(i, mark) calls mark(j) after call j): the interval that ends with
+    a call holds its kernels and the dispatch gap before them, back to back
+    with the rest of the step, so a step's intervals add up to the step.
+    Returns n_calls lists of milliseconds."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+          for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        ev[i][0].record(stream)
+        step(base + i, lambda j, i=i: ev[i][j + 1].record(stream))
+    torch.cuda.synchronize()
+    return [[ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_steps)]
+            for j in range(n_calls)]
+
+
 def make_steps(K, w, pool_inputs, torch, paired=False):
     """Pre-allocated outputs and the list of (name, op, bytes, launch fn)
     that make one step.  Every launch goes to torch's current stream and
@@ -425,12 +502,36 @@ def cache_bench(args, cw, K, torch, dev):
                 K.kivi_time_next_launch(*arm[a])
             cache.append(ks[a], vs[a])
 
-    for i in range(args.warmup):
+    disp = Dispatches(K)
+    cache.c.T, cache.c.Q = T0, Q0
+    n_launch = []            # launches of each append (the first step)
+    for a in range(cw.appends):
+        c0 = K.kivi_launch_count()
+        cache.append(pool[0][0][a], pool[0][1][a])
+        n_launch.append(K.kivi_launch_count() - c0)
+
+    def append_kind(a):
+        """The per-kernel name of append a's first launch: the flush (of K
+        and V together when it is one launch, and with the ring store too
+        when that is the append's only launch), else the ring store."""
+        F, cp = plan[a][3], plan[a][4]
+        if not F:
+            return "cache_ring_store"
+        if not cache_flush_paired(cw, F):
+            return "cache_flush_keys"
+        return "cache_append_kv" if cp and n_launch[a] == 1 else "cache_flush_kv"
+
+    labels = []
+    for a in range(cw.appends):
+        labels += [append_kind(a)] + [f"{append_kind(a)}#{k}"
+                                      for k in range(2, n_launch[a] + 1)]
+    for i in range(1, args.warmup):
         step(i)
+    base = max(args.warmup, 1)
     torch.cuda.synchronize()
-    use_graphs = (args.launch == "graphs" or
-                  (args.launch == "auto" and step_bytes < 256e6))
+    use_graphs = launch_bound(args, step_bytes, len(labels))
     graphs = None
+    disp.eager()
     if use_graphs:
         graphs = []
         cap = torch.cuda.Stream(device=dev)
@@ -438,21 +539,27 @@ def cache_bench(args, cw, K, torch, dev):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 step(ph)
-            graphs.append(g)
+            graphs.append((g, disp.captured()))
             g.replay()
+            disp.replayed(graphs[-1][1])
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    before = disp.n
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         if graphs is not None:
-            graphs[(args.warmup + i) % P].replay()
+            g, k = graphs[(base + i) % P]
+            g.replay()
+            disp.replayed(k)
         else:
-            step(args.warmup + i)
+            step(base + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    disp.eager()
+    layout = profile_layout(before, disp.n - before, labels)
     ms_per_step = start.elapsed_time(end) / args.steps
 
     # kernel durations: the first kernel of every append (the key flush when
@@ -469,16 +576,14 @@ def cache_bench(args, cw, K, torch, dev):
     arms = [pairs() for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, arms[i])
+        step(base + args.steps + i, arms[i])
     torch.cuda.synchronize()
     kinds = {}
     for a, (_, _, n, F, cp) in enumerate(plan):
-        # the first launch of the append: the flush (of K and V together
-        # when it is one launch), else the ring store
-        paired = F and cache_flush_paired(cw, F)
-        name = ("cache_flush_kv" if paired else "cache_flush_keys") if F \
-            else "cache_ring_store"
-        b = (cache_bytes(cw, F, cp, flush_only=True) if paired
+        name = append_kind(a)
+        b = (cache_bytes(cw, F, cp) if name == "cache_append_kv"
+             else cache_bytes(cw, F, cp, flush_only=True)
+             if name == "cache_flush_kv"
              else cache_bytes(cw, F, cp, keys_flush_only=True) if F
              else cw.BH * cp * cw.D * 2 * 2 * 2)
         d = [arms[i][a][0].elapsed_time(arms[i][a][1])
@@ -540,6 +645,7 @@ def cache_bench(args, cw, K, torch, dev):
                             "per_kernel: the first kernel of every append of "
                             "a second pass of K eager steps"),
         "kernel_source_hash": kernel_source_hash("cache"),
+        "profile_layout": dict(layout, per_kernel_timing="first_launch"),
         "cpu_baseline": (None if args.no_cpu_baseline else
                          cache_cpu_baseline(cw, args.cpu_threads, plan,
                                             step_bytes)),
@@ -594,11 +700,14 @@ def attend_bench(args, aw, K, torch, dev):
     def step(i):
         caches[i % P].attend(qs[i % P], sm, out=out, work=work)
 
-    for i in range(args.warmup):
+    disp = Dispatches(K)
+    labels = launch_labels(K, [("attend_chunks", lambda: step(0))])
+    for i in range(1, args.warmup):
         step(i)
-    use_graphs = (args.launch == "graphs" or
-                  (args.launch == "auto" and step_bytes < 256e6))
+    base = max(args.warmup, 1)
+    use_graphs = launch_bound(args, step_bytes, len(labels))
     graphs = None
+    disp.eager()
     if use_graphs:
         graphs = []
         cap = torch.cuda.Stream(device=dev)
@@ -606,21 +715,27 @@ def attend_bench(args, aw, K, torch, dev):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=cap):
                 step(ph)
-            graphs.append(g)
+            graphs.append((g, disp.captured()))
             g.replay()
+            disp.replayed(graphs[-1][1])
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    before = disp.n
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         if graphs is not None:
-            graphs[(args.warmup + i) % P].replay()
+            g, k = graphs[(base + i) % P]
+            g.replay()
+            disp.replayed(k)
         else:
-            step(args.warmup + i)
+            step(base + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    disp.eager()
+    layout = profile_layout(before, disp.n - before, labels)
     ms_per_step = start.elapsed_time(end) / args.steps
 
     # the attention kernel proper (the first of the call's two launches)
@@ -632,7 +747,7 @@ def attend_bench(args, aw, K, torch, dev):
     torch.cuda.synchronize()
     for i in range(args.steps):
         K.kivi_time_next_launch(*ev[i])
-        step(args.warmup + args.steps + i)
+        step(base + args.steps + i)
     torch.cuda.synchronize()
     d = [a_.elapsed_time(b_) for a_, b_ in ev]
     kb = step_bytes - out_bytes
@@ -704,6 +819,7 @@ def attend_bench(args, aw, K, torch, dev):
         },
         "per_kernel": pk,
         "kernel_source_hash": kernel_source_hash("attend"),
+        "profile_layout": dict(layout, per_kernel_timing="first_launch"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -756,66 +872,67 @@ def sink_bench(args, sw, K, torch, dev):
     k_keep = torch.empty((B, H, sw.n_sink, D), dtype=tdt, device=dev)
     v_keep = torch.empty_like(k_keep)
     stream = torch.cuda.current_stream(dev)
-    names = ["sink_score", "quant_keys_sink", "quant_values", "sink_gather_k",
+    names = ["sink_select", "quant_keys_sink", "quant_values", "sink_gather_k",
              "sink_gather_v"]
+    call_bytes = dict(nb)
+    call_bytes["sink_select"] = nb["sink_score"] + nb["sink_select"]
 
-    def step(i, arm=None):
+    calls = [
+        lambda k, v: K.kivi_sink_select(k, sw.n_sink, score=score, idx=idx),
+        lambda k, v: K.kivi_quant_keys_sink(k, idx, sw.bits, sw.group_k,
+                                            codes=kc, scale=ks, zero=kz),
+        lambda k, v: K.kivi_quant_values(v, sw.bits, sw.group_v, codes=vc,
+                                         scale=vs, zero=vz),
+        lambda k, v: K.kivi_sink_gather(k, idx, out=k_keep),
+        lambda k, v: K.kivi_sink_gather(v, idx, out=v_keep),
+    ]
+
+    def step(i, mark=None):
         k, v = inputs[i % P]
-        if arm == 0:
-            K.kivi_time_next_launch(*ev)
-        K.kivi_sink_select(k, sw.n_sink, score=score, idx=idx)
-        if arm == 1:
-            K.kivi_time_next_launch(*ev)
-        K.kivi_quant_keys_sink(k, idx, sw.bits, sw.group_k, codes=kc,
-                               scale=ks, zero=kz)
-        if arm == 2:
-            K.kivi_time_next_launch(*ev)
-        K.kivi_quant_values(v, sw.bits, sw.group_v, codes=vc, scale=vs, zero=vz)
-        if arm == 3:
-            K.kivi_time_next_launch(*ev)
-        K.kivi_sink_gather(k, idx, out=k_keep)
-        if arm == 4:
-            K.kivi_time_next_launch(*ev)
-        K.kivi_sink_gather(v, idx, out=v_keep)
+        for a, fn in enumerate(calls):
+            fn(k, v)
+            if mark is not None:
+                mark(a)
 
-    ev = None
-    for i in range(args.warmup):
+    disp = Dispatches(K)
+    labels = launch_labels(K, [(n, lambda fn=fn: fn(*inputs[0]))
+                               for n, fn in zip(names, calls)])
+    for i in range(1, args.warmup):
         step(i)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    base = max(args.warmup, 1)
+    disp.eager()
+    before = disp.n
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(base + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    disp.eager()
+    layout = profile_layout(before, disp.n - before, labels)
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # per call: its interval between plain events recorded between the
+    # calls of K more back-to-back steps (call_intervals)
     pk = {}
-    base = args.warmup + args.steps
+    iv = call_intervals(torch, stream, step, len(calls), args.steps,
+                        base + args.steps)
     for a, name in enumerate(names):
-        d = []
-        for i in range(args.steps):
-            ev = (torch.cuda.Event(enable_timing=True),
-                  torch.cuda.Event(enable_timing=True))
-            ev[0].record(stream)   # torch times only events it has recorded;
-            ev[1].record(stream)   # the armed launch then re-records both
-            step(base + i, arm=a)
-            torch.cuda.synchronize()
-            d.append(ev[0].elapsed_time(ev[1]))
-        base += args.steps
+        d = iv[a]
         avg = float(np.mean(d))
-        b = nb[name]
+        b = call_bytes[name]
         pk[name] = {"avg_us": round(avg * 1e3, 3),
                     "median_us": round(float(np.median(d)) * 1e3, 3),
                     "min_us": round(float(np.min(d)) * 1e3, 3),
                     "max_us": round(float(np.max(d)) * 1e3, 3),
                     "algorithmic_bytes": int(b),
                     "gbs": round(b / (avg * 1e-3) / 1e9, 1)}
-    ev = None
-    dom = max(("sink_score", "quant_keys_sink"), key=lambda n: pk[n]["avg_us"])
+    layout["per_kernel_timing"] = "calls"
+    dom = max(pk, key=lambda n: pk[n]["avg_us"])
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     cpu = None
@@ -874,6 +991,7 @@ def sink_bench(args, sw, K, torch, dev):
         },
         "per_kernel": pk,
         "kernel_source_hash": kernel_source_hash("sink"),
+        "profile_layout": layout,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -950,48 +1068,48 @@ def mixed_bench(args, mw, K, torch, dev):
         calls.append((f"dequant_values_{name}", lambda k, v, pos=pos, bits=bits, vb=vb:
                       K.kivi_dequant_values_rows(*vb, pos, v_out, bits, mw.group_v)))
 
-    def step(i, arm=None):
+    def step(i, mark=None):
         k, v = inputs[i % P]
         for a, (_, fn) in enumerate(calls):
-            if a == arm:
-                K.kivi_time_next_launch(*ev)
             fn(k, v)
+            if mark is not None:
+                mark(a)
 
-    ev = None
-    for i in range(args.warmup):
+    disp = Dispatches(K)
+    labels = launch_labels(K, [(n, lambda fn=fn: fn(*inputs[0]))
+                               for n, fn in calls])
+    for i in range(1, args.warmup):
         step(i)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    base = max(args.warmup, 1)
+    disp.eager()
+    before = disp.n
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(base + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    disp.eager()
+    layout = profile_layout(before, disp.n - before, labels)
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # per call: its interval between plain events recorded between the
+    # calls of K more back-to-back steps (call_intervals)
     pk = {}
-    base = args.warmup + args.steps
-    n_time = max(5, args.steps // 4)
+    iv = call_intervals(torch, stream, step, len(calls), args.steps,
+                        base + args.steps)
     for a, (name, _) in enumerate(calls):
-        d = []
-        for i in range(n_time):
-            ev = (torch.cuda.Event(enable_timing=True),
-                  torch.cuda.Event(enable_timing=True))
-            ev[0].record(stream)   # torch times only events it has recorded;
-            ev[1].record(stream)   # the armed launch then re-records both
-            step(base + i, arm=a)
-            torch.cuda.synchronize()
-            d.append(ev[0].elapsed_time(ev[1]))
-        base += n_time
+        d = iv[a]
         avg = float(np.mean(d))
         pk[name] = {"avg_us": round(avg * 1e3, 3),
                     "median_us": round(float(np.median(d)) * 1e3, 3),
                     "algorithmic_bytes": int(nb[name]),
                     "gbs": round(nb[name] / (avg * 1e-3) / 1e9, 1)}
-    ev = None
+    layout["per_kernel_timing"] = "calls"
     dom = max(pk, key=lambda n: pk[n]["avg_us"])
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -1052,9 +1170,288 @@ def mixed_bench(args, mw, K, torch, dev):
         },
         "per_kernel": pk,
         "kernel_source_hash": kernel_source_hash("mixed"),
+        "profile_layout": layout,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (profiles/): the recipe and the summarizers
+# --------------------------------------------------------------------------
+
+def profile_recipe(workload, repo="<repo>", out="<dir>"):
+    """The commands behind a workload's profiles: a plain run, a
+    kernel-trace run and one counter pass per counter, all of the same
+    launch configuration as the default benchmark run; the counter scale
+    comes from a plain device copy of known size (--calibrate-copy)."""
+    b = f"python3 {repo}/bench.py --workload {workload} --no-cpu-baseline"
+    return {
+        "plain": f"{b} --steps 20 --warmup 3 > {out}/plain.json",
+        "trace": (f"rocprofv3 --kernel-trace --stats -f csv -d {out}/trace "
+                  f"-o bench -- {b} --steps 20 --warmup 3 > {out}/profiled.json"),
+        "fetch": (f"rocprofv3 --pmc FETCH_SIZE -f csv -d {out}/pmc_fetch -o bench"
+                  f" -- {b} --steps 2 --warmup 1 > {out}/fetch.json"),
+        "write": (f"rocprofv3 --pmc WRITE_SIZE -f csv -d {out}/pmc_write -o bench"
+                  f" -- {b} --steps 2 --warmup 1 > {out}/write.json"),
+        "copy_fetch": (f"rocprofv3 --pmc FETCH_SIZE -f csv -d <copydir>/fetch -o "
+                       f"copy -- python3 {repo}/bench.py --calibrate-copy 512 "
+                       "--steps 3"),
+        "copy_write": (f"rocprofv3 --pmc WRITE_SIZE -f csv -d <copydir>/write -o "
+                       f"copy -- python3 {repo}/bench.py --calibrate-copy 512 "
+                       "--steps 3"),
+    }
+
+
+def _json_line(path):
+    """The benchmark's result line in a captured stdout."""
+    found = None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                try:
+                    d = json.loads(line)
+                except ValueError:
+                    continue
+                if "metric" in d or "calibration" in d:
+                    found = d
+    if found is None:
+        raise SystemExit(f"no result line in {path}")
+    return found
+
+
+def _one_csv(d, suffix):
+    import glob
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if len(hits) != 1:
+        raise SystemExit(f"expected one *{suffix} under {d}, found {hits}")
+    return hits[0]
+
+
+def _template(name):
+    """The kernel's template signature without its parameter list."""
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _library_dispatches(rows, value_of=None):
+    """Per dispatch of a library kernel (name in namespace kivi), in the
+    order the GPU ran them: (kernel name, start, end, value) where value
+    comes from value_of(rows of that dispatch) (counter runs) or None."""
+    import collections
+    by = collections.OrderedDict()
+    for r in rows:
+        if "kivi::" not in r["Kernel_Name"]:
+            continue
+        by.setdefault(r["Dispatch_Id"], []).append(r)
+    out = []
+    for rs in by.values():
+        r0 = rs[0]
+        out.append((r0["Kernel_Name"], int(r0["Start_Timestamp"]),
+                    int(r0["End_Timestamp"]),
+                    value_of(rs) if value_of else None))
+    out.sort(key=lambda x: x[1])
+    return out
+
+
+def _timed(disp, layout):
+    """The dispatches of the timed region, each with its step label."""
+    a = layout["dispatches_before_timed"]
+    n = layout["timed_dispatches"]
+    labels = layout["step_launches"]
+    if len(disp) < a + n or n % len(labels):
+        raise SystemExit(f"trace holds {len(disp)} library dispatches; the "
+                         f"layout asks for {a} + {n} ({len(labels)} a step)")
+    sel = disp[a:a + n]
+    return [(labels[j % len(labels)],) + d for j, d in enumerate(sel)]
+
+
+def summarize_trace(d, workload):
+    import csv
+    prof = _json_line(os.path.join(d, "profiled.json"))
+    plain = _json_line(os.path.join(d, "plain.json"))
+    rows = list(csv.DictReader(open(_one_csv(os.path.join(d, "trace"),
+                                             "kernel_trace.csv"))))
+    disp = _library_dispatches(rows)
+    timed = _timed(disp, prof["profile_layout"])
+    per = {}
+    for label, name, t0, t1, _ in timed:
+        e = per.setdefault(label, {"template": _template(name), "d": []})
+        if e["template"] != _template(name):
+            raise SystemExit(f"label {label} maps to two kernels")
+        e["d"].append((t1 - t0) / 1e3)
+    lay = prof["profile_layout"]
+    timing = lay.get("per_kernel_timing", "first_launch")
+    n_l = len(lay["step_launches"])
+    per_call = {}          # call -> its launches' summed duration per step
+    for idx, (label, _, t0, t1, _) in enumerate(timed):
+        c = per_call.setdefault(label.split("#")[0], {})
+        c[idx // n_l] = c.get(idx // n_l, 0.0) + (t1 - t0) / 1e3
+    alld = {}
+    for name, t0, t1, _ in disp:
+        alld.setdefault(_template(name), []).append((t1 - t0) / 1e3)
+    rec = profile_recipe(workload)
+    fam = ("cache" if workload in W.CACHE_WORKLOADS else "attend"
+           if workload in W.ATTEND_WORKLOADS else "sink"
+           if workload in W.SINK_WORKLOADS else "mixed"
+           if workload in W.MIXED_WORKLOADS else "flush")
+    L = []
+    L.append(f"# rocprofv3 kernel trace: {workload}\n")
+    L.append(f"workload: {plain['config']['workload']}\n")
+    L.append("commands (run from /tmp with TMPDIR=/tmp, one after the other "
+             "on one GPU):")
+    L.append(f"  {rec['plain']}")
+    L.append(f"  {rec['trace']}")
+    L.append(f"  python3 <repo>/bench.py --summarize-trace <dir> --workload "
+             f"{workload}   (this summary)\n")
+    L.append(f"kernel source hash (bench.py kernel_source_hash, family {fam}): "
+             f"{kernel_source_hash(fam)}; profiled run's hash "
+             f"{prof.get('kernel_source_hash')}\n")
+    L.append(f"Timed region of the profiled run: library dispatches "
+             f"{lay['dispatches_before_timed']} .. "
+             f"{lay['dispatches_before_timed'] + lay['timed_dispatches'] - 1} "
+             f"({prof['steps']} steps of {len(lay['step_launches'])} launches; "
+             f"launch: {plain['config'].get('launch')}), per launch of a step:")
+    pk_plain = plain.get("per_kernel", {})
+    pk_prof = prof.get("per_kernel", {})
+    L.append(f"{'launch':24s} {'n':>4s} {'rocprof avg us':>15s} {'min':>8s} "
+             f"{'max':>8s} {'events, plain run':>18s}   template")
+    for label, e in per.items():
+        dd = e["d"]
+        ev = pk_plain.get(label, {}).get("avg_us")
+        L.append(f"{label:24s} {len(dd):4d} {np.mean(dd):15.2f} {min(dd):8.2f} "
+                 f"{max(dd):8.2f} {ev if ev is not None else '-':>18}   "
+                 f"{e['template']}")
+    if timing == "calls":
+        L.append("\nPer call (its launches summed), against the benchmark's "
+                 "own per-call intervals (plain events between the calls of "
+                 "back-to-back steps, each interval also holding the dispatch "
+                 "gap before the call):")
+        L.append(f"{'call':24s} {'rocprof avg us':>15s} {'intervals, plain':>17s}"
+                 f" {'intervals, profiled':>20s}")
+        for c, dd in per_call.items():
+            a = pk_plain.get(c, {}).get("avg_us")
+            b = pk_prof.get(c, {}).get("avg_us")
+            L.append(f"{c:24s} {np.mean(list(dd.values())):15.2f} "
+                     f"{a if a is not None else '-':>17} "
+                     f"{b if b is not None else '-':>20}")
+    L.append("\nEvery dispatch of the run (setup, warmup, timed region, "
+             "per-kernel pass), for reference:")
+    for t, dd in alld.items():
+        L.append(f"  {len(dd):4d} x {np.mean(dd):9.2f} us avg   {t}")
+    dom = plain["roofline"]["kernel"]
+    b = pk_plain[dom]["algorithmic_bytes"]
+    avg = (float(np.mean(list(per_call[dom].values()))) if timing == "calls"
+           else float(np.mean(per[dom]["d"])))
+    gbs = b / (avg * 1e-6) / 1e9
+    L.append(f"\ndominant kernel {dom}: {b} algorithmic bytes / {avg:.2f} us "
+             f"(rocprof, timed region) = {gbs:.1f} GB/s, frac {gbs / PEAK_HBM_GBS:.4f}")
+    L.append(f"plain run: value {plain['value']} GB/s ({plain['pct_of_peak']}% "
+             f"of 8 TB/s), {plain['ms_per_step'] * 1e3:.1f} us per step; "
+             f"roofline {dom} {plain['roofline']['avg_us']} us by events, "
+             f"{plain['roofline']['achieved']} GB/s, frac "
+             f"{plain['roofline']['frac']} ({100 * (plain['roofline']['avg_us'] / avg - 1):+.1f}% "
+             f"against rocprof)")
+    L.append(f"profiled run: value {prof['value']} GB/s, "
+             f"{prof['ms_per_step'] * 1e3:.1f} us per step; roofline {dom} "
+             f"{prof['roofline']['avg_us']} us, frac {prof['roofline']['frac']} "
+             f"({100 * (prof['roofline']['avg_us'] / avg - 1):+.1f}% against "
+             f"rocprof in the same run)")
+    L.append(f"per-kernel timing: {timing} ("
+             + ("intervals between plain events between the calls of "
+                "back-to-back steps" if timing == "calls" else
+                "HIP events at each kernel's own dispatch, in an eager pass; "
+                "the timed region replays graphs") + ")")
+    print("\n".join(L))
+
+
+def summarize_traffic(d, workload, copy_dir):
+    """HBM bytes per launch from the FETCH_SIZE and WRITE_SIZE passes, over
+    the timed region's dispatches, scaled by the same counters on a plain
+    copy of known size; prints the summary and updates
+    profiles/traffic.json."""
+    import csv
+
+    def value(rs):
+        return sum(float(r["Counter_Value"]) for r in rs)
+
+    def counter(sub, js):
+        prof = _json_line(os.path.join(d, js))
+        rows = list(csv.DictReader(open(_one_csv(os.path.join(d, sub),
+                                                 "counter_collection.csv"))))
+        timed = _timed(_library_dispatches(rows, value), prof["profile_layout"])
+        per = {}
+        for label, name, _, _, v in timed:
+            per.setdefault(label, []).append(v)
+        return prof, {k: float(np.mean(v)) for k, v in per.items()}
+
+    def copy_scale(sub, per_launch):
+        rows = list(csv.DictReader(open(_one_csv(os.path.join(copy_dir, sub),
+                                                 "counter_collection.csv"))))
+        calib = _json_line(os.path.join(copy_dir, sub + ".json"))
+        n = calib["size_bytes"] * per_launch
+        vals = {}
+        for r in rows:
+            if "copyBuffer" in r["Kernel_Name"]:
+                vals.setdefault(r["Dispatch_Id"], 0.0)
+                vals[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        kib = float(np.median(list(vals.values())))
+        return n / (kib * 1024.0)
+
+    prof, fetch = counter("pmc_fetch", "fetch.json")
+    _, write = counter("pmc_write", "write.json")
+    fs = copy_scale("fetch", 1)
+    wsc = copy_scale("write", 1)
+    fam = ("cache" if workload in W.CACHE_WORKLOADS else "attend"
+           if workload in W.ATTEND_WORKLOADS else "sink"
+           if workload in W.SINK_WORKLOADS else "mixed"
+           if workload in W.MIXED_WORKLOADS else "flush")
+    h = kernel_source_hash(fam)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    rec = profile_recipe(workload)
+    L = [f"# HBM traffic per launch from rocprofv3 counters: {workload}\n",
+         f"workload: {prof['config']['workload']}\n",
+         "commands (run from /tmp with TMPDIR=/tmp), one counter per pass:",
+         f"  {rec['fetch']}", f"  {rec['write']}", f"  {rec['copy_fetch']}",
+         f"  {rec['copy_write']}",
+         f"  python3 <repo>/bench.py --summarize-traffic <dir> --copy-dir "
+         f"<copydir> --workload {workload}   (this summary)\n",
+         f"Scale from a plain device copy of 512e6 bytes "
+         f"(__amd_rocclr_copyBuffer): bytes = FETCH_SIZE KiB * 1024 * "
+         f"{fs:.4f}; WRITE_SIZE KiB * 1024 * {wsc:.4f}\n",
+         f"kernel source hash (family {fam}): {h}\n",
+         "averages over the timed region's dispatches of each launch:",
+         f"{'launch':24s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} "
+         f"{'read MB':>9s} {'write MB':>9s} {'HBM MB':>9s} {'alg MB':>9s} "
+         f"{'HBM/alg':>8s}"]
+    pk = prof.get("per_kernel", {})
+    for label in fetch:
+        rb = fetch[label] * 1024 * fs
+        wb = write.get(label, 0.0) * 1024 * wsc
+        alg = pk.get(label, {}).get("algorithmic_bytes")
+        L.append(f"{label:24s} {fetch[label]:11.0f} {write.get(label, 0):11.0f} "
+                 f"{rb / 1e6:9.2f} {wb / 1e6:9.2f} {(rb + wb) / 1e6:9.2f} "
+                 + (f"{alg / 1e6:9.2f} {(rb + wb) / alg:8.3f}" if alg else
+                    f"{'-':>9s} {'-':>8s}"))
+        if alg:
+            data[f"{label}@{workload}"] = {
+                "source_hash": h, "hbm_bytes_per_launch": int(rb + wb),
+                "fetch_bytes": int(rb), "write_bytes": int(wb),
+                "algorithmic_bytes": int(alg), "fetch_scale": round(fs, 4),
+                "write_scale": round(wsc, 4)}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print("\n".join(L))
 
 
 def main():
@@ -1082,14 +1479,30 @@ def main():
     ap.add_argument("--single-calls", action="store_true",
                     help="decode/tiny: time the separate key and value calls "
                          "instead of the K+V calls")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel-trace summary of a profiled run "
+                         "(DIR holds plain.json, profiled.json and trace/; "
+                         "see profile_recipe)")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="print the HBM traffic summary of the counter runs "
+                         "in DIR and update profiles/traffic.json")
+    ap.add_argument("--copy-dir", metavar="DIR",
+                    help="the copy-calibration counter runs (fetch/, write/, "
+                         "fetch.json, write.json)")
     ap.add_argument("--launch", choices=("auto", "graphs", "eager"),
                     default="auto",
                     help="timed steps as HIP graph replays or eager launches; "
-                         "auto: graphs for launch-bound steps (under 256 MB "
-                         "of traffic), eager otherwise (graph replays add "
-                         "1-4%% to long steps)")
+                         "auto: graphs for launch-bound steps (under 16 MB "
+                         "of traffic per launch), eager otherwise (a replay "
+                         "costs more than a launch it does not hide)")
     args = ap.parse_args()
 
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.workload, args.copy_dir)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus},"
@@ -1144,7 +1557,10 @@ def main():
     step_bytes = sum(s[2] for s in steps)
     stream = torch.cuda.current_stream(dev)
 
-    for i in range(args.warmup):
+    disp = Dispatches(K)
+    labels = launch_labels(K, [(name, lambda fn=fn: fn(0))
+                               for name, _, _, fn in steps])
+    for i in range(1, args.warmup):
         for _, _, _, fn in steps:
             fn(i)
     torch.cuda.synchronize()
@@ -1176,9 +1592,9 @@ def main():
     # and replayed in order; kernels and arguments are exactly those of the
     # eager calls.
     period = int(np.lcm(pool, N_CODE_SETS))
-    use_graphs = (args.launch == "graphs" or
-                  (args.launch == "auto" and step_bytes < 256e6))
+    use_graphs = launch_bound(args, step_bytes, len(labels))
     graphs = None
+    disp.eager()
     if use_graphs:
         graphs = []
         cap = torch.cuda.Stream(device=dev)
@@ -1187,47 +1603,71 @@ def main():
             with torch.cuda.graph(g, stream=cap):
                 for _, _, _, fn in steps:
                     fn(ph)
-            graphs.append(g)
-        for ph in range(period):      # first replays happen outside the timing
-            graphs[ph].replay()
+            graphs.append((g, disp.captured()))
+        for g, k in graphs:           # first replays happen outside the timing
+            g.replay()
+            disp.replayed(k)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    base = args.warmup
+    base = max(args.warmup, 1)
     torch.cuda.synchronize()
+    before = disp.n
     t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         if graphs is not None:
-            graphs[(base + i) % period].replay()
+            g, k = graphs[(base + i) % period]
+            g.replay()
+            disp.replayed(k)
         else:
             for _, _, _, fn in steps:
                 fn(base + i)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
+    disp.eager()
+    layout = profile_layout(before, disp.n - before, labels)
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
-    # Pass 2, kernel durations: K more steps in which every launch records
-    # its own start/stop event pair at its dispatch (kivi_time_next_launch,
-    # hipExtLaunchKernel), on the launch's stream.  HIP queues each pair as
-    # marker packets around the kernel, which adds a few microseconds of
-    # dispatch per armed launch; that is why the step is timed in a pass of
-    # its own.  The dominant kernel (longest average) gives the roofline.
+    # Pass 2, kernel durations, over K more steps.  Steps timed eagerly (the
+    # HBM-bound workloads) are launched exactly as in the timed region, with
+    # a plain event between calls (call_intervals): each kernel's interval
+    # is its share of a back-to-back step, including the write-back of the
+    # kernel before it that it competes with, so the intervals add up to the
+    # step and agree with a profiler's durations of the timed region.
+    # Launch-bound steps (graph replays in the timed region) would count the
+    # host's launch gaps that way, so there every launch records its own
+    # start/stop pair at its dispatch instead (kivi_time_next_launch,
+    # hipExtLaunchKernel): the kernel alone.  The dominant kernel (longest
+    # average) gives the roofline.
     n_k = len(steps)
-    kev = [event_pairs(n_k) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    base = args.warmup + args.steps
-    for i in range(args.steps):
-        for jj, (_, _, _, fn) in enumerate(steps):
-            K.kivi_time_next_launch(*kev[i][jj])
-            fn(base + i)
-    torch.cuda.synchronize()
+    base = max(args.warmup, 1) + args.steps
     per_kernel = {}
-    for jj, (name, op, b, _) in enumerate(steps):
-        d = [kev[i][jj][0].elapsed_time(kev[i][jj][1])
-             for i in range(args.steps)]
-        per_kernel[name] = stats(name, op, b, d)
+    if graphs is None:
+        def timed_step(i, mark):
+            for jj, (_, _, _, fn) in enumerate(steps):
+                fn(i)
+                mark(jj)
+
+        iv = call_intervals(torch, stream, timed_step, n_k, args.steps, base)
+        for jj, (name, op, b, _) in enumerate(steps):
+            per_kernel[name] = stats(name, op, b, iv[jj])
+        timing = "calls"
+    else:
+        kev = [event_pairs(n_k) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            for jj, (_, _, _, fn) in enumerate(steps):
+                K.kivi_time_next_launch(*kev[i][jj])
+                fn(base + i)
+        torch.cuda.synchronize()
+        for jj, (name, op, b, _) in enumerate(steps):
+            d = [kev[i][jj][0].elapsed_time(kev[i][jj][1])
+                 for i in range(args.steps)]
+            per_kernel[name] = stats(name, op, b, d)
+        timing = "first_launch"
+    layout["per_kernel_timing"] = timing
     dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_us"])
     dk = per_kernel[dom]
 
@@ -1274,9 +1714,14 @@ def main():
         "per_kernel": per_kernel,
         "per_kernel_note": ("value: K steps with no per-launch events; "
                             "per_kernel and roofline: a second pass of K "
-                            "steps, every launch timed by HIP events at its "
-                            "own dispatch"),
+                            "steps, " + (
+                                "each call's interval between plain events "
+                                "recorded between the calls of back-to-back "
+                                "steps" if timing == "calls" else
+                                "every launch timed by HIP events at its own "
+                                "dispatch")),
         "kernel_source_hash": src_hash,
+        "profile_layout": layout,
     }
     if not args.no_cpu_baseline:
         n_bh = args.cpu_sample_bh or max(1, (1 << 27) // (w.S * w.D))

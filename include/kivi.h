@@ -30,7 +30,9 @@
  * Ownership and execution: every pointer is caller-owned device memory
  * (e.g. allocated by PyTorch); the library never allocates, frees or
  * synchronises and keeps no state between calls (apart from the per-thread
- * profiling events of kivi_time_next_launch); calls are re-entrant.
+ * profiling events of kivi_time_next_launch, the launch counter of
+ * kivi_launch_count and the per-device workspace of
+ * kivi_cache_attend_noalloc); calls are re-entrant.
  * Work is enqueued on `stream` (0 = the null stream) and runs
  * asynchronously; outputs are valid once the stream has reached the call.
  * Inputs and outputs must not overlap.
@@ -436,10 +438,17 @@ kivi_status kivi_dequant_values_rows(const uint8_t* codes, const float* scale,
  * kivi_cache_append up to three, kivi_cache_attend and kivi_sink_select
  * two (the pair times the first), and calls that
  * launch nothing -- errors, empty tensors -- leave it armed.  Passing NULL
- * for either disarms it.  This thread-local pair is the library's only
- * state.
+ * for either disarms it.
  */
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
+/*
+ * Profiling aid: the number of kernel launches the library has made in this
+ * process (every thread, every device; a launch recorded into a graph under
+ * capture counts once, however often the graph is replayed).  Lets a
+ * profiler's dispatch trace be split into the phases of a benchmark.
+ */
+int64_t kivi_launch_count(void);
 
 /*
  * Self-test of the division shortcuts the quantizers use on this GPU.  The

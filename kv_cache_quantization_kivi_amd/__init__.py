@@ -715,6 +715,15 @@ def kivi_time_next_launch(start, stop):
     _lib().kivi_time_next_launch(h(start), h(stop))
 
 
+def kivi_launch_count():
+    """Kernel launches the library has made in this process (a launch
+    recorded into a graph counts once)."""
+    L = _lib()
+    L.kivi_launch_count.argtypes = []
+    L.kivi_launch_count.restype = ctypes.c_int64
+    return int(L.kivi_launch_count())
+
+
 def kivi_selftest_division(device="cuda", stream=None):
     """Number of mismatches of the kernels' exact division shortcuts
     against IEEE division on this GPU (0 is required)."""

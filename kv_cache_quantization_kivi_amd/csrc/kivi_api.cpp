@@ -7,12 +7,17 @@
 
 #include "kivi_launch.h"
 
+#include <atomic>
+
 namespace kivi {
 
 namespace {
 thread_local hipEvent_t g_start = nullptr;
 thread_local hipEvent_t g_stop = nullptr;
+std::atomic<int64_t> g_launches{0};
 }  // namespace
+
+void count_launch() { g_launches.fetch_add(1, std::memory_order_relaxed); }
 
 void take_launch_events(hipEvent_t* start, hipEvent_t* stop) {
     *start = g_start;
@@ -514,6 +519,8 @@ kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
     const int64_t Q_new =
         T_new >= c->R ? c->G_k * ((T_new - c->R) / c->G_k) : 0;
     const int64_t Q_to = Q_new > c->Q ? Q_new : c->Q;
+    bool flush = false, one_launch = false;
+    kivi::CacheFlushJob fk{}, fvv{};
     if (c->BH > 0 && Q_to > c->Q) {
         // flush tokens [Q, Q_to): keys per channel, values per token
         kivi::CacheFlushJob f{c->k_ring, k_new, (int)c->dtype, c->BH, c->D,
@@ -527,17 +534,37 @@ kivi_status kivi_cache_append(kivi_cache* c, const void* k_new,
         fv.codes = c->v_codes;
         fv.scale = c->v_scale;
         fv.zero = c->v_zero;
-        if (kivi::launch_cache_flush_kv(f, fv) != hipSuccess)
+        flush = true;
+        one_launch = kivi::cache_append_fits(f, fv);
+        if (one_launch) {
+            fk = f;
+            fvv = fv;
+        } else if (kivi::launch_cache_flush_kv(f, fv) != hipSuccess) {
             return KIVI_ERR_LAUNCH;
+        }
     }
-    // the new tokens that stay unquantized go to their ring slots (after the
-    // flush has read the slots they may reuse: same stream, in order)
+    // The new tokens that stay unquantized go to their ring slots.  The
+    // flush reads the ring slots of tokens [Q, min(Q_to, T)); a new token s
+    // shares a slot with one of them only if s - Q >= ring, so when
+    // T_new - Q <= ring (every decode-time append) or no flushed token comes
+    // from the ring (T == Q), the copy runs in the flush's own launch;
+    // otherwise it is a launch of its own after the flush, on the same stream.
     const int64_t s_first = Q_to > c->T ? Q_to : c->T;
-    if (c->BH > 0 && T_new > s_first) {
-        if (kivi::launch_ring_store(k_new, v_new, c->k_ring, c->v_ring, c->BH,
-                                    c->D, n, c->T, s_first, c->ring,
-                                    stream) != hipSuccess)
+    const bool copy = c->BH > 0 && T_new > s_first;
+    const kivi::RingStore rs =
+        copy ? kivi::make_ring_store(k_new, v_new, c->k_ring, c->v_ring, c->BH,
+                                     c->D, n, c->T, s_first, c->ring)
+             : kivi::RingStore{};
+    if (flush && one_launch) {
+        const bool together = copy && (T_new - c->Q <= c->ring || c->T == c->Q);
+        if (kivi::launch_cache_append(fk, fvv, together ? &rs : nullptr) !=
+            hipSuccess)
             return KIVI_ERR_LAUNCH;
+        if (copy && !together &&
+            kivi::launch_ring_store(rs, stream) != hipSuccess)
+            return KIVI_ERR_LAUNCH;
+    } else if (copy && kivi::launch_ring_store(rs, stream) != hipSuccess) {
+        return KIVI_ERR_LAUNCH;
     }
     c->T = T_new;
     c->Q = Q_to;
@@ -598,6 +625,10 @@ kivi_status kivi_cache_attend_noalloc(const kivi_cache* c, const void* q,
     float* work = nullptr;
     if (kivi::attend_scratch(&work) != hipSuccess) return KIVI_ERR_LAUNCH;
     return attend_launch(c, q, n_q, sm_scale, out, work, stream);
+}
+
+int64_t kivi_launch_count(void) {
+    return kivi::g_launches.load(std::memory_order_relaxed);
 }
 
 void kivi_time_next_launch(hipEvent_t start, hipEvent_t stop) {

@@ -13,12 +13,16 @@ namespace kivi {
 // launch; take_launch_events hands them over once and disarms them.
 void take_launch_events(hipEvent_t* start, hipEvent_t* stop);
 
+// Counts every launch (kivi_launch_count).
+void count_launch();
+
 // Every kernel of the library is launched through here: with armed events
 // the launch records them at the dispatch's start and end
 // (hipExtLaunchKernel), so they time the kernel alone.
 template <typename... Params, typename... Args>
 hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block,
                          uint32_t shmem, hipStream_t stream, Args... args) {
+    count_launch();
     hipEvent_t start = nullptr, stop = nullptr;
     take_launch_events(&start, &stop);
     if (start != nullptr && stop != nullptr)
@@ -192,12 +196,30 @@ hipError_t launch_cache_flush_values(const CacheFlushJob& j);
 // with four times its item bound (kCacheKvPairBelow), else the key and
 // value launches.
 hipError_t launch_cache_flush_kv(const CacheFlushJob& k, const CacheFlushJob& v);
-// Copy tokens [s_first, T + n_in) of the appended keys and values into
-// their ring slots, both tensors in one launch (16-byte chunks).
-hipError_t launch_ring_store(const void* k_in, const void* v_in, void* k_ring,
-                             void* v_ring, int64_t BH, int64_t D, int64_t n_in,
-                             int64_t T, int64_t s_first, int64_t ring_len,
-                             hipStream_t stream);
+// The copy of tokens [s_first, T + n_in) of the appended keys and values
+// into their ring slots (ring_store_lane, kivi_rows.h): 2 * half lanes of
+// one 16-byte chunk each.
+struct RingStore {
+    const uint16_t* k_in;    // [BH, n_in, D] appended tokens
+    const uint16_t* v_in;
+    uint16_t* k_ring;        // [BH, ring_len, D]
+    uint16_t* v_ring;
+    uint32_t half;           // lanes per tensor: BH * ncopy * D8
+    uint32_t D8, ncopy;
+    int32_t s_first, T, n_in, ring_len;
+};
+RingStore make_ring_store(const void* k_in, const void* v_in, void* k_ring,
+                          void* v_ring, int64_t BH, int64_t D, int64_t n_in,
+                          int64_t T, int64_t s_first, int64_t ring_len);
+// The ring store alone, both tensors in one launch.
+hipError_t launch_ring_store(const RingStore& r, hipStream_t stream);
+// The flush of both tensors and, when ring != nullptr, the ring store in one
+// launch (the caller has checked that the ring store writes no slot the
+// flush reads); false if the flush does not take the one-launch form
+// (nothing is launched then).
+bool cache_append_fits(const CacheFlushJob& k, const CacheFlushJob& v);
+hipError_t launch_cache_append(const CacheFlushJob& k, const CacheFlushJob& v,
+                               const RingStore* ring);
 
 // Fallback kernels for shapes the fast kernels do not cover (keys with
 // D % 8 != 0 or group > 32; values with D % 8 != 0, D > 2048 or a group

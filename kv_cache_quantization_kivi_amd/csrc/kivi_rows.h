@@ -16,6 +16,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kivi_device.h"
+#include "kivi_launch.h"
+
 namespace kivi {
 
 // The rows of one key tile (the tokens s0, s0 + 1, ... of one bh): row t is
@@ -98,6 +101,28 @@ struct CacheRows {
         return (int64_t)bh * S_max + Q + ((uint32_t)r - bh * (uint32_t)F);
     }
 };
+
+// The ring store (RingStore, kivi_launch.h): lane gid of 2 * half, keys
+// then values, (bh, token j, 16-byte chunk c) with c fastest, so a wave
+// copies whole contiguous rows.  Token s = s_first + j is row s - T of the
+// appended block and goes to slot s % ring_len; the ring is read again by
+// the next flush, so the stores are plain (cached).
+__device__ __forceinline__ void ring_store_lane(const RingStore& r,
+                                                uint32_t gid) {
+    if (gid >= 2u * r.half) return;
+    const bool val = gid >= r.half;
+    const uint32_t lid = val ? gid - r.half : gid;
+    const uint32_t c = lid % r.D8;
+    const uint32_t j = (lid / r.D8) % r.ncopy;
+    const uint32_t bh = lid / (r.D8 * r.ncopy);
+    const int32_t s = r.s_first + (int32_t)j;
+    const int64_t D = (int64_t)r.D8 * 8;
+    const uint16_t* in = val ? r.v_in : r.k_in;
+    uint16_t* ring = val ? r.v_ring : r.k_ring;
+    const uint4 v = load16_nt(in + ((int64_t)bh * r.n_in + (s - r.T)) * D + c * 8);
+    *reinterpret_cast<uint4*>(ring + ((int64_t)bh * r.ring_len + s % r.ring_len) * D +
+                              c * 8) = v;
+}
 
 // Rows of one key tile of a listed set: row t is token pos[t] of the bh's
 // [S, D] rows.  A position outside [0, S) is clamped, so a bad list reads

@@ -510,8 +510,37 @@ hipError_t launch_quant_kv(const QuantJob& k, const QuantJob& v) {
 // a third of a key flush that size.
 constexpr uint64_t kCacheKvPairBelow = 4 * kKeySplitBelow;
 
+// A residual-window cache append in one launch: the flush of both tensors
+// and, when the append has one, its ring store.  Blocks [0, k_blocks) run
+// the 4-lane split key body, the next v_blocks the value body, the rest the
+// ring store; the caller guarantees that the ring store writes no slot the
+// flush reads, so the three need no ordering.  The key blocks come first:
+// their waves run longest, and started first they do not trail the launch.
 template <int DT, int BITS>
-static hipError_t launch_cache_kv_t(const CacheFlushJob& k, const CacheFlushJob& v) {
+__global__ __launch_bounds__(256) void cache_append_kernel(
+    CacheRows kio, uint32_t k_lanes, uint32_t D8, uint32_t NG,
+    uint8_t* __restrict__ kc, float* __restrict__ ks, float* __restrict__ kz,
+    CacheRows vio, int64_t n_rows, uint32_t lp, uint32_t red, uint32_t gl,
+    uint32_t NGD, int32_t vec, uint8_t* __restrict__ vc,
+    float* __restrict__ vs, float* __restrict__ vz, uint32_t k_blocks,
+    uint32_t v_blocks, RingStore ring) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
+    if (blockIdx.x < k_blocks) {
+        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, true, false, true,
+                              CacheRows>(kio, blockIdx.x * 256u + threadIdx.x,
+                                         k_lanes, D8, NG, kc, ks, kz, nullptr);
+    } else if (blockIdx.x < k_blocks + v_blocks) {
+        quant_values_body<DT, BITS, 1, true, false, CacheRows>(
+            vio, (uint64_t)(blockIdx.x - k_blocks) * 256u + threadIdx.x, lds,
+            n_rows, D8, lp, red, gl, NGD, vec, 0, vc, vs, vz, nullptr);
+    } else {
+        ring_store_lane(ring, (blockIdx.x - k_blocks - v_blocks) * 256u + threadIdx.x);
+    }
+}
+
+template <int DT, int BITS>
+static hipError_t launch_cache_kv_t(const CacheFlushJob& k, const CacheFlushJob& v,
+                                    const RingStore* ring) {
     const uint32_t D8 = (uint32_t)(k.D / 8);
     const uint32_t NG = (uint32_t)(k.F / k.G_k);          // groups flushed per bh
     const uint64_t k_lanes = (uint64_t)k.BH * NG * D8 * 4;
@@ -530,38 +559,49 @@ static hipError_t launch_cache_kv_t(const CacheFlushJob& k, const CacheFlushJob&
     const int64_t n_rows = v.BH * v.F;
     const uint32_t v_blocks = (uint32_t)((((uint64_t)n_rows << lp) + 255) / 256);
     const int32_t vec = (D8 % 4) == 0;
-    const uint32_t blocks = v_blocks + (uint32_t)((k_lanes + 255) / 256);
-    return launch_kernel((quant_kv_kernel<DT, BITS, true, false, CacheRows>),
-                         dim3(blocks), dim3(256), 0, k.stream, rows(k),
-                         (uint32_t)k_lanes, D8, NG, k.codes, k.scale, k.zero,
-                         (uint16_t*)nullptr, rows(v), n_rows, lp, red, gl, NGD,
-                         vec, (int32_t)0, v.codes, v.scale, v.zero,
-                         (uint16_t*)nullptr, v_blocks);
+    const uint32_t k_blocks = (uint32_t)((k_lanes + 255) / 256);
+    RingStore none{};
+    const RingStore& r = ring != nullptr ? *ring : none;
+    const uint32_t r_blocks = (uint32_t)((2ull * r.half + 255) / 256);
+    return launch_kernel((cache_append_kernel<DT, BITS>),
+                         dim3(k_blocks + v_blocks + r_blocks), dim3(256), 0,
+                         k.stream, rows(k), (uint32_t)k_lanes, D8, NG, k.codes,
+                         k.scale, k.zero, rows(v), n_rows, lp, red, gl, NGD, vec,
+                         v.codes, v.scale, v.zero, k_blocks, v_blocks, r);
 }
 
 template <int DT>
-static hipError_t launch_cache_kv_bits(const CacheFlushJob& k, const CacheFlushJob& v) {
+static hipError_t launch_cache_kv_bits(const CacheFlushJob& k, const CacheFlushJob& v,
+                                       const RingStore* ring) {
     switch (k.bits) {
-        case 1: return launch_cache_kv_t<DT, 1>(k, v);
-        case 2: return launch_cache_kv_t<DT, 2>(k, v);
-        case 4: return launch_cache_kv_t<DT, 4>(k, v);
-        default: return launch_cache_kv_t<DT, 8>(k, v);
+        case 1: return launch_cache_kv_t<DT, 1>(k, v, ring);
+        case 2: return launch_cache_kv_t<DT, 2>(k, v, ring);
+        case 4: return launch_cache_kv_t<DT, 4>(k, v, ring);
+        default: return launch_cache_kv_t<DT, 8>(k, v, ring);
     }
 }
 
 hipError_t launch_cache_flush_kv(const CacheFlushJob& k, const CacheFlushJob& v) {
-    const uint64_t D8 = (uint64_t)(k.D / 8);
-    const uint64_t items = (uint64_t)k.BH * (k.F / k.G_k) * D8;
-    const int64_t g32 = v.group / 32;
-    const bool pair = items < kCacheKvPairBelow && 64 % (D8 * 4) == 0 &&
-                      k.G_k > kKeyGMaxPair / 2 && k.G_k <= kKeyGMaxPair &&
-                      v.group % 32 == 0 && (g32 & (g32 - 1)) == 0;
-    if (!pair) {
+    if (!cache_append_fits(k, v)) {
         const hipError_t e = launch_cache_flush_keys(k);
         return e != hipSuccess ? e : launch_cache_flush_values(v);
     }
-    return k.dtype == DT_F16 ? launch_cache_kv_bits<DT_F16>(k, v)
-                             : launch_cache_kv_bits<DT_BF16>(k, v);
+    return launch_cache_append(k, v, nullptr);
+}
+
+bool cache_append_fits(const CacheFlushJob& k, const CacheFlushJob& v) {
+    const uint64_t D8 = (uint64_t)(k.D / 8);
+    const uint64_t items = (uint64_t)k.BH * (k.F / k.G_k) * D8;
+    const int64_t g32 = v.group / 32;
+    return items < kCacheKvPairBelow && 64 % (D8 * 4) == 0 &&
+           k.G_k > kKeyGMaxPair / 2 && k.G_k <= kKeyGMaxPair &&
+           v.group % 32 == 0 && (g32 & (g32 - 1)) == 0;
+}
+
+hipError_t launch_cache_append(const CacheFlushJob& k, const CacheFlushJob& v,
+                               const RingStore* ring) {
+    return k.dtype == DT_F16 ? launch_cache_kv_bits<DT_F16>(k, v, ring)
+                             : launch_cache_kv_bits<DT_BF16>(k, v, ring);
 }
 
 hipError_t launch_quant_values(const QuantJob& j) {

@@ -1,0 +1,77 @@
+"""bench.py's profile summarizers on the CPU: a fabricated rocprofv3 kernel
+trace and counter runs, split into phases by the run's dispatch layout."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _result(layout, per_kernel, dom, extra=None):
+    d = {"metric": "m", "value": 5000.0, "pct_of_peak": 62.5, "steps": 2,
+         "ms_per_step": 0.1, "config": {"workload": "w", "launch": "eager"},
+         "per_kernel": per_kernel, "kernel_source_hash": "x",
+         "roofline": {"kernel": dom, "avg_us": 51.0, "achieved": 1.0,
+                      "frac": 0.5},
+         "profile_layout": layout}
+    d.update(extra or {})
+    return json.dumps(d)
+
+
+def _write_csv(path, rows, fields):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+import pytest
+
+
+@pytest.mark.parametrize("timing", ["first_launch", "calls"])
+def test_trace_summary_uses_the_timed_region_only(tmp_path, timing):
+    # setup: 2 dispatches, then per step: "a" (kivi::ka) and "b" (kivi::kb,
+    # two launches), 2 timed steps, then 2 armed steps; torch kernels mixed
+    # in are ignored
+    names = {"a": "void kivi::ka<0>(int)", "b": "void kivi::kb<1>(int)"}
+    seq = ["a", "b", "b"] * 2
+    disp = ([("a", 500)] * 2 + [(k, 40) for k in seq]
+            + [(k, 50 if k == "a" else 10) for k in seq]
+            + [(k, 70) for k in seq])
+    rows, t, i = [], 1000, 0
+    for k, dur in disp:
+        i += 1
+        rows.append({"Dispatch_Id": i, "Kernel_Name": names[k],
+                     "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+        t += dur * 1000 + 10
+        i += 1
+        rows.append({"Dispatch_Id": i, "Kernel_Name": "at::fill<float>()",
+                     "Start_Timestamp": t, "End_Timestamp": t + 5})
+        t += 20
+    _write_csv(str(tmp_path / "trace" / "x" / "bench_kernel_trace.csv"), rows,
+               ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                "End_Timestamp"])
+    layout = {"dispatches_before_timed": 8, "timed_dispatches": 6,
+              "step_launches": ["a", "b", "b#2"], "per_kernel_timing": timing}
+    pk = {"a": {"avg_us": 51.0, "algorithmic_bytes": 400000},
+          "b": {"avg_us": 10.0, "algorithmic_bytes": 1000}}
+    for f in ("plain.json", "profiled.json"):
+        (tmp_path / f).write_text("noise\n" + _result(layout, pk, "a") + "\n")
+    out = subprocess.run(
+        [sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-trace",
+         str(tmp_path), "--workload", "roundtrip"],
+        capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    text = out.stdout
+    # timed "a" dispatches last 50 us: 400000 B / 50 us = 8 GB/s
+    assert "400000 algorithmic bytes / 50.00 us" in text, text
+    assert "frac 0.0010" in text
+    lines = [ln for ln in text.splitlines() if ln.startswith("b#2 ")]
+    assert lines and " 10.00 " in lines[0]
+    if timing == "calls":    # the call "b" is its two launches
+        lines = [ln for ln in text.splitlines() if ln.startswith("b ")]
+        assert any(" 20.00 " in ln for ln in lines), text
