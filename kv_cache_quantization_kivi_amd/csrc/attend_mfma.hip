@@ -8,12 +8,14 @@
 // chunks stay on the vector units):
 //
 //   scores  s[t][j] = sum_d (q[j][d] scale[g][d]) code[t][d] + sum_d q[j][d] zero[g][d]
-//           A = codes (M = 16 tokens, K = 32 channels) as f16, exact;
+//           A = codes (M = 16 tokens, K = 32 channels) as the f16
+//               subnormals code * 2^-24, exact;
 //           B = the scaled queries (K = channels, N = query heads), split in
 //               two f16 parts hi + lo after scaling by a power of two 2^e
 //               per (key group, head) that keeps them inside f16's range;
 //   values  o[j][d] = sum_t (p[j][t] vscale[t][gv]) code[t][d] + sum_t p[j][t] vzero[t][gv]
-//           A = codes transposed through LDS (M = 16 channels, K = 32 tokens);
+//           A = codes transposed through LDS (M = 16 channels, K = 32 tokens),
+//               as f16 subnormals too;
 //           B = the weights p * vscale, hi + lo after a power-of-two scaling
 //               per value group.
 // f16 x f16 products are exact in fp32 and the matrix core accumulates in
@@ -76,24 +78,14 @@ __device__ __forceinline__ h8_t as_h8(uint32_t a, uint32_t b, uint32_t c,
     return __builtin_bit_cast(h8_t, make_uint4(a, b, c, d));
 }
 
-// The f16 pair (c0, c1) from c0 | c1 << 16 (c0, c1 < 1024), exactly: the
-// pattern 0x6400 | c is the f16 1024 + c, and subtracting 1024 is exact.
-__device__ __forceinline__ uint32_t pair_f16(uint32_t c01) {
-    const h2x_t one_k = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const h2x_t v = __builtin_bit_cast(h2x_t, c01 | 0x64006400u) - one_k;
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// (x & m) | c in one instruction, with m and c held in registers (a VOP3
-// instruction here reads at most one scalar or constant operand).
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
-    return r;
-}
+// Codes enter the matrix cores as f16 subnormals: the bit pattern c (c <
+// 1024) is exactly the f16 value c * 2^-24, so a code needs only to be
+// masked into place; the products' 2^-24 is taken out again, exactly, with
+// the operands' power-of-two scaling (kCodeExp).
+constexpr int kCodeExp = 24;
 
 // 8 codes held LSB-first in the low 8 * BITS bits of `bits` (higher bits
-// zero) as 8 f16 values.
+// zero) as 8 f16 values code * 2^-24, code 2k and 2k + 1 in dword k.
 template <int BITS>
 __device__ __forceinline__ h8_t codes8(uint32_t bits) {
     constexpr uint32_t M = (1u << BITS) - 1u;
@@ -101,17 +93,16 @@ __device__ __forceinline__ h8_t codes8(uint32_t bits) {
     if constexpr (BITS <= 2) {
         // a second copy 16 - BITS bits up puts code 2k + 1 at bit 16 + 2k BITS
         const uint32_t t = bits | (bits << (16 - BITS));
-        const h2x_t one_k = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {   // pair_f16 with the mask and 0x6400s in one step
-            const uint32_t f = and_or(t >> (2 * k * BITS), M | (M << 16), 0x64006400u);
-            d[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2x_t, f) - one_k);
-        }
+        for (int k = 0; k < 4; ++k) d[k] = (t >> (2 * k * BITS)) & (M | (M << 16));
     } else {
+        // byte k holds codes 2k (low nibble) and 2k + 1: the low nibbles and
+        // the high ones apart, then one byte permute per pair
+        const uint32_t u = bits & 0x0f0f0f0fu, v = (bits >> 4) & 0x0f0f0f0fu;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            d[k] = pair_f16(((bits >> (2 * k * BITS)) & M) |
-                            (((bits >> ((2 * k + 1) * BITS)) & M) << 16));
+            d[k] = __builtin_amdgcn_perm(v, u, (uint32_t)k | 0x0c00u |
+                                                   ((uint32_t)(4 + k) << 16) | 0x0c000000u);
     }
     return as_h8(d[0], d[1], d[2], d[3]);
 }
@@ -358,7 +349,7 @@ void attend_mfma_kernel(AttendArgs a) {
             const float bias = kbias_s[g][m16];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                p_s[m16][tok0 + kb * 4 + i] = __builtin_ldexpf(acc[i], -e) + bias;
+                p_s[m16][tok0 + kb * 4 + i] = __builtin_ldexpf(acc[i], kCodeExp - e) + bias;
         }
     }
     __syncthreads();
@@ -542,13 +533,9 @@ void attend_mfma_kernel(AttendArgs a) {
             const uint4 d = *reinterpret_cast<const uint4*>(&vp_s[q][P0]);
             const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
             constexpr uint32_t M = (1u << BITS) - 1u;
-            const h2x_t one_k = {(_Float16)1024.0f, (_Float16)1024.0f};
             uint32_t pr[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {   // as pair_f16, the mask and 0x6400s in one step
-                const uint32_t f = and_or(dw[k] >> sh, pmask, 0x64006400u);
-                pr[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2x_t, f) - one_k);
-            }
+            for (int k = 0; k < 4; ++k) pr[k] = (dw[k] >> sh) & pmask;   // codes * 2^-24
             const h8_t A = as_h8(pr[0], pr[1], pr[2], pr[3]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                 A, __builtin_bit_cast(h8_t, bp[2 * s4]), acc, 0, 0, 0);
@@ -563,7 +550,8 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ch = mt * 16 + kb * 4 + i;
-                wj[2 + ch] = __builtin_ldexpf(acc[i], -e) + zs + (has_ring ? q_s[m16][ch] : 0.0f);
+                wj[2 + ch] = __builtin_ldexpf(acc[i], kCodeExp - e) + zs +
+                             (has_ring ? q_s[m16][ch] : 0.0f);
             }
         }
     }

@@ -77,8 +77,13 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
     const int lane = tid & 63;
     const float* sc = score + (int64_t)b * S;
     const int n_rounds = (S + kPartRound - 1) / kPartRound;
-    uint32_t key[kPartPer];                    // this thread's run (one round)
-    const auto load_run = [&](int r) {         // every thread, barriers inside
+    // this thread's run of the round: in registers for the radix passes,
+    // read from LDS in the final pass (with the 32 keys live there too the
+    // kernel needed more than the 128 VGPRs of a 1024-thread block, and
+    // spilled)
+    const uint32_t* run_s = stage_s + tid * (kPartPer + 1);
+    uint32_t key[kPartPer];
+    const auto load_run = [&](int r, bool regs) {   // every thread, barriers inside
         __syncthreads();
 #pragma unroll 8
         for (int i = tid; i < kPartRound; i += kPartThreads) {
@@ -86,10 +91,12 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
             stage_s[i + i / 32] = p < S ? order_key(sc[p]) : 0u;
         }
         __syncthreads();
+        if (regs) {
 #pragma unroll
-        for (int i = 0; i < kPartPer; ++i) key[i] = stage_s[tid * (kPartPer + 1) + i];
+            for (int i = 0; i < kPartPer; ++i) key[i] = run_s[i];
+        }
     };
-    if (n_rounds == 1) load_run(0);
+    if (n_rounds == 1) load_run(0, true);
     uint32_t prefix = 0, need = (uint32_t)n_hi;   // keys above prefix still to take
     if (n_hi > 0 && n_hi < S) {
         for (int shift = 24; shift >= 0; shift -= 8) {
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
             __syncthreads();
             const uint32_t hmask = shift == 24 ? 0u : ~0u << (shift + 8);
             for (int r = 0; r < n_rounds; ++r) {
-                if (n_rounds > 1) load_run(r);
+                if (n_rounds > 1) load_run(r, true);
                 const int32_t s0 = r * kPartRound + tid * kPartPer;
 #pragma unroll
                 for (int i = 0; i < kPartPer; ++i) {
@@ -159,12 +166,12 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
     const bool all_hi = n_hi == S, none_hi = n_hi == 0;
     uint32_t eq_base = 0, hi_base = 0;
     for (int r = 0; r < n_rounds; ++r) {
-        if (n_rounds > 1) load_run(r);
+        if (n_rounds > 1) load_run(r, false);
         const int32_t s0 = r * kPartRound + tid * kPartPer;
         uint32_t n_eq = 0;
 #pragma unroll
         for (int i = 0; i < kPartPer; ++i)
-            n_eq += (s0 + i < S && !all_hi && !none_hi && key[i] == prefix) ? 1u : 0u;
+            n_eq += (s0 + i < S && !all_hi && !none_hi && run_s[i] == prefix) ? 1u : 0u;
         uint32_t eq_all, hi_all;
         uint32_t eq_rank = eq_base + block_scan(n_eq, wsum, &eq_all);
         uint32_t hi_here = 0;
@@ -172,8 +179,8 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
 #pragma unroll
         for (int i = 0; i < kPartPer; ++i) {
             const bool real = s0 + i < S;
-            const bool eq = real && !all_hi && !none_hi && key[i] == prefix;
-            const bool hi = real && (all_hi || (!none_hi && (key[i] > prefix ||
+            const bool eq = real && !all_hi && !none_hi && run_s[i] == prefix;
+            const bool hi = real && (all_hi || (!none_hi && (run_s[i] > prefix ||
                                                              (eq && eq_rank < need))));
             eq_rank += eq ? 1u : 0u;
             hi_here += hi ? 1u : 0u;
@@ -361,12 +368,69 @@ __global__ __launch_bounds__(256) void list_dequant_keys_kernel(
     }
 }
 
+// Keys at D = 128 (16 chunks), codes of at most 4 bits, groups of at most 32:
+// one wave per (bh, group of the set), four lanes per chunk with
+// interleaved tokens, so that every store instruction writes four
+// consecutive entries of the list (mostly consecutive rows); the group's
+// codes (at most 32 rows of 16 * BITS bytes, contiguous in the set's codes)
+// and positions go through LDS first, so the token loop is stores only.
+template <int DT, int BITS>
+__global__ __launch_bounds__(64) void list_dequant_keys_split_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ scale,
+    const float* __restrict__ zero, uint32_t NG, int32_t S, int32_t n,
+    int32_t H, int32_t G, const int32_t* __restrict__ pos,
+    uint16_t* __restrict__ out) {
+    static_assert(BITS <= 4, "a group's codes are at most 2 KiB");
+    constexpr int64_t D = 128;
+    constexpr int64_t row_bytes = 16 * BITS;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[32 * row_bytes];
+    __shared__ int32_t pos_s[32];
+    const uint32_t lane = threadIdx.x;
+    const uint32_t tile = blockIdx.x;              // bh * NG + g
+    const uint32_t c = lane % 16u, part = lane / 16u;
+    const uint32_t g = tile % NG, bh = tile / NG;
+    const int32_t j0 = (int32_t)g * G;
+    const int32_t nt = min(G, n - j0);
+    const int64_t crow0 = (int64_t)bh * n + j0;    // the group's first code row
+    const uint32_t n16 = (uint32_t)nt * BITS;      // 16-byte pieces of its codes
+    uint4 t4[2];
+#pragma unroll
+    for (uint32_t k = 0; k < 2; ++k)
+        if (k * 64u + lane < n16)
+            t4[k] = load16_nt(codes + crow0 * row_bytes + (k * 64u + lane) * 16u);
+    const int32_t* lp = pos + (int64_t)(bh / (uint32_t)H) * n + j0;
+    const int32_t my_pos = lane < (uint32_t)nt ? lp[lane] : -1;
+    const int64_t p = (int64_t)tile * D + (int64_t)c * 8;
+    const float4 s_a = *reinterpret_cast<const float4*>(scale + p);
+    const float4 s_b = *reinterpret_cast<const float4*>(scale + p + 4);
+    const float4 z_a = *reinterpret_cast<const float4*>(zero + p);
+    const float4 z_b = *reinterpret_cast<const float4*>(zero + p + 4);
+#pragma unroll
+    for (uint32_t k = 0; k < 2; ++k)
+        if (k * 64u + lane < n16)
+            *reinterpret_cast<uint4*>(lds + (k * 64u + lane) * 16u) = t4[k];
+    if (lane < 32u) pos_s[lane] = my_pos;
+    wave_lds_sync();
+    const float sc[8] = {s_a.x, s_a.y, s_a.z, s_a.w, s_b.x, s_b.y, s_b.z, s_b.w};
+    const float z[8] = {z_a.x, z_a.y, z_a.z, z_a.w, z_b.x, z_b.y, z_b.z, z_b.w};
+    uint16_t* dst = out + (int64_t)bh * S * D + (int64_t)c * 8;
+#pragma unroll
+    for (int32_t i = 0; i < 8; ++i) {
+        const int32_t t = (int32_t)part + 4 * i;
+        if (t < nt) {
+            const int32_t s = pos_s[t];
+            const uint64_t q = lds_key_codes<BITS>(lds + t * row_bytes + c * BITS);
+            if (s >= 0 && s < S)
+                store16_nt(dst + (int64_t)s * D, dequant_chunk<DT, BITS>(q, sc, z));
+        }
+    }
+}
+
 // Values: one lane per (row of the set, CPL consecutive 8-channel chunks):
 // one CPL * BITS-byte code load and one (scale, zero) load per value group
 // it touches (groups are multiples of 8 channels).  The reconstruction goes
 // out through LDS: a wave's rows are parked there and stored with one lane
 // per 16-byte chunk, so each store instruction writes whole rows.
-constexpr int kLdvWaveRowsMax = 64;
 
 template <int DT, int BITS, int CPL, int D8>
 __global__ __launch_bounds__(256) void list_dequant_values_kernel(
@@ -440,6 +504,14 @@ static hipError_t launch_list_dq_t(const ListJob& j, bool keys, void* out) {
     uint16_t* o = static_cast<uint16_t*>(out);
     if (keys) {
         const uint32_t NG = (uint32_t)((j.n + j.group - 1) / j.group);
+        if constexpr (BITS <= 4) {
+            if (D8 == 16 && j.group <= 32)
+                return launch_kernel((list_dequant_keys_split_kernel<DT, BITS>),
+                                     dim3((uint32_t)(j.B * j.H) * NG), dim3(64),
+                                     0, j.stream, j.codes, j.scale, j.zero, NG,
+                                     (int32_t)j.S, (int32_t)j.n, (int32_t)j.H,
+                                     (int32_t)j.group, j.pos, o);
+        }
         const uint32_t n = (uint32_t)(j.B * j.H) * NG * D8;
         const int32_t stage = BITS <= 4 && 64 % D8 == 0 && D8 >= 4 &&
                               j.group <= 32 && (j.group * BITS) % 16 == 0;
