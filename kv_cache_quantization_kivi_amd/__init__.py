@@ -120,6 +120,17 @@ def _load():
         getattr(L, name).restype = I
     L.kivi_status_string.argtypes = [I]
     L.kivi_status_string.restype = ctypes.c_char_p
+    C = ctypes.POINTER(_Cache)
+    L.kivi_cache_append.argtypes = [C, P, P, I64, P]
+    L.kivi_cache_append.restype = I
+    L.kivi_cache_attend.argtypes = [C, P, I64, ctypes.c_float, P, P, I64, P]
+    L.kivi_cache_attend.restype = I
+    L.kivi_cache_attend_noalloc.argtypes = [C, P, I64, ctypes.c_float, P, P]
+    L.kivi_cache_attend_noalloc.restype = I
+    L.kivi_cache_attend_work_bytes.argtypes = [C, I64]
+    L.kivi_cache_attend_work_bytes.restype = I64
+    L.kivi_launch_count.argtypes = []
+    L.kivi_launch_count.restype = I64
     return L
 
 
@@ -617,15 +628,10 @@ class KiviCache:
         if v_new.shape != k_new.shape:
             raise ValueError("k_new and v_new differ in shape")
         L = _lib()
-        L.kivi_cache_append.argtypes = [ctypes.POINTER(_Cache),
-                                        ctypes.c_void_p, ctypes.c_void_p,
-                                        ctypes.c_int64, ctypes.c_void_p]
-        L.kivi_cache_append.restype = ctypes.c_int
         st = L.kivi_cache_append(ctypes.byref(self.c), _ptr(k_new),
                                  _ptr(v_new), n,
                                  _stream(k_new.device, stream))
         _check(st, "kivi_cache_append")
-
 
     def attend(self, q, sm_scale, out=None, work=None, stream=None):
         """Decode attention of q [BH, n_q, D] (the cache's dtype) over the
@@ -636,14 +642,6 @@ class KiviCache:
             raise ValueError("q: a contiguous tensor of the cache's dtype")
         n_q = q.shape[-2]
         L = _lib()
-        L.kivi_cache_attend_work_bytes.argtypes = [ctypes.POINTER(_Cache),
-                                                   ctypes.c_int64]
-        L.kivi_cache_attend_work_bytes.restype = ctypes.c_int64
-        L.kivi_cache_attend.argtypes = [
-            ctypes.POINTER(_Cache), ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_void_p]
-        L.kivi_cache_attend.restype = ctypes.c_int
         nb = L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
         if out is None:
             out = torch.empty_like(q)
@@ -665,10 +663,6 @@ class KiviCache:
         if out is None or out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out: a tensor shaped and typed like q")
         L = _lib()
-        L.kivi_cache_attend_noalloc.argtypes = [
-            ctypes.POINTER(_Cache), ctypes.c_void_p, ctypes.c_int64,
-            ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
-        L.kivi_cache_attend_noalloc.restype = ctypes.c_int
         st = L.kivi_cache_attend_noalloc(ctypes.byref(self.c), _ptr(q),
                                          q.shape[-2], float(sm_scale),
                                          _ptr(out), _stream(q.device, stream))
@@ -677,9 +671,6 @@ class KiviCache:
 
     def attend_work_bytes(self, n_q):
         L = _lib()
-        L.kivi_cache_attend_work_bytes.argtypes = [ctypes.POINTER(_Cache),
-                                                   ctypes.c_int64]
-        L.kivi_cache_attend_work_bytes.restype = ctypes.c_int64
         return L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
 
 
@@ -719,8 +710,6 @@ def kivi_launch_count():
     """Kernel launches the library has made in this process (a launch
     recorded into a graph counts once)."""
     L = _lib()
-    L.kivi_launch_count.argtypes = []
-    L.kivi_launch_count.restype = ctypes.c_int64
     return int(L.kivi_launch_count())
 
 
