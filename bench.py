@@ -1364,12 +1364,15 @@ def summarize_trace(d, workload):
              f"{prof['ms_per_step'] * 1e3:.1f} us per step; roofline {dom} "
              f"{prof['roofline']['avg_us']} us, frac {prof['roofline']['frac']} "
              f"({100 * (prof['roofline']['avg_us'] / avg - 1):+.1f}% against "
-             f"rocprof in the same run)")
+             f"rocprof in the same run"
+             + ("" if timing == "calls" else
+                "; under the profiler its dispatch interception falls between "
+                "the armed events and the kernel") + ")")
     L.append(f"per-kernel timing: {timing} ("
              + ("intervals between plain events between the calls of "
                 "back-to-back steps" if timing == "calls" else
-                "HIP events at each kernel's own dispatch, in an eager pass; "
-                "the timed region replays graphs") + ")")
+                "HIP events recorded at each kernel's own dispatch, in an "
+                "eager pass after the timed region") + ")")
     print("\n".join(L))
 
 
@@ -1387,11 +1390,17 @@ def summarize_traffic(d, workload, copy_dir):
         prof = _json_line(os.path.join(d, js))
         rows = list(csv.DictReader(open(_one_csv(os.path.join(d, sub),
                                                  "counter_collection.csv"))))
-        timed = _timed(_library_dispatches(rows, value), prof["profile_layout"])
+        lay = prof["profile_layout"]
+        timed = _timed(_library_dispatches(rows, value), lay)
+        calls = lay.get("per_kernel_timing") == "calls"
+        n_l = len(lay["step_launches"])
         per = {}
-        for label, name, _, _, v in timed:
-            per.setdefault(label, []).append(v)
-        return prof, {k: float(np.mean(v)) for k, v in per.items()}
+        for idx, (label, name, _, _, v) in enumerate(timed):
+            # per call (its launches summed) where the benchmark times calls
+            key = label.split("#")[0] if calls else label
+            acc = per.setdefault(key, {})
+            acc[idx // n_l] = acc.get(idx // n_l, 0.0) + v
+        return prof, {k: float(np.mean(list(v.values()))) for k, v in per.items()}
 
     def copy_scale(sub, per_launch):
         rows = list(csv.DictReader(open(_one_csv(os.path.join(copy_dir, sub),
@@ -1429,7 +1438,8 @@ def summarize_traffic(d, workload, copy_dir):
          f"(__amd_rocclr_copyBuffer): bytes = FETCH_SIZE KiB * 1024 * "
          f"{fs:.4f}; WRITE_SIZE KiB * 1024 * {wsc:.4f}\n",
          f"kernel source hash (family {fam}): {h}\n",
-         "averages over the timed region's dispatches of each launch:",
+         "averages over the timed region's dispatches (per call, its launches "
+         "summed, where the benchmark times calls):",
          f"{'launch':24s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} "
          f"{'read MB':>9s} {'write MB':>9s} {'HBM MB':>9s} {'alg MB':>9s} "
          f"{'HBM/alg':>8s}"]
