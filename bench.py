@@ -1290,11 +1290,12 @@ def summarize_trace(d, workload):
         e["d"].append((t1 - t0) / 1e3)
     lay = prof["profile_layout"]
     timing = lay.get("per_kernel_timing", "first_launch")
-    n_l = len(lay["step_launches"])
-    per_call = {}          # call -> its launches' summed duration per step
-    for idx, (label, _, t0, t1, _) in enumerate(timed):
+    per_call = {}          # call -> its launches' summed duration, per call
+    call = -1
+    for label, _, t0, t1, _ in timed:
+        call += "#" not in label
         c = per_call.setdefault(label.split("#")[0], {})
-        c[idx // n_l] = c.get(idx // n_l, 0.0) + (t1 - t0) / 1e3
+        c[call] = c.get(call, 0.0) + (t1 - t0) / 1e3
     alld = {}
     for name, t0, t1, _ in disp:
         alld.setdefault(_template(name), []).append((t1 - t0) / 1e3)
@@ -1376,11 +1377,11 @@ def summarize_trace(d, workload):
     print("\n".join(L))
 
 
-def summarize_traffic(d, workload, copy_dir):
+def summarize_traffic(d, workload, copy_dir, path=None):
     """HBM bytes per launch from the FETCH_SIZE and WRITE_SIZE passes, over
     the timed region's dispatches, scaled by the same counters on a plain
-    copy of known size; prints the summary and updates
-    profiles/traffic.json."""
+    copy of known size; prints the summary and updates the traffic record
+    at path (default profiles/traffic.json)."""
     import csv
 
     def value(rs):
@@ -1393,13 +1394,18 @@ def summarize_traffic(d, workload, copy_dir):
         lay = prof["profile_layout"]
         timed = _timed(_library_dispatches(rows, value), lay)
         calls = lay.get("per_kernel_timing") == "calls"
-        n_l = len(lay["step_launches"])
         per = {}
+        call = -1
         for idx, (label, name, _, _, v) in enumerate(timed):
-            # per call (its launches summed) where the benchmark times calls
+            # per call (its launches summed: name, name#2, ...) where the
+            # benchmark times calls, else per dispatch; a label that recurs
+            # in a step (a ring store per decode token) averages over its
+            # calls or launches
+            call += "#" not in label
             key = label.split("#")[0] if calls else label
             acc = per.setdefault(key, {})
-            acc[idx // n_l] = acc.get(idx // n_l, 0.0) + v
+            slot = call if calls else idx
+            acc[slot] = acc.get(slot, 0.0) + v
         return prof, {k: float(np.mean(list(v.values()))) for k, v in per.items()}
 
     def copy_scale(sub, per_launch):
@@ -1424,7 +1430,7 @@ def summarize_traffic(d, workload, copy_dir):
            if workload in W.SINK_WORKLOADS else "mixed"
            if workload in W.MIXED_WORKLOADS else "flush")
     h = kernel_source_hash(fam)
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     rec = profile_recipe(workload)
     L = [f"# HBM traffic per launch from rocprofv3 counters: {workload}\n",
@@ -1438,8 +1444,10 @@ def summarize_traffic(d, workload, copy_dir):
          f"(__amd_rocclr_copyBuffer): bytes = FETCH_SIZE KiB * 1024 * "
          f"{fs:.4f}; WRITE_SIZE KiB * 1024 * {wsc:.4f}\n",
          f"kernel source hash (family {fam}): {h}\n",
-         "averages over the timed region's dispatches (per call, its launches "
-         "summed, where the benchmark times calls):",
+         "averages over the timed region's dispatches, "
+         + ("per call of a step (its launches summed):"
+            if prof["profile_layout"].get("per_kernel_timing") == "calls"
+            else "per launch:"),
          f"{'launch':24s} {'FETCH KiB':>11s} {'WRITE KiB':>11s} "
          f"{'read MB':>9s} {'write MB':>9s} {'HBM MB':>9s} {'alg MB':>9s} "
          f"{'HBM/alg':>8s}"]
@@ -1499,6 +1507,9 @@ def main():
     ap.add_argument("--copy-dir", metavar="DIR",
                     help="the copy-calibration counter runs (fetch/, write/, "
                          "fetch.json, write.json)")
+    ap.add_argument("--traffic-json", metavar="PATH", default=None,
+                    help="the traffic record --summarize-traffic updates "
+                         "(default profiles/traffic.json)")
     ap.add_argument("--launch", choices=("auto", "graphs", "eager"),
                     default="auto",
                     help="timed steps as HIP graph replays or eager launches; "
@@ -1511,7 +1522,8 @@ def main():
         summarize_trace(args.summarize_trace, args.workload)
         return
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic, args.workload, args.copy_dir)
+        summarize_traffic(args.summarize_traffic, args.workload, args.copy_dir,
+                          args.traffic_json)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

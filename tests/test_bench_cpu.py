@@ -75,3 +75,67 @@ def test_trace_summary_uses_the_timed_region_only(tmp_path, timing):
     if timing == "calls":    # the call "b" is its two launches
         lines = [ln for ln in text.splitlines() if ln.startswith("b ")]
         assert any(" 20.00 " in ln for ln in lines), text
+
+
+def _counter_csv(path, disp, counter):
+    """A rocprofv3 counter_collection.csv: disp = [(kernel name, KiB)], each
+    dispatch split over two rows (two counter instances) as the tool does."""
+    rows, t = [], 1000
+    for i, (name, kib) in enumerate(disp, 1):
+        for half in (0.25, 0.75):
+            rows.append({"Dispatch_Id": i, "Kernel_Name": name,
+                         "Counter_Name": counter, "Counter_Value": kib * half,
+                         "Start_Timestamp": t, "End_Timestamp": t + 500})
+        t += 1000
+    _write_csv(path, rows, ["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                            "Counter_Value", "Start_Timestamp",
+                            "End_Timestamp"])
+
+
+@pytest.mark.parametrize("timing", ["first_launch", "calls"])
+def test_traffic_summary_per_launch_or_per_call(tmp_path, timing):
+    # per step: "r" three times (a label that recurs, as a ring store per
+    # decode token does) and "c" with two launches (c, c#2); one setup
+    # dispatch before the two timed steps, one armed step after
+    names = {"r": "void kivi::kr<0>(int)", "c": "void kivi::kc<1>(int)",
+             "c#2": "void kivi::kc2(int)"}
+    step = ["r", "r", "r", "c", "c#2"]
+    kib = {"r": 10.0, "c": 100.0, "c#2": 20.0}
+    disp = ([(names["c"], 9999.0)]
+            + [(names[k], kib[k]) for k in step * 2]
+            + [(names[k], 7777.0) for k in step])
+    disp.insert(3, ("void at::fill<float>(int)", 5555.0))   # not the library's
+    for sub, counter in (("pmc_fetch", "FETCH_SIZE"),
+                         ("pmc_write", "WRITE_SIZE")):
+        _counter_csv(str(tmp_path / "run" / sub / "x" /
+                         "bench_counter_collection.csv"), disp, counter)
+    layout = {"dispatches_before_timed": 1, "timed_dispatches": 10,
+              "step_launches": ["r", "r", "r", "c", "c#2"],
+              "per_kernel_timing": timing}
+    pk = {"r": {"avg_us": 1.0, "algorithmic_bytes": 20480},
+          "c": {"avg_us": 9.0, "algorithmic_bytes": 245760}}
+    for f in ("fetch.json", "write.json"):
+        (tmp_path / "run" / f).write_text(_result(layout, pk, "c") + "\n")
+    # the copy: 1 MiB per launch; FETCH_SIZE reads half of it, WRITE_SIZE all
+    for sub, k in (("fetch", 512.0), ("write", 1024.0)):
+        _counter_csv(str(tmp_path / "copy" / sub / "x" /
+                         "copy_counter_collection.csv"),
+                     [("__amd_rocclr_copyBuffer", k)] * 3, "X")
+        (tmp_path / "copy" / (sub + ".json")).write_text(
+            json.dumps({"calibration": {}, "size_bytes": 1 << 20}) + "\n")
+    rec = tmp_path / "traffic.json"
+    out = subprocess.run(
+        [sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-traffic",
+         str(tmp_path / "run"), "--copy-dir", str(tmp_path / "copy"),
+         "--workload", "cache-decode", "--traffic-json", str(rec)],
+        capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    data = json.loads(rec.read_text())
+    r = data["r@cache-decode"]
+    # every "r" launch: 10 KiB fetched (x2 by the copy's scale), 10 written
+    assert (r["fetch_bytes"], r["write_bytes"]) == (20480, 10240), out.stdout
+    c = data["c@cache-decode"]
+    if timing == "calls":       # the call: both launches summed
+        assert (c["fetch_bytes"], c["write_bytes"]) == (245760, 122880)
+    else:                       # the first launch only; c#2 has no bytes
+        assert (c["fetch_bytes"], c["write_bytes"]) == (204800, 102400)
