@@ -77,8 +77,8 @@ def ulp_distance16(a, b):
 
 
 def assert_recon_equal(got, want, what, max_ulp=0):
-    """Reconstructions: bit-exact expected (max_ulp 0); the stated bar is
-    one ulp of the output type.  +0 and -0 compare equal."""
+    """Reconstructions: 0 ulp of the output type (max_ulp 0), which is bit
+    for bit except that +0 and -0, the same value, compare equal."""
     got = np.asarray(got, np.uint16)
     want = np.asarray(want, np.uint16)
     assert got.shape == want.shape, (what, got.shape, want.shape)
