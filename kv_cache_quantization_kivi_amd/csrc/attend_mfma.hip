@@ -4,8 +4,8 @@
 // and expands them in registers, never in memory).  Same chunking,
 // workspace and merge as the token-per-thread kernel in attend.hip; this
 // kernel computes the same quantities with the contractions over the
-// quantized tokens moved to MFMA (the ring's exact tokens of the last
-// chunks stay on the vector units):
+// quantized tokens moved to MFMA, and the scores of the ring's exact tokens
+// too (their values stay on the vector units):
 //
 //   scores  s[t][j] = sum_d (q[j][d] scale[g][d]) code[t][d] + sum_d q[j][d] zero[g][d]
 //           A = codes (M = 16 tokens, K = 32 channels) as the f16
@@ -18,9 +18,12 @@
 //               as f16 subnormals too;
 //           B = the weights p * vscale, hi + lo after a power-of-two scaling
 //               per value group.
-// f16 x f16 products are exact in fp32 and the matrix core accumulates in
-// fp32; hi + lo carries about 22 bits of each scaled operand.  The bias and
-// zero-point sums stay on the vector units in fp32.
+// The hi parts of head j are B's column j and the lo parts its column 8 + j
+// (n_q <= 8), so one instruction takes both; the two columns of C meet in
+// one add across lanes 8 apart (DPP row rotation).  f16 x f16 products are
+// exact in fp32 and the matrix core accumulates in fp32; hi + lo carries
+// about 22 bits of each scaled operand.  The bias and zero-point sums stay
+// on the vector units in fp32.
 //
 // Operand layout of the 16x16x32 instruction (probed on gfx950): lane l
 // holds A[l % 16][8 (l / 16) + i] and B[8 (l / 16) + i][l % 16] for i < 8,
@@ -36,6 +39,7 @@ namespace kivi {
 namespace {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 h2x_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
@@ -59,12 +63,13 @@ struct MfmaShape {
     static constexpr int KGROUPS = kMChunk / GK;      // key groups of a chunk
     static constexpr int MAXGV = D / GK;              // value groups of a row
     static constexpr int VKS = kMChunk / 32;          // k-steps over the tokens
-    static constexpr int kKOps = KGROUPS * 4 * NQ * KS * 2;   // uint4 key operands
-    static constexpr int kVOps = MAXGV * 4 * NQ * VKS * 2;    // uint4 value operands
+    static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KS;   // uint4 key operands
+    static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKS;    // uint4 value operands
     static constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
-    static constexpr int kZero = 2 * (KS > VKS ? KS : VKS);   // zero block (uint4)
+    // half-items of the key operands (a key group's 4 channels) per thread
+    static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
-        NQ * D * 4 + kOps * 16 + kZero * 16 + 2 * KGROUPS * NQ * 4 +
+        NQ * D * 4 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
         NQ * kMChunk * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
@@ -128,9 +133,21 @@ __device__ __forceinline__ void split16x2(float x0, float x1, uint32_t& hi,
     lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// An operand, or zeros when `keep` is false.
-__device__ __forceinline__ h8_t pick_op(uint4 v, bool keep) {
-    return as_h8(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+// B column of this lane (m16 = lane % 16): head m16's hi parts in columns
+// [0, NQ), its lo parts in [8, 8 + NQ); the other columns of C are never
+// used, so their lanes read column 0's operands (the same addresses as the
+// lanes of column 0).
+template <int NQ>
+__device__ __forceinline__ int b_col(int m16) {
+    return m16 < NQ ? m16 : (m16 >= 8 && m16 < 8 + NQ ? NQ + m16 - 8 : 0);
+}
+
+// x plus the value of the lane 8 up in its row of 16 (lane l + 8 for
+// l % 16 < 8): a head's hi-part sum and its lo-part sum.
+__device__ __forceinline__ float add_lo_half(float x) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */,
+                                              0xf, 0xf, false);
+    return x + __int_as_float(y);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -144,6 +161,17 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// One 16x16x32 product of 16-bit operands of the cache's type.
+template <int DT>
+__device__ __forceinline__ f4_t mfma16(uint4 A, uint4 B, f4_t C) {
+    if constexpr (DT == DT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, A),
+                                                      __builtin_bit_cast(h8_t, B), C, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, A),
+                                                       __builtin_bit_cast(b8_t, B), C, 0, 0, 0);
+}
+
 template <int DT>
 __device__ __forceinline__ float widen_h(uint16_t h) {
     if constexpr (DT == DT_F16)
@@ -154,16 +182,19 @@ __device__ __forceinline__ float widen_h(uint16_t h) {
 
 }  // namespace
 
-// One 128-thread block (two waves) per (chunk, bh).  The chunk's quantized
-// tokens (a whole number of key groups, since Q is G_k-aligned) go through
-// the matrix cores; its ring tokens through the vector units.  The caller
+// One 128-thread block (two waves) per (chunk, bh).  The chunk's scores go
+// through the matrix cores, its quantized tokens' values too (Q is
+// G_k-aligned, so a 16-token tile is all quantized or all exact); the ring's
+// exact values are summed on the vector units.  The caller
 // guarantees D in {64, 128}, BITS <= 4, G_k in {16, 32}, a value group of
 // 16 * 2^k channels and n_q <= NQ.
 //
 // B operands live in LDS, each lane's operands of one group contiguous:
-// keys [g][kb][j][k-step][hi, lo], values [gv][kb][j][k-step][hi, lo]
-// (uint4 = 8 halves each).  Lanes past the query heads read a zero block
-// instead (an LDS address select), so no operand needs masking.
+// keys [g][kb][column][k-step], values [gv][kb][column][k-step] (uint4 = 8
+// halves each; columns: the heads' hi parts, then their lo parts).  A wave
+// loads one group's operands into registers and uses them for every tile
+// of that group: its tiles are taken group by group (tiles 2w, 2w + 1,
+// 2w + 4, 2w + 5 of wave w).
 template <int DT, int BITS, int D, int NQ, int GK>
 __global__ __launch_bounds__(kMChunk, (MfmaShape<BITS, D, NQ, GK>::kWaves))
 void attend_mfma_kernel(AttendArgs a) {
@@ -171,12 +202,11 @@ void attend_mfma_kernel(AttendArgs a) {
     constexpr int D8 = Sh::D8, KS = Sh::KS, CPL = Sh::CPL, LB = Sh::LB;
     constexpr int DW = Sh::DW, MT = Sh::MT, MAXGV = Sh::MAXGV, VKS = Sh::VKS;
     constexpr int kMaxKGroups = Sh::KGROUPS;
-    constexpr int kOps = Sh::kOps, kZero = Sh::kZero;
+    constexpr int kOps = Sh::kOps, KH = Sh::KH;
     static_assert(NQ * MAXGV * kMChunk <= kOps * 4, "zero-point rows fit");
 
     __shared__ __attribute__((aligned(16))) float q_s[NQ][D];
     __shared__ __attribute__((aligned(16))) uint4 ops_s[kOps];
-    __shared__ __attribute__((aligned(16))) uint4 zero_s[kZero];
     __shared__ float kbias_s[kMaxKGroups][NQ];
     __shared__ int kexp_s[kMaxKGroups][NQ];
     __shared__ __attribute__((aligned(16))) float p_s[NQ][kMChunk];
@@ -191,7 +221,13 @@ void attend_mfma_kernel(AttendArgs a) {
     __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
 
-    const int chunk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    // Blocks run the chunks from the last one down, every bh of a chunk
+    // before the next chunk: the chunks that hold the ring's exact tokens,
+    // which take longest, start first instead of closing the grid.
+    const int n_bh = (int)(gridDim.x / (uint32_t)a.n_chunks);
+    const int bh = (int)(blockIdx.x % (uint32_t)n_bh);
+    const int chunk = a.n_chunks - 1 - (int)(blockIdx.x / (uint32_t)n_bh);
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, kb = lane >> 4;
     const int nq = a.n_q;
@@ -210,30 +246,29 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
         qv[j] = (tid < D && j < nq) ? widen_h<DT>(a.q[((int64_t)bh * nq + j) * D + tid]) : 0.0f;
-    // key params of this thread's item (key group g, 8-channel chunk c8)
-    const bool kitem = tid < ngk * D8;
-    const int kg = kitem ? tid / D8 : 0, kc8 = tid % D8;
-    float ksc[8], kzr[8];
-    {
-        const int64_t p = ((int64_t)bh * a.NG + g0 + kg) * D + kc8 * 8;
-        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0, z0 = s0, z1 = s0;
-        if (kitem) {
+    // key params of this thread's half-items: half-item h = tid + 128 r is
+    // 4 channels (c4) of key group h / (2 D8), the group's half-items in
+    // consecutive lanes
+    float ksc[KH][4], kzr[KH][4];
+#pragma unroll
+    for (int r = 0; r < KH; ++r) {
+        const int h = tid + kMChunk * r;
+        const int kg = h / (2 * D8), c4 = h % (2 * D8);
+        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), z0 = s0;
+        if (h < ngk * D8 * 2) {
+            const int64_t p = ((int64_t)bh * a.NG + g0 + kg) * D + c4 * 4;
             s0 = *reinterpret_cast<const float4*>(a.k_scale + p);
-            s1 = *reinterpret_cast<const float4*>(a.k_scale + p + 4);
             z0 = *reinterpret_cast<const float4*>(a.k_zero + p);
-            z1 = *reinterpret_cast<const float4*>(a.k_zero + p + 4);
         }
-        ksc[0] = s0.x; ksc[1] = s0.y; ksc[2] = s0.z; ksc[3] = s0.w;
-        ksc[4] = s1.x; ksc[5] = s1.y; ksc[6] = s1.z; ksc[7] = s1.w;
-        kzr[0] = z0.x; kzr[1] = z0.y; kzr[2] = z0.z; kzr[3] = z0.w;
-        kzr[4] = z1.x; kzr[5] = z1.y; kzr[6] = z1.z; kzr[7] = z1.w;
+        ksc[r][0] = s0.x; ksc[r][1] = s0.y; ksc[r][2] = s0.z; ksc[r][3] = s0.w;
+        kzr[r][0] = z0.x; kzr[r][1] = z0.y; kzr[r][2] = z0.z; kzr[r][3] = z0.w;
     }
     // this lane's key code blocks of its four 16-token tiles
     constexpr int LBW = LB >= 4 ? LB / 4 : 1;
     uint32_t kw[4][LBW];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
-        const int tok0 = (wave + 2 * tt) * 16;
+        const int tok0 = ((tt >> 1) * 4 + 2 * wave + (tt & 1)) * 16;
         kw[tt][0] = 0u;
         if (tok0 >= nq_tok) continue;          // no codes past Q
         const uint8_t* crow = a.k_codes +
@@ -280,99 +315,130 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
         if (tid < D) q_s[j][tid] = qv[j];
-    if (tid < kZero) zero_s[tid] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
 
     // ---- key operands: q[j][d] scale[g][d] 2^e(g, j) as hi + lo and the
-    // zero bias.  Thread = item (g, 8-channel chunk) for every head; the D8
-    // items of a group sit in consecutive lanes (all items, or none), where
-    // each head's maximum (for e) and bias sum meet in xor shuffles. ----
-    if (kitem) {
+    // zero bias, on both waves.  Thread = half-item (g, 4 channels) for
+    // every head; the 2 D8 half-items of a group sit in consecutive lanes
+    // (all of them, or none), where each head's maximum (for e) and bias sum
+    // meet in xor shuffles. ----
+#pragma unroll
+    for (int r = 0; r < KH; ++r) {
+        const int h = tid + kMChunk * r;
+        if (h >= ngk * D8 * 2) continue;
+        const int kg = h / (2 * D8), c4 = h % (2 * D8);
+        const int d = c4 * 4, blk = d / CPL, s = (d % CPL) / 8, half = (d % 8) / 4;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
-            float pr[8], b = 0.0f, mxl = 0.0f;
+            float pr[4], b = 0.0f, mxl = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float qd = q_s[j][kc8 * 8 + i];
-                pr[i] = qd * ksc[i];
+            for (int i = 0; i < 4; ++i) {
+                const float qd = q_s[j][d + i];
+                pr[i] = qd * ksc[r][i];
                 mxl = fmaxf(mxl, fabsf(pr[i]));
-                b = __builtin_fmaf(qd, kzr[i], b);
+                b = __builtin_fmaf(qd, kzr[r][i], b);
             }
 #pragma unroll
-            for (int o = 1; o < D8; o <<= 1) {
+            for (int o = 1; o < 2 * D8; o <<= 1) {
                 b += __shfl_xor(b, o);
                 mxl = fmaxf(mxl, __shfl_xor(mxl, o));
             }
-            if (kitem) {
-                const int e = op_exp(mxl);
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int i = 0; i < 8; i += 2) {
-                    split16x2(__builtin_ldexpf(pr[i], e), __builtin_ldexpf(pr[i + 1], e),
-                              hw[i / 2], lw[i / 2]);
-                }
-                const int d = kc8 * 8, blk = d / CPL, s = (d % CPL) / 8;
-                uint4* ob = ops_s + ((kg * 4 + blk) * NQ + j) * (2 * KS);
-                ob[2 * s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                ob[2 * s + 1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-                if (kc8 == 0) {
-                    kbias_s[kg][j] = b;
-                    kexp_s[kg][j] = e;
-                }
+            const int e = op_exp(mxl);
+            uint32_t h0, h1, l0, l1;
+            split16x2(__builtin_ldexpf(pr[0], e), __builtin_ldexpf(pr[1], e), h0, l0);
+            split16x2(__builtin_ldexpf(pr[2], e), __builtin_ldexpf(pr[3], e), h1, l1);
+            uint2* hb = reinterpret_cast<uint2*>(
+                ops_s + (((kg * 4 + blk) * 2 * NQ + j) * KS + s)) + half;
+            uint2* lb = reinterpret_cast<uint2*>(
+                ops_s + (((kg * 4 + blk) * 2 * NQ + NQ + j) * KS + s)) + half;
+            *hb = make_uint2(h0, h1);
+            *lb = make_uint2(l0, l1);
+            if (c4 == 0) {
+                kbias_s[kg][j] = b;
+                kexp_s[kg][j] = e;
             }
         }
     }
     __syncthreads();
 
-    // ---- scores on the matrix cores: wave w takes 16-token tiles w, w+2, ...
+    // ---- scores on the matrix cores: wave w takes 16-token tiles 2w,
+    // 2w + 1, 2w + 4, 2w + 5 (two whole key groups of 32 tokens), with the
+    // B operands of a group loaded once.  Tiles of the ring's exact tokens
+    // (Q is a multiple of 16, so a tile is all quantized or all exact) take
+    // the keys themselves as A and the 16-bit query as B, both exact in the
+    // cache's type: their scores need no split, no scaling and no bias.
+    {
+        const int col = b_col<NQ>(m16);
+        int gcur = -1;
+        uint4 bk[KS];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int tok0 = (wave + 2 * tt) * 16;
-        if (tok0 >= nq_tok) break;             // wave-uniform
-        const int g = tok0 >> gk_sh;
-        const uint4* bp = m16 < NQ ? ops_s + ((g * 4 + kb) * NQ + m16) * (2 * KS) : zero_s;
-        f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tt = 0; tt < 4; ++tt) {
+            const int tok0 = ((tt >> 1) * 4 + 2 * wave + (tt & 1)) * 16;
+            if (tok0 >= nq_tok) continue;          // wave-uniform
+            const int g = tok0 >> gk_sh;
+            if (g != gcur) {                       // wave-uniform
+                const uint4* bp = ops_s + ((g * 4 + kb) * 2 * NQ + col) * KS;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            constexpr int SB = 8 * BITS;                    // bits per k-step
-            const int bit = s * SB;
-            uint32_t bits = kw[tt][bit / 32] >> (bit % 32);
-            if constexpr (SB < 32) bits &= (1u << SB) - 1u;
-            const h8_t A = codes8<BITS>(bits);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s + 1]), acc, 0, 0, 0);
-        }
-        if (m16 < NQ) {
-            const int e = kexp_s[g][m16];
-            const float bias = kbias_s[g][m16];
+                for (int s = 0; s < KS; ++s) bk[s] = bp[s];
+                gcur = g;
+            }
+            f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p_s[m16][tok0 + kb * 4 + i] = __builtin_ldexpf(acc[i], kCodeExp - e) + bias;
-        }
-    }
-    __syncthreads();
-
-    // ---- the ring's exact keys (tokens nq_tok .. nt - 1): thread = token
-    if (tid >= nq_tok && tid < nt) {
-        const uint16_t* krow = a.k_ring + ((int64_t)bh * a.ring + (t0 + tid) % a.ring) * D;
-        float sc[NQ];
+            for (int s = 0; s < KS; ++s) {
+                constexpr int SB = 8 * BITS;                // bits per k-step
+                const int bit = s * SB;
+                uint32_t bits = kw[tt][bit / 32] >> (bit % 32);
+                if constexpr (SB < 32) bits &= (1u << SB) - 1u;
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    codes8<BITS>(bits), __builtin_bit_cast(h8_t, bk[s]), acc, 0, 0, 0);
+            }
+            float sc[4];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) sc[j] = 0.0f;
-#pragma unroll 4
-        for (int c8 = 0; c8 < D8; ++c8) {
-            const uint4 x = *reinterpret_cast<const uint4*>(krow + c8 * 8);
-            const uint32_t wx[4] = {x.x, x.y, x.z, x.w};
+            for (int i = 0; i < 4; ++i) sc[i] = add_lo_half(acc[i]);
+            if (m16 < NQ) {
+                const int e = kexp_s[g][m16];
+                const float bias = kbias_s[g][m16];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float k = widen_h<DT>((uint16_t)(wx[e >> 1] >> ((e & 1) * 16)));
-#pragma unroll
-                for (int j = 0; j < NQ; ++j) sc[j] = __builtin_fmaf(q_s[j][c8 * 8 + e], k, sc[j]);
+                for (int i = 0; i < 4; ++i)
+                    p_s[m16][tok0 + kb * 4 + i] = __builtin_ldexpf(sc[i], kCodeExp - e) + bias;
             }
         }
+    }
+    if (nq_tok < nt) {                             // block-uniform: ring tiles
+        bool have_q = false;
+        uint4 bq[KS];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) p_s[j][tid] = sc[j];
+        for (int tt = 0; tt < 4; ++tt) {
+            const int tok0 = ((tt >> 1) * 4 + 2 * wave + (tt & 1)) * 16;
+            if (tok0 < nq_tok || tok0 >= nt) continue;   // wave-uniform
+            if (!have_q) {
+                // B = the query of head m16 (zeros in the other columns)
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const int d0 = kb * CPL + s * 8;
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    if (m16 < NQ) {   // exact: the query is of the cache's type
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            w[i] = narrow2<DT>(q_s[m16][d0 + 2 * i], q_s[m16][d0 + 2 * i + 1]);
+                    }
+                    bq[s] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+                have_q = true;
+            }
+            // A = the keys of tokens tok0 + m16, channels of lane block kb
+            // (a row past T holds another ring token; its score is never read)
+            const uint16_t* krow = a.k_ring +
+                ((int64_t)bh * a.ring + (t0 + tok0 + m16) % a.ring) * D + kb * CPL;
+            f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                acc = mfma16<DT>(*reinterpret_cast<const uint4*>(krow + s * 8), bq[s], acc);
+            if (m16 < NQ) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p_s[m16][tok0 + kb * 4 + i] = acc[i];
+            }
+        }
     }
     __syncthreads();
 
@@ -432,29 +498,41 @@ void attend_mfma_kernel(AttendArgs a) {
     for (int j = 0; j < NQ; ++j) p_s[j][tid] = pt[j];
     __syncthreads();
     // the ring's exact values: thread = channel, summed over the ring tokens
-    // into the (now free) query rows
+    // into the (now free) query rows.  The chunk's ring tokens are fewer
+    // than the ring's slots (T - Q < R + G_k <= ring), so their slots follow
+    // the first one with at most one wrap.  Sixteen tokens' loads are in
+    // flight at a time, the next sixteen issued before this batch's sums.
     const bool has_ring = nq_tok < nt;        // block-uniform
     if (has_ring && tid < D) {
         float o[NQ];
 #pragma unroll
         for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
-        // eight tokens' loads in flight at a time
-        for (int tb = nq_tok; tb < nt; tb += 8) {
-            float v[8];
+        const uint16_t* vcol = a.v_ring + (int64_t)bh * a.ring * D + tid;
+        const int slot0 = (t0 + nq_tok) % a.ring;
+        const int n_ring = nt - nq_tok;
+        uint16_t v[16], vn[16] = {};
+        auto load16 = [&](uint16_t* dst, int base) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int t = min(tb + u, nt - 1);
-                v[u] = widen_h<DT>(
-                    a.v_ring[((int64_t)bh * a.ring + (t0 + t) % a.ring) * D + tid]);
+            for (int u = 0; u < 16; ++u) {
+                int sl = slot0 + min(base + u, n_ring - 1);
+                if (sl >= a.ring) sl -= a.ring;
+                dst[u] = vcol[(int64_t)sl * D];
             }
+        };
+        load16(v, 0);
+        for (int tb = 0; tb < n_ring; tb += 16) {
+            if (tb + 16 < n_ring) load16(vn, tb + 16);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                if (tb + u < nt) {
+            for (int u = 0; u < 16; ++u) {
+                if (tb + u < n_ring) {
+                    const float x = widen_h<DT>(v[u]);
 #pragma unroll
                     for (int j = 0; j < NQ; ++j)
-                        o[j] = __builtin_fmaf(p_s[j][tb + u], v[u], o[j]);
+                        o[j] = __builtin_fmaf(p_s[j][nq_tok + tb + u], x, o[j]);
                 }
             }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = vn[u];
         }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) q_s[j][tid] = o[j];
@@ -506,9 +584,10 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     if (j + u < NQ) {
-                        _Float16* vb = vops + ((gv * 4 + blk) * NQ + j + u) * (2 * VKS) * 8;
-                        vb[(2 * s4) * 8 + i] = __builtin_bit_cast(_Float16, (uint16_t)(hi >> (16 * u)));
-                        vb[(2 * s4 + 1) * 8 + i] = __builtin_bit_cast(_Float16, (uint16_t)(lo >> (16 * u)));
+                        _Float16* vh = vops + (((gv * 4 + blk) * 2 * NQ + j + u) * VKS + s4) * 8;
+                        _Float16* vl = vops + (((gv * 4 + blk) * 2 * NQ + NQ + j + u) * VKS + s4) * 8;
+                        vh[i] = __builtin_bit_cast(_Float16, (uint16_t)(hi >> (16 * u)));
+                        vl[i] = __builtin_bit_cast(_Float16, (uint16_t)(lo >> (16 * u)));
                     }
                 }
             }
@@ -516,42 +595,56 @@ void attend_mfma_kernel(AttendArgs a) {
     }
     __syncthreads();
 
-    // ---- values on the matrix cores: wave w takes channel tiles w, w+2, ...
+    // ---- values on the matrix cores: wave w takes channel tiles 2w, 2w + 1,
+    // 2w + 4, 2w + 5 (pairs of tiles in one value group when groups have 32
+    // channels or more), with the B operands of a group loaded once
     float* wbase = a.work + ((int64_t)bh * a.n_chunks + chunk) * nq * (D + 2);
-    for (int mt = wave; mt < MT; mt += 2) {
-        const int gv = (mt * 16) >> gv_sh;
-        const int ch = mt * 16 + m16;                   // this lane's A row
-        const int q = (ch * BITS) / 16, sh = (ch * BITS) % 16;
-        const uint32_t pmask = ((1u << BITS) - 1u) * 0x10001u;
-        const uint4* bp = m16 < NQ ? ops_s + ((gv * 4 + kb) * NQ + m16) * (2 * VKS) : zero_s;
-        f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    {
+        const int col = b_col<NQ>(m16);
+        int gcur = -1;
+        uint4 bv[VKS];
 #pragma unroll
-        for (int s4 = 0; s4 < VKS; ++s4) {
-            // tokens s4*32 + kb*8 + [0, 8) are pairs P0 .. P0 + 3, each dword
-            // holding this channel's two codes sh bits up in its two halves
-            const int P0 = s4 * 16 + kb * 4;
-            const uint4 d = *reinterpret_cast<const uint4*>(&vp_s[q][P0]);
-            const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-            constexpr uint32_t M = (1u << BITS) - 1u;
-            uint32_t pr[4];
+        for (int u = 0; u < MT / 2; ++u) {
+            const int mt = (u >> 1) * 4 + 2 * wave + (u & 1);
+            const int gv = (mt * 16) >> gv_sh;
+            if (gv != gcur) {                      // wave-uniform
+                const uint4* bp = ops_s + ((gv * 4 + kb) * 2 * NQ + col) * VKS;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) pr[k] = (dw[k] >> sh) & pmask;   // codes * 2^-24
-            const h8_t A = as_h8(pr[0], pr[1], pr[2], pr[3]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s4]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(h8_t, bp[2 * s4 + 1]), acc, 0, 0, 0);
-        }
-        // C: lane (head m16, row block kb) holds channels mt*16 + 4 kb + i
-        if (m16 < nq) {
-            const int e = op_exp(vmax_s[gv]);
-            const float zs = zsum_s[m16 * ngd + gv];
-            float* wj = wbase + m16 * (D + 2);
+                for (int s4 = 0; s4 < VKS; ++s4) bv[s4] = bp[s4];
+                gcur = gv;
+            }
+            const int ch = mt * 16 + m16;                   // this lane's A row
+            const int q = (ch * BITS) / 16, sh = (ch * BITS) % 16;
+            const uint32_t pmask = ((1u << BITS) - 1u) * 0x10001u;
+            f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = mt * 16 + kb * 4 + i;
-                wj[2 + ch] = __builtin_ldexpf(acc[i], kCodeExp - e) + zs +
-                             (has_ring ? q_s[m16][ch] : 0.0f);
+            for (int s4 = 0; s4 < VKS; ++s4) {
+                // tokens s4*32 + kb*8 + [0, 8) are pairs P0 .. P0 + 3, each dword
+                // holding this channel's two codes sh bits up in its two halves
+                const int P0 = s4 * 16 + kb * 4;
+                const uint4 d = *reinterpret_cast<const uint4*>(&vp_s[q][P0]);
+                const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+                uint32_t pr[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pr[k] = (dw[k] >> sh) & pmask;   // codes * 2^-24
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    as_h8(pr[0], pr[1], pr[2], pr[3]), __builtin_bit_cast(h8_t, bv[s4]),
+                    acc, 0, 0, 0);
+            }
+            float ov[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = add_lo_half(acc[i]);
+            // C: lane (head m16, row block kb) holds channels mt*16 + 4 kb + i
+            if (m16 < nq) {
+                const int e = op_exp(vmax_s[gv]);
+                const float zs = zsum_s[m16 * ngd + gv];
+                float* wj = wbase + m16 * (D + 2);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = mt * 16 + kb * 4 + i;
+                    wj[2 + c] = __builtin_ldexpf(ov[i], kCodeExp - e) + zs +
+                                (has_ring ? q_s[m16][c] : 0.0f);
+                }
             }
         }
     }
@@ -564,7 +657,10 @@ void attend_mfma_kernel(AttendArgs a) {
 template <int DT, int BITS, int D, int NQ>
 static hipError_t launch_mfma_t(const AttendArgs& a, int64_t BH, int n_full,
                                 hipStream_t stream) {
-    const dim3 grid((uint32_t)n_full, (uint32_t)BH), block(kMChunk);
+    // one block per (chunk, bh), every chunk of the call (see the kernel)
+    if (n_full != a.n_chunks || (int64_t)n_full * BH >= (1ll << 31))
+        return hipErrorInvalidConfiguration;
+    const dim3 grid((uint32_t)(n_full * BH)), block(kMChunk);
     if (a.G_k == 32 && a.G_v >= 32)
         return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 32>), grid,
                              block, 0, stream, a);
