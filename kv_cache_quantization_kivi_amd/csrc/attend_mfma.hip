@@ -142,23 +142,61 @@ __device__ __forceinline__ int b_col(int m16) {
     return m16 < NQ ? m16 : (m16 >= 8 && m16 < 8 + NQ ? NQ + m16 - 8 : 0);
 }
 
+
+// Lane permutations inside rows of 16 lanes (DPP) and across the halves of
+// 32 lanes (an LDS-unit swizzle that touches no memory), for reductions
+// over aligned blocks of lanes.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float xor16_f(float v) {   // lane l reads lane l ^ 16
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+__device__ __forceinline__ uint32_t xor16_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
+// Sum over aligned blocks of N lanes (N a power of two <= 32); every lane of
+// a block receives the same value (each step adds a pair in both orders).
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror,
+// then lane ^ 16.
+template <int N>
+__device__ __forceinline__ float block_sum(float v) {
+    if constexpr (N > 1) v += dpp_f<0xB1>(v);
+    if constexpr (N > 2) v += dpp_f<0x4E>(v);
+    if constexpr (N > 4) v += dpp_f<0x141>(v);
+    if constexpr (N > 8) v += dpp_f<0x140>(v);
+    if constexpr (N > 16) v += xor16_f(v);
+    return v;
+}
+// Maximum of non-negative floats over aligned blocks of N lanes, on their
+// bit patterns (which order like the values).
+template <int N>
+__device__ __forceinline__ float block_max_nonneg(float x) {
+    uint32_t v = __float_as_uint(x);
+    if constexpr (N > 1) v = max(v, dpp_u<0xB1>(v));
+    if constexpr (N > 2) v = max(v, dpp_u<0x4E>(v));
+    if constexpr (N > 4) v = max(v, dpp_u<0x141>(v));
+    if constexpr (N > 8) v = max(v, dpp_u<0x140>(v));
+    if constexpr (N > 16) v = max(v, xor16_u(v));
+    return __uint_as_float(v);
+}
+// Maximum over aligned blocks of 8 lanes.
+__device__ __forceinline__ float block8_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    return fmaxf(v, dpp_f<0x141>(v));
+}
+
 // x plus the value of the lane 8 up in its row of 16 (lane l + 8 for
 // l % 16 < 8): a head's hi-part sum and its lo-part sum.
 __device__ __forceinline__ float add_lo_half(float x) {
-    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */,
-                                              0xf, 0xf, false);
-    return x + __int_as_float(y);
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return x + dpp_f<0x128>(x);   // row_ror:8
 }
 
 // One 16x16x32 product of 16-bit operands of the cache's type.
@@ -338,11 +376,8 @@ void attend_mfma_kernel(AttendArgs a) {
                 mxl = fmaxf(mxl, fabsf(pr[i]));
                 b = __builtin_fmaf(qd, kzr[r][i], b);
             }
-#pragma unroll
-            for (int o = 1; o < 2 * D8; o <<= 1) {
-                b += __shfl_xor(b, o);
-                mxl = fmaxf(mxl, __shfl_xor(mxl, o));
-            }
+            b = block_sum<2 * D8>(b);
+            mxl = block_max_nonneg<2 * D8>(mxl);
             const int e = op_exp(mxl);
             uint32_t h0, h1, l0, l1;
             split16x2(__builtin_ldexpf(pr[0], e), __builtin_ldexpf(pr[1], e), h0, l0);
@@ -454,8 +489,7 @@ void attend_mfma_kernel(AttendArgs a) {
             const int t = (tid & 7) + 8 * ((u + j) & (kMChunk / 8 - 1));
             if (t < nt) v = fmaxf(v, p_s[j][t] * a.sm_scale);
         }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+        v = block8_max(v);
         if ((tid & 7) == 0) ml_s[0][j] = v;
     }
     // value codes (by token pair) and value scales of this thread's token
@@ -472,7 +506,7 @@ void attend_mfma_kernel(AttendArgs a) {
         for (int k = 0; k < DW / 2; ++k) {
             const uint32_t lo_w = vw[k], hi_w = vw[k + DW / 2];   // static indices
             const uint32_t mine = even ? lo_w : hi_w;
-            const uint32_t other = (uint32_t)__shfl_xor((int)(even ? hi_w : lo_w), 1);
+            const uint32_t other = dpp_u<0xB1>(even ? hi_w : lo_w);   // lane ^ 1
             row[(2 * k) * kVpStride] = __builtin_amdgcn_perm(other, mine, sel_lo);
             row[(2 * k + 1) * kVpStride] = __builtin_amdgcn_perm(other, mine, sel_hi);
         }
@@ -548,8 +582,7 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll 4
             for (int u = 0; u < kMChunk / 8; ++u)
                 v += row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))];
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o);
+            v = block_sum<8>(v);
             if ((tid & 7) == 0) {
                 if (k < NQ) ml_s[1][k] = v;
                 else zsum_s[k - NQ] = v;
@@ -560,8 +593,7 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll 4
             for (int u = 0; u < kMChunk / 8; ++u)
                 v = fmaxf(v, row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))]);
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+            v = block8_max(v);
             if ((tid & 7) == 0) vmax_s[k - n_sum] = v;
         }
     }

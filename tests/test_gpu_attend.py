@@ -73,6 +73,20 @@ def test_attend_long_context_chunks(K, O):
     _run_case(K, O, LONG_CASE)
 
 
+# more (chunk, bh) blocks than the device holds at once (128 heads x 33
+# chunks, 97 heads x 33 chunks), in fp16 with 2-bit codes and in bf16 with
+# 4-bit codes, an even and an odd block count
+MANY_BLOCKS = [
+    (128, 128, 32, 32, 32, 2, FP16, 3, [4096, 3]),
+    (97, 128, 32, 16, 32, 4, 1, 2, [2048, 2048, 40]),
+]
+
+
+@pytest.mark.parametrize("case", MANY_BLOCKS, ids=case_id)
+def test_attend_many_blocks(K, O, case):
+    _run_case(K, O, case)
+
+
 def test_attend_rejects(K):
     c = K.KiviCache(2, 256, 64, 8, 8, 8, 2, torch.float16)  # D = 256
     x = torch.zeros((2, 4, 256), dtype=torch.float16, device="cuda")
