@@ -112,14 +112,29 @@ __device__ __forceinline__ h8_t codes8(uint32_t bits) {
     return as_h8(d[0], d[1], d[2], d[3]);
 }
 
-// Scaling exponent for operands bounded by P: P * 2^e < 2^14, so that hi
-// and lo stay finite f16 values (0 when P is 0 or not finite).
+// The 16 two-bit codes of a dword as the A operands of two k-steps (codes
+// 0-7, codes 8-15), f16 subnormals as codes8 makes them: the four codes
+// 4k + r of byte k sit in byte k of copy r (a shift and a mask each), and
+// one byte permute per operand dword takes a code pair from two copies.
+__device__ __forceinline__ void codes16_2bit(uint32_t w, h8_t& A0, h8_t& A1) {
+    const uint32_t m = 0x03030303u;
+    const uint32_t u0 = w & m, v0 = (w >> 2) & m, u1 = (w >> 4) & m, v1 = (w >> 6) & m;
+    // byte 0 of the result from byte b of the first copy, byte 2 from byte b
+    // of the second, bytes 1 and 3 zero
+#define KIVI_PAIR(x, y, b) __builtin_amdgcn_perm((y), (x), 0x0c000c00u | (b) | ((4u + (b)) << 16))
+    A0 = as_h8(KIVI_PAIR(u0, v0, 0u), KIVI_PAIR(u1, v1, 0u), KIVI_PAIR(u0, v0, 1u),
+               KIVI_PAIR(u1, v1, 1u));
+    A1 = as_h8(KIVI_PAIR(u0, v0, 2u), KIVI_PAIR(u1, v1, 2u), KIVI_PAIR(u0, v0, 3u),
+               KIVI_PAIR(u1, v1, 3u));
+#undef KIVI_PAIR
+}
+
+// Scaling exponent for operands bounded by a finite P >= 0: with
+// P = m 2^x, m in [1/2, 1) (frexp, subnormals included), P * 2^(14 - x) lies
+// in [2^13, 2^14), so that hi and lo stay finite f16 values with the most
+// bits kept (P = 0 gives 14, and every operand is 0).
 __device__ __forceinline__ int op_exp(float P) {
-    if (!(P > 0.0f) || !(P <= 3.0e38f)) return 0;
-    // floor(log2 P) from the exponent field (a subnormal P counts as 2^-127,
-    // which still keeps P * 2^e below 2^14)
-    const int lg = (int)((__float_as_uint(P) >> 23) & 0xffu) - 127;
-    return 13 - lg;
+    return 14 - __builtin_amdgcn_frexp_expf(P);
 }
 
 // x = hi + lo with hi = RN16(x) and lo = RN16(x - hi), for two values at
@@ -128,8 +143,11 @@ __device__ __forceinline__ int op_exp(float P) {
 __device__ __forceinline__ void split16x2(float x0, float x1, uint32_t& hi,
                                           uint32_t& lo) {
     const h2x_t h = {(_Float16)x0, (_Float16)x1};
-    const h2x_t l = {(_Float16)(x0 - (float)h.x), (_Float16)(x1 - (float)h.y)};
     hi = __builtin_bit_cast(uint32_t, h);
+    // the hi parts widened back from the packed pair
+    const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)hi);
+    const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(hi >> 16));
+    const h2x_t l = {(_Float16)(x0 - h0), (_Float16)(x1 - h1)};
     lo = __builtin_bit_cast(uint32_t, l);
 }
 
@@ -255,7 +273,7 @@ void attend_mfma_kernel(AttendArgs a) {
     constexpr int kVpStride = kMChunk / 2 + 4;
     __shared__ __attribute__((aligned(16))) uint32_t vp_s[2 * DW][kVpStride];
     __shared__ __attribute__((aligned(16))) float sv_s[MAXGV][kMChunk];
-    __shared__ float vmax_s[MAXGV];
+    __shared__ int vexp_s[MAXGV];          // scaling exponent of each value group
     __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
 
@@ -418,14 +436,26 @@ void attend_mfma_kernel(AttendArgs a) {
                 gcur = g;
             }
             f4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (BITS == 2) {
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                constexpr int SB = 8 * BITS;                // bits per k-step
-                const int bit = s * SB;
-                uint32_t bits = kw[tt][bit / 32] >> (bit % 32);
-                if constexpr (SB < 32) bits &= (1u << SB) - 1u;
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    codes8<BITS>(bits), __builtin_bit_cast(h8_t, bk[s]), acc, 0, 0, 0);
+                for (int s = 0; s < KS; s += 2) {         // a code dword per two k-steps
+                    h8_t A0, A1;
+                    codes16_2bit(kw[tt][s / 2], A0, A1);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A0, __builtin_bit_cast(h8_t, bk[s]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        A1, __builtin_bit_cast(h8_t, bk[s + 1]), acc, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    constexpr int SB = 8 * BITS;            // bits per k-step
+                    const int bit = s * SB;
+                    uint32_t bits = kw[tt][bit / 32] >> (bit % 32);
+                    if constexpr (SB < 32) bits &= (1u << SB) - 1u;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        codes8<BITS>(bits), __builtin_bit_cast(h8_t, bk[s]), acc, 0, 0, 0);
+                }
             }
             float sc[4];
 #pragma unroll
@@ -478,19 +508,30 @@ void attend_mfma_kernel(AttendArgs a) {
     __syncthreads();
 
     // ---- softmax partial of the chunk: eight lanes per head find the max,
-    // then every thread takes its token's p, then eight lanes per head sum
-    // (rows are 512 bytes apart, so each row's lanes start at another eight
-    // banks: lane i of row j reads t = i + 8 ((u + j) mod 16) at step u)
+    // then every thread takes its token's p, then eight lanes per row sum.
+    // Eight lanes read a 128-token row as four 16-byte pieces each: lane i
+    // takes tokens 4i .. 4i + 3 of each block of 32, the blocks in an order
+    // rotated by one on odd rows, so that the two rows of a 16-lane LDS pass
+    // sit in different banks (rows are 512 bytes apart).
+    const int i8 = tid & 7;
+    auto row4 = [&](const float* row, int k, int m) {
+        return *reinterpret_cast<const float4*>(
+            row + ((4 * i8 + 32 * (m + (k & 1))) & (kMChunk - 1)));
+    };
     if (tid < 8 * NQ) {
         const int j = tid >> 3;
         float v = -__builtin_huge_valf();
-#pragma unroll 4
-        for (int u = 0; u < kMChunk / 8; ++u) {
-            const int t = (tid & 7) + 8 * ((u + j) & (kMChunk / 8 - 1));
-            if (t < nt) v = fmaxf(v, p_s[j][t] * a.sm_scale);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 x = row4(p_s[j], j, m);
+            const int t = (4 * i8 + 32 * (m + (j & 1))) & (kMChunk - 1);
+            const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (nt == kMChunk || t + e < nt) v = fmaxf(v, xs[e] * a.sm_scale);
         }
         v = block8_max(v);
-        if ((tid & 7) == 0) ml_s[0][j] = v;
+        if (i8 == 0) ml_s[0][j] = v;
     }
     // value codes (by token pair) and value scales of this thread's token
     // into LDS
@@ -571,30 +612,31 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) q_s[j][tid] = o[j];
     }
-    // eight lanes per row: the sums of p (per head) and of p * zero, and the
-    // maxima of the value scales (rotated starts as above: the eight rows a
-    // wave reads at once sit in distinct banks)
+    // eight lanes per row (read as above): the sums of p (per head) and of
+    // p * zero, and the maxima of the value scales (non-negative)
     const int n_sum = NQ + NQ * ngd;
     for (int k = tid >> 3; k < n_sum + ngd; k += kMChunk / 8) {
+        const float* row = k < NQ ? p_s[k] : k < n_sum ? zrows + (k - NQ) * kMChunk
+                                                       : sv_s[k - n_sum];
+        float4 x[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) x[m] = row4(row, k, m);
         if (k < n_sum) {
-            const float* row = k < NQ ? p_s[k] : zrows + (k - NQ) * kMChunk;
             float v = 0.0f;
-#pragma unroll 4
-            for (int u = 0; u < kMChunk / 8; ++u)
-                v += row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v = ((v + x[m].x) + x[m].y) + (x[m].z + x[m].w);
             v = block_sum<8>(v);
-            if ((tid & 7) == 0) {
+            if (i8 == 0) {
                 if (k < NQ) ml_s[1][k] = v;
                 else zsum_s[k - NQ] = v;
             }
         } else {
-            const float* row = sv_s[k - n_sum];
             float v = 0.0f;
-#pragma unroll 4
-            for (int u = 0; u < kMChunk / 8; ++u)
-                v = fmaxf(v, row[(tid & 7) + 8 * ((u + k) & (kMChunk / 8 - 1))]);
-            v = block8_max(v);
-            if ((tid & 7) == 0) vmax_s[k - n_sum] = v;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                v = fmaxf(fmaxf(v, fmaxf(x[m].x, x[m].y)), fmaxf(x[m].z, x[m].w));
+            v = block_max_nonneg<8>(v);
+            if (i8 == 0) vexp_s[k - n_sum] = op_exp(v);
         }
     }
     __syncthreads();
@@ -604,13 +646,14 @@ void attend_mfma_kernel(AttendArgs a) {
         _Float16* vops = reinterpret_cast<_Float16*>(ops_s);
         const int s4 = tid >> 5, blk = (tid >> 3) & 3, i = tid & 7;
         for (int gv = 0; gv < ngd; ++gv) {
-            const int e = op_exp(vmax_s[gv]);
-            const float sv = sv_s[gv][tid];   // this token's scale
+            // this token's scale times 2^e (exact unless it falls below
+            // fp32's normal range; e keeps it below 2^14)
+            const float sv = __builtin_ldexpf(sv_s[gv][tid], vexp_s[gv]);
             // heads in pairs: one paired conversion per pair for hi and lo
 #pragma unroll
             for (int j = 0; j < NQ; j += 2) {
-                const float w0 = __builtin_ldexpf(pt[j] * sv, e);
-                const float w1 = j + 1 < NQ ? __builtin_ldexpf(pt[j + 1] * sv, e) : 0.0f;
+                const float w0 = pt[j] * sv;
+                const float w1 = j + 1 < NQ ? pt[j + 1] * sv : 0.0f;
                 uint32_t hi, lo;
                 split16x2(w0, w1, hi, lo);
 #pragma unroll
@@ -668,7 +711,7 @@ void attend_mfma_kernel(AttendArgs a) {
             for (int i = 0; i < 4; ++i) ov[i] = add_lo_half(acc[i]);
             // C: lane (head m16, row block kb) holds channels mt*16 + 4 kb + i
             if (m16 < nq) {
-                const int e = op_exp(vmax_s[gv]);
+                const int e = vexp_s[gv];
                 const float zs = zsum_s[m16 * ngd + gv];
                 float* wj = wbase + m16 * (D + 2);
 #pragma unroll
