@@ -31,6 +31,8 @@
 // map to any channel (or token) as long as A and B agree: lane block
 // kb = l / 16 takes channels [kb D/4, (kb + 1) D/4), so a lane's codes of one
 // token are one contiguous load.
+#include <algorithm>
+
 #include "kivi_device.h"
 #include "kivi_launch.h"
 
@@ -63,14 +65,18 @@ struct MfmaShape {
     static constexpr int KGROUPS = kMChunk / GK;      // key groups of a chunk
     static constexpr int MAXGV = D / GK;              // value groups of a row
     static constexpr int VKS = kMChunk / 32;          // k-steps over the tokens
-    static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KS;   // uint4 key operands
-    static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKS;    // uint4 value operands
+    // a B column's k-steps, padded by one uint4 so that the columns a
+    // 16-lane LDS pass reads sit in different banks
+    static constexpr int KSP = KS + 1, VKSP = VKS + 1;
+    static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KSP;  // uint4 key operands
+    static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKSP;   // uint4 value operands
+    static constexpr int kPRow = kMChunk + 4;   // score rows, padded by 16 bytes
     static constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
     // half-items of the key operands (a key group's 4 channels) per thread
     static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
         NQ * D * 4 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
-        NQ * kMChunk * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
+        NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
     // 4-bit codes hold twice the key code registers: at most 4 waves there
@@ -253,7 +259,7 @@ __device__ __forceinline__ float widen_h(uint16_t h) {
 // 2w + 4, 2w + 5 of wave w).
 template <int DT, int BITS, int D, int NQ, int GK>
 __global__ __launch_bounds__(kMChunk, (MfmaShape<BITS, D, NQ, GK>::kWaves))
-void attend_mfma_kernel(AttendArgs a) {
+void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     using Sh = MfmaShape<BITS, D, NQ, GK>;
     constexpr int D8 = Sh::D8, KS = Sh::KS, CPL = Sh::CPL, LB = Sh::LB;
     constexpr int DW = Sh::DW, MT = Sh::MT, MAXGV = Sh::MAXGV, VKS = Sh::VKS;
@@ -265,7 +271,9 @@ void attend_mfma_kernel(AttendArgs a) {
     __shared__ __attribute__((aligned(16))) uint4 ops_s[kOps];
     __shared__ float kbias_s[kMaxKGroups][NQ];
     __shared__ int kexp_s[kMaxKGroups][NQ];
-    __shared__ __attribute__((aligned(16))) float p_s[NQ][kMChunk];
+    // scores, then weights, per head (rows padded: the heads' lanes of a
+    // matrix-core tile write their rows at once)
+    __shared__ __attribute__((aligned(16))) float p_s[NQ][Sh::kPRow];
     // value codes by token pair: row q holds, for each pair of tokens
     // (2P, 2P + 1), the q-th 16 bits of each token's code row, the even
     // token's in the low half (rows padded to 68 dwords, which keeps the
@@ -277,12 +285,12 @@ void attend_mfma_kernel(AttendArgs a) {
     __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
 
-    // Blocks run the chunks from the last one down, every bh of a chunk
-    // before the next chunk: the chunks that hold the ring's exact tokens,
-    // which take longest, start first instead of closing the grid.
-    const int n_bh = (int)(gridDim.x / (uint32_t)a.n_chunks);
-    const int bh = (int)(blockIdx.x % (uint32_t)n_bh);
-    const int chunk = a.n_chunks - 1 - (int)(blockIdx.x / (uint32_t)n_bh);
+    // Blocks run the chunks from the last one down (grid x = bh, y = chunk
+    // counted down from chunk_top), every bh of a chunk before the next
+    // chunk: the chunks that hold the ring's exact tokens, which take
+    // longest, start first instead of closing the grid.
+    const int bh = (int)blockIdx.x;
+    const int chunk = chunk_top - (int)blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int m16 = lane & 15, kb = lane >> 4;
@@ -401,9 +409,9 @@ void attend_mfma_kernel(AttendArgs a) {
             split16x2(__builtin_ldexpf(pr[0], e), __builtin_ldexpf(pr[1], e), h0, l0);
             split16x2(__builtin_ldexpf(pr[2], e), __builtin_ldexpf(pr[3], e), h1, l1);
             uint2* hb = reinterpret_cast<uint2*>(
-                ops_s + (((kg * 4 + blk) * 2 * NQ + j) * KS + s)) + half;
+                ops_s + (((kg * 4 + blk) * 2 * NQ + j) * Sh::KSP + s)) + half;
             uint2* lb = reinterpret_cast<uint2*>(
-                ops_s + (((kg * 4 + blk) * 2 * NQ + NQ + j) * KS + s)) + half;
+                ops_s + (((kg * 4 + blk) * 2 * NQ + NQ + j) * Sh::KSP + s)) + half;
             *hb = make_uint2(h0, h1);
             *lb = make_uint2(l0, l1);
             if (c4 == 0) {
@@ -430,7 +438,7 @@ void attend_mfma_kernel(AttendArgs a) {
             if (tok0 >= nq_tok) continue;          // wave-uniform
             const int g = tok0 >> gk_sh;
             if (g != gcur) {                       // wave-uniform
-                const uint4* bp = ops_s + ((g * 4 + kb) * 2 * NQ + col) * KS;
+                const uint4* bp = ops_s + ((g * 4 + kb) * 2 * NQ + col) * Sh::KSP;
 #pragma unroll
                 for (int s = 0; s < KS; ++s) bk[s] = bp[s];
                 gcur = g;
@@ -659,8 +667,8 @@ void attend_mfma_kernel(AttendArgs a) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     if (j + u < NQ) {
-                        _Float16* vh = vops + (((gv * 4 + blk) * 2 * NQ + j + u) * VKS + s4) * 8;
-                        _Float16* vl = vops + (((gv * 4 + blk) * 2 * NQ + NQ + j + u) * VKS + s4) * 8;
+                        _Float16* vh = vops + (((gv * 4 + blk) * 2 * NQ + j + u) * Sh::VKSP + s4) * 8;
+                        _Float16* vl = vops + (((gv * 4 + blk) * 2 * NQ + NQ + j + u) * Sh::VKSP + s4) * 8;
                         vh[i] = __builtin_bit_cast(_Float16, (uint16_t)(hi >> (16 * u)));
                         vl[i] = __builtin_bit_cast(_Float16, (uint16_t)(lo >> (16 * u)));
                     }
@@ -683,7 +691,7 @@ void attend_mfma_kernel(AttendArgs a) {
             const int mt = (u >> 1) * 4 + 2 * wave + (u & 1);
             const int gv = (mt * 16) >> gv_sh;
             if (gv != gcur) {                      // wave-uniform
-                const uint4* bp = ops_s + ((gv * 4 + kb) * 2 * NQ + col) * VKS;
+                const uint4* bp = ops_s + ((gv * 4 + kb) * 2 * NQ + col) * Sh::VKSP;
 #pragma unroll
                 for (int s4 = 0; s4 < VKS; ++s4) bv[s4] = bp[s4];
                 gcur = gv;
@@ -732,15 +740,20 @@ void attend_mfma_kernel(AttendArgs a) {
 template <int DT, int BITS, int D, int NQ>
 static hipError_t launch_mfma_t(const AttendArgs& a, int64_t BH, int n_full,
                                 hipStream_t stream) {
-    // one block per (chunk, bh), every chunk of the call (see the kernel)
-    if (n_full != a.n_chunks || (int64_t)n_full * BH >= (1ll << 31))
-        return hipErrorInvalidConfiguration;
-    const dim3 grid((uint32_t)(n_full * BH)), block(kMChunk);
-    if (a.G_k == 32 && a.G_v >= 32)
-        return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 32>), grid,
-                             block, 0, stream, a);
-    return launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 16>), grid,
-                         block, 0, stream, a);
+    // one block per (chunk, bh), the chunks from n_full - 1 down, at most
+    // 65535 chunks (the grid's y limit) per launch
+    constexpr int kMaxY = 65535;
+    for (int top = n_full - 1; top >= 0; top -= kMaxY) {
+        const dim3 grid((uint32_t)BH, (uint32_t)std::min(top + 1, kMaxY)), block(kMChunk);
+        const hipError_t e =
+            a.G_k == 32 && a.G_v >= 32
+                ? launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 32>), grid, block, 0,
+                                stream, a, top)
+                : launch_kernel((attend_mfma_kernel<DT, BITS, D, NQ, 16>), grid, block, 0,
+                                stream, a, top);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DT, int BITS, int D>
