@@ -65,18 +65,15 @@ struct MfmaShape {
     static constexpr int KGROUPS = kMChunk / GK;      // key groups of a chunk
     static constexpr int MAXGV = D / GK;              // value groups of a row
     static constexpr int VKS = kMChunk / 32;          // k-steps over the tokens
-    // a B column's k-steps, padded by one uint4 so that the columns a
-    // 16-lane LDS pass reads sit in different banks
-    static constexpr int KSP = KS + 1, VKSP = VKS + 1;
-    static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KSP;  // uint4 key operands
-    static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKSP;   // uint4 value operands
+    static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KS;   // uint4 key operands
+    static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKS;    // uint4 value operands
     static constexpr int kPRow = kMChunk + 4;   // score rows, padded by 16 bytes
     static constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
     // half-items of the key operands (a key group's 4 channels) per thread
     static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
         NQ * D * 4 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
-        NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * kMChunk * 4 +
+        NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * 16 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
     // 4-bit codes hold twice the key code registers: at most 4 waves there
@@ -280,7 +277,8 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     // two writers of a pair off one bank)
     constexpr int kVpStride = kMChunk / 2 + 4;
     __shared__ __attribute__((aligned(16))) uint32_t vp_s[2 * DW][kVpStride];
-    __shared__ __attribute__((aligned(16))) float sv_s[MAXGV][kMChunk];
+    // the largest value scale of each value group, per half wave
+    __shared__ float vmx_s[MAXGV][4];
     __shared__ int vexp_s[MAXGV];          // scaling exponent of each value group
     __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
@@ -409,9 +407,9 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             split16x2(__builtin_ldexpf(pr[0], e), __builtin_ldexpf(pr[1], e), h0, l0);
             split16x2(__builtin_ldexpf(pr[2], e), __builtin_ldexpf(pr[3], e), h1, l1);
             uint2* hb = reinterpret_cast<uint2*>(
-                ops_s + (((kg * 4 + blk) * 2 * NQ + j) * Sh::KSP + s)) + half;
+                ops_s + (((kg * 4 + blk) * 2 * NQ + j) * KS + s)) + half;
             uint2* lb = reinterpret_cast<uint2*>(
-                ops_s + (((kg * 4 + blk) * 2 * NQ + NQ + j) * Sh::KSP + s)) + half;
+                ops_s + (((kg * 4 + blk) * 2 * NQ + NQ + j) * KS + s)) + half;
             *hb = make_uint2(h0, h1);
             *lb = make_uint2(l0, l1);
             if (c4 == 0) {
@@ -438,7 +436,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             if (tok0 >= nq_tok) continue;          // wave-uniform
             const int g = tok0 >> gk_sh;
             if (g != gcur) {                       // wave-uniform
-                const uint4* bp = ops_s + ((g * 4 + kb) * 2 * NQ + col) * Sh::KSP;
+                const uint4* bp = ops_s + ((g * 4 + kb) * 2 * NQ + col) * KS;
 #pragma unroll
                 for (int s = 0; s < KS; ++s) bk[s] = bp[s];
                 gcur = g;
@@ -561,8 +559,12 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
         }
     }
 #pragma unroll
-    for (int gv = 0; gv < MAXGV; ++gv)
-        if (gv < ngd) sv_s[gv][tid] = svv[gv];
+    for (int gv = 0; gv < MAXGV; ++gv) {
+        if (gv < ngd) {                        // block-uniform
+            const float m = block_max_nonneg<32>(svv[gv]);
+            if ((tid & 31) == 0) vmx_s[gv][tid >> 5] = m;
+        }
+    }
     __syncthreads();
     float pt[NQ];                              // this token's p per head
 #pragma unroll
@@ -621,42 +623,38 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
         for (int j = 0; j < NQ; ++j) q_s[j][tid] = o[j];
     }
     // eight lanes per row (read as above): the sums of p (per head) and of
-    // p * zero, and the maxima of the value scales (non-negative)
+    // p * zero; and each value group's scaling exponent from the largest
+    // scale of its four half waves (non-negative)
     const int n_sum = NQ + NQ * ngd;
-    for (int k = tid >> 3; k < n_sum + ngd; k += kMChunk / 8) {
-        const float* row = k < NQ ? p_s[k] : k < n_sum ? zrows + (k - NQ) * kMChunk
-                                                       : sv_s[k - n_sum];
+    for (int k = tid >> 3; k < n_sum; k += kMChunk / 8) {
+        const float* row = k < NQ ? p_s[k] : zrows + (k - NQ) * kMChunk;
         float4 x[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) x[m] = row4(row, k, m);
-        if (k < n_sum) {
-            float v = 0.0f;
+        float v = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) v = ((v + x[m].x) + x[m].y) + (x[m].z + x[m].w);
-            v = block_sum<8>(v);
-            if (i8 == 0) {
-                if (k < NQ) ml_s[1][k] = v;
-                else zsum_s[k - NQ] = v;
-            }
-        } else {
-            float v = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                v = fmaxf(fmaxf(v, fmaxf(x[m].x, x[m].y)), fmaxf(x[m].z, x[m].w));
-            v = block_max_nonneg<8>(v);
-            if (i8 == 0) vexp_s[k - n_sum] = op_exp(v);
+        for (int m = 0; m < 4; ++m) v = ((v + x[m].x) + x[m].y) + (x[m].z + x[m].w);
+        v = block_sum<8>(v);
+        if (i8 == 0) {
+            if (k < NQ) ml_s[1][k] = v;
+            else zsum_s[k - NQ] = v;
         }
     }
+    if (tid < ngd)
+        vexp_s[tid] = op_exp(fmaxf(fmaxf(vmx_s[tid][0], vmx_s[tid][1]),
+                                   fmaxf(vmx_s[tid][2], vmx_s[tid][3])));
     __syncthreads();
     // weights p * vscale * 2^e(gv) of this token, hi + lo, at k index
     // (token) k-step tid / 32, lane block (tid % 32) / 8, element tid % 8
     {
         _Float16* vops = reinterpret_cast<_Float16*>(ops_s);
         const int s4 = tid >> 5, blk = (tid >> 3) & 3, i = tid & 7;
-        for (int gv = 0; gv < ngd; ++gv) {
+#pragma unroll
+        for (int gv = 0; gv < MAXGV; ++gv) {
+            if (gv >= ngd) break;              // block-uniform
             // this token's scale times 2^e (exact unless it falls below
             // fp32's normal range; e keeps it below 2^14)
-            const float sv = __builtin_ldexpf(sv_s[gv][tid], vexp_s[gv]);
+            const float sv = __builtin_ldexpf(svv[gv], vexp_s[gv]);
             // heads in pairs: one paired conversion per pair for hi and lo
 #pragma unroll
             for (int j = 0; j < NQ; j += 2) {
@@ -667,8 +665,8 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     if (j + u < NQ) {
-                        _Float16* vh = vops + (((gv * 4 + blk) * 2 * NQ + j + u) * Sh::VKSP + s4) * 8;
-                        _Float16* vl = vops + (((gv * 4 + blk) * 2 * NQ + NQ + j + u) * Sh::VKSP + s4) * 8;
+                        _Float16* vh = vops + (((gv * 4 + blk) * 2 * NQ + j + u) * VKS + s4) * 8;
+                        _Float16* vl = vops + (((gv * 4 + blk) * 2 * NQ + NQ + j + u) * VKS + s4) * 8;
                         vh[i] = __builtin_bit_cast(_Float16, (uint16_t)(hi >> (16 * u)));
                         vl[i] = __builtin_bit_cast(_Float16, (uint16_t)(lo >> (16 * u)));
                     }
@@ -691,7 +689,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             const int mt = (u >> 1) * 4 + 2 * wave + (u & 1);
             const int gv = (mt * 16) >> gv_sh;
             if (gv != gcur) {                      // wave-uniform
-                const uint4* bp = ops_s + ((gv * 4 + kb) * 2 * NQ + col) * Sh::VKSP;
+                const uint4* bp = ops_s + ((gv * 4 + kb) * 2 * NQ + col) * VKS;
 #pragma unroll
                 for (int s4 = 0; s4 < VKS; ++s4) bv[s4] = bp[s4];
                 gcur = gv;
