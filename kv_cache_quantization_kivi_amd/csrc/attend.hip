@@ -339,8 +339,16 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
 
 // Merge the chunks of each (bh, query head): out = sum_c e^{m_c - M} o_c /
 // sum_c e^{m_c - M} l_c with M = max_c m_c.  One wave per (bh, head), four
-// per block: the lanes take the chunks for M and the denominator (wave
-// reductions, no barrier), then the channels for the numerator.
+// per block, over batches of 16 chunks: every load of a batch is issued at
+// once (lane c takes chunk c's m and l, every lane its channels of each
+// chunk's o); the batch's maximum and denominator are reduced over the
+// first 16 lanes (one DPP row) and read back as wave-uniform values, and
+// the running sums are rescaled when the maximum grows (online softmax).
+template <int CTRL>
+__device__ __forceinline__ float merge_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
                                                            int32_t n_pairs) {
@@ -351,24 +359,52 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
     const int bh = pair / nq, j = pair - bh * nq;
     const int64_t cs = (int64_t)nq * att_slot(D);        // chunk stride
     const float* w = a.work + (int64_t)bh * nc * cs + (int64_t)j * att_slot(D);
-    float mx = -__builtin_huge_valf();
-    for (int c = lane; c < nc; c += 64) mx = fmaxf(mx, w[c * cs]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    float ls = 0.0f;
-    for (int c = lane; c < nc; c += 64) ls += __expf(w[c * cs] - mx) * w[c * cs + 1];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o);
     constexpr int PER = D / 64;                  // channels per lane
+    constexpr int B = 16;                        // chunks per batch
+    float mx = -__builtin_huge_valf(), ls = 0.0f;
     float O[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) O[i] = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < nc; ++c) {
-        const float e = __expf(w[c * cs] - mx);
+    for (int c0 = 0; c0 < nc; c0 += B) {         // wave-uniform
+        const int nb = min(B, nc - c0);
+        float2 ml = make_float2(-__builtin_huge_valf(), 0.0f);
+        if (lane < nb) ml = *reinterpret_cast<const float2*>(w + (c0 + lane) * cs);
+        float ov[B][PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-            O[i] = __builtin_fmaf(e, w[c * cs + 2 + lane + 64 * i], O[i]);
+        for (int c = 0; c < B; ++c)
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                ov[c][i] = c < nb ? w[(c0 + c) * cs + 2 + lane + 64 * i] : 0.0f;
+        // the batch maximum over lanes 0..15: quad_perm [1,0,3,2],
+        // quad_perm [2,3,0,1], row_half_mirror, row_mirror
+        float bm = ml.x;
+        bm = fmaxf(bm, merge_dpp<0xB1>(bm));
+        bm = fmaxf(bm, merge_dpp<0x4E>(bm));
+        bm = fmaxf(bm, merge_dpp<0x141>(bm));
+        bm = fmaxf(bm, merge_dpp<0x140>(bm));
+        // lane 0 (the first active lane: the whole wave runs) holds row 0's result
+        const float mnew =
+            fmaxf(mx, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bm))));
+        const float scale = __expf(mx - mnew);   // 0 on the first batch
+        const float e = lane < nb ? __expf(ml.x - mnew) : 0.0f;
+        float el = e * ml.y;
+        el += merge_dpp<0xB1>(el);
+        el += merge_dpp<0x4E>(el);
+        el += merge_dpp<0x141>(el);
+        el += merge_dpp<0x140>(el);
+        ls = ls * scale + __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(el)));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) O[i] *= scale;
+#pragma unroll
+        for (int c = 0; c < B; ++c) {
+            if (c < nb) {                        // wave-uniform
+                const float ec = __int_as_float(
+                    __builtin_amdgcn_readlane(__float_as_int(e), c));
+#pragma unroll
+                for (int i = 0; i < PER; ++i) O[i] = __builtin_fmaf(ec, ov[c][i], O[i]);
+            }
+        }
+        mx = mnew;
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
