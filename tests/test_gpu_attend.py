@@ -87,6 +87,49 @@ def test_attend_many_blocks(K, O, case):
     _run_case(K, O, case)
 
 
+@pytest.mark.parametrize("dtype", [FP16, 1], ids=["fp16", "bf16"])
+def test_attend_exact_tokens_with_subnormal_keys(K, O, dtype):
+    """A cache of exact tokens only (T < R): their keys are 16-bit subnormals
+    (different per token) in one channel and zero elsewhere, the query is
+    large in that channel, so every score, and the softmax over them, rests
+    on the subnormal keys entering the matrix-core products unflushed."""
+    BH, D, R, G, n_q, T = 2, 128, 32, 32, 2, 20
+    case = (BH, D, R, G, G, 2, dtype, n_q, [T])
+    S_max = T + 8
+    k = np.zeros((BH, S_max, D), np.uint16)
+    t = np.arange(S_max)
+    # fp16 subnormal m: m 2^-24; bf16 subnormal m (7 bits): m 2^-133
+    k[:, :, 5] = (t + 1) if dtype == FP16 else (t + 1) * 4
+    k[1, :, 5] |= 0x8000                                   # negative in bh 1
+    r = np.random.default_rng(7)
+    vf = r.standard_normal((BH, S_max, D)).astype(np.float32)
+    if dtype == FP16:
+        v = vf.astype(np.float16).view(np.uint16)
+    else:
+        v = (torch.from_numpy(vf).to(torch.bfloat16).view(torch.int16)
+             .numpy().view(np.uint16))
+    q = np.zeros((BH, n_q, D), np.uint16)
+    q[:, 0, 5] = 0x7800 if dtype == FP16 else 0x7E80       # 2^15, 2^126
+    q[:, 1, 5] = 0x7400 if dtype == FP16 else 0x7E00       # 2^14, 2^125
+    sm = 64.0 if dtype == FP16 else 16.0
+    tdt = torch.float16 if dtype == FP16 else torch.bfloat16
+    c = K.KiviCache(BH, D, S_max, R, G, G, 2, tdt)
+    c.append(_dev(k[:, :T], dtype), _dev(v[:, :T], dtype))
+    oc = oracle_cache(O, case, k, v, S_max)
+    assert (c.T, c.Q) == (oc.T, oc.Q) == (T, 0)
+    out = c.attend(_dev(q, dtype), sm)
+    torch.cuda.synchronize()
+    got = O.widen(host(out.view(torch.int16)).view(np.uint16),
+                  dtype).astype(np.float64)
+    bound, ref = attend_bound(O, oc, q, sm)
+    # the scores span a range wide enough that flushed keys (all scores 0,
+    # uniform weights) would leave the bound
+    uniform = O.widen(np.ascontiguousarray(v[:, :T]), dtype).astype(np.float64).mean(axis=1)
+    assert (np.abs(uniform[:, None, :] - ref) > bound).any()
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float((err / bound).max())
+
+
 def test_attend_rejects(K):
     c = K.KiviCache(2, 256, 64, 8, 8, 8, 2, torch.float16)  # D = 256
     x = torch.zeros((2, 4, 256), dtype=torch.float16, device="cuda")
