@@ -444,8 +444,9 @@ template <int DT, int BITS>
 static hipError_t launch_attend_t(const AttendArgs& a0, int64_t BH,
                                   hipStream_t stream) {
     // Every chunk goes to the matrix-core kernel when its shape rules hold
-    // (it takes the ring's exact tokens on the vector units); otherwise all
-    // go to the token-per-thread kernel.
+    // (it takes the ring's exact tokens too: their scores on the matrix
+    // cores, their values on the vector units); otherwise all go to the
+    // token-per-thread kernel.
     AttendArgs a = a0;
     a.chunk0 = 0;
     const bool mfma = BITS <= 4 && (a.G_k == 16 || a.G_k == 32) && a.G_v >= 16;
