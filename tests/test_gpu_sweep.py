@@ -7,6 +7,8 @@
 - K+V calls: each equals the two single calls on its tensors.
 - Residual-window cache: random append sequences; after every append the
   store and the ring must equal the oracle scheduler's.
+- Decode attention over random caches: within the derived bound of the
+  oracle's exact attention (tests/attend_bound.py).
 
 The cases come from a fixed seed; the test ids name each case's
 parameters."""
@@ -197,3 +199,55 @@ def test_cache_sweep(K, O, case):
         torch.cuda.synchronize()
         cache_compare(c, o, f"cache sweep append {i} (n={n}, T={t + n})")
         t += n
+
+
+def attend_cases(n=40, seed=11):
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        BH = int(r.integers(1, 7))
+        D = int(r.choice([64, 128]))
+        R = int(r.choice([0, 3, 8, 32, 40]))
+        gk = int(r.choice([8, 16, 32]))
+        gv = int(r.choice([8, 16, 32, 64, D]))
+        bits = int(r.choice([1, 2, 4, 8]))
+        if D * bits < 128:                 # kivi_cache_attend's rule
+            bits = 2 if D == 64 else bits
+        dtype = int(r.integers(0, 2))
+        n_q = int(r.integers(1, 9))
+        sizes = tuple(int(s) for s in r.choice([1, 1, 2, 9, 31, 64, 127, 128, 129, 300],
+                                               size=int(r.integers(1, 6))))
+        cases.append((BH, D, R, gk, gv, bits, dtype, n_q, sizes))
+    return cases
+
+
+@pytest.mark.parametrize("case", attend_cases(),
+                         ids=lambda c: case_id(c[:8]) + "_" + "-".join(map(str, c[8])))
+def test_attend_sweep(K, O, case):
+    """kivi_cache_attend on random caches (both chunk kernels: G_k = 8 and
+    8-bit codes take the token-per-thread one) within the derived bound of
+    the oracle's exact attention."""
+    from attend_bound import attend_bound, oracle_cache
+    BH, D, R, gk, gv, bits, dtype, n_q, sizes = case
+    S_max = sum(sizes) + 8
+    seed = _seed(case)
+    k = values(seed, BH, S_max, D, dtype, "outliers")
+    v = values(seed + 1, BH, S_max, D, dtype, "normal")
+    q = values(seed + 2, BH, n_q, D, dtype, "normal")   # 16-bit patterns
+    tdt = torch.float16 if dtype == FP16 else torch.bfloat16
+    c = K.KiviCache(BH, D, S_max, R, gk, gv, bits, tdt)
+    t = 0
+    for n in sizes:
+        c.append(to_dev(np.ascontiguousarray(k[:, t:t + n]), dtype),
+                 to_dev(np.ascontiguousarray(v[:, t:t + n]), dtype))
+        t += n
+    oc = oracle_cache(O, (BH, D, R, gk, gv, bits, dtype, n_q, list(sizes)), k, v, S_max)
+    assert (c.T, c.Q) == (oc.T, oc.Q)
+    sm = float(np.float32(1.0 / np.sqrt(D)))
+    say(f"[attend sweep {case_id(case[:8])} T={c.T} Q={c.Q}]")
+    out = c.attend(to_dev(q, dtype), sm)
+    torch.cuda.synchronize()
+    got = O.widen(host(out.view(torch.int16)).view(np.uint16), dtype).astype(np.float64)
+    bound, ref = attend_bound(O, oc, q, sm)
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float((err / bound).max())
