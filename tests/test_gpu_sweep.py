@@ -9,6 +9,8 @@
   store and the ring must equal the oracle scheduler's.
 - Decode attention over random caches: within the derived bound of the
   oracle's exact attention (tests/attend_bound.py).
+- KIVI-Sink and per-token mixed precision on random prompts: scores, lists,
+  codes, params and reconstructions bit for bit.
 
 The cases come from a fixed seed; the test ids name each case's
 parameters."""
@@ -251,3 +253,107 @@ def test_attend_sweep(K, O, case):
     bound, ref = attend_bound(O, oc, q, sm)
     err = np.abs(got - ref)
     assert (err <= bound).all(), float((err / bound).max())
+
+
+def sink_cases(n=24, seed=13):
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(r.integers(1, 4))
+        H = int(r.integers(1, 5))
+        S = int(r.choice([1, 5, 31, 64, 100, 257, 600]))
+        D = int(r.choice([8, 16, 64, 128, 256]))   # a power of two (the selection's rule)
+        n_sink = int(min(S, r.choice([0, 1, 3, 5, 16, 64])))
+        bits = int(r.choice([1, 2, 4, 8]))
+        G = int(r.choice([1, 3, 8, 16, 31, 32]))
+        dtype = int(r.integers(0, 2))
+        dist = DISTS[int(r.integers(0, len(DISTS)))]
+        cases.append((B, H, S, D, n_sink, bits, G, dtype, dist))
+    return cases
+
+
+@pytest.mark.parametrize("case", sink_cases(), ids=case_id)
+def test_sink_sweep(K, O, case):
+    """KIVI-Sink on random prompts: scores, lists, the sink-masked key
+    quantization (codes, params, reconstruction) and the gathered rows, bit
+    for bit against the oracle."""
+    from gpu_util import (assert_codes_equal, assert_f32_bits_equal,
+                          assert_recon_equal, bits16)
+    B, H, S, D, n_sink, bits, G, dtype, dist = case
+    x = values(_seed(case), B * H, S, D, dtype, dist)
+    xd = to_dev(x, dtype)
+    say(f"[sink sweep {case_id(case)}]")
+    idx_d, score_d = K.kivi_sink_select(xd, n_sink, H=H)
+    recon, codes, scale, zero = K.kivi_quant_keys_sink(xd, idx_d, bits, G, H=H,
+                                                       with_recon=True)
+    kept = K.kivi_sink_gather(xd, idx_d, H=H)
+    torch.cuda.synchronize()
+    want_s = O.sink_scores(x, dtype, H)
+    assert np.array_equal(host(score_d).view(np.uint32), want_s.view(np.uint32)), "scores"
+    idx = host(idx_d)
+    assert np.array_equal(idx, O.sink_select(want_s, n_sink)), "sink lists"
+    wc, ws, wz = O.quant_keys_sink(x, dtype, H, bits, G, idx)
+    assert_codes_equal(host(codes), wc, "codes")
+    assert_f32_bits_equal(host(scale), ws, "scale")
+    assert_f32_bits_equal(host(zero), wz, "zero")
+    assert_recon_equal(bits16(recon), O.sink_recon(x, dtype, H, bits, G, idx), "recon")
+    assert np.array_equal(bits16(kept), O.sink_gather(x, H, idx)), "gathered rows"
+
+
+def mixed_cases(n=24, seed=17):
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(r.integers(1, 4))
+        H = int(r.integers(1, 4))
+        S = int(r.choice([1, 7, 40, 128, 300, 1000]))
+        D = int(r.choice([8, 32, 64, 128, 256]))
+        n_hi = int(r.integers(0, S + 1))
+        hi_bits, lo_bits = [int(b) for b in r.choice([[4, 2], [8, 4], [2, 1], [4, 1]])]
+        Gk = int(r.choice([1, 5, 8, 16, 32]))
+        Gv = int(r.choice([8, 16, 32, 64, D]))
+        dtype = int(r.integers(0, 2))
+        dist = DISTS[int(r.integers(0, len(DISTS)))]
+        cases.append((B, H, S, D, n_hi, hi_bits, lo_bits, Gk, Gv, dtype, dist))
+    return cases
+
+
+@pytest.mark.parametrize("case", mixed_cases(), ids=case_id)
+def test_mixed_sweep(K, O, case):
+    """Per-token mixed precision on random prompts: the key-norm partition
+    and both sets' listed-row quantization and dequantization, bit for bit
+    against the oracle."""
+    from gpu_util import (TORCH_DT, assert_codes_equal, assert_f32_bits_equal,
+                          assert_recon_equal, bits16, to_dev_raw)
+    B, H, S, D, n_hi, hb, lb, Gk, Gv, dtype, dist = case
+    seed = _seed(case)
+    k = values(seed, B * H, S, D, dtype, dist)
+    v = values(seed + 1, B * H, S, D, dtype, "normal")
+    kd, vd = to_dev(k, dtype), to_dev(v, dtype)
+    say(f"[mixed sweep {case_id(case)}]")
+    score = K.kivi_key_scores(kd, H=H)
+    hi, lo = K.kivi_partition_top(score, n_hi)
+    torch.cuda.synchronize()
+    want_s = O.sink_scores(k, dtype, H)
+    ehi, elo = O.partition_top(want_s, n_hi)
+    assert np.array_equal(host(hi), ehi) and np.array_equal(host(lo), elo), "partition"
+    for pos, bits in ((ehi, hb), (elo, lb)):
+        if pos.shape[1] == 0:
+            continue
+        pd = to_dev_raw(np.ascontiguousarray(pos))
+        for keys, x, xd, G in ((True, k, kd, Gk), (False, v, vd, Gv)):
+            q = K.kivi_quant_keys_rows if keys else K.kivi_quant_values_rows
+            dq = K.kivi_dequant_keys_rows if keys else K.kivi_dequant_values_rows
+            codes, scale, zero = q(xd, pd, bits, G, H=H)
+            out = torch.zeros((B * H, S, D), dtype=TORCH_DT[dtype], device="cuda")
+            dq(codes, scale, zero, pd, out, bits, G, H=H)
+            torch.cuda.synchronize()
+            oq = O.quant_keys_rows if keys else O.quant_values_rows
+            odq = O.dequant_keys_rows if keys else O.dequant_values_rows
+            wc, ws, wz = oq(x, dtype, H, bits, G, pos)
+            tag = f"bits={bits} keys={keys}"
+            assert_codes_equal(host(codes), wc, "codes " + tag)
+            assert_f32_bits_equal(host(scale), ws, "scale " + tag)
+            assert_f32_bits_equal(host(zero), wz, "zero " + tag)
+            assert_recon_equal(bits16(out), odq(wc, ws, wz, x.shape, H, bits, G, pos, dtype),
+                               "recon " + tag)
