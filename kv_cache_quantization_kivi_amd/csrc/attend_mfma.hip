@@ -72,7 +72,7 @@ struct MfmaShape {
     // half-items of the key operands (a key group's 4 channels) per thread
     static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
-        NQ * D * 4 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
+        NQ * D * 2 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
         NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * 16 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
@@ -264,7 +264,8 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     constexpr int kOps = Sh::kOps, KH = Sh::KH;
     static_assert(NQ * MAXGV * kMChunk <= kOps * 4, "zero-point rows fit");
 
-    __shared__ __attribute__((aligned(16))) float q_s[NQ][D];
+    // the query, 16-bit patterns of the cache's type
+    __shared__ __attribute__((aligned(16))) uint16_t q_s[NQ][D];
     __shared__ __attribute__((aligned(16))) uint4 ops_s[kOps];
     __shared__ float kbias_s[kMaxKGroups][NQ];
     __shared__ int kexp_s[kMaxKGroups][NQ];
@@ -304,10 +305,10 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     const int gv_sh = 31 - __builtin_clz((unsigned)a.G_v);   // G_v a power of two
 
     // ---- every load that depends on nothing, issued up front ----
-    float qv[NQ];                              // query element d = tid
+    uint16_t qv[NQ];                           // query element d = tid
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
-        qv[j] = (tid < D && j < nq) ? widen_h<DT>(a.q[((int64_t)bh * nq + j) * D + tid]) : 0.0f;
+        qv[j] = (tid < D && j < nq) ? a.q[((int64_t)bh * nq + j) * D + tid] : (uint16_t)0;
     // key params of this thread's half-items: half-item h = tid + 128 r is
     // 4 channels (c4) of key group h / (2 D8), the group's half-items in
     // consecutive lanes
@@ -395,7 +396,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             float pr[4], b = 0.0f, mxl = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float qd = q_s[j][d + i];
+                const float qd = widen_h<DT>(q_s[j][d + i]);
                 pr[i] = qd * ksc[r][i];
                 mxl = fmaxf(mxl, fabsf(pr[i]));
                 b = __builtin_fmaf(qd, kzr[r][i], b);
@@ -487,13 +488,8 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     const int d0 = kb * CPL + s * 8;
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
-                    if (m16 < NQ) {   // exact: the query is of the cache's type
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            w[i] = narrow2<DT>(q_s[m16][d0 + 2 * i], q_s[m16][d0 + 2 * i + 1]);
-                    }
-                    bq[s] = make_uint4(w[0], w[1], w[2], w[3]);
+                    bq[s] = m16 < NQ ? *reinterpret_cast<const uint4*>(&q_s[m16][d0])
+                                     : make_uint4(0u, 0u, 0u, 0u);
                 }
                 have_q = true;
             }
@@ -583,15 +579,16 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     for (int j = 0; j < NQ; ++j) p_s[j][tid] = pt[j];
     __syncthreads();
     // the ring's exact values: thread = channel, summed over the ring tokens
-    // into the (now free) query rows.  The chunk's ring tokens are fewer
+    // in registers (they go to the score rows once the reductions below have
+    // read those).  The chunk's ring tokens are fewer
     // than the ring's slots (T - Q < R + G_k <= ring), so their slots follow
     // the first one with at most one wrap.  Sixteen tokens' loads are in
     // flight at a time, the next sixteen issued before this batch's sums.
     const bool has_ring = nq_tok < nt;        // block-uniform
-    if (has_ring && tid < D) {
-        float o[NQ];
+    float o[NQ];
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
+    for (int j = 0; j < NQ; ++j) o[j] = 0.0f;
+    if (has_ring && tid < D) {
         const uint16_t* vcol = a.v_ring + (int64_t)bh * a.ring * D + tid;
         const int slot0 = (t0 + nq_tok) % a.ring;
         const int n_ring = nt - nq_tok;
@@ -619,8 +616,6 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) v[u] = vn[u];
         }
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) q_s[j][tid] = o[j];
     }
     // eight lanes per row (read as above): the sums of p (per head) and of
     // p * zero; and each value group's scaling exponent from the largest
@@ -644,6 +639,12 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
         vexp_s[tid] = op_exp(fmaxf(fmaxf(vmx_s[tid][0], vmx_s[tid][1]),
                                    fmaxf(vmx_s[tid][2], vmx_s[tid][3])));
     __syncthreads();
+    // the ring values' sums into the score rows (free now, and read only
+    // after the barrier below)
+    if (has_ring && tid < D) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) p_s[j][tid] = o[j];
+    }
     // weights p * vscale * 2^e(gv) of this token, hi + lo, at k index
     // (token) k-step tid / 32, lane block (tid % 32) / 8, element tid % 8
     {
@@ -724,7 +725,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
                 for (int i = 0; i < 4; ++i) {
                     const int c = mt * 16 + kb * 4 + i;
                     wj[2 + c] = __builtin_ldexpf(ov[i], kCodeExp - e) + zs +
-                                (has_ring ? q_s[m16][c] : 0.0f);
+                                (has_ring ? p_s[m16][c] : 0.0f);
                 }
             }
         }
