@@ -72,7 +72,7 @@ struct MfmaShape {
     // half-items of the key operands (a key group's 4 channels) per thread
     static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
-        NQ * D * 2 + kOps * 16 + 2 * KGROUPS * NQ * 4 +
+        NQ * D * 2 + kOps * 16 + 2 * KGROUPS * NQ * 4 + NQ * 8 * 4 +
         NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * 16 +
         MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
@@ -207,12 +207,6 @@ __device__ __forceinline__ float block_max_nonneg(float x) {
     if constexpr (N > 16) v = max(v, xor16_u(v));
     return __uint_as_float(v);
 }
-// Maximum over aligned blocks of 8 lanes.
-__device__ __forceinline__ float block8_max(float v) {
-    v = fmaxf(v, dpp_f<0xB1>(v));
-    v = fmaxf(v, dpp_f<0x4E>(v));
-    return fmaxf(v, dpp_f<0x141>(v));
-}
 
 // x plus the value of the lane 8 up in its row of 16 (lane l + 8 for
 // l % 16 < 8): a head's hi-part sum and its lo-part sum.
@@ -283,6 +277,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     __shared__ int vexp_s[MAXGV];          // scaling exponent of each value group
     __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
+    __shared__ __attribute__((aligned(16))) float mxp_s[NQ][8];   // per wave and lane block
 
     // Blocks run the chunks from the last one down (grid x = bh, y = chunk
     // counted down from chunk_top), every bh of a chunk before the next
@@ -427,6 +422,9 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     // (Q is a multiple of 16, so a tile is all quantized or all exact) take
     // the keys themselves as A and the 16-bit query as B, both exact in the
     // cache's type: their scores need no split, no scaling and no bias.
+    // Scores go to LDS already times sm_scale; each lane keeps the largest
+    // of its valid ones, one partial max per head, wave and lane block.
+    float lmx = -__builtin_huge_valf();
     {
         const int col = b_col<NQ>(m16);
         int gcur = -1;
@@ -471,8 +469,11 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
                 const int e = kexp_s[g][m16];
                 const float bias = kbias_s[g][m16];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    p_s[m16][tok0 + kb * 4 + i] = __builtin_ldexpf(sc[i], kCodeExp - e) + bias;
+                for (int i = 0; i < 4; ++i) {
+                    const float x = (__builtin_ldexpf(sc[i], kCodeExp - e) + bias) * a.sm_scale;
+                    p_s[m16][tok0 + kb * 4 + i] = x;
+                    lmx = fmaxf(lmx, x);
+                }
             }
         }
     }
@@ -503,14 +504,20 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
                 acc = mfma16<DT>(*reinterpret_cast<const uint4*>(krow + s * 8), bq[s], acc);
             if (m16 < NQ) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) p_s[m16][tok0 + kb * 4 + i] = acc[i];
+                for (int i = 0; i < 4; ++i) {
+                    const float x = acc[i] * a.sm_scale;
+                    p_s[m16][tok0 + kb * 4 + i] = x;
+                    if (tok0 + kb * 4 + i < nt) lmx = fmaxf(lmx, x);
+                }
             }
         }
     }
+    if (m16 < NQ) mxp_s[m16][wave * 4 + kb] = lmx;
     __syncthreads();
 
-    // ---- softmax partial of the chunk: eight lanes per head find the max,
-    // then every thread takes its token's p, then eight lanes per row sum.
+    // ---- softmax partial of the chunk: a thread per head takes the max of
+    // the eight partial maxima, then every thread takes its token's p, then
+    // eight lanes per row sum.
     // Eight lanes read a 128-token row as four 16-byte pieces each: lane i
     // takes tokens 4i .. 4i + 3 of each block of 32, the blocks in an order
     // rotated by one on odd rows, so that the two rows of a 16-lane LDS pass
@@ -520,20 +527,11 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
         return *reinterpret_cast<const float4*>(
             row + ((4 * i8 + 32 * (m + (k & 1))) & (kMChunk - 1)));
     };
-    if (tid < 8 * NQ) {
-        const int j = tid >> 3;
-        float v = -__builtin_huge_valf();
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float4 x = row4(p_s[j], j, m);
-            const int t = (4 * i8 + 32 * (m + (j & 1))) & (kMChunk - 1);
-            const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (nt == kMChunk || t + e < nt) v = fmaxf(v, xs[e] * a.sm_scale);
-        }
-        v = block8_max(v);
-        if (i8 == 0) ml_s[0][j] = v;
+    if (tid < NQ) {
+        const float4 x = *reinterpret_cast<const float4*>(&mxp_s[tid][0]);
+        const float4 y = *reinterpret_cast<const float4*>(&mxp_s[tid][4]);
+        ml_s[0][tid] = fmaxf(fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)),
+                             fmaxf(fmaxf(y.x, y.y), fmaxf(y.z, y.w)));
     }
     // value codes (by token pair) and value scales of this thread's token
     // into LDS
@@ -565,7 +563,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     float pt[NQ];                              // this token's p per head
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
-        pt[j] = tid < nt ? __expf(p_s[j][tid] * a.sm_scale - ml_s[0][j]) : 0.0f;
+        pt[j] = tid < nt ? __expf(p_s[j][tid] - ml_s[0][j]) : 0.0f;
     // zero-point products into the (now free) operand region, [j*ngd+gv][t]
     float* zrows = reinterpret_cast<float*>(ops_s);
 #pragma unroll
