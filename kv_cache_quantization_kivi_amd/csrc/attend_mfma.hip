@@ -68,13 +68,15 @@ struct MfmaShape {
     static constexpr int kKOps = KGROUPS * 4 * 2 * NQ * KS;   // uint4 key operands
     static constexpr int kVOps = MAXGV * 4 * 2 * NQ * VKS;    // uint4 value operands
     static constexpr int kPRow = kMChunk + 4;   // score rows, padded by 16 bytes
+    static constexpr int kVpStride = kMChunk / 2 + 4;   // value code rows, padded
+    static constexpr int kEarly = NQ * D * 2 + 2 * KGROUPS * NQ * 4;
+    static constexpr int kVp = 2 * DW * kVpStride * 4;
     static constexpr int kOps = kKOps > kVOps ? kKOps : kVOps;
     // half-items of the key operands (a key group's 4 channels) per thread
     static constexpr int KH = (KGROUPS * D8 * 2 + kMChunk - 1) / kMChunk;
     static constexpr int kLds =
-        NQ * D * 2 + kOps * 16 + 2 * KGROUPS * NQ * 4 + NQ * 8 * 4 +
-        NQ * kPRow * 4 + DW * kMChunk * 4 + MAXGV * 16 +
-        MAXGV * 4 + NQ * MAXGV * 4 + 2 * NQ * 4 + 256;       // + alignment
+        (kEarly > kVp ? kEarly : kVp) + kOps * 16 + NQ * kPRow * 4 +
+        MAXGV * 16 + MAXGV * 4 + NQ * 8 * 4 + 2 * NQ * 4 + 256;   // + alignment
     static constexpr int kBlocks = (160 * 1024) / kLds;
     // 4-bit codes hold twice the key code registers: at most 4 waves there
     static constexpr int kCap = BITS == 4 ? 4 : 5;
@@ -259,10 +261,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     static_assert(NQ * MAXGV * kMChunk <= kOps * 4, "zero-point rows fit");
 
     // the query, 16-bit patterns of the cache's type
-    __shared__ __attribute__((aligned(16))) uint16_t q_s[NQ][D];
     __shared__ __attribute__((aligned(16))) uint4 ops_s[kOps];
-    __shared__ float kbias_s[kMaxKGroups][NQ];
-    __shared__ int kexp_s[kMaxKGroups][NQ];
     // scores, then weights, per head (rows padded: the heads' lanes of a
     // matrix-core tile write their rows at once)
     __shared__ __attribute__((aligned(16))) float p_s[NQ][Sh::kPRow];
@@ -270,14 +269,36 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     // (2P, 2P + 1), the q-th 16 bits of each token's code row, the even
     // token's in the low half (rows padded to 68 dwords, which keeps the
     // two writers of a pair off one bank)
-    constexpr int kVpStride = kMChunk / 2 + 4;
-    __shared__ __attribute__((aligned(16))) uint32_t vp_s[2 * DW][kVpStride];
+    constexpr int kVpStride = Sh::kVpStride;
+    // The query (16-bit patterns of the cache's type) and each key group's
+    // bias and scaling exponent are last read by the scores; the value codes
+    // are first written after them.  One region holds both.
+    union EarlyLate {
+        struct {
+            uint16_t q[NQ][D];
+            float kbias[kMaxKGroups][NQ];
+            int kexp[kMaxKGroups][NQ];
+        } early;
+        uint32_t vp[2 * DW][kVpStride];
+    };
+    __shared__ __attribute__((aligned(16))) EarlyLate el_s;
+    auto& q_s = el_s.early.q;
+    auto& kbias_s = el_s.early.kbias;
+    auto& kexp_s = el_s.early.kexp;
+    auto& vp_s = el_s.vp;
     // the largest value scale of each value group, per half wave
     __shared__ float vmx_s[MAXGV][4];
     __shared__ int vexp_s[MAXGV];          // scaling exponent of each value group
-    __shared__ float zsum_s[NQ * MAXGV];
     __shared__ float ml_s[2][NQ];
-    __shared__ __attribute__((aligned(16))) float mxp_s[NQ][8];   // per wave and lane block
+    // the partial score maxima (per wave and lane block) are read before
+    // the sums of p * zero per value group are written
+    union MaxZero {
+        float mxp[NQ][8];
+        float zsum[NQ * MAXGV];
+    };
+    __shared__ __attribute__((aligned(16))) MaxZero mz_s;
+    auto& mxp_s = mz_s.mxp;
+    auto& zsum_s = mz_s.zsum;
 
     // Blocks run the chunks from the last one down (grid x = bh, y = chunk
     // counted down from chunk_top), every bh of a chunk before the next
