@@ -67,8 +67,6 @@ __device__ __forceinline__ float widen16(uint16_t h) {
         return __uint_as_float((uint32_t)h << 16);
 }
 
-// Workspace per (bh, chunk, query head): m, l, then D partial outputs.
-__host__ __device__ inline int64_t att_slot(int64_t D) { return D + 2; }
 
 // The 8 codes (8 * BITS bits) of channel chunk c8 from a token's code row
 // held as 32-bit words.
@@ -333,7 +331,7 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
             wj[1] = l[j];
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wj[2 + c8 * 8 + e] = o[j][e] + acc_s[j][c8 * 8 + e];
+        for (int e = 0; e < 8; ++e) wj[kAttData + c8 * 8 + e] = o[j][e] + acc_s[j][c8 * 8 + e];
     }
 }
 
@@ -374,7 +372,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
         for (int c = 0; c < B; ++c)
 #pragma unroll
             for (int i = 0; i < PER; ++i)
-                ov[c][i] = c < nb ? w[(c0 + c) * cs + 2 + lane + 64 * i] : 0.0f;
+                ov[c][i] = c < nb ? w[(c0 + c) * cs + kAttData + lane + 64 * i] : 0.0f;
         // the batch maximum over lanes 0..15: quad_perm [1,0,3,2],
         // quad_perm [2,3,0,1], row_half_mirror, row_mirror
         float bm = ml.x;

@@ -320,7 +320,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     const int ngd = a.NGD;                     // value groups per token
     const int gv_sh = 31 - __builtin_clz((unsigned)a.G_v);   // G_v a power of two
 
-    // ---- every load that depends on nothing, issued up front ----
+    // ---- the loads the key side needs, issued up front ----
     uint16_t qv[NQ];                           // query element d = tid
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
@@ -364,32 +364,6 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             kw[tt][0] = *reinterpret_cast<const uint16_t*>(crow);
         }
     }
-    // this thread's token: value code row and value params
-    const int64_t vrow = (int64_t)bh * a.S_max + t0 + tid;
-    uint32_t vw[DW];
-#pragma unroll
-    for (int k = 0; k < DW; ++k) vw[k] = 0u;
-    const bool vq = tid < nq_tok;              // this token is quantized
-    if (vq) {
-        const uint8_t* vp = a.v_codes + vrow * (D * BITS / 8);
-        if constexpr (DW >= 4) {
-#pragma unroll
-            for (int k = 0; k < DW / 4; ++k) {
-                const uint4 v = *reinterpret_cast<const uint4*>(vp + 16 * k);
-                vw[4 * k] = v.x; vw[4 * k + 1] = v.y; vw[4 * k + 2] = v.z; vw[4 * k + 3] = v.w;
-            }
-        } else {
-            const uint2 v = *reinterpret_cast<const uint2*>(vp);
-            vw[0] = v.x; vw[1] = v.y;
-        }
-    }
-    float svv[MAXGV], zvv[MAXGV];
-#pragma unroll
-    for (int gv = 0; gv < MAXGV; ++gv) {
-        svv[gv] = (vq && gv < ngd) ? a.v_scale[vrow * ngd + gv] : 0.0f;
-        zvv[gv] = (vq && gv < ngd) ? a.v_zero[vrow * ngd + gv] : 0.0f;
-    }
-
     // queries and the zero block into LDS
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
@@ -435,6 +409,35 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             }
         }
     }
+    // This thread's token: value code row and value params.  Issued only
+    // now, once the key side's data has arrived: when every resident block
+    // asks for all its bytes at once, the key side's share arrives no sooner
+    // than the rest, and the key operands and the scores then wait longer.
+    const int64_t vrow = (int64_t)bh * a.S_max + t0 + tid;
+    uint32_t vw[DW];
+#pragma unroll
+    for (int k = 0; k < DW; ++k) vw[k] = 0u;
+    const bool vq = tid < nq_tok;              // this token is quantized
+    if (vq) {
+        const uint8_t* vp = a.v_codes + vrow * (D * BITS / 8);
+        if constexpr (DW >= 4) {
+#pragma unroll
+            for (int k = 0; k < DW / 4; ++k) {
+                const uint4 v = *reinterpret_cast<const uint4*>(vp + 16 * k);
+                vw[4 * k] = v.x; vw[4 * k + 1] = v.y; vw[4 * k + 2] = v.z; vw[4 * k + 3] = v.w;
+            }
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(vp);
+            vw[0] = v.x; vw[1] = v.y;
+        }
+    }
+    float svv[MAXGV], zvv[MAXGV];
+#pragma unroll
+    for (int gv = 0; gv < MAXGV; ++gv) {
+        svv[gv] = (vq && gv < ngd) ? a.v_scale[vrow * ngd + gv] : 0.0f;
+        zvv[gv] = (vq && gv < ngd) ? a.v_zero[vrow * ngd + gv] : 0.0f;
+    }
+
     __syncthreads();
 
     // ---- scores on the matrix cores: wave w takes 16-token tiles 2w,
@@ -658,9 +661,9 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
         vexp_s[tid] = op_exp(fmaxf(fmaxf(vmx_s[tid][0], vmx_s[tid][1]),
                                    fmaxf(vmx_s[tid][2], vmx_s[tid][3])));
     __syncthreads();
-    // the ring values' sums into the score rows (free now, and read only
-    // after the barrier below)
-    if (has_ring && tid < D) {
+    // the ring values' sums (zeros without ring tokens) into the score rows
+    // (free now, and read only after the barrier below)
+    if (tid < D) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j) p_s[j][tid] = o[j];
     }
@@ -699,7 +702,7 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     // ---- values on the matrix cores: wave w takes channel tiles 2w, 2w + 1,
     // 2w + 4, 2w + 5 (pairs of tiles in one value group when groups have 32
     // channels or more), with the B operands of a group loaded once
-    float* wbase = a.work + ((int64_t)bh * a.n_chunks + chunk) * nq * (D + 2);
+    float* wbase = a.work + ((int64_t)bh * a.n_chunks + chunk) * nq * att_slot(D);
     {
         const int col = b_col<NQ>(m16);
         int gcur = -1;
@@ -739,19 +742,22 @@ void attend_mfma_kernel(AttendArgs a, int chunk_top) {
             if (m16 < nq) {
                 const int e = vexp_s[gv];
                 const float zs = zsum_s[m16 * ngd + gv];
-                float* wj = wbase + m16 * (D + 2);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = mt * 16 + kb * 4 + i;
-                    wj[2 + c] = __builtin_ldexpf(ov[i], kCodeExp - e) + zs +
-                                (has_ring ? p_s[m16][c] : 0.0f);
-                }
+                const int c0 = mt * 16 + kb * 4;
+                // plus the ring values' sums (zeros in a chunk without ring
+                // tokens); four channels, one 16-byte store
+                const float4 rv = *reinterpret_cast<const float4*>(&p_s[m16][c0]);
+                float4 r;
+                r.x = __builtin_ldexpf(ov[0], kCodeExp - e) + zs + rv.x;
+                r.y = __builtin_ldexpf(ov[1], kCodeExp - e) + zs + rv.y;
+                r.z = __builtin_ldexpf(ov[2], kCodeExp - e) + zs + rv.z;
+                r.w = __builtin_ldexpf(ov[3], kCodeExp - e) + zs + rv.w;
+                *reinterpret_cast<float4*>(wbase + m16 * att_slot(D) + kAttData + c0) = r;
             }
         }
     }
     if (tid < nq) {
-        wbase[tid * (D + 2)] = ml_s[0][tid];
-        wbase[tid * (D + 2) + 1] = ml_s[1][tid];
+        wbase[tid * att_slot(D)] = ml_s[0][tid];
+        wbase[tid * att_slot(D) + 1] = ml_s[1][tid];
     }
 }
 

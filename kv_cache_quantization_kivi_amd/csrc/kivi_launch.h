@@ -106,6 +106,10 @@ struct AttendArgs {
     int32_t chunk0;        // first chunk of the token-per-thread kernel
 };
 int64_t attend_chunks(int64_t T);
+// Workspace slot per (bh, chunk, query head): m, l, two unused floats, then
+// the D partial outputs (16-byte aligned for whole-vector stores).
+constexpr int kAttData = 4;
+__host__ __device__ inline int64_t att_slot(int64_t D) { return D + kAttData; }
 int64_t attend_work_floats(int64_t BH, int64_t T, int64_t D, int64_t n_q);
 // The library-held attention workspace of the current device
 // (attend_scratch_bytes bytes): its device address, looked up on the

@@ -251,9 +251,9 @@ def test_attend_noalloc_rejects_before_any_launch(K):
     assert call(cache(), n_q=9) == SHAPE
     assert call(cache(T=0, Q=0)) == SHAPE
     assert call(cache(G_k=16, ring=64, D=256)) == SHAPE
-    # workspace = BH * chunks * n_q * (D + 2) * 4 bytes
+    # workspace = BH * chunks * n_q * (D + 4) * 4 bytes
     big = cache(T=32000, Q=31968)
-    need = 224 * ((32000 + 127) // 128) * 3 * 130 * 4
+    need = 224 * ((32000 + 127) // 128) * 3 * 132 * 4
     assert need > K.ATTEND_SCRATCH_BYTES
     assert call(big) == SCRATCH
     assert K.kivi_status_string(SCRATCH).startswith("the call needs more")
