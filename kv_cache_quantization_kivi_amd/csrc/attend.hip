@@ -337,14 +337,21 @@ __global__ __launch_bounds__(kAttChunk) void attend_partial_kernel(AttendArgs a)
 
 // Merge the chunks of each (bh, query head): out = sum_c e^{m_c - M} o_c /
 // sum_c e^{m_c - M} l_c with M = max_c m_c.  One wave per (bh, head), four
-// per block, over batches of 16 chunks: every load of a batch is issued at
+// per block, over batches of 32 chunks: every load of a batch is issued at
 // once (lane c takes chunk c's m and l, every lane its channels of each
 // chunk's o); the batch's maximum and denominator are reduced over the
-// first 16 lanes (one DPP row) and read back as wave-uniform values, and
+// first 32 lanes (two DPP rows, then a swizzle) and read back as
+// wave-uniform values, and
 // the running sums are rescaled when the maximum grows (online softmax).
 template <int CTRL>
 __device__ __forceinline__ float merge_dpp(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// The value of lane l ^ 16 (within each 32 lanes): ds_swizzle, bit mode
+// with xor mask 16.
+__device__ __forceinline__ float merge_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
 }
 
 template <int DT, int D>
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
     const int64_t cs = (int64_t)nq * att_slot(D);        // chunk stride
     const float* w = a.work + (int64_t)bh * nc * cs + (int64_t)j * att_slot(D);
     constexpr int PER = D / 64;                  // channels per lane
-    constexpr int B = 16;                        // chunks per batch
+    constexpr int B = 32;                        // chunks per batch
     float mx = -__builtin_huge_valf(), ls = 0.0f;
     float O[PER];
 #pragma unroll
@@ -373,14 +380,16 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
 #pragma unroll
             for (int i = 0; i < PER; ++i)
                 ov[c][i] = c < nb ? w[(c0 + c) * cs + kAttData + lane + 64 * i] : 0.0f;
-        // the batch maximum over lanes 0..15: quad_perm [1,0,3,2],
-        // quad_perm [2,3,0,1], row_half_mirror, row_mirror
+        // the batch maximum over lanes 0..31: quad_perm [1,0,3,2],
+        // quad_perm [2,3,0,1], row_half_mirror, row_mirror, then lane ^ 16
+        // (an LDS-unit swizzle)
         float bm = ml.x;
         bm = fmaxf(bm, merge_dpp<0xB1>(bm));
         bm = fmaxf(bm, merge_dpp<0x4E>(bm));
         bm = fmaxf(bm, merge_dpp<0x141>(bm));
         bm = fmaxf(bm, merge_dpp<0x140>(bm));
-        // lane 0 (the first active lane: the whole wave runs) holds row 0's result
+        bm = fmaxf(bm, merge_xor16(bm));
+        // lane 0 (the first active lane: the whole wave runs) holds the result
         const float mnew =
             fmaxf(mx, __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(bm))));
         const float scale = __expf(mx - mnew);   // 0 on the first batch
@@ -390,6 +399,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a,
         el += merge_dpp<0x4E>(el);
         el += merge_dpp<0x141>(el);
         el += merge_dpp<0x140>(el);
+        el += merge_xor16(el);
         ls = ls * scale + __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(el)));
 #pragma unroll
         for (int i = 0; i < PER; ++i) O[i] *= scale;
