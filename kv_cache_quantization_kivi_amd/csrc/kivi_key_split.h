@@ -33,7 +33,8 @@ constexpr int kKeyGMaxPair = 32;   // key groups of the paired K+V launch: 17..3
 // dst + t * cstride bytes and its recon row at rdst + t * rstride elements.
 // With SINKS, bit t of `sinks` marks the lane's token t as a sink: code 0,
 // and its own row as the reconstruction.
-template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL, bool SINKS>
+template <int DT, int BITS, bool WQ, bool WR, bool FAST, int TPL, bool SINKS,
+          bool TO_LDS = false>
 __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
                                            const Params (&pk)[8], int32_t n,
                                            uint8_t* dst, int64_t cstride,
@@ -53,8 +54,9 @@ __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
             // quantize-only: codes streamed (measured faster for this
             // kernel and for the kernels after it); the fused form keeps
             // plain stores (streaming them beside the reconstruction was
-            // slower)
-            if constexpr (WQ) store_codes<BITS, !WR>(dst + t * cstride, q);
+            // slower).  TO_LDS: dst is the tile's code block in LDS.
+            if constexpr (WQ && TO_LDS) store_codes<BITS, false>(dst + t * cstride, q);
+            else if constexpr (WQ) store_codes<BITS, !WR>(dst + t * cstride, q);
             if constexpr (WR) store16_nt(rdst + t * rstride, r);
         }
     }
@@ -63,8 +65,13 @@ __device__ __forceinline__ void emit_split(const uint4 (&v)[TPL],
 // IO: the row layout (DenseRows, CacheRows or ListRows, kivi_rows.h); NG here is the
 // number of groups per bh that this launch quantizes.
 // gid: the lane's index over all lanes of the launch (waves 64-aligned).
+// STAGE (with D = 128): a tile's codes are gathered in LDS and stored as
+// 16-byte pieces of its contiguous code block (a group's rows are
+// consecutive in every row layout), instead of one BITS-byte store per
+// lane and token; BLOCK is the launch's block size, whose lanes map to
+// tiles from lane 0 (gid = block * BLOCK + thread).
 template <int DT, int BITS, int TPL, int SPLIT, bool WQ, bool WR, bool ILV,
-          typename IO>
+          typename IO, bool STAGE = false, int BLOCK = 64>
 __device__ __forceinline__ void quant_keys_split_body(
     IO io, uint32_t gid, uint32_t n_lanes, uint32_t D8, uint32_t NG,
     uint8_t* __restrict__ codes, float* __restrict__ scale,
@@ -157,8 +164,39 @@ __device__ __forceinline__ void quant_keys_split_body(
     const int32_t step = ILV ? SPLIT : 1;
     const int64_t row_bytes = (int64_t)D8 * BITS;
     const int64_t orow = io.out_row(bh, s0 + first);
-    uint8_t* dst = WQ ? codes + orow * row_bytes + (int64_t)c * BITS : nullptr;
     uint16_t* rdst = WR ? recon + orow * D + (int64_t)c * 8 : nullptr;
+    if constexpr (STAGE && WQ) {
+        constexpr int TL = 16 * SPLIT;                // a tile's lanes at D = 128
+        constexpr int TB = TPL * SPLIT * 16 * BITS;   // a tile's code bytes, at most
+        static_assert(BLOCK % TL == 0, "tiles whole inside a block");
+        __shared__ __attribute__((aligned(16))) uint8_t code_s[BLOCK / TL][TB];
+        if (D8 == 16) {                               // launch-uniform
+            uint8_t* tl = code_s[threadIdx.x / TL];
+            uint8_t* ldst = tl + (int64_t)first * row_bytes + (int64_t)c * BITS;
+            if (fast)
+                emit_split<DT, BITS, WQ, WR, true, TPL, IO::kSinks, true>(
+                    v, pk, n, ldst, step * row_bytes, rdst, step * D, lane_sinks);
+            else
+                emit_split<DT, BITS, WQ, WR, false, TPL, IO::kSinks, true>(
+                    v, pk, n, ldst, step * row_bytes, rdst, step * D, lane_sinks);
+            wave_lds_sync();
+            // nt rows of 16 * BITS bytes: a multiple of 16 bytes
+            const int32_t bytes = nt * (int32_t)row_bytes;
+            uint8_t* gdst = codes + io.out_row(bh, s0) * row_bytes;
+            const int32_t lt = (int32_t)(threadIdx.x % TL);
+#pragma unroll
+            for (int k = 0; k < (TB + 16 * TL - 1) / (16 * TL); ++k) {
+                const int32_t piece = lt + TL * k;
+                if (piece * 16 < bytes) {
+                    const uint4 w = *reinterpret_cast<const uint4*>(tl + piece * 16);
+                    if constexpr (!WR) store16_nt(gdst + piece * 16, w);
+                    else *reinterpret_cast<uint4*>(gdst + piece * 16) = w;
+                }
+            }
+            return;
+        }
+    }
+    uint8_t* dst = WQ ? codes + orow * row_bytes + (int64_t)c * BITS : nullptr;
     if (fast)
         emit_split<DT, BITS, WQ, WR, true, TPL, IO::kSinks>(
             v, pk, n, dst, step * row_bytes, rdst, step * D, lane_sinks);

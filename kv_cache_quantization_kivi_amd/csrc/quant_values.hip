@@ -429,7 +429,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(
             vio, (uint64_t)blockIdx.x * 256u + threadIdx.x, lds, n_rows, D8, lp,
             red, gl, NGD, vec, tile, vc, vs, vz, vr);
     } else {
-        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, WQ, WR, true, IO>(
+        quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, WQ, WR, true, IO,
+                              (BITS <= 4), 256>(
             kio, (blockIdx.x - v_blocks) * 256u + threadIdx.x, k_lanes, D8, NG,
             kc, ks, kz, kr);
     }
@@ -527,8 +528,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t lds[4 * kRecWaveBytes];
     if (blockIdx.x < k_blocks) {
         quant_keys_split_body<DT, BITS, kKeyGMaxPair / 4, 4, true, false, true,
-                              CacheRows>(kio, blockIdx.x * 256u + threadIdx.x,
-                                         k_lanes, D8, NG, kc, ks, kz, nullptr);
+                              CacheRows, (BITS <= 4), 256>(
+            kio, blockIdx.x * 256u + threadIdx.x, k_lanes, D8, NG, kc, ks, kz, nullptr);
     } else if (blockIdx.x < k_blocks + v_blocks) {
         quant_values_body<DT, BITS, 1, true, false, CacheRows>(
             vio, (uint64_t)(blockIdx.x - k_blocks) * 256u + threadIdx.x, lds,
