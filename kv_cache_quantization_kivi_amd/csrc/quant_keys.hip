@@ -257,8 +257,13 @@ static hipError_t launch_keys_mode(const QuantJob& j) {
     const uint64_t D8 = (uint64_t)(j.D / 8);
     const uint64_t NG = (uint64_t)((j.S + j.group - 1) / j.group);
     const uint64_t items = (uint64_t)j.BH * NG * D8;
-    // n_lanes = items * SPLIT must fit the kernel's 32-bit lane index
-    if (items < kKeySplitBelow && 64 % (D8 * 4) == 0)
+    // n_lanes = items * SPLIT must fit the kernel's 32-bit lane index.
+    // With a reconstruction to write, 4 lanes per item at every size: each
+    // reconstruction store instruction then covers 4 consecutive rows of a
+    // tile (1 KiB at D = 128), and those stores are most of the kernel's
+    // bytes.  A/B on the roundtrip tensor: the fused kernel 1-2% faster; the
+    // quantize-only kernel 8-10% slower the same way, its loads dominating.
+    if ((items < kKeySplitBelow || (wr && items < (1ull << 30))) && 64 % (D8 * 4) == 0)
         return launch_keys_split_mode<DT, BITS, GMAX, 4>(j);
     if (items < (1ull << 31) && 64 % (D8 * 2) == 0)
         return launch_keys_split_mode<DT, BITS, GMAX, 2>(j);
