@@ -66,7 +66,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m "
-            "kv_cache_quantization_kivi_amd.build` (or __graft_entry__.build())")
+            "kv_cache_quantization_kivi_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64

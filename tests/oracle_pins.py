@@ -493,7 +493,7 @@ def _cosine_unit_norm_keys(o, bits, n_tok=4096, D=128, seed=53):
 
 def pin_cosine_statistics(o):
     c2 = _cosine_unit_norm_keys(o, 2)
-    assert 0.92 <= c2 <= 0.94, c2        # pages: "around 0.93"
+    assert 0.92 <= c2 <= 0.94, c2        # the pages give about 0.93
     c4 = _cosine_unit_norm_keys(o, 4)
     assert c4 > 0.995, c4                # pages: 4-bit "> 0.995"
 
