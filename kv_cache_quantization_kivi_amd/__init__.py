@@ -179,10 +179,24 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _stream(device, stream):
+# torch's current stream as a raw handle, without building a Stream object
+# (a few microseconds per call, which a one-token cache append notices)
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(device, stream):
+    """The stream as an int handle: `stream` if given, else torch's current
+    stream on `device`."""
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+        return int(stream)
+    if _RAW_STREAM is not None:
+        idx = device.index
+        return _RAW_STREAM(idx if idx is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _stream(device, stream):
+    return ctypes.c_void_p(_stream_handle(device, stream))
 
 
 def _check(st, what):
@@ -609,6 +623,7 @@ class KiviCache:
                             self.k_ring, self.v_ring, self.k_codes,
                             self.v_codes, self.k_scale, self.k_zero,
                             self.v_scale, self.v_zero)], 0, 0)
+        self._cref = ctypes.byref(self.c)      # reused by every call
 
     @property
     def T(self):
@@ -627,11 +642,12 @@ class KiviCache:
         n = k_new.shape[-2]
         if v_new.shape != k_new.shape:
             raise ValueError("k_new and v_new differ in shape")
-        L = _lib()
-        st = L.kivi_cache_append(ctypes.byref(self.c), _ptr(k_new),
-                                 _ptr(v_new), n,
-                                 _stream(k_new.device, stream))
-        _check(st, "kivi_cache_append")
+        # every argument type is declared, so plain ints marshal directly
+        st = _lib().kivi_cache_append(self._cref, k_new.data_ptr(),
+                                      v_new.data_ptr(), n,
+                                      _stream_handle(k_new.device, stream))
+        if st != 0:
+            raise KiviError(st, "kivi_cache_append")
 
     def attend(self, q, sm_scale, out=None, work=None, stream=None):
         """Decode attention of q [BH, n_q, D] (the cache's dtype) over the
@@ -642,15 +658,16 @@ class KiviCache:
             raise ValueError("q: a contiguous tensor of the cache's dtype")
         n_q = q.shape[-2]
         L = _lib()
-        nb = L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
         if out is None:
             out = torch.empty_like(q)
         if work is None:
+            nb = L.kivi_cache_attend_work_bytes(self._cref, n_q)
             work = torch.empty(max(nb, 16), dtype=torch.uint8,
                                device=q.device)
-        st = L.kivi_cache_attend(ctypes.byref(self.c), _ptr(q), n_q,
-                                 float(sm_scale), _ptr(out), _ptr(work),
-                                 work.numel(), _stream(q.device, stream))
+        st = L.kivi_cache_attend(self._cref, q.data_ptr(), n_q,
+                                 float(sm_scale), out.data_ptr(),
+                                 work.data_ptr(), work.numel(),
+                                 _stream_handle(q.device, stream))
         _check(st, "kivi_cache_attend")
         return out
 
@@ -663,15 +680,15 @@ class KiviCache:
         if out is None or out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out: a tensor shaped and typed like q")
         L = _lib()
-        st = L.kivi_cache_attend_noalloc(ctypes.byref(self.c), _ptr(q),
+        st = L.kivi_cache_attend_noalloc(self._cref, q.data_ptr(),
                                          q.shape[-2], float(sm_scale),
-                                         _ptr(out), _stream(q.device, stream))
+                                         out.data_ptr(),
+                                         _stream_handle(q.device, stream))
         _check(st, "kivi_cache_attend_noalloc")
         return out
 
     def attend_work_bytes(self, n_q):
-        L = _lib()
-        return L.kivi_cache_attend_work_bytes(ctypes.byref(self.c), n_q)
+        return _lib().kivi_cache_attend_work_bytes(self._cref, n_q)
 
 
 def kivi_cache_attend(cache, q, sm_scale, out=None, work=None, stream=None):
