@@ -216,6 +216,12 @@ KEY_PATHS = [
     (2, 64, 256, FP16, 2, 32),    # D8 = 32: one lane (small), two (large)
     (2, 64, 512, BF16, 4, 32),    # D8 = 64: one lane per item, staged codes
     (2, 96, 64, FP16, 2, 48),     # group > 32: generic quantizer, direct dequant
+    # D = 128 with codes of at most 4 bits: a tile's codes go through LDS
+    # and out as 16-byte pieces of its code block; ragged last groups
+    (3, 70, 128, BF16, 2, 32),    # last group of 6 tokens
+    (2, 45, 128, FP16, 1, 32),    # 1-bit rows of 16 bytes
+    (2, 41, 128, BF16, 4, 8),     # GMAX 8, last group of one token
+    (2, 50, 128, FP16, 2, 16),    # GMAX 16, last group of 2 tokens
 ]
 KEY_SPLIT_BELOW = 65536
 
