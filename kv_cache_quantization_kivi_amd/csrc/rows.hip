@@ -215,12 +215,13 @@ __global__ __launch_bounds__(kPartThreads) void partition_top_kernel(
 #pragma unroll
             for (int i = 0; i < kPartPer; ++i) {
                 const int32_t s = s0 + i;
-                if (s >= S) break;
-                if ((mark >> i) & 1u) {
-                    pos_hi[(int64_t)b * n_hi + hi_rank] = s;
-                    ++hi_rank;
-                } else {
-                    pos_lo[(int64_t)b * (S - n_hi) + (s - (int32_t)hi_rank)] = s;
+                if (s < S) {                       // positions past S: none
+                    if ((mark >> i) & 1u) {
+                        pos_hi[(int64_t)b * n_hi + hi_rank] = s;
+                        ++hi_rank;
+                    } else {
+                        pos_lo[(int64_t)b * (S - n_hi) + (s - (int32_t)hi_rank)] = s;
+                    }
                 }
             }
         }
