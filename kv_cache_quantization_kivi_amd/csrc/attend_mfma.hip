@@ -50,10 +50,14 @@ constexpr int kMChunk = 128;            // tokens per block, one per thread
 // Sizes of one instantiation.  GK is the smallest key and value group the
 // instantiation serves (16, or 32 when G_k = 32 and G_v >= 32): it bounds
 // the key groups of a chunk and the value groups of a row, and so the LDS
-// that holds their operands.  kWaves: the waves per SIMD that the LDS
-// footprint allows (two waves per block, four SIMDs per CU, 160 KiB of LDS
-// per CU), capped at 5 (4 for 4-bit codes); the launch bounds ask the
-// compiler for registers that allow as many.
+// that holds their operands.  kMinBlocks: the launch bounds' second
+// argument, the blocks per CU whose residency the compiler must allow with
+// its register choice (k blocks of two waves on four SIMDs: registers for
+// k / 2 waves per SIMD).  It is half the blocks the LDS footprint allows
+// (160 KiB per CU), capped at 5 (4 for 4-bit codes, whose key code
+// registers double), so it only limits the largest instantiations; the
+// common ones compile well inside it (2-bit, D = 128, three query heads:
+// 75 VGPRs, 6 waves per SIMD).
 template <int BITS, int D, int NQ, int GK>
 struct MfmaShape {
     static constexpr int D8 = D / 8;
@@ -80,7 +84,8 @@ struct MfmaShape {
     static constexpr int kBlocks = (160 * 1024) / kLds;
     // 4-bit codes hold twice the key code registers: at most 4 waves there
     static constexpr int kCap = BITS == 4 ? 4 : 5;
-    static constexpr int kWaves = kBlocks / 2 < 1 ? 1 : (kBlocks / 2 > kCap ? kCap : kBlocks / 2);
+    static constexpr int kMinBlocks =
+        kBlocks / 2 < 1 ? 1 : (kBlocks / 2 > kCap ? kCap : kBlocks / 2);
 };
 
 __device__ __forceinline__ h8_t as_h8(uint32_t a, uint32_t b, uint32_t c,
@@ -251,7 +256,7 @@ __device__ __forceinline__ float widen_h(uint16_t h) {
 // of that group: its tiles are taken group by group (tiles 2w, 2w + 1,
 // 2w + 4, 2w + 5 of wave w).
 template <int DT, int BITS, int D, int NQ, int GK>
-__global__ __launch_bounds__(kMChunk, (MfmaShape<BITS, D, NQ, GK>::kWaves))
+__global__ __launch_bounds__(kMChunk, (MfmaShape<BITS, D, NQ, GK>::kMinBlocks))
 void attend_mfma_kernel(AttendArgs a, int chunk_top) {
     using Sh = MfmaShape<BITS, D, NQ, GK>;
     constexpr int D8 = Sh::D8, KS = Sh::KS, CPL = Sh::CPL, LB = Sh::LB;
