@@ -1245,7 +1245,11 @@ def _template(name):
 def _library_dispatches(rows, value_of=None):
     """Per dispatch of a library kernel (name in namespace kivi), in the
     order the GPU ran them: (kernel name, start, end, value) where value
-    comes from value_of(rows of that dispatch) (counter runs) or None."""
+    comes from value_of(rows of that dispatch) (counter runs) or None.
+    The order is the dispatch id's, the order of submission: every step
+    runs on one stream, whose kernels run in that order, while the
+    profiler's start timestamps of back-to-back kernels can land a few
+    hundred nanoseconds out of order."""
     import collections
     by = collections.OrderedDict()
     for r in rows:
@@ -1255,11 +1259,11 @@ def _library_dispatches(rows, value_of=None):
     out = []
     for rs in by.values():
         r0 = rs[0]
-        out.append((r0["Kernel_Name"], int(r0["Start_Timestamp"]),
-                    int(r0["End_Timestamp"]),
+        out.append((int(r0["Dispatch_Id"]), r0["Kernel_Name"],
+                    int(r0["Start_Timestamp"]), int(r0["End_Timestamp"]),
                     value_of(rs) if value_of else None))
-    out.sort(key=lambda x: x[1])
-    return out
+    out.sort(key=lambda x: x[0])
+    return [x[1:] for x in out]
 
 
 def _timed(disp, layout):

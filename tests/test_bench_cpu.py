@@ -139,3 +139,26 @@ def test_traffic_summary_per_launch_or_per_call(tmp_path, timing):
         assert (c["fetch_bytes"], c["write_bytes"]) == (245760, 122880)
     else:                       # the first launch only; c#2 has no bytes
         assert (c["fetch_bytes"], c["write_bytes"]) == (204800, 102400)
+
+
+def test_dispatch_order_is_submission_order():
+    # back-to-back kernels of one stream whose profiler start timestamps
+    # land out of order (the second one stamped 100 ns before the first)
+    # stay in dispatch order; other namespaces are ignored
+    sys.path.insert(0, ROOT)
+    import bench
+    rows = [
+        {"Dispatch_Id": "7", "Kernel_Name": "void kivi::chunk<0>(int)",
+         "Start_Timestamp": "1000", "End_Timestamp": "2000"},
+        {"Dispatch_Id": "8", "Kernel_Name": "at::fill<float>()",
+         "Start_Timestamp": "2010", "End_Timestamp": "2020"},
+        {"Dispatch_Id": "9", "Kernel_Name": "void kivi::merge<0>(int)",
+         "Start_Timestamp": "2100", "End_Timestamp": "2500"},
+        {"Dispatch_Id": "10", "Kernel_Name": "void kivi::chunk<0>(int)",
+         "Start_Timestamp": "2000", "End_Timestamp": "3000"},
+    ]
+    got = bench._library_dispatches(rows)
+    assert [g[0] for g in got] == ["void kivi::chunk<0>(int)",
+                                   "void kivi::merge<0>(int)",
+                                   "void kivi::chunk<0>(int)"]
+    assert [g[1] for g in got] == [1000, 2100, 2000]
