@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of quantization and dequantization
 runs in the HIP kernels behind the C ABI declared in include/kivi.h.  Torch
-tensors supply device memory and the current HIP stream; outputs that are
+tensors supply device memory and the current HIP stream (every call also
+takes stream=, a torch.cuda.Stream or a raw handle); outputs that are
 not passed in are allocated with torch on the input's device.  Importing
 this package works without the library (so that its `build` submodule can
 run from a clean checkout), but the first call of any function below fails
@@ -185,10 +186,10 @@ _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream_handle(device, stream):
-    """The stream as an int handle: `stream` if given, else torch's current
-    stream on `device`."""
+    """The stream as an int handle: `stream` if given (a torch.cuda.Stream
+    or a raw hipStream_t handle), else torch's current stream on `device`."""
     if stream is not None:
-        return int(stream)
+        return int(getattr(stream, "cuda_stream", stream))
     if _RAW_STREAM is not None:
         idx = device.index
         return _RAW_STREAM(idx if idx is not None else torch.cuda.current_device())

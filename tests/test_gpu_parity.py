@@ -334,6 +334,13 @@ def test_deterministic_and_stream(K):
         s.synchronize()
     for u, v in zip(a, b):
         assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    # stream= given as a torch stream and as its raw handle
+    s2 = torch.cuda.Stream()
+    for st in (s2, s2.cuda_stream):
+        out = K.kivi_quant_keys(x, 2, 32, stream=st)
+        s2.synchronize()
+        for u, v in zip(a, [host(t) for t in out]):
+            assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
 
 
 @pytest.mark.parametrize("shape", [(224, 32, 128), (512, 256, 128)],
