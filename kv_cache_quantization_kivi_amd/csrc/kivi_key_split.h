@@ -92,12 +92,27 @@ __device__ __forceinline__ void quant_keys_split_body(
     uint32_t lane_sinks = 0;   // bit t: this lane's token t is a sink
     uint32_t group_sinks = 0;  // bit t: token s0 + t is a sink
     if constexpr (IO::kSinks) group_sinks = io.sink_mask(bh, s0, nt);
+    if constexpr (IO::kOff32) {
+        // a 32-bit byte offset from the wave-uniform base: the loads take
+        // the scalar-base form and the per-token address is one 32-bit add
+        const char* xb = reinterpret_cast<const char*>(io.x);
+        const uint32_t b0 =
+            (uint32_t)((((uint64_t)bh * (uint32_t)io.S + (uint32_t)s0) * (uint64_t)D +
+                        (uint64_t)c * 8u) * 2u);
 #pragma unroll
-    for (int t = 0; t < TPL; ++t) {
-        const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
-                                   : (int32_t)part * TPL + t, nt - 1);
-        v[t] = load16_nt(rows.row(tt, D) + (int64_t)c * 8);
-        if constexpr (IO::kSinks) lane_sinks |= ((group_sinks >> tt) & 1u) << t;
+        for (int t = 0; t < TPL; ++t) {
+            const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
+                                       : (int32_t)part * TPL + t, nt - 1);
+            v[t] = load16_nt(xb + (b0 + (uint32_t)tt * (uint32_t)D * 2u));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) {
+            const int32_t tt = min(ILV ? (int32_t)part + SPLIT * t
+                                       : (int32_t)part * TPL + t, nt - 1);
+            v[t] = load16_nt(rows.row(tt, D) + (int64_t)c * 8);
+            if constexpr (IO::kSinks) lane_sinks |= ((group_sinks >> tt) & 1u) << t;
+        }
     }
 
     // A sink takes no part in the min/max: it is replaced there by the

@@ -53,6 +53,7 @@ struct DenseRows {
     }
     // no sinks: every token takes part in its group's min/max
     static constexpr bool kSinks = false;
+    static constexpr bool kOff32 = false;
     __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     // value rows: row r of the flattened [BH * S] rows
     static constexpr bool kContiguous = true;
@@ -60,6 +61,12 @@ struct DenseRows {
         return x + r * D;
     }
     __device__ int64_t vout(int64_t r) const { return r; }
+};
+
+// DenseRows of a tensor under 4 GiB: the key body forms each row's address
+// as a 32-bit byte offset from x.
+struct DenseRows32 : DenseRows {
+    static constexpr bool kOff32 = true;
 };
 
 struct CacheRows {
@@ -90,6 +97,7 @@ struct CacheRows {
         return (int64_t)bh * NG_out + (uint32_t)(Q / G) + g;
     }
     static constexpr bool kSinks = false;
+    static constexpr bool kOff32 = false;
     __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     static constexpr bool kContiguous = false;
     __device__ const uint16_t* vrow(int64_t r, int64_t D) const {
@@ -157,6 +165,7 @@ struct ListRows {
         return (int64_t)bh * NG + g;
     }
     static constexpr bool kSinks = false;
+    static constexpr bool kOff32 = false;
     __device__ uint32_t sink_mask(uint32_t, int32_t, int32_t) const { return 0u; }
     // value rows: row r of the flattened [BH * n] set rows (fewer than 2^31)
     static constexpr bool kContiguous = false;

@@ -220,6 +220,16 @@ static hipError_t launch_keys_split_t(const QuantJob& j) {
     const uint32_t blocks = (uint32_t)((n_lanes + 63) / 64);
     const DenseRows io{static_cast<const uint16_t*>(j.x), (int32_t)j.S, NG,
                        (int32_t)j.group};
+    // a tensor under 4 GiB: row addresses as 32-bit offsets (measured 1-2%
+    // faster on the roundtrip tensor)
+    if ((uint64_t)j.BH * (uint64_t)j.S * (uint64_t)j.D * 2u < (1ull << 32)) {
+        DenseRows32 io32;
+        static_cast<DenseRows&>(io32) = io;
+        return launch_kernel(
+            (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true, DenseRows32>),
+            dim3(blocks), dim3(64), 0, j.stream, io32, (uint32_t)n_lanes, D8, NG,
+            j.codes, j.scale, j.zero, static_cast<uint16_t*>(j.recon));
+    }
     return launch_kernel(
         (quant_keys_split_kernel<DT, BITS, TPL, SPLIT, WQ, WR, true, DenseRows>),
         dim3(blocks), dim3(64), 0, j.stream, io, (uint32_t)n_lanes, D8, NG,
