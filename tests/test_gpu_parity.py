@@ -429,6 +429,42 @@ def test_more_than_2_31_elements(K, O):
         torch.cuda.empty_cache()
 
 
+def test_keys_just_under_4_gib(K, O):
+    """A [511, 32768, 128] fp16 tensor (4 286 578 688 bytes, just under
+    2^32): the dense key quantizer forms its row addresses as 32-bit byte
+    offsets here.  The two topmost slices (offsets within 16 MB of 2^32)
+    are checked against the oracle, quantize-only and fused."""
+    BH, S, D = 511, 32768, 128
+    assert BH * S * D * 2 < 2 ** 32 and (BH + 1) * S * D * 2 > 2 ** 32 - 2 ** 23
+    w = W.WORKLOADS["prefill"]
+    base = W.gen_tensor(w, "K", range(8))
+    say(f"[4 GiB] uploading {BH}x{S}x{D}")
+    x = torch.empty((BH, S, D), dtype=torch.float16, device="cuda")
+    bd = to_dev(base, FP16)
+    for i in range(0, BH, 8):
+        n = min(8, BH - i)
+        x[i:i + n] = bd[:n]
+    del bd
+    sel = [509, 510]
+    xs = base[[b % 8 for b in sel]]
+    oc, os_, oz = O.quant_keys(xs, FP16, 2, 32)
+    want = O.dequant_keys(oc, os_, oz, xs.shape, 2, 32, FP16)
+    say("[4 GiB] quant keys")
+    c, s_, z = K.kivi_quant_keys(x, 2, 32)
+    torch.cuda.synchronize()
+    assert_codes_equal(host(c[sel]), oc, "4 GiB key codes")
+    assert_f32_bits_equal(host(s_[sel]), os_, "4 GiB key scale")
+    assert_f32_bits_equal(host(z[sel]), oz, "4 GiB key zero")
+    del c, s_, z
+    say("[4 GiB] fused keys")
+    r, c, s_, z = K.kivi_quant_dequant_keys(x, 2, 32)
+    torch.cuda.synchronize()
+    assert_codes_equal(host(c[sel]), oc, "4 GiB fused key codes")
+    assert_recon_equal(bits16(r[sel]), want, "4 GiB fused key recon")
+    del r, c, s_, z, x
+    torch.cuda.empty_cache()
+
+
 def test_selftest_division(K):
     """The exact-division shortcuts hold on this GPU for every significand
     at every exponent the kernels use them."""
